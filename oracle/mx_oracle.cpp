@@ -1,0 +1,739 @@
+// CPU oracle for MXFP8 block-scaled attention (forward and backward), the MX quantizer,
+// the jagged scale scatter and the RMSNorm+quantize producer.
+//
+// TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the benchmark's CPU
+// baseline may load this library. The product path (the HIP library) never calls it, and
+// the two share no code, header, table or constant generator.
+//
+// Sources (the pages this follows; cited by short name below):
+//   [AE]  andresseo.expert, "MXFP8 FlashAttention-4 Hits 2.85 Petaflops in Meta's Production
+//         Training". Sections: "Inside the TMEM Bargain and Zero-Gather Jagged Pipeline" (TMEM),
+//         "What the Benchmarks Show About Low-Precision Training" (Bench).
+//   [BR]  brifing.si, "Meta's FlashAttention-4 Achieves 2.85 PF/s with MXFP8 on Blackwell GPUs",
+//         numbered items 1-12.
+//   [TC]  theclarity.today, "Meta's MXFP8 FlashAttention-4 kernel, tackling TMEM scale-factor
+//         constraints, hits up to 1.6x over BF16", paragraphs 1-4.
+//   [KC]  kongchang.com, "Low-Precision FlashAttention-4: End-to-End Block-Scaled Attention on
+//         Blackwell". Sections "Why MXFP8", "Hardware Adaptation for Blackwell".
+//
+// Style: plain loops, FP64 wherever the pages do not fix a precision, FP32 rounding exactly at
+// the points where the pages put FP32 (softmax, the FP32 accumulators), one function per step.
+// Readings of points the pages leave open are marked READING and listed in the design doc.
+//
+// Parity status of each function is stated at its definition ("pinned by ..." names the
+// non-oracle fact each one is checked against in tests/test_oracle_pins.py).
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <cstdlib>
+#include <vector>
+#include <thread>
+#include <atomic>
+#include <algorithm>
+#include <limits>
+
+namespace {
+
+// ---------------------------------------------------------------------------------------------
+// Scalar formats
+// ---------------------------------------------------------------------------------------------
+
+// fp32 rounding of an exact (double) value: C's double->float conversion rounds to nearest even.
+inline double fl32(double x) { return (double)(float)x; }
+
+inline double pow2(int e) { return std::ldexp(1.0, e); }
+
+// bf16 is the top half of an fp32 pattern.
+inline double bf16_value(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+// fp32 -> bf16 with round to nearest even; NaN stays a quiet NaN.
+inline uint16_t bf16_round(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
+  uint32_t lsb = (u >> 16) & 1u;
+  u += 0x7fffu + lsb;
+  return (uint16_t)(u >> 16);
+}
+
+// E4M3 ("FN" variant of the OCP MX formats named in [KC "Why MXFP8"]): 1 sign, 4 exponent bits
+// with bias 7, 3 mantissa bits. Exponent field 0 holds subnormals m * 2^-9. The patterns
+// S.1111.111 are NaN and there is no infinity, so the largest finite magnitude is 1.75 * 2^8 = 448.
+// Pinned by: exhaustive decode of all 256 codes against known values; monotonicity.
+double e4m3_decode(uint8_t c) {
+  int s = c >> 7, e = (c >> 3) & 0xf, m = c & 7;
+  if (e == 0xf && m == 7) return std::numeric_limits<double>::quiet_NaN();
+  double mag = (e == 0) ? m * pow2(-9) : (1.0 + m / 8.0) * pow2(e - 7);
+  return s ? -mag : mag;
+}
+
+// Code of a representable, non-negative E4M3 value (inverse of the table above).
+uint8_t e4m3_code_of_magnitude(double y) {
+  if (y < pow2(-6)) return (uint8_t)(y / pow2(-9));  // subnormal: y = m * 2^-9, m in 0..7
+  int ex;
+  std::frexp(y, &ex);  // y = f * 2^ex, f in [0.5, 1)  =>  y in [2^(ex-1), 2^ex)
+  int e = ex - 1;
+  int mant = (int)((y / pow2(e) - 1.0) * 8.0);
+  return (uint8_t)(((e + 7) << 3) | mant);
+}
+
+// Encode with round-to-nearest-even at every exponent (subnormals included) and saturation of
+// magnitudes above 448 to 448. A value that rounds to zero keeps its sign. NaN -> 0x7F.
+// READING (the pages name only "E4M3"; the saturating round-to-nearest-even pack is fixed by the
+// method's statement of the quantizer): see DESIGN.md, "Readings".
+// Pinned by: brute-force nearest-even search over all 127 non-negative finite codes.
+uint8_t e4m3_encode(double v) {
+  if (std::isnan(v)) return 0x7f;
+  uint8_t sign = std::signbit(v) ? 0x80 : 0x00;
+  double a = std::fabs(v);
+  if (std::isinf(a) || a >= 448.0) return sign | 0x7e;
+  // Spacing of representable values around a: 2^(e-3) in the normal binade [2^e, 2^(e+1)),
+  // e >= -6; 2^-9 below 2^-6.
+  int e = -6;
+  if (a >= pow2(-6)) {
+    int ex;
+    std::frexp(a, &ex);
+    e = ex - 1;
+  }
+  double quantum = pow2(e - 3);
+  double n = a / quantum;  // exact: a power-of-two division
+  double r = std::nearbyint(n);  // default rounding mode: nearest, ties to even
+  double y = r * quantum;
+  if (y > 448.0) y = 448.0;
+  return sign | e4m3_code_of_magnitude(y);
+}
+
+// E8M0 shared scale: the byte e stands for 2^(e-127); 255 is NaN [KC "Why MXFP8": one shared
+// exponent per block of 32].
+// Scale rule [AE TMEM: "bit extraction instead of logarithms or division"]: the block's scale
+// exponent is floor(log2(amax)) minus the largest E4M3 exponent (8), so the largest element lands
+// in [256, 512). In fp32 bits this is (exponent field of amax) - 8. Clamped to [0, 254]; a block
+// with no non-zero element gets 0; a block holding NaN or Inf gets 255 (READING A1).
+// Pinned by: code(1.0) = 119, code(448) = 127, code(512) = 128, clamps, specials.
+int e8m0_code(double amax) {
+  if (!std::isfinite(amax)) return 255;
+  if (amax == 0.0) return 0;
+  int ex;
+  std::frexp(amax, &ex);  // floor(log2 amax) = ex - 1
+  int code = (ex - 1) + 127 - 8;
+  if (code < 0) code = 0;
+  if (code > 254) code = 254;
+  return code;
+}
+
+double e8m0_value(int code) {
+  if (code == 255) return std::numeric_limits<double>::quiet_NaN();
+  return pow2(code - 127);
+}
+
+// binary16 rounding (nearest even), overflow to infinity; used for the FP16 dQ accumulator.
+double fp16_round(double v) {
+  if (std::isnan(v) || std::isinf(v) || v == 0.0) return v;
+  double a = std::fabs(v);
+  int e = -14;  // subnormal spacing 2^-24
+  if (a >= pow2(-14)) {
+    int ex;
+    std::frexp(a, &ex);
+    e = ex - 1;
+  }
+  double quantum = pow2(e - 10);
+  double y = std::nearbyint(a / quantum) * quantum;
+  if (y >= 65520.0) y = std::numeric_limits<double>::infinity();  // beyond max+half ulp
+  return std::copysign(y, v);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Block structure of a jagged [T, C] matrix
+// ---------------------------------------------------------------------------------------------
+
+enum Mode { ROW32 = 0, COL32 = 1, SQ32 = 2 };
+
+// Token blocks of 32 start at each sequence start; the last block of a sequence may be partial
+// (READING A3: a block never straddles two sequences, because the scale tensors are padded per
+// sequence [AE TMEM, jagged handling]).
+int64_t blockrow_offset(const int32_t* cu, int s) {
+  int64_t off = 0;
+  for (int r = 0; r < s; ++r) off += (cu[r + 1] - cu[r] + 31) / 32;
+  return off;
+}
+
+int64_t padded_offset(const int32_t* cu, int s) {
+  int64_t off = 0;
+  for (int r = 0; r < s; ++r) off += (int64_t)(cu[r + 1] - cu[r] + 127) / 128 * 128;
+  return off;
+}
+
+// Quantize one block given the element values and their output positions.
+void quantize_block(const std::vector<double>& vals, const std::vector<int64_t>& pos, uint8_t* data,
+                    uint8_t* scale_byte) {
+  double amax = 0.0;
+  bool nonfinite = false;
+  for (double x : vals) {
+    if (!std::isfinite(x)) nonfinite = true;
+    else amax = std::max(amax, std::fabs(x));
+  }
+  int code = nonfinite ? 255 : e8m0_code(amax);
+  *scale_byte = (uint8_t)code;
+  for (size_t i = 0; i < vals.size(); ++i) {
+    if (code == 255) {
+      data[pos[i]] = 0x7f;
+    } else {
+      // x * 2^(127 - code) is exact in double; the single rounding happens in the E4M3 encode.
+      data[pos[i]] = e4m3_encode(vals[i] * pow2(127 - code));
+    }
+  }
+}
+
+// MX quantization of a [T, C] matrix (row-major, values already widened to double).
+// [AE TMEM]: 32-element blocks; [TC paragraph 3]: scales along the contraction dimension;
+// [AE TMEM] / [BR item 6]: square 32 x 32 blocks for the backward operands.
+// Pinned by: SQ32(X^T) = SQ32(X)^T, ROW32(X^T) = COL32(X)^T, jagged == per-sequence dense,
+// dequantization error bounds.
+void quantize_matrix(const double* x, int64_t T, int C, const int32_t* cu, int nseq, int mode, uint8_t* data,
+                     uint8_t* scale, uint8_t* scale_t) {
+  int64_t NB = blockrow_offset(cu, nseq);
+  std::vector<double> vals;
+  std::vector<int64_t> pos;
+  if (mode == ROW32) {
+    for (int64_t t = 0; t < T; ++t)
+      for (int cb = 0; cb < C / 32; ++cb) {
+        vals.clear();
+        pos.clear();
+        for (int c = cb * 32; c < cb * 32 + 32; ++c) {
+          vals.push_back(x[t * C + c]);
+          pos.push_back(t * C + c);
+        }
+        quantize_block(vals, pos, data, &scale[t * (C / 32) + cb]);
+      }
+    return;
+  }
+  for (int s = 0; s < nseq; ++s) {
+    int64_t t0 = cu[s], L = cu[s + 1] - cu[s];
+    int64_t br0 = blockrow_offset(cu, s);
+    for (int64_t b = 0; b * 32 < L; ++b) {
+      int64_t ta = t0 + b * 32, tb = std::min<int64_t>(t0 + L, ta + 32);
+      if (mode == COL32) {
+        for (int c = 0; c < C; ++c) {
+          vals.clear();
+          pos.clear();
+          for (int64_t t = ta; t < tb; ++t) {
+            vals.push_back(x[t * C + c]);
+            pos.push_back(t * C + c);
+          }
+          quantize_block(vals, pos, data, &scale[(br0 + b) * C + c]);
+        }
+      } else {
+        for (int cb = 0; cb < C / 32; ++cb) {
+          vals.clear();
+          pos.clear();
+          for (int64_t t = ta; t < tb; ++t)
+            for (int c = cb * 32; c < cb * 32 + 32; ++c) {
+              vals.push_back(x[t * C + c]);
+              pos.push_back(t * C + c);
+            }
+          uint8_t* sb = &scale[(br0 + b) * (C / 32) + cb];
+          quantize_block(vals, pos, data, sb);
+          if (scale_t) scale_t[(int64_t)cb * NB + br0 + b] = *sb;
+        }
+      }
+    }
+  }
+}
+
+// Dequantization: element (t, c) times the scale that covers it, compact layouts:
+//   ROW32: [T][C/32]      (1 x 32 along the columns)
+//   COL32: [NB][C]        (32 x 1 along the tokens)
+//   SQ32 : [NB][C/32]     (32 x 32)
+// with NB = sum over sequences of ceil(L/32) and block row = offset(sequence) + (t - start) / 32.
+void dequantize_matrix(const uint8_t* data, const uint8_t* scale, int64_t T, int C, const int32_t* cu, int nseq,
+                       int mode, double* out) {
+  for (int s = 0; s < nseq; ++s) {
+    int64_t br0 = blockrow_offset(cu, s);
+    for (int64_t t = cu[s]; t < cu[s + 1]; ++t) {
+      int64_t br = br0 + (t - cu[s]) / 32;
+      for (int c = 0; c < C; ++c) {
+        int64_t si;
+        if (mode == ROW32) si = t * (C / 32) + c / 32;
+        else if (mode == COL32) si = br * C + c;
+        else si = br * (C / 32) + c / 32;
+        out[t * C + c] = e4m3_decode(data[t * C + c]) * e8m0_value(scale[si]);
+      }
+    }
+  }
+  (void)T;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Work distribution: independent (sequence, head) units over std::thread. Each unit's arithmetic
+// order is fixed, so results do not depend on the thread count.
+// ---------------------------------------------------------------------------------------------
+
+template <class F>
+void parallel_units(int n_units, int nthreads, F f) {
+  if (nthreads <= 1 || n_units <= 1) {
+    for (int u = 0; u < n_units; ++u) f(u);
+    return;
+  }
+  std::atomic<int> next(0);
+  std::vector<std::thread> pool;
+  for (int t = 0; t < nthreads; ++t)
+    pool.emplace_back([&]() {
+      for (int u = next++; u < n_units; u = next++) f(u);
+    });
+  for (auto& th : pool) th.join();
+}
+
+const int TILE = 128;  // Q and KV tile rows [TC paragraph 2: [128, 128] tiles, K/V tiles along N]
+
+// ---------------------------------------------------------------------------------------------
+// Attention forward
+// ---------------------------------------------------------------------------------------------
+//
+// Per (sequence, head), per 128-row Q tile, KV tiles of 128 rows in ascending order:
+//   S  = Q K^T, accumulated exactly and rounded to fp32 (the MMA accumulates in FP32).
+//   online softmax in FP32 [TC paragraph 1: softmax runs in FP32, then P is converted]:
+//     m' = max(m, rowmax S);  alpha = exp(c (m - m'));  P = exp(c (S - m'));  l = alpha l + rowsum P
+//   P is quantized to E4M3 with the static scale 2^-8 (E8M0 code 119) on every 32-block: P <= 1
+//     because the row max m' is the reference point [BR item 4: constant scale, P in [0,1];
+//     AE TMEM: the softmax row max is reused, so no extra max pass] (READING A5).
+//   O  = alpha O + deq(P_q) V, rounded to fp32 per tile.
+//   At the end: O_out = bf16(fl32(O / l)), LSE = fl32(c m + ln l).
+// quant_p = 0 skips the P quantization (pinning mode).
+// Pinned by: FP64 brute-force softmax attention (no-quant mode), one-tile == many tiles,
+// closed forms (K = 0, causal row 0, one-hot scores), the quantization error bound.
+void attn_fwd_unit(const double* q, const double* k, const double* v, int64_t q0, int64_t Lq, int64_t k0,
+                   int64_t Lk, int H, int D, int h, double c, int causal, int quant_p, int kv_tile,
+                   uint16_t* o_bf16, float* o_f32, float* lse, int64_t lse_stride) {
+  const int64_t C = (int64_t)H * D;
+  std::vector<double> S(TILE * (size_t)kv_tile), O((size_t)TILE * D);
+  std::vector<double> m(TILE), l(TILE);
+  for (int64_t qt = 0; qt < Lq; qt += TILE) {
+    int64_t nq = std::min<int64_t>(TILE, Lq - qt);
+    for (int64_t i = 0; i < nq; ++i) {
+      m[i] = -std::numeric_limits<double>::infinity();
+      l[i] = 0.0;
+      for (int d = 0; d < D; ++d) O[i * D + d] = 0.0;
+    }
+    for (int64_t kt = 0; kt < Lk; kt += kv_tile) {
+      int64_t nk = std::min<int64_t>(kv_tile, Lk - kt);
+      if (causal && kt > qt + nq - 1) break;  // every key of this and later tiles is masked
+      for (int64_t i = 0; i < nq; ++i) {
+        const double* qi = q + (q0 + qt + i) * C + (int64_t)h * D;
+        int64_t gi = qt + i;  // position in the sequence
+        // scores for this row
+        double rowmax = -std::numeric_limits<double>::infinity();
+        for (int64_t j = 0; j < nk; ++j) {
+          int64_t gj = kt + j;
+          if (causal && gj > gi) {
+            S[i * kv_tile + j] = -std::numeric_limits<double>::infinity();
+            continue;
+          }
+          const double* kj = k + (k0 + gj) * C + (int64_t)h * D;
+          double acc = 0.0;
+          for (int d = 0; d < D; ++d) acc += qi[d] * kj[d];
+          S[i * kv_tile + j] = fl32(acc);
+          rowmax = std::max(rowmax, S[i * kv_tile + j]);
+        }
+        double mnew = std::max(m[i], rowmax);
+        if (mnew == -std::numeric_limits<double>::infinity()) continue;  // no key seen yet
+        double alpha = (m[i] == -std::numeric_limits<double>::infinity()) ? 0.0 : fl32(std::exp(c * (m[i] - mnew)));
+        double psum = 0.0;
+        std::vector<double> pv(D, 0.0);
+        for (int64_t j = 0; j < nk; ++j) {
+          double s = S[i * kv_tile + j];
+          if (s == -std::numeric_limits<double>::infinity()) continue;
+          double p = fl32(std::exp(c * (s - mnew)));
+          psum += p;
+          double pd = p;
+          if (quant_p) pd = e4m3_decode(e4m3_encode(p * 256.0)) * e8m0_value(119);
+          const double* vj = v + (k0 + kt + j) * C + (int64_t)h * D;
+          for (int d = 0; d < D; ++d) pv[d] += pd * vj[d];
+        }
+        l[i] = fl32(alpha * l[i] + psum);
+        for (int d = 0; d < D; ++d) O[i * D + d] = fl32(alpha * O[i * D + d] + pv[d]);
+        m[i] = mnew;
+      }
+    }
+    for (int64_t i = 0; i < nq; ++i) {
+      int64_t row = q0 + qt + i;
+      for (int d = 0; d < D; ++d) {
+        double o = (l[i] > 0.0) ? fl32(O[i * D + d] / l[i]) : 0.0;
+        if (o_f32) o_f32[row * C + (int64_t)h * D + d] = (float)o;
+        if (o_bf16) o_bf16[row * C + (int64_t)h * D + d] = bf16_round((float)o);
+      }
+      double L = (l[i] > 0.0) ? fl32(c * m[i] + std::log(l[i])) : -std::numeric_limits<double>::infinity();
+      if (lse) lse[(int64_t)h * lse_stride + row] = (float)L;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Attention backward
+// ---------------------------------------------------------------------------------------------
+//
+// Recomputation with five GEMMs [AE TMEM: backward requires five GEMMs; KC "Hardware Adaptation
+// for Blackwell": recompute instead of storing P]. Per (sequence, head), KV tiles outer, Q tiles
+// inner in ascending order:
+//   S   = Q K^T (fp32)                                         GEMM 1
+//   P   = exp(c S - LSE) (fp32); masked entries 0
+//   P_q = E4M3(P 2^8), static code 119 [BR item 4]
+//   dV += deq(P_q)^T deq(dO_q)                                 GEMM 2
+//   dP  = deq(dO_q) deq(V)^T (fp32)                            GEMM 3
+//   dS  = P (dP - Delta) (fp32),  Delta_i = sum_d dO_id O_id   (READING A8)
+//   dS_q: 32 x 32 square blocks of the tile, dynamic E8M0 scale from the block's absolute
+//         maximum [AE TMEM: dS quantized once per square block with a warp-wide abs-max]
+//   dK += deq(dS_q)^T deq(Q_q)                                 GEMM 4
+//   dQ_t = deq(dS_q) deq(K_q), added to the dQ accumulator     GEMM 5
+//     FP32 mode: acc = fl32(acc + fl32(dQ_t))
+//     FP16 mode: acc = fp16(acc + fp16(sigma dQ_t))  [AE TMEM: FP16 dQ with a static scale]
+// Outputs: dQ = bf16(c acc / sigma), dK = bf16(c dK), dV = bf16(dV).
+// quant = 0 skips the P and dS quantization (pinning mode).
+// Pinned by: FP64 central finite differences of the no-quant mode on tiny inputs; FP16 vs FP32
+// accumulator bound.
+struct BwdArgs {
+  const double *q, *k, *v, *dO_mm, *o_delta, *do_delta;
+  const float* lse;
+  int64_t lse_stride;
+  int H, D;
+  double c;
+  int causal, quant, dq_mode;
+  double sigma;
+  double* dq_acc;    // [Tq, C]: fp32-valued (FP32 mode) or fp16-valued (FP16 mode)
+  double *dk, *dv;   // [Tk, C] fp32-valued accumulators
+  std::atomic<int>* overflow;
+};
+
+void attn_bwd_unit(const BwdArgs& a, int64_t q0, int64_t Lq, int64_t k0, int64_t Lk, int h) {
+  const int D = a.D;
+  const int64_t C = (int64_t)a.H * D;
+  const double c = a.c;
+  // Delta for every query row of this (sequence, head)
+  std::vector<double> delta(Lq);
+  for (int64_t i = 0; i < Lq; ++i) {
+    double s = 0.0;
+    for (int d = 0; d < D; ++d)
+      s += a.do_delta[(q0 + i) * C + (int64_t)h * D + d] * a.o_delta[(q0 + i) * C + (int64_t)h * D + d];
+    delta[i] = fl32(s);
+  }
+  std::vector<double> P(TILE * TILE), dS(TILE * TILE), dSq(TILE * TILE), Pq(TILE * TILE);
+  std::vector<double> dkt(TILE * (size_t)D), dvt(TILE * (size_t)D);
+  for (int64_t kt = 0; kt < Lk; kt += TILE) {
+    int64_t nk = std::min<int64_t>(TILE, Lk - kt);
+    std::fill(dkt.begin(), dkt.end(), 0.0);
+    std::fill(dvt.begin(), dvt.end(), 0.0);
+    for (int64_t qt = 0; qt < Lq; qt += TILE) {
+      int64_t nq = std::min<int64_t>(TILE, Lq - qt);
+      if (a.causal && kt > qt + nq - 1) continue;  // fully masked tile pair
+      // GEMM 1 and P
+      for (int64_t i = 0; i < nq; ++i)
+        for (int64_t j = 0; j < nk; ++j) {
+          int64_t gi = qt + i, gj = kt + j;
+          double p = 0.0;
+          if (!(a.causal && gj > gi)) {
+            const double* qi = a.q + (q0 + gi) * C + (int64_t)h * D;
+            const double* kj = a.k + (k0 + gj) * C + (int64_t)h * D;
+            double acc = 0.0;
+            for (int d = 0; d < D; ++d) acc += qi[d] * kj[d];
+            double s = fl32(acc);
+            p = fl32(std::exp(c * s - (double)a.lse[(int64_t)h * a.lse_stride + q0 + gi]));
+          }
+          P[i * TILE + j] = p;
+          Pq[i * TILE + j] = a.quant ? e4m3_decode(e4m3_encode(p * 256.0)) * e8m0_value(119) : p;
+        }
+      // GEMM 2: dV += P_q^T dO
+      for (int64_t j = 0; j < nk; ++j)
+        for (int d = 0; d < D; ++d) {
+          double acc = 0.0;
+          for (int64_t i = 0; i < nq; ++i) acc += Pq[i * TILE + j] * a.dO_mm[(q0 + qt + i) * C + (int64_t)h * D + d];
+          dvt[j * D + d] = fl32(dvt[j * D + d] + acc);
+        }
+      // GEMM 3 and dS
+      for (int64_t i = 0; i < nq; ++i)
+        for (int64_t j = 0; j < nk; ++j) {
+          const double* doi = a.dO_mm + (q0 + qt + i) * C + (int64_t)h * D;
+          const double* vj = a.v + (k0 + kt + j) * C + (int64_t)h * D;
+          double acc = 0.0;
+          for (int d = 0; d < D; ++d) acc += doi[d] * vj[d];
+          double dp = fl32(acc);
+          dS[i * TILE + j] = fl32(P[i * TILE + j] * (dp - delta[qt + i]));
+        }
+      // dS quantization in 32 x 32 blocks of the tile
+      for (int64_t bi = 0; bi < nq; bi += 32)
+        for (int64_t bj = 0; bj < nk; bj += 32) {
+          int64_t ei = std::min<int64_t>(nq, bi + 32), ej = std::min<int64_t>(nk, bj + 32);
+          if (!a.quant) {
+            for (int64_t i = bi; i < ei; ++i)
+              for (int64_t j = bj; j < ej; ++j) dSq[i * TILE + j] = dS[i * TILE + j];
+            continue;
+          }
+          double amax = 0.0;
+          bool nonfinite = false;
+          for (int64_t i = bi; i < ei; ++i)
+            for (int64_t j = bj; j < ej; ++j) {
+              double x = dS[i * TILE + j];
+              if (!std::isfinite(x)) nonfinite = true;
+              else amax = std::max(amax, std::fabs(x));
+            }
+          int code = nonfinite ? 255 : e8m0_code(amax);
+          for (int64_t i = bi; i < ei; ++i)
+            for (int64_t j = bj; j < ej; ++j) {
+              uint8_t pl = (code == 255) ? 0x7f : e4m3_encode(dS[i * TILE + j] * pow2(127 - code));
+              dSq[i * TILE + j] = e4m3_decode(pl) * e8m0_value(code);
+            }
+        }
+      // GEMM 4: dK += dS_q^T Q
+      for (int64_t j = 0; j < nk; ++j)
+        for (int d = 0; d < D; ++d) {
+          double acc = 0.0;
+          for (int64_t i = 0; i < nq; ++i) acc += dSq[i * TILE + j] * a.q[(q0 + qt + i) * C + (int64_t)h * D + d];
+          dkt[j * D + d] = fl32(dkt[j * D + d] + acc);
+        }
+      // GEMM 5: dQ_t = dS_q K, then the accumulator update
+      for (int64_t i = 0; i < nq; ++i)
+        for (int d = 0; d < D; ++d) {
+          double acc = 0.0;
+          for (int64_t j = 0; j < nk; ++j) acc += dSq[i * TILE + j] * a.k[(k0 + kt + j) * C + (int64_t)h * D + d];
+          double& cell = a.dq_acc[(q0 + qt + i) * C + (int64_t)h * D + d];
+          if (a.dq_mode == 0) {
+            cell = fl32(cell + fl32(acc));
+          } else {
+            cell = fp16_round(cell + fp16_round(a.sigma * acc));
+            if (std::isinf(cell)) a.overflow->store(1);
+          }
+        }
+    }
+    for (int64_t j = 0; j < nk; ++j)
+      for (int d = 0; d < D; ++d) {
+        a.dk[(k0 + kt + j) * C + (int64_t)h * D + d] = dkt[j * D + d];
+        a.dv[(k0 + kt + j) * C + (int64_t)h * D + d] = dvt[j * D + d];
+      }
+  }
+}
+
+}  // namespace
+
+// =============================================================================================
+// C API (ctypes). All pointers are host pointers. Returns 0 on success, -1 on a bad argument.
+// =============================================================================================
+extern "C" {
+
+double orc_e4m3_decode(uint8_t c) { return e4m3_decode(c); }
+uint8_t orc_e4m3_encode(double v) { return e4m3_encode(v); }
+int orc_e8m0_code(double amax) { return e8m0_code(amax); }
+double orc_e8m0_value(int code) { return e8m0_value(code); }
+double orc_fp16_round(double v) { return fp16_round(v); }
+uint16_t orc_f32_to_bf16(float f) { return bf16_round(f); }
+
+void orc_e4m3_encode_array(const float* x, int64_t n, uint8_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = e4m3_encode((double)x[i]);
+}
+
+int64_t orc_num_blockrows(const int32_t* cu, int nseq) { return blockrow_offset(cu, nseq); }
+int64_t orc_padded_rows(const int32_t* cu, int nseq) { return padded_offset(cu, nseq); }
+
+static bool valid_cu(const int32_t* cu, int nseq, int64_t T) {
+  if (!cu || nseq < 1 || cu[0] != 0) return false;
+  for (int s = 0; s < nseq; ++s)
+    if (cu[s + 1] < cu[s]) return false;
+  return cu[nseq] == T;
+}
+
+// x: bf16 [T, ld] (first C columns used). Outputs in the compact layout.
+int orc_quantize_bf16(const uint16_t* x, int64_t ld, int64_t T, int C, const int32_t* cu, int nseq, int mode,
+                      uint8_t* data, uint8_t* scale, uint8_t* scale_t) {
+  if (C % 32 || ld < C || mode < 0 || mode > 2 || !valid_cu(cu, nseq, T)) return -1;
+  std::vector<double> xd((size_t)T * C);
+  for (int64_t t = 0; t < T; ++t)
+    for (int c = 0; c < C; ++c) xd[t * C + c] = bf16_value(x[t * ld + c]);
+  quantize_matrix(xd.data(), T, C, cu, nseq, mode, data, scale, mode == SQ32 ? scale_t : nullptr);
+  return 0;
+}
+
+// x: fp32 [T, C] (used for quantizing values that are not bf16, e.g. in pins)
+int orc_quantize_f32(const float* x, int64_t T, int C, const int32_t* cu, int nseq, int mode, uint8_t* data,
+                     uint8_t* scale, uint8_t* scale_t) {
+  if (C % 32 || mode < 0 || mode > 2 || !valid_cu(cu, nseq, T)) return -1;
+  std::vector<double> xd((size_t)T * C);
+  for (int64_t i = 0; i < T * C; ++i) xd[i] = (double)x[i];
+  quantize_matrix(xd.data(), T, C, cu, nseq, mode, data, scale, mode == SQ32 ? scale_t : nullptr);
+  return 0;
+}
+
+int orc_dequantize(const uint8_t* data, const uint8_t* scale, int64_t T, int C, const int32_t* cu, int nseq,
+                   int mode, double* out) {
+  if (C % 32 || mode < 0 || mode > 2 || !valid_cu(cu, nseq, T)) return -1;
+  dequantize_matrix(data, scale, T, C, cu, nseq, mode, out);
+  return 0;
+}
+
+// Jagged zero-gather scale path [AE TMEM: only the scale tensors are padded and aligned, the FP8
+// data stays compact; BR item 5: scatter kernels move scale factors without changing values].
+// Moves each sequence's compact scale rows to a padded layout in which every sequence starts at a
+// row that is a multiple of 128 tokens; rows in the padding are 0x00.
+//   ROW32: compact [T][C/32] token rows       -> padded [P][C/32], P = sum round_up(L, 128)
+//   COL32: compact [NB][C] block rows          -> padded [P/32][C]
+//   SQ32 : compact [NB][C/32] block rows       -> padded [P/32][C/32]
+// padded_rows is the caller's row count of the padded tensor in the layout's own row unit.
+int orc_scale_scatter(const uint8_t* compact, const int32_t* cu, int nseq, int C, int mode, uint8_t* padded,
+                      int64_t padded_rows) {
+  if (C % 32 || mode < 0 || mode > 2 || !cu || nseq < 1) return -1;
+  int64_t P = padded_offset(cu, nseq);
+  int64_t width = (mode == COL32) ? C : C / 32;
+  int64_t need = (mode == ROW32) ? P : P / 32;
+  if (padded_rows < need) return -1;
+  std::memset(padded, 0, (size_t)(padded_rows * width));
+  for (int s = 0; s < nseq; ++s) {
+    int64_t L = cu[s + 1] - cu[s];
+    if (mode == ROW32) {
+      for (int64_t r = 0; r < L; ++r)
+        for (int64_t w = 0; w < width; ++w)
+          padded[(padded_offset(cu, s) + r) * width + w] = compact[(cu[s] + r) * width + w];
+    } else {
+      int64_t nb = (L + 31) / 32;
+      for (int64_t b = 0; b < nb; ++b)
+        for (int64_t w = 0; w < width; ++w)
+          padded[(padded_offset(cu, s) / 32 + b) * width + w] = compact[(blockrow_offset(cu, s) + b) * width + w];
+    }
+  }
+  return 0;
+}
+
+// Forward on dequantized (double) inputs q, k, v: [T, H*D] row-major.
+// o_bf16, o_f32: [Tq, H*D] (either may be NULL); lse: [H][Tq].
+int orc_attn_fwd_f64(const double* q, const double* k, const double* v, const int32_t* cu_q, const int32_t* cu_k,
+                     int nseq, int H, int D, float softmax_scale, int causal, int quant_p, int kv_tile,
+                     uint16_t* o_bf16, float* o_f32, float* lse, int nthreads) {
+  if (!cu_q || !cu_k || nseq < 1 || H < 1 || D < 1 || kv_tile < 1 || kv_tile > 4096) return -1;
+  int64_t Tq = cu_q[nseq];
+  parallel_units(nseq * H, nthreads, [&](int u) {
+    int s = u / H, h = u % H;
+    attn_fwd_unit(q, k, v, cu_q[s], cu_q[s + 1] - cu_q[s], cu_k[s], cu_k[s + 1] - cu_k[s], H, D, h,
+                  (double)softmax_scale, causal, quant_p, kv_tile, o_bf16, o_f32, lse, Tq);
+  });
+  return 0;
+}
+
+// Forward on MX inputs in the compact layout (payload [T, H*D], scales per mode).
+int orc_attn_fwd_mx(const uint8_t* q, const uint8_t* q_scale, int q_mode, const uint8_t* k, const uint8_t* k_scale,
+                    int k_mode, const uint8_t* v, const uint8_t* v_scale, int v_mode, const int32_t* cu_q,
+                    const int32_t* cu_k, int nseq, int H, int D, float softmax_scale, int causal, uint16_t* o_bf16,
+                    float* o_f32, float* lse, int nthreads) {
+  if (!cu_q || !cu_k || nseq < 1 || (H * D) % 32) return -1;
+  int64_t Tq = cu_q[nseq], Tk = cu_k[nseq];
+  int C = H * D;
+  std::vector<double> qd((size_t)Tq * C), kd((size_t)Tk * C), vd((size_t)Tk * C);
+  dequantize_matrix(q, q_scale, Tq, C, cu_q, nseq, q_mode, qd.data());
+  dequantize_matrix(k, k_scale, Tk, C, cu_k, nseq, k_mode, kd.data());
+  dequantize_matrix(v, v_scale, Tk, C, cu_k, nseq, v_mode, vd.data());
+  return orc_attn_fwd_f64(qd.data(), kd.data(), vd.data(), cu_q, cu_k, nseq, H, D, softmax_scale, causal, 1, TILE,
+                          o_bf16, o_f32, lse, nthreads);
+}
+
+// Backward on double inputs. q, k: as used in GEMMs 1, 4, 5; v: along-D V for GEMM 3;
+// dO_mm: dO as used in GEMMs 2 and 3; o_delta, do_delta: O and dO for Delta. lse: [H][Tq].
+// Outputs (each may be NULL): dq/dk/dv bf16 [T, H*D], dq_f/dk_f/dv_f fp32 [T, H*D] of the same
+// values before bf16 rounding. overflow (may be NULL) is set to 1 if an FP16 accumulator hit Inf.
+int orc_attn_bwd_f64(const double* q, const double* k, const double* v, const double* dO_mm, const double* o_delta,
+                     const double* do_delta, const float* lse, const int32_t* cu_q, const int32_t* cu_k, int nseq,
+                     int H, int D, float softmax_scale, int causal, int quant, int dq_mode, float dq_sigma,
+                     uint16_t* dq, uint16_t* dk, uint16_t* dv, float* dq_f, float* dk_f, float* dv_f, int* overflow,
+                     int nthreads) {
+  if (!cu_q || !cu_k || nseq < 1 || H < 1 || D < 1 || (dq_mode != 0 && dq_mode != 1)) return -1;
+  if (dq_mode == 1 && !(dq_sigma > 0.0f)) return -1;
+  int64_t Tq = cu_q[nseq], Tk = cu_k[nseq];
+  int64_t C = (int64_t)H * D;
+  std::vector<double> acc((size_t)(Tq * C), 0.0), dka((size_t)(Tk * C), 0.0), dva((size_t)(Tk * C), 0.0);
+  std::atomic<int> ovf(0);
+  BwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.dO_mm = dO_mm; a.o_delta = o_delta; a.do_delta = do_delta;
+  a.lse = lse; a.lse_stride = Tq; a.H = H; a.D = D; a.c = (double)softmax_scale;
+  a.causal = causal; a.quant = quant; a.dq_mode = dq_mode; a.sigma = (double)dq_sigma;
+  a.dq_acc = acc.data(); a.dk = dka.data(); a.dv = dva.data(); a.overflow = &ovf;
+  parallel_units(nseq * H, nthreads, [&](int u) {
+    int s = u / H, h = u % H;
+    attn_bwd_unit(a, cu_q[s], cu_q[s + 1] - cu_q[s], cu_k[s], cu_k[s + 1] - cu_k[s], h);
+  });
+  double sig = (dq_mode == 1) ? (double)dq_sigma : 1.0;
+  for (int64_t i = 0; i < Tq * C; ++i) {
+    float x = (float)fl32(a.c * acc[i] / sig);
+    if (dq_f) dq_f[i] = x;
+    if (dq) dq[i] = bf16_round(x);
+  }
+  for (int64_t i = 0; i < Tk * C; ++i) {
+    float xk = (float)fl32(a.c * dka[i]);
+    float xv = (float)dva[i];
+    if (dk_f) dk_f[i] = xk;
+    if (dk) dk[i] = bf16_round(xk);
+    if (dv_f) dv_f[i] = xv;
+    if (dv) dv[i] = bf16_round(xv);
+  }
+  if (overflow) *overflow = ovf.load();
+  return 0;
+}
+
+// Backward on MX inputs (compact layouts). Q, K, dO are SQ32 (one payload serves the transposed and
+// the plain GEMM [AE TMEM: square 32 x 32 blocks]); v_d is V quantized along D (ROW32 or SQ32);
+// o, do_ are the bf16 O and dO used for Delta.
+int orc_attn_bwd_mx(const uint8_t* q, const uint8_t* q_scale, const uint8_t* k, const uint8_t* k_scale,
+                    const uint8_t* v, const uint8_t* v_scale, int v_mode, const uint8_t* dO, const uint8_t* dO_scale,
+                    const uint16_t* o_bf16, const uint16_t* do_bf16, const float* lse, const int32_t* cu_q,
+                    const int32_t* cu_k, int nseq, int H, int D, float softmax_scale, int causal, int dq_mode,
+                    float dq_sigma, uint16_t* dq, uint16_t* dk, uint16_t* dv, float* dq_f, float* dk_f, float* dv_f,
+                    int* overflow, int nthreads) {
+  if (!cu_q || !cu_k || nseq < 1 || (H * D) % 32) return -1;
+  int64_t Tq = cu_q[nseq], Tk = cu_k[nseq];
+  int C = H * D;
+  std::vector<double> qd((size_t)Tq * C), kd((size_t)Tk * C), vd((size_t)Tk * C), dod((size_t)Tq * C);
+  std::vector<double> od((size_t)Tq * C), dobf((size_t)Tq * C);
+  dequantize_matrix(q, q_scale, Tq, C, cu_q, nseq, SQ32, qd.data());
+  dequantize_matrix(k, k_scale, Tk, C, cu_k, nseq, SQ32, kd.data());
+  dequantize_matrix(v, v_scale, Tk, C, cu_k, nseq, v_mode, vd.data());
+  dequantize_matrix(dO, dO_scale, Tq, C, cu_q, nseq, SQ32, dod.data());
+  for (int64_t i = 0; i < Tq * C; ++i) {
+    od[i] = bf16_value(o_bf16[i]);
+    dobf[i] = bf16_value(do_bf16[i]);
+  }
+  return orc_attn_bwd_f64(qd.data(), kd.data(), vd.data(), dod.data(), od.data(), dobf.data(), lse, cu_q, cu_k, nseq,
+                          H, D, softmax_scale, causal, 1, dq_mode, dq_sigma, dq, dk, dv, dq_f, dk_f, dv_f, overflow,
+                          nthreads);
+}
+
+// Fused RMSNorm + quantize producer [AE TMEM: quantization fused into RMSNorm; BR item 7: FP8
+// output with dual scale layouts in one pass]. READING A11:
+//   ss = fl32(sum_c x^2) (exact sum, one rounding), r = 1 / sqrtf(ss / C + eps) in fp32 with IEEE
+//   division and square root, y = fl32(fl32(x r) gamma); then SQ32 quantization of y with token
+//   blocks aligned to sequence starts; scale written in [NB][C/32] and transposed [C/32][NB].
+// y_out (may be NULL) receives y.
+// Pinned by: mean(y^2) = 1/(1 + eps/mean(x^2)) for gamma = 1; constant rows.
+int orc_rmsnorm_quantize(const uint16_t* x, int64_t ld, int64_t T, int C, const float* gamma, float eps,
+                         const int32_t* cu, int nseq, uint8_t* data, uint8_t* scale, uint8_t* scale_t, float* y_out) {
+  if (C % 32 || ld < C || !gamma || !valid_cu(cu, nseq, T)) return -1;
+  std::vector<double> y((size_t)T * C);
+  for (int64_t t = 0; t < T; ++t) {
+    double ss = 0.0;
+    for (int c = 0; c < C; ++c) {
+      double xv = bf16_value(x[t * ld + c]);
+      ss += xv * xv;
+    }
+    float ss32 = (float)ss;
+    float ms = ss32 / (float)C;
+    float den = std::sqrt(ms + eps);
+    float r = 1.0f / den;
+    for (int c = 0; c < C; ++c) {
+      float xr = (float)bf16_value(x[t * ld + c]) * r;
+      float yv = xr * gamma[c];
+      y[t * C + c] = (double)yv;
+      if (y_out) y_out[t * C + c] = yv;
+    }
+  }
+  quantize_matrix(y.data(), T, C, cu, nseq, SQ32, data, scale, scale_t);
+  return 0;
+}
+
+}  // extern "C"
