@@ -1,0 +1,183 @@
+"""Benchmark of the MXFP8 attention training hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input at the B=4, H=16,
+N=4096, D=128 shape (non-causal, inputs ~ N(0,1) bf16, already resident in HBM):
+  quantize Q, K (32x32 square blocks), V (32x1 along keys for the forward, 1x32 along D for the
+  backward) and dO (square blocks)  ->  attention forward  ->  attention backward (FP16 dQ with a
+  static scale of 1).
+value = attention FLOPs of the step (forward 4 N^2 D per head, backward 2.5x forward) / step time,
+in PF/s. The forward and backward calls are also timed on their own (HIP events on the stream the
+kernels run on), which gives the per-call PF/s and the fraction of the MI355X dense MXFP8 MFMA
+peak (5.03 PF/s = 256 CU x 4 SIMD x 2048 FLOP/clk x 2.4 GHz).
+
+cpu_baseline: the CPU oracle, as it is, on a bounded sample of the same workload (batch element 0,
+all 16 heads, N = 4096, forward + backward) on this host's cores.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_MXFP8 = 5.03e15  # FLOP/s
+PEAK_HBM = 8.0e12     # B/s
+B, H, N, D = 4, 16, 4096, 128
+SEED = 2
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--dq-mode", type=int, default=1, help="0 = FP32 dQ, 1 = FP16 static-scale dQ")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def make_inputs(torch, synth):
+    T, C = B * N, H * D
+    cu = synth.cu_seqlens([N] * B)
+    host = {n: synth.normal_bf16(SEED, s, (T, C)) for n, s in
+            (("q", synth.STREAM_Q), ("k", synth.STREAM_K), ("v", synth.STREAM_V), ("do", synth.STREAM_DO))}
+    dev = {n: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda() for n, a in host.items()}
+    cu_d = torch.from_numpy(cu).cuda()
+    return host, dev, cu, cu_d
+
+
+def cpu_baseline(host, cu):
+    import oracle
+    nthreads = max(1, min(16, os.cpu_count() or 1))
+    # sample: sequence 0 (N tokens), all heads, forward + backward (FP32 dQ), training modes
+    xs = {n: np.ascontiguousarray(a[:N]) for n, a in host.items()}
+    cu0 = np.array([0, N], np.int32)
+    c = float(np.float32(1 / math.sqrt(D)))
+    t0 = time.perf_counter()
+    q = oracle.quantize(xs["q"], cu0, oracle.SQ32)
+    k = oracle.quantize(xs["k"], cu0, oracle.SQ32)
+    v = oracle.quantize(xs["v"], cu0, oracle.COL32)
+    vd = oracle.quantize(xs["v"], cu0, oracle.ROW32)
+    do = oracle.quantize(xs["do"], cu0, oracle.SQ32)
+    o16, _, lse = oracle.attn_fwd_mx(q[0], q[1], 2, k[0], k[1], 2, v[0], v[1], 1, cu0, cu0, H, D, c, False,
+                                     nthreads=nthreads)
+    oracle.attn_bwd_mx(q[0], q[1], k[0], k[1], vd[0], vd[1], 0, do[0], do[1], o16, xs["do"], lse, cu0, cu0, H, D, c,
+                       False, 0, 1.0, nthreads=nthreads)
+    dt = time.perf_counter() - t0
+    flops = 3.5 * 4.0 * N * N * D * H
+    return {"value": flops / dt / 1e15, "unit": "PF/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"batch element 0 of the step: {H} heads x N={N}, quantize + forward + backward (FP32 dQ), "
+                      f"{dt:.1f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); the per-GPU shard is the "
+              "single-GPU kernel at its real shape, see DESIGN.md for how the path would shard", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import precision_mxfp8_block_amd as mx
+    import synth
+
+    torch.cuda.set_device(0)
+    host, dev, cu, cu_d = make_inputs(torch, synth)
+    T, C = B * N, H * D
+    c = float(np.float32(1 / math.sqrt(D)))
+    stream = torch.cuda.current_stream()
+    nb = T // 32
+
+    # outputs and workspace allocated once (the library never allocates)
+    def u8(*shape):
+        return torch.empty(shape, dtype=torch.uint8, device="cuda")
+    qd, kd, vd_, vrd, dod = u8(T, C), u8(T, C), u8(T, C), u8(T, C), u8(T, C)
+    qs, ks, dos = u8(nb, C // 32), u8(nb, C // 32), u8(nb, C // 32)
+    vs, vrs = u8(nb, C), u8(T, C // 32)
+    o = torch.empty((T, C), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((H, T), dtype=torch.float32, device="cuda")
+    dq = torch.empty((T, C), dtype=torch.bfloat16, device="cuda")
+    dk = torch.empty_like(dq)
+    dv = torch.empty_like(dq)
+    ws_bytes = mx.mxfa_bwd_workspace_size(T, H, D, args.dq_mode)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    attn = mx.AttnArgs(mx.MxOperand(qd, qs, mx.SQ32), mx.MxOperand(kd, ks, mx.SQ32), mx.MxOperand(vd_, vs, mx.COL32),
+                       cu_d, cu_d, B, N, N, T, T, H, D, c, False)
+    vop, doop = mx.MxOperand(vrd, vrs, mx.ROW32), mx.MxOperand(dod, dos, mx.SQ32)
+
+    names = ("quant", "fwd", "bwd")
+    ev = {n: [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)] for n in names}
+
+    def step(i):
+        record = i is not None
+        if record:
+            ev["quant"][i][0].record(stream)
+        mx.mxfa_quantize(dev["q"], C, T, C, cu_d, B, N, mx.SQ32, qd, qs, None, stream)
+        mx.mxfa_quantize(dev["k"], C, T, C, cu_d, B, N, mx.SQ32, kd, ks, None, stream)
+        mx.mxfa_quantize(dev["v"], C, T, C, cu_d, B, N, mx.COL32, vd_, vs, None, stream)
+        mx.mxfa_quantize(dev["v"], C, T, C, cu_d, B, N, mx.ROW32, vrd, vrs, None, stream)
+        mx.mxfa_quantize(dev["do"], C, T, C, cu_d, B, N, mx.SQ32, dod, dos, None, stream)
+        if record:
+            ev["quant"][i][1].record(stream)
+            ev["fwd"][i][0].record(stream)
+        mx.mxfa_fwd(attn, o, lse, stream)
+        if record:
+            ev["fwd"][i][1].record(stream)
+            ev["bwd"][i][0].record(stream)
+        mx.mxfa_bwd(attn, vop, doop, o, dev["do"], lse, args.dq_mode, 1.0, ws, ws_bytes, dq, dk, dv, stream)
+        if record:
+            ev["bwd"][i][1].record(stream)
+
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    print(f"# warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    print(f"# timed {args.steps} steps in {wall:.3f} s", file=sys.stderr, flush=True)
+
+    times = {n: [e[0].elapsed_time(e[1]) * 1e-3 for e in ev[n]] for n in names}
+    med = {n: float(np.median(v)) for n, v in times.items()}
+    f_fwd = 4.0 * N * N * D * B * H
+    f_bwd = 2.5 * f_fwd
+    step_s = wall / args.steps
+    value = (f_fwd + f_bwd) / step_s / 1e15
+    quant_bytes = 5 * T * C * (2 + 1) + 3 * T * C / 1024 + T * C / 32 * 2  # bf16 in, e4m3 out, scales
+    fwd_pf, bwd_pf = f_fwd / med["fwd"] / 1e15, f_bwd / med["bwd"] / 1e15
+    dominant = "bwd" if med["bwd"] >= med["fwd"] else "fwd"
+    flops_dom = f_bwd if dominant == "bwd" else f_fwd
+    roof = {"bound": "mfma", "achieved": flops_dom / med[dominant] / 1e12, "peak": PEAK_MXFP8 / 1e12,
+            "unit": "TFLOP/s", "frac": flops_dom / med[dominant] / PEAK_MXFP8, "traffic": None,
+            "kernel": "mxfa_bwd (dK/dV main kernel + Delta preprocess + dQ finalize)" if dominant == "bwd"
+            else "attn_fwd_kernel"}
+    out = {
+        "metric": "MXFP8 attention fwd/bwd PF/s and % of MI355X dense MXFP8 MFMA peak",
+        "value": round(value, 4), "unit": "PF/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "mxfp8_e4m3 (fp32 accumulate)", "data": "synthetic",
+        "config": {"workload": "MXFP8 attention training step (quantize + fwd + bwd), non-causal",
+                   "B": B, "H": H, "N": N, "D": D, "dq_mode": "fp16_static" if args.dq_mode else "fp32",
+                   "dq_static_scale": 1.0},
+        "fwd_pflops": round(fwd_pf, 4), "fwd_frac_peak": round(fwd_pf * 1e15 / PEAK_MXFP8, 4),
+        "bwd_pflops": round(bwd_pf, 4), "bwd_frac_peak": round(bwd_pf * 1e15 / PEAK_MXFP8, 4),
+        "fwd_us": round(med["fwd"] * 1e6, 2), "bwd_us": round(med["bwd"] * 1e6, 2),
+        "quant_us": round(med["quant"] * 1e6, 2),
+        "quant_gbps": round(quant_bytes / med["quant"] / 1e9, 1),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        print("# cpu baseline (oracle) ...", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(host, cu)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

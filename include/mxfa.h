@@ -1,0 +1,178 @@
+/*
+ * mxfa.h -- C ABI of the MXFP8 block-scaled attention library for AMD MI355X (gfx950).
+ *
+ * The operations follow four web pages about MXFP8 FlashAttention-4 (cited by short name):
+ *   [AE] andresseo.expert, "MXFP8 FlashAttention-4 Hits 2.85 Petaflops in Meta's Production
+ *        Training", section "Inside the TMEM Bargain and Zero-Gather Jagged Pipeline" (AE-TMEM).
+ *   [BR] brifing.si, "Meta's FlashAttention-4 Achieves 2.85 PF/s with MXFP8 on Blackwell GPUs",
+ *        numbered items.
+ *   [TC] theclarity.today, "Meta's MXFP8 FlashAttention-4 kernel, tackling TMEM scale-factor
+ *        constraints, hits up to 1.6x over BF16", paragraphs 1-4.
+ *   [KC] kongchang.com, "Low-Precision FlashAttention-4: End-to-End Block-Scaled Attention on
+ *        Blackwell", section "Why MXFP8".
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every pointer is a DEVICE pointer unless marked (host). Pointers must be 16-byte aligned;
+ *    row strides (ld_x) must be multiples of 8 elements.
+ *  - The caller owns every buffer (inputs, outputs, workspace). The library never allocates,
+ *    frees or synchronizes; it keeps no state between calls and may be called from any thread.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the default stream).
+ *  - All argument checks run on the host before anything is enqueued: a call that returns an
+ *    error has enqueued nothing and written nothing. The thread-local message of the last error
+ *    is available from mxfa_last_error_message().
+ *  - Device-resident cu_seqlens arrays (int32, nseq + 1 entries, cu[0] = 0, non-decreasing,
+ *    cu[nseq] = total tokens, every length <= the host max_seqlen) are a precondition that the
+ *    host cannot check without a synchronization; violating it is undefined behaviour.
+ *
+ * MX data (MXFP8, OCP microscaling [KC]): an E4M3 payload byte per element and one E8M0 scale
+ * byte (value 2^(e-127), 255 = NaN) per block of 32 elements. A matrix X is [T, C] row-major
+ * (T tokens of a jagged batch, C = heads * head_dim columns); token blocks start at each
+ * sequence start, the last block of a sequence may be partial. Block shapes:
+ *   MXFA_ROW32: 1 x 32 along the columns       scales [T][C/32]
+ *   MXFA_COL32: 32 x 1 along the tokens        scales [NB][C]
+ *   MXFA_SQ32 : 32 x 32 square blocks          scales [NB][C/32] (+ optional transpose [C/32][NB])
+ * with NB = sum over sequences of ceil(L/32) ("compact" layout, written by the quantizer).
+ * The attention entry points read scales in the "padded" layout written by
+ * mxfa_varlen_scale_scatter: sequence s starts at token row P_s = sum_{r<s} round_up(L_r, 128)
+ * (block row P_s/32), rows in the padding are 0x00 [AE-TMEM: only the scale tensors are padded
+ * and aligned, the FP8 data stays compact]. When every length is a multiple of 128 the two
+ * layouts coincide and no scatter is needed.
+ */
+#ifndef MXFA_H
+#define MXFA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MXFA_OK = 0,
+  MXFA_ERR_INVALID = 1,     /* bad pointer, size, alignment, enum or workspace */
+  MXFA_ERR_UNSUPPORTED = 2, /* valid but not implemented (e.g. head_dim != 128) */
+  MXFA_ERR_HIP = 3          /* a HIP launch failed; see mxfa_last_error_message() */
+} mxfa_status;
+
+typedef enum { MXFA_ROW32 = 0, MXFA_COL32 = 1, MXFA_SQ32 = 2 } mxfa_block;
+
+typedef enum {
+  MXFA_DQ_FP32 = 0,        /* dQ partials added atomically in FP32 [AE, Bench: FP32 dQ] */
+  MXFA_DQ_FP16_STATIC = 1  /* dQ partials times a static power-of-two scale sigma, added
+                              atomically in FP16 [AE-TMEM: dQ reduction in FP16 with static
+                              scaling; BR item 6] */
+} mxfa_dq_mode;
+
+/* One MX operand: payload [T, C] (row stride C bytes) and its scale tensor in `mode`'s layout. */
+typedef struct {
+  const uint8_t* data;
+  const uint8_t* scale;
+  mxfa_block mode;
+} mxfa_mx;
+
+/* Attention problem shared by the forward and the backward.
+ * q: [T_q, H*D]; k, v: [T_k, H*D]; scales in the PADDED layout.
+ * Allowed modes (scales along the MMA contraction dimension [TC paragraph 3]):
+ *   q, k : ROW32 (along D) or SQ32 (square; one payload serves both GEMM directions [AE-TMEM])
+ *   v    : COL32 (along the keys, for O = P V) or SQ32.
+ * Causal masking is top-left aligned (key j visible to query i iff j <= i, positions counted
+ * from each sequence start). head_dim must be 128. */
+typedef struct {
+  mxfa_mx q, k, v;
+  const int32_t* cu_seqlens_q; /* device, nseq + 1 */
+  const int32_t* cu_seqlens_k; /* device, nseq + 1 */
+  int nseq;
+  int max_seqlen_q;  /* (host) max length over sequences */
+  int max_seqlen_k;  /* (host) */
+  int64_t total_q;   /* (host) T_q = cu_seqlens_q[nseq] */
+  int64_t total_k;   /* (host) T_k = cu_seqlens_k[nseq] */
+  int num_heads;
+  int head_dim;
+  float softmax_scale; /* c in softmax(c Q K^T) */
+  int causal;
+} mxfa_attn_args;
+
+/* MX quantization of a bf16 matrix [AE-TMEM: 32-element blocks, the scale from bit extraction
+ * instead of logarithms or division; BR item 6: square 32x32 blocks].
+ * Per block: amax = max |x|; scale code e = clamp(exponent_field(amax) - 8, 0, 254), 255 if the
+ * block holds NaN or Inf; payload = E4M3(x * 2^(127-e)) with round-to-nearest-even and saturation
+ * to +-448 (NaN blocks: every payload byte 0x7F).
+ *   x          : bf16 bits [T, ld_x] (first C columns used)
+ *   C          : columns, multiple of 32
+ *   cu_seqlens : sequence boundaries (device). ROW32 does not use it (may be NULL).
+ *   nseq, max_seqlen : (host) sequence count and maximum length (COL32 / SQ32)
+ *   data_out   : [T, C] payload; scale_out: compact scales (see above)
+ *   scale_t_out: SQ32 only, nullable: the same scales transposed, [C/32][NB] ("dual scale
+ *                layouts" [BR item 7]); must be NULL for other modes. */
+mxfa_status mxfa_quantize(const uint16_t* x, int64_t ld_x, int64_t T, int C, const int32_t* cu_seqlens, int nseq,
+                          int max_seqlen, mxfa_block mode, uint8_t* data_out, uint8_t* scale_out,
+                          uint8_t* scale_t_out, void* stream);
+
+/* Jagged zero-gather scale path [AE-TMEM: split addressing; BR item 5: lightweight scatter that
+ * moves scale factors without changing values]. Copies compact scales (as written by
+ * mxfa_quantize) to the padded layout: sequence s starts at token row P_s (ROW32) or block row
+ * P_s/32 (COL32, SQ32), P_s = sum_{r<s} round_up(L_r, 128); rows inside each sequence's padding
+ * are written 0x00; rows at and beyond the total padded count are not written.
+ *   padded_rows: (host) rows of padded_out in the layout's row unit (token rows for ROW32, block
+ *   rows otherwise); must be >= the total padded count. */
+mxfa_status mxfa_varlen_scale_scatter(const uint8_t* compact, const int32_t* cu_seqlens, int nseq, int max_seqlen,
+                                      int C, mxfa_block mode, uint8_t* padded_out, int64_t padded_rows,
+                                      void* stream);
+
+/* Host helper: padded row count for given host-side sequence lengths (NULL-safe). */
+int64_t mxfa_padded_token_rows(const int32_t* cu_seqlens_host, int nseq);
+
+/* Attention forward [AE-TMEM: S = Q K^T, FP32 online softmax, P converted online to MXFP8, O = P V;
+ * TC paragraph 1: softmax in FP32, then P quantized with its scales in the same step; BR item 4:
+ * constant scale for P because softmax output lies in [0, 1]].
+ * Per 128-row query tile and 128-row key tiles: m' = max(m, rowmax S); P = exp(c (S - m'));
+ * l = exp(c (m - m')) l + rowsum P; P quantized to E4M3 with the static block scale 2^-8;
+ * O = exp(c (m - m')) O + deq(P) V. Outputs O / l as bf16 and LSE = c m + ln l.
+ *   o  : bf16 [T_q, H*D]
+ *   lse: fp32 [H][T_q]; rows of a sequence with no keys get O = 0 and LSE = -inf. */
+mxfa_status mxfa_fwd(const mxfa_attn_args* a, uint16_t* o, float* lse, void* stream);
+
+/* Workspace bytes mxfa_bwd needs: the dQ accumulator [T_q, H*D] (FP32 or FP16) plus
+ * Delta [H][T_q] fp32, each 256-byte aligned. */
+size_t mxfa_bwd_workspace_size(int64_t total_q, int num_heads, int head_dim, mxfa_dq_mode dq_mode);
+
+/* Attention backward with recomputation [AE-TMEM: five GEMMs; Q, K and dO in square 32x32 blocks
+ * so one E4M3 payload serves the plain and the transposed GEMM; dS quantized once per square block
+ * with a wave-wide absolute maximum; dQ reduced in FP16 with a static scale, or in FP32].
+ *   a        : the forward's problem; q and k must be SQ32, v is ignored here
+ *   v_d      : V quantized along D (ROW32 or SQ32), padded layout, for dP = dO V^T
+ *   dout     : dO quantized SQ32, padded layout
+ *   o, dout_bf16 : bf16 [T_q, H*D] forward output and incoming gradient (for Delta = rowsum(dO o O))
+ *   lse      : fp32 [H][T_q] from mxfa_fwd on the same inputs
+ *   dq_mode, dq_static_scale : accumulator type; sigma must be a positive power of two
+ *                              (FP16 holds sigma * dQ; the finalize divides by sigma)
+ *   workspace, workspace_bytes : >= mxfa_bwd_workspace_size(...), 256-byte aligned
+ *   dq, dk, dv : bf16 [T, H*D] outputs. */
+mxfa_status mxfa_bwd(const mxfa_attn_args* a, mxfa_mx v_d, mxfa_mx dout, const uint16_t* o,
+                     const uint16_t* dout_bf16, const float* lse, mxfa_dq_mode dq_mode, float dq_static_scale,
+                     void* workspace, size_t workspace_bytes, uint16_t* dq, uint16_t* dk, uint16_t* dv,
+                     void* stream);
+
+/* Fused RMSNorm + quantize producer [AE-TMEM: quantization fused into RMSNorm, no separate
+ * global-memory pass; BR item 7: FP8 output with dual scale layouts in one pass].
+ * y = fl32(fl32(x * r) * gamma[c]), r = 1 / sqrtf(ss / C + eps), ss = sum of x^2 over the row
+ * rounded once to fp32; then SQ32 quantization of y (token blocks aligned to sequence starts).
+ *   x: bf16 [T, ld_x]; gamma: fp32 [C] (device); outputs as mxfa_quantize in SQ32 mode, with
+ *   scale_t_out nullable. */
+mxfa_status mxfa_rmsnorm_quantize(const uint16_t* x, int64_t ld_x, int64_t T, int C, const float* gamma, float eps,
+                                  const int32_t* cu_seqlens, int nseq, int max_seqlen, uint8_t* data_out,
+                                  uint8_t* scale_out, uint8_t* scale_t_out, void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* mxfa_status_string(mxfa_status s);
+
+/* Thread-local message describing the last error returned on this thread ("" if none). */
+const char* mxfa_last_error_message(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXFA_H */

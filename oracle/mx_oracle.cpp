@@ -579,7 +579,8 @@ int orc_dequantize(const uint8_t* data, const uint8_t* scale, int64_t T, int C, 
 //   ROW32: compact [T][C/32] token rows       -> padded [P][C/32], P = sum round_up(L, 128)
 //   COL32: compact [NB][C] block rows          -> padded [P/32][C]
 //   SQ32 : compact [NB][C/32] block rows       -> padded [P/32][C/32]
-// padded_rows is the caller's row count of the padded tensor in the layout's own row unit.
+// padded_rows is the caller's row count of the padded tensor in the layout's own row unit; rows at
+// and beyond the total padded count are not written.
 int orc_scale_scatter(const uint8_t* compact, const int32_t* cu, int nseq, int C, int mode, uint8_t* padded,
                       int64_t padded_rows) {
   if (C % 32 || mode < 0 || mode > 2 || !cu || nseq < 1) return -1;
@@ -587,7 +588,7 @@ int orc_scale_scatter(const uint8_t* compact, const int32_t* cu, int nseq, int C
   int64_t width = (mode == COL32) ? C : C / 32;
   int64_t need = (mode == ROW32) ? P : P / 32;
   if (padded_rows < need) return -1;
-  std::memset(padded, 0, (size_t)(padded_rows * width));
+  std::memset(padded, 0, (size_t)(need * width));
   for (int s = 0; s < nseq; ++s) {
     int64_t L = cu[s + 1] - cu[s];
     if (mode == ROW32) {

@@ -1,0 +1,257 @@
+"""MXFP8 block-scaled attention for AMD MI355X (gfx950): Python binding of libmxfa.so.
+
+The functions named mxfa_* are the C ABI of include/mxfa.h, one to one: they only turn torch
+tensors (device memory) and Python numbers into pointers and integers and raise MxfaError on a
+non-OK status. Every step of the computation runs in the HIP kernels of libmxfa.so; there is no
+fallback path. The allocate-and-call helpers at the end (quantize, scale_scatter, fwd, bwd,
+rmsnorm_quantize) size the output tensors with torch and call the same entry points.
+"""
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "ROW32", "COL32", "SQ32", "DQ_FP32", "DQ_FP16_STATIC", "MxfaError",
+    "mxfa_quantize", "mxfa_varlen_scale_scatter", "mxfa_padded_token_rows", "mxfa_fwd", "mxfa_bwd",
+    "mxfa_bwd_workspace_size", "mxfa_rmsnorm_quantize", "mxfa_status_string", "mxfa_last_error_message",
+    "MxOperand", "AttnArgs", "quantize", "scale_scatter", "fwd", "bwd", "rmsnorm_quantize",
+    "library_path",
+]
+
+ROW32, COL32, SQ32 = 0, 1, 2
+DQ_FP32, DQ_FP16_STATIC = 0, 1
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmxfa.so")
+_lib = None
+
+
+class MxfaError(RuntimeError):
+    pass
+
+
+def library_path():
+    return _LIB_PATH
+
+
+class _Mx(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("scale", ctypes.c_void_p), ("mode", ctypes.c_int)]
+
+
+class _AttnArgs(ctypes.Structure):
+    _fields_ = [("q", _Mx), ("k", _Mx), ("v", _Mx),
+                ("cu_seqlens_q", ctypes.c_void_p), ("cu_seqlens_k", ctypes.c_void_p),
+                ("nseq", ctypes.c_int), ("max_seqlen_q", ctypes.c_int), ("max_seqlen_k", ctypes.c_int),
+                ("total_q", ctypes.c_int64), ("total_k", ctypes.c_int64),
+                ("num_heads", ctypes.c_int), ("head_dim", ctypes.c_int),
+                ("softmax_scale", ctypes.c_float), ("causal", ctypes.c_int)]
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing: build it with __graft_entry__.build() "
+                          "(hipcc --offload-arch=gfx950); there is no fallback implementation")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+    lib.mxfa_quantize.argtypes = [P, i64, i64, i32, P, i32, i32, i32, P, P, P, P]
+    lib.mxfa_varlen_scale_scatter.argtypes = [P, P, i32, i32, i32, i32, P, i64, P]
+    lib.mxfa_padded_token_rows.argtypes = [P, i32]
+    lib.mxfa_padded_token_rows.restype = i64
+    lib.mxfa_fwd.argtypes = [ctypes.POINTER(_AttnArgs), P, P, P]
+    lib.mxfa_bwd_workspace_size.argtypes = [i64, i32, i32, i32]
+    lib.mxfa_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.mxfa_bwd.argtypes = [ctypes.POINTER(_AttnArgs), _Mx, _Mx, P, P, P, i32, f32, P, ctypes.c_size_t, P, P, P, P]
+    lib.mxfa_rmsnorm_quantize.argtypes = [P, i64, i64, i32, P, f32, P, i32, i32, P, P, P, P]
+    lib.mxfa_status_string.argtypes = [i32]
+    lib.mxfa_status_string.restype = ctypes.c_char_p
+    lib.mxfa_last_error_message.argtypes = []
+    lib.mxfa_last_error_message.restype = ctypes.c_char_p
+    for n in ("mxfa_quantize", "mxfa_varlen_scale_scatter", "mxfa_fwd", "mxfa_bwd", "mxfa_rmsnorm_quantize"):
+        getattr(lib, n).restype = i32
+    _lib = lib
+    return lib
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status, name):
+    if status != 0:
+        lib = _load()
+        raise MxfaError(f"{name}: {lib.mxfa_status_string(status).decode()}: "
+                        f"{lib.mxfa_last_error_message().decode()}")
+
+
+# ------------------------------------------------------------------------------------------------
+# The C ABI, one function per entry point
+# ------------------------------------------------------------------------------------------------
+
+def mxfa_status_string(status):
+    return _load().mxfa_status_string(int(status)).decode()
+
+
+def mxfa_last_error_message():
+    return _load().mxfa_last_error_message().decode()
+
+
+def mxfa_quantize(x, ld_x, T, C, cu_seqlens, nseq, max_seqlen, mode, data_out, scale_out, scale_t_out=None,
+                  stream=None):
+    _check(_load().mxfa_quantize(_ptr(x), ld_x, T, C, _ptr(cu_seqlens), nseq, max_seqlen, mode, _ptr(data_out),
+                                 _ptr(scale_out), _ptr(scale_t_out), _stream(stream)), "mxfa_quantize")
+
+
+def mxfa_varlen_scale_scatter(compact, cu_seqlens, nseq, max_seqlen, C, mode, padded_out, padded_rows, stream=None):
+    _check(_load().mxfa_varlen_scale_scatter(_ptr(compact), _ptr(cu_seqlens), nseq, max_seqlen, C, mode,
+                                             _ptr(padded_out), padded_rows, _stream(stream)),
+           "mxfa_varlen_scale_scatter")
+
+
+def mxfa_padded_token_rows(cu_seqlens_host):
+    """cu_seqlens_host: a CPU int32 tensor or numpy array."""
+    import numpy as np
+    cu = np.ascontiguousarray(cu_seqlens_host.cpu().numpy() if hasattr(cu_seqlens_host, "cpu") else cu_seqlens_host,
+                              dtype=np.int32)
+    return int(_load().mxfa_padded_token_rows(cu.ctypes.data_as(ctypes.c_void_p), cu.size - 1))
+
+
+class MxOperand:
+    """Payload [T, C] uint8 tensor + scale uint8 tensor (layout per `mode`)."""
+
+    def __init__(self, data, scale, mode):
+        self.data, self.scale, self.mode = data, scale, mode
+
+    def _c(self):
+        return _Mx(_ptr(self.data), _ptr(self.scale), self.mode)
+
+
+class AttnArgs:
+    """Python mirror of mxfa_attn_args."""
+
+    def __init__(self, q, k, v, cu_seqlens_q, cu_seqlens_k, nseq, max_seqlen_q, max_seqlen_k, total_q, total_k,
+                 num_heads, head_dim, softmax_scale, causal=False):
+        self.q, self.k, self.v = q, k, v
+        self.cu_seqlens_q, self.cu_seqlens_k = cu_seqlens_q, cu_seqlens_k
+        self.nseq, self.max_seqlen_q, self.max_seqlen_k = nseq, max_seqlen_q, max_seqlen_k
+        self.total_q, self.total_k = total_q, total_k
+        self.num_heads, self.head_dim = num_heads, head_dim
+        self.softmax_scale, self.causal = softmax_scale, causal
+
+    def _c(self):
+        return _AttnArgs(self.q._c(), self.k._c(), self.v._c(), _ptr(self.cu_seqlens_q), _ptr(self.cu_seqlens_k),
+                         self.nseq, self.max_seqlen_q, self.max_seqlen_k, self.total_q, self.total_k,
+                         self.num_heads, self.head_dim, self.softmax_scale, 1 if self.causal else 0)
+
+
+def mxfa_fwd(args, o, lse, stream=None):
+    a = args._c()
+    _check(_load().mxfa_fwd(ctypes.byref(a), _ptr(o), _ptr(lse), _stream(stream)), "mxfa_fwd")
+
+
+def mxfa_bwd_workspace_size(total_q, num_heads, head_dim, dq_mode):
+    return int(_load().mxfa_bwd_workspace_size(total_q, num_heads, head_dim, dq_mode))
+
+
+def mxfa_bwd(args, v_d, dout, o, dout_bf16, lse, dq_mode, dq_static_scale, workspace, workspace_bytes, dq, dk, dv,
+             stream=None):
+    a = args._c()
+    _check(_load().mxfa_bwd(ctypes.byref(a), v_d._c(), dout._c(), _ptr(o), _ptr(dout_bf16), _ptr(lse), dq_mode,
+                            dq_static_scale, _ptr(workspace), workspace_bytes, _ptr(dq), _ptr(dk), _ptr(dv),
+                            _stream(stream)), "mxfa_bwd")
+
+
+def mxfa_rmsnorm_quantize(x, ld_x, T, C, gamma, eps, cu_seqlens, nseq, max_seqlen, data_out, scale_out,
+                          scale_t_out=None, stream=None):
+    _check(_load().mxfa_rmsnorm_quantize(_ptr(x), ld_x, T, C, _ptr(gamma), eps, _ptr(cu_seqlens), nseq, max_seqlen,
+                                         _ptr(data_out), _ptr(scale_out), _ptr(scale_t_out), _stream(stream)),
+           "mxfa_rmsnorm_quantize")
+
+
+# ------------------------------------------------------------------------------------------------
+# Allocate-and-call helpers (outputs sized with torch on x's device)
+# ------------------------------------------------------------------------------------------------
+
+def _blockrows(lens):
+    return int(sum((int(L) + 31) // 32 for L in lens))
+
+
+def _lens(cu_host):
+    cu = [int(v) for v in cu_host]
+    return [cu[i + 1] - cu[i] for i in range(len(cu) - 1)]
+
+
+def quantize(x_bf16, cu_host, cu_dev, mode, want_scale_t=False, stream=None):
+    """x_bf16: torch.bfloat16 [T, C] on the GPU. Returns (data, scale, scale_t or None), compact layout."""
+    T, C = x_bf16.shape
+    lens = _lens(cu_host)
+    dev = x_bf16.device
+    data = torch.empty((T, C), dtype=torch.uint8, device=dev)
+    nb = _blockrows(lens)
+    shape = {ROW32: (T, C // 32), COL32: (nb, C), SQ32: (nb, C // 32)}[mode]
+    scale = torch.empty(shape, dtype=torch.uint8, device=dev)
+    scale_t = torch.empty((C // 32, nb), dtype=torch.uint8, device=dev) if (want_scale_t and mode == SQ32) else None
+    mxfa_quantize(x_bf16, x_bf16.stride(0), T, C, cu_dev, len(lens), max(lens) if lens else 0, mode, data, scale,
+                  scale_t, stream)
+    return data, scale, scale_t
+
+
+def scale_scatter(compact, cu_host, cu_dev, C, mode, stream=None):
+    lens = _lens(cu_host)
+    P = sum((L + 127) // 128 * 128 for L in lens)
+    rows = P if mode == ROW32 else P // 32
+    width = C if mode == COL32 else C // 32
+    out = torch.empty((rows, width), dtype=torch.uint8, device=compact.device)
+    mxfa_varlen_scale_scatter(compact, cu_dev, len(lens), max(lens) if lens else 0, C, mode, out, rows, stream)
+    return out
+
+
+def fwd(args, stream=None):
+    """Returns (o bf16 [T_q, H*D], lse fp32 [H, T_q])."""
+    dev = args.q.data.device
+    o = torch.empty((args.total_q, args.num_heads * args.head_dim), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((args.num_heads, args.total_q), dtype=torch.float32, device=dev)
+    mxfa_fwd(args, o, lse, stream)
+    return o, lse
+
+
+def bwd(args, v_d, dout, o, dout_bf16, lse, dq_mode=DQ_FP32, dq_static_scale=1.0, workspace=None, stream=None):
+    """Returns (dq, dk, dv) bf16."""
+    dev = args.q.data.device
+    C = args.num_heads * args.head_dim
+    need = mxfa_bwd_workspace_size(args.total_q, args.num_heads, args.head_dim, dq_mode)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    dq = torch.empty((args.total_q, C), dtype=torch.bfloat16, device=dev)
+    dk = torch.empty((args.total_k, C), dtype=torch.bfloat16, device=dev)
+    dv = torch.empty((args.total_k, C), dtype=torch.bfloat16, device=dev)
+    mxfa_bwd(args, v_d, dout, o, dout_bf16, lse, dq_mode, dq_static_scale, workspace, workspace.numel(), dq, dk, dv,
+             stream)
+    return dq, dk, dv
+
+
+def rmsnorm_quantize(x_bf16, gamma, eps, cu_host, cu_dev, want_scale_t=True, stream=None):
+    T, C = x_bf16.shape
+    lens = _lens(cu_host)
+    dev = x_bf16.device
+    nb = _blockrows(lens)
+    data = torch.empty((T, C), dtype=torch.uint8, device=dev)
+    scale = torch.empty((nb, C // 32), dtype=torch.uint8, device=dev)
+    scale_t = torch.empty((C // 32, nb), dtype=torch.uint8, device=dev) if want_scale_t else None
+    mxfa_rmsnorm_quantize(x_bf16, x_bf16.stride(0), T, C, gamma, eps, cu_dev, len(lens), max(lens) if lens else 0,
+                          data, scale, scale_t, stream)
+    return data, scale, scale_t

@@ -1,0 +1,244 @@
+// C ABI of the MXFP8 attention library: argument validation (host only, before any launch) and
+// dispatch to the kernel launchers. Declarations and the contract of every entry point are in
+// include/mxfa.h.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "mxfa.h"
+#include "mxfa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+mxfa_status fail(mxfa_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+mxfa_status ok() {
+  g_last_error.clear();
+  return MXFA_OK;
+}
+
+mxfa_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(MXFA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool valid_mode(int m) { return m == MXFA_ROW32 || m == MXFA_COL32 || m == MXFA_SQ32; }
+
+bool is_pow2(float x) {
+  if (!(x > 0.0f) || !std::isfinite(x)) return false;
+  int e;
+  return std::frexp(x, &e) == 0.5f;
+}
+
+constexpr int kMaxGridY = 65535;
+
+mxfa_status check_jagged(const int32_t* cu, int nseq, int max_seqlen, int64_t T, const char* fn) {
+  if (!cu) return fail(MXFA_ERR_INVALID, "%s: cu_seqlens is NULL", fn);
+  if (!aligned(cu, 4)) return fail(MXFA_ERR_INVALID, "%s: cu_seqlens not 4-byte aligned", fn);
+  if (nseq < 1 || nseq > kMaxGridY) return fail(MXFA_ERR_INVALID, "%s: nseq=%d out of [1, %d]", fn, nseq, kMaxGridY);
+  if (max_seqlen < 0 || (int64_t)max_seqlen > T)
+    return fail(MXFA_ERR_INVALID, "%s: max_seqlen=%d not in [0, T=%lld]", fn, max_seqlen, (long long)T);
+  if ((max_seqlen + 31) / 32 > kMaxGridY) return fail(MXFA_ERR_INVALID, "%s: max_seqlen too large", fn);
+  return MXFA_OK;
+}
+
+mxfa_status check_attn(const mxfa_attn_args* a, const char* fn) {
+  if (!a) return fail(MXFA_ERR_INVALID, "%s: args is NULL", fn);
+  if (a->head_dim != 128) return fail(MXFA_ERR_UNSUPPORTED, "%s: head_dim=%d (only 128 is implemented)", fn, a->head_dim);
+  if (a->num_heads < 1) return fail(MXFA_ERR_INVALID, "%s: num_heads=%d", fn, a->num_heads);
+  if (a->nseq < 1) return fail(MXFA_ERR_INVALID, "%s: nseq=%d", fn, a->nseq);
+  if (a->total_q < 0 || a->total_k < 0) return fail(MXFA_ERR_INVALID, "%s: negative total tokens", fn);
+  if (a->max_seqlen_q < 0 || a->max_seqlen_q > a->total_q || a->max_seqlen_k < 0 || a->max_seqlen_k > a->total_k)
+    return fail(MXFA_ERR_INVALID, "%s: max_seqlen out of range", fn);
+  if (!a->cu_seqlens_q || !a->cu_seqlens_k || !aligned(a->cu_seqlens_q, 4) || !aligned(a->cu_seqlens_k, 4))
+    return fail(MXFA_ERR_INVALID, "%s: cu_seqlens NULL or misaligned", fn);
+  if (!std::isfinite(a->softmax_scale)) return fail(MXFA_ERR_INVALID, "%s: softmax_scale not finite", fn);
+  const mxfa_mx* ops[3] = {&a->q, &a->k, &a->v};
+  const char* names[3] = {"q", "k", "v"};
+  for (int i = 0; i < 3; ++i) {
+    if (!ops[i]->data || !ops[i]->scale) return fail(MXFA_ERR_INVALID, "%s: %s data/scale is NULL", fn, names[i]);
+    if (!aligned(ops[i]->data, 16) || !aligned(ops[i]->scale, 16))
+      return fail(MXFA_ERR_INVALID, "%s: %s data/scale not 16-byte aligned", fn, names[i]);
+  }
+  if (a->q.mode != MXFA_ROW32 && a->q.mode != MXFA_SQ32)
+    return fail(MXFA_ERR_INVALID, "%s: q.mode must be ROW32 or SQ32", fn);
+  if (a->k.mode != MXFA_ROW32 && a->k.mode != MXFA_SQ32)
+    return fail(MXFA_ERR_INVALID, "%s: k.mode must be ROW32 or SQ32", fn);
+  const int64_t qtiles = ((int64_t)a->max_seqlen_q + 127) / 128, ktiles = ((int64_t)a->max_seqlen_k + 127) / 128;
+  const int64_t items = (qtiles > ktiles ? qtiles : ktiles) * a->num_heads * a->nseq;
+  if (items >= (int64_t)1 << 31) return fail(MXFA_ERR_INVALID, "%s: problem too large for one launch", fn);
+  return MXFA_OK;
+}
+
+mxfa::AttnProblem to_problem(const mxfa_attn_args* a) {
+  mxfa::AttnProblem p;
+  p.q = {a->q.data, a->q.scale, (int)a->q.mode};
+  p.k = {a->k.data, a->k.scale, (int)a->k.mode};
+  p.v = {a->v.data, a->v.scale, (int)a->v.mode};
+  p.cu_q = a->cu_seqlens_q;
+  p.cu_k = a->cu_seqlens_k;
+  p.nseq = a->nseq;
+  p.max_seqlen_q = a->max_seqlen_q;
+  p.max_seqlen_k = a->max_seqlen_k;
+  p.total_q = a->total_q;
+  p.total_k = a->total_k;
+  p.H = a->num_heads;
+  p.softmax_scale = a->softmax_scale;
+  p.causal = a->causal ? 1 : 0;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mxfa_status_string(mxfa_status s) {
+  switch (s) {
+    case MXFA_OK: return "MXFA_OK";
+    case MXFA_ERR_INVALID: return "MXFA_ERR_INVALID";
+    case MXFA_ERR_UNSUPPORTED: return "MXFA_ERR_UNSUPPORTED";
+    case MXFA_ERR_HIP: return "MXFA_ERR_HIP";
+  }
+  return "MXFA_UNKNOWN_STATUS";
+}
+
+const char* mxfa_last_error_message(void) { return g_last_error.c_str(); }
+
+int64_t mxfa_padded_token_rows(const int32_t* cu_host, int nseq) {
+  if (!cu_host || nseq < 1) return 0;
+  int64_t p = 0;
+  for (int s = 0; s < nseq; ++s) p += ((int64_t)cu_host[s + 1] - cu_host[s] + 127) / 128 * 128;
+  return p;
+}
+
+mxfa_status mxfa_quantize(const uint16_t* x, int64_t ld_x, int64_t T, int C, const int32_t* cu_seqlens, int nseq,
+                          int max_seqlen, mxfa_block mode, uint8_t* data_out, uint8_t* scale_out,
+                          uint8_t* scale_t_out, void* stream) {
+  const char* fn = "mxfa_quantize";
+  if (!valid_mode(mode)) return fail(MXFA_ERR_INVALID, "%s: bad block mode %d", fn, (int)mode);
+  if (T < 0) return fail(MXFA_ERR_INVALID, "%s: T=%lld < 0", fn, (long long)T);
+  if (C <= 0 || C % 32) return fail(MXFA_ERR_INVALID, "%s: C=%d must be a positive multiple of 32", fn, C);
+  if (ld_x < C || ld_x % 8) return fail(MXFA_ERR_INVALID, "%s: ld_x=%lld must be >= C and a multiple of 8", fn, (long long)ld_x);
+  if (!x || !data_out || !scale_out) return fail(MXFA_ERR_INVALID, "%s: NULL x/data_out/scale_out", fn);
+  if (!aligned(x, 16) || !aligned(data_out, 16) || !aligned(scale_out, 16))
+    return fail(MXFA_ERR_INVALID, "%s: x/data_out/scale_out not 16-byte aligned", fn);
+  if (scale_t_out && mode != MXFA_SQ32) return fail(MXFA_ERR_INVALID, "%s: scale_t_out is for SQ32 only", fn);
+  if (scale_t_out && !aligned(scale_t_out, 16)) return fail(MXFA_ERR_INVALID, "%s: scale_t_out not aligned", fn);
+  if (mode != MXFA_ROW32) {
+    mxfa_status st = check_jagged(cu_seqlens, nseq, max_seqlen, T, fn);
+    if (st != MXFA_OK) return st;
+  }
+  if (mode == MXFA_ROW32 && T * (C / 16) / 256 >= ((int64_t)1 << 31))
+    return fail(MXFA_ERR_INVALID, "%s: tensor too large for one launch", fn);
+  return hip_status(mxfa::launch_quantize(x, ld_x, T, C, cu_seqlens, nseq, max_seqlen, (int)mode, data_out, scale_out,
+                                          scale_t_out, (hipStream_t)stream),
+                    fn);
+}
+
+mxfa_status mxfa_varlen_scale_scatter(const uint8_t* compact, const int32_t* cu_seqlens, int nseq, int max_seqlen,
+                                      int C, mxfa_block mode, uint8_t* padded_out, int64_t padded_rows,
+                                      void* stream) {
+  const char* fn = "mxfa_varlen_scale_scatter";
+  if (!valid_mode(mode)) return fail(MXFA_ERR_INVALID, "%s: bad block mode %d", fn, (int)mode);
+  if (C <= 0 || C % 32) return fail(MXFA_ERR_INVALID, "%s: C=%d must be a positive multiple of 32", fn, C);
+  if (!compact || !padded_out) return fail(MXFA_ERR_INVALID, "%s: NULL compact/padded_out", fn);
+  if (padded_rows < 0) return fail(MXFA_ERR_INVALID, "%s: padded_rows < 0", fn);
+  if (!cu_seqlens || !aligned(cu_seqlens, 4)) return fail(MXFA_ERR_INVALID, "%s: cu_seqlens NULL or misaligned", fn);
+  if (nseq < 1 || nseq > kMaxGridY) return fail(MXFA_ERR_INVALID, "%s: nseq=%d out of range", fn, nseq);
+  if (max_seqlen < 0 || (max_seqlen + 127) / 128 > (int64_t)1 << 30)
+    return fail(MXFA_ERR_INVALID, "%s: max_seqlen=%d out of range", fn, max_seqlen);
+  const int unit = mode == MXFA_ROW32 ? 1 : 32;
+  const int64_t min_rows = ((int64_t)max_seqlen + 127) / 128 * 128 / unit;
+  if (padded_rows < min_rows)
+    return fail(MXFA_ERR_INVALID, "%s: padded_rows=%lld smaller than one padded sequence", fn, (long long)padded_rows);
+  return hip_status(mxfa::launch_scale_scatter(compact, cu_seqlens, nseq, max_seqlen, C, (int)mode, padded_out,
+                                               padded_rows, (hipStream_t)stream),
+                    fn);
+}
+
+mxfa_status mxfa_fwd(const mxfa_attn_args* a, uint16_t* o, float* lse, void* stream) {
+  const char* fn = "mxfa_fwd";
+  mxfa_status st = check_attn(a, fn);
+  if (st != MXFA_OK) return st;
+  if (a->v.mode != MXFA_COL32 && a->v.mode != MXFA_SQ32)
+    return fail(MXFA_ERR_INVALID, "%s: v.mode must be COL32 or SQ32", fn);
+  if (!o || !lse) return fail(MXFA_ERR_INVALID, "%s: NULL o/lse", fn);
+  if (!aligned(o, 16) || !aligned(lse, 4)) return fail(MXFA_ERR_INVALID, "%s: o/lse misaligned", fn);
+  return hip_status(mxfa::launch_attn_fwd(to_problem(a), o, lse, (hipStream_t)stream), fn);
+}
+
+size_t mxfa_bwd_workspace_size(int64_t total_q, int num_heads, int head_dim, mxfa_dq_mode dq_mode) {
+  if (total_q < 0 || num_heads < 1 || head_dim < 1) return 0;
+  return mxfa::bwd_workspace_bytes(total_q, num_heads, head_dim, dq_mode == MXFA_DQ_FP16_STATIC ? 1 : 0);
+}
+
+mxfa_status mxfa_bwd(const mxfa_attn_args* a, mxfa_mx v_d, mxfa_mx dout, const uint16_t* o,
+                     const uint16_t* dout_bf16, const float* lse, mxfa_dq_mode dq_mode, float dq_static_scale,
+                     void* workspace, size_t workspace_bytes, uint16_t* dq, uint16_t* dk, uint16_t* dv,
+                     void* stream) {
+  const char* fn = "mxfa_bwd";
+  mxfa_status st = check_attn(a, fn);
+  if (st != MXFA_OK) return st;
+  if (a->q.mode != MXFA_SQ32 || a->k.mode != MXFA_SQ32)
+    return fail(MXFA_ERR_INVALID, "%s: q and k must be SQ32 (square blocks serve both GEMM directions)", fn);
+  if (v_d.mode != MXFA_ROW32 && v_d.mode != MXFA_SQ32)
+    return fail(MXFA_ERR_INVALID, "%s: v_d.mode must be ROW32 or SQ32", fn);
+  if (dout.mode != MXFA_SQ32) return fail(MXFA_ERR_INVALID, "%s: dout.mode must be SQ32", fn);
+  if (!v_d.data || !v_d.scale || !dout.data || !dout.scale)
+    return fail(MXFA_ERR_INVALID, "%s: NULL v_d/dout data or scale", fn);
+  if (!aligned(v_d.data, 16) || !aligned(v_d.scale, 16) || !aligned(dout.data, 16) || !aligned(dout.scale, 16))
+    return fail(MXFA_ERR_INVALID, "%s: v_d/dout not 16-byte aligned", fn);
+  if (!o || !dout_bf16 || !lse || !dq || !dk || !dv) return fail(MXFA_ERR_INVALID, "%s: NULL tensor argument", fn);
+  if (!aligned(o, 16) || !aligned(dout_bf16, 16) || !aligned(lse, 4) || !aligned(dq, 16) || !aligned(dk, 16) ||
+      !aligned(dv, 16))
+    return fail(MXFA_ERR_INVALID, "%s: misaligned tensor argument", fn);
+  if (dq_mode != MXFA_DQ_FP32 && dq_mode != MXFA_DQ_FP16_STATIC)
+    return fail(MXFA_ERR_INVALID, "%s: bad dq_mode %d", fn, (int)dq_mode);
+  if (dq_mode == MXFA_DQ_FP16_STATIC && !is_pow2(dq_static_scale))
+    return fail(MXFA_ERR_INVALID, "%s: dq_static_scale=%g must be a positive power of two", fn,
+                (double)dq_static_scale);
+  const size_t need = mxfa_bwd_workspace_size(a->total_q, a->num_heads, a->head_dim, dq_mode);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+    return fail(MXFA_ERR_INVALID, "%s: workspace NULL, misaligned or smaller than %zu bytes", fn, need);
+  mxfa::MxOperand vv{v_d.data, v_d.scale, (int)v_d.mode};
+  mxfa::MxOperand dd{dout.data, dout.scale, (int)dout.mode};
+  return hip_status(mxfa::launch_attn_bwd(to_problem(a), vv, dd, o, dout_bf16, lse,
+                                          dq_mode == MXFA_DQ_FP16_STATIC ? 1 : 0,
+                                          dq_mode == MXFA_DQ_FP16_STATIC ? dq_static_scale : 1.0f, workspace, dq, dk,
+                                          dv, (hipStream_t)stream),
+                    fn);
+}
+
+mxfa_status mxfa_rmsnorm_quantize(const uint16_t* x, int64_t ld_x, int64_t T, int C, const float* gamma, float eps,
+                                  const int32_t* cu_seqlens, int nseq, int max_seqlen, uint8_t* data_out,
+                                  uint8_t* scale_out, uint8_t* scale_t_out, void* stream) {
+  const char* fn = "mxfa_rmsnorm_quantize";
+  if (T < 0) return fail(MXFA_ERR_INVALID, "%s: T < 0", fn);
+  if (C <= 0 || C % 32 || C > 32768) return fail(MXFA_ERR_INVALID, "%s: C=%d must be a multiple of 32 in [32, 32768]", fn, C);
+  if (ld_x < C || ld_x % 8) return fail(MXFA_ERR_INVALID, "%s: bad ld_x", fn);
+  if (!x || !gamma || !data_out || !scale_out) return fail(MXFA_ERR_INVALID, "%s: NULL argument", fn);
+  if (!aligned(x, 16) || !aligned(gamma, 4) || !aligned(data_out, 16) || !aligned(scale_out, 16) ||
+      (scale_t_out && !aligned(scale_t_out, 16)))
+    return fail(MXFA_ERR_INVALID, "%s: misaligned argument", fn);
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(MXFA_ERR_INVALID, "%s: eps must be finite and >= 0", fn);
+  mxfa_status st = check_jagged(cu_seqlens, nseq, max_seqlen, T, fn);
+  if (st != MXFA_OK) return st;
+  return hip_status(mxfa::launch_rmsnorm_quantize(x, ld_x, C, gamma, eps, cu_seqlens, nseq, max_seqlen, data_out,
+                                                  scale_out, scale_t_out, (hipStream_t)stream),
+                    fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,449 @@
+// MXFP8 attention backward for gfx950: recomputation with five scaled-MFMA GEMMs on square-block
+// (32 x 32) quantized Q, K and dO, online dS quantization, dQ reduced through global atomics.
+//
+// What is computed (andresseo.expert "MXFP8 FlashAttention-4 Hits 2.85 Petaflops...", section
+// "Inside the TMEM Bargain and Zero-Gather Jagged Pipeline": five GEMMs; Q, K and dO in square
+// 32 x 32 blocks so one E4M3 payload serves the plain and the transposed GEMM; dS quantized once per
+// square block with a wave-wide absolute maximum; dQ reduction in FP16 with a static scale, or FP32;
+// brifing.si item 6):
+//   Delta_i = sum_d dO_id O_id                                   (preprocess)
+//   per KV tile (workgroup), per Q tile (inner loop):
+//     S = Q K^T;  P = exp(c S - LSE);  P_q = E4M3(P 2^8) at code 119
+//     dV += P_q^T dO;  dP = dO V^T;  dS = P (dP - Delta);  dS_q = SQ32(dS)
+//     dK += dS_q^T Q;  dQ_partial = dS_q K  -> atomically added (FP32, or FP16 holding sigma dQ)
+//   dK = c dK, dQ = c acc / sigma (finalize).
+//
+// gfx950 layout choices:
+//  * Workgroup = 4 waves = one 128-row KV tile; wave w owns key rows 32w..32w+31. Its K and V rows
+//    stay in VGPRs as the B operands of S = Q K^T and dP = dO V^T, so S and dP come out with one
+//    key per lane (column) and 16 queries per lane per 32-query block.
+//  * That accumulator layout is exactly the A operand of dV = P^T dO and dK = dS^T Q (one key per
+//    lane, contraction over queries): P_q and dS_q bytes are used in place, in the accumulator's
+//    query order; dO^T and Q^T are read from LDS with ds_read_b64_tr_b8 in the same order.
+//  * dQ = dS K contracts over all 128 keys of the tile (all four waves): dS_q goes to LDS key-major,
+//    each wave then computes 32 query rows and adds them to the accumulator with coalesced atomics
+//    (packed FP16 pairs or FP32).
+//  * LDS tiles use the same 16-byte-chunk XOR swizzle as the forward.
+#include "mx_device.h"
+#include "mxfa_internal.h"
+
+namespace {
+
+constexpr int kTile = 128;
+constexpr int kD = 128;
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row & 8) >> 1); }
+
+__device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t total) {
+  const int64_t per = total / 8, rem = total % 8;
+  const int64_t x = bid % 8, slot = bid / 8;
+  return x * per + (x < rem ? x : rem) + slot;
+}
+
+// Copy a 128 x 128-byte tile (rows row0.. of a [T, C] payload, head h) into swizzled LDS; rows at or
+// past `valid` are zero.
+__device__ __forceinline__ void load_tile(uint8_t* lds, const uint8_t* g, int64_t row0, int valid, int C, int h) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = threadIdx.x + 256 * j;
+    const int row = i >> 3, ch = i & 7;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (row < valid) v = *reinterpret_cast<const uint4*>(g + (row0 + row) * (int64_t)C + h * kD + 16 * ch);
+    *reinterpret_cast<uint4*>(lds + row * kD + 16 * (ch ^ swz(row))) = v;
+  }
+}
+
+// A/B operand of a 32x32x64 MFMA from a row of a swizzled LDS tile: 16 bytes at k = 16 hh and
+// 16 bytes at k = 32 + 16 hh of the 64-byte step ds.
+__device__ __forceinline__ mx_v8i lds_row_operand(const uint8_t* lds, int row, int ds, int hh) {
+  const uint8_t* p = lds + row * kD;
+  const int sw = swz(row);
+  uint4 lo = *reinterpret_cast<const uint4*>(p + 16 * ((4 * ds + hh) ^ sw));
+  uint4 hi = *reinterpret_cast<const uint4*>(p + 16 * ((4 * ds + 2 + hh) ^ sw));
+  return mx_v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
+// Transposed operand from a swizzled [row][col] LDS tile: lane (column col0 + l % 32, hh) receives
+// rows 64 ks + {8 i + 4 hh + t} (bytes 0-15) and 64 ks + 32 + {8 i + 4 hh + t} (bytes 16-31),
+// i, t = 0..3, i.e. the key/query order of an MFMA accumulator.
+__device__ __forceinline__ mx_v8i lds_tr_operand(const uint8_t* lds, int ks, int col0, int tr_row, int tr_col,
+                                                 int tr_swz) {
+  mx_v2i part[4];
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc) {
+    const int row = 64 * ks + 32 * (cc >> 1) + 16 * (cc & 1) + tr_row;
+    const int col = col0 + tr_col;
+    const int off = row * kD + 16 * ((col >> 4) ^ tr_swz) + (col & 15);
+    part[cc] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((MX_LDS mx_v2i*)(lds + off));
+  }
+  return mx_v8i{part[0].x, part[0].y, part[1].x, part[1].y, part[2].x, part[2].y, part[3].x, part[3].y};
+}
+
+// ---------------------------------------------------------------------------------------------
+// Preprocess: Delta[h][t] = sum_d dO[t, h, d] * O[t, h, d] (fp32), and zero the dQ accumulator.
+// One wave per (token, head) row of 128: two bf16 pairs per lane.
+// ---------------------------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) bwd_preprocess_kernel(const uint16_t* __restrict__ o,
+                                                             const uint16_t* __restrict__ dout, int64_t T, int H,
+                                                             float* __restrict__ delta, uint32_t* __restrict__ acc,
+                                                             int64_t acc_words) {
+  const int64_t gw = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int lane = threadIdx.x & 63;
+  if (gw < T * H) {
+    const int64_t t = gw / H;
+    const int h = (int)(gw % H);
+    const uint32_t a = *reinterpret_cast<const uint32_t*>(o + gw * kD + 2 * lane);
+    const uint32_t b = *reinterpret_cast<const uint32_t*>(dout + gw * kD + 2 * lane);
+    float sum = bf16_to_f32(a & 0xffffu) * bf16_to_f32(b & 0xffffu) + bf16_to_f32(a >> 16) * bf16_to_f32(b >> 16);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
+    if (lane == 0) delta[(int64_t)h * T + t] = sum;
+  }
+  // zero the accumulator (grid-stride over 16-byte words)
+  const int64_t nthreads = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < acc_words / 4; i += nthreads)
+    reinterpret_cast<uint4*>(acc)[i] = make_uint4(0, 0, 0, 0);
+}
+
+struct BwdParams {
+  const uint8_t *q, *k, *v, *dO;
+  const uint8_t *q_scale, *k_scale, *v_scale, *dO_scale;
+  int v_row_shift;  // V along D: 0 ROW32, 5 SQ32
+  const int32_t *cu_q, *cu_k;
+  int nseq, H, n_ktiles;
+  int64_t total_items;
+  float c2;  // c * log2(e)
+  int causal;
+  const float* lse;    // [H][Tq]
+  const float* delta;  // [H][Tq]
+  int64_t Tq;
+  int dq_fp16;
+  float sigma;
+  void* dq_acc;  // [Tq, C] fp32 or fp16
+  float c;
+  uint16_t *dk, *dv;
+};
+
+__global__ void __launch_bounds__(256, 1) attn_bwd_kernel(BwdParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k[kTile * kD];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_q[kTile * kD];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_do[kTile * kD];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_ds[kTile * kD];  // dS_q, key-major [kv][q]
+  __shared__ float lds_lse2[kTile];   // LSE * log2(e)
+  __shared__ float lds_delta[kTile];
+  __shared__ uint8_t lds_dscode[4][4];  // [kv block][q block]
+  __shared__ int64_t red[16];
+
+  const int64_t item = xcd_remap(blockIdx.x, p.total_items);
+  const int kt = (int)(item % p.n_ktiles);
+  const int h = (int)((item / p.n_ktiles) % p.H);
+  const int s = (int)(item / ((int64_t)p.n_ktiles * p.H));
+  const int64_t q_start = p.cu_q[s], k_start = p.cu_k[s];
+  const int Lq = p.cu_q[s + 1] - (int)q_start;
+  const int Lk = p.cu_k[s + 1] - (int)k_start;
+  if (kt * kTile >= Lk) return;
+
+  const SeqOffsets qoff = seq_offsets(p.cu_q, s, red);
+  const SeqOffsets koff = seq_offsets(p.cu_k, s, red);
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int r = lane & 31, hh = lane >> 5;
+  const int C = p.H * kD;
+  const int Cs = C >> 5;
+  const int kv0 = kt * kTile;
+  const int kvrow = kv0 + 32 * wave + r;  // this lane's key row (B operands of S and dP)
+
+  // K tile in LDS (for dQ = dS K), and this wave's K and V rows in VGPRs
+  load_tile(lds_k, p.k, k_start + kv0, Lk - kv0, C, h);
+  mx_v8i kb_op[2], vb_op[2];
+  {
+    const bool valid = kvrow < Lk;
+    const uint8_t* ks = p.k + (k_start + kvrow) * (int64_t)C + h * kD;
+    const uint8_t* vs = p.v + (k_start + kvrow) * (int64_t)C + h * kD;
+#pragma unroll
+    for (int ds = 0; ds < 2; ++ds) {
+      uint4 a0 = make_uint4(0, 0, 0, 0), a1 = a0, b0 = a0, b1 = a0;
+      if (valid) {
+        a0 = *reinterpret_cast<const uint4*>(ks + 64 * ds + 16 * hh);
+        a1 = *reinterpret_cast<const uint4*>(ks + 64 * ds + 32 + 16 * hh);
+        b0 = *reinterpret_cast<const uint4*>(vs + 64 * ds + 16 * hh);
+        b1 = *reinterpret_cast<const uint4*>(vs + 64 * ds + 32 + 16 * hh);
+      }
+      kb_op[ds] = mx_v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+      vb_op[ds] = mx_v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+    }
+  }
+  // K (SQ32) and V (ROW32/SQ32) scales along D of this lane's key row: byte 0 = d-block hh, byte 2 =
+  // d-block 2 + hh
+  const uint32_t ksc_b =
+      *reinterpret_cast<const uint32_t*>(p.k_scale + ((koff.padded + kvrow) >> 5) * (int64_t)Cs + h * 4) >> (8 * hh);
+  const uint32_t vsc_b =
+      *reinterpret_cast<const uint32_t*>(p.v_scale + ((koff.padded + kvrow) >> p.v_row_shift) * (int64_t)Cs + h * 4) >>
+      (8 * hh);
+
+  mx_v16f dk_acc[4], dv_acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    dk_acc[i] = mx_v16f{};
+    dv_acc[i] = mx_v16f{};
+  }
+
+  // per-lane constants of the transposed LDS reads
+  const int grp = lane >> 4, gl = lane & 15;
+  const int tb = gl >> 1, ts = gl & 1;
+  const int tr_row = 8 * (tb >> 2) + 4 * (grp >> 1) + (tb & 3);
+  const int tr_col = 16 * (grp & 1) + 8 * ts;
+  const int tr_swz = swz(tr_row);
+
+  const int n_qtiles = (Lq + kTile - 1) / kTile;
+  const int qt_begin = p.causal ? kt : 0;
+  for (int qt = qt_begin; qt < n_qtiles; ++qt) {
+    const int q0 = qt * kTile;
+    __syncthreads();  // previous iteration's LDS readers are done
+    load_tile(lds_q, p.q, q_start + q0, Lq - q0, C, h);
+    load_tile(lds_do, p.dO, q_start + q0, Lq - q0, C, h);
+    if (tid < kTile) {
+      const int qi = q0 + tid;
+      lds_lse2[tid] = qi < Lq ? p.lse[(int64_t)h * p.Tq + q_start + qi] * kLog2e : 0.0f;
+      lds_delta[tid] = qi < Lq ? p.delta[(int64_t)h * p.Tq + q_start + qi] : 0.0f;
+    }
+    __syncthreads();
+
+    const int64_t qbrow0 = (qoff.padded + q0) >> 5;  // scale block row of query block 0 of this tile
+
+    // ---- G1: S = Q K^T  and  G2: dP = dO V^T  (accumulator: key = column, 16 queries per lane) ----
+    mx_v16f sacc[4], dpacc[4];
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+      const uint32_t qsc =
+          *reinterpret_cast<const uint32_t*>(p.q_scale + (qbrow0 + qb) * (int64_t)Cs + h * 4) >> (8 * hh);
+      const uint32_t dosc =
+          *reinterpret_cast<const uint32_t*>(p.dO_scale + (qbrow0 + qb) * (int64_t)Cs + h * 4) >> (8 * hh);
+      sacc[qb] = mx_v16f{};
+      dpacc[qb] = mx_v16f{};
+      const int row = 32 * qb + r;
+      mx_v8i qa0 = lds_row_operand(lds_q, row, 0, hh);
+      mx_v8i qa1 = lds_row_operand(lds_q, row, 1, hh);
+      sacc[qb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa0, kb_op[0], sacc[qb], 0, 0, 0, (int)qsc, 0,
+                                                                 (int)ksc_b);
+      sacc[qb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa1, kb_op[1], sacc[qb], 0, 0, 2, (int)qsc, 2,
+                                                                 (int)ksc_b);
+      mx_v8i da0 = lds_row_operand(lds_do, row, 0, hh);
+      mx_v8i da1 = lds_row_operand(lds_do, row, 1, hh);
+      dpacc[qb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(da0, vb_op[0], dpacc[qb], 0, 0, 0, (int)dosc, 0,
+                                                                  (int)vsc_b);
+      dpacc[qb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(da1, vb_op[1], dpacc[qb], 0, 0, 2, (int)dosc, 2,
+                                                                  (int)vsc_b);
+    }
+
+    // ---- P, dS, and their E4M3 bytes (lane: key kvrow; queries 32 qb + 8 i + 4 hh + t) ----
+    uint32_t pk[4][4], dsk[4][4];
+    uint32_t dscode[4];
+    const bool kv_ok = kvrow < Lk;
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+      uint32_t amax = 0;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int ql = 32 * qb + 8 * (v >> 2) + 4 * hh + (v & 3);  // query row inside the tile
+        const bool ok = kv_ok && (q0 + ql < Lq) && !(p.causal && kvrow > q0 + ql);
+        const float pv = ok ? __builtin_amdgcn_exp2f(fmaf(sacc[qb][v], p.c2, -lds_lse2[ql])) : 0.0f;
+        const float dsv = pv * (dpacc[qb][v] - lds_delta[ql]);
+        sacc[qb][v] = pv;
+        dpacc[qb][v] = dsv;
+        amax = max(amax, __float_as_uint(dsv) & 0x7fffffffu);
+      }
+      amax = wave_max_u32(amax);
+      dscode[qb] = mx_code_from_amax_bits(amax);
+      const float inv = dscode[qb] == 255u ? 0.0f : mx_inv_scale(dscode[qb]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pk[qb][i] = mx_pack4_inrange(sacc[qb][4 * i] * 256.0f, sacc[qb][4 * i + 1] * 256.0f,
+                                     sacc[qb][4 * i + 2] * 256.0f, sacc[qb][4 * i + 3] * 256.0f);
+        uint32_t w = mx_pack4(dpacc[qb][4 * i] * inv, dpacc[qb][4 * i + 1] * inv, dpacc[qb][4 * i + 2] * inv,
+                              dpacc[qb][4 * i + 3] * inv);
+        dsk[qb][i] = dscode[qb] == 255u ? 0x7f7f7f7fu : w;
+      }
+    }
+
+    // ---- dS_q to LDS, key-major [kv][q], for dQ ----
+    {
+      const int kvl = 32 * wave + r;  // key row inside the tile
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int ql = 32 * qb + 8 * i + 4 * hh;
+          *reinterpret_cast<uint32_t*>(lds_ds + kvl * kD + 16 * ((ql >> 4) ^ swz(kvl)) + (ql & 15)) = dsk[qb][i];
+        }
+      if (lane == 0) {
+#pragma unroll
+        for (int qb = 0; qb < 4; ++qb) lds_dscode[wave][qb] = (uint8_t)dscode[qb];
+      }
+    }
+
+    // ---- G3: dV += P_q^T dO  and  G4: dK += dS_q^T Q  (contraction over 128 queries) ----
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      mx_v8i pa{(int)pk[2 * ks][0], (int)pk[2 * ks][1], (int)pk[2 * ks][2], (int)pk[2 * ks][3],
+                (int)pk[2 * ks + 1][0], (int)pk[2 * ks + 1][1], (int)pk[2 * ks + 1][2], (int)pk[2 * ks + 1][3]};
+      mx_v8i sa{(int)dsk[2 * ks][0], (int)dsk[2 * ks][1], (int)dsk[2 * ks][2], (int)dsk[2 * ks][3],
+                (int)dsk[2 * ks + 1][0], (int)dsk[2 * ks + 1][1], (int)dsk[2 * ks + 1][2], (int)dsk[2 * ks + 1][3]};
+      // A-operand scale of dS_q: k-block hh of this step is query block 2 ks + hh
+      const uint32_t sa_sc = hh ? dscode[2 * ks + 1] : dscode[2 * ks];
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        // B-operand scales (dO and Q, SQ32): query block 2 ks + hh, d-block db
+        const int64_t sidx = (qbrow0 + 2 * ks + hh) * (int64_t)Cs + h * 4 + db;
+        const uint32_t do_sc = p.dO_scale[sidx];
+        const uint32_t q_sc = p.q_scale[sidx];
+        mx_v8i dob = lds_tr_operand(lds_do, ks, 32 * db, tr_row, tr_col, tr_swz);
+        dv_acc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(pa, dob, dv_acc[db], 0, 0, 0, 119, 0, (int)do_sc);
+        mx_v8i qbt = lds_tr_operand(lds_q, ks, 32 * db, tr_row, tr_col, tr_swz);
+        dk_acc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(sa, qbt, dk_acc[db], 0, 0, 0, (int)sa_sc, 0,
+                                                                     (int)q_sc);
+      }
+    }
+    __syncthreads();  // dS_q of all four waves is in LDS
+
+    // ---- G5: dQ rows 32 wave.. of this tile = dS_q K over the 128 keys; atomics ----
+    {
+      const int qrow = q0 + 32 * wave;  // first query row of this wave's block
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        mx_v16f acc = mx_v16f{};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          mx_v8i dsa = lds_tr_operand(lds_ds, ks, 32 * wave, tr_row, tr_col, tr_swz);
+          mx_v8i kbt = lds_tr_operand(lds_k, ks, 32 * db, tr_row, tr_col, tr_swz);
+          const uint32_t a_sc = lds_dscode[2 * ks + hh][wave];
+          const uint32_t b_sc = p.k_scale[((koff.padded + kv0) / 32 + 2 * ks + hh) * (int64_t)Cs + h * 4 + db];
+          acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(dsa, kbt, acc, 0, 0, 0, (int)a_sc, 0, (int)b_sc);
+        }
+        // acc: column d = 32 db + r, rows q = 8 (v/4) + 4 hh + v%4 of the wave's 32-query block
+        const int d = h * kD + 32 * db + r;
+        if (!p.dq_fp16) {
+          float* dst = reinterpret_cast<float*>(p.dq_acc);
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int qr = qrow + 8 * (v >> 2) + 4 * hh + (v & 3);
+            if (qr < Lq) unsafeAtomicAdd(dst + (q_start + qr) * (int64_t)C + d, acc[v]);
+          }
+        } else {
+          // pair neighbouring columns: even lane takes (row v, d d+1), odd lane takes (row v+1, d-1 d)
+          __half2* dst = reinterpret_cast<__half2*>(p.dq_acc);
+          const bool odd = r & 1;
+#pragma unroll
+          for (int v = 0; v < 16; v += 2) {
+            const float mine_keep = odd ? acc[v + 1] : acc[v];
+            const float mine_send = odd ? acc[v] : acc[v + 1];
+            const float other = __shfl_xor(mine_send, 1, 64);
+            const float lo = odd ? other : mine_keep;  // column d (even)
+            const float hi = odd ? mine_keep : other;  // column d + 1
+            const int qr = qrow + 8 * (v >> 2) + 4 * hh + (v & 3) + (odd ? 1 : 0);
+            const int dcol = d - (odd ? 1 : 0);
+            if (qr < Lq) {
+              __half2 val = __floats2half2_rn(lo * p.sigma, hi * p.sigma);
+              unsafeAtomicAdd(dst + (((q_start + qr) * (int64_t)C + dcol) >> 1), val);
+            }
+          }
+        }
+      }
+    }
+  }
+
+  // ---- epilogue: dK = c dK, dV -> bf16 (accumulator: column d = 32 db + r, rows kv) ----
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int kr = kv0 + 32 * wave + 8 * (v >> 2) + 4 * hh + (v & 3);
+      if (kr < Lk) {
+        const int64_t idx = (k_start + kr) * (int64_t)C + h * kD + 32 * db + r;
+        p.dk[idx] = (uint16_t)f32_to_bf16(dk_acc[db][v] * p.c);
+        p.dv[idx] = (uint16_t)f32_to_bf16(dv_acc[db][v]);
+      }
+    }
+}
+
+// dQ = bf16(c * acc / sigma)
+__global__ void __launch_bounds__(256) bwd_finalize_kernel(const void* __restrict__ acc, int dq_fp16, float mult,
+                                                           int64_t n, uint16_t* __restrict__ dq) {
+  const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (i >= n) return;
+  float v[4];
+  if (dq_fp16) {
+    const __half2* a = reinterpret_cast<const __half2*>(acc) + i / 2;
+    float2 x0 = __half22float2(a[0]), x1 = __half22float2(a[1]);
+    v[0] = x0.x; v[1] = x0.y; v[2] = x1.x; v[3] = x1.y;
+  } else {
+    float4 x = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(acc) + i);
+    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+  }
+  uint2 out;
+  out.x = f32_to_bf16(v[0] * mult) | (f32_to_bf16(v[1] * mult) << 16);
+  out.y = f32_to_bf16(v[2] * mult) | (f32_to_bf16(v[3] * mult) << 16);
+  *reinterpret_cast<uint2*>(dq + i) = out;
+}
+
+}  // namespace
+
+namespace mxfa {
+
+size_t bwd_workspace_bytes(int64_t Tq, int H, int D, int dq_fp16) {
+  const size_t acc = (size_t)Tq * H * D * (dq_fp16 ? 2 : 4);
+  const size_t acc_al = (acc + 255) / 256 * 256;
+  const size_t del = (size_t)Tq * H * 4;
+  return acc_al + (del + 255) / 256 * 256;
+}
+
+hipError_t launch_attn_bwd(const AttnProblem& a, const MxOperand& v_d, const MxOperand& dout, const uint16_t* o,
+                           const uint16_t* dout_bf16, const float* lse, int dq_fp16, float sigma, void* workspace,
+                           uint16_t* dq, uint16_t* dk, uint16_t* dv, hipStream_t stream) {
+  const int64_t Tq = a.total_q;
+  const int C = a.H * kD;
+  const size_t acc_bytes = (size_t)Tq * C * (dq_fp16 ? 2 : 4);
+  uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
+  void* acc = ws;
+  float* delta = reinterpret_cast<float*>(ws + (acc_bytes + 255) / 256 * 256);
+  {
+    const int64_t rows = Tq * a.H;  // one wave per row
+    int64_t blocks = (rows + 3) / 4;
+    if (blocks < 1) blocks = 1;
+    const int64_t acc_words = (int64_t)((acc_bytes + 15) / 16 * 4);
+    hipLaunchKernelGGL(bwd_preprocess_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, o, dout_bf16, Tq, a.H,
+                       delta, reinterpret_cast<uint32_t*>(acc), acc_words);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  BwdParams p;
+  p.q = a.q.data; p.k = a.k.data; p.v = v_d.data; p.dO = dout.data;
+  p.q_scale = a.q.scale; p.k_scale = a.k.scale; p.v_scale = v_d.scale; p.dO_scale = dout.scale;
+  p.v_row_shift = v_d.mode == 0 ? 0 : 5;
+  p.cu_q = a.cu_q; p.cu_k = a.cu_k;
+  p.nseq = a.nseq; p.H = a.H;
+  p.n_ktiles = (a.max_seqlen_k + kTile - 1) / kTile;
+  p.total_items = (int64_t)p.n_ktiles * a.H * a.nseq;
+  p.c2 = a.softmax_scale * kLog2e;
+  p.causal = a.causal;
+  p.lse = lse; p.delta = delta; p.Tq = Tq;
+  p.dq_fp16 = dq_fp16; p.sigma = sigma; p.dq_acc = acc;
+  p.c = a.softmax_scale;
+  p.dk = dk; p.dv = dv;
+  if (p.total_items > 0) {
+    hipLaunchKernelGGL(attn_bwd_kernel, dim3((unsigned)p.total_items), dim3(256), 0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t n = Tq * C;
+  if (n > 0) {
+    const float mult = a.softmax_scale / (dq_fp16 ? sigma : 1.0f);
+    hipLaunchKernelGGL(bwd_finalize_kernel, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, stream, acc, dq_fp16,
+                       mult, n, dq);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+}  // namespace mxfa

@@ -1,0 +1,116 @@
+// Device-side MX helpers for gfx950 (CDNA4): E8M0 scale from exponent bits, saturating E4M3 pack
+// on the hardware converter, wave reductions, and the operand layouts of the scaled MFMA.
+//
+// Lane layouts of the scaled matrix instructions, as measured on gfx950:
+//   v_mfma_scale_f32_32x32x64_f8f6f4 (A: 32 x 64, B: 64 x 32, both 8 VGPRs of E4M3 per lane):
+//     lane l holds row r = l % 32 of A (column r of B); with h = l / 32, bytes 0-15 are
+//     k = 16h + [0,16) and bytes 16-31 are k = 32 + 16h + [0,16). The E8M0 scale of row r's
+//     k-block kb (k in [32kb, 32kb+32)) is taken from lane r + 32kb, byte `opsel` of the scale VGPR.
+//     Accumulator: lane l holds column l % 32, rows 8*(v/4) + 4*(l/32) + v%4 for v = 0..15.
+//   Only two facts matter to the kernels: the contraction order inside an MFMA is free as long as
+//   A and B agree on it, and the 16 bytes at the same byte offset of lanes r and r+32 form one
+//   scale block.
+//   ds_read_b64_tr_b8: in each group of 16 lanes, destination lane j receives byte b = byte (j & 7)
+//     of the 8 bytes addressed by lane 2b + (j >> 3) of the group.
+//   v_permlane32_swap(x, x): every lane receives x of lane l % 32 and of lane l % 32 + 32.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+typedef int mx_v8i __attribute__((ext_vector_type(8)));
+typedef int mx_v4i __attribute__((ext_vector_type(4)));
+typedef int mx_v2i __attribute__((ext_vector_type(2)));
+typedef float mx_v16f __attribute__((ext_vector_type(16)));
+typedef float mx_v4f __attribute__((ext_vector_type(4)));
+
+#define MX_LDS __attribute__((address_space(3)))
+
+// E8M0 code of a block from the bit pattern of its absolute maximum (sign already clear): the
+// fp32 exponent field minus 8 (= floor(log2 amax) - 8 + 127, the largest E4M3 exponent being 8),
+// clamped at 0; 255 when amax is Inf or NaN (bit patterns >= 0x7f800000 order above all finite
+// magnitudes as integers). This is the "bit extraction instead of logarithms" scale rule.
+__device__ __forceinline__ uint32_t mx_code_from_amax_bits(uint32_t amax_bits) {
+  uint32_t e = amax_bits >> 23;
+  if (e >= 255u) return 255u;
+  return e > 8u ? e - 8u : 0u;
+}
+
+// 2^(127 - code) as an fp32 (exact for code <= 253; finite amax never gives a code above 246).
+__device__ __forceinline__ float mx_inv_scale(uint32_t code) { return __uint_as_float((254u - code) << 23); }
+
+// Two floats -> two E4M3 bytes, round to nearest even, saturating at +-448. The hardware converter
+// turns out-of-range values into NaN, so values are clamped with v_med3 first (NaN blocks are
+// handled by the caller through code 255).
+__device__ __forceinline__ uint32_t mx_pack2_lo(float a, float b, uint32_t old) {
+  a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+  b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, false);
+}
+__device__ __forceinline__ uint32_t mx_pack2_hi(float a, float b, uint32_t old) {
+  a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+  b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, true);
+}
+// Four floats already known to lie in [-448, 448] (no clamp needed), e.g. P * 256 <= 256.
+__device__ __forceinline__ uint32_t mx_pack4_inrange(float a, float b, float c, float d) {
+  uint32_t r = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, (int)r, true);
+}
+__device__ __forceinline__ uint32_t mx_pack4(float a, float b, float c, float d) {
+  return mx_pack2_hi(c, d, mx_pack2_lo(a, b, 0u));
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Wave-wide (64 lanes) maximum of an unsigned value.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    uint32_t o = (uint32_t)__shfl_xor((int)v, off, 64);
+    v = v > o ? v : o;
+  }
+  return v;
+}
+
+// Sum of a per-thread integer over a workgroup of `nthreads` (<= 1024) threads; every thread gets
+// the total. `red` is a workgroup-shared scratch of at least 16 ints.
+__device__ __forceinline__ int64_t block_sum_i64(int64_t v, int64_t* red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nw = (blockDim.x + 63) >> 6;
+  __syncthreads();
+  if (lane == 0) red[wid] = v;
+  __syncthreads();
+  int64_t t = 0;
+  for (int w = 0; w < nw; ++w) t += red[w];
+  __syncthreads();
+  return t;
+}
+
+// Offsets of sequence s in the compact and padded layouts, computed by the whole workgroup from
+// the device cu_seqlens: blocks32 = sum_{r<s} ceil(L_r/32), padded = sum_{r<s} round_up(L_r,128).
+struct SeqOffsets {
+  int64_t blocks32;
+  int64_t padded;
+};
+__device__ __forceinline__ SeqOffsets seq_offsets(const int32_t* cu, int s, int64_t* red) {
+  int64_t b = 0, p = 0;
+  for (int r = threadIdx.x; r < s; r += blockDim.x) {
+    int64_t L = (int64_t)cu[r + 1] - cu[r];
+    b += (L + 31) >> 5;
+    p += (L + 127) >> 7;
+  }
+  SeqOffsets o;
+  o.blocks32 = block_sum_i64(b, red);
+  o.padded = block_sum_i64(p, red) << 7;
+  return o;
+}

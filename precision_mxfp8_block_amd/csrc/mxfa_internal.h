@@ -1,0 +1,40 @@
+// Internal interface between the C ABI layer (api.cpp) and the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace mxfa {
+
+struct MxOperand {
+  const uint8_t* data;
+  const uint8_t* scale;
+  int mode;  // 0 ROW32, 1 COL32, 2 SQ32
+};
+
+struct AttnProblem {
+  MxOperand q, k, v;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int nseq, max_seqlen_q, max_seqlen_k;
+  int64_t total_q, total_k;
+  int H;
+  float softmax_scale;
+  int causal;
+};
+
+hipError_t launch_quantize(const uint16_t* x, int64_t ld_x, int64_t T, int C, const int32_t* cu, int nseq,
+                           int max_seqlen, int mode, uint8_t* data, uint8_t* scale, uint8_t* scale_t,
+                           hipStream_t stream);
+hipError_t launch_scale_scatter(const uint8_t* compact, const int32_t* cu, int nseq, int max_seqlen, int C, int mode,
+                                uint8_t* padded, int64_t padded_rows, hipStream_t stream);
+hipError_t launch_rmsnorm_quantize(const uint16_t* x, int64_t ld_x, int C, const float* gamma, float eps,
+                                   const int32_t* cu, int nseq, int max_seqlen, uint8_t* data, uint8_t* scale,
+                                   uint8_t* scale_t, hipStream_t stream);
+hipError_t launch_attn_fwd(const AttnProblem& a, uint16_t* o, float* lse, hipStream_t stream);
+size_t bwd_workspace_bytes(int64_t Tq, int H, int D, int dq_fp16);
+hipError_t launch_attn_bwd(const AttnProblem& a, const MxOperand& v_d, const MxOperand& dout, const uint16_t* o,
+                           const uint16_t* dout_bf16, const float* lse, int dq_fp16, float sigma, void* workspace,
+                           uint16_t* dq, uint16_t* dk, uint16_t* dv, hipStream_t stream);
+
+}  // namespace mxfa

@@ -1,0 +1,334 @@
+// MX quantizer, jagged scale scatter and the fused RMSNorm + quantize producer (gfx950).
+//
+// All three are HBM-bound streaming kernels: every input byte is read once with 16-byte (or
+// 8-byte) coalesced loads, every output byte written once. The block scale comes from the
+// exponent bits of the block maximum (integer max over magnitude bit patterns, no logarithm or
+// division), the payload from the hardware E4M3 converter after a saturating clamp.
+// Pages: andresseo.expert "MXFP8 FlashAttention-4 Hits 2.85 Petaflops...", section "Inside the
+// TMEM Bargain and Zero-Gather Jagged Pipeline" (32-element blocks, bit-extraction scale, fused
+// RMSNorm producer, scale-only padding for jagged inputs); brifing.si items 5-7.
+#include "mx_device.h"
+#include "mxfa_internal.h"
+
+namespace {
+
+// ---------------------------------------------------------------------------------------------
+// ROW32: 1 x 32 blocks along the columns. Two lanes share a block, 16 bf16 each (two 16-byte loads).
+// ---------------------------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) quantize_row32_kernel(const uint16_t* __restrict__ x, int64_t ld_x, int64_t T,
+                                                             int C, uint8_t* __restrict__ data,
+                                                             uint8_t* __restrict__ scale) {
+  const int64_t chunks_per_row = C >> 4;
+  const int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (u >= T * chunks_per_row) return;  // pairs of lanes leave together (chunks_per_row is even)
+  const int64_t t = u / chunks_per_row;
+  const int j = (int)(u - t * chunks_per_row);
+  const uint4* src = reinterpret_cast<const uint4*>(x + t * ld_x + (int64_t)j * 16);
+  uint4 a = src[0], b = src[1];
+  uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  uint32_t amax = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t lo = w[i] & 0x7fffu, hi = (w[i] >> 16) & 0x7fffu;
+    amax = max(amax, max(lo, hi));
+  }
+  amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1, 64));
+  const uint32_t code = mx_code_from_amax_bits(amax << 16);
+  uint4 out;
+  if (code == 255u) {
+    out = make_uint4(0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu);
+  } else {
+    const float inv = mx_inv_scale(code);
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t p = w[2 * i], q = w[2 * i + 1];
+      o[i] = mx_pack4(bf16_to_f32(p & 0xffffu) * inv, bf16_to_f32(p >> 16) * inv, bf16_to_f32(q & 0xffffu) * inv,
+                      bf16_to_f32(q >> 16) * inv);
+    }
+    out = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+  *reinterpret_cast<uint4*>(data + t * C + (int64_t)j * 16) = out;
+  if ((j & 1) == 0) scale[t * (C >> 5) + (j >> 1)] = (uint8_t)code;
+}
+
+// ---------------------------------------------------------------------------------------------
+// COL32: 32 x 1 blocks along the tokens. A thread owns 4 adjacent columns of one 32-token block
+// (8-byte loads, 64 lanes cover 512 contiguous bytes of a row).
+// Grid: x = column groups / 256, y = block index inside the sequence, z = sequence.
+// ---------------------------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) quantize_col32_kernel(const uint16_t* __restrict__ x, int64_t ld_x, int C,
+                                                             const int32_t* __restrict__ cu,
+                                                             uint8_t* __restrict__ data,
+                                                             uint8_t* __restrict__ scale) {
+  __shared__ int64_t red[16];
+  const int s = blockIdx.z, b = blockIdx.y;
+  const int64_t t0 = cu[s], L = (int64_t)cu[s + 1] - t0;
+  if ((int64_t)b * 32 >= L) return;  // uniform over the workgroup
+  const SeqOffsets off = seq_offsets(cu, s, red);
+  const int g = blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= (C >> 2)) return;
+  const int rows = (int)min<int64_t>(32, L - (int64_t)b * 32);
+  const int64_t ta = t0 + (int64_t)b * 32;
+  uint2 v[32];
+  uint32_t am[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int r = 0; r < 32; ++r) {
+    if (r < rows) {
+      v[r] = *reinterpret_cast<const uint2*>(x + (ta + r) * ld_x + (int64_t)g * 4);
+      am[0] = max(am[0], v[r].x & 0x7fffu);
+      am[1] = max(am[1], (v[r].x >> 16) & 0x7fffu);
+      am[2] = max(am[2], v[r].y & 0x7fffu);
+      am[3] = max(am[3], (v[r].y >> 16) & 0x7fffu);
+    }
+  }
+  uint32_t code[4];
+  float inv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    code[i] = mx_code_from_amax_bits(am[i] << 16);
+    inv[i] = code[i] == 255u ? 0.0f : mx_inv_scale(code[i]);
+  }
+#pragma unroll
+  for (int r = 0; r < 32; ++r) {
+    if (r < rows) {
+      uint32_t o = mx_pack4(bf16_to_f32(v[r].x & 0xffffu) * inv[0], bf16_to_f32(v[r].x >> 16) * inv[1],
+                            bf16_to_f32(v[r].y & 0xffffu) * inv[2], bf16_to_f32(v[r].y >> 16) * inv[3]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (code[i] == 255u) o = (o & ~(0xffu << (8 * i))) | (0x7fu << (8 * i));
+      *reinterpret_cast<uint32_t*>(data + (ta + r) * C + (int64_t)g * 4) = o;
+    }
+  }
+  const int64_t br = off.blocks32 + b;
+  *reinterpret_cast<uint32_t*>(scale + br * C + (int64_t)g * 4) =
+      code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
+}
+
+// ---------------------------------------------------------------------------------------------
+// SQ32: 32 x 32 blocks, one wave per block: lane l covers row l/2 and 16 columns (two 16-byte
+// loads). The block maximum is a wave-wide reduction. Four waves cover 128 adjacent columns.
+// Grid: x = C / 128 (rounded up), y = block index inside the sequence, z = sequence.
+// ---------------------------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) quantize_sq32_kernel(const uint16_t* __restrict__ x, int64_t ld_x, int C,
+                                                            const int32_t* __restrict__ cu, int nseq,
+                                                            uint8_t* __restrict__ data, uint8_t* __restrict__ scale,
+                                                            uint8_t* __restrict__ scale_t) {
+  __shared__ int64_t red[16];
+  const int s = blockIdx.z, b = blockIdx.y;
+  const int64_t t0 = cu[s], L = (int64_t)cu[s + 1] - t0;
+  if ((int64_t)b * 32 >= L) return;
+  const SeqOffsets off = seq_offsets(cu, s, red);
+  int64_t nb_total = 0;
+  if (scale_t) nb_total = seq_offsets(cu, nseq, red).blocks32;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int cb = blockIdx.x * 4 + wave;  // 32-column block
+  if (cb >= (C >> 5)) return;            // whole wave leaves together
+  const int r = lane >> 1, half = lane & 1;
+  const int rows = (int)min<int64_t>(32, L - (int64_t)b * 32);
+  const int64_t t = t0 + (int64_t)b * 32 + r;
+  uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (r < rows) {
+    const uint4* src = reinterpret_cast<const uint4*>(x + t * ld_x + (int64_t)cb * 32 + half * 16);
+    uint4 a = src[0], c = src[1];
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w; w[4] = c.x; w[5] = c.y; w[6] = c.z; w[7] = c.w;
+  }
+  uint32_t amax = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = max(amax, max(w[i] & 0x7fffu, (w[i] >> 16) & 0x7fffu));
+  amax = wave_max_u32(amax);
+  const uint32_t code = mx_code_from_amax_bits(amax << 16);
+  if (r < rows) {
+    uint4 out;
+    if (code == 255u) {
+      out = make_uint4(0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu);
+    } else {
+      const float inv = mx_inv_scale(code);
+      uint32_t o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t p = w[2 * i], q = w[2 * i + 1];
+        o[i] = mx_pack4(bf16_to_f32(p & 0xffffu) * inv, bf16_to_f32(p >> 16) * inv, bf16_to_f32(q & 0xffffu) * inv,
+                        bf16_to_f32(q >> 16) * inv);
+      }
+      out = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+    *reinterpret_cast<uint4*>(data + t * C + (int64_t)cb * 32 + half * 16) = out;
+  }
+  if (lane == 0) {
+    const int64_t br = off.blocks32 + b;
+    scale[br * (C >> 5) + cb] = (uint8_t)code;
+    if (scale_t) scale_t[(int64_t)cb * nb_total + br] = (uint8_t)code;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Scale scatter: compact rows -> padded rows; each workgroup moves the rows of one 128-token group
+// of one sequence and zero-fills the rows of that group that lie past the sequence end.
+// Grid: x = 128-token groups (max_seqlen / 128 rounded up), y = sequence.
+// ---------------------------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) scale_scatter_kernel(const uint8_t* __restrict__ compact,
+                                                            const int32_t* __restrict__ cu, int C, int mode,
+                                                            uint8_t* __restrict__ padded, int64_t padded_rows) {
+  __shared__ int64_t red[16];
+  const int s = blockIdx.y, g = blockIdx.x;
+  const int64_t L = (int64_t)cu[s + 1] - cu[s];
+  if ((int64_t)g * 128 >= L) return;
+  const SeqOffsets off = seq_offsets(cu, s, red);
+  const int width = (mode == 1) ? C : (C >> 5);
+  const int unit = (mode == 0) ? 1 : 32;                 // tokens per layout row
+  const int rows_per_group = 128 / unit;
+  const int64_t valid_rows = (L + unit - 1) / unit;      // rows of this sequence in the compact tensor
+  const int64_t src_row0 = (mode == 0) ? (int64_t)cu[s] : off.blocks32;
+  const int64_t dst_row0 = off.padded / unit;
+  const int64_t nbytes = (int64_t)rows_per_group * width;
+  for (int64_t i = threadIdx.x; i < nbytes; i += blockDim.x) {
+    const int64_t rr = (int64_t)g * rows_per_group + i / width;  // row inside the sequence
+    const int64_t col = i % width;
+    uint8_t v = 0;
+    if (rr < valid_rows) v = compact[(src_row0 + rr) * width + col];
+    if (dst_row0 + rr < padded_rows) padded[(dst_row0 + rr) * width + col] = v;  // never past the buffer
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Fused RMSNorm + SQ32 quantize. One workgroup per (sequence, 32-token block), all C columns:
+//   pass 1: per-row sum of squares (FP64 adds of exact bf16 squares, one rounding to fp32),
+//           r = 1 / sqrtf(ss / C + eps) with IEEE division and square root;
+//   pass 2: y = (x * r) * gamma, block maxima per 32-column block (integer max in LDS);
+//   pass 3: y again, quantize with the block's code, store payload and both scale layouts.
+// Passes 2 and 3 re-read the 32 x C tile, which the L2 holds; HBM sees one read and one write.
+// ---------------------------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) rmsnorm_quantize_kernel(const uint16_t* __restrict__ x, int64_t ld_x, int C,
+                                                               const float* __restrict__ gamma, float eps,
+                                                               const int32_t* __restrict__ cu, int nseq,
+                                                               uint8_t* __restrict__ data,
+                                                               uint8_t* __restrict__ scale,
+                                                               uint8_t* __restrict__ scale_t) {
+  __shared__ int64_t red[16];
+  __shared__ float rs[32];
+  __shared__ uint32_t bmax[1024];  // up to C = 32768 columns
+  const int s = blockIdx.y, b = blockIdx.x;
+  const int64_t t0 = cu[s], L = (int64_t)cu[s + 1] - t0;
+  if ((int64_t)b * 32 >= L) return;
+  const SeqOffsets off = seq_offsets(cu, s, red);
+  int64_t nb_total = 0;
+  if (scale_t) nb_total = seq_offsets(cu, nseq, red).blocks32;
+  const int rows = (int)min<int64_t>(32, L - (int64_t)b * 32);
+  const int64_t ta = t0 + (int64_t)b * 32;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nwaves = blockDim.x >> 6;
+  const int ncb = C >> 5;
+  for (int i = threadIdx.x; i < ncb; i += blockDim.x) bmax[i] = 0;
+  // pass 1: one wave per row
+  for (int r = wave; r < rows; r += nwaves) {
+    const uint16_t* row = x + (ta + r) * ld_x;
+    double ss = 0.0;
+    for (int c = lane * 8; c < C; c += 64 * 8) {
+      uint4 v = *reinterpret_cast<const uint4*>(row + c);
+      uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float a = bf16_to_f32(w[i] & 0xffffu), bb = bf16_to_f32(w[i] >> 16);
+        ss += (double)(a * a) + (double)(bb * bb);  // squares of bf16 values are exact in fp32
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
+    if (lane == 0) {
+      float ms = (float)ss / (float)C;
+      rs[r] = 1.0f / __fsqrt_rn(ms + eps);
+    }
+  }
+  __syncthreads();
+  // pass 2: block maxima of y. Thread covers 8 columns of one row.
+  const int chunks = C >> 3;
+  for (int i = threadIdx.x; i < rows * chunks; i += blockDim.x) {
+    const int r = i / chunks, ch = i % chunks;
+    uint4 v = *reinterpret_cast<const uint4*>(x + (ta + r) * ld_x + (int64_t)ch * 8);
+    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    const float rr = rs[r];
+    uint32_t am = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float y0 = __fmul_rn(__fmul_rn(bf16_to_f32(w[k] & 0xffffu), rr), gamma[ch * 8 + 2 * k]);
+      float y1 = __fmul_rn(__fmul_rn(bf16_to_f32(w[k] >> 16), rr), gamma[ch * 8 + 2 * k + 1]);
+      am = max(am, max(__float_as_uint(y0) & 0x7fffffffu, __float_as_uint(y1) & 0x7fffffffu));
+    }
+    atomicMax(&bmax[ch >> 2], am);
+  }
+  __syncthreads();
+  // pass 3: quantize and store
+  for (int i = threadIdx.x; i < rows * chunks; i += blockDim.x) {
+    const int r = i / chunks, ch = i % chunks;
+    uint4 v = *reinterpret_cast<const uint4*>(x + (ta + r) * ld_x + (int64_t)ch * 8);
+    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    const float rr = rs[r];
+    const uint32_t code = mx_code_from_amax_bits(bmax[ch >> 2]);
+    uint2 out;
+    if (code == 255u) {
+      out = make_uint2(0x7f7f7f7fu, 0x7f7f7f7fu);
+    } else {
+      const float inv = mx_inv_scale(code);
+      float y[8];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        y[2 * k] = __fmul_rn(__fmul_rn(bf16_to_f32(w[k] & 0xffffu), rr), gamma[ch * 8 + 2 * k]);
+        y[2 * k + 1] = __fmul_rn(__fmul_rn(bf16_to_f32(w[k] >> 16), rr), gamma[ch * 8 + 2 * k + 1]);
+      }
+      out.x = mx_pack4(y[0] * inv, y[1] * inv, y[2] * inv, y[3] * inv);
+      out.y = mx_pack4(y[4] * inv, y[5] * inv, y[6] * inv, y[7] * inv);
+    }
+    *reinterpret_cast<uint2*>(data + (ta + r) * C + (int64_t)ch * 8) = out;
+  }
+  const int64_t br = off.blocks32 + b;
+  for (int cb = threadIdx.x; cb < ncb; cb += blockDim.x) {
+    const uint8_t code = (uint8_t)mx_code_from_amax_bits(bmax[cb]);
+    scale[br * ncb + cb] = code;
+    if (scale_t) scale_t[(int64_t)cb * nb_total + br] = code;
+  }
+}
+
+}  // namespace
+
+namespace mxfa {
+
+hipError_t launch_quantize(const uint16_t* x, int64_t ld_x, int64_t T, int C, const int32_t* cu, int nseq,
+                           int max_seqlen, int mode, uint8_t* data, uint8_t* scale, uint8_t* scale_t,
+                           hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  if (mode == 0) {
+    const int64_t units = T * (C >> 4);
+    const int64_t blocks = (units + 255) / 256;
+    hipLaunchKernelGGL(quantize_row32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, ld_x, T, C, data,
+                       scale);
+  } else if (mode == 1) {
+    dim3 grid((unsigned)(((C >> 2) + 255) / 256), (unsigned)((max_seqlen + 31) / 32), (unsigned)nseq);
+    hipLaunchKernelGGL(quantize_col32_kernel, grid, dim3(256), 0, stream, x, ld_x, C, cu, data, scale);
+  } else {
+    dim3 grid((unsigned)((C + 127) / 128), (unsigned)((max_seqlen + 31) / 32), (unsigned)nseq);
+    hipLaunchKernelGGL(quantize_sq32_kernel, grid, dim3(256), 0, stream, x, ld_x, C, cu, nseq, data, scale,
+                       scale_t);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_scale_scatter(const uint8_t* compact, const int32_t* cu, int nseq, int max_seqlen, int C, int mode,
+                                uint8_t* padded, int64_t padded_rows, hipStream_t stream) {
+  if (max_seqlen == 0) return hipSuccess;
+  dim3 grid((unsigned)((max_seqlen + 127) / 128), (unsigned)nseq);
+  hipLaunchKernelGGL(scale_scatter_kernel, grid, dim3(256), 0, stream, compact, cu, C, mode, padded, padded_rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_quantize(const uint16_t* x, int64_t ld_x, int C, const float* gamma, float eps,
+                                   const int32_t* cu, int nseq, int max_seqlen, uint8_t* data, uint8_t* scale,
+                                   uint8_t* scale_t, hipStream_t stream) {
+  if (max_seqlen == 0) return hipSuccess;
+  dim3 grid((unsigned)((max_seqlen + 31) / 32), (unsigned)nseq);
+  hipLaunchKernelGGL(rmsnorm_quantize_kernel, grid, dim3(256), 0, stream, x, ld_x, C, gamma, eps, cu, nseq, data,
+                     scale, scale_t);
+  return hipGetLastError();
+}
+
+}  // namespace mxfa

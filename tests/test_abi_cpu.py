@@ -1,0 +1,151 @@
+"""CPU tests of the boundary: the library loads and exports every entry point the header declares,
+every argument error is reported before anything is enqueued (no GPU needed: the calls below fail
+validation, so no HIP call is made), and host-only helpers compute what the header states."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import precision_mxfp8_block_amd as mx
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxfa.h")
+
+OK, INVALID, UNSUPPORTED = 0, 1, 2
+P = 0x100000  # an aligned, never dereferenced stand-in pointer
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mxfa_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_abi():
+    names = _declared_functions()
+    for n in ["mxfa_quantize", "mxfa_fwd", "mxfa_bwd", "mxfa_varlen_scale_scatter", "mxfa_rmsnorm_quantize",
+              "mxfa_bwd_workspace_size", "mxfa_status_string", "mxfa_last_error_message"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(mx.library_path())
+    for n in _declared_functions():
+        assert hasattr(lib, n), n
+
+
+def _lib():
+    return mx._load()
+
+
+def _last():
+    return mx.mxfa_last_error_message()
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(mode=7), INVALID),
+    (dict(C=48), INVALID),
+    (dict(ld_x=100), INVALID),          # ld_x < C
+    (dict(ld_x=132), INVALID),          # not a multiple of 8
+    (dict(x=0), INVALID),
+    (dict(x=P + 8), INVALID),           # misaligned
+    (dict(T=-1), INVALID),
+    (dict(scale_t=P), INVALID),         # scale_t only for SQ32 (mode ROW32 here)
+    (dict(mode=2, cu=0), INVALID),      # jagged modes need cu_seqlens
+    (dict(mode=2, nseq=0), INVALID),
+    (dict(mode=1, max_seqlen=10 ** 6), INVALID),  # > T
+])
+def test_quantize_argument_errors(kw, expect):
+    a = dict(x=P, ld_x=128, T=256, C=128, cu=P, nseq=1, max_seqlen=256, mode=0, data=P, scale=P, scale_t=0)
+    a.update(kw)
+    st = _lib().mxfa_quantize(a["x"], a["ld_x"], a["T"], a["C"], a["cu"], a["nseq"], a["max_seqlen"], a["mode"],
+                              a["data"], a["scale"], a["scale_t"], 0)
+    assert st == expect
+    assert _last() != ""
+    assert mx.mxfa_status_string(st) == {INVALID: "MXFA_ERR_INVALID", UNSUPPORTED: "MXFA_ERR_UNSUPPORTED"}[expect]
+
+
+def _args(**kw):
+    a = dict(q=(P, P, 2), k=(P, P, 2), v=(P, P, 1), cu_q=P, cu_k=P, nseq=1, max_q=256, max_k=256, total_q=256,
+             total_k=256, H=1, D=128, scale=0.088, causal=0)
+    a.update(kw)
+    return mx._AttnArgs(mx._Mx(*a["q"]), mx._Mx(*a["k"]), mx._Mx(*a["v"]), a["cu_q"], a["cu_k"], a["nseq"],
+                        a["max_q"], a["max_k"], a["total_q"], a["total_k"], a["H"], a["D"], a["scale"], a["causal"])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(D=64), UNSUPPORTED),
+    (dict(H=0), INVALID),
+    (dict(nseq=0), INVALID),
+    (dict(max_q=300), INVALID),         # > total_q
+    (dict(cu_q=0), INVALID),
+    (dict(q=(P, P, 1)), INVALID),       # q must be ROW32 or SQ32
+    (dict(v=(P, P, 0)), INVALID),       # v must be COL32 or SQ32
+    (dict(k=(0, P, 2)), INVALID),
+    (dict(k=(P + 4, P, 2)), INVALID),
+    (dict(scale=float("inf")), INVALID),
+])
+def test_fwd_argument_errors(kw, expect):
+    a = _args(**kw)
+    st = _lib().mxfa_fwd(ctypes.byref(a), P, P, 0)
+    assert st == expect, _last()
+    assert _last() != ""
+
+
+def test_fwd_null_outputs():
+    a = _args()
+    assert _lib().mxfa_fwd(ctypes.byref(a), 0, P, 0) == INVALID
+    assert _lib().mxfa_fwd(None, P, P, 0) == INVALID
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(args=dict(q=(P, P, 0))), INVALID),   # backward needs SQ32 q and k
+    (dict(vd_mode=1), INVALID),                # v_d must be along D
+    (dict(do_mode=0), INVALID),                # dO must be SQ32
+    (dict(dq_mode=1, sigma=3.0), INVALID),     # sigma not a power of two
+    (dict(dq_mode=1, sigma=0.0), INVALID),
+    (dict(dq_mode=5), INVALID),
+    (dict(ws_bytes=16), INVALID),              # workspace too small
+    (dict(ws=P + 64), INVALID),                # workspace not 256-aligned
+])
+def test_bwd_argument_errors(kw, expect):
+    a = _args(**kw.get("args", {}))
+    need = mx.mxfa_bwd_workspace_size(256, 1, 128, kw.get("dq_mode", 0) if kw.get("dq_mode", 0) in (0, 1) else 0)
+    st = _lib().mxfa_bwd(ctypes.byref(a), mx._Mx(P, P, kw.get("vd_mode", 0)), mx._Mx(P, P, kw.get("do_mode", 2)), P, P,
+                         P, kw.get("dq_mode", 0), kw.get("sigma", 1.0), kw.get("ws", P), kw.get("ws_bytes", need), P,
+                         P, P, 0)
+    assert st == expect, _last()
+
+
+def test_scatter_and_rmsnorm_argument_errors():
+    lib = _lib()
+    assert lib.mxfa_varlen_scale_scatter(P, P, 1, 256, 100, 0, P, 256, 0) == INVALID  # C % 32
+    assert lib.mxfa_varlen_scale_scatter(P, P, 1, 256, 128, 0, P, 100, 0) == INVALID  # padded_rows too small
+    assert lib.mxfa_varlen_scale_scatter(0, P, 1, 256, 128, 0, P, 256, 0) == INVALID
+    assert lib.mxfa_rmsnorm_quantize(P, 1024, 64, 1024, P, -1.0, P, 1, 64, P, P, 0, 0) == INVALID  # eps < 0
+    assert lib.mxfa_rmsnorm_quantize(P, 1024, 64, 1024, 0, 1e-6, P, 1, 64, P, P, 0, 0) == INVALID  # gamma NULL
+    assert lib.mxfa_rmsnorm_quantize(P, 1024, 64, 1000, P, 1e-6, P, 1, 64, P, P, 0, 0) == INVALID  # C % 32
+
+
+def test_workspace_size_and_padded_rows():
+    # dQ accumulator fp32 [Tq, H*D] + Delta [H][Tq], each rounded up to 256 bytes
+    assert mx.mxfa_bwd_workspace_size(1000, 2, 128, 0) == 1000 * 256 * 4 + (8000 + 255) // 256 * 256
+    assert mx.mxfa_bwd_workspace_size(1000, 2, 128, 1) == 1000 * 256 * 2 + (8000 + 255) // 256 * 256
+    assert mx.mxfa_padded_token_rows(np.array([0, 1, 129, 129, 385], np.int32)) == 128 + 128 + 0 + 256
+
+
+def test_device_code_has_no_packed_fp32_instructions():
+    """Every kernel file compiled for gfx950 contains no packed-FP32 VALU instruction."""
+    csrc = os.path.join(ROOT, "precision_mxfp8_block_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if not f.endswith(".hip"):
+            continue
+        r = subprocess.run(["/opt/rocm/bin/hipcc", "--offload-arch=gfx950", "-O3", "-std=c++17", "-S",
+                            "--cuda-device-only", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                            "-I", os.path.join(ROOT, "include"), "-I", csrc, os.path.join(csrc, f), "-o", "-"],
+                           capture_output=True, text=True, check=True)
+        bad = [l for l in r.stdout.splitlines() if re.search(r"\bv_pk_(add|mul|fma)_f32\b", l)]
+        assert not bad, (f, bad[:3])

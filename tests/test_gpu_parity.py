@@ -1,0 +1,173 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on identical seeded inputs.
+
+Bit-exact for the quantizer, the scale scatter and the RMSNorm+quantize producer; tolerances of
+tests/mx_cases.py for attention. Sizes here finish in seconds on the oracle and still span several
+tiles and ragged tails; full-size sampled checks are in test_gpu_fullsize.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import precision_mxfp8_block_amd as mx
+import synth
+from mx_cases import AttnCase, check_grads, check_o, cu_dev, say, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def _special_matrix(seed, T, C):
+    """N(0,1) bf16 with outliers, exact zeros, bf16 subnormals, a NaN and an Inf block, and
+    values that scale onto E4M3 rounding ties."""
+    x = synth.normal_bf16(seed, 1, (T, C), outlier_p=0.01)
+    xf = synth.bf16_bits_to_f32(x).copy()
+    xf[0, :64] = 0.0
+    xf[1, 32:64] = np.float32(1e-39)  # bf16 subnormals
+    xf[1, 40] = np.float32(3e-39)
+    xf[2, 0:32] = np.float32([1.0625, 1.1875, 2.0, 432.0] * 8)  # ties after scaling
+    if T > 40:
+        xf[40, 5] = np.nan
+        xf[37, 100 % C] = np.inf
+    return synth.f32_to_bf16_bits(xf)
+
+
+@pytest.mark.parametrize("mode", [oracle.ROW32, oracle.COL32, oracle.SQ32])
+@pytest.mark.parametrize("lens", [[256], [37, 128, 1, 300, 95, 64]])
+def test_quantize_bit_exact(mode, lens):
+    say(f"quantize mode={mode} lens={lens}")
+    cu = synth.cu_seqlens(lens)
+    T, C = int(cu[-1]), 384
+    x = _special_matrix(3 + mode, T, C)
+    d_ref, s_ref, st_ref = oracle.quantize(x, cu, mode)
+    data, scale, scale_t = mx.quantize(to_dev_bf16(x), cu, cu_dev(cu), mode, want_scale_t=(mode == oracle.SQ32))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(data.cpu().numpy(), d_ref)
+    np.testing.assert_array_equal(scale.cpu().numpy(), s_ref)
+    if mode == oracle.SQ32:
+        np.testing.assert_array_equal(scale_t.cpu().numpy(), st_ref)
+
+
+def test_quantize_strided_rows():
+    """ld_x > C: the quantizer reads the first C columns of each row."""
+    say("quantize strided")
+    T, C, ld = 64, 128, 200
+    full = synth.normal_bf16(4, 1, (T, ld))
+    cu = synth.cu_seqlens([T])
+    d_ref, s_ref, _ = oracle.quantize(np.ascontiguousarray(full[:, :C]), cu, oracle.SQ32)
+    xd = to_dev_bf16(full)
+    data = torch.empty((T, C), dtype=torch.uint8, device="cuda")
+    scale = torch.empty((2, C // 32), dtype=torch.uint8, device="cuda")
+    mx.mxfa_quantize(xd, ld, T, C, cu_dev(cu), 1, T, mx.SQ32, data, scale)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(data.cpu().numpy(), d_ref)
+    np.testing.assert_array_equal(scale.cpu().numpy(), s_ref)
+
+
+@pytest.mark.parametrize("mode", [oracle.ROW32, oracle.COL32, oracle.SQ32])
+def test_scale_scatter_bit_exact(mode):
+    lens = [37, 128, 1, 300, 95, 256]
+    say(f"scatter mode={mode}")
+    cu = synth.cu_seqlens(lens)
+    T, C = int(cu[-1]), 256
+    x = synth.normal_bf16(5, 1, (T, C))
+    _, s_ref, _ = oracle.quantize(x, cu, mode)
+    p_ref = oracle.scale_scatter(s_ref, cu, C, mode)
+    cud = cu_dev(cu)
+    _, scale, _ = mx.quantize(to_dev_bf16(x), cu, cud, mode)
+    padded = mx.scale_scatter(scale, cu, cud, C, mode)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(padded.cpu().numpy(), p_ref)
+
+
+@pytest.mark.parametrize("lens", [[64], [37, 128, 1, 95]])
+def test_rmsnorm_quantize_bit_exact(lens):
+    say(f"rmsnorm lens={lens}")
+    cu = synth.cu_seqlens(lens)
+    T, C = int(cu[-1]), 1024
+    x = synth.normal_bf16(6, synth.STREAM_ACT, (T, C))
+    gamma = (1.0 + 0.1 * synth.normal(6, synth.STREAM_WEIGHT, C)).astype(np.float32)
+    d_ref, s_ref, st_ref, _ = oracle.rmsnorm_quantize(x, gamma, 1e-6, cu)
+    data, scale, scale_t = mx.rmsnorm_quantize(to_dev_bf16(x), torch.from_numpy(gamma).cuda(), 1e-6, cu, cu_dev(cu))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(data.cpu().numpy(), d_ref)
+    np.testing.assert_array_equal(scale.cpu().numpy(), s_ref)
+    np.testing.assert_array_equal(scale_t.cpu().numpy(), st_ref)
+
+
+FWD_CASES = [
+    # (label, seed, lens_q, lens_k, H, causal, outlier_p, modes)
+    ("tiny_N256_train", 1, [256], None, 1, False, 0.0, "train"),
+    ("N512_H2_fwdonly", 2, [512], None, 2, False, 0.0, "fwd"),
+    ("ragged_train", 3, [200, 77, 384, 1], None, 2, False, 0.0, "train"),
+    ("ragged_causal_outliers", 4, [300, 129, 512], None, 1, True, 0.005, "train"),
+    ("cross_lens", 5, [256, 64], [1000, 33], 1, False, 0.0, "fwd"),
+]
+
+
+@pytest.mark.parametrize("case", FWD_CASES, ids=[c[0] for c in FWD_CASES])
+def test_fwd_parity(case):
+    label, seed, lq, lk, H, causal, op, modes = case
+    say(f"fwd {label}")
+    c = AttnCase(seed, lq, lk, H=H, causal=causal, outlier_p=op, fwd_modes=modes)
+    o_gpu, lse_gpu = c.run_gpu_fwd()
+    _, o32, lse = c.run_oracle_fwd()
+    check_o(o_gpu, o32, lse_gpu, lse, label)
+
+
+def test_fwd_empty_key_sequence():
+    """A sequence with no keys gives O = 0 and LSE = -inf."""
+    say("fwd empty keys")
+    c = AttnCase(7, [128, 64], [256, 0], H=1, fwd_modes="fwd")
+    o_gpu, lse_gpu = c.run_gpu_fwd()
+    _, o32, lse = c.run_oracle_fwd()
+    check_o(o_gpu, o32, lse_gpu, lse, "empty_keys")
+    assert np.all(o_gpu[128:] == 0)
+
+
+BWD_CASES = [
+    # (label, seed, lens, H, causal, outlier_p, FP16 static scale sigma)
+    ("tiny_N256", 1, [256], 1, False, 0.0, 1.0),
+    ("N512_H2", 2, [512], 2, False, 0.0, 1.0),
+    ("ragged", 3, [200, 77, 384, 1], 2, False, 0.0, 1.0),
+    # x64 outliers make |dQ / c| reach ~1.5e5: sigma = 2^-4 keeps the FP16 accumulator finite
+    ("ragged_causal_outliers", 4, [300, 129, 512], 1, True, 0.005, 0.0625),
+]
+
+
+@pytest.mark.parametrize("dq_mode", [mx.DQ_FP32, mx.DQ_FP16_STATIC])
+@pytest.mark.parametrize("case", BWD_CASES, ids=[c[0] for c in BWD_CASES])
+def test_bwd_parity(case, dq_mode):
+    label, seed, lens, H, causal, op, sigma = case
+    say(f"bwd {label} dq_mode={dq_mode} sigma={sigma}")
+    c = AttnCase(seed, lens, None, H=H, causal=causal, outlier_p=op, fwd_modes="train")
+    o_gpu, lse_gpu = c.run_gpu_fwd()
+    c.run_oracle_fwd()
+    g = c.run_gpu_bwd(dq_mode, sigma)
+    ref = c.run_oracle_bwd(o_gpu, lse_gpu, dq_mode, sigma)
+    assert ref["overflow"] == 0
+    check_grads(g, ref, label)
+
+
+def test_bwd_fp16_sigma_scaling():
+    """sigma = 2^-4: FP16 accumulator holds sigma dQ; the finalize divides it out."""
+    say("bwd sigma")
+    c = AttnCase(8, [256], None, H=1)
+    o_gpu, lse_gpu = c.run_gpu_fwd()
+    c.run_oracle_fwd()
+    g = c.run_gpu_bwd(mx.DQ_FP16_STATIC, 0.0625)
+    ref = c.run_oracle_bwd(o_gpu, lse_gpu, 1, 0.0625)
+    check_grads(g, ref, "sigma")
+
+
+def test_bwd_fp32_deterministic_up_to_atomic_order():
+    """Two FP32-dQ runs differ at most by the reordering of FP32 atomic additions."""
+    say("bwd determinism")
+    c = AttnCase(9, [512], None, H=2)
+    c.run_gpu_fwd()
+    a = c.run_gpu_bwd(mx.DQ_FP32)
+    b = c.run_gpu_bwd(mx.DQ_FP32)
+    np.testing.assert_array_equal(a[1], b[1])  # dK, dV have no atomics: identical
+    np.testing.assert_array_equal(a[2], b[2])
+    da = synth.bf16_bits_to_f32(a[0]).astype(np.float64)
+    db = synth.bf16_bits_to_f32(b[0]).astype(np.float64)
+    assert np.max(np.abs(da - db)) <= 2 ** -6 * np.max(np.abs(da)) + 1e-6
