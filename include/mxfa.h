@@ -134,8 +134,8 @@ int64_t mxfa_padded_token_rows(const int32_t* cu_seqlens_host, int nseq);
  *   lse: fp32 [H][T_q]; rows of a sequence with no keys get O = 0 and LSE = -inf. */
 mxfa_status mxfa_fwd(const mxfa_attn_args* a, uint16_t* o, float* lse, void* stream);
 
-/* Workspace bytes mxfa_bwd needs: the dQ accumulator [T_q, H*D] (FP32 or FP16) plus
- * Delta [H][T_q] fp32, each 256-byte aligned. */
+/* Workspace bytes mxfa_bwd needs: the dQ accumulator [T_q, H*D] (FP32 or FP16) plus two fp32
+ * [H][T_q] row vectors (Delta and the softmax exponent offsets), each 256-byte aligned. */
 size_t mxfa_bwd_workspace_size(int64_t total_q, int num_heads, int head_dim, mxfa_dq_mode dq_mode);
 
 /* Attention backward with recomputation [AE-TMEM: five GEMMs; Q, K and dO in square 32x32 blocks

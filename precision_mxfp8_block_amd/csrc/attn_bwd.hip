@@ -23,7 +23,10 @@
 //  * dQ = dS K contracts over all 128 keys of the tile (all four waves): dS_q goes to LDS key-major,
 //    each wave then computes 32 query rows and adds them to the accumulator with coalesced atomics
 //    (packed FP16 pairs or FP32).
-//  * LDS tiles use the same 16-byte-chunk XOR swizzle as the forward.
+//  * Q and dO tiles (and the tile's LSE and Delta) are double-buffered in LDS and fetched one tile
+//    ahead with direct global -> LDS loads; all LDS tiles use the forward's XOR swizzle.
+//  * P is produced as 256 P straight from exp2 (the static scale folded into the exponent); dS is
+//    carried as 256 dS, which shifts its E8M0 code by exactly 8 (power-of-two scaling is exact).
 #include "mx_device.h"
 #include "mxfa_internal.h"
 
@@ -33,24 +36,44 @@ constexpr int kTile = 128;
 constexpr int kD = 128;
 constexpr float kLog2e = 1.4426950408889634f;
 
-__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row & 8) >> 1); }
+__device__ __forceinline__ int swz(int row) { return lds_swz(row); }
 
-__device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t total) {
-  const int64_t per = total / 8, rem = total % 8;
-  const int64_t x = bid % 8, slot = bid / 8;
+__device__ __forceinline__ int xcd_remap(int bid, int total) {
+  const int per = total >> 3, rem = total & 7;
+  const int x = bid & 7, slot = bid >> 3;
   return x * per + (x < rem ? x : rem) + slot;
 }
 
-// Copy a 128 x 128-byte tile (rows row0.. of a [T, C] payload, head h) into swizzled LDS; rows at or
-// past `valid` are zero.
-__device__ __forceinline__ void load_tile(uint8_t* lds, const uint8_t* g, int64_t row0, int valid, int C, int h) {
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Per-lane constants for filling a 128 x 128-byte swizzled LDS tile with direct global -> LDS loads:
+// lane piece c of wave w covers tile row trow[c], logical chunk byte offset tcol[c].
+struct TileLane {
+  int trow[4], tcol[4];
+  uint32_t toff[4];  // trow * C + tcol (full tiles)
+};
+
+__device__ __forceinline__ TileLane tile_lane(int wave, int lane, int C) {
+  TileLane t;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int i = threadIdx.x + 256 * j;
-    const int row = i >> 3, ch = i & 7;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (row < valid) v = *reinterpret_cast<const uint4*>(g + (row0 + row) * (int64_t)C + h * kD + 16 * ch);
-    *reinterpret_cast<uint4*>(lds + row * kD + 16 * (ch ^ swz(row))) = v;
+  for (int c = 0; c < 4; ++c) {
+    const int p = (wave * 4 + c) * 64 + lane;
+    t.trow[c] = p >> 3;
+    t.tcol[c] = 16 * ((p & 7) ^ swz(p >> 3));
+    t.toff[c] = (uint32_t)(t.trow[c] * C + t.tcol[c]);
+  }
+  return t;
+}
+
+// Asynchronous copy of a tile whose first row is at `base` (this head's columns). Rows at or past
+// `valid` re-fetch the last valid row (finite data; their contributions are masked to zero).
+__device__ __forceinline__ void issue_tile_load(uint8_t* lds_tile, const uint8_t* base, int valid, int C,
+                                                const TileLane& t, int wave_s) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const uint32_t off = valid >= kTile ? t.toff[c] : (uint32_t)(min(t.trow[c], valid - 1) * C + t.tcol[c]);
+    __builtin_amdgcn_global_load_lds((const void*)(base + off), (MX_LDS void*)(lds_tile + (wave_s * 4 + c) * 1024),
+                                     16, 0, 0);
   }
 }
 
@@ -80,14 +103,28 @@ __device__ __forceinline__ mx_v8i lds_tr_operand(const uint8_t* lds, int ks, int
   return mx_v8i{part[0].x, part[0].y, part[1].x, part[1].y, part[2].x, part[2].y, part[3].x, part[3].y};
 }
 
+// Maximum over the 64 lanes of a wave: DPP within rows of 16, one bpermute across rows, one
+// permlane32 swap across the halves.
+__device__ __forceinline__ uint32_t wave_max_dpp(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x140, 0xF, 0xF, false));  // row_mirror
+  v = max(v, (uint32_t)__shfl_xor((int)v, 16, 64));
+  auto s = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return max((uint32_t)s[0], (uint32_t)s[1]);
+}
+
 // ---------------------------------------------------------------------------------------------
-// Preprocess: Delta[h][t] = sum_d dO[t, h, d] * O[t, h, d] (fp32), and zero the dQ accumulator.
+// Preprocess: Delta[h][t] = sum_d dO[t, h, d] * O[t, h, d] (fp32); the exponent offset of 256 P,
+// b[h][t] = 8 - LSE[h][t] log2(e) (so 256 P = exp2(c log2(e) S + b)); and zero the dQ accumulator.
 // One wave per (token, head) row of 128: two bf16 pairs per lane.
 // ---------------------------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) bwd_preprocess_kernel(const uint16_t* __restrict__ o,
-                                                             const uint16_t* __restrict__ dout, int64_t T, int H,
-                                                             float* __restrict__ delta, uint32_t* __restrict__ acc,
-                                                             int64_t acc_words) {
+                                                             const uint16_t* __restrict__ dout,
+                                                             const float* __restrict__ lse, int64_t T, int H,
+                                                             float* __restrict__ delta, float* __restrict__ pexp,
+                                                             uint32_t* __restrict__ acc, int64_t acc_words) {
   const int64_t gw = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   const int lane = threadIdx.x & 63;
   if (gw < T * H) {
@@ -98,7 +135,10 @@ __global__ void __launch_bounds__(256) bwd_preprocess_kernel(const uint16_t* __r
     float sum = bf16_to_f32(a & 0xffffu) * bf16_to_f32(b & 0xffffu) + bf16_to_f32(a >> 16) * bf16_to_f32(b >> 16);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
-    if (lane == 0) delta[(int64_t)h * T + t] = sum;
+    if (lane == 0) {
+      delta[(int64_t)h * T + t] = sum;
+      pexp[(int64_t)h * T + t] = 8.0f - lse[(int64_t)h * T + t] * kLog2e;
+    }
   }
   // zero the accumulator (grid-stride over 16-byte words)
   const int64_t nthreads = (int64_t)gridDim.x * blockDim.x;
@@ -112,10 +152,10 @@ struct BwdParams {
   int v_row_shift;  // V along D: 0 ROW32, 5 SQ32
   const int32_t *cu_q, *cu_k;
   int nseq, H, n_ktiles;
-  int64_t total_items;
+  int total_items;
   float c2;  // c * log2(e)
   int causal;
-  const float* lse;    // [H][Tq]
+  const float* pexp;   // [H][Tq]: 8 - LSE log2(e)
   const float* delta;  // [H][Tq]
   int64_t Tq;
   int dq_fp16;
@@ -126,19 +166,17 @@ struct BwdParams {
 };
 
 __global__ void __launch_bounds__(256, 1) attn_bwd_kernel(BwdParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_k[kTile * kD];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_q[kTile * kD];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_do[kTile * kD];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_ds[kTile * kD];  // dS_q, key-major [kv][q]
-  __shared__ float lds_lse2[kTile];   // LSE * log2(e)
-  __shared__ float lds_delta[kTile];
-  __shared__ uint8_t lds_dscode[4][4];  // [kv block][q block]
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_k[kTile * kD];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_qd[2][2][kTile * kD];  // [stage][Q, dO]
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_ds[kTile * kD];        // dS_q, key-major [kv][q]
+  __shared__ __attribute__((aligned(512))) float lds_ld[2][2][kTile];          // [stage][8 - LSE log2e, Delta]
+  __shared__ uint32_t lds_dscode[4];                                           // [kv block] -> 4 q-block codes
   __shared__ int64_t red[16];
 
-  const int64_t item = xcd_remap(blockIdx.x, p.total_items);
-  const int kt = (int)(item % p.n_ktiles);
-  const int h = (int)((item / p.n_ktiles) % p.H);
-  const int s = (int)(item / ((int64_t)p.n_ktiles * p.H));
+  const int item = xcd_remap((int)blockIdx.x, p.total_items);
+  const int kt = item % p.n_ktiles;
+  const int h = (item / p.n_ktiles) % p.H;
+  const int s = item / (p.n_ktiles * p.H);
   const int64_t q_start = p.cu_q[s], k_start = p.cu_k[s];
   const int Lq = p.cu_q[s + 1] - (int)q_start;
   const int Lk = p.cu_k[s + 1] - (int)k_start;
@@ -148,14 +186,45 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_kernel(BwdParams p) {
   const SeqOffsets koff = seq_offsets(p.cu_k, s, red);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   const int r = lane & 31, hh = lane >> 5;
   const int C = p.H * kD;
   const int Cs = C >> 5;
   const int kv0 = kt * kTile;
   const int kvrow = kv0 + 32 * wave + r;  // this lane's key row (B operands of S and dP)
+  const TileLane tl = tile_lane(wave, lane, C);
 
-  // K tile in LDS (for dQ = dS K), and this wave's K and V rows in VGPRs
-  load_tile(lds_k, p.k, k_start + kv0, Lk - kv0, C, h);
+  const int n_qtiles = (Lq + kTile - 1) / kTile;
+  const int qt_begin = p.causal ? kt : 0;
+
+  const uint8_t* qbase = p.q + q_start * (int64_t)C + h * kD;
+  const uint8_t* dobase = p.dO + q_start * (int64_t)C + h * kD;
+  const float* lse_base = p.pexp + (int64_t)h * p.Tq + q_start;
+  const float* del_base = p.delta + (int64_t)h * p.Tq + q_start;
+  // exponent offsets and Delta of a query tile: waves 0 and 1 each copy one 128-float vector (one
+  // 4-byte element per lane, two pieces of 64 lanes).
+  auto issue_ld_load = [&](int st, int q0) {
+    if (wave_s < 2) {
+      const float* src = wave_s == 0 ? lse_base : del_base;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int row = min(q0 + c * 64 + lane, Lq - 1);
+        __builtin_amdgcn_global_load_lds((const void*)(src + row), (MX_LDS void*)(&lds_ld[st][wave_s][c * 64]), 4, 0,
+                                         0);
+      }
+    }
+  };
+
+  // prologue: K tile, the first Q/dO tile and its LSE/Delta
+  issue_tile_load(lds_k, p.k + (k_start + kv0) * (int64_t)C + h * kD, Lk - kv0, C, tl, wave_s);
+  if (qt_begin < n_qtiles) {
+    const int64_t q0 = (int64_t)qt_begin * kTile;
+    issue_tile_load(lds_qd[qt_begin & 1][0], qbase + q0 * C, Lq - (int)q0, C, tl, wave_s);
+    issue_tile_load(lds_qd[qt_begin & 1][1], dobase + q0 * C, Lq - (int)q0, C, tl, wave_s);
+    issue_ld_load(qt_begin & 1, (int)q0);
+  }
+
+  // this wave's K and V rows in VGPRs (B operands of S = Q K^T and dP = dO V^T)
   mx_v8i kb_op[2], vb_op[2];
   {
     const bool valid = kvrow < Lk;
@@ -181,6 +250,26 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_kernel(BwdParams p) {
   const uint32_t vsc_b =
       *reinterpret_cast<const uint32_t*>(p.v_scale + ((koff.padded + kvrow) >> p.v_row_shift) * (int64_t)Cs + h * 4) >>
       (8 * hh);
+  // K's scales for dQ = dS K (B operand: key block 2 ks + hh, d-block db): one word per key step
+  uint32_t kq_sc[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+    kq_sc[ks] =
+        *reinterpret_cast<const uint32_t*>(p.k_scale + ((koff.padded + kv0) / 32 + 2 * ks + hh) * (int64_t)Cs + h * 4);
+
+  // Q and dO scales of a query tile (SQ32): one word (4 d-blocks) per query block, raw
+  const uint8_t* qs_base = p.q_scale + (qoff.padded >> 5) * (int64_t)Cs + h * 4;
+  const uint8_t* ds_base = p.dO_scale + (qoff.padded >> 5) * (int64_t)Cs + h * 4;
+  uint32_t qsc[4], dosc[4];
+  auto load_q_scales = [&](int qt) {
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+      const uint32_t off = (uint32_t)((qt * 4 + qb) * Cs);
+      qsc[qb] = *reinterpret_cast<const uint32_t*>(qs_base + off);
+      dosc[qb] = *reinterpret_cast<const uint32_t*>(ds_base + off);
+    }
+  };
+  if (qt_begin < n_qtiles) load_q_scales(qt_begin);
 
   mx_v16f dk_acc[4], dv_acc[4];
 #pragma unroll
@@ -196,91 +285,119 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_kernel(BwdParams p) {
   const int tr_col = 16 * (grp & 1) + 8 * ts;
   const int tr_swz = swz(tr_row);
 
-  const int n_qtiles = (Lq + kTile - 1) / kTile;
-  const int qt_begin = p.causal ? kt : 0;
+  // dQ accumulator addressing: element (query row, column) of this head
+  float* dq32 = reinterpret_cast<float*>(p.dq_acc) + q_start * (int64_t)C + h * kD;
+  __half2* dq16 = reinterpret_cast<__half2*>(reinterpret_cast<__half*>(p.dq_acc) + q_start * (int64_t)C + h * kD);
+  const bool odd = r & 1;
+
+  wait_vm();
+  __syncthreads();
+
   for (int qt = qt_begin; qt < n_qtiles; ++qt) {
     const int q0 = qt * kTile;
-    __syncthreads();  // previous iteration's LDS readers are done
-    load_tile(lds_q, p.q, q_start + q0, Lq - q0, C, h);
-    load_tile(lds_do, p.dO, q_start + q0, Lq - q0, C, h);
-    if (tid < kTile) {
-      const int qi = q0 + tid;
-      lds_lse2[tid] = qi < Lq ? p.lse[(int64_t)h * p.Tq + q_start + qi] * kLog2e : 0.0f;
-      lds_delta[tid] = qi < Lq ? p.delta[(int64_t)h * p.Tq + q_start + qi] : 0.0f;
+    const int st = qt & 1;
+    const uint8_t* lds_q = lds_qd[st][0];
+    const uint8_t* lds_do = lds_qd[st][1];
+    const float* pexp = lds_ld[st][0];
+    const float* dlt = lds_ld[st][1];
+    // prefetch the next query tile
+    if (qt + 1 < n_qtiles) {
+      const int64_t nq0 = (int64_t)(q0 + kTile);
+      issue_tile_load(lds_qd[st ^ 1][0], qbase + nq0 * C, Lq - (int)nq0, C, tl, wave_s);
+      issue_tile_load(lds_qd[st ^ 1][1], dobase + nq0 * C, Lq - (int)nq0, C, tl, wave_s);
+      issue_ld_load(st ^ 1, (int)nq0);
     }
-    __syncthreads();
-
-    const int64_t qbrow0 = (qoff.padded + q0) >> 5;  // scale block row of query block 0 of this tile
 
     // ---- G1: S = Q K^T  and  G2: dP = dO V^T  (accumulator: key = column, 16 queries per lane) ----
     mx_v16f sacc[4], dpacc[4];
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
-      const uint32_t qsc =
-          *reinterpret_cast<const uint32_t*>(p.q_scale + (qbrow0 + qb) * (int64_t)Cs + h * 4) >> (8 * hh);
-      const uint32_t dosc =
-          *reinterpret_cast<const uint32_t*>(p.dO_scale + (qbrow0 + qb) * (int64_t)Cs + h * 4) >> (8 * hh);
-      sacc[qb] = mx_v16f{};
-      dpacc[qb] = mx_v16f{};
       const int row = 32 * qb + r;
+      const uint32_t qs = qsc[qb] >> (8 * hh), dss = dosc[qb] >> (8 * hh);
       mx_v8i qa0 = lds_row_operand(lds_q, row, 0, hh);
       mx_v8i qa1 = lds_row_operand(lds_q, row, 1, hh);
-      sacc[qb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa0, kb_op[0], sacc[qb], 0, 0, 0, (int)qsc, 0,
+      sacc[qb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa0, kb_op[0], mx_v16f{}, 0, 0, 0, (int)qs, 0,
                                                                  (int)ksc_b);
-      sacc[qb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa1, kb_op[1], sacc[qb], 0, 0, 2, (int)qsc, 2,
+      sacc[qb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa1, kb_op[1], sacc[qb], 0, 0, 2, (int)qs, 2,
                                                                  (int)ksc_b);
       mx_v8i da0 = lds_row_operand(lds_do, row, 0, hh);
       mx_v8i da1 = lds_row_operand(lds_do, row, 1, hh);
-      dpacc[qb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(da0, vb_op[0], dpacc[qb], 0, 0, 0, (int)dosc, 0,
+      dpacc[qb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(da0, vb_op[0], mx_v16f{}, 0, 0, 0, (int)dss, 0,
                                                                   (int)vsc_b);
-      dpacc[qb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(da1, vb_op[1], dpacc[qb], 0, 0, 2, (int)dosc, 2,
+      dpacc[qb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(da1, vb_op[1], dpacc[qb], 0, 0, 2, (int)dss, 2,
                                                                   (int)vsc_b);
     }
+    // raw Q and dO scales for the B operands of G3 and G4 (query block 2 ks + hh, d-block db)
+    uint32_t qsc_t[2], dosc_t[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      qsc_t[ks] = hh ? qsc[2 * ks + 1] : qsc[2 * ks];
+      dosc_t[ks] = hh ? dosc[2 * ks + 1] : dosc[2 * ks];
+    }
+    if (qt + 1 < n_qtiles) load_q_scales(qt + 1);
 
-    // ---- P, dS, and their E4M3 bytes (lane: key kvrow; queries 32 qb + 8 i + 4 hh + t) ----
-    uint32_t pk[4][4], dsk[4][4];
-    uint32_t dscode[4];
-    const bool kv_ok = kvrow < Lk;
+    // ---- 256 P, 256 dS (lane: key kvrow; queries 32 qb + 8 i + 4 hh + t) ----
+    const bool need_mask = (q0 + kTile > Lq) || (kv0 + kTile > Lk) || (p.causal && kv0 + kTile - 1 > q0);
+    uint32_t amax[4];
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
-      uint32_t amax = 0;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int ql = 32 * qb + 8 * (v >> 2) + 4 * hh + (v & 3);  // query row inside the tile
-        const bool ok = kv_ok && (q0 + ql < Lq) && !(p.causal && kvrow > q0 + ql);
-        const float pv = ok ? __builtin_amdgcn_exp2f(fmaf(sacc[qb][v], p.c2, -lds_lse2[ql])) : 0.0f;
-        const float dsv = pv * (dpacc[qb][v] - lds_delta[ql]);
-        sacc[qb][v] = pv;
-        dpacc[qb][v] = dsv;
-        amax = max(amax, __float_as_uint(dsv) & 0x7fffffffu);
-      }
-      amax = wave_max_u32(amax);
-      dscode[qb] = mx_code_from_amax_bits(amax);
-      const float inv = dscode[qb] == 255u ? 0.0f : mx_inv_scale(dscode[qb]);
+      uint32_t am = 0;
+      float4 pe4[4], dl4[4];  // the 16 query rows of this lane: 4 runs of 4 consecutive rows
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        pk[qb][i] = mx_pack4_inrange(sacc[qb][4 * i] * 256.0f, sacc[qb][4 * i + 1] * 256.0f,
-                                     sacc[qb][4 * i + 2] * 256.0f, sacc[qb][4 * i + 3] * 256.0f);
-        uint32_t w = mx_pack4(dpacc[qb][4 * i] * inv, dpacc[qb][4 * i + 1] * inv, dpacc[qb][4 * i + 2] * inv,
-                              dpacc[qb][4 * i + 3] * inv);
+        pe4[i] = *reinterpret_cast<const float4*>(pexp + 32 * qb + 8 * i + 4 * hh);
+        dl4[i] = *reinterpret_cast<const float4*>(dlt + 32 * qb + 8 * i + 4 * hh);
+      }
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int ql = 32 * qb + 8 * (v >> 2) + 4 * hh + (v & 3);
+        const float pe = (&pe4[v >> 2].x)[v & 3], dl = (&dl4[v >> 2].x)[v & 3];
+        float e = __builtin_amdgcn_exp2f(fmaf(sacc[qb][v], p.c2, pe));  // 256 P
+        if (need_mask) {
+          const bool ok = (kvrow < Lk) && (q0 + ql < Lq) && !(p.causal && kvrow > q0 + ql);
+          e = ok ? e : 0.0f;
+        }
+        const float dsv = e * (dpacc[qb][v] - dl);
+        sacc[qb][v] = e;
+        dpacc[qb][v] = dsv;
+        am = max(am, __float_as_uint(dsv) & 0x7fffffffu);
+      }
+      amax[qb] = am;
+    }
+    // block maxima over the wave (one 32 x 32 block per query block)
+    uint32_t dscode[4];
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+      const uint32_t c256 = mx_code_from_amax_bits(wave_max_dpp(amax[qb]));  // code of 256 dS
+      dscode[qb] = c256 == 255u ? 255u : (c256 > 8u ? c256 - 8u : 0u);        // code of dS
+    }
+    uint32_t pk[4][4], dsk[4][4];
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+      // 256 dS * 2^(127 - (code + 8)) = dS * 2^(127 - code); for code 0 the factor is 2^119
+      const float inv = dscode[qb] == 255u ? 0.0f : mx_inv_scale(dscode[qb] + 8u);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pk[qb][i] = mx_pack4_inrange(sacc[qb][4 * i], sacc[qb][4 * i + 1], sacc[qb][4 * i + 2], sacc[qb][4 * i + 3]);
+        const uint32_t w = mx_pack4(dpacc[qb][4 * i] * inv, dpacc[qb][4 * i + 1] * inv, dpacc[qb][4 * i + 2] * inv,
+                                    dpacc[qb][4 * i + 3] * inv);
         dsk[qb][i] = dscode[qb] == 255u ? 0x7f7f7f7fu : w;
       }
     }
 
-    // ---- dS_q to LDS, key-major [kv][q], for dQ ----
+    // ---- dS_q to LDS, key-major [kv][q], for dQ; codes of this wave's key block ----
     {
       const int kvl = 32 * wave + r;  // key row inside the tile
+      const int sw = swz(kvl);
 #pragma unroll
       for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int ql = 32 * qb + 8 * i + 4 * hh;
-          *reinterpret_cast<uint32_t*>(lds_ds + kvl * kD + 16 * ((ql >> 4) ^ swz(kvl)) + (ql & 15)) = dsk[qb][i];
+          *reinterpret_cast<uint32_t*>(lds_ds + kvl * kD + 16 * ((ql >> 4) ^ sw) + (ql & 15)) = dsk[qb][i];
         }
-      if (lane == 0) {
-#pragma unroll
-        for (int qb = 0; qb < 4; ++qb) lds_dscode[wave][qb] = (uint8_t)dscode[qb];
-      }
+      if (lane == 0)
+        lds_dscode[wave] = dscode[0] | (dscode[1] << 8) | (dscode[2] << 16) | (dscode[3] << 24);
     }
 
     // ---- G3: dV += P_q^T dO  and  G4: dK += dS_q^T Q  (contraction over 128 queries) ----
@@ -294,75 +411,85 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_kernel(BwdParams p) {
       const uint32_t sa_sc = hh ? dscode[2 * ks + 1] : dscode[2 * ks];
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        // B-operand scales (dO and Q, SQ32): query block 2 ks + hh, d-block db
-        const int64_t sidx = (qbrow0 + 2 * ks + hh) * (int64_t)Cs + h * 4 + db;
-        const uint32_t do_sc = p.dO_scale[sidx];
-        const uint32_t q_sc = p.q_scale[sidx];
         mx_v8i dob = lds_tr_operand(lds_do, ks, 32 * db, tr_row, tr_col, tr_swz);
-        dv_acc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(pa, dob, dv_acc[db], 0, 0, 0, 119, 0, (int)do_sc);
+        dv_acc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(pa, dob, dv_acc[db], 0, 0, 0, 119, 0,
+                                                                     (int)(dosc_t[ks] >> (8 * db)));
         mx_v8i qbt = lds_tr_operand(lds_q, ks, 32 * db, tr_row, tr_col, tr_swz);
         dk_acc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(sa, qbt, dk_acc[db], 0, 0, 0, (int)sa_sc, 0,
-                                                                     (int)q_sc);
+                                                                     (int)(qsc_t[ks] >> (8 * db)));
+        // Keep these MFMAs here (the compiler would otherwise sink them below the barrier and hold all
+        // of their operands in registers); the accumulators stay in AGPRs.
+        asm volatile("" : "+a"(dv_acc[db]), "+a"(dk_acc[db])::"memory");
       }
     }
     __syncthreads();  // dS_q of all four waves is in LDS
 
     // ---- G5: dQ rows 32 wave.. of this tile = dS_q K over the 128 keys; atomics ----
     {
-      const int qrow = q0 + 32 * wave;  // first query row of this wave's block
+      const int qr0 = q0 + 32 * wave;  // first query row of this wave's block
+      uint32_t a_sc[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) a_sc[ks] = lds_dscode[2 * ks + hh] >> (8 * wave);
+      mx_v8i dsa[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) dsa[ks] = lds_tr_operand(lds_ds, ks, 32 * wave, tr_row, tr_col, tr_swz);
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         mx_v16f acc = mx_v16f{};
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          mx_v8i dsa = lds_tr_operand(lds_ds, ks, 32 * wave, tr_row, tr_col, tr_swz);
           mx_v8i kbt = lds_tr_operand(lds_k, ks, 32 * db, tr_row, tr_col, tr_swz);
-          const uint32_t a_sc = lds_dscode[2 * ks + hh][wave];
-          const uint32_t b_sc = p.k_scale[((koff.padded + kv0) / 32 + 2 * ks + hh) * (int64_t)Cs + h * 4 + db];
-          acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(dsa, kbt, acc, 0, 0, 0, (int)a_sc, 0, (int)b_sc);
+          acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(dsa[ks], kbt, acc, 0, 0, 0, (int)a_sc[ks], 0,
+                                                                (int)(kq_sc[ks] >> (8 * db)));
         }
         // acc: column d = 32 db + r, rows q = 8 (v/4) + 4 hh + v%4 of the wave's 32-query block
-        const int d = h * kD + 32 * db + r;
         if (!p.dq_fp16) {
-          float* dst = reinterpret_cast<float*>(p.dq_acc);
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int qr = qrow + 8 * (v >> 2) + 4 * hh + (v & 3);
-            if (qr < Lq) unsafeAtomicAdd(dst + (q_start + qr) * (int64_t)C + d, acc[v]);
-          }
+#define MXFA_DQ32(V)                                                                              \
+  {                                                                                               \
+    const int qr = qr0 + 8 * ((V) >> 2) + 4 * hh + ((V) & 3);                                     \
+    if (qr < Lq) unsafeAtomicAdd(dq32 + (uint32_t)(qr * C + 32 * db + r), acc[V]);                \
+  }
+          MXFA_DQ32(0) MXFA_DQ32(1) MXFA_DQ32(2) MXFA_DQ32(3) MXFA_DQ32(4) MXFA_DQ32(5) MXFA_DQ32(6) MXFA_DQ32(7)
+          MXFA_DQ32(8) MXFA_DQ32(9) MXFA_DQ32(10) MXFA_DQ32(11) MXFA_DQ32(12) MXFA_DQ32(13) MXFA_DQ32(14)
+          MXFA_DQ32(15)
+#undef MXFA_DQ32
         } else {
-          // pair neighbouring columns: even lane takes (row v, d d+1), odd lane takes (row v+1, d-1 d)
-          __half2* dst = reinterpret_cast<__half2*>(p.dq_acc);
-          const bool odd = r & 1;
-#pragma unroll
-          for (int v = 0; v < 16; v += 2) {
-            const float mine_keep = odd ? acc[v + 1] : acc[v];
-            const float mine_send = odd ? acc[v] : acc[v + 1];
-            const float other = __shfl_xor(mine_send, 1, 64);
-            const float lo = odd ? other : mine_keep;  // column d (even)
-            const float hi = odd ? mine_keep : other;  // column d + 1
-            const int qr = qrow + 8 * (v >> 2) + 4 * hh + (v & 3) + (odd ? 1 : 0);
-            const int dcol = d - (odd ? 1 : 0);
-            if (qr < Lq) {
-              __half2 val = __floats2half2_rn(lo * p.sigma, hi * p.sigma);
-              unsafeAtomicAdd(dst + (((q_start + qr) * (int64_t)C + dcol) >> 1), val);
-            }
-          }
+          // pair neighbouring columns: the even lane takes (row v, columns d, d+1), the odd lane takes
+          // (row v+1, columns d-1, d); one exchange per pair
+#define MXFA_DQ16(V)                                                                              \
+  {                                                                                               \
+    const float keep = odd ? acc[(V) + 1] : acc[V];                                               \
+    const float send = odd ? acc[V] : acc[(V) + 1];                                               \
+    const float other = __shfl_xor(send, 1, 64);                                                  \
+    const float lo = odd ? other : keep;                                                          \
+    const float hi = odd ? keep : other;                                                          \
+    const int qr = qr0 + 8 * ((V) >> 2) + 4 * hh + ((V) & 3) + (odd ? 1 : 0);                     \
+    if (qr < Lq)                                                                                  \
+      unsafeAtomicAdd(dq16 + (uint32_t)((qr * C + 32 * db + r - (odd ? 1 : 0)) >> 1),            \
+                      __floats2half2_rn(lo * p.sigma, hi * p.sigma));                             \
+  }
+          MXFA_DQ16(0) MXFA_DQ16(2) MXFA_DQ16(4) MXFA_DQ16(6) MXFA_DQ16(8) MXFA_DQ16(10) MXFA_DQ16(12)
+          MXFA_DQ16(14)
+#undef MXFA_DQ16
         }
       }
     }
+    wait_vm();        // this thread's part of the next tile has landed
+    __syncthreads();  // everyone's; and all reads of this stage, dS_q and the codes are done
   }
 
   // ---- epilogue: dK = c dK, dV -> bf16 (accumulator: column d = 32 db + r, rows kv) ----
+  uint16_t* dkb = p.dk + (k_start + kv0 + 32 * wave) * (int64_t)C + h * kD;
+  uint16_t* dvb = p.dv + (k_start + kv0 + 32 * wave) * (int64_t)C + h * kD;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int kr = kv0 + 32 * wave + 8 * (v >> 2) + 4 * hh + (v & 3);
-      if (kr < Lk) {
-        const int64_t idx = (k_start + kr) * (int64_t)C + h * kD + 32 * db + r;
-        p.dk[idx] = (uint16_t)f32_to_bf16(dk_acc[db][v] * p.c);
-        p.dv[idx] = (uint16_t)f32_to_bf16(dv_acc[db][v]);
+      const int kr = 8 * (v >> 2) + 4 * hh + (v & 3);
+      if (kv0 + 32 * wave + kr < Lk) {
+        const uint32_t idx = (uint32_t)(kr * C + 32 * db + r);
+        dkb[idx] = (uint16_t)f32_to_bf16(dk_acc[db][v] * p.c);
+        dvb[idx] = (uint16_t)f32_to_bf16(dv_acc[db][v]);
       }
     }
 }
@@ -391,11 +518,12 @@ __global__ void __launch_bounds__(256) bwd_finalize_kernel(const void* __restric
 
 namespace mxfa {
 
+// Workspace: dQ accumulator [Tq, H*D] (fp32 or fp16), then Delta [H][Tq] and the exponent offsets
+// [H][Tq] (fp32), each 256-byte aligned.
 size_t bwd_workspace_bytes(int64_t Tq, int H, int D, int dq_fp16) {
   const size_t acc = (size_t)Tq * H * D * (dq_fp16 ? 2 : 4);
-  const size_t acc_al = (acc + 255) / 256 * 256;
-  const size_t del = (size_t)Tq * H * 4;
-  return acc_al + (del + 255) / 256 * 256;
+  const size_t vec = ((size_t)Tq * H * 4 + 255) / 256 * 256;
+  return (acc + 255) / 256 * 256 + 2 * vec;
 }
 
 hipError_t launch_attn_bwd(const AttnProblem& a, const MxOperand& v_d, const MxOperand& dout, const uint16_t* o,
@@ -407,13 +535,14 @@ hipError_t launch_attn_bwd(const AttnProblem& a, const MxOperand& v_d, const MxO
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
   void* acc = ws;
   float* delta = reinterpret_cast<float*>(ws + (acc_bytes + 255) / 256 * 256);
+  float* pexp = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(delta) + ((size_t)Tq * a.H * 4 + 255) / 256 * 256);
   {
     const int64_t rows = Tq * a.H;  // one wave per row
     int64_t blocks = (rows + 3) / 4;
     if (blocks < 1) blocks = 1;
     const int64_t acc_words = (int64_t)((acc_bytes + 15) / 16 * 4);
-    hipLaunchKernelGGL(bwd_preprocess_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, o, dout_bf16, Tq, a.H,
-                       delta, reinterpret_cast<uint32_t*>(acc), acc_words);
+    hipLaunchKernelGGL(bwd_preprocess_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, o, dout_bf16, lse, Tq,
+                       a.H, delta, pexp, reinterpret_cast<uint32_t*>(acc), acc_words);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -424,10 +553,10 @@ hipError_t launch_attn_bwd(const AttnProblem& a, const MxOperand& v_d, const MxO
   p.cu_q = a.cu_q; p.cu_k = a.cu_k;
   p.nseq = a.nseq; p.H = a.H;
   p.n_ktiles = (a.max_seqlen_k + kTile - 1) / kTile;
-  p.total_items = (int64_t)p.n_ktiles * a.H * a.nseq;
+  p.total_items = p.n_ktiles * a.H * a.nseq;  // < 2^31, checked by the caller
   p.c2 = a.softmax_scale * kLog2e;
   p.causal = a.causal;
-  p.lse = lse; p.delta = delta; p.Tq = Tq;
+  p.pexp = pexp; p.delta = delta; p.Tq = Tq;
   p.dq_fp16 = dq_fp16; p.sigma = sigma; p.dq_acc = acc;
   p.c = a.softmax_scale;
   p.dk = dk; p.dv = dv;

@@ -20,9 +20,8 @@
 //    block, which is all the block scale of V requires.
 //  * V^T is read from the row-major LDS tile with ds_read_b64_tr_b8 (8 keys x 1 column per lane per
 //    read), in exactly that key order.
-//  * LDS tiles are 128 rows x 128 bytes with the 16-byte chunk index XOR-swizzled by
-//    (row & 7) ^ ((row & 8) >> 1): conflict-free for the row reads of K and the transposed reads
-//    of V.
+//  * LDS tiles are 128 rows x 128 bytes with the 16-byte chunk index XOR-swizzled (lds_swz):
+//    conflict-free for the row reads of K and the transposed reads of V.
 //  * Grid order is XCD-aware: consecutive workgroup IDs land on different XCDs, so IDs are remapped
 //    to give each XCD a contiguous range of (sequence, head, tile) items; the query tiles of one
 //    head then share one XCD's L2, which holds that head's K and V.
@@ -48,7 +47,7 @@ struct FwdParams {
   const int32_t* cu_q;
   const int32_t* cu_k;
   int nseq, H, n_qtiles;
-  int64_t total_items;
+  int total_items;
   float c;   // softmax scale
   float c2;  // softmax scale * log2(e)
   int causal;
@@ -57,24 +56,43 @@ struct FwdParams {
   int64_t Tq;
 };
 
-__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row & 8) >> 1); }
+__device__ __forceinline__ int swz(int row) { return lds_swz(row); }
 
-// XCD-aware mapping of a linear workgroup id to a work item (bijective for any total).
-__device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t total) {
-  const int64_t per = total / 8, rem = total % 8;
-  const int64_t x = bid % 8, slot = bid / 8;
+// XCD-aware mapping of a linear workgroup id to a work item (bijective for any total < 2^31).
+__device__ __forceinline__ int xcd_remap(int bid, int total) {
+  const int per = total >> 3, rem = total & 7;
+  const int x = bid & 7, slot = bid >> 3;
   return x * per + (x < rem ? x : rem) + slot;
 }
 
-__global__ void __launch_bounds__(256, 1) attn_fwd_kernel(FwdParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_k[kTile * kD];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_v[kTile * kD];
+// Issue the asynchronous global -> LDS copy of one 128 x 128-byte tile into a swizzled LDS tile.
+// `base` is the wave-uniform address of the tile's first row (this head's columns); each wave
+// writes four contiguous 1 KB pieces (64 lanes x 16 bytes), and the swizzle is applied by choosing
+// which logical chunk each lane fetches: lane piece c covers row trow[c], logical chunk offset
+// tcol[c]. Rows past the end of the sequence fetch the last valid row instead (finite data; the
+// scores of those rows are masked and their P is exactly 0).
+__device__ __forceinline__ void issue_tile_load(uint8_t* lds_tile, const uint8_t* base, int valid, int C,
+                                                const int* trow, const int* tcol, const uint32_t* toff,
+                                                int wave_s) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const uint32_t off = valid >= kTile ? toff[c] : (uint32_t)(min(trow[c], valid - 1) * C + tcol[c]);
+    __builtin_amdgcn_global_load_lds((const void*)(base + off), (MX_LDS void*)(lds_tile + (wave_s * 4 + c) * 1024),
+                                     16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
+  // two stages x (K tile, V tile)
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2][2][kTile * kD];
   __shared__ int64_t red[16];
 
-  const int64_t item = xcd_remap(blockIdx.x, p.total_items);
-  const int qt = p.n_qtiles - 1 - (int)(item % p.n_qtiles);  // heavy (late) query tiles first
-  const int h = (int)((item / p.n_qtiles) % p.H);
-  const int s = (int)(item / ((int64_t)p.n_qtiles * p.H));
+  const int item = xcd_remap((int)blockIdx.x, p.total_items);
+  const int qt = p.n_qtiles - 1 - item % p.n_qtiles;  // heavy (late) query tiles first
+  const int h = (item / p.n_qtiles) % p.H;
+  const int s = item / (p.n_qtiles * p.H);
   const int64_t q_start = p.cu_q[s], k_start = p.cu_k[s];
   const int Lq = p.cu_q[s + 1] - (int)q_start;
   const int Lk = p.cu_k[s + 1] - (int)k_start;
@@ -86,7 +104,29 @@ __global__ void __launch_bounds__(256, 1) attn_fwd_kernel(FwdParams p) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r = lane & 31, hh = lane >> 5;
   const int C = p.H * kD;
-  const int Cs = C >> 5;  // scale bytes per row in the along-D layouts
+  const int Cs = C >> 5;
+
+  int n_ktiles = (Lk + kTile - 1) / kTile;
+  if (p.causal) {
+    const int q_last = min(qt * kTile + kTile - 1, Lq - 1);
+    n_ktiles = min(n_ktiles, q_last / kTile + 1);
+  }
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // wave index as a scalar
+  int trow[4], tcol[4];
+  uint32_t toff[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int pchunk = (wave * 4 + c) * 64 + lane;  // physical 16-byte chunk index in the tile
+    trow[c] = pchunk >> 3;
+    tcol[c] = 16 * ((pchunk & 7) ^ swz(pchunk >> 3));
+    toff[c] = (uint32_t)(trow[c] * C + tcol[c]);
+  }
+  const uint8_t* kbase = p.k + k_start * (int64_t)C + h * kD;
+  const uint8_t* vbase = p.v + k_start * (int64_t)C + h * kD;
+  if (n_ktiles > 0) {
+    issue_tile_load(lds[0][0], kbase, Lk, C, trow, tcol, toff, wave_s);
+    issue_tile_load(lds[0][1], vbase, Lk, C, trow, tcol, toff, wave_s);
+  }
 
   // ---- Q tile rows of this wave, held as the B operand of S^T = K Q^T ----
   const int qrow = qt * kTile + wave * 32 + r;  // position in the sequence
@@ -109,17 +149,40 @@ __global__ void __launch_bounds__(256, 1) attn_fwd_kernel(FwdParams p) {
       *reinterpret_cast<const uint32_t*>(p.q_scale + ((qoff.padded + qrow) >> p.q_row_shift) * (int64_t)Cs + h * 4) >>
       (8 * hh);
 
+  // K and V scales of a key tile: K along D per key row (4 rows per lane), V along the keys per
+  // column (8 per lane: 2 key steps x 4 D-blocks). The next tile's scales are loaded into the same
+  // registers right after their last use for the current tile.
+  // scale rows are addressed from wave-uniform bases with 32-bit per-lane offsets
+  const uint8_t* ksbase = p.k_scale + (koff.padded >> p.k_row_shift) * (int64_t)Cs + h * 4;
+  const uint8_t* vsbase = p.v_scale + (koff.padded >> 5) * (int64_t)(C >> p.v_col_shift);
+  const int vcs = C >> p.v_col_shift;
+  // (raw 4-byte words; the per-lane byte shift is applied at use, so that no instruction consumes a
+  // load before the end-of-tile wait, which would also wait for the in-flight tile prefetch)
+  auto load_k_scales = [&](int kv0, uint32_t* ksc) {
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+      ksc[kb] = *reinterpret_cast<const uint32_t*>(ksbase + (uint32_t)(((kv0 + 32 * kb + r) >> p.k_row_shift) * Cs));
+  };
+  auto load_v_scales = [&](int kv0, uint32_t* vsc) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int vrow = (kv0 + 64 * ks + 32 * hh) >> 5;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+        vsc[ks * 4 + db] = vsbase[(uint32_t)(vrow * vcs + ((h * kD + 32 * db + r) >> p.v_col_shift))];
+    }
+  };
+  uint32_t ksc[4], vsc[8];
+  if (n_ktiles > 0) {
+    load_k_scales(0, ksc);
+    load_v_scales(0, vsc);
+  }
+
   float m = -INFINITY;  // running max of raw scores for query row qrow
   float lsum = 0.0f;    // this lane's half of the row sum of P * 256
   mx_v16f oacc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) oacc[i] = mx_v16f{};
-
-  int n_ktiles = (Lk + kTile - 1) / kTile;
-  if (p.causal) {
-    const int q_last = min(qt * kTile + kTile - 1, Lq - 1);
-    n_ktiles = min(n_ktiles, q_last / kTile + 1);
-  }
 
   // per-lane constants of the transposed V read (see the lane map in mx_device.h)
   const int grp = lane >> 4, gl = lane & 15;
@@ -128,35 +191,26 @@ __global__ void __launch_bounds__(256, 1) attn_fwd_kernel(FwdParams p) {
   const int tr_col = 16 * (grp & 1) + 8 * ts;                    // + 32 dblk
   const int tr_swz = swz(tr_row);
 
+  wait_vm();
+  __syncthreads();
+
   for (int kt = 0; kt < n_ktiles; ++kt) {
     const int kv0 = kt * kTile;
-    __syncthreads();
-    // ---- K and V tiles: global -> LDS (16-byte chunks, swizzled) ----
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int i = tid + 256 * j;
-      const int row = i >> 3, ch = i & 7;
-      uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-      if (kv0 + row < Lk) {
-        const int64_t g = (k_start + kv0 + row) * (int64_t)C + h * kD + 16 * ch;
-        kv = *reinterpret_cast<const uint4*>(p.k + g);
-        vv = *reinterpret_cast<const uint4*>(p.v + g);
-      }
-      const int off = row * kD + 16 * (ch ^ swz(row));
-      *reinterpret_cast<uint4*>(lds_k + off) = kv;
-      *reinterpret_cast<uint4*>(lds_v + off) = vv;
+    const int st = kt & 1;
+    const uint8_t* lds_k = lds[st][0];
+    const uint8_t* lds_v = lds[st][1];
+    // prefetch the next tile (data straight into the other LDS stage, scales into VGPRs)
+    if (kt + 1 < n_ktiles) {
+      const int64_t next = (int64_t)(kv0 + kTile) * C;
+      issue_tile_load(lds[st ^ 1][0], kbase + next, Lk - kv0 - kTile, C, trow, tcol, toff, wave_s);
+      issue_tile_load(lds[st ^ 1][1], vbase + next, Lk - kv0 - kTile, C, trow, tcol, toff, wave_s);
     }
-    __syncthreads();
 
     // ---- S^T = K Q^T : 4 key blocks of 32 x 2 D-steps of 64 ----
     mx_v16f sacc[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const int row = 32 * kb + r;
-      const uint32_t ksc =
-          *reinterpret_cast<const uint32_t*>(p.k_scale + ((koff.padded + kv0 + row) >> p.k_row_shift) * (int64_t)Cs +
-                                             h * 4) >>
-          (8 * hh);
       sacc[kb] = mx_v16f{};
       const uint8_t* krow = lds_k + row * kD;
       const int sw = swz(row);
@@ -165,14 +219,18 @@ __global__ void __launch_bounds__(256, 1) attn_fwd_kernel(FwdParams p) {
         uint4 lo = *reinterpret_cast<const uint4*>(krow + 16 * ((4 * ds + hh) ^ sw));
         uint4 hi = *reinterpret_cast<const uint4*>(krow + 16 * ((4 * ds + 2 + hh) ^ sw));
         mx_v8i ka{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        const uint32_t kscb = ksc[kb] >> (8 * hh);
         if (ds == 0)
-          sacc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qa[0], sacc[kb], 0, 0, 0, (int)ksc, 0,
+          sacc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qa[0], sacc[kb], 0, 0, 0, (int)kscb, 0,
                                                                      (int)qsc);
         else
-          sacc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qa[1], sacc[kb], 0, 0, 2, (int)ksc, 2,
+          sacc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qa[1], sacc[kb], 0, 0, 2, (int)kscb, 2,
                                                                      (int)qsc);
       }
     }
+
+    if (kt + 1 < n_ktiles) load_k_scales(kv0 + kTile, ksc);
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---- mask (ragged tail, causal diagonal) ----
     const bool need_mask = (kv0 + kTile > Lk) || (p.causal && kv0 + kTile - 1 > qt * kTile + wave * 32);
@@ -191,15 +249,24 @@ __global__ void __launch_bounds__(256, 1) attn_fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kb][v]);
+      for (int v = 0; v < 16; v += 2) mx = max3f(mx, sacc[kb][v], sacc[kb][v + 1]);
     {
       auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
       mx = fmaxf(__uint_as_float(sw2[0]), __uint_as_float(sw2[1]));
     }
     const float m_new = fmaxf(m, mx);
     const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f((m - m_use) * p.c2);
     const float base = m_use * p.c2 - 8.0f;  // exp2(S c2 - base) = 256 P
+    // O and l need rescaling only where the row max moved; skip the multiplies when no row of the
+    // wave moved (exact either way)
+    if (__builtin_amdgcn_ballot_w64(m_new > m)) {
+      const float alpha = __builtin_amdgcn_exp2f((m - m_use) * p.c2);
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
+    }
     m = m_new;
     uint32_t pk[4][4];
     float ps = 0.0f;
@@ -214,19 +281,20 @@ __global__ void __launch_bounds__(256, 1) attn_fwd_kernel(FwdParams p) {
         ps += (e0 + e1) + (e2 + e3);
         pk[kb][i] = mx_pack4_inrange(e0, e1, e2, e3);
       }
-    lsum = lsum * alpha + ps;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
+    lsum += ps;
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---- O^T += V^T P^T : 2 key steps of 64 x 4 D-blocks of 32 ----
+    // Software-pipelined one step ahead: the transposed V reads of step i+1 are issued before the
+    // MFMA of step i; an empty asm statement that uses the MFMA result and clobbers memory keeps
+    // the compiler from hoisting further reads (which would hold all eight V operands in VGPRs).
+    {
+      mx_v8i pb[2];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      mx_v8i pb{(int)pk[2 * ks][0], (int)pk[2 * ks][1], (int)pk[2 * ks][2], (int)pk[2 * ks][3],
-                (int)pk[2 * ks + 1][0], (int)pk[2 * ks + 1][1], (int)pk[2 * ks + 1][2], (int)pk[2 * ks + 1][3]};
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
+      for (int ks = 0; ks < 2; ++ks)
+        pb[ks] = mx_v8i{(int)pk[2 * ks][0], (int)pk[2 * ks][1], (int)pk[2 * ks][2], (int)pk[2 * ks][3],
+                        (int)pk[2 * ks + 1][0], (int)pk[2 * ks + 1][1], (int)pk[2 * ks + 1][2], (int)pk[2 * ks + 1][3]};
+      auto read_v = [&](int ks, int db) {
         mx_v2i part[4];
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) {
@@ -235,14 +303,23 @@ __global__ void __launch_bounds__(256, 1) attn_fwd_kernel(FwdParams p) {
           const int off = row * kD + 16 * ((col >> 4) ^ tr_swz) + (col & 15);
           part[cc] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((MX_LDS mx_v2i*)(lds_v + off));
         }
-        mx_v8i va{part[0].x, part[0].y, part[1].x, part[1].y, part[2].x, part[2].y, part[3].x, part[3].y};
-        // V scale of key block (2 ks + hh), column 32 db + r
-        const int64_t vrow = (koff.padded + kv0 + 64 * ks + 32 * hh) >> 5;
-        const int vcol = (h * kD + 32 * db + r) >> p.v_col_shift;
-        const uint32_t vsc = p.v_scale[vrow * (int64_t)(C >> p.v_col_shift) + vcol];
-        oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, oacc[db], 0, 0, 0, (int)vsc, 0, 119);
+        return mx_v8i{part[0].x, part[0].y, part[1].x, part[1].y, part[2].x, part[2].y, part[3].x, part[3].y};
+      };
+      mx_v8i va_next = read_v(0, 0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int ks = i >> 2, db = i & 3;
+        const mx_v8i va = va_next;
+        if (i + 1 < 8) va_next = read_v((i + 1) >> 2, (i + 1) & 3);
+        oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb[ks], oacc[db], 0, 0, 0, (int)vsc[i], 0, 119);
+        // pin the MFMA here and keep later LDS reads below it
+        asm volatile("" : "+v"(oacc[db])::"memory");
       }
     }
+
+    if (kt + 1 < n_ktiles) load_v_scales(kv0 + kTile, vsc);
+    wait_vm();        // this thread's part of the next tile has landed in LDS
+    __syncthreads();  // ... everyone's, and nobody still reads the stage the next prefetch overwrites
   }
 
   // ---- epilogue: O / l -> bf16, LSE ----
@@ -281,7 +358,7 @@ hipError_t launch_attn_fwd(const AttnProblem& a, uint16_t* o, float* lse, hipStr
   p.cu_q = a.cu_q; p.cu_k = a.cu_k;
   p.nseq = a.nseq; p.H = a.H;
   p.n_qtiles = (a.max_seqlen_q + kTile - 1) / kTile;
-  p.total_items = (int64_t)p.n_qtiles * a.H * a.nseq;
+  p.total_items = p.n_qtiles * a.H * a.nseq;  // < 2^31, checked by the caller
   p.c = a.softmax_scale;
   p.c2 = a.softmax_scale * kLog2e;
   p.causal = a.causal;

@@ -70,6 +70,25 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+// max(a, b, c) in one v_max3_f32. Written as asm because the compiler, in IEEE mode, first
+// quiets (canonicalizes) every input that comes from an MFMA, which costs one extra instruction
+// per element; MFMA results are never signalling NaNs.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float d;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
+}
+
+// XOR swizzle of the 16-byte chunk index inside a 128-byte LDS row. With 64 four-byte banks, a
+// wave's 16-byte row reads (16 consecutive rows, one chunk) and the transposed 8-byte reads of
+// ds_read_b64_tr_b8 (rows {0-3, 8-11} or {4-7, 12-15} of a 16-row group, two adjacent chunks) both
+// touch 16 distinct (row parity, physical chunk) pairs, i.e. no bank conflicts. k = (row >> 1) & 7,
+// result = k with its two low bits exchanged.
+__device__ __forceinline__ int lds_swz(int row) {
+  const int k = (row >> 1) & 7;
+  return (k & 4) | ((k & 1) << 1) | ((k >> 1) & 1);
+}
+
 // Wave-wide (64 lanes) maximum of an unsigned value.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll

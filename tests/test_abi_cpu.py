@@ -131,9 +131,9 @@ def test_scatter_and_rmsnorm_argument_errors():
 
 
 def test_workspace_size_and_padded_rows():
-    # dQ accumulator fp32 [Tq, H*D] + Delta [H][Tq], each rounded up to 256 bytes
-    assert mx.mxfa_bwd_workspace_size(1000, 2, 128, 0) == 1000 * 256 * 4 + (8000 + 255) // 256 * 256
-    assert mx.mxfa_bwd_workspace_size(1000, 2, 128, 1) == 1000 * 256 * 2 + (8000 + 255) // 256 * 256
+    # dQ accumulator fp32/fp16 [Tq, H*D] + two fp32 [H][Tq] vectors, each rounded up to 256 bytes
+    assert mx.mxfa_bwd_workspace_size(1000, 2, 128, 0) == 1000 * 256 * 4 + 2 * ((8000 + 255) // 256 * 256)
+    assert mx.mxfa_bwd_workspace_size(1000, 2, 128, 1) == 1000 * 256 * 2 + 2 * ((8000 + 255) // 256 * 256)
     assert mx.mxfa_padded_token_rows(np.array([0, 1, 129, 129, 385], np.int32)) == 128 + 128 + 0 + 256
 
 
