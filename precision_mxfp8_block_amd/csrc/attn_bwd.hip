@@ -27,6 +27,9 @@
 //    ahead with direct global -> LDS loads; all LDS tiles use the forward's XOR swizzle.
 //  * P is produced as 256 P straight from exp2 (the static scale folded into the exponent); dS is
 //    carried as 256 dS, which shifts its E8M0 code by exactly 8 (power-of-two scaling is exact).
+#include <cmath>
+#include <type_traits>
+
 #include "mx_device.h"
 #include "mxfa_internal.h"
 
@@ -159,7 +162,7 @@ struct BwdParams {
   const float* delta;  // [H][Tq]
   int64_t Tq;
   int dq_fp16;
-  float sigma;
+  int log2_sigma;  // FP16 static scale sigma = 2^log2_sigma (0 in FP32 mode)
   void* dq_acc;  // [Tq, C] fp32 or fp16
   float c;
   uint16_t *dk, *dv;
@@ -308,25 +311,6 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_kernel(BwdParams p) {
       issue_ld_load(st ^ 1, (int)nq0);
     }
 
-    // ---- G1: S = Q K^T  and  G2: dP = dO V^T  (accumulator: key = column, 16 queries per lane) ----
-    mx_v16f sacc[4], dpacc[4];
-#pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
-      const int row = 32 * qb + r;
-      const uint32_t qs = qsc[qb] >> (8 * hh), dss = dosc[qb] >> (8 * hh);
-      mx_v8i qa0 = lds_row_operand(lds_q, row, 0, hh);
-      mx_v8i qa1 = lds_row_operand(lds_q, row, 1, hh);
-      sacc[qb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa0, kb_op[0], mx_v16f{}, 0, 0, 0, (int)qs, 0,
-                                                                 (int)ksc_b);
-      sacc[qb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa1, kb_op[1], sacc[qb], 0, 0, 2, (int)qs, 2,
-                                                                 (int)ksc_b);
-      mx_v8i da0 = lds_row_operand(lds_do, row, 0, hh);
-      mx_v8i da1 = lds_row_operand(lds_do, row, 1, hh);
-      dpacc[qb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(da0, vb_op[0], mx_v16f{}, 0, 0, 0, (int)dss, 0,
-                                                                  (int)vsc_b);
-      dpacc[qb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(da1, vb_op[1], dpacc[qb], 0, 0, 2, (int)dss, 2,
-                                                                  (int)vsc_b);
-    }
     // raw Q and dO scales for the B operands of G3 and G4 (query block 2 ks + hh, d-block db)
     uint32_t qsc_t[2], dosc_t[2];
 #pragma unroll
@@ -334,105 +318,156 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_kernel(BwdParams p) {
       qsc_t[ks] = hh ? qsc[2 * ks + 1] : qsc[2 * ks];
       dosc_t[ks] = hh ? dosc[2 * ks + 1] : dosc[2 * ks];
     }
+    uint32_t qsc_c[4], dosc_c[4];  // this tile's along-D scales for G1 and G2
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+      qsc_c[qb] = qsc[qb] >> (8 * hh);
+      dosc_c[qb] = dosc[qb] >> (8 * hh);
+    }
     if (qt + 1 < n_qtiles) load_q_scales(qt + 1);
-
-    // ---- 256 P, 256 dS (lane: key kvrow; queries 32 qb + 8 i + 4 hh + t) ----
     const bool need_mask = (q0 + kTile > Lq) || (kv0 + kTile > Lk) || (p.causal && kv0 + kTile - 1 > q0);
-    uint32_t amax[4];
-#pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
-      uint32_t am = 0;
-      float4 pe4[4], dl4[4];  // the 16 query rows of this lane: 4 runs of 4 consecutive rows
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pe4[i] = *reinterpret_cast<const float4*>(pexp + 32 * qb + 8 * i + 4 * hh);
-        dl4[i] = *reinterpret_cast<const float4*>(dlt + 32 * qb + 8 * i + 4 * hh);
-      }
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int ql = 32 * qb + 8 * (v >> 2) + 4 * hh + (v & 3);
-        const float pe = (&pe4[v >> 2].x)[v & 3], dl = (&dl4[v >> 2].x)[v & 3];
-        float e = __builtin_amdgcn_exp2f(fmaf(sacc[qb][v], p.c2, pe));  // 256 P
-        if (need_mask) {
-          const bool ok = (kvrow < Lk) && (q0 + ql < Lq) && !(p.causal && kvrow > q0 + ql);
-          e = ok ? e : 0.0f;
-        }
-        const float dsv = e * (dpacc[qb][v] - dl);
-        sacc[qb][v] = e;
-        dpacc[qb][v] = dsv;
-        am = max(am, __float_as_uint(dsv) & 0x7fffffffu);
-      }
-      amax[qb] = am;
-    }
-    // block maxima over the wave (one 32 x 32 block per query block)
-    uint32_t dscode[4];
-#pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
-      const uint32_t c256 = mx_code_from_amax_bits(wave_max_dpp(amax[qb]));  // code of 256 dS
-      dscode[qb] = c256 == 255u ? 255u : (c256 > 8u ? c256 - 8u : 0u);        // code of dS
-    }
-    uint32_t pk[4][4], dsk[4][4];
-#pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
-      // 256 dS * 2^(127 - (code + 8)) = dS * 2^(127 - code); for code 0 the factor is 2^119
-      const float inv = dscode[qb] == 255u ? 0.0f : mx_inv_scale(dscode[qb] + 8u);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pk[qb][i] = mx_pack4_inrange(sacc[qb][4 * i], sacc[qb][4 * i + 1], sacc[qb][4 * i + 2], sacc[qb][4 * i + 3]);
-        const uint32_t w = mx_pack4(dpacc[qb][4 * i] * inv, dpacc[qb][4 * i + 1] * inv, dpacc[qb][4 * i + 2] * inv,
-                                    dpacc[qb][4 * i + 3] * inv);
-        dsk[qb][i] = dscode[qb] == 255u ? 0x7f7f7f7fu : w;
-      }
-    }
+    uint32_t codes = 0;  // dS codes of the four query blocks, one byte each
 
-    // ---- dS_q to LDS, key-major [kv][q], for dQ; codes of this wave's key block ----
-    {
-      const int kvl = 32 * wave + r;  // key row inside the tile
-      const int sw = swz(kvl);
+    // Two halves of 64 queries (query blocks 2 ks, 2 ks + 1): the 64-query contraction step of G3/G4.
+    // Software pipeline inside the wave: the S and dP MFMAs of half 1 are issued before the
+    // elementwise work of half 0, so the matrix core runs them while the VALU works.
+    auto g12 = [&](int ks, mx_v16f* sacc, mx_v16f* dpacc) {
 #pragma unroll
-      for (int qb = 0; qb < 4; ++qb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int ql = 32 * qb + 8 * i + 4 * hh;
-          *reinterpret_cast<uint32_t*>(lds_ds + kvl * kD + 16 * ((ql >> 4) ^ sw) + (ql & 15)) = dsk[qb][i];
-        }
-      if (lane == 0)
-        lds_dscode[wave] = dscode[0] | (dscode[1] << 8) | (dscode[2] << 16) | (dscode[3] << 24);
-    }
-
-    // ---- G3: dV += P_q^T dO  and  G4: dK += dS_q^T Q  (contraction over 128 queries) ----
+      for (int j = 0; j < 2; ++j) {
+        const int qb = 2 * ks + j;
+        const int row = 32 * qb + r;
+        mx_v8i qa0 = lds_row_operand(lds_q, row, 0, hh);
+        mx_v8i qa1 = lds_row_operand(lds_q, row, 1, hh);
+        sacc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa0, kb_op[0], mx_v16f{}, 0, 0, 0, (int)qsc_c[qb], 0,
+                                                                  (int)ksc_b);
+        sacc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa1, kb_op[1], sacc[j], 0, 0, 2, (int)qsc_c[qb], 2,
+                                                                  (int)ksc_b);
+        mx_v8i da0 = lds_row_operand(lds_do, row, 0, hh);
+        mx_v8i da1 = lds_row_operand(lds_do, row, 1, hh);
+        dpacc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(da0, vb_op[0], mx_v16f{}, 0, 0, 0, (int)dosc_c[qb],
+                                                                   0, (int)vsc_b);
+        dpacc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(da1, vb_op[1], dpacc[j], 0, 0, 2, (int)dosc_c[qb], 2,
+                                                                   (int)vsc_b);
+        // issue order: these MFMAs stay here, ahead of the elementwise work that follows
+        asm volatile("" : "+v"(sacc[j]), "+v"(dpacc[j])::"memory");
+      }
+    };
+    mx_v16f sacc_h[2][2], dpacc_h[2][2];
+    g12(0, sacc_h[0], dpacc_h[0]);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      mx_v8i pa{(int)pk[2 * ks][0], (int)pk[2 * ks][1], (int)pk[2 * ks][2], (int)pk[2 * ks][3],
-                (int)pk[2 * ks + 1][0], (int)pk[2 * ks + 1][1], (int)pk[2 * ks + 1][2], (int)pk[2 * ks + 1][3]};
-      mx_v8i sa{(int)dsk[2 * ks][0], (int)dsk[2 * ks][1], (int)dsk[2 * ks][2], (int)dsk[2 * ks][3],
-                (int)dsk[2 * ks + 1][0], (int)dsk[2 * ks + 1][1], (int)dsk[2 * ks + 1][2], (int)dsk[2 * ks + 1][3]};
-      // A-operand scale of dS_q: k-block hh of this step is query block 2 ks + hh
-      const uint32_t sa_sc = hh ? dscode[2 * ks + 1] : dscode[2 * ks];
+      if (ks == 0) g12(1, sacc_h[1], dpacc_h[1]);
+      mx_v16f* sacc = sacc_h[ks];
+      mx_v16f* dpacc = dpacc_h[ks];
+
+      // ---- 256 P, 256 dS (lane: key kvrow; queries 32 qb + 8 i + 4 hh + t) ----
+      // Two instantiations behind one wave-uniform branch: interior tiles carry no mask code.
+      uint32_t pk[2][4], dsk[2][4], dscode[2];
+      auto elementwise = [&](auto masked) {
+        constexpr bool MASK = decltype(masked)::value;
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        mx_v8i dob = lds_tr_operand(lds_do, ks, 32 * db, tr_row, tr_col, tr_swz);
-        dv_acc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(pa, dob, dv_acc[db], 0, 0, 0, 119, 0,
-                                                                     (int)(dosc_t[ks] >> (8 * db)));
-        mx_v8i qbt = lds_tr_operand(lds_q, ks, 32 * db, tr_row, tr_col, tr_swz);
-        dk_acc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(sa, qbt, dk_acc[db], 0, 0, 0, (int)sa_sc, 0,
-                                                                     (int)(qsc_t[ks] >> (8 * db)));
-        // Keep these MFMAs here (the compiler would otherwise sink them below the barrier and hold all
-        // of their operands in registers); the accumulators stay in AGPRs.
-        asm volatile("" : "+a"(dv_acc[db]), "+a"(dk_acc[db])::"memory");
+        for (int j = 0; j < 2; ++j) {
+          const int qb = 2 * ks + j;
+          uint32_t am = 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            // the lane's 4 consecutive query rows 32 qb + 8 i + 4 hh + (0..3)
+            const float4 pe4 = *reinterpret_cast<const float4*>(pexp + 32 * qb + 8 * i + 4 * hh);
+            const float4 dl4 = *reinterpret_cast<const float4*>(dlt + 32 * qb + 8 * i + 4 * hh);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const int v = 4 * i + t;
+              const float pe = (&pe4.x)[t], dl = (&dl4.x)[t];
+              float e = __builtin_amdgcn_exp2f(fmaf(sacc[j][v], p.c2, pe));  // 256 P
+              if (MASK) {
+                const int qpos = q0 + 32 * qb + 8 * i + 4 * hh + t;
+                const bool ok = (kvrow < Lk) & (qpos < Lq) & ((p.causal == 0) | (kvrow <= qpos));
+                e = ok ? e : 0.0f;
+              }
+              const float dsv = e * (dpacc[j][v] - dl);  // 256 dS
+              sacc[j][v] = e;
+              dpacc[j][v] = dsv;
+              am = max(am, __float_as_uint(dsv) & 0x7fffffffu);
+            }
+          }
+          // block maximum over the wave (one 32 x 32 block), code of dS = code of 256 dS - 8
+          const uint32_t c256 = mx_code_from_amax_bits(wave_max_dpp(am));
+          dscode[j] = c256 == 255u ? 255u : (c256 > 8u ? c256 - 8u : 0u);
+          // 256 dS * 2^(127 - (code + 8)) = dS * 2^(127 - code)
+          const float inv = dscode[j] == 255u ? 0.0f : mx_inv_scale(dscode[j] + 8u);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            pk[j][i] = mx_pack4_inrange(sacc[j][4 * i], sacc[j][4 * i + 1], sacc[j][4 * i + 2], sacc[j][4 * i + 3]);
+            const uint32_t w = mx_pack4(dpacc[j][4 * i] * inv, dpacc[j][4 * i + 1] * inv, dpacc[j][4 * i + 2] * inv,
+                                        dpacc[j][4 * i + 3] * inv);
+            dsk[j][i] = dscode[j] == 255u ? 0x7f7f7f7fu : w;
+          }
+        }
+      };
+      if (need_mask)
+        elementwise(std::true_type{});
+      else
+        elementwise(std::false_type{});
+      codes |= (dscode[0] << (16 * ks)) | (dscode[1] << (16 * ks + 8));
+
+      // ---- dS_q to LDS, key-major [kv][q], for dQ ----
+      {
+        const int kvl = 32 * wave + r;  // key row inside the tile
+        const int sw = swz(kvl);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int ql = 32 * (2 * ks + j) + 8 * i + 4 * hh;
+            *reinterpret_cast<uint32_t*>(lds_ds + kvl * kD + 16 * ((ql >> 4) ^ sw) + (ql & 15)) = dsk[j][i];
+          }
+      }
+
+      // ---- G3: dV += P_q^T dO  and  G4: dK += dS_q^T Q  (this 64-query step) ----
+      {
+        mx_v8i pa{(int)pk[0][0], (int)pk[0][1], (int)pk[0][2], (int)pk[0][3],
+                  (int)pk[1][0], (int)pk[1][1], (int)pk[1][2], (int)pk[1][3]};
+        mx_v8i sa{(int)dsk[0][0], (int)dsk[0][1], (int)dsk[0][2], (int)dsk[0][3],
+                  (int)dsk[1][0], (int)dsk[1][1], (int)dsk[1][2], (int)dsk[1][3]};
+        // A-operand scale of dS_q: k-block hh of this step is query block 2 ks + hh
+        const uint32_t sa_sc = hh ? dscode[1] : dscode[0];
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          mx_v8i dob = lds_tr_operand(lds_do, ks, 32 * db, tr_row, tr_col, tr_swz);
+          dv_acc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(pa, dob, dv_acc[db], 0, 0, 0, 119, 0,
+                                                                       (int)(dosc_t[ks] >> (8 * db)));
+          mx_v8i qbt = lds_tr_operand(lds_q, ks, 32 * db, tr_row, tr_col, tr_swz);
+          dk_acc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(sa, qbt, dk_acc[db], 0, 0, 0, (int)sa_sc, 0,
+                                                                       (int)(qsc_t[ks] >> (8 * db)));
+          // Keep these MFMAs here (the compiler would otherwise sink them below the barrier and hold
+          // all of their operands in registers); the accumulators stay in AGPRs.
+          asm volatile("" : "+a"(dv_acc[db]), "+a"(dk_acc[db])::"memory");
+        }
       }
     }
+    if (lane == 0) lds_dscode[wave] = codes;
     __syncthreads();  // dS_q of all four waves is in LDS
+    // This thread's part of the next query tile has landed (and the previous tile's dQ atomics,
+    // which had a whole iteration to drain, are done); this tile's atomics stay in flight.
+    wait_vm();
 
     // ---- G5: dQ rows 32 wave.. of this tile = dS_q K over the 128 keys; atomics ----
+    // The FP16 static scale sigma (a power of two) is folded into dS_q's E8M0 code here, so the MFMA
+    // returns sigma dQ exactly with no multiply.
     {
-      const int qr0 = q0 + 32 * wave;  // first query row of this wave's block
       uint32_t a_sc[2];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) a_sc[ks] = lds_dscode[2 * ks + hh] >> (8 * wave);
+      for (int ks = 0; ks < 2; ++ks) {
+        const int c = (int)((lds_dscode[2 * ks + hh] >> (8 * wave)) & 0xffu);
+        a_sc[ks] = c == 255 ? 255u : (uint32_t)min(max(c + p.log2_sigma, 0), 254);
+      }
       mx_v8i dsa[2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) dsa[ks] = lds_tr_operand(lds_ds, ks, 32 * wave, tr_row, tr_col, tr_swz);
+      // rows of the wave's block: 8 (v/4) + 4 hh + v%4; the v-dependent part is a scalar offset
+      const int qr0 = q0 + 32 * wave;
+      const bool full = qr0 + 32 <= Lq;  // wave-uniform: no row of this block is past the sequence
+      const uint32_t lane_row = (uint32_t)(4 * hh);
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         mx_v16f acc = mx_v16f{};
@@ -442,40 +477,43 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_kernel(BwdParams p) {
           acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(dsa[ks], kbt, acc, 0, 0, 0, (int)a_sc[ks], 0,
                                                                 (int)(kq_sc[ks] >> (8 * db)));
         }
-        // acc: column d = 32 db + r, rows q = 8 (v/4) + 4 hh + v%4 of the wave's 32-query block
+        // acc: column d = 32 db + r, rows 8 (v/4) + 4 hh + v%4 of the wave's 32-query block
         if (!p.dq_fp16) {
+          const uint32_t lane_off = lane_row * C + 32 * db + r;
 #define MXFA_DQ32(V)                                                                              \
   {                                                                                               \
-    const int qr = qr0 + 8 * ((V) >> 2) + 4 * hh + ((V) & 3);                                     \
-    if (qr < Lq) unsafeAtomicAdd(dq32 + (uint32_t)(qr * C + 32 * db + r), acc[V]);                \
+    const int rv = 8 * ((V) >> 2) + ((V) & 3);                                                    \
+    float* rowp = dq32 + (size_t)(qr0 + rv) * C; /* wave-uniform */                               \
+    if (full || qr0 + rv + (int)lane_row < Lq) unsafeAtomicAdd(rowp + lane_off, acc[V]);          \
   }
           MXFA_DQ32(0) MXFA_DQ32(1) MXFA_DQ32(2) MXFA_DQ32(3) MXFA_DQ32(4) MXFA_DQ32(5) MXFA_DQ32(6) MXFA_DQ32(7)
           MXFA_DQ32(8) MXFA_DQ32(9) MXFA_DQ32(10) MXFA_DQ32(11) MXFA_DQ32(12) MXFA_DQ32(13) MXFA_DQ32(14)
           MXFA_DQ32(15)
 #undef MXFA_DQ32
         } else {
-          // pair neighbouring columns: the even lane takes (row v, columns d, d+1), the odd lane takes
-          // (row v+1, columns d-1, d); one exchange per pair
+          // Pair neighbouring columns: the even lane adds (row v, columns d, d+1), the odd lane adds
+          // (row v+1, columns d-1, d). One DPP swap with the neighbour lane per pair.
+          const uint32_t lane_off = (lane_row + (odd ? 1u : 0u)) * (uint32_t)(C >> 1) + (uint32_t)((32 * db + r) >> 1);
 #define MXFA_DQ16(V)                                                                              \
   {                                                                                               \
-    const float keep = odd ? acc[(V) + 1] : acc[V];                                               \
     const float send = odd ? acc[V] : acc[(V) + 1];                                               \
-    const float other = __shfl_xor(send, 1, 64);                                                  \
-    const float lo = odd ? other : keep;                                                          \
-    const float hi = odd ? keep : other;                                                          \
-    const int qr = qr0 + 8 * ((V) >> 2) + 4 * hh + ((V) & 3) + (odd ? 1 : 0);                     \
-    if (qr < Lq)                                                                                  \
-      unsafeAtomicAdd(dq16 + (uint32_t)((qr * C + 32 * db + r - (odd ? 1 : 0)) >> 1),            \
-                      __floats2half2_rn(lo * p.sigma, hi * p.sigma));                             \
+    const float other = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), 0xB1, 0xF, 0xF, false)); \
+    const float lo = odd ? other : acc[V];                                                        \
+    const float hi = odd ? acc[(V) + 1] : other;                                                  \
+    const int rv = 8 * ((V) >> 2) + ((V) & 3);                                                    \
+    __half2* rowp = dq16 + (size_t)(qr0 + rv) * (C >> 1); /* wave-uniform */                      \
+    if (full || qr0 + rv + (int)lane_row + (odd ? 1 : 0) < Lq)                                    \
+      unsafeAtomicAdd(rowp + lane_off, __floats2half2_rn(lo, hi));                                \
   }
           MXFA_DQ16(0) MXFA_DQ16(2) MXFA_DQ16(4) MXFA_DQ16(6) MXFA_DQ16(8) MXFA_DQ16(10) MXFA_DQ16(12)
           MXFA_DQ16(14)
 #undef MXFA_DQ16
         }
+        asm volatile("" ::: "memory");  // the next D-block's operand reads stay below these atomics
       }
     }
-    wait_vm();        // this thread's part of the next tile has landed
-    __syncthreads();  // everyone's; and all reads of this stage, dS_q and the codes are done
+    __syncthreads();  // every thread's part of the next tile has landed; all reads of this stage,
+                      // of dS_q and of the codes are done
   }
 
   // ---- epilogue: dK = c dK, dV -> bf16 (accumulator: column d = 32 db + r, rows kv) ----
@@ -557,7 +595,13 @@ hipError_t launch_attn_bwd(const AttnProblem& a, const MxOperand& v_d, const MxO
   p.c2 = a.softmax_scale * kLog2e;
   p.causal = a.causal;
   p.pexp = pexp; p.delta = delta; p.Tq = Tq;
-  p.dq_fp16 = dq_fp16; p.sigma = sigma; p.dq_acc = acc;
+  p.dq_fp16 = dq_fp16;
+  {
+    int e = 0;
+    std::frexp(dq_fp16 ? sigma : 1.0f, &e);  // sigma = 0.5 * 2^e exactly (a power of two, checked by the caller)
+    p.log2_sigma = e - 1;
+  }
+  p.dq_acc = acc;
   p.c = a.softmax_scale;
   p.dk = dk; p.dv = dv;
   if (p.total_items > 0) {
