@@ -165,6 +165,23 @@ mxfa_status mxfa_rmsnorm_quantize(const uint16_t* x, int64_t ld_x, int64_t T, in
                                   const int32_t* cu_seqlens, int nseq, int max_seqlen, uint8_t* data_out,
                                   uint8_t* scale_out, uint8_t* scale_t_out, void* stream);
 
+/* Fused projection GEMM + quantize producer [AE-TMEM: quantization fused into the epilogue of the
+ * projection GEMM, no separate global-memory pass; BR item 7: FP8 output with dual scale layouts in
+ * one pass]. Y = deq(x) deq(w)^T accumulated in FP32, then SQ32 quantization of Y exactly as
+ * mxfa_quantize does it (token blocks aligned to sequence starts). Y itself is never stored.
+ *   x          : [T, C_in] payload with compact SQ32 (or ROW32) scales, e.g. from
+ *                mxfa_rmsnorm_quantize
+ *   w          : [C_out, C_in] payload with ROW32 scales [C_out][C_in/32] (1 x 32 along C_in)
+ *   C_in, C_out: multiples of 128 (C_out = heads * head_dim: the output is [T, heads, head_dim])
+ *   cu_seqlens, nseq, max_seqlen : as mxfa_quantize (device cu_seqlens, host sizes)
+ *   data_out [T, C_out]; scale_out [NB][C_out/32]; scale_t_out nullable, [C_out/32][NB].
+ * The FP32 accumulation order is the hardware's, so a payload byte or scale can differ from a
+ * correctly rounded Y where Y lies within rounding of an E4M3 midpoint or a block maximum within
+ * rounding of a power of two. */
+mxfa_status mxfa_linear_quantize(mxfa_mx x, mxfa_mx w, int64_t T, int C_in, int C_out, const int32_t* cu_seqlens,
+                                 int nseq, int max_seqlen, uint8_t* data_out, uint8_t* scale_out,
+                                 uint8_t* scale_t_out, void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* mxfa_status_string(mxfa_status s);
 

@@ -65,9 +65,10 @@ def _load():
     lib.orc_attn_bwd_mx.argtypes = [P, P, P, P, P, P, i32, P, P, P, P, P, P, P, i32, i32, i32, f32, i32, i32, f32,
                                     P, P, P, P, P, P, P, i32]
     lib.orc_rmsnorm_quantize.argtypes = [P, i64, i64, i32, P, f32, P, i32, P, P, P, P]
+    lib.orc_linear_quantize.argtypes = [P, P, i32, P, P, i64, i32, i32, P, i32, P, P, P, P, i32]
     for name in ["orc_quantize_bf16", "orc_quantize_f32", "orc_dequantize", "orc_scale_scatter",
                  "orc_attn_fwd_f64", "orc_attn_fwd_mx", "orc_attn_bwd_f64", "orc_attn_bwd_mx",
-                 "orc_rmsnorm_quantize"]:
+                 "orc_rmsnorm_quantize", "orc_linear_quantize"]:
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -276,4 +277,23 @@ def rmsnorm_quantize(x_bf16, gamma, eps, cu):
     rc = lib.orc_rmsnorm_quantize(_p(x), C, T, C, _p(gamma), eps, _p(cu), cu.size - 1, _p(data), _p(scale),
                                   _p(scale_t), _p(y))
     _check(rc, "rmsnorm_quantize")
+    return data, scale, scale_t, y
+
+
+def linear_quantize(x, x_scale, w, w_scale, cu, x_mode=SQ32, nthreads=None):
+    """x [T, C_in] payload with SQ32 compact (or ROW32) scales; w [C_out, C_in] payload with ROW32 scales.
+    Returns (data [T, C_out], scale [NB, C_out/32], scale_t [C_out/32, NB], y float32 [T, C_out])."""
+    lib = _load()
+    cu = _c(cu, np.int32)
+    x, xs, w, ws = (_c(a, np.uint8) for a in (x, x_scale, w, w_scale))
+    T, C_in = x.shape
+    C_out = w.shape[0]
+    nb = num_blockrows(cu)
+    data = np.empty((T, C_out), np.uint8)
+    scale = np.empty((nb, C_out // 32), np.uint8)
+    scale_t = np.empty((C_out // 32, nb), np.uint8)
+    y = np.empty((T, C_out), np.float32)
+    rc = lib.orc_linear_quantize(_p(x), _p(xs), int(x_mode), _p(w), _p(ws), T, C_in, C_out, _p(cu), cu.size - 1, _p(data),
+                                 _p(scale), _p(scale_t), _p(y), nthreads or default_threads())
+    _check(rc, "linear_quantize")
     return data, scale, scale_t, y

@@ -737,4 +737,36 @@ int orc_rmsnorm_quantize(const uint16_t* x, int64_t ld, int64_t T, int C, const 
   return 0;
 }
 
+// Fused projection GEMM + quantize producer [AE TMEM: quantization fused into the projection GEMM
+// epilogue; BR item 7: FP8 output with dual scale layouts in one pass]. READING A12:
+//   Y = fl32(sum_k deq(X)_tk deq(W)_nk)  (X [T, C_in] SQ32 compact or ROW32, W [C_out, C_in] ROW32
+//   along C_in)
+//   then SQ32 quantization of Y with token blocks aligned to sequence starts; scales written in
+//   [NB][C_out/32] and transposed [C_out/32][NB]. y_out (may be NULL) receives Y.
+// The GPU accumulates in a different FP32 order, so its bytes may differ where Y lies within
+// rounding of an E4M3 midpoint or a block maximum within rounding of a power of two; the test
+// certifies every such byte from y_out and the exact products.
+// Pinned by: W = I (exact) reproduces X's own SQ32 quantization; small-integer products are exact;
+// Y equals a library matmul of the dequantized operands.
+int orc_linear_quantize(const uint8_t* x, const uint8_t* x_scale, int x_mode, const uint8_t* w,
+                        const uint8_t* w_scale, int64_t T, int C_in, int C_out, const int32_t* cu, int nseq,
+                        uint8_t* data, uint8_t* scale, uint8_t* scale_t, float* y_out, int nthreads) {
+  if (C_in % 32 || C_out % 32 || !valid_cu(cu, nseq, T) || (x_mode != SQ32 && x_mode != ROW32)) return -1;
+  std::vector<double> xd((size_t)T * C_in), wd((size_t)C_out * C_in), y((size_t)T * C_out);
+  dequantize_matrix(x, x_scale, T, C_in, cu, nseq, x_mode, xd.data());
+  const int32_t wcu[2] = {0, C_out};
+  dequantize_matrix(w, w_scale, C_out, C_in, wcu, 1, ROW32, wd.data());
+  parallel_units((int)T, nthreads, [&](int t) {
+    for (int n = 0; n < C_out; ++n) {
+      double acc = 0.0;
+      for (int k = 0; k < C_in; ++k) acc += xd[(size_t)t * C_in + k] * wd[(size_t)n * C_in + k];
+      y[(size_t)t * C_out + n] = fl32(acc);
+    }
+  });
+  if (y_out)
+    for (int64_t i = 0; i < T * C_out; ++i) y_out[i] = (float)y[i];
+  quantize_matrix(y.data(), T, C_out, cu, nseq, SQ32, data, scale, scale_t);
+  return 0;
+}
+
 }  // extern "C"

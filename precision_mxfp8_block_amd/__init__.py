@@ -4,7 +4,7 @@ The functions named mxfa_* are the C ABI of include/mxfa.h, one to one: they onl
 tensors (device memory) and Python numbers into pointers and integers and raise MxfaError on a
 non-OK status. Every step of the computation runs in the HIP kernels of libmxfa.so; there is no
 fallback path. The allocate-and-call helpers at the end (quantize, scale_scatter, fwd, bwd,
-rmsnorm_quantize) size the output tensors with torch and call the same entry points.
+rmsnorm_quantize, linear_quantize) size the output tensors with torch and call the same entry points.
 """
 import ctypes
 import os
@@ -14,8 +14,9 @@ import torch
 __all__ = [
     "ROW32", "COL32", "SQ32", "DQ_FP32", "DQ_FP16_STATIC", "MxfaError",
     "mxfa_quantize", "mxfa_varlen_scale_scatter", "mxfa_padded_token_rows", "mxfa_fwd", "mxfa_bwd",
-    "mxfa_bwd_workspace_size", "mxfa_rmsnorm_quantize", "mxfa_status_string", "mxfa_last_error_message",
-    "MxOperand", "AttnArgs", "quantize", "scale_scatter", "fwd", "bwd", "rmsnorm_quantize",
+    "mxfa_bwd_workspace_size", "mxfa_rmsnorm_quantize", "mxfa_linear_quantize", "mxfa_status_string",
+    "mxfa_last_error_message", "MxOperand", "AttnArgs", "quantize", "scale_scatter", "fwd", "bwd",
+    "rmsnorm_quantize", "linear_quantize",
     "library_path",
 ]
 
@@ -65,11 +66,13 @@ def _load():
     lib.mxfa_bwd_workspace_size.restype = ctypes.c_size_t
     lib.mxfa_bwd.argtypes = [ctypes.POINTER(_AttnArgs), _Mx, _Mx, P, P, P, i32, f32, P, ctypes.c_size_t, P, P, P, P]
     lib.mxfa_rmsnorm_quantize.argtypes = [P, i64, i64, i32, P, f32, P, i32, i32, P, P, P, P]
+    lib.mxfa_linear_quantize.argtypes = [_Mx, _Mx, i64, i32, i32, P, i32, i32, P, P, P, P]
     lib.mxfa_status_string.argtypes = [i32]
     lib.mxfa_status_string.restype = ctypes.c_char_p
     lib.mxfa_last_error_message.argtypes = []
     lib.mxfa_last_error_message.restype = ctypes.c_char_p
-    for n in ("mxfa_quantize", "mxfa_varlen_scale_scatter", "mxfa_fwd", "mxfa_bwd", "mxfa_rmsnorm_quantize"):
+    for n in ("mxfa_quantize", "mxfa_varlen_scale_scatter", "mxfa_fwd", "mxfa_bwd", "mxfa_rmsnorm_quantize",
+              "mxfa_linear_quantize"):
         getattr(lib, n).restype = i32
     _lib = lib
     return lib
@@ -254,4 +257,27 @@ def rmsnorm_quantize(x_bf16, gamma, eps, cu_host, cu_dev, want_scale_t=True, str
     scale_t = torch.empty((C // 32, nb), dtype=torch.uint8, device=dev) if want_scale_t else None
     mxfa_rmsnorm_quantize(x_bf16, x_bf16.stride(0), T, C, gamma, eps, cu_dev, len(lens), max(lens) if lens else 0,
                           data, scale, scale_t, stream)
+    return data, scale, scale_t
+
+
+def mxfa_linear_quantize(x, w, T, C_in, C_out, cu_seqlens, nseq, max_seqlen, data_out, scale_out, scale_t_out=None,
+                         stream=None):
+    """x, w: MxOperand (x SQ32 or ROW32 compact scales, w ROW32)."""
+    _check(_load().mxfa_linear_quantize(x._c(), w._c(), T, C_in, C_out, _ptr(cu_seqlens), nseq, max_seqlen,
+                                        _ptr(data_out), _ptr(scale_out), _ptr(scale_t_out), _stream(stream)),
+           "mxfa_linear_quantize")
+
+
+def linear_quantize(x, w, cu_host, cu_dev, want_scale_t=True, stream=None):
+    """Projection + SQ32 quantize: returns (data [T, C_out], scale [NB, C_out/32], scale_t or None)."""
+    T, C_in = x.data.shape
+    C_out = w.data.shape[0]
+    lens = _lens(cu_host)
+    dev = x.data.device
+    nb = _blockrows(lens)
+    data = torch.empty((T, C_out), dtype=torch.uint8, device=dev)
+    scale = torch.empty((nb, C_out // 32), dtype=torch.uint8, device=dev)
+    scale_t = torch.empty((C_out // 32, nb), dtype=torch.uint8, device=dev) if want_scale_t else None
+    mxfa_linear_quantize(x, w, T, C_in, C_out, cu_dev, len(lens), max(lens) if lens else 0, data, scale, scale_t,
+                         stream)
     return data, scale, scale_t

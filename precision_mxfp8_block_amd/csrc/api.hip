@@ -241,4 +241,30 @@ mxfa_status mxfa_rmsnorm_quantize(const uint16_t* x, int64_t ld_x, int64_t T, in
                     fn);
 }
 
+mxfa_status mxfa_linear_quantize(mxfa_mx x, mxfa_mx w, int64_t T, int C_in, int C_out, const int32_t* cu_seqlens,
+                                 int nseq, int max_seqlen, uint8_t* data_out, uint8_t* scale_out,
+                                 uint8_t* scale_t_out, void* stream) {
+  const char* fn = "mxfa_linear_quantize";
+  if (T < 0) return fail(MXFA_ERR_INVALID, "%s: T < 0", fn);
+  if (C_in <= 0 || C_in % 128 || C_in > 65536)
+    return fail(MXFA_ERR_INVALID, "%s: C_in=%d must be a multiple of 128 in [128, 65536]", fn, C_in);
+  if (C_out <= 0 || C_out % 128) return fail(MXFA_ERR_INVALID, "%s: C_out=%d must be a positive multiple of 128", fn, C_out);
+  if (x.mode != MXFA_SQ32 && x.mode != MXFA_ROW32) return fail(MXFA_ERR_INVALID, "%s: x.mode must be SQ32 or ROW32", fn);
+  if (w.mode != MXFA_ROW32) return fail(MXFA_ERR_INVALID, "%s: w.mode must be ROW32 (scales along C_in)", fn);
+  if (!x.data || !x.scale || !w.data || !w.scale || !data_out || !scale_out)
+    return fail(MXFA_ERR_INVALID, "%s: NULL argument", fn);
+  if (!aligned(x.data, 16) || !aligned(x.scale, 16) || !aligned(w.data, 16) || !aligned(w.scale, 16) ||
+      !aligned(data_out, 16) || !aligned(scale_out, 16) || (scale_t_out && !aligned(scale_t_out, 16)))
+    return fail(MXFA_ERR_INVALID, "%s: misaligned argument", fn);
+  mxfa_status st = check_jagged(cu_seqlens, nseq, max_seqlen, T, fn);
+  if (st != MXFA_OK) return st;
+  if ((int64_t)nseq * ((max_seqlen + 127) / 128) * (C_out / 128) >= ((int64_t)1 << 31))
+    return fail(MXFA_ERR_INVALID, "%s: problem too large for one launch", fn);
+  mxfa::MxOperand xx{x.data, x.scale, (int)x.mode};
+  mxfa::MxOperand ww{w.data, w.scale, (int)w.mode};
+  return hip_status(mxfa::launch_linear_quantize(xx, ww, T, C_in, C_out, cu_seqlens, nseq, max_seqlen, data_out,
+                                                 scale_out, scale_t_out, (hipStream_t)stream),
+                    fn);
+}
+
 }  // extern "C"

@@ -1,0 +1,242 @@
+// Fused projection GEMM + MX quantize producer for gfx950: Y = deq(X) deq(W)^T on scaled MFMA with
+// FP32 accumulation, and an epilogue that quantizes Y in 32 x 32 square blocks and writes both
+// scale layouts.
+//
+// What is computed (andresseo.expert "MXFP8 FlashAttention-4 Hits 2.85 Petaflops...", section
+// "Inside the TMEM Bargain and Zero-Gather Jagged Pipeline": the quantization moves into the
+// epilogue of the projection GEMM, so no separate pass over Y in global memory; brifing.si item 7:
+// FP8 output with the scales in both layouts from one pass):
+//   X [T, C_in] E4M3 with SQ32 (or ROW32) scales, W [C_out, C_in] E4M3 with 1 x 32 scales along
+//   C_in, Y = sum_k deq(X)_tk deq(W)_nk in FP32; per 32 x 32 block of Y (token blocks start at
+//   sequence starts, a sequence's last block may be partial): code = clamp(expbits(amax) - 8, 0,
+//   254), payload = E4M3_RNE_sat(Y 2^(127 - code)); scales [NB][C_out/32] and [C_out/32][NB].
+//
+// gfx950 design:
+//  * Workgroup = 4 waves = 128 tokens of one sequence x 128 output columns (one attention head when
+//    the head size is 128). Wave w owns token block w, so each of its four 32 x 32 accumulators is
+//    exactly one output scale block and the block maximum is a wave-wide reduction.
+//  * The product is computed transposed, Y^T = W X^T (A = W rows, B = X rows, both read from LDS
+//    as 16-byte row pieces): the accumulator gives each lane one token and 4 x 4 consecutive
+//    output columns, i.e. four 4-byte payload stores per block.
+//  * X and W chunks of 128 x 128 bytes are double-buffered in LDS (direct global -> LDS loads,
+//    XOR-swizzled chunks) and fetched one chunk of C_in ahead; the E8M0 scales of the next chunk
+//    are fetched into registers at the same time.
+//  * Items are (sequence, token tile, column tile) with the column tile fastest, remapped so that
+//    each XCD works on a contiguous item range: the column tiles of one token tile then share one
+//    L2, which serves the X tile to all of them.
+#include "mx_device.h"
+#include "mxfa_internal.h"
+
+namespace {
+
+constexpr int kTile = 128;   // tokens and output columns per workgroup
+constexpr int kChunk = 128;  // bytes of C_in per LDS stage
+
+struct LinearParams {
+  const uint8_t* x;
+  const uint8_t* x_scale;
+  int x_row_shift;  // 5: SQ32 (a scale row per 32 tokens), 0: ROW32 (a scale row per token)
+  const uint8_t* w;
+  const uint8_t* w_scale;
+  const int32_t* cu;
+  int nseq, tiles_per_seq, n_coltiles, total_items;
+  int C_in, C_out;
+  uint8_t* data;
+  uint8_t* scale;
+  uint8_t* scale_t;
+};
+
+__device__ __forceinline__ int xcd_remap(int bid, int total) {
+  const int per = total >> 3, rem = total & 7;
+  const int x = bid & 7, slot = bid >> 3;
+  return x * per + (x < rem ? x : rem) + slot;
+}
+
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Global -> LDS copy of a 128-row x 128-byte chunk (row stride ld bytes) into a swizzled LDS tile;
+// rows at or past `valid` re-fetch the last valid row (finite data, never stored).
+__device__ __forceinline__ void issue_chunk_load(uint8_t* lds_tile, const uint8_t* base, int valid, int ld,
+                                                 const int* trow, const int* tcol, int wave_s) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const uint32_t off = (uint32_t)(min(trow[c], valid - 1) * ld + tcol[c]);
+    __builtin_amdgcn_global_load_lds((const void*)(base + off), (MX_LDS void*)(lds_tile + (wave_s * 4 + c) * 1024),
+                                     16, 0, 0);
+  }
+}
+
+// Operand of a 32x32x64 MFMA from row `row` of a swizzled LDS tile, 64-byte step ds.
+__device__ __forceinline__ mx_v8i lds_row_operand(const uint8_t* lds, int row, int ds, int hh) {
+  const uint8_t* p = lds + row * kChunk;
+  const int sw = lds_swz(row);
+  uint4 lo = *reinterpret_cast<const uint4*>(p + 16 * ((4 * ds + hh) ^ sw));
+  uint4 hi = *reinterpret_cast<const uint4*>(p + 16 * ((4 * ds + 2 + hh) ^ sw));
+  return mx_v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
+// Maximum over the 64 lanes of a wave (DPP inside rows of 16, then across rows and halves).
+__device__ __forceinline__ uint32_t wave_max_dpp(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x140, 0xF, 0xF, false));  // row_mirror
+  v = max(v, (uint32_t)__shfl_xor((int)v, 16, 64));
+  auto s = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return max((uint32_t)s[0], (uint32_t)s[1]);
+}
+
+__global__ void __launch_bounds__(256, 2) linear_quantize_kernel(LinearParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2][2][kTile * kChunk];  // stage x (X, W)
+  __shared__ int64_t red[16];
+
+  const int item = xcd_remap((int)blockIdx.x, p.total_items);
+  const int ct = item % p.n_coltiles;
+  const int tt = (item / p.n_coltiles) % p.tiles_per_seq;
+  const int s = item / (p.n_coltiles * p.tiles_per_seq);
+  const int64_t start = p.cu[s];
+  const int L = p.cu[s + 1] - (int)start;
+  const int t0 = tt * kTile;
+  if (t0 >= L) return;  // uniform over the workgroup
+  const int valid = min(kTile, L - t0);
+  const int64_t br0 = seq_offsets(p.cu, s, red).blocks32 + (t0 >> 5);  // first 32-token block row
+  const int64_t nb_total = p.scale_t ? seq_offsets(p.cu, p.nseq, red).blocks32 : 0;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int r = lane & 31, hh = lane >> 5;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const int ldw = p.C_in;            // row stride of X and W in bytes
+  const int lds_s = p.C_in >> 5;     // scale row length in bytes (both X and W)
+  int trow[4], tcol[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int pc = (wave * 4 + c) * 64 + lane;
+    trow[c] = pc >> 3;
+    tcol[c] = 16 * ((pc & 7) ^ lds_swz(pc >> 3));
+  }
+  const uint8_t* xbase = p.x + (start + t0) * (int64_t)ldw;
+  const uint8_t* wbase = p.w + (int64_t)ct * kTile * ldw;
+
+  // Scale rows: W rows 32 j + r of this column tile; X: the wave's token block (SQ32) or the lane's
+  // token (ROW32), clamped into the sequence (clamped rows are never stored).
+  const int tok = min(wave * 32 + r, valid - 1);
+  const int64_t xs_row = p.x_row_shift ? br0 + (min(wave * 32, valid - 1) >> 5) : start + t0 + tok;
+  const uint32_t* xs_ptr = reinterpret_cast<const uint32_t*>(p.x_scale + xs_row * lds_s);
+  const uint32_t* ws_ptr[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    ws_ptr[j] = reinterpret_cast<const uint32_t*>(p.w_scale + ((int64_t)ct * kTile + 32 * j + r) * lds_s);
+
+  const int nchunks = p.C_in / kChunk;
+  uint32_t xsc = xs_ptr[0], wsc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) wsc[j] = ws_ptr[j][0];
+  issue_chunk_load(lds[0][0], xbase, valid, ldw, trow, tcol, wave_s);
+  issue_chunk_load(lds[0][1], wbase, kTile, ldw, trow, tcol, wave_s);
+  wait_vm();
+  __syncthreads();
+
+  mx_v16f acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = mx_v16f{};
+
+  for (int c = 0; c < nchunks; ++c) {
+    const int st = c & 1;
+    uint32_t xsn = 0, wsn[4] = {0, 0, 0, 0};
+    if (c + 1 < nchunks) {
+      xsn = xs_ptr[c + 1];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) wsn[j] = ws_ptr[j][c + 1];
+      issue_chunk_load(lds[st ^ 1][0], xbase + (c + 1) * kChunk, valid, ldw, trow, tcol, wave_s);
+      issue_chunk_load(lds[st ^ 1][1], wbase + (c + 1) * kChunk, kTile, ldw, trow, tcol, wave_s);
+    }
+    const uint32_t xs_l = xsc >> (8 * hh);
+#pragma unroll
+    for (int ds = 0; ds < 2; ++ds) {
+      const mx_v8i xb = lds_row_operand(lds[st][0], wave * 32 + r, ds, hh);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const mx_v8i wa = lds_row_operand(lds[st][1], 32 * j + r, ds, hh);
+        const uint32_t ws_l = wsc[j] >> (8 * hh);
+        if (ds == 0)
+          acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wa, xb, acc[j], 0, 0, 0, (int)ws_l, 0, (int)xs_l);
+        else
+          acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wa, xb, acc[j], 0, 0, 2, (int)ws_l, 2, (int)xs_l);
+        asm volatile("" : "+v"(acc[j])::"memory");
+      }
+    }
+    wait_vm();
+    __syncthreads();
+    xsc = xsn;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) wsc[j] = wsn[j];
+  }
+
+  // ---- epilogue: one 32 x 32 output block per accumulator ----
+  if (wave * 32 >= valid) return;  // token block entirely past the sequence end (no barrier below)
+  const bool live = wave * 32 + r < valid;
+  const int64_t br = br0 + wave;
+  const int ncs = p.C_out >> 5;
+  uint8_t* drow = p.data + (start + t0 + wave * 32 + r) * (int64_t)p.C_out + ct * kTile + 4 * hh;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t m = 0;
+    if (live) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) m = max(m, __float_as_uint(acc[j][v]) & 0x7fffffffu);
+    }
+    m = wave_max_dpp(m);
+    const uint32_t code = mx_code_from_amax_bits(m);
+    uint32_t words[4];
+    if (code == 255u) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) words[i] = 0x7f7f7f7fu;
+    } else {
+      const float inv = mx_inv_scale(code);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        words[i] = mx_pack4(acc[j][4 * i] * inv, acc[j][4 * i + 1] * inv, acc[j][4 * i + 2] * inv,
+                            acc[j][4 * i + 3] * inv);
+    }
+    if (live) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) *reinterpret_cast<uint32_t*>(drow + 32 * j + 8 * i) = words[i];
+    }
+    if (lane == 0) {
+      const int cb = ct * 4 + j;
+      p.scale[br * ncs + cb] = (uint8_t)code;
+      if (p.scale_t) p.scale_t[(int64_t)cb * nb_total + br] = (uint8_t)code;
+    }
+  }
+}
+
+}  // namespace
+
+namespace mxfa {
+
+hipError_t launch_linear_quantize(const MxOperand& x, const MxOperand& w, int64_t T, int C_in, int C_out,
+                                  const int32_t* cu, int nseq, int max_seqlen, uint8_t* data,
+                                  uint8_t* scale, uint8_t* scale_t, hipStream_t stream) {
+  LinearParams p;
+  p.x = x.data;
+  p.x_scale = x.scale;
+  p.x_row_shift = x.mode == 2 ? 5 : 0;
+  p.w = w.data;
+  p.w_scale = w.scale;
+  p.cu = cu;
+  p.nseq = nseq;
+  p.tiles_per_seq = (max_seqlen + kTile - 1) / kTile;
+  p.n_coltiles = C_out / kTile;
+  p.C_in = C_in;
+  p.C_out = C_out;
+  p.data = data;
+  p.scale = scale;
+  p.scale_t = scale_t;
+  const int64_t items = (int64_t)nseq * p.tiles_per_seq * p.n_coltiles;
+  if (T == 0 || items == 0) return hipSuccess;
+  p.total_items = (int)items;
+  hipLaunchKernelGGL(linear_quantize_kernel, dim3((unsigned)items), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace mxfa

@@ -11,6 +11,9 @@ Box-Muller transform; values are rounded to bf16 with round-to-nearest-even.
 Streams (fixed order): 0 lengths, 1 Q, 2 K, 3 V, 4 dO, 5 outlier masks (+ tensor index),
 8 weights (+ index), 16 activations (+ index).
 """
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 GOLDEN = np.uint64(0x9E3779B97F4A7C15)
@@ -40,10 +43,11 @@ def uniform(seed, stream, n, offset=0):
     return ((r >> np.uint64(11)).astype(np.float64) + 0.5) * (1.0 / 9007199254740992.0)
 
 
-def normal(seed, stream, n):
-    """Standard normal doubles by Box-Muller over pairs of uniforms."""
+def normal(seed, stream, n, offset=0):
+    """Standard normal doubles by Box-Muller over pairs of uniforms (draws 2*offset' onwards for
+    an even element offset, so any even-aligned chunk reproduces the same values)."""
     m = (n + 1) // 2
-    u = uniform(seed, stream, 2 * m)
+    u = uniform(seed, stream, 2 * m, offset)
     u1, u2 = u[0::2], u[1::2]
     r = np.sqrt(-2.0 * np.log(u1))
     z = np.empty(2 * m)
@@ -66,16 +70,38 @@ def bf16_bits_to_f32(b):
     return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
+_CHUNK = 1 << 20  # elements per worker chunk (even, so Box-Muller pairs never straddle chunks)
+
+
+def _normal_bf16_chunk(seed, stream, start, n, std, outlier_p, outlier_mult, os_):
+    x = (normal(seed, stream, n, offset=start) * std).astype(np.float32)
+    if outlier_p > 0:
+        mask = uniform(seed, os_, n, offset=start) < outlier_p
+        x[mask] *= np.float32(outlier_mult)
+    return f32_to_bf16_bits(x)
+
+
 def normal_bf16(seed, stream, shape, std=1.0, outlier_p=0.0, outlier_mult=64.0, outlier_stream=None):
     """bf16 bits of N(0, std^2) values; each entry independently (probability outlier_p) is
-    multiplied by outlier_mult in fp32 before the bf16 rounding."""
+    multiplied by outlier_mult in fp32 before the bf16 rounding. Element i always takes draws
+    2*floor(i/2)+{1,2} of the value stream and draw i+1 of the outlier stream, so large tensors are
+    generated in parallel chunks with identical results."""
     n = int(np.prod(shape))
-    x = (normal(seed, stream, n) * std).astype(np.float32)
-    if outlier_p > 0:
-        os_ = outlier_stream if outlier_stream is not None else STREAM_OUTLIER * 8 + stream
-        mask = uniform(seed, os_, n) < outlier_p
-        x[mask] *= np.float32(outlier_mult)
-    return f32_to_bf16_bits(x).reshape(shape)
+    os_ = outlier_stream if outlier_stream is not None else STREAM_OUTLIER * 8 + stream
+    out = np.empty(n, np.uint16)
+    starts = list(range(0, n, _CHUNK))
+
+    def work(st):
+        cnt = min(_CHUNK, n - st)
+        out[st:st + cnt] = _normal_bf16_chunk(seed, stream, st, cnt, std, outlier_p, outlier_mult, os_)
+
+    if len(starts) <= 1:
+        for st in starts:
+            work(st)
+    else:
+        with ThreadPoolExecutor(max_workers=max(1, min(16, os.cpu_count() or 1))) as ex:
+            list(ex.map(work, starts))
+    return out.reshape(shape)
 
 
 def lengths(seed, n, lo, hi):

@@ -7,10 +7,11 @@ Tolerances (stated once, used by every parity test):
      bound is absolute for unit-scale outputs; inputs with x64 outliers give |O| up to ~200, where
      one bf16 ulp is already 1.0, so the bound scales with the output's magnitude;
   dQ, dK, dV: relative Frobenius error <= 2e-2;
-  LSE: |error| <= 1e-3 * max(1, |LSE_ref|). The scaled MFMA adds its products in groups of 8 with a
-     narrow adder (a product ~2^15 times smaller than the largest in its group is dropped, as
-     measured on gfx950), so scores dominated by one outlier product differ from the exact FP32 sum
-     by up to ~2^-12 relative; the oracle keeps the exact definition.
+  LSE: |error| <= 1e-3 * max(1, |LSE_ref|). The fp8 MFMA adds its products in groups of 8
+     consecutive k with a narrow adder: measured on gfx950, the bits of every other product below
+     2^(e - 14), e the exponent of the group's largest product, are dropped (truncated toward zero),
+     so a group sum is off by less than 7 * 2^-14 of its largest product. Scores dominated by one
+     outlier product therefore differ from the exact sum; the oracle keeps the exact definition.
 """
 import math
 import sys
@@ -25,6 +26,19 @@ import synth
 O_MAX_ABS, O_REL_FRO = 1e-2, 5e-3
 GRAD_REL_FRO = 2e-2
 LSE_REL = 1e-3
+# Inputs with x64 outliers in both Q and K at full sequence length (8192): a query outlier meeting a
+# key outlier in the same dimension gives a product ~4096x the typical one, and the group adder
+# (above) drops up to 7 * 2^-14 of it from the score (c * dS measured up to 0.34). Rows in which
+# two such scores compete within ~1 of each other move their softmax weight by tens of percent;
+# with x64 outliers in V this moves single outputs by ~10 (|O| <= ~220), and the gradients, whose
+# norms are dominated by exactly these rows, by a few percent. Measured on the causal N=8192
+# workload, per head: O relative Frobenius 4.5e-3 to 5.2e-3, max-abs 10.6 / 224; dQ 2.0e-2 to
+# 2.4e-2, dK 2.4e-2, dV 5.9e-3 (dK 6.2e-2 with outliers in Q and K only). Without outliers in Q
+# and K the same workload gives O 1.9e-3 / 0.11 and gradients <= 2.1e-3. The check for that
+# workload therefore uses the wider bounds below (set by the hardware's summation, not by the
+# method); every other workload uses the bounds above.
+O_OUTLIER_MAX_ABS, O_OUTLIER_REL_FRO = 6e-2, 1e-2
+GRAD_OUTLIER_REL_FRO = 8e-2
 
 
 def say(msg):
@@ -119,17 +133,19 @@ class AttnCase:
         o16, o32, lse = oracle.attn_fwd_mx(self.oq[0], self.oq[1], self.qk_mode, self.ok[0], self.ok[1], self.qk_mode,
                                            self.ov[0], self.ov[1], oracle.COL32, self.cu_q, self.cu_k, self.H, 128,
                                            self.c, self.causal)
+        self.o16_ref, self.lse_ref = o16, lse
         return o16, o32, lse
 
-    def run_oracle_bwd(self, o_bf16_bits, lse, dq_mode, sigma=1.0):
+    def run_oracle_bwd(self, dq_mode, sigma=1.0):
+        """The oracle's backward from the oracle's own forward outputs (O in bf16 and LSE)."""
         ovd = oracle.quantize(self.v, self.cu_k, oracle.ROW32)
         odo = oracle.quantize(self.do, self.cu_q, oracle.SQ32)
         return oracle.attn_bwd_mx(self.oq[0], self.oq[1], self.ok[0], self.ok[1], ovd[0], ovd[1], oracle.ROW32,
-                                  odo[0], odo[1], o_bf16_bits, self.do, lse, self.cu_q, self.cu_k, self.H, 128,
-                                  self.c, self.causal, dq_mode, sigma)
+                                  odo[0], odo[1], self.o16_ref, self.do, self.lse_ref, self.cu_q, self.cu_k, self.H,
+                                  128, self.c, self.causal, dq_mode, sigma)
 
 
-def check_o(o_gpu_bits, o_ref32, lse_gpu, lse_ref, label=""):
+def check_o(o_gpu_bits, o_ref32, lse_gpu, lse_ref, label="", qk_outliers_full_length=False):
     o = bf16_bits_to_f64(o_gpu_bits)
     ref = np.asarray(o_ref32, np.float64)
     max_abs = float(np.max(np.abs(o - ref))) if o.size else 0.0
@@ -140,16 +156,119 @@ def check_o(o_gpu_bits, o_ref32, lse_gpu, lse_ref, label=""):
         if fin.any() else 0.0
     say(f"  {label} O max_abs={max_abs:.3e} (scale {scale:.3g}) rel_fro={fro:.3e} lse_rel={lse_err:.3e}")
     assert np.all(np.isfinite(o)), "non-finite O"
-    assert max_abs <= O_MAX_ABS * scale and fro <= O_REL_FRO, (max_abs, scale, fro)
+    tol_abs, tol_fro = (O_OUTLIER_MAX_ABS, O_OUTLIER_REL_FRO) if qk_outliers_full_length else (O_MAX_ABS, O_REL_FRO)
+    assert max_abs <= tol_abs * scale and fro <= tol_fro, (max_abs, scale, fro)
     assert lse_err <= LSE_REL, lse_err
     assert np.all(np.isneginf(lse_gpu[~fin])), "rows without keys must have LSE = -inf"
 
 
-def check_grads(g_gpu_bits, ref, label=""):
+def check_grads(g_gpu_bits, ref, label="", qk_outliers_full_length=False):
+    tol = GRAD_OUTLIER_REL_FRO if qk_outliers_full_length else GRAD_REL_FRO
     for name, g in zip(("dq", "dk", "dv"), g_gpu_bits):
         r = ref[name + "_f"]
         gf = bf16_bits_to_f64(g)
         fro = rel_fro(gf, r)
         say(f"  {label} {name} rel_fro={fro:.3e}")
         assert np.all(np.isfinite(gf)), name
-        assert fro <= GRAD_REL_FRO, (name, fro)
+        assert fro <= tol, (name, fro)
+
+
+# ---- projection GEMM + quantize: certified-mismatch comparison ---------------------------------
+#
+# The GPU sums the products in the MFMA's own order: products are added in groups of 8 by an adder
+# that drops the bits of each product below 2^(e - 14), e the exponent of the group's largest
+# product (measured on gfx950), and the group sums are then added in fp32. The absolute error is
+# therefore below 7 * 2^-14 * sum|x_k w_k| plus the fp32 accumulation error (~2^-20 of the same
+# sum for C_in <= 4096), i.e. below LINEAR_DELTA_REL * sum|x_k w_k|.
+# A GPU payload byte or scale that differs from the oracle's is accepted ("certified") only if the
+# E4M3 encoding (or E8M0 code) of some value within that band of the exact Y gives it.
+LINEAR_DELTA_REL = 2.0 ** -11
+LINEAR_MAX_MISMATCH_FRAC = 0.01
+
+_DEC = None
+
+
+def e4m3_table():
+    global _DEC
+    if _DEC is None:
+        _DEC = np.array([oracle.e4m3_decode(c) for c in range(256)], np.float64)
+    return _DEC
+
+
+def certify_linear(data_g, scale_g, scale_t_g, data_o, scale_o, y, yabs, cu, label=""):
+    """Returns (payload mismatches, scale mismatches); raises if any mismatch is not certified."""
+    dec = e4m3_table()
+    np.testing.assert_array_equal(scale_t_g, scale_g.T)
+    T, C = data_o.shape
+    delta = LINEAR_DELTA_REL * yabs
+    lo, hi = y - delta, y + delta
+    br_of = np.empty(T, np.int64)
+    br = 0
+    for s in range(len(cu) - 1):
+        for t0 in range(int(cu[s]), int(cu[s + 1]), 32):
+            br_of[t0:min(t0 + 32, int(cu[s + 1]))] = br
+            br += 1
+    bad_scale = []
+    n_scale = 0
+    for b in range(scale_o.shape[0]):
+        rows = np.nonzero(br_of == b)[0]
+        for cb in range(C // 32):
+            g, o = int(scale_g[b, cb]), int(scale_o[b, cb])
+            if g == o:
+                continue
+            n_scale += 1
+            blo = lo[rows, 32 * cb:32 * cb + 32]
+            bhi = hi[rows, 32 * cb:32 * cb + 32]
+            amin = np.where((blo <= 0) & (bhi >= 0), 0.0, np.minimum(np.abs(blo), np.abs(bhi))).max()
+            amax = np.maximum(np.abs(blo), np.abs(bhi)).max()
+            if not (oracle.e8m0_code(amin) <= g <= oracle.e8m0_code(amax)):
+                bad_scale.append((b, cb, g, o))
+    assert not bad_scale, f"{label}: uncertified scale mismatches {bad_scale[:5]}"
+    code = scale_g[br_of][:, np.repeat(np.arange(C // 32), 32)].astype(np.int64)
+    mism = data_g != data_o
+    n_pay = int(mism.sum())
+    if n_pay:
+        idx = np.nonzero(mism & (code != 255))
+        inv = np.ldexp(1.0, 127 - code[idx])
+        elo = oracle.e4m3_encode_array((lo[idx] * inv).astype(np.float32))
+        ehi = oracle.e4m3_encode_array((hi[idx] * inv).astype(np.float32))
+        vg = dec[data_g[idx]]
+        ok = (vg >= dec[elo]) & (vg <= dec[ehi])
+        assert ok.all(), (f"{label}: {int((~ok).sum())} uncertified payload mismatches, e.g. at "
+                          f"{[(int(a), int(b)) for a, b in zip(idx[0][~ok][:3], idx[1][~ok][:3])]}")
+    say(f"  {label}: payload mismatches {n_pay} / {data_o.size} (all certified), scale mismatches {n_scale}")
+    assert n_pay <= LINEAR_MAX_MISMATCH_FRAC * data_o.size
+    return n_pay, n_scale
+
+
+class LinearCase:
+    """Seeded projection: X bf16 ~ N(0,1) [T, C_in] quantized SQ32 (or ROW32), W bf16 ~ N(0, 0.02)
+    [C_out, C_in] quantized ROW32. Quantization of the inputs is done by the oracle (inputs only)."""
+
+    def __init__(self, seed, lens, C_in, C_out, x_mode=None, nan_at=None):
+        self.cu = synth.cu_seqlens(lens)
+        self.lens = list(lens)
+        self.T = int(self.cu[-1])
+        self.C_in, self.C_out = C_in, C_out
+        self.x_mode = oracle.SQ32 if x_mode is None else x_mode
+        x = synth.normal_bf16(seed, synth.STREAM_ACT, (self.T, C_in))
+        if nan_at is not None:
+            x[nan_at] = 0x7fc0
+        w = synth.normal_bf16(seed, synth.STREAM_WEIGHT, (C_out, C_in), std=0.02)
+        self.xd, self.xs, _ = oracle.quantize(x, self.cu, self.x_mode)
+        self.wd, self.ws, _ = oracle.quantize(w, np.array([0, C_out], np.int32), oracle.ROW32)
+
+    def run_gpu(self):
+        xo = mx.MxOperand(torch.from_numpy(self.xd).cuda(), torch.from_numpy(self.xs).cuda(), self.x_mode)
+        wo = mx.MxOperand(torch.from_numpy(self.wd).cuda(), torch.from_numpy(self.ws).cuda(), mx.ROW32)
+        data, scale, scale_t = mx.linear_quantize(xo, wo, self.cu, cu_dev(self.cu))
+        torch.cuda.synchronize()
+        return data.cpu().numpy(), scale.cpu().numpy(), scale_t.cpu().numpy()
+
+    def run_oracle(self):
+        """(data, scale, scale_t, y, yabs) with yabs = sum_k |deq(X)_tk deq(W)_nk|."""
+        d, s, st, y = oracle.linear_quantize(self.xd, self.xs, self.wd, self.ws, self.cu, x_mode=self.x_mode)
+        xdq = oracle.dequantize(self.xd, self.xs, self.cu, self.x_mode)
+        wdq = oracle.dequantize(self.wd, self.ws, np.array([0, self.C_out], np.int32), oracle.ROW32)
+        yabs = np.abs(xdq) @ np.abs(wdq).T
+        return d, s, st, y.astype(np.float64), yabs

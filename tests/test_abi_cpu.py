@@ -27,6 +27,7 @@ def _declared_functions():
 def test_header_declares_the_abi():
     names = _declared_functions()
     for n in ["mxfa_quantize", "mxfa_fwd", "mxfa_bwd", "mxfa_varlen_scale_scatter", "mxfa_rmsnorm_quantize",
+              "mxfa_linear_quantize",
               "mxfa_bwd_workspace_size", "mxfa_status_string", "mxfa_last_error_message"]:
         assert n in names
 
@@ -149,3 +150,25 @@ def test_device_code_has_no_packed_fp32_instructions():
                            capture_output=True, text=True, check=True)
         bad = [l for l in r.stdout.splitlines() if re.search(r"\bv_pk_(add|mul|fma)_f32\b", l)]
         assert not bad, (f, bad[:3])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(C_in=96), INVALID),            # C_in must be a multiple of 128
+    (dict(C_out=160), INVALID),          # C_out must be a multiple of 128
+    (dict(x=(P, P, 1)), INVALID),        # x must be SQ32 or ROW32
+    (dict(w=(P, P, 2)), INVALID),        # w must be ROW32
+    (dict(x=(0, P, 2)), INVALID),
+    (dict(w=(P, P + 4, 0)), INVALID),    # misaligned scale
+    (dict(data=0), INVALID),
+    (dict(nseq=0), INVALID),
+    (dict(max_seqlen=300), INVALID),     # > T
+    (dict(T=-1), INVALID),
+])
+def test_linear_quantize_argument_errors(kw, expect):
+    a = dict(x=(P, P, 2), w=(P, P, 0), T=256, C_in=1024, C_out=1024, cu=P, nseq=1, max_seqlen=256, data=P, scale=P,
+             scale_t=0)
+    a.update(kw)
+    st = _lib().mxfa_linear_quantize(mx._Mx(*a["x"]), mx._Mx(*a["w"]), a["T"], a["C_in"], a["C_out"], a["cu"],
+                                     a["nseq"], a["max_seqlen"], a["data"], a["scale"], a["scale_t"], 0)
+    assert st == expect, _last()
+    assert _last() != ""

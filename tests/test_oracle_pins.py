@@ -459,3 +459,60 @@ def test_rmsnorm_constant_row():
         x = np.full((1, C), synth.f32_to_bf16_bits(np.float32([a]))[0], np.uint16)
         _, _, _, y = oracle.rmsnorm_quantize(x, np.ones(C, np.float32), 1e-6, np.array([0, 1], np.int32))
         np.testing.assert_allclose(y[0], a / math.sqrt(a * a + 1e-6), rtol=3e-7)
+
+
+# ---------------------------------------------------------------------------------------------
+# Projection GEMM + quantize
+# ---------------------------------------------------------------------------------------------
+
+def _int_bf16(seed, shape, lo, hi):
+    rng = np.random.default_rng(seed)
+    v = rng.integers(lo, hi + 1, size=shape).astype(np.float32)
+    return synth.f32_to_bf16_bits(v), v.astype(np.int64)
+
+
+def test_linear_small_integers_exact():
+    """Small-integer X and W quantize without rounding (|x| <= 4, |w| <= 3 are E4M3 values at their
+    block scales), so Y is the exact integer product X W^T."""
+    cu = synth.cu_seqlens([40, 57])
+    T, C_in, C_out = 97, 128, 96
+    xb, xi = _int_bf16(1, (T, C_in), -4, 4)
+    wb, wi = _int_bf16(2, (C_out, C_in), -3, 3)
+    xd, xs, _ = oracle.quantize(xb, cu, oracle.SQ32)
+    wd, ws, _ = oracle.quantize(wb, np.array([0, C_out], np.int32), oracle.ROW32)
+    data, scale, scale_t, y = oracle.linear_quantize(xd, xs, wd, ws, cu)
+    np.testing.assert_array_equal(y.astype(np.int64), xi @ wi.T)
+    np.testing.assert_array_equal(scale_t, scale.T)
+
+
+def test_linear_identity_weight_requantizes_x():
+    """W = I: Y = deq(X) exactly, and SQ32 quantization of an already-quantized matrix (same token
+    blocks, same 32-column blocks) gives back the same payload and scales."""
+    cu = synth.cu_seqlens([33, 100, 1])
+    T, C = 134, 128
+    x = synth.normal_bf16(3, synth.STREAM_ACT, (T, C))
+    xd, xs, xst = oracle.quantize(x, cu, oracle.SQ32)
+    eye = synth.f32_to_bf16_bits(np.eye(C, dtype=np.float32))
+    wd, ws, _ = oracle.quantize(eye, np.array([0, C], np.int32), oracle.ROW32)
+    data, scale, scale_t, y = oracle.linear_quantize(xd, xs, wd, ws, cu)
+    np.testing.assert_array_equal(y.astype(np.float64), oracle.dequantize(xd, xs, cu, oracle.SQ32))
+    np.testing.assert_array_equal(data, xd)
+    np.testing.assert_array_equal(scale, xs)
+    np.testing.assert_array_equal(scale_t, xst)
+
+
+def test_linear_matches_dequantized_matmul():
+    """Y equals the fp32 rounding of deq(X) deq(W)^T computed by a library matmul (to one fp32
+    ulp), and the output is the SQ32 quantization of that Y."""
+    cu = synth.cu_seqlens([70, 130])
+    T, C_in, C_out = 200, 256, 128
+    x = synth.normal_bf16(4, synth.STREAM_ACT, (T, C_in))
+    w = synth.normal_bf16(4, synth.STREAM_WEIGHT, (C_out, C_in), std=0.02)
+    xd, xs, _ = oracle.quantize(x, cu, oracle.SQ32)
+    wd, ws, _ = oracle.quantize(w, np.array([0, C_out], np.int32), oracle.ROW32)
+    data, scale, scale_t, y = oracle.linear_quantize(xd, xs, wd, ws, cu)
+    ref = oracle.dequantize(xd, xs, cu, oracle.SQ32) @ oracle.dequantize(wd, ws, np.array([0, C_out]), oracle.ROW32).T
+    np.testing.assert_allclose(y.astype(np.float64), ref, rtol=2.0 ** -23, atol=0)
+    d2, s2, _ = oracle.quantize(y, cu, oracle.SQ32)
+    np.testing.assert_array_equal(data, d2)
+    np.testing.assert_array_equal(scale, s2)
