@@ -11,7 +11,7 @@ kernels run on), which gives the per-call PF/s and the fraction of the MI355X de
 peak (5.03 PF/s = 256 CU x 4 SIMD x 2048 FLOP/clk x 2.4 GHz).
 
 cpu_baseline: the CPU oracle, as it is, on a bounded sample of the same workload (batch element 0,
-all 16 heads, N = 4096, forward + backward) on this host's cores.
+6 of the 16 heads, N = 4096, forward + backward) on this host's cores.
 """
 import argparse
 import json
@@ -38,7 +38,36 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--dq-mode", type=int, default=1, help="0 = FP32 dQ, 1 = FP16 static-scale dQ")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 512 MiB device copy first (reference kernel for HBM byte counters)")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bwd_B4_H16_N4096_hbm_traffic.md")
+BWD_SOURCES = [os.path.join(ROOT, "precision_mxfp8_block_amd", "csrc", f) for f in ("attn_bwd.hip", "mx_device.h")]
+
+
+def bwd_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in BWD_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per backward call from the committed counter summary, or None when the backward
+    kernel sources changed since the counters were taken (or no summary exists)."""
+    import re
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    txt = open(TRAFFIC_FILE).read()
+    m_hash = re.search(r"source_sha256_16:\s*([0-9a-f]{16})", txt)
+    m_bytes = re.search(r"hbm_bytes_per_call:\s*([0-9.eE+]+)", txt)
+    if not m_hash or not m_bytes or m_hash.group(1) != bwd_source_hash():
+        return None
+    return float(m_bytes.group(1))
 
 
 def make_inputs(torch, synth):
@@ -51,11 +80,15 @@ def make_inputs(torch, synth):
     return host, dev, cu, cu_d
 
 
+CPU_HEADS = 6  # heads of batch element 0 in the CPU sample (about 25 s of oracle work on 16 cores)
+
+
 def cpu_baseline(host, cu):
     import oracle
     nthreads = max(1, min(16, os.cpu_count() or 1))
-    # sample: sequence 0 (N tokens), all heads, forward + backward (FP32 dQ), training modes
-    xs = {n: np.ascontiguousarray(a[:N]) for n, a in host.items()}
+    # sample: sequence 0 (N tokens), the first CPU_HEADS heads, forward + backward (FP32 dQ)
+    hs = CPU_HEADS
+    xs = {n: np.ascontiguousarray(a[:N, :hs * D]) for n, a in host.items()}
     cu0 = np.array([0, N], np.int32)
     c = float(np.float32(1 / math.sqrt(D)))
     t0 = time.perf_counter()
@@ -64,15 +97,15 @@ def cpu_baseline(host, cu):
     v = oracle.quantize(xs["v"], cu0, oracle.COL32)
     vd = oracle.quantize(xs["v"], cu0, oracle.ROW32)
     do = oracle.quantize(xs["do"], cu0, oracle.SQ32)
-    o16, _, lse = oracle.attn_fwd_mx(q[0], q[1], 2, k[0], k[1], 2, v[0], v[1], 1, cu0, cu0, H, D, c, False,
+    o16, _, lse = oracle.attn_fwd_mx(q[0], q[1], 2, k[0], k[1], 2, v[0], v[1], 1, cu0, cu0, hs, D, c, False,
                                      nthreads=nthreads)
-    oracle.attn_bwd_mx(q[0], q[1], k[0], k[1], vd[0], vd[1], 0, do[0], do[1], o16, xs["do"], lse, cu0, cu0, H, D, c,
+    oracle.attn_bwd_mx(q[0], q[1], k[0], k[1], vd[0], vd[1], 0, do[0], do[1], o16, xs["do"], lse, cu0, cu0, hs, D, c,
                        False, 0, 1.0, nthreads=nthreads)
     dt = time.perf_counter() - t0
-    flops = 3.5 * 4.0 * N * N * D * H
+    flops = 3.5 * 4.0 * N * N * D * hs
     return {"value": flops / dt / 1e15, "unit": "PF/s", "cores": nthreads, "kind": "oracle",
-            "sample": f"batch element 0 of the step: {H} heads x N={N}, quantize + forward + backward (FP32 dQ), "
-                      f"{dt:.1f} s wall"}
+            "sample": f"batch element 0 of the step, heads 0-{hs - 1} of {H} (N={N}): quantize + forward + "
+                      f"backward (FP32 dQ), {dt:.1f} s wall"}
 
 
 def main():
@@ -86,6 +119,14 @@ def main():
     import synth
 
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print("# copy calibration: 536870912 bytes read and written by one copy kernel", file=sys.stderr, flush=True)
+        del src, dst
     host, dev, cu, cu_d = make_inputs(torch, synth)
     T, C = B * N, H * D
     c = float(np.float32(1 / math.sqrt(D)))
@@ -144,6 +185,20 @@ def main():
     wall = time.perf_counter() - t0
     print(f"# timed {args.steps} steps in {wall:.3f} s", file=sys.stderr, flush=True)
 
+    # the backward once more with FP32 dQ (own workspace), timed on the same stream
+    ws32_bytes = mx.mxfa_bwd_workspace_size(T, H, D, 0)
+    ws32 = torch.empty(ws32_bytes, dtype=torch.uint8, device="cuda")
+    n32 = 5
+    e32 = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n32)]
+    for i in range(n32 + 1):
+        if i:
+            e32[i - 1][0].record(stream)
+        mx.mxfa_bwd(attn, vop, doop, o, dev["do"], lse, 0, 1.0, ws32, ws32_bytes, dq, dk, dv, stream)
+        if i:
+            e32[i - 1][1].record(stream)
+    torch.cuda.synchronize()
+    bwd32_s = float(np.median([e[0].elapsed_time(e[1]) * 1e-3 for e in e32]))
+
     times = {n: [e[0].elapsed_time(e[1]) * 1e-3 for e in ev[n]] for n in names}
     med = {n: float(np.median(v)) for n, v in times.items()}
     f_fwd = 4.0 * N * N * D * B * H
@@ -155,9 +210,11 @@ def main():
     dominant = "bwd" if med["bwd"] >= med["fwd"] else "fwd"
     flops_dom = f_bwd if dominant == "bwd" else f_fwd
     roof = {"bound": "mfma", "achieved": flops_dom / med[dominant] / 1e12, "peak": PEAK_MXFP8 / 1e12,
-            "unit": "TFLOP/s", "frac": flops_dom / med[dominant] / PEAK_MXFP8, "traffic": None,
-            "kernel": "mxfa_bwd (dK/dV main kernel + Delta preprocess + dQ finalize)" if dominant == "bwd"
-            else "attn_fwd_kernel"}
+            "unit": "TFLOP/s", "frac": flops_dom / med[dominant] / PEAK_MXFP8,
+            "traffic": measured_traffic() if dominant == "bwd" else None,
+            "kernel": "mxfa_bwd call: attn_bwd_kernel + bwd_preprocess_kernel + bwd_finalize_kernel"
+            if dominant == "bwd" else "attn_fwd_kernel",
+            "launch_us": round(med[dominant] * 1e6, 2)}
     out = {
         "metric": "MXFP8 attention fwd/bwd PF/s and % of MI355X dense MXFP8 MFMA peak",
         "value": round(value, 4), "unit": "PF/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -169,6 +226,7 @@ def main():
         "fwd_pflops": round(fwd_pf, 4), "fwd_frac_peak": round(fwd_pf * 1e15 / PEAK_MXFP8, 4),
         "bwd_pflops": round(bwd_pf, 4), "bwd_frac_peak": round(bwd_pf * 1e15 / PEAK_MXFP8, 4),
         "fwd_us": round(med["fwd"] * 1e6, 2), "bwd_us": round(med["bwd"] * 1e6, 2),
+        "bwd_fp32dq_us": round(bwd32_s * 1e6, 2), "bwd_fp32dq_pflops": round(f_bwd / bwd32_s / 1e15, 4),
         "quant_us": round(med["quant"] * 1e6, 2),
         "quant_gbps": round(quant_bytes / med["quant"] / 1e9, 1),
         "roofline": roof,
