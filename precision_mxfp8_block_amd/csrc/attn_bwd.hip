@@ -14,15 +14,20 @@
 //   dK = c dK, dQ = c acc / sigma (finalize).
 //
 // gfx950 layout choices:
-//  * Workgroup = 4 waves = one 128-row KV tile; wave w owns key rows 32w..32w+31. Its K and V rows
-//    stay in VGPRs as the B operands of S = Q K^T and dP = dO V^T, so S and dP come out with one
-//    key per lane (column) and 16 queries per lane per 32-query block.
+//  * Workgroup = 8 waves (two per SIMD) = one 128-row KV tile. Wave w owns key rows 32 (w & 3) ..
+//    +31 and query half w >> 2 of every query tile (queries 64 (w >> 2) .. +63). Its K and V rows
+//    (from the K and V tiles in LDS) are the B operands of S = Q K^T and dP = dO V^T, so S and dP
+//    come out with one key per lane (column) and 16 queries per lane per 32-query block.
 //  * That accumulator layout is exactly the A operand of dV = P^T dO and dK = dS^T Q (one key per
 //    lane, contraction over queries): P_q and dS_q bytes are used in place, in the accumulator's
 //    query order; dO^T and Q^T are read from LDS with ds_read_b64_tr_b8 in the same order.
-//  * dQ = dS K contracts over all 128 keys of the tile (all four waves): dS_q goes to LDS key-major,
-//    each wave then computes 32 query rows and adds them to the accumulator with coalesced atomics
-//    (packed FP16 pairs or FP32).
+//  * The two waves that share a key block split the accumulators instead of duplicating them: the
+//    query-half-0 wave accumulates dV, the query-half-1 wave dK, over all 128 queries of the tile.
+//    Each hands the other the packed operand it lacks (P_q or dS_q of its half, 2 KB) through LDS,
+//    so a wave holds one 32 x 128 FP32 accumulator and two waves fit on each SIMD.
+//  * dQ = dS K contracts over all 128 keys of the tile: dS_q goes to LDS key-major, each wave then
+//    computes one 32 x 64 block of the tile's dQ and adds it to the accumulator with coalesced
+//    buffer atomics (packed FP16 pairs or FP32).
 //  * Q and dO tiles (and the tile's LSE and Delta) are double-buffered in LDS and fetched one tile
 //    ahead with direct global -> LDS loads; all LDS tiles use the forward's XOR swizzle.
 //  * P is produced as 256 P straight from exp2 (the static scale folded into the exponent); dS is
@@ -47,20 +52,28 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
   return x * per + (x < rem ? x : rem) + slot;
 }
 
-__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8; the
+// counters not waited on are at their maximum).
+constexpr int kWaitVm0 = 0x0F70;
+constexpr int kWaitVm16 = 0x4F70;
+constexpr int kWaitVm32 = 0x8F70;
+__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(kWaitVm0); }
+
+constexpr int kWaves = 8;
+constexpr int kPieces = kTile * kD / 1024 / kWaves;  // 1 KB pieces (64 lanes x 16 B) per wave per tile
 
 // Per-lane constants for filling a 128 x 128-byte swizzled LDS tile with direct global -> LDS loads:
 // lane piece c of wave w covers tile row trow[c], logical chunk byte offset tcol[c].
 struct TileLane {
-  int trow[4], tcol[4];
-  uint32_t toff[4];  // trow * C + tcol (full tiles)
+  int trow[kPieces], tcol[kPieces];
+  uint32_t toff[kPieces];  // trow * C + tcol (full tiles)
 };
 
 __device__ __forceinline__ TileLane tile_lane(int wave, int lane, int C) {
   TileLane t;
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const int p = (wave * 4 + c) * 64 + lane;
+  for (int c = 0; c < kPieces; ++c) {
+    const int p = (wave * kPieces + c) * 64 + lane;
     t.trow[c] = p >> 3;
     t.tcol[c] = 16 * ((p & 7) ^ swz(p >> 3));
     t.toff[c] = (uint32_t)(t.trow[c] * C + t.tcol[c]);
@@ -73,10 +86,9 @@ __device__ __forceinline__ TileLane tile_lane(int wave, int lane, int C) {
 __device__ __forceinline__ void issue_tile_load(uint8_t* lds_tile, const uint8_t* base, int valid, int C,
                                                 const TileLane& t, int wave_s) {
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
+  for (int c = 0; c < kPieces; ++c) {
     const uint32_t off = valid >= kTile ? t.toff[c] : (uint32_t)(min(t.trow[c], valid - 1) * C + t.tcol[c]);
-    __builtin_amdgcn_global_load_lds((const void*)(base + off), (MX_LDS void*)(lds_tile + (wave_s * 4 + c) * 1024),
-                                     16, 0, 0);
+    mx_lds_dma16((MX_LDS void*)(lds_tile + (wave_s * kPieces + c) * 1024), base, off);
   }
 }
 
@@ -168,12 +180,15 @@ struct BwdParams {
   uint16_t *dk, *dv;
 };
 
-__global__ void __launch_bounds__(256, 1) attn_bwd_kernel(BwdParams p) {
+__global__ void __launch_bounds__(512, 1) attn_bwd_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds_k[kTile * kD];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_v[kTile * kD];         // V along D (for dP)
   __shared__ __attribute__((aligned(1024))) uint8_t lds_qd[2][2][kTile * kD];  // [stage][Q, dO]
   __shared__ __attribute__((aligned(1024))) uint8_t lds_ds[kTile * kD];        // dS_q, key-major [kv][q]
+  __shared__ __attribute__((aligned(1024))) uint4 lds_xchg[kWaves][2][64];     // operand handed to the partner
   __shared__ __attribute__((aligned(512))) float lds_ld[2][2][kTile];          // [stage][8 - LSE log2e, Delta]
-  __shared__ uint32_t lds_dscode[4];                                           // [kv block] -> 4 q-block codes
+  __shared__ __attribute__((aligned(256))) uint32_t lds_sc[2][64];             // [stage][Q, dO scale words]
+  __shared__ uint8_t lds_dscode[4][4];                                         // dS codes [kv block][q block]
   __shared__ int64_t red[16];
 
   const int item = xcd_remap((int)blockIdx.x, p.total_items);
@@ -190,20 +205,23 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_kernel(BwdParams p) {
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const int kw = wave_s & 3;    // key block of this wave
+  const int half = wave_s >> 2;  // query half of every tile; 0: accumulates dV, 1: accumulates dK
   const int r = lane & 31, hh = lane >> 5;
   const int C = p.H * kD;
   const int Cs = C >> 5;
   const int kv0 = kt * kTile;
-  const int kvrow = kv0 + 32 * wave + r;  // this lane's key row (B operands of S and dP)
+  const int kvrow = kv0 + 32 * kw + r;  // this lane's key row (B operands of S and dP)
   const TileLane tl = tile_lane(wave, lane, C);
 
   const int n_qtiles = (Lq + kTile - 1) / kTile;
   const int qt_begin = p.causal ? kt : 0;
 
-  const uint8_t* qbase = p.q + q_start * (int64_t)C + h * kD;
-  const uint8_t* dobase = p.dO + q_start * (int64_t)C + h * kD;
-  const float* lse_base = p.pexp + (int64_t)h * p.Tq + q_start;
-  const float* del_base = p.delta + (int64_t)h * p.Tq + q_start;
+  // wave-uniform base pointers, kept in scalar registers
+  const uint8_t* qbase = (const uint8_t*)mx_uniform_ptr((void*)(p.q + q_start * (int64_t)C + h * kD));
+  const uint8_t* dobase = (const uint8_t*)mx_uniform_ptr((void*)(p.dO + q_start * (int64_t)C + h * kD));
+  const float* lse_base = (const float*)mx_uniform_ptr((void*)(p.pexp + (int64_t)h * p.Tq + q_start));
+  const float* del_base = (const float*)mx_uniform_ptr((void*)(p.delta + (int64_t)h * p.Tq + q_start));
   // exponent offsets and Delta of a query tile: waves 0 and 1 each copy one 128-float vector (one
   // 4-byte element per lane, two pieces of 64 lanes).
   auto issue_ld_load = [&](int st, int q0) {
@@ -212,14 +230,14 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_kernel(BwdParams p) {
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const int row = min(q0 + c * 64 + lane, Lq - 1);
-        __builtin_amdgcn_global_load_lds((const void*)(src + row), (MX_LDS void*)(&lds_ld[st][wave_s][c * 64]), 4, 0,
-                                         0);
+        mx_lds_dma4((MX_LDS void*)(&lds_ld[st][wave_s][c * 64]), src, (uint32_t)row * 4u);
       }
     }
   };
 
-  // prologue: K tile, the first Q/dO tile and its LSE/Delta
+  // prologue: K and V tiles, the first Q/dO tile and its LSE/Delta
   issue_tile_load(lds_k, p.k + (k_start + kv0) * (int64_t)C + h * kD, Lk - kv0, C, tl, wave_s);
+  issue_tile_load(lds_v, p.v + (k_start + kv0) * (int64_t)C + h * kD, Lk - kv0, C, tl, wave_s);
   if (qt_begin < n_qtiles) {
     const int64_t q0 = (int64_t)qt_begin * kTile;
     issue_tile_load(lds_qd[qt_begin & 1][0], qbase + q0 * C, Lq - (int)q0, C, tl, wave_s);
@@ -227,25 +245,6 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_kernel(BwdParams p) {
     issue_ld_load(qt_begin & 1, (int)q0);
   }
 
-  // this wave's K and V rows in VGPRs (B operands of S = Q K^T and dP = dO V^T)
-  mx_v8i kb_op[2], vb_op[2];
-  {
-    const bool valid = kvrow < Lk;
-    const uint8_t* ks = p.k + (k_start + kvrow) * (int64_t)C + h * kD;
-    const uint8_t* vs = p.v + (k_start + kvrow) * (int64_t)C + h * kD;
-#pragma unroll
-    for (int ds = 0; ds < 2; ++ds) {
-      uint4 a0 = make_uint4(0, 0, 0, 0), a1 = a0, b0 = a0, b1 = a0;
-      if (valid) {
-        a0 = *reinterpret_cast<const uint4*>(ks + 64 * ds + 16 * hh);
-        a1 = *reinterpret_cast<const uint4*>(ks + 64 * ds + 32 + 16 * hh);
-        b0 = *reinterpret_cast<const uint4*>(vs + 64 * ds + 16 * hh);
-        b1 = *reinterpret_cast<const uint4*>(vs + 64 * ds + 32 + 16 * hh);
-      }
-      kb_op[ds] = mx_v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-      vb_op[ds] = mx_v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-    }
-  }
   // K (SQ32) and V (ROW32/SQ32) scales along D of this lane's key row: byte 0 = d-block hh, byte 2 =
   // d-block 2 + hh
   const uint32_t ksc_b =
@@ -260,26 +259,24 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_kernel(BwdParams p) {
     kq_sc[ks] =
         *reinterpret_cast<const uint32_t*>(p.k_scale + ((koff.padded + kv0) / 32 + 2 * ks + hh) * (int64_t)Cs + h * 4);
 
-  // Q and dO scales of a query tile (SQ32): one word (4 d-blocks) per query block, raw
+  // Q and dO scales of a query tile (SQ32): one word (4 d-blocks) per query block, raw. Wave 2 copies
+  // them into LDS with the tile (lanes 0-3: Q blocks, lanes 4-7: dO blocks, the rest repeat lane 0).
   const uint8_t* qs_base = p.q_scale + (qoff.padded >> 5) * (int64_t)Cs + h * 4;
   const uint8_t* ds_base = p.dO_scale + (qoff.padded >> 5) * (int64_t)Cs + h * 4;
-  uint32_t qsc[4], dosc[4];
-  auto load_q_scales = [&](int qt) {
-#pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
-      const uint32_t off = (uint32_t)((qt * 4 + qb) * Cs);
-      qsc[qb] = *reinterpret_cast<const uint32_t*>(qs_base + off);
-      dosc[qb] = *reinterpret_cast<const uint32_t*>(ds_base + off);
+  auto issue_sc_load = [&](int st, int qt) {
+    if (wave_s == 2) {
+      const int i = lane < 8 ? lane : 0;
+      const uint8_t* src = (i < 4 ? qs_base : ds_base) + (int64_t)((qt * 4 + (i & 3)) * Cs);
+      mx_lds_dma4_addr((MX_LDS void*)&lds_sc[st][0], src);
     }
   };
-  if (qt_begin < n_qtiles) load_q_scales(qt_begin);
+  if (qt_begin < n_qtiles) issue_sc_load(qt_begin & 1, qt_begin);
+  uint32_t qsc[4], dosc[4];
 
-  mx_v16f dk_acc[4], dv_acc[4];
+  // dV (query-half-0 waves) or dK (query-half-1 waves) of this wave's 32 keys
+  mx_v16f kv_acc[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    dk_acc[i] = mx_v16f{};
-    dv_acc[i] = mx_v16f{};
-  }
+  for (int i = 0; i < 4; ++i) kv_acc[i] = mx_v16f{};
 
   // per-lane constants of the transposed LDS reads
   const int grp = lane >> 4, gl = lane & 15;
@@ -287,11 +284,8 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_kernel(BwdParams p) {
   const int tr_row = 8 * (tb >> 2) + 4 * (grp >> 1) + (tb & 3);
   const int tr_col = 16 * (grp & 1) + 8 * ts;
   const int tr_swz = swz(tr_row);
-
-  // dQ accumulator addressing: element (query row, column) of this head
-  float* dq32 = reinterpret_cast<float*>(p.dq_acc) + q_start * (int64_t)C + h * kD;
-  __half2* dq16 = reinterpret_cast<__half2*>(reinterpret_cast<__half*>(p.dq_acc) + q_start * (int64_t)C + h * kD);
   const bool odd = r & 1;
+  const uint64_t odd_lanes = 0xAAAAAAAAAAAAAAAAull;
 
   wait_vm();
   __syncthreads();
@@ -304,10 +298,19 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_kernel(BwdParams p) {
     const float* pexp = lds_ld[st][0];
     const float* dlt = lds_ld[st][1];
     // prefetch the next query tile
+    // this tile's scale words (landed with the tile)
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+      qsc[qb] = lds_sc[st][qb];
+      dosc[qb] = lds_sc[st][4 + qb];
+    }
     if (qt + 1 < n_qtiles) {
       const int64_t nq0 = (int64_t)(q0 + kTile);
-      issue_tile_load(lds_qd[st ^ 1][0], qbase + nq0 * C, Lq - (int)nq0, C, tl, wave_s);
-      issue_tile_load(lds_qd[st ^ 1][1], dobase + nq0 * C, Lq - (int)nq0, C, tl, wave_s);
+      issue_sc_load(st ^ 1, qt + 1);
+      issue_tile_load(lds_qd[st ^ 1][0], (const uint8_t*)mx_uniform_ptr((void*)(qbase + nq0 * C)), Lq - (int)nq0, C,
+                      tl, wave_s);
+      issue_tile_load(lds_qd[st ^ 1][1], (const uint8_t*)mx_uniform_ptr((void*)(dobase + nq0 * C)), Lq - (int)nq0, C,
+                      tl, wave_s);
       issue_ld_load(st ^ 1, (int)nq0);
     }
 
@@ -318,217 +321,249 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_kernel(BwdParams p) {
       qsc_t[ks] = hh ? qsc[2 * ks + 1] : qsc[2 * ks];
       dosc_t[ks] = hh ? dosc[2 * ks + 1] : dosc[2 * ks];
     }
-    uint32_t qsc_c[4], dosc_c[4];  // this tile's along-D scales for G1 and G2
+    uint32_t qsc_c[2], dosc_c[2];  // this wave's query blocks' along-D scales for G1 and G2
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
-      qsc_c[qb] = qsc[qb] >> (8 * hh);
-      dosc_c[qb] = dosc[qb] >> (8 * hh);
+    for (int j = 0; j < 2; ++j) {
+      qsc_c[j] = (half ? qsc[2 + j] : qsc[j]) >> (8 * hh);
+      dosc_c[j] = (half ? dosc[2 + j] : dosc[j]) >> (8 * hh);
     }
-    if (qt + 1 < n_qtiles) load_q_scales(qt + 1);
     const bool need_mask = (q0 + kTile > Lq) || (kv0 + kTile > Lk) || (p.causal && kv0 + kTile - 1 > q0);
-    uint32_t codes = 0;  // dS codes of the four query blocks, one byte each
 
-    // Two halves of 64 queries (query blocks 2 ks, 2 ks + 1): the 64-query contraction step of G3/G4.
-    // Software pipeline inside the wave: the S and dP MFMAs of half 1 are issued before the
-    // elementwise work of half 0, so the matrix core runs them while the VALU works.
-    auto g12 = [&](int ks, mx_v16f* sacc, mx_v16f* dpacc) {
+    // ---- per query block j of this wave's half: G1, G2 (S and dP), then 256 P, 256 dS ----
+    // (lane: key kvrow; queries 64 half + 32 j + 8 i + 4 hh + t). Two instantiations of the
+    // elementwise part behind one wave-uniform branch: interior tiles carry no mask code.
+    uint32_t pk[2][4], dsk[2][4], dscode[2];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int qb = 2 * ks + j;
-        const int row = 32 * qb + r;
+    for (int j = 0; j < 2; ++j) {
+      const int ql0 = 64 * half + 32 * j;  // first query of the block inside the tile
+      mx_v16f sacc, dpacc;
+      {
+        const int row = ql0 + r;       // query row (A operand)
+        const int krow = 32 * kw + r;  // key row (B operand), from the K and V tiles in LDS
         mx_v8i qa0 = lds_row_operand(lds_q, row, 0, hh);
+        mx_v8i kb0 = lds_row_operand(lds_k, krow, 0, hh);
         mx_v8i qa1 = lds_row_operand(lds_q, row, 1, hh);
-        sacc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa0, kb_op[0], mx_v16f{}, 0, 0, 0, (int)qsc_c[qb], 0,
-                                                                  (int)ksc_b);
-        sacc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa1, kb_op[1], sacc[j], 0, 0, 2, (int)qsc_c[qb], 2,
-                                                                  (int)ksc_b);
+        mx_v8i kb1 = lds_row_operand(lds_k, krow, 1, hh);
+        sacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa0, kb0, mx_v16f{}, 0, 0, 0, (int)qsc_c[j], 0,
+                                                               (int)ksc_b);
+        sacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa1, kb1, sacc, 0, 0, 2, (int)qsc_c[j], 2, (int)ksc_b);
         mx_v8i da0 = lds_row_operand(lds_do, row, 0, hh);
+        mx_v8i vb0 = lds_row_operand(lds_v, krow, 0, hh);
         mx_v8i da1 = lds_row_operand(lds_do, row, 1, hh);
-        dpacc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(da0, vb_op[0], mx_v16f{}, 0, 0, 0, (int)dosc_c[qb],
-                                                                   0, (int)vsc_b);
-        dpacc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(da1, vb_op[1], dpacc[j], 0, 0, 2, (int)dosc_c[qb], 2,
-                                                                   (int)vsc_b);
-        // issue order: these MFMAs stay here, ahead of the elementwise work that follows
-        asm volatile("" : "+v"(sacc[j]), "+v"(dpacc[j])::"memory");
+        mx_v8i vb1 = lds_row_operand(lds_v, krow, 1, hh);
+        dpacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(da0, vb0, mx_v16f{}, 0, 0, 0, (int)dosc_c[j], 0,
+                                                                (int)vsc_b);
+        dpacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(da1, vb1, dpacc, 0, 0, 2, (int)dosc_c[j], 2,
+                                                                (int)vsc_b);
+        asm volatile("" : "+v"(sacc), "+v"(dpacc)::"memory");
       }
-    };
-    mx_v16f sacc_h[2][2], dpacc_h[2][2];
-    g12(0, sacc_h[0], dpacc_h[0]);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      if (ks == 0) g12(1, sacc_h[1], dpacc_h[1]);
-      mx_v16f* sacc = sacc_h[ks];
-      mx_v16f* dpacc = dpacc_h[ks];
-
-      // ---- 256 P, 256 dS (lane: key kvrow; queries 32 qb + 8 i + 4 hh + t) ----
-      // Two instantiations behind one wave-uniform branch: interior tiles carry no mask code.
-      uint32_t pk[2][4], dsk[2][4], dscode[2];
       auto elementwise = [&](auto masked) {
         constexpr bool MASK = decltype(masked)::value;
+        float am = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int qb = 2 * ks + j;
-          uint32_t am = 0;
+        for (int i = 0; i < 4; ++i) {
+          // the lane's 4 consecutive query rows ql0 + 8 i + 4 hh + (0..3)
+          const float4 pe4 = *reinterpret_cast<const float4*>(pexp + ql0 + 8 * i + 4 * hh);
+          const float4 dl4 = *reinterpret_cast<const float4*>(dlt + ql0 + 8 * i + 4 * hh);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            // the lane's 4 consecutive query rows 32 qb + 8 i + 4 hh + (0..3)
-            const float4 pe4 = *reinterpret_cast<const float4*>(pexp + 32 * qb + 8 * i + 4 * hh);
-            const float4 dl4 = *reinterpret_cast<const float4*>(dlt + 32 * qb + 8 * i + 4 * hh);
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              const int v = 4 * i + t;
-              const float pe = (&pe4.x)[t], dl = (&dl4.x)[t];
-              float e = __builtin_amdgcn_exp2f(fmaf(sacc[j][v], p.c2, pe));  // 256 P
-              if (MASK) {
-                const int qpos = q0 + 32 * qb + 8 * i + 4 * hh + t;
-                const bool ok = (kvrow < Lk) & (qpos < Lq) & ((p.causal == 0) | (kvrow <= qpos));
-                e = ok ? e : 0.0f;
-              }
-              const float dsv = e * (dpacc[j][v] - dl);  // 256 dS
-              sacc[j][v] = e;
-              dpacc[j][v] = dsv;
-              am = max(am, __float_as_uint(dsv) & 0x7fffffffu);
+          for (int t = 0; t < 4; ++t) {
+            const int v = 4 * i + t;
+            const float pe = (&pe4.x)[t], dl = (&dl4.x)[t];
+            float e = __builtin_amdgcn_exp2f(fmaf(sacc[v], p.c2, pe));  // 256 P
+            if (MASK) {
+              const int qpos = q0 + ql0 + 8 * i + 4 * hh + t;
+              const bool ok = (kvrow < Lk) & (qpos < Lq) & ((p.causal == 0) | (kvrow <= qpos));
+              e = ok ? e : 0.0f;
             }
+            const float dsv = e * (dpacc[v] - dl);  // 256 dS
+            sacc[v] = e;
+            dpacc[v] = dsv;
           }
-          // block maximum over the wave (one 32 x 32 block), code of dS = code of 256 dS - 8
-          const uint32_t c256 = mx_code_from_amax_bits(wave_max_dpp(am));
-          dscode[j] = c256 == 255u ? 255u : (c256 > 8u ? c256 - 8u : 0u);
-          // 256 dS * 2^(127 - (code + 8)) = dS * 2^(127 - code)
-          const float inv = dscode[j] == 255u ? 0.0f : mx_inv_scale(dscode[j] + 8u);
+          am = max3_abs(am, dpacc[4 * i], dpacc[4 * i + 1]);
+          am = max3_abs(am, dpacc[4 * i + 2], dpacc[4 * i + 3]);
+        }
+        // block maximum over the wave (one 32 x 32 block), code of dS = code of 256 dS - 8
+        const uint32_t c256 = mx_code_from_amax_bits(wave_max_dpp(__float_as_uint(am)));
+        dscode[j] = c256 == 255u ? 255u : (c256 > 8u ? c256 - 8u : 0u);
+        // 256 dS * 2^(127 - (code + 8)) = dS * 2^(127 - code)
+        const float inv = dscode[j] == 255u ? 0.0f : mx_inv_scale(dscode[j] + 8u);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            pk[j][i] = mx_pack4_inrange(sacc[j][4 * i], sacc[j][4 * i + 1], sacc[j][4 * i + 2], sacc[j][4 * i + 3]);
-            const uint32_t w = mx_pack4(dpacc[j][4 * i] * inv, dpacc[j][4 * i + 1] * inv, dpacc[j][4 * i + 2] * inv,
-                                        dpacc[j][4 * i + 3] * inv);
-            dsk[j][i] = dscode[j] == 255u ? 0x7f7f7f7fu : w;
-          }
+        for (int i = 0; i < 4; ++i) {
+          pk[j][i] = mx_pack4_inrange(sacc[4 * i], sacc[4 * i + 1], sacc[4 * i + 2], sacc[4 * i + 3]);
+          const uint32_t w =
+              mx_pack4(dpacc[4 * i] * inv, dpacc[4 * i + 1] * inv, dpacc[4 * i + 2] * inv, dpacc[4 * i + 3] * inv);
+          dsk[j][i] = dscode[j] == 255u ? 0x7f7f7f7fu : w;
         }
       };
       if (need_mask)
         elementwise(std::true_type{});
       else
         elementwise(std::false_type{});
-      codes |= (dscode[0] << (16 * ks)) | (dscode[1] << (16 * ks + 8));
+    }
 
-      // ---- dS_q to LDS, key-major [kv][q], for dQ ----
-      {
-        const int kvl = 32 * wave + r;  // key row inside the tile
-        const int sw = swz(kvl);
+    // ---- dS_q to LDS key-major [kv][q] (for dQ); the partner's operand; the block codes ----
+    {
+      const int kvl = 32 * kw + r;  // key row inside the tile
+      const int sw = swz(kvl);
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int ql = 32 * (2 * ks + j) + 8 * i + 4 * hh;
-            *reinterpret_cast<uint32_t*>(lds_ds + kvl * kD + 16 * ((ql >> 4) ^ sw) + (ql & 15)) = dsk[j][i];
-          }
+        for (int i = 0; i < 4; ++i) {
+          const int ql = 64 * half + 32 * j + 8 * i + 4 * hh;
+          *reinterpret_cast<uint32_t*>(lds_ds + kvl * kD + 16 * ((ql >> 4) ^ sw) + (ql & 15)) = dsk[j][i];
+        }
+      // the dV wave (half 0) needs the other half's P_q, the dK wave (half 1) the other half's dS_q
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        lds_xchg[wave_s][j][lane] = half ? make_uint4(pk[j][0], pk[j][1], pk[j][2], pk[j][3])
+                                         : make_uint4(dsk[j][0], dsk[j][1], dsk[j][2], dsk[j][3]);
+      if (lane == 0) {
+        lds_dscode[kw][2 * half] = (uint8_t)dscode[0];
+        lds_dscode[kw][2 * half + 1] = (uint8_t)dscode[1];
       }
+    }
+    __syncthreads();  // dS_q, the partner operands and the codes of all eight waves are in LDS
 
-      // ---- G3: dV += P_q^T dO  and  G4: dK += dS_q^T Q  (this 64-query step) ----
-      {
-        mx_v8i pa{(int)pk[0][0], (int)pk[0][1], (int)pk[0][2], (int)pk[0][3],
-                  (int)pk[1][0], (int)pk[1][1], (int)pk[1][2], (int)pk[1][3]};
-        mx_v8i sa{(int)dsk[0][0], (int)dsk[0][1], (int)dsk[0][2], (int)dsk[0][3],
-                  (int)dsk[1][0], (int)dsk[1][1], (int)dsk[1][2], (int)dsk[1][3]};
-        // A-operand scale of dS_q: k-block hh of this step is query block 2 ks + hh
-        const uint32_t sa_sc = hh ? dscode[1] : dscode[0];
+    // ---- G3 (half-0 waves): dV += P_q^T dO;  G4 (half-1 waves): dK += dS_q^T Q; all 128 queries ----
+    {
+      const int partner = wave_s ^ 4;
+      const uint4 x0 = lds_xchg[partner][0][lane], x1 = lds_xchg[partner][1][lane];
+      const mx_v8i other{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+      if (half == 0) {
+        const mx_v8i own{(int)pk[0][0], (int)pk[0][1], (int)pk[0][2], (int)pk[0][3],
+                         (int)pk[1][0], (int)pk[1][1], (int)pk[1][2], (int)pk[1][3]};
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          mx_v8i dob = lds_tr_operand(lds_do, ks, 32 * db, tr_row, tr_col, tr_swz);
-          dv_acc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(pa, dob, dv_acc[db], 0, 0, 0, 119, 0,
-                                                                       (int)(dosc_t[ks] >> (8 * db)));
-          mx_v8i qbt = lds_tr_operand(lds_q, ks, 32 * db, tr_row, tr_col, tr_swz);
-          dk_acc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(sa, qbt, dk_acc[db], 0, 0, 0, (int)sa_sc, 0,
-                                                                       (int)(qsc_t[ks] >> (8 * db)));
-          // Keep these MFMAs here (the compiler would otherwise sink them below the barrier and hold
-          // all of their operands in registers); the accumulators stay in AGPRs.
-          asm volatile("" : "+a"(dv_acc[db]), "+a"(dk_acc[db])::"memory");
+        for (int ks = 0; ks < 2; ++ks) {
+          const mx_v8i pa = ks == 0 ? own : other;
+#pragma unroll
+          for (int db = 0; db < 4; ++db) {
+            mx_v8i dob = lds_tr_operand(lds_do, ks, 32 * db, tr_row, tr_col, tr_swz);
+            kv_acc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(pa, dob, kv_acc[db], 0, 0, 0, 119, 0,
+                                                                         (int)(dosc_t[ks] >> (8 * db)));
+            asm volatile("" : "+v"(kv_acc[db])::"memory");
+          }
+        }
+      } else {
+        const mx_v8i own{(int)dsk[0][0], (int)dsk[0][1], (int)dsk[0][2], (int)dsk[0][3],
+                         (int)dsk[1][0], (int)dsk[1][1], (int)dsk[1][2], (int)dsk[1][3]};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const mx_v8i sa = ks == 1 ? own : other;
+          // A-operand scale of dS_q: k-block hh of this step is query block 2 ks + hh
+          const uint32_t sa_sc = lds_dscode[kw][2 * ks + hh];
+#pragma unroll
+          for (int db = 0; db < 4; ++db) {
+            mx_v8i qbt = lds_tr_operand(lds_q, ks, 32 * db, tr_row, tr_col, tr_swz);
+            kv_acc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(sa, qbt, kv_acc[db], 0, 0, 0, (int)sa_sc, 0,
+                                                                         (int)(qsc_t[ks] >> (8 * db)));
+            asm volatile("" : "+v"(kv_acc[db])::"memory");
+          }
         }
       }
     }
-    if (lane == 0) lds_dscode[wave] = codes;
-    __syncthreads();  // dS_q of all four waves is in LDS
-    // This thread's part of the next query tile has landed (and the previous tile's dQ atomics,
-    // which had a whole iteration to drain, are done); this tile's atomics stay in flight.
-    wait_vm();
 
-    // ---- G5: dQ rows 32 wave.. of this tile = dS_q K over the 128 keys; atomics ----
+    // ---- G5: dQ block (query block wave & 3, d-blocks 2 half, 2 half + 1) = dS_q K; atomics ----
     // The FP16 static scale sigma (a power of two) is folded into dS_q's E8M0 code here, so the MFMA
     // returns sigma dQ exactly with no multiply.
     {
+      const int qb = kw;
       uint32_t a_sc[2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const int c = (int)((lds_dscode[2 * ks + hh] >> (8 * wave)) & 0xffu);
+        const int c = (int)lds_dscode[2 * ks + hh][qb];
         a_sc[ks] = c == 255 ? 255u : (uint32_t)min(max(c + p.log2_sigma, 0), 254);
       }
       mx_v8i dsa[2];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) dsa[ks] = lds_tr_operand(lds_ds, ks, 32 * wave, tr_row, tr_col, tr_swz);
-      // rows of the wave's block: 8 (v/4) + 4 hh + v%4; the v-dependent part is a scalar offset
-      const int qr0 = q0 + 32 * wave;
-      const bool full = qr0 + 32 <= Lq;  // wave-uniform: no row of this block is past the sequence
-      const uint32_t lane_row = (uint32_t)(4 * hh);
+      for (int ks = 0; ks < 2; ++ks) dsa[ks] = lds_tr_operand(lds_ds, ks, 32 * qb, tr_row, tr_col, tr_swz);
+      mx_v16f acc[2];
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        mx_v16f acc = mx_v16f{};
+      for (int e = 0; e < 2; ++e) {
+        const int db = 2 * half + e;
+        acc[e] = mx_v16f{};
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           mx_v8i kbt = lds_tr_operand(lds_k, ks, 32 * db, tr_row, tr_col, tr_swz);
-          acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(dsa[ks], kbt, acc, 0, 0, 0, (int)a_sc[ks], 0,
-                                                                (int)(kq_sc[ks] >> (8 * db)));
+          acc[e] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(dsa[ks], kbt, acc[e], 0, 0, 0, (int)a_sc[ks], 0,
+                                                                   (int)(kq_sc[ks] >> (8 * db)));
         }
-        // acc: column d = 32 db + r, rows 8 (v/4) + 4 hh + v%4 of the wave's 32-query block
-        if (!p.dq_fp16) {
-          const uint32_t lane_off = lane_row * C + 32 * db + r;
-#define MXFA_DQ32(V)                                                                              \
-  {                                                                                               \
-    const int rv = 8 * ((V) >> 2) + ((V) & 3);                                                    \
-    float* rowp = dq32 + (size_t)(qr0 + rv) * C; /* wave-uniform */                               \
-    if (full || qr0 + rv + (int)lane_row < Lq) unsafeAtomicAdd(rowp + lane_off, acc[V]);          \
-  }
-          MXFA_DQ32(0) MXFA_DQ32(1) MXFA_DQ32(2) MXFA_DQ32(3) MXFA_DQ32(4) MXFA_DQ32(5) MXFA_DQ32(6) MXFA_DQ32(7)
-          MXFA_DQ32(8) MXFA_DQ32(9) MXFA_DQ32(10) MXFA_DQ32(11) MXFA_DQ32(12) MXFA_DQ32(13) MXFA_DQ32(14)
-          MXFA_DQ32(15)
-#undef MXFA_DQ32
-        } else {
-          // Pair neighbouring columns: the even lane adds (row v, columns d, d+1), the odd lane adds
-          // (row v+1, columns d-1, d). One DPP swap with the neighbour lane per pair.
-          const uint32_t lane_off = (lane_row + (odd ? 1u : 0u)) * (uint32_t)(C >> 1) + (uint32_t)((32 * db + r) >> 1);
-#define MXFA_DQ16(V)                                                                              \
-  {                                                                                               \
-    const float send = odd ? acc[V] : acc[(V) + 1];                                               \
-    const float other = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), 0xB1, 0xF, 0xF, false)); \
-    const float lo = odd ? other : acc[V];                                                        \
-    const float hi = odd ? acc[(V) + 1] : other;                                                  \
-    const int rv = 8 * ((V) >> 2) + ((V) & 3);                                                    \
-    __half2* rowp = dq16 + (size_t)(qr0 + rv) * (C >> 1); /* wave-uniform */                      \
-    if (full || qr0 + rv + (int)lane_row + (odd ? 1 : 0) < Lq)                                    \
-      unsafeAtomicAdd(rowp + lane_off, __floats2half2_rn(lo, hi));                                \
-  }
-          MXFA_DQ16(0) MXFA_DQ16(2) MXFA_DQ16(4) MXFA_DQ16(6) MXFA_DQ16(8) MXFA_DQ16(10) MXFA_DQ16(12)
-          MXFA_DQ16(14)
-#undef MXFA_DQ16
+        asm volatile("" : "+v"(acc[e])::"memory");
+      }
+      // rows of the block: 8 (v/4) + 4 hh + v%4; the v-dependent part is a scalar offset
+      const int qr0 = q0 + 32 * qb;
+      const bool full = qr0 + 32 <= Lq;  // wave-uniform: no row of this block is past the sequence
+      const uint32_t lane_row = (uint32_t)(4 * hh);
+      // buffer over the block's 32 accumulator rows: scalar base, per-lane byte offset, scalar row offset
+      const uint32_t esize = p.dq_fp16 ? 2u : 4u;
+      const __amdgpu_buffer_rsrc_t dq_rsrc = mx_buffer_rsrc(
+          mx_uniform_ptr(reinterpret_cast<char*>(p.dq_acc) + ((q_start + qr0) * (int64_t)C + h * kD) * esize),
+          (uint32_t)__builtin_amdgcn_readfirstlane((int)(32u * C * esize)));
+      // acc[e]: column d = 32 db + r, rows 8 (v/4) + 4 hh + v%4 of the query block
+      auto atomics = [&](auto all_rows) {
+        constexpr bool FULL = decltype(all_rows)::value;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int db = 2 * half + e;
+          if (!p.dq_fp16) {
+            const int lane_boff = (int)((lane_row * C + 32 * db + r) * 4u);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int rv = 8 * (v >> 2) + (v & 3);
+              if (FULL || qr0 + rv + (int)lane_row < Lq)
+                __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[e][v], dq_rsrc, lane_boff, rv * C * 4, 0);
+            }
+          } else {
+            // Pair neighbouring columns: the even lane adds (row v, columns d, d+1), the odd lane adds
+            // (row v+1, columns d-1, d). One DPP swap with the neighbour lane per pair.
+            const int lane_boff =
+                (int)(((lane_row + (odd ? 1u : 0u)) * (uint32_t)(C >> 1) + (uint32_t)((32 * db + r) >> 1)) * 4u);
+#pragma unroll
+            for (int v = 0; v < 16; v += 2) {
+              const float a0 = acc[e][v], a1 = acc[e][v + 1];
+              const float send = mx_select(odd_lanes, a0, a1);
+              const float other =
+                  __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), 0xB1, 0xF, 0xF, false));
+              const float lo = mx_select(odd_lanes, other, a0);
+              const float hi = mx_select(odd_lanes, a1, other);
+              const int rv = 8 * (v >> 2) + (v & 3);
+              if (FULL || qr0 + rv + (int)lane_row + (odd ? 1 : 0) < Lq) {
+                const __half2 hv = __floats2half2_rn(lo, hi);
+                __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_v2f16(__builtin_bit_cast(mx_h2, hv), dq_rsrc, lane_boff,
+                                                                  rv * C * 2, 0);
+              }
+            }
+          }
         }
-        asm volatile("" ::: "memory");  // the next D-block's operand reads stay below these atomics
+      };
+      // Wait for this thread's part of the next query tile (issued at the top of the iteration).
+      // Vector memory operations complete in issue order, so allowing the atomics issued since then
+      // (16 FP16 or 32 FP32 per wave on full blocks) to stay in flight still covers the tile loads;
+      // the atomics drain behind the next tile's work instead of stalling this wave.
+      if (full) {
+        atomics(std::true_type{});
+        if (p.dq_fp16)
+          __builtin_amdgcn_s_waitcnt(kWaitVm16);
+        else
+          __builtin_amdgcn_s_waitcnt(kWaitVm32);
+      } else {
+        atomics(std::false_type{});
+        wait_vm();
       }
     }
     __syncthreads();  // every thread's part of the next tile has landed; all reads of this stage,
-                      // of dS_q and of the codes are done
+                      // of dS_q, of the partner operands and of the codes are done
   }
 
-  // ---- epilogue: dK = c dK, dV -> bf16 (accumulator: column d = 32 db + r, rows kv) ----
-  uint16_t* dkb = p.dk + (k_start + kv0 + 32 * wave) * (int64_t)C + h * kD;
-  uint16_t* dvb = p.dv + (k_start + kv0 + 32 * wave) * (int64_t)C + h * kD;
+  // ---- epilogue: half-0 waves store dV, half-1 waves dK = c dK (accumulator: column d = 32 db + r,
+  // rows kv 8 (v/4) + 4 hh + v%4 of the wave's key block) ----
+  uint16_t* outb = (half ? p.dk : p.dv) + (k_start + kv0 + 32 * kw) * (int64_t)C + h * kD;
+  const float mult = half ? p.c : 1.0f;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int kr = 8 * (v >> 2) + 4 * hh + (v & 3);
-      if (kv0 + 32 * wave + kr < Lk) {
-        const uint32_t idx = (uint32_t)(kr * C + 32 * db + r);
-        dkb[idx] = (uint16_t)f32_to_bf16(dk_acc[db][v] * p.c);
-        dvb[idx] = (uint16_t)f32_to_bf16(dv_acc[db][v]);
-      }
+      if (kv0 + 32 * kw + kr < Lk) outb[(uint32_t)(kr * C + 32 * db + r)] = (uint16_t)f32_to_bf16(kv_acc[db][v] * mult);
     }
 }
 
@@ -605,7 +640,7 @@ hipError_t launch_attn_bwd(const AttnProblem& a, const MxOperand& v_d, const MxO
   p.c = a.softmax_scale;
   p.dk = dk; p.dv = dv;
   if (p.total_items > 0) {
-    hipLaunchKernelGGL(attn_bwd_kernel, dim3((unsigned)p.total_items), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(attn_bwd_kernel, dim3((unsigned)p.total_items), dim3(64 * kWaves), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

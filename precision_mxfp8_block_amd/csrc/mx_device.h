@@ -23,6 +23,7 @@ typedef int mx_v4i __attribute__((ext_vector_type(4)));
 typedef int mx_v2i __attribute__((ext_vector_type(2)));
 typedef float mx_v16f __attribute__((ext_vector_type(16)));
 typedef float mx_v4f __attribute__((ext_vector_type(4)));
+typedef _Float16 mx_h2 __attribute__((ext_vector_type(2)));
 
 #define MX_LDS __attribute__((address_space(3)))
 
@@ -79,6 +80,62 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
   return d;
 }
 
+// max(acc, |a|, |b|) in one v_max3_f32 with absolute-value source modifiers (used for block maxima of
+// non-negative running values). A NaN operand does not propagate (IEEE maxNum), an infinity does.
+__device__ __forceinline__ float max3_abs(float acc, float a, float b) {
+  float d;
+  asm("v_max3_f32 %0, %1, |%2|, |%3|" : "=v"(d) : "v"(acc), "v"(a), "v"(b));
+  return d;
+}
+
+// Raw buffer resource over [base, base + bytes) (stride 0; gfx9-family word 3: 32-bit data format).
+// Buffer atomics take a scalar base, a 32-bit per-lane offset and a scalar offset, so a wave-uniform
+// row pointer costs no per-lane 64-bit address arithmetic.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t mx_buffer_rsrc(void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, 0x00020000);
+}
+
+// A pointer the caller knows to be wave-uniform, moved to scalar registers (a buffer resource built
+// from a value in vector registers would need a loop over its distinct values).
+__device__ __forceinline__ void* mx_uniform_ptr(void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  return reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+}
+
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane l's 16 bytes at
+// base + voff land at lds_dst + 16 l. Written as asm so that the compiler does not treat later LDS
+// reads as dependent on it (it would wait for every outstanding vector memory operation before the
+// next LDS read); the caller waits (s_waitcnt vmcnt) before reading the destination. lds_dst and base
+// must be wave-uniform. M0 carries the LDS address; no other code here keeps a value in M0.
+__device__ __forceinline__ void mx_lds_dma16(MX_LDS void* lds_dst, const void* base, uint32_t voff) {
+  const uint32_t m = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)lds_dst);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m), "v"(voff), "s"(mx_uniform_ptr((void*)base))
+               : "memory");
+}
+
+// The same for 4 bytes per lane (global_load_lds_dword): lane l's word lands at lds_dst + 4 l.
+__device__ __forceinline__ void mx_lds_dma4(MX_LDS void* lds_dst, const void* base, uint32_t voff) {
+  const uint32_t m = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)lds_dst);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(m), "v"(voff), "s"(mx_uniform_ptr((void*)base))
+               : "memory");
+}
+
+// The same with a 64-bit per-lane address (the lanes may read from different arrays).
+__device__ __forceinline__ void mx_lds_dma4_addr(MX_LDS void* lds_dst, const void* addr) {
+  const uint32_t m = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)lds_dst);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(m), "v"(addr) : "memory");
+}
+
+// v_cndmask_b32 with a lane mask held in an SGPR pair: mask bit set -> if_set, else if_clear. Written
+// as asm so that a select between two elements of one vector is not turned into an indexed extract.
+__device__ __forceinline__ float mx_select(uint64_t mask, float if_set, float if_clear) {
+  float d;
+  asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(d) : "v"(if_clear), "v"(if_set), "s"(mask));
+  return d;
+}
+
 // XOR swizzle of the 16-byte chunk index inside a 128-byte LDS row. With 64 four-byte banks, a
 // wave's 16-byte row reads (16 consecutive rows, one chunk) and the transposed 8-byte reads of
 // ds_read_b64_tr_b8 (rows {0-3, 8-11} or {4-7, 12-15} of a 16-row group, two adjacent chunks) both
@@ -115,6 +172,14 @@ __device__ __forceinline__ int64_t block_sum_i64(int64_t v, int64_t* red) {
   return t;
 }
 
+// A 64-bit value the caller knows to be wave-uniform, moved to scalar registers (so that addresses
+// derived from it stay scalar and uniform loads become scalar loads).
+__device__ __forceinline__ int64_t mx_uniform_i64(int64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // Offsets of sequence s in the compact and padded layouts, computed by the whole workgroup from
 // the device cu_seqlens: blocks32 = sum_{r<s} ceil(L_r/32), padded = sum_{r<s} round_up(L_r,128).
 struct SeqOffsets {
@@ -129,7 +194,7 @@ __device__ __forceinline__ SeqOffsets seq_offsets(const int32_t* cu, int s, int6
     p += (L + 127) >> 7;
   }
   SeqOffsets o;
-  o.blocks32 = block_sum_i64(b, red);
-  o.padded = block_sum_i64(p, red) << 7;
+  o.blocks32 = mx_uniform_i64(block_sum_i64(b, red));
+  o.padded = mx_uniform_i64(block_sum_i64(p, red)) << 7;
   return o;
 }
