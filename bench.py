@@ -144,11 +144,11 @@ def main():
     dq = torch.empty((T, C), dtype=torch.bfloat16, device="cuda")
     dk = torch.empty_like(dq)
     dv = torch.empty_like(dq)
-    ws_bytes = mx.mxfa_bwd_workspace_size(T, H, D, args.dq_mode)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     attn = mx.AttnArgs(mx.MxOperand(qd, qs, mx.SQ32), mx.MxOperand(kd, ks, mx.SQ32), mx.MxOperand(vd_, vs, mx.COL32),
                        cu_d, cu_d, B, N, N, T, T, H, D, c, False)
     vop, doop = mx.MxOperand(vrd, vrs, mx.ROW32), mx.MxOperand(dod, dos, mx.SQ32)
+    ws_bytes = mx.mxfa_bwd_workspace_size(attn, args.dq_mode)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
 
     names = ("quant", "fwd", "bwd")
     ev = {n: [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)] for n in names}
@@ -185,9 +185,8 @@ def main():
     wall = time.perf_counter() - t0
     print(f"# timed {args.steps} steps in {wall:.3f} s", file=sys.stderr, flush=True)
 
-    # the backward once more with FP32 dQ (own workspace), timed on the same stream
-    ws32_bytes = mx.mxfa_bwd_workspace_size(T, H, D, 0)
-    ws32 = torch.empty(ws32_bytes, dtype=torch.uint8, device="cuda")
+    # the backward once more with FP32 dQ, timed on the same stream
+    ws32, ws32_bytes = ws, ws_bytes  # the workspace layout does not depend on the dQ mode
     n32 = 5
     e32 = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n32)]
     for i in range(n32 + 1):

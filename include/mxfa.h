@@ -134,13 +134,19 @@ int64_t mxfa_padded_token_rows(const int32_t* cu_seqlens_host, int nseq);
  *   lse: fp32 [H][T_q]; rows of a sequence with no keys get O = 0 and LSE = -inf. */
 mxfa_status mxfa_fwd(const mxfa_attn_args* a, uint16_t* o, float* lse, void* stream);
 
-/* Workspace bytes mxfa_bwd needs: the dQ accumulator [T_q, H*D] (FP32 or FP16) plus two fp32
- * [H][T_q] row vectors (Delta and the softmax exponent offsets), each 256-byte aligned. */
-size_t mxfa_bwd_workspace_size(int64_t total_q, int num_heads, int head_dim, mxfa_dq_mode dq_mode);
+/* Workspace bytes mxfa_bwd needs for problem `a` (host struct; only nseq, max_seqlen_q/k, total_q and
+ * num_heads are read): one 16 KB FP8 dS tile plus 16 bytes of block codes per (head, sequence,
+ * 128-query tile, 128-key tile) of the longest sequences, i.e. H * nseq * ceil(max_q/128) *
+ * ceil(max_k/128) tiles, then two fp32 [H][T_q] row vectors (Delta and the softmax exponent
+ * offsets); each region 256-byte aligned. 0 if `a` is NULL or malformed. The size does not depend
+ * on dq_mode. */
+size_t mxfa_bwd_workspace_size(const mxfa_attn_args* a, mxfa_dq_mode dq_mode);
 
 /* Attention backward with recomputation [AE-TMEM: five GEMMs; Q, K and dO in square 32x32 blocks
  * so one E4M3 payload serves the plain and the transposed GEMM; dS quantized once per square block
  * with a wave-wide absolute maximum; dQ reduced in FP16 with a static scale, or in FP32].
+ * The dQ reduction runs over the KV tiles in order (per query tile: acc = fp16(acc + fp16(sigma
+ * dS_q K_tile)) or acc = fl32(acc + dS_q K_tile)), so the result is deterministic.
  *   a        : the forward's problem; q and k must be SQ32, v is ignored here
  *   v_d      : V quantized along D (ROW32 or SQ32), padded layout, for dP = dO V^T
  *   dout     : dO quantized SQ32, padded layout

@@ -62,7 +62,7 @@ def _load():
     lib.mxfa_padded_token_rows.argtypes = [P, i32]
     lib.mxfa_padded_token_rows.restype = i64
     lib.mxfa_fwd.argtypes = [ctypes.POINTER(_AttnArgs), P, P, P]
-    lib.mxfa_bwd_workspace_size.argtypes = [i64, i32, i32, i32]
+    lib.mxfa_bwd_workspace_size.argtypes = [ctypes.POINTER(_AttnArgs), i32]
     lib.mxfa_bwd_workspace_size.restype = ctypes.c_size_t
     lib.mxfa_bwd.argtypes = [ctypes.POINTER(_AttnArgs), _Mx, _Mx, P, P, P, i32, f32, P, ctypes.c_size_t, P, P, P, P]
     lib.mxfa_rmsnorm_quantize.argtypes = [P, i64, i64, i32, P, f32, P, i32, i32, P, P, P, P]
@@ -166,8 +166,10 @@ def mxfa_fwd(args, o, lse, stream=None):
     _check(_load().mxfa_fwd(ctypes.byref(a), _ptr(o), _ptr(lse), _stream(stream)), "mxfa_fwd")
 
 
-def mxfa_bwd_workspace_size(total_q, num_heads, head_dim, dq_mode):
-    return int(_load().mxfa_bwd_workspace_size(total_q, num_heads, head_dim, dq_mode))
+def mxfa_bwd_workspace_size(args, dq_mode):
+    """args: AttnArgs (or the ctypes struct)."""
+    a = args._c() if hasattr(args, "_c") else args
+    return int(_load().mxfa_bwd_workspace_size(ctypes.byref(a), dq_mode))
 
 
 def mxfa_bwd(args, v_d, dout, o, dout_bf16, lse, dq_mode, dq_static_scale, workspace, workspace_bytes, dq, dk, dv,
@@ -236,7 +238,7 @@ def bwd(args, v_d, dout, o, dout_bf16, lse, dq_mode=DQ_FP32, dq_static_scale=1.0
     """Returns (dq, dk, dv) bf16."""
     dev = args.q.data.device
     C = args.num_heads * args.head_dim
-    need = mxfa_bwd_workspace_size(args.total_q, args.num_heads, args.head_dim, dq_mode)
+    need = mxfa_bwd_workspace_size(args, dq_mode)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     dq = torch.empty((args.total_q, C), dtype=torch.bfloat16, device=dev)

@@ -180,9 +180,10 @@ mxfa_status mxfa_fwd(const mxfa_attn_args* a, uint16_t* o, float* lse, void* str
   return hip_status(mxfa::launch_attn_fwd(to_problem(a), o, lse, (hipStream_t)stream), fn);
 }
 
-size_t mxfa_bwd_workspace_size(int64_t total_q, int num_heads, int head_dim, mxfa_dq_mode dq_mode) {
-  if (total_q < 0 || num_heads < 1 || head_dim < 1) return 0;
-  return mxfa::bwd_workspace_bytes(total_q, num_heads, head_dim, dq_mode == MXFA_DQ_FP16_STATIC ? 1 : 0);
+size_t mxfa_bwd_workspace_size(const mxfa_attn_args* a, mxfa_dq_mode dq_mode) {
+  (void)dq_mode;  // the layout is the same for both reductions
+  if (!a || a->total_q < 0 || a->num_heads < 1 || a->nseq < 1 || a->max_seqlen_q < 0 || a->max_seqlen_k < 0) return 0;
+  return mxfa::bwd_workspace_bytes(a->total_q, a->num_heads, a->nseq, a->max_seqlen_q, a->max_seqlen_k);
 }
 
 mxfa_status mxfa_bwd(const mxfa_attn_args* a, mxfa_mx v_d, mxfa_mx dout, const uint16_t* o,
@@ -210,7 +211,7 @@ mxfa_status mxfa_bwd(const mxfa_attn_args* a, mxfa_mx v_d, mxfa_mx dout, const u
   if (dq_mode == MXFA_DQ_FP16_STATIC && !is_pow2(dq_static_scale))
     return fail(MXFA_ERR_INVALID, "%s: dq_static_scale=%g must be a positive power of two", fn,
                 (double)dq_static_scale);
-  const size_t need = mxfa_bwd_workspace_size(a->total_q, a->num_heads, a->head_dim, dq_mode);
+  const size_t need = mxfa_bwd_workspace_size(a, dq_mode);
   if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
     return fail(MXFA_ERR_INVALID, "%s: workspace NULL, misaligned or smaller than %zu bytes", fn, need);
   mxfa::MxOperand vv{v_d.data, v_d.scale, (int)v_d.mode};

@@ -10,8 +10,9 @@
 //   per KV tile (workgroup), per Q tile (inner loop):
 //     S = Q K^T;  P = exp(c S - LSE);  P_q = E4M3(P 2^8) at code 119
 //     dV += P_q^T dO;  dP = dO V^T;  dS = P (dP - Delta);  dS_q = SQ32(dS)
-//     dK += dS_q^T Q;  dQ_partial = dS_q K  -> atomically added (FP32, or FP16 holding sigma dQ)
-//   dK = c dK, dQ = c acc / sigma (finalize).
+//     dK += dS_q^T Q;  dS_q stored for the dQ kernel
+//   dK = c dK;  per Q tile (dQ kernel): dQ = c/sigma * reduction over KV tiles, in KV-tile order, of
+//   dS_q K (FP16 holding sigma dQ, or FP32).
 //
 // gfx950 layout choices:
 //  * Workgroup = 8 waves (two per SIMD) = one 128-row KV tile. Wave w owns key rows 32 (w & 3) ..
@@ -25,9 +26,12 @@
 //    query-half-0 wave accumulates dV, the query-half-1 wave dK, over all 128 queries of the tile.
 //    Each hands the other the packed operand it lacks (P_q or dS_q of its half, 2 KB) through LDS,
 //    so a wave holds one 32 x 128 FP32 accumulator and two waves fit on each SIMD.
-//  * dQ = dS K contracts over all 128 keys of the tile: dS_q goes to LDS key-major, each wave then
-//    computes one 32 x 64 block of the tile's dQ and adds it to the accumulator with coalesced
-//    buffer atomics (packed FP16 pairs or FP32).
+//  * dQ is not reduced with atomics: device-scope atomics on gfx950 are executed beyond the XCD's
+//    L2 and sustain about 1.3 TB/s of payload (measured), so 32 KV tiles x 67 MB of FP16 partials
+//    bound the backward at ~1.6 ms at 4 x 16 x 4096. Instead each (Q tile, KV tile) pair writes its
+//    16 KB dS_q tile (FP8, half the bytes of an FP16 partial, plain streaming stores) and the dQ
+//    kernel reads them back per Q tile and reduces dS_q K over the KV tiles in order, in FP16 with
+//    the static scale or in FP32, with no atomics and a deterministic result.
 //  * Q and dO tiles (and the tile's LSE and Delta) are double-buffered in LDS and fetched one tile
 //    ahead with direct global -> LDS loads; all LDS tiles use the forward's XOR swizzle.
 //  * P is produced as 256 P straight from exp2 (the static scale folded into the exponent); dS is
@@ -55,8 +59,7 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
 // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8; the
 // counters not waited on are at their maximum).
 constexpr int kWaitVm0 = 0x0F70;
-constexpr int kWaitVm16 = 0x4F70;
-constexpr int kWaitVm32 = 0x8F70;
+constexpr int kWaitVm2 = 0x0F72;
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(kWaitVm0); }
 
 constexpr int kWaves = 8;
@@ -132,14 +135,13 @@ __device__ __forceinline__ uint32_t wave_max_dpp(uint32_t v) {
 
 // ---------------------------------------------------------------------------------------------
 // Preprocess: Delta[h][t] = sum_d dO[t, h, d] * O[t, h, d] (fp32); the exponent offset of 256 P,
-// b[h][t] = 8 - LSE[h][t] log2(e) (so 256 P = exp2(c log2(e) S + b)); and zero the dQ accumulator.
+// b[h][t] = 8 - LSE[h][t] log2(e) (so 256 P = exp2(c log2(e) S + b)).
 // One wave per (token, head) row of 128: two bf16 pairs per lane.
 // ---------------------------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) bwd_preprocess_kernel(const uint16_t* __restrict__ o,
                                                              const uint16_t* __restrict__ dout,
                                                              const float* __restrict__ lse, int64_t T, int H,
-                                                             float* __restrict__ delta, float* __restrict__ pexp,
-                                                             uint32_t* __restrict__ acc, int64_t acc_words) {
+                                                             float* __restrict__ delta, float* __restrict__ pexp) {
   const int64_t gw = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   const int lane = threadIdx.x & 63;
   if (gw < T * H) {
@@ -155,10 +157,6 @@ __global__ void __launch_bounds__(256) bwd_preprocess_kernel(const uint16_t* __r
       pexp[(int64_t)h * T + t] = 8.0f - lse[(int64_t)h * T + t] * kLog2e;
     }
   }
-  // zero the accumulator (grid-stride over 16-byte words)
-  const int64_t nthreads = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < acc_words / 4; i += nthreads)
-    reinterpret_cast<uint4*>(acc)[i] = make_uint4(0, 0, 0, 0);
 }
 
 struct BwdParams {
@@ -173,9 +171,9 @@ struct BwdParams {
   const float* pexp;   // [H][Tq]: 8 - LSE log2(e)
   const float* delta;  // [H][Tq]
   int64_t Tq;
-  int dq_fp16;
-  int log2_sigma;  // FP16 static scale sigma = 2^log2_sigma (0 in FP32 mode)
-  void* dq_acc;  // [Tq, C] fp32 or fp16
+  int ntq_max, ntk_max;  // query / key tiles of the longest sequences (dS image grid)
+  uint8_t* ds_img;       // [H][nseq][ntq_max][ntk_max] 16 KB dS_q images
+  uint8_t* ds_codes;     // [H][nseq][ntq_max][ntk_max] 16 E8M0 codes
   float c;
   uint16_t *dk, *dv;
 };
@@ -284,8 +282,6 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_kernel(BwdParams p) {
   const int tr_row = 8 * (tb >> 2) + 4 * (grp >> 1) + (tb & 3);
   const int tr_col = 16 * (grp & 1) + 8 * ts;
   const int tr_swz = swz(tr_row);
-  const bool odd = r & 1;
-  const uint64_t odd_lanes = 0xAAAAAAAAAAAAAAAAull;
 
   wait_vm();
   __syncthreads();
@@ -462,93 +458,22 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_kernel(BwdParams p) {
       }
     }
 
-    // ---- G5: dQ block (query block wave & 3, d-blocks 2 half, 2 half + 1) = dS_q K; atomics ----
-    // The FP16 static scale sigma (a power of two) is folded into dS_q's E8M0 code here, so the MFMA
-    // returns sigma dQ exactly with no multiply.
+    // ---- dS_q of this (query tile, KV tile) pair to global memory for the dQ kernel: the 16 KB LDS
+    // image as it is (swizzled, key-major) and the 16 block codes; 2 KB per wave, 16 B per lane ----
     {
-      const int qb = kw;
-      uint32_t a_sc[2];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int c = (int)lds_dscode[2 * ks + hh][qb];
-        a_sc[ks] = c == 255 ? 255u : (uint32_t)min(max(c + p.log2_sigma, 0), 254);
-      }
-      mx_v8i dsa[2];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) dsa[ks] = lds_tr_operand(lds_ds, ks, 32 * qb, tr_row, tr_col, tr_swz);
-      mx_v16f acc[2];
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int db = 2 * half + e;
-        acc[e] = mx_v16f{};
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          mx_v8i kbt = lds_tr_operand(lds_k, ks, 32 * db, tr_row, tr_col, tr_swz);
-          acc[e] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(dsa[ks], kbt, acc[e], 0, 0, 0, (int)a_sc[ks], 0,
-                                                                   (int)(kq_sc[ks] >> (8 * db)));
-        }
-        asm volatile("" : "+v"(acc[e])::"memory");
-      }
-      // rows of the block: 8 (v/4) + 4 hh + v%4; the v-dependent part is a scalar offset
-      const int qr0 = q0 + 32 * qb;
-      const bool full = qr0 + 32 <= Lq;  // wave-uniform: no row of this block is past the sequence
-      const uint32_t lane_row = (uint32_t)(4 * hh);
-      // buffer over the block's 32 accumulator rows: scalar base, per-lane byte offset, scalar row offset
-      const uint32_t esize = p.dq_fp16 ? 2u : 4u;
-      const __amdgpu_buffer_rsrc_t dq_rsrc = mx_buffer_rsrc(
-          mx_uniform_ptr(reinterpret_cast<char*>(p.dq_acc) + ((q_start + qr0) * (int64_t)C + h * kD) * esize),
-          (uint32_t)__builtin_amdgcn_readfirstlane((int)(32u * C * esize)));
-      // acc[e]: column d = 32 db + r, rows 8 (v/4) + 4 hh + v%4 of the query block
-      auto atomics = [&](auto all_rows) {
-        constexpr bool FULL = decltype(all_rows)::value;
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int db = 2 * half + e;
-          if (!p.dq_fp16) {
-            const int lane_boff = (int)((lane_row * C + 32 * db + r) * 4u);
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const int rv = 8 * (v >> 2) + (v & 3);
-              if (FULL || qr0 + rv + (int)lane_row < Lq)
-                __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[e][v], dq_rsrc, lane_boff, rv * C * 4, 0);
-            }
-          } else {
-            // Pair neighbouring columns: the even lane adds (row v, columns d, d+1), the odd lane adds
-            // (row v+1, columns d-1, d). One DPP swap with the neighbour lane per pair.
-            const int lane_boff =
-                (int)(((lane_row + (odd ? 1u : 0u)) * (uint32_t)(C >> 1) + (uint32_t)((32 * db + r) >> 1)) * 4u);
-#pragma unroll
-            for (int v = 0; v < 16; v += 2) {
-              const float a0 = acc[e][v], a1 = acc[e][v + 1];
-              const float send = mx_select(odd_lanes, a0, a1);
-              const float other =
-                  __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), 0xB1, 0xF, 0xF, false));
-              const float lo = mx_select(odd_lanes, other, a0);
-              const float hi = mx_select(odd_lanes, a1, other);
-              const int rv = 8 * (v >> 2) + (v & 3);
-              if (FULL || qr0 + rv + (int)lane_row + (odd ? 1 : 0) < Lq) {
-                const __half2 hv = __floats2half2_rn(lo, hi);
-                __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_v2f16(__builtin_bit_cast(mx_h2, hv), dq_rsrc, lane_boff,
-                                                                  rv * C * 2, 0);
-              }
-            }
-          }
-        }
-      };
+      const int64_t tile = (((int64_t)h * p.nseq + s) * p.ntq_max + qt) * p.ntk_max + kt;
+      uint8_t* img = p.ds_img + tile * (kTile * kD);
+      const int o0 = wave_s * 2048 + lane * 16;
+      const uint4 w0 = *reinterpret_cast<const uint4*>(lds_ds + o0);
+      const uint4 w1 = *reinterpret_cast<const uint4*>(lds_ds + o0 + 1024);
+      *reinterpret_cast<uint4*>(img + o0) = w0;
+      *reinterpret_cast<uint4*>(img + o0 + 1024) = w1;
+      if (wave_s == 0 && lane == 0)
+        *reinterpret_cast<uint4*>(p.ds_codes + tile * 16) = *reinterpret_cast<const uint4*>(lds_dscode);
       // Wait for this thread's part of the next query tile (issued at the top of the iteration).
-      // Vector memory operations complete in issue order, so allowing the atomics issued since then
-      // (16 FP16 or 32 FP32 per wave on full blocks) to stay in flight still covers the tile loads;
-      // the atomics drain behind the next tile's work instead of stalling this wave.
-      if (full) {
-        atomics(std::true_type{});
-        if (p.dq_fp16)
-          __builtin_amdgcn_s_waitcnt(kWaitVm16);
-        else
-          __builtin_amdgcn_s_waitcnt(kWaitVm32);
-      } else {
-        atomics(std::false_type{});
-        wait_vm();
-      }
+      // Vector memory operations complete in issue order, so leaving the two stores issued since then
+      // in flight still covers the tile loads.
+      __builtin_amdgcn_s_waitcnt(kWaitVm2);
     }
     __syncthreads();  // every thread's part of the next tile has landed; all reads of this stage,
                       // of dS_q, of the partner operands and of the codes are done
@@ -567,36 +492,188 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_kernel(BwdParams p) {
     }
 }
 
-// dQ = bf16(c * acc / sigma)
-__global__ void __launch_bounds__(256) bwd_finalize_kernel(const void* __restrict__ acc, int dq_fp16, float mult,
-                                                           int64_t n, uint16_t* __restrict__ dq) {
-  const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
-  if (i >= n) return;
-  float v[4];
-  if (dq_fp16) {
-    const __half2* a = reinterpret_cast<const __half2*>(acc) + i / 2;
-    float2 x0 = __half22float2(a[0]), x1 = __half22float2(a[1]);
-    v[0] = x0.x; v[1] = x0.y; v[2] = x1.x; v[3] = x1.y;
-  } else {
-    float4 x = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(acc) + i);
-    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+// ---------------------------------------------------------------------------------------------
+// dQ = c * sum over KV tiles of dS_q K, reduced in KV-tile order: per tile, the 32 x 32 x 128 partial
+// of an MFMA block is added either in FP16 holding sigma dQ (acc = fp16(acc + fp16(sigma partial)),
+// the static scale folded into dS_q's E8M0 code) or in FP32 (acc = fl32(acc + partial)); then
+// dQ = bf16(c acc / sigma). One workgroup of 8 waves per (sequence, head, 128-query tile); wave w
+// owns query block w & 3 and d-blocks 2 (w >> 2), 2 (w >> 2) + 1. The dS_q images and the K tiles
+// are double-buffered in LDS with direct loads.
+// ---------------------------------------------------------------------------------------------
+struct DqParams {
+  const uint8_t* k;
+  const uint8_t* k_scale;
+  const int32_t *cu_q, *cu_k;
+  int nseq, H, ntq_max, ntk_max;
+  int total_items;
+  int causal;
+  const uint8_t* ds_img;
+  const uint8_t* ds_codes;
+  int dq_fp16;
+  int log2_sigma;  // sigma = 2^log2_sigma (0 in FP32 mode)
+  float mult;      // c / sigma
+  uint16_t* dq;
+};
+
+__global__ void __launch_bounds__(512, 1) attn_dq_kernel(DqParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_img0[kTile * kD];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_img1[kTile * kD];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_kt0[kTile * kD];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_kt1[kTile * kD];
+  __shared__ __attribute__((aligned(256))) uint32_t lds_codes[2][64];
+  __shared__ __attribute__((aligned(256))) uint32_t lds_ksc[2][64];
+  __shared__ int64_t red[16];
+
+  const int item = xcd_remap((int)blockIdx.x, p.total_items);
+  const int qt = item % p.ntq_max;
+  const int h = (item / p.ntq_max) % p.H;
+  const int s = item / (p.ntq_max * p.H);
+  const int64_t q_start = p.cu_q[s], k_start = p.cu_k[s];
+  const int Lq = p.cu_q[s + 1] - (int)q_start;
+  const int Lk = p.cu_k[s + 1] - (int)k_start;
+  const int q0 = qt * kTile;
+  if (q0 >= Lq) return;  // uniform over the workgroup
+  const SeqOffsets koff = seq_offsets(p.cu_k, s, red);
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const int qb = wave_s & 3, half = wave_s >> 2;
+  const int r = lane & 31, hh = lane >> 5;
+  const int C = p.H * kD;
+  const int Cs = C >> 5;
+  const TileLane tl = tile_lane(wave, lane, C);
+  int ntk = (Lk + kTile - 1) / kTile;
+  if (p.causal) ntk = min(ntk, qt + 1);  // key tiles past the query tile are fully masked
+
+  const uint8_t* kbase = (const uint8_t*)mx_uniform_ptr((void*)(p.k + k_start * (int64_t)C + h * kD));
+  const int64_t tile0 = (((int64_t)h * p.nseq + s) * p.ntq_max + qt) * p.ntk_max;  // image of key tile 0
+  const uint8_t* img_base = (const uint8_t*)mx_uniform_ptr((void*)(p.ds_img + tile0 * (kTile * kD)));
+  const uint8_t* code_base = p.ds_codes + tile0 * 16;
+  const uint8_t* ksc_base = p.k_scale + (koff.padded / 32) * (int64_t)Cs + h * 4;
+  auto issue_loads = [&](int kt, uint8_t* img, uint8_t* ktile, uint32_t* codes, uint32_t* kscw) {
+    // the dS_q image is copied as it is (2 KB per wave, 16 B per lane)
+#pragma unroll
+    for (int c = 0; c < kPieces; ++c) {
+      const uint32_t off = (uint32_t)((wave_s * kPieces + c) * 1024 + lane * 16);
+      mx_lds_dma16((MX_LDS void*)(img + (wave_s * kPieces + c) * 1024), img_base + (int64_t)kt * (kTile * kD), off);
+    }
+    issue_tile_load(ktile, kbase + (int64_t)kt * kTile * C, Lk - kt * kTile, C, tl, wave_s);
+    if (wave_s == 2) mx_lds_dma4_addr((MX_LDS void*)codes, code_base + (int64_t)kt * 16 + 4 * (lane & 3));
+    // K's scale words along D of the tile's four key blocks (lanes 0-3; the rest repeat them)
+    if (wave_s == 3) mx_lds_dma4_addr((MX_LDS void*)kscw, ksc_base + (int64_t)(4 * kt + (lane & 3)) * Cs);
+  };
+
+  // per-lane constants of the transposed LDS reads
+  const int grp = lane >> 4, gl = lane & 15;
+  const int tb = gl >> 1, ts = gl & 1;
+  const int tr_row = 8 * (tb >> 2) + 4 * (grp >> 1) + (tb & 3);
+  const int tr_col = 16 * (grp & 1) + 8 * ts;
+  const int tr_swz = swz(tr_row);
+
+  // accumulators of the wave's two 32 x 32 blocks: FP32 values, or FP16 pairs (rows v, v + 1)
+  mx_v16f acc32[2];
+  uint32_t acc16[2][8];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    acc32[e] = mx_v16f{};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc16[e][i] = 0u;
   }
-  uint2 out;
-  out.x = f32_to_bf16(v[0] * mult) | (f32_to_bf16(v[1] * mult) << 16);
-  out.y = f32_to_bf16(v[2] * mult) | (f32_to_bf16(v[3] * mult) << 16);
-  *reinterpret_cast<uint2*>(dq + i) = out;
+
+  if (ntk > 0) issue_loads(0, lds_img0, lds_kt0, lds_codes[0], lds_ksc[0]);
+  wait_vm();
+  __syncthreads();
+  for (int kt = 0; kt < ntk; ++kt) {
+    const int st = kt & 1;
+    const uint8_t* img = st ? lds_img1 : lds_img0;
+    const uint8_t* ktile = st ? lds_kt1 : lds_kt0;
+    const uint32_t* codes = lds_codes[st];
+    // K's scales along D for this tile (B operand: key block 2 ks + hh, d-block db)
+    uint32_t kq_sc[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) kq_sc[ks] = lds_ksc[st][2 * ks + hh];
+    if (kt + 1 < ntk)
+      issue_loads(kt + 1, st ? lds_img0 : lds_img1, st ? lds_kt0 : lds_kt1, lds_codes[st ^ 1], lds_ksc[st ^ 1]);
+    // dS_q scale of (key block 2 ks + hh, query block qb), sigma folded in for the FP16 reduction
+    uint32_t a_sc[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int c = (int)((codes[2 * ks + hh] >> (8 * qb)) & 0xffu);
+      a_sc[ks] = c == 255 ? 255u : (uint32_t)min(max(c + p.log2_sigma, 0), 254);
+    }
+    mx_v8i dsa[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) dsa[ks] = lds_tr_operand(img, ks, 32 * qb, tr_row, tr_col, tr_swz);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int db = 2 * half + e;
+      mx_v16f part = mx_v16f{};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        mx_v8i kbt = lds_tr_operand(ktile, ks, 32 * db, tr_row, tr_col, tr_swz);
+        part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(dsa[ks], kbt, part, 0, 0, 0, (int)a_sc[ks], 0,
+                                                               (int)(kq_sc[ks] >> (8 * db)));
+      }
+      if (p.dq_fp16) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          // fp16(acc + fp16(partial)): round the partial to FP16, then one FP16 addition
+          const uint32_t ph = (uint32_t)__builtin_bit_cast(uint32_t, __floats2half2_rn(part[2 * i], part[2 * i + 1]));
+          const __half2 sum = __hadd2(__builtin_bit_cast(__half2, acc16[e][i]), __builtin_bit_cast(__half2, ph));
+          acc16[e][i] = __builtin_bit_cast(uint32_t, sum);
+        }
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc32[e][v] += part[v];
+      }
+    }
+    wait_vm();
+    __syncthreads();  // the next tile has landed; all reads of this stage are done
+  }
+
+  // ---- epilogue: dQ = bf16(c acc / sigma); block rows 8 (v/4) + 4 hh + v%4, column 32 db + r ----
+  uint16_t* dqb = p.dq + (q_start + q0 + 32 * qb) * (int64_t)C + h * kD;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int db = 2 * half + e;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      float x;
+      if (p.dq_fp16) {
+        const float2 f = __half22float2(__builtin_bit_cast(__half2, acc16[e][v >> 1]));
+        x = (v & 1) ? f.y : f.x;
+      } else {
+        x = acc32[e][v];
+      }
+      const int qr = 8 * (v >> 2) + 4 * hh + (v & 3);
+      if (q0 + 32 * qb + qr < Lq) dqb[(uint32_t)(qr * C + 32 * db + r)] = (uint16_t)f32_to_bf16(x * p.mult);
+    }
+  }
 }
 
 }  // namespace
 
 namespace mxfa {
 
-// Workspace: dQ accumulator [Tq, H*D] (fp32 or fp16), then Delta [H][Tq] and the exponent offsets
-// [H][Tq] (fp32), each 256-byte aligned.
-size_t bwd_workspace_bytes(int64_t Tq, int H, int D, int dq_fp16) {
-  const size_t acc = (size_t)Tq * H * D * (dq_fp16 ? 2 : 4);
-  const size_t vec = ((size_t)Tq * H * 4 + 255) / 256 * 256;
-  return (acc + 255) / 256 * 256 + 2 * vec;
+// Workspace: the dS_q images [H][nseq][ntq_max][ntk_max] (16 KB each), their block codes (16 B
+// each), then Delta [H][Tq] and the exponent offsets [H][Tq] (fp32), each region 256-byte aligned.
+struct BwdWorkspace {
+  size_t img, codes, delta, pexp, total;
+};
+static BwdWorkspace bwd_workspace_layout(int64_t Tq, int H, int nseq, int max_q, int max_k) {
+  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t tiles = (size_t)H * nseq * ((max_q + kTile - 1) / kTile) * ((max_k + kTile - 1) / kTile);
+  BwdWorkspace w;
+  w.img = 0;
+  w.codes = al(tiles * kTile * kD);
+  w.delta = w.codes + al(tiles * 16);
+  w.pexp = w.delta + al((size_t)Tq * H * 4);
+  w.total = w.pexp + al((size_t)Tq * H * 4);
+  return w;
+}
+
+size_t bwd_workspace_bytes(int64_t Tq, int H, int nseq, int max_q, int max_k) {
+  return bwd_workspace_layout(Tq, H, nseq, max_q, max_k).total;
 }
 
 hipError_t launch_attn_bwd(const AttnProblem& a, const MxOperand& v_d, const MxOperand& dout, const uint16_t* o,
@@ -604,18 +681,17 @@ hipError_t launch_attn_bwd(const AttnProblem& a, const MxOperand& v_d, const MxO
                            uint16_t* dq, uint16_t* dk, uint16_t* dv, hipStream_t stream) {
   const int64_t Tq = a.total_q;
   const int C = a.H * kD;
-  const size_t acc_bytes = (size_t)Tq * C * (dq_fp16 ? 2 : 4);
+  const BwdWorkspace w = bwd_workspace_layout(Tq, a.H, a.nseq, a.max_seqlen_q, a.max_seqlen_k);
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
-  void* acc = ws;
-  float* delta = reinterpret_cast<float*>(ws + (acc_bytes + 255) / 256 * 256);
-  float* pexp = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(delta) + ((size_t)Tq * a.H * 4 + 255) / 256 * 256);
-  {
+  float* delta = reinterpret_cast<float*>(ws + w.delta);
+  float* pexp = reinterpret_cast<float*>(ws + w.pexp);
+  const int ntq_max = (a.max_seqlen_q + kTile - 1) / kTile;
+  const int ntk_max = (a.max_seqlen_k + kTile - 1) / kTile;
+  if (Tq > 0) {
     const int64_t rows = Tq * a.H;  // one wave per row
-    int64_t blocks = (rows + 3) / 4;
-    if (blocks < 1) blocks = 1;
-    const int64_t acc_words = (int64_t)((acc_bytes + 15) / 16 * 4);
+    const int64_t blocks = (rows + 3) / 4;
     hipLaunchKernelGGL(bwd_preprocess_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, o, dout_bf16, lse, Tq,
-                       a.H, delta, pexp, reinterpret_cast<uint32_t*>(acc), acc_words);
+                       a.H, delta, pexp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -625,18 +701,14 @@ hipError_t launch_attn_bwd(const AttnProblem& a, const MxOperand& v_d, const MxO
   p.v_row_shift = v_d.mode == 0 ? 0 : 5;
   p.cu_q = a.cu_q; p.cu_k = a.cu_k;
   p.nseq = a.nseq; p.H = a.H;
-  p.n_ktiles = (a.max_seqlen_k + kTile - 1) / kTile;
+  p.n_ktiles = ntk_max;
   p.total_items = p.n_ktiles * a.H * a.nseq;  // < 2^31, checked by the caller
   p.c2 = a.softmax_scale * kLog2e;
   p.causal = a.causal;
   p.pexp = pexp; p.delta = delta; p.Tq = Tq;
-  p.dq_fp16 = dq_fp16;
-  {
-    int e = 0;
-    std::frexp(dq_fp16 ? sigma : 1.0f, &e);  // sigma = 0.5 * 2^e exactly (a power of two, checked by the caller)
-    p.log2_sigma = e - 1;
-  }
-  p.dq_acc = acc;
+  p.ntq_max = ntq_max; p.ntk_max = ntk_max;
+  p.ds_img = ws + w.img;
+  p.ds_codes = ws + w.codes;
   p.c = a.softmax_scale;
   p.dk = dk; p.dv = dv;
   if (p.total_items > 0) {
@@ -644,11 +716,24 @@ hipError_t launch_attn_bwd(const AttnProblem& a, const MxOperand& v_d, const MxO
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int64_t n = Tq * C;
-  if (n > 0) {
-    const float mult = a.softmax_scale / (dq_fp16 ? sigma : 1.0f);
-    hipLaunchKernelGGL(bwd_finalize_kernel, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, stream, acc, dq_fp16,
-                       mult, n, dq);
+  DqParams d;
+  d.k = a.k.data; d.k_scale = a.k.scale;
+  d.cu_q = a.cu_q; d.cu_k = a.cu_k;
+  d.nseq = a.nseq; d.H = a.H; d.ntq_max = ntq_max; d.ntk_max = ntk_max;
+  d.total_items = ntq_max * a.H * a.nseq;
+  d.causal = a.causal;
+  d.ds_img = ws + w.img;
+  d.ds_codes = ws + w.codes;
+  d.dq_fp16 = dq_fp16;
+  {
+    int e = 0;
+    std::frexp(dq_fp16 ? sigma : 1.0f, &e);  // sigma = 0.5 * 2^e exactly (a power of two, checked by the caller)
+    d.log2_sigma = e - 1;
+  }
+  d.mult = a.softmax_scale / (dq_fp16 ? sigma : 1.0f);
+  d.dq = dq;
+  if (d.total_items > 0) {
+    hipLaunchKernelGGL(attn_dq_kernel, dim3((unsigned)d.total_items), dim3(64 * kWaves), 0, stream, d);
     return hipGetLastError();
   }
   return hipSuccess;

@@ -35,7 +35,7 @@ hipError_t launch_linear_quantize(const MxOperand& x, const MxOperand& w, int64_
                                   const int32_t* cu, int nseq, int max_seqlen, uint8_t* data, uint8_t* scale,
                                   uint8_t* scale_t, hipStream_t stream);
 hipError_t launch_attn_fwd(const AttnProblem& a, uint16_t* o, float* lse, hipStream_t stream);
-size_t bwd_workspace_bytes(int64_t Tq, int H, int D, int dq_fp16);
+size_t bwd_workspace_bytes(int64_t Tq, int H, int nseq, int max_q, int max_k);
 hipError_t launch_attn_bwd(const AttnProblem& a, const MxOperand& v_d, const MxOperand& dout, const uint16_t* o,
                            const uint16_t* dout_bf16, const float* lse, int dq_fp16, float sigma, void* workspace,
                            uint16_t* dq, uint16_t* dk, uint16_t* dv, hipStream_t stream);

@@ -114,7 +114,7 @@ def test_fwd_null_outputs():
 ])
 def test_bwd_argument_errors(kw, expect):
     a = _args(**kw.get("args", {}))
-    need = mx.mxfa_bwd_workspace_size(256, 1, 128, kw.get("dq_mode", 0) if kw.get("dq_mode", 0) in (0, 1) else 0)
+    need = mx.mxfa_bwd_workspace_size(a, 0)
     st = _lib().mxfa_bwd(ctypes.byref(a), mx._Mx(P, P, kw.get("vd_mode", 0)), mx._Mx(P, P, kw.get("do_mode", 2)), P, P,
                          P, kw.get("dq_mode", 0), kw.get("sigma", 1.0), kw.get("ws", P), kw.get("ws_bytes", need), P,
                          P, P, 0)
@@ -132,9 +132,15 @@ def test_scatter_and_rmsnorm_argument_errors():
 
 
 def test_workspace_size_and_padded_rows():
-    # dQ accumulator fp32/fp16 [Tq, H*D] + two fp32 [H][Tq] vectors, each rounded up to 256 bytes
-    assert mx.mxfa_bwd_workspace_size(1000, 2, 128, 0) == 1000 * 256 * 4 + 2 * ((8000 + 255) // 256 * 256)
-    assert mx.mxfa_bwd_workspace_size(1000, 2, 128, 1) == 1000 * 256 * 2 + 2 * ((8000 + 255) // 256 * 256)
+    # H * nseq * ceil(max_q/128) * ceil(max_k/128) dS tiles of 16 KB, their 16-byte code blocks, then two
+    # fp32 [H][Tq] vectors; each region rounded up to 256 bytes
+    a = _args(nseq=3, max_q=300, max_k=129, total_q=1000, total_k=1000, H=2)
+    tiles = 2 * 3 * 3 * 2
+    al = lambda x: (x + 255) // 256 * 256
+    expect = al(tiles * 16384) + al(tiles * 16) + 2 * al(1000 * 2 * 4)
+    assert mx.mxfa_bwd_workspace_size(a, 0) == expect
+    assert mx.mxfa_bwd_workspace_size(a, 1) == expect
+    assert mx.mxfa_bwd_workspace_size(_args(H=0), 0) == 0
     assert mx.mxfa_padded_token_rows(np.array([0, 1, 129, 129, 385], np.int32)) == 128 + 128 + 0 + 256
 
 
