@@ -56,11 +56,14 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
   return x * per + (x < rem ? x : rem) + slot;
 }
 
-// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8; the
-// counters not waited on are at their maximum).
-constexpr int kWaitVm0 = 0x0F70;
-constexpr int kWaitVm2 = 0x0F72;
-__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(kWaitVm0); }
+// Waits on the vector memory counter, written as asm: the direct LDS loads are asm too, so the
+// compiler does not see them and would drop a builtin wait it believes to be redundant.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_vm() { wait_vmcnt<0>(); }
 
 constexpr int kWaves = 8;
 constexpr int kPieces = kTile * kD / 1024 / kWaves;  // 1 KB pieces (64 lanes x 16 B) per wave per tile
@@ -136,26 +139,33 @@ __device__ __forceinline__ uint32_t wave_max_dpp(uint32_t v) {
 // ---------------------------------------------------------------------------------------------
 // Preprocess: Delta[h][t] = sum_d dO[t, h, d] * O[t, h, d] (fp32); the exponent offset of 256 P,
 // b[h][t] = 8 - LSE[h][t] log2(e) (so 256 P = exp2(c log2(e) S + b)).
-// One wave per (token, head) row of 128: two bf16 pairs per lane.
+// Sixteen lanes per (token, head) row of 128: eight bf16 of O and of dO per lane.
 // ---------------------------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) bwd_preprocess_kernel(const uint16_t* __restrict__ o,
                                                              const uint16_t* __restrict__ dout,
                                                              const float* __restrict__ lse, int64_t T, int H,
                                                              float* __restrict__ delta, float* __restrict__ pexp) {
-  const int64_t gw = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-  const int lane = threadIdx.x & 63;
-  if (gw < T * H) {
-    const int64_t t = gw / H;
-    const int h = (int)(gw % H);
-    const uint32_t a = *reinterpret_cast<const uint32_t*>(o + gw * kD + 2 * lane);
-    const uint32_t b = *reinterpret_cast<const uint32_t*>(dout + gw * kD + 2 * lane);
-    float sum = bf16_to_f32(a & 0xffffu) * bf16_to_f32(b & 0xffffu) + bf16_to_f32(a >> 16) * bf16_to_f32(b >> 16);
+  // 16 lanes per (token, head) row of 128: 8 bf16 of O and of dO per lane (16-byte loads)
+  const int64_t row = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 4;
+  const int g = threadIdx.x & 15;
+  const bool valid = row < T * H;
+  float sum = 0.0f;
+  if (valid) {
+    const uint4 a = *reinterpret_cast<const uint4*>(o + row * kD + 8 * g);
+    const uint4 b = *reinterpret_cast<const uint4*>(dout + row * kD + 8 * g);
+    const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
-    if (lane == 0) {
-      delta[(int64_t)h * T + t] = sum;
-      pexp[(int64_t)h * T + t] = 8.0f - lse[(int64_t)h * T + t] * kLog2e;
-    }
+    for (int i = 0; i < 4; ++i)
+      sum += bf16_to_f32(aw[i] & 0xffffu) * bf16_to_f32(bw[i] & 0xffffu) +
+             bf16_to_f32(aw[i] >> 16) * bf16_to_f32(bw[i] >> 16);
+  }
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 16);
+  if (valid && g == 0) {
+    const int64_t t = row / H;
+    const int h = (int)(row % H);
+    delta[(int64_t)h * T + t] = sum;
+    pexp[(int64_t)h * T + t] = 8.0f - lse[(int64_t)h * T + t] * kLog2e;
   }
 }
 
@@ -473,7 +483,7 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_kernel(BwdParams p) {
       // Wait for this thread's part of the next query tile (issued at the top of the iteration).
       // Vector memory operations complete in issue order, so leaving the two stores issued since then
       // in flight still covers the tile loads.
-      __builtin_amdgcn_s_waitcnt(kWaitVm2);
+      wait_vmcnt<2>();
     }
     __syncthreads();  // every thread's part of the next tile has landed; all reads of this stage,
                       // of dS_q, of the partner operands and of the codes are done
@@ -498,7 +508,7 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_kernel(BwdParams p) {
 // the static scale folded into dS_q's E8M0 code) or in FP32 (acc = fl32(acc + partial)); then
 // dQ = bf16(c acc / sigma). One workgroup of 8 waves per (sequence, head, 128-query tile); wave w
 // owns query block w & 3 and d-blocks 2 (w >> 2), 2 (w >> 2) + 1. The dS_q images and the K tiles
-// are double-buffered in LDS with direct loads.
+// stream through an LDS ring with direct loads.
 // ---------------------------------------------------------------------------------------------
 struct DqParams {
   const uint8_t* k;
@@ -515,13 +525,15 @@ struct DqParams {
   uint16_t* dq;
 };
 
+// LDS ring of (dS image, K tile) stages (a power of two). Two stages keep the LDS at 66 KB so two
+// workgroups share a CU, which measured faster than deeper prefetching with one workgroup per CU.
+constexpr int kDqStages = 2;
+
 __global__ void __launch_bounds__(512, 1) attn_dq_kernel(DqParams p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_img0[kTile * kD];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_img1[kTile * kD];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_kt0[kTile * kD];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_kt1[kTile * kD];
-  __shared__ __attribute__((aligned(256))) uint32_t lds_codes[2][64];
-  __shared__ __attribute__((aligned(256))) uint32_t lds_ksc[2][64];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_img[kDqStages][kTile * kD];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_kt[kDqStages][kTile * kD];
+  __shared__ __attribute__((aligned(256))) uint32_t lds_codes[kDqStages][64];
+  __shared__ __attribute__((aligned(256))) uint32_t lds_ksc[kDqStages][64];
   __shared__ int64_t red[16];
 
   const int item = xcd_remap((int)blockIdx.x, p.total_items);
@@ -580,20 +592,44 @@ __global__ void __launch_bounds__(512, 1) attn_dq_kernel(DqParams p) {
     for (int i = 0; i < 8; ++i) acc16[e][i] = 0u;
   }
 
-  if (ntk > 0) issue_loads(0, lds_img0, lds_kt0, lds_codes[0], lds_ksc[0]);
-  wait_vm();
-  __syncthreads();
+  // Each stage's loads are 4 vector memory operations per wave (5 for waves 2 and 3). Waiting for
+  // the oldest of the tiles in flight leaves the newer ones' operations outstanding (they complete
+  // in issue order). Supports up to three tiles in flight.
+  static_assert(kDqStages >= 2 && kDqStages <= 4 && (kDqStages & (kDqStages - 1)) == 0, "ring size");
+  const bool extra_op = wave_s == 2 || wave_s == 3;
+  auto wait_tile = [&](int newer) {
+    if (newer <= 0)
+      wait_vmcnt<0>();
+    else if (newer == 1) {
+      if (extra_op)
+        wait_vmcnt<5>();
+      else
+        wait_vmcnt<4>();
+    } else {
+      if (extra_op)
+        wait_vmcnt<10>();
+      else
+        wait_vmcnt<8>();
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < kDqStages - 1; ++i)
+    if (i < ntk) issue_loads(i, lds_img[i], lds_kt[i], lds_codes[i], lds_ksc[i]);
   for (int kt = 0; kt < ntk; ++kt) {
-    const int st = kt & 1;
-    const uint8_t* img = st ? lds_img1 : lds_img0;
-    const uint8_t* ktile = st ? lds_kt1 : lds_kt0;
+    const int st = kt & (kDqStages - 1);
+    wait_tile(min(kDqStages - 2, ntk - 1 - kt));
+    __syncthreads();  // tile kt has landed for every wave; all reads of the stage refilled below are done
+    if (kt + kDqStages - 1 < ntk) {
+      const int ns = (kt + kDqStages - 1) & (kDqStages - 1);
+      issue_loads(kt + kDqStages - 1, lds_img[ns], lds_kt[ns], lds_codes[ns], lds_ksc[ns]);
+    }
+    const uint8_t* img = lds_img[st];
+    const uint8_t* ktile = lds_kt[st];
     const uint32_t* codes = lds_codes[st];
     // K's scales along D for this tile (B operand: key block 2 ks + hh, d-block db)
     uint32_t kq_sc[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) kq_sc[ks] = lds_ksc[st][2 * ks + hh];
-    if (kt + 1 < ntk)
-      issue_loads(kt + 1, st ? lds_img0 : lds_img1, st ? lds_kt0 : lds_kt1, lds_codes[st ^ 1], lds_ksc[st ^ 1]);
     // dS_q scale of (key block 2 ks + hh, query block qb), sigma folded in for the FP16 reduction
     uint32_t a_sc[2];
 #pragma unroll
@@ -627,8 +663,6 @@ __global__ void __launch_bounds__(512, 1) attn_dq_kernel(DqParams p) {
         for (int v = 0; v < 16; ++v) acc32[e][v] += part[v];
       }
     }
-    wait_vm();
-    __syncthreads();  // the next tile has landed; all reads of this stage are done
   }
 
   // ---- epilogue: dQ = bf16(c acc / sigma); block rows 8 (v/4) + 4 hh + v%4, column 32 db + r ----
@@ -688,8 +722,8 @@ hipError_t launch_attn_bwd(const AttnProblem& a, const MxOperand& v_d, const MxO
   const int ntq_max = (a.max_seqlen_q + kTile - 1) / kTile;
   const int ntk_max = (a.max_seqlen_k + kTile - 1) / kTile;
   if (Tq > 0) {
-    const int64_t rows = Tq * a.H;  // one wave per row
-    const int64_t blocks = (rows + 3) / 4;
+    const int64_t rows = Tq * a.H;  // 16 lanes per row
+    const int64_t blocks = (rows + 15) / 16;
     hipLaunchKernelGGL(bwd_preprocess_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, o, dout_bf16, lse, Tq,
                        a.H, delta, pexp);
     hipError_t e = hipGetLastError();
