@@ -77,16 +77,22 @@ __device__ __forceinline__ void issue_tile_load(uint8_t* lds_tile, const uint8_t
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const uint32_t off = valid >= kTile ? toff[c] : (uint32_t)(min(trow[c], valid - 1) * C + tcol[c]);
-    __builtin_amdgcn_global_load_lds((const void*)(base + off), (MX_LDS void*)(lds_tile + (wave_s * 4 + c) * 1024),
-                                     16, 0, 0);
+    mx_lds_dma16((MX_LDS void*)(lds_tile + (wave_s * 4 + c) * 1024), base, off);
   }
 }
 
+// The direct LDS loads are inline asm (mx_lds_dma16/4): the compiler would otherwise wait for every
+// outstanding vector memory operation before the next LDS read, i.e. for the prefetch of the next
+// tile right after issuing it. Their waits are asm as well.
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
   // two stages x (K tile, V tile)
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2][2][kTile * kD];
+  // the tile's K scale words (one per key row) and V scale bytes (4 key blocks x 128 columns), copied
+  // with the tile
+  __shared__ __attribute__((aligned(512))) uint32_t lds_ksc[2][kTile];
+  __shared__ __attribute__((aligned(512))) uint32_t lds_vsc[2][kTile];
   __shared__ int64_t red[16];
 
   const int item = xcd_remap((int)blockIdx.x, p.total_items);
@@ -121,8 +127,8 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
     tcol[c] = 16 * ((pchunk & 7) ^ swz(pchunk >> 3));
     toff[c] = (uint32_t)(trow[c] * C + tcol[c]);
   }
-  const uint8_t* kbase = p.k + k_start * (int64_t)C + h * kD;
-  const uint8_t* vbase = p.v + k_start * (int64_t)C + h * kD;
+  const uint8_t* kbase = (const uint8_t*)mx_uniform_ptr((void*)(p.k + k_start * (int64_t)C + h * kD));
+  const uint8_t* vbase = (const uint8_t*)mx_uniform_ptr((void*)(p.v + k_start * (int64_t)C + h * kD));
   if (n_ktiles > 0) {
     issue_tile_load(lds[0][0], kbase, Lk, C, trow, tcol, toff, wave_s);
     issue_tile_load(lds[0][1], vbase, Lk, C, trow, tcol, toff, wave_s);
@@ -149,34 +155,27 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
       *reinterpret_cast<const uint32_t*>(p.q_scale + ((qoff.padded + qrow) >> p.q_row_shift) * (int64_t)Cs + h * 4) >>
       (8 * hh);
 
-  // K and V scales of a key tile: K along D per key row (4 rows per lane), V along the keys per
-  // column (8 per lane: 2 key steps x 4 D-blocks). The next tile's scales are loaded into the same
-  // registers right after their last use for the current tile.
-  // scale rows are addressed from wave-uniform bases with 32-bit per-lane offsets
+  // K and V scales of a key tile, copied into LDS with the tile: word l of lds_ksc is the K scale
+  // word (4 d-blocks) of key row kv0 + l (ROW32) or of its 32-row block (SQ32); lds_vsc holds, for
+  // key block vb = 0..3, the 128 V scale bytes of this head's columns (COL32) or its 4 d-block
+  // bytes (SQ32) at byte offset 128 vb. Waves 0-1 copy K, waves 2-3 copy V (64 words each).
   const uint8_t* ksbase = p.k_scale + (koff.padded >> p.k_row_shift) * (int64_t)Cs + h * 4;
   const uint8_t* vsbase = p.v_scale + (koff.padded >> 5) * (int64_t)(C >> p.v_col_shift);
   const int vcs = C >> p.v_col_shift;
-  // (raw 4-byte words; the per-lane byte shift is applied at use, so that no instruction consumes a
-  // load before the end-of-tile wait, which would also wait for the in-flight tile prefetch)
-  auto load_k_scales = [&](int kv0, uint32_t* ksc) {
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-      ksc[kb] = *reinterpret_cast<const uint32_t*>(ksbase + (uint32_t)(((kv0 + 32 * kb + r) >> p.k_row_shift) * Cs));
-  };
-  auto load_v_scales = [&](int kv0, uint32_t* vsc) {
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int vrow = (kv0 + 64 * ks + 32 * hh) >> 5;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-        vsc[ks * 4 + db] = vsbase[(uint32_t)(vrow * vcs + ((h * kD + 32 * db + r) >> p.v_col_shift))];
+  auto issue_scale_load = [&](int kv0, int st) {
+    const int l = 64 * (wave_s & 1) + lane;  // word index 0..127
+    if (wave_s < 2) {
+      const uint8_t* src = ksbase + (int64_t)(((kv0 + l) >> p.k_row_shift) * Cs);
+      mx_lds_dma4_addr((MX_LDS void*)&lds_ksc[st][64 * wave_s], src);
+    } else {
+      const int vb = l >> 5;
+      const int col = p.v_col_shift ? h * 4 : h * kD + 4 * (l & 31);
+      const uint8_t* src = vsbase + (int64_t)(((kv0 >> 5) + vb) * vcs + col);
+      mx_lds_dma4_addr((MX_LDS void*)&lds_vsc[st][64 * (wave_s & 1)], src);
     }
   };
+  if (n_ktiles > 0) issue_scale_load(0, 0);
   uint32_t ksc[4], vsc[8];
-  if (n_ktiles > 0) {
-    load_k_scales(0, ksc);
-    load_v_scales(0, vsc);
-  }
 
   float m = -INFINITY;  // running max of raw scores for query row qrow
   float lsum = 0.0f;    // this lane's half of the row sum of P * 256
@@ -199,11 +198,23 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
     const int st = kt & 1;
     const uint8_t* lds_k = lds[st][0];
     const uint8_t* lds_v = lds[st][1];
-    // prefetch the next tile (data straight into the other LDS stage, scales into VGPRs)
+    // this tile's scales (landed with the tile)
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) ksc[kb] = lds_ksc[st][32 * kb + r];
+    {
+      const uint8_t* vb8 = reinterpret_cast<const uint8_t*>(lds_vsc[st]);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+          vsc[ks * 4 + db] = vb8[128 * (2 * ks + hh) + (p.v_col_shift ? db : 32 * db + r)];
+    }
+    // prefetch the next tile (data and scales straight into the other LDS stage)
     if (kt + 1 < n_ktiles) {
       const int64_t next = (int64_t)(kv0 + kTile) * C;
       issue_tile_load(lds[st ^ 1][0], kbase + next, Lk - kv0 - kTile, C, trow, tcol, toff, wave_s);
       issue_tile_load(lds[st ^ 1][1], vbase + next, Lk - kv0 - kTile, C, trow, tcol, toff, wave_s);
+      issue_scale_load(kv0 + kTile, st ^ 1);
     }
 
     // ---- S^T = K Q^T : 4 key blocks of 32 x 2 D-steps of 64 ----
@@ -229,7 +240,6 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
       }
     }
 
-    if (kt + 1 < n_ktiles) load_k_scales(kv0 + kTile, ksc);
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- mask (ragged tail, causal diagonal) ----
@@ -317,7 +327,6 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
       }
     }
 
-    if (kt + 1 < n_ktiles) load_v_scales(kv0 + kTile, vsc);
     wait_vm();        // this thread's part of the next tile has landed in LDS
     __syncthreads();  // ... everyone's, and nobody still reads the stage the next prefetch overwrites
   }
