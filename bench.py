@@ -57,8 +57,8 @@ def bwd_source_hash():
 
 
 def measured_traffic():
-    """HBM bytes per backward call from the committed counter summary, or None when the backward
-    kernel sources changed since the counters were taken (or no summary exists)."""
+    """HBM bytes per backward call (its three kernels) from the committed counter summary, or None
+    when the backward kernel sources changed since the counters were taken (or no summary exists)."""
     import re
     if not os.path.exists(TRAFFIC_FILE):
         return None
@@ -211,7 +211,7 @@ def main():
     roof = {"bound": "mfma", "achieved": flops_dom / med[dominant] / 1e12, "peak": PEAK_MXFP8 / 1e12,
             "unit": "TFLOP/s", "frac": flops_dom / med[dominant] / PEAK_MXFP8,
             "traffic": measured_traffic() if dominant == "bwd" else None,
-            "kernel": "mxfa_bwd call: attn_bwd_kernel + bwd_preprocess_kernel + bwd_finalize_kernel"
+            "kernel": "mxfa_bwd call: bwd_preprocess_kernel + attn_bwd_kernel + attn_dq_kernel"
             if dominant == "bwd" else "attn_fwd_kernel",
             "launch_us": round(med[dominant] * 1e6, 2)}
     out = {
