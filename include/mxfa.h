@@ -59,10 +59,9 @@ typedef enum {
 typedef enum { MXFA_ROW32 = 0, MXFA_COL32 = 1, MXFA_SQ32 = 2 } mxfa_block;
 
 typedef enum {
-  MXFA_DQ_FP32 = 0,        /* dQ partials added atomically in FP32 [AE, Bench: FP32 dQ] */
-  MXFA_DQ_FP16_STATIC = 1  /* dQ partials times a static power-of-two scale sigma, added
-                              atomically in FP16 [AE-TMEM: dQ reduction in FP16 with static
-                              scaling; BR item 6] */
+  MXFA_DQ_FP32 = 0,        /* dQ partials of the KV tiles summed in FP32 [AE, Bench: FP32 dQ] */
+  MXFA_DQ_FP16_STATIC = 1  /* dQ partials times a static power-of-two scale sigma, summed in FP16
+                              [AE-TMEM: dQ reduction in FP16 with static scaling; BR item 6] */
 } mxfa_dq_mode;
 
 /* One MX operand: payload [T, C] (row stride C bytes) and its scale tensor in `mode`'s layout. */

@@ -1,5 +1,5 @@
 // MXFP8 attention backward for gfx950: recomputation with five scaled-MFMA GEMMs on square-block
-// (32 x 32) quantized Q, K and dO, online dS quantization, dQ reduced through global atomics.
+// (32 x 32) quantized Q, K and dO, online dS quantization, dQ reduced over the KV tiles in order.
 //
 // What is computed (andresseo.expert "MXFP8 FlashAttention-4 Hits 2.85 Petaflops...", section
 // "Inside the TMEM Bargain and Zero-Gather Jagged Pipeline": five GEMMs; Q, K and dO in square

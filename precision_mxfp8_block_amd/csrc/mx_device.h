@@ -23,7 +23,6 @@ typedef int mx_v4i __attribute__((ext_vector_type(4)));
 typedef int mx_v2i __attribute__((ext_vector_type(2)));
 typedef float mx_v16f __attribute__((ext_vector_type(16)));
 typedef float mx_v4f __attribute__((ext_vector_type(4)));
-typedef _Float16 mx_h2 __attribute__((ext_vector_type(2)));
 
 #define MX_LDS __attribute__((address_space(3)))
 
@@ -88,13 +87,6 @@ __device__ __forceinline__ float max3_abs(float acc, float a, float b) {
   return d;
 }
 
-// Raw buffer resource over [base, base + bytes) (stride 0; gfx9-family word 3: 32-bit data format).
-// Buffer atomics take a scalar base, a 32-bit per-lane offset and a scalar offset, so a wave-uniform
-// row pointer costs no per-lane 64-bit address arithmetic.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t mx_buffer_rsrc(void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, 0x00020000);
-}
-
 // A pointer the caller knows to be wave-uniform, moved to scalar registers (a buffer resource built
 // from a value in vector registers would need a loop over its distinct values).
 __device__ __forceinline__ void* mx_uniform_ptr(void* p) {
@@ -128,13 +120,6 @@ __device__ __forceinline__ void mx_lds_dma4_addr(MX_LDS void* lds_dst, const voi
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(m), "v"(addr) : "memory");
 }
 
-// v_cndmask_b32 with a lane mask held in an SGPR pair: mask bit set -> if_set, else if_clear. Written
-// as asm so that a select between two elements of one vector is not turned into an indexed extract.
-__device__ __forceinline__ float mx_select(uint64_t mask, float if_set, float if_clear) {
-  float d;
-  asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(d) : "v"(if_clear), "v"(if_set), "s"(mask));
-  return d;
-}
 
 // XOR swizzle of the 16-byte chunk index inside a 128-byte LDS row. With 64 four-byte banks, a
 // wave's 16-byte row reads (16 consecutive rows, one chunk) and the transposed 8-byte reads of
