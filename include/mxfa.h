@@ -136,7 +136,7 @@ mxfa_status mxfa_fwd(const mxfa_attn_args* a, uint16_t* o, float* lse, void* str
 /* Workspace bytes mxfa_bwd needs for problem `a` (host struct; only nseq, max_seqlen_q/k, total_q and
  * num_heads are read): one 16 KB FP8 dS tile plus 16 bytes of block codes per (head, sequence,
  * 128-query tile, 128-key tile) of the longest sequences, i.e. H * nseq * ceil(max_q/128) *
- * ceil(max_k/128) tiles, then two fp32 [H][T_q] row vectors (Delta and the softmax exponent
+ * ceil(max_k/128) tiles, then two fp32 [H][T_q] row vectors (-Delta and the softmax exponent
  * offsets); each region 256-byte aligned. 0 if `a` is NULL or malformed. The size does not depend
  * on dq_mode. */
 size_t mxfa_bwd_workspace_size(const mxfa_attn_args* a, mxfa_dq_mode dq_mode);

@@ -15,27 +15,35 @@
 //   dS_q K (FP16 holding sigma dQ, or FP32).
 //
 // gfx950 layout choices:
-//  * Workgroup = 8 waves (two per SIMD) = one 128-row KV tile. Wave w owns key rows 32 (w & 3) ..
-//    +31 and query half w >> 2 of every query tile (queries 64 (w >> 2) .. +63). Its K and V rows
-//    (from the K and V tiles in LDS) are the B operands of S = Q K^T and dP = dO V^T, so S and dP
-//    come out with one key per lane (column) and 16 queries per lane per 32-query block.
-//  * That accumulator layout is exactly the A operand of dV = P^T dO and dK = dS^T Q (one key per
-//    lane, contraction over queries): P_q and dS_q bytes are used in place, in the accumulator's
-//    query order; dO^T and Q^T are read from LDS with ds_read_b64_tr_b8 in the same order.
-//  * The two waves that share a key block split the accumulators instead of duplicating them: the
-//    query-half-0 wave accumulates dV, the query-half-1 wave dK, over all 128 queries of the tile.
-//    Each hands the other the packed operand it lacks (P_q or dS_q of its half, 2 KB) through LDS,
-//    so a wave holds one 32 x 128 FP32 accumulator and two waves fit on each SIMD.
+//  * Workgroup = 8 waves = one 128-row KV tile; waves w and w + 4 share a SIMD (measured) and own
+//    the same 32 keys (32 (w & 3) .. +31), with different roles. Producer waves (0-3) run G1 and G2
+//    (their K and V rows, the B operands, stay in registers for the whole loop, so S and dP come out
+//    with one key per lane and 16 queries per lane per 32-query block) and the elementwise part, and
+//    write P_q and dS_q to LDS. Consumer waves (4-7) hold dV and dK (32 x 128 FP32 each) and run G3
+//    and G4 one query tile behind, plus all global -> LDS copies and the dS_q image stores. The
+//    SIMD's one VALU-heavy wave and one MFMA-heavy wave overlap, and both stay within 256 VGPRs, so
+//    every MFMA keeps its accumulator in VGPRs.
+//  * The S and dP accumulator layout (one key per lane, contraction over queries) is exactly the A
+//    operand of dV = P^T dO and dK = dS^T Q: P_q and dS_q bytes are handed over in that order;
+//    dO^T and Q^T are read from LDS with ds_read_b64_tr_b8 in the same order.
+//  * The producer software-pipelines its four 32-query blocks: block j + 1's scaled MFMAs are in
+//    flight while block j's first elementwise half (exp2, dS, P_q, wave-wide maximum) runs beside
+//    block j - 1's second half (dS_q and the LDS writes); the last block's second half runs in the
+//    next period beside that tile's first loads and MFMAs.
+//  * dP - Delta comes out of the MFMA: the dP accumulator starts at -Delta (the preprocess stores
+//    the negated row sums).
 //  * dQ is not reduced with atomics: device-scope atomics on gfx950 are executed beyond the XCD's
 //    L2 and sustain about 1.3 TB/s of payload (measured), so 32 KV tiles x 67 MB of FP16 partials
 //    bound the backward at ~1.6 ms at 4 x 16 x 4096. Instead each (Q tile, KV tile) pair writes its
 //    16 KB dS_q tile (FP8, half the bytes of an FP16 partial, plain streaming stores) and the dQ
 //    kernel reads them back per Q tile and reduces dS_q K over the KV tiles in order, in FP16 with
 //    the static scale or in FP32, with no atomics and a deterministic result.
-//  * Q and dO tiles (and the tile's LSE and Delta) are double-buffered in LDS and fetched one tile
-//    ahead with direct global -> LDS loads; all LDS tiles use the forward's XOR swizzle.
+//  * Q and dO tiles (and the tile's LSE and Delta) pass through three LDS stages (the producers read
+//    tile k, the consumers tile k - 1, tile k + 1 lands) with direct global -> LDS loads; all LDS
+//    tiles use the forward's XOR swizzle.
 //  * P is produced as 256 P straight from exp2 (the static scale folded into the exponent); dS is
-//    carried as 256 dS, which shifts its E8M0 code by exactly 8 (power-of-two scaling is exact).
+//    carried as 256 dS, which shifts its E8M0 code by exactly 8 (power-of-two scaling is exact), and
+//    converted with the scaled FP8 conversion after clamping to +-448 times the block scale.
 #include <cmath>
 #include <type_traits>
 
@@ -65,21 +73,24 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 __device__ __forceinline__ void wait_vm() { wait_vmcnt<0>(); }
 
-constexpr int kWaves = 8;
-constexpr int kPieces = kTile * kD / 1024 / kWaves;  // 1 KB pieces (64 lanes x 16 B) per wave per tile
+constexpr int kBwdWaves = 8;  // main kernel: two waves per SIMD (a producer and a consumer)
+constexpr int kDqWaves = 8;   // dQ kernel: two waves per SIMD
 
-// Per-lane constants for filling a 128 x 128-byte swizzled LDS tile with direct global -> LDS loads:
-// lane piece c of wave w covers tile row trow[c], logical chunk byte offset tcol[c].
+// Per-lane constants for filling a 128 x 128-byte swizzled LDS tile with direct global -> LDS loads
+// by W waves: lane piece c of wave w covers tile row trow[c], logical chunk byte offset tcol[c].
+template <int W>
 struct TileLane {
+  static constexpr int kPieces = kTile * kD / 1024 / W;  // 1 KB pieces (64 lanes x 16 B) per wave
   int trow[kPieces], tcol[kPieces];
   uint32_t toff[kPieces];  // trow * C + tcol (full tiles)
 };
 
-__device__ __forceinline__ TileLane tile_lane(int wave, int lane, int C) {
-  TileLane t;
+template <int W>
+__device__ __forceinline__ TileLane<W> tile_lane(int wave, int lane, int C) {
+  TileLane<W> t;
 #pragma unroll
-  for (int c = 0; c < kPieces; ++c) {
-    const int p = (wave * kPieces + c) * 64 + lane;
+  for (int c = 0; c < TileLane<W>::kPieces; ++c) {
+    const int p = (wave * TileLane<W>::kPieces + c) * 64 + lane;
     t.trow[c] = p >> 3;
     t.tcol[c] = 16 * ((p & 7) ^ swz(p >> 3));
     t.toff[c] = (uint32_t)(t.trow[c] * C + t.tcol[c]);
@@ -89,12 +100,14 @@ __device__ __forceinline__ TileLane tile_lane(int wave, int lane, int C) {
 
 // Asynchronous copy of a tile whose first row is at `base` (this head's columns). Rows at or past
 // `valid` re-fetch the last valid row (finite data; their contributions are masked to zero).
+template <int W>
 __device__ __forceinline__ void issue_tile_load(uint8_t* lds_tile, const uint8_t* base, int valid, int C,
-                                                const TileLane& t, int wave_s) {
+                                                const TileLane<W>& t, int wave_s) {
+  constexpr int P = TileLane<W>::kPieces;
 #pragma unroll
-  for (int c = 0; c < kPieces; ++c) {
+  for (int c = 0; c < P; ++c) {
     const uint32_t off = valid >= kTile ? t.toff[c] : (uint32_t)(min(t.trow[c], valid - 1) * C + t.tcol[c]);
-    mx_lds_dma16((MX_LDS void*)(lds_tile + (wave_s * kPieces + c) * 1024), base, off);
+    mx_lds_dma16((MX_LDS void*)(lds_tile + (wave_s * P + c) * 1024), base, off);
   }
 }
 
@@ -124,27 +137,29 @@ __device__ __forceinline__ mx_v8i lds_tr_operand(const uint8_t* lds, int ks, int
   return mx_v8i{part[0].x, part[0].y, part[1].x, part[1].y, part[2].x, part[2].y, part[3].x, part[3].y};
 }
 
-// Maximum over the 64 lanes of a wave: DPP within rows of 16, one bpermute across rows, one
-// permlane32 swap across the halves.
+// Maximum over the 64 lanes of a wave: DPP within rows of 16, then permlane16 and permlane32 swaps
+// across rows (no LDS traffic).
 __device__ __forceinline__ uint32_t wave_max_dpp(uint32_t v) {
   v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
   v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
   v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x141, 0xF, 0xF, false));  // row_half_mirror
   v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x140, 0xF, 0xF, false));  // row_mirror
-  v = max(v, (uint32_t)__shfl_xor((int)v, 16, 64));
-  auto s = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-  return max((uint32_t)s[0], (uint32_t)s[1]);
+  auto s16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);  // rows 0 <-> 1, 2 <-> 3
+  v = max((uint32_t)s16[0], (uint32_t)s16[1]);
+  auto s32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);  // halves
+  return max((uint32_t)s32[0], (uint32_t)s32[1]);
 }
 
 // ---------------------------------------------------------------------------------------------
-// Preprocess: Delta[h][t] = sum_d dO[t, h, d] * O[t, h, d] (fp32); the exponent offset of 256 P,
-// b[h][t] = 8 - LSE[h][t] log2(e) (so 256 P = exp2(c log2(e) S + b)).
+// Preprocess: the negated row sums -Delta[h][t] = -sum_d dO[t, h, d] * O[t, h, d] (fp32, the
+// initial value of the dP accumulator) and the exponent offset of 256 P, b[h][t] = 8 - LSE[h][t]
+// log2(e) (so 256 P = exp2(c log2(e) S + b)).
 // Sixteen lanes per (token, head) row of 128: eight bf16 of O and of dO per lane.
 // ---------------------------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) bwd_preprocess_kernel(const uint16_t* __restrict__ o,
                                                              const uint16_t* __restrict__ dout,
                                                              const float* __restrict__ lse, int64_t T, int H,
-                                                             float* __restrict__ delta, float* __restrict__ pexp) {
+                                                             float* __restrict__ ndelta, float* __restrict__ pexp) {
   // 16 lanes per (token, head) row of 128: 8 bf16 of O and of dO per lane (16-byte loads)
   const int64_t row = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 4;
   const int g = threadIdx.x & 15;
@@ -164,7 +179,7 @@ __global__ void __launch_bounds__(256) bwd_preprocess_kernel(const uint16_t* __r
   if (valid && g == 0) {
     const int64_t t = row / H;
     const int h = (int)(row % H);
-    delta[(int64_t)h * T + t] = sum;
+    ndelta[(int64_t)h * T + t] = -sum;
     pexp[(int64_t)h * T + t] = 8.0f - lse[(int64_t)h * T + t] * kLog2e;
   }
 }
@@ -178,8 +193,8 @@ struct BwdParams {
   int total_items;
   float c2;  // c * log2(e)
   int causal;
-  const float* pexp;   // [H][Tq]: 8 - LSE log2(e)
-  const float* delta;  // [H][Tq]
+  const float* pexp;    // [H][Tq]: 8 - LSE log2(e)
+  const float* ndelta;  // [H][Tq]: -Delta
   int64_t Tq;
   int ntq_max, ntk_max;  // query / key tiles of the longest sequences (dS image grid)
   uint8_t* ds_img;       // [H][nseq][ntq_max][ntk_max] 16 KB dS_q images
@@ -188,15 +203,16 @@ struct BwdParams {
   uint16_t *dk, *dv;
 };
 
-__global__ void __launch_bounds__(512, 1) attn_bwd_kernel(BwdParams p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_k[kTile * kD];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_v[kTile * kD];         // V along D (for dP)
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_qd[2][2][kTile * kD];  // [stage][Q, dO]
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_ds[kTile * kD];        // dS_q, key-major [kv][q]
-  __shared__ __attribute__((aligned(1024))) uint4 lds_xchg[kWaves][2][64];     // operand handed to the partner
-  __shared__ __attribute__((aligned(512))) float lds_ld[2][2][kTile];          // [stage][8 - LSE log2e, Delta]
-  __shared__ __attribute__((aligned(256))) uint32_t lds_sc[2][64];             // [stage][Q, dO scale words]
-  __shared__ uint8_t lds_dscode[4][4];                                         // dS codes [kv block][q block]
+__global__ void __launch_bounds__(64 * kBwdWaves, 1) attn_bwd_kernel(BwdParams p) {
+  // [stage][Q, dO] tiles, three stages: the producers read tile k while the consumers read tile k - 1
+  // and tile k + 1 lands. The prologue parks the K and V tiles in stage 2.
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_qd[3][2][kTile * kD];
+  __shared__ __attribute__((aligned(1024))) uint4 lds_pq[4][4][64];  // P_q, lane order [key block][q block][lane]
+  __shared__ __attribute__((aligned(1024))) uint4 lds_sq[4][4][64];  // dS_q, lane order
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_ds[kTile * kD];  // dS_q image, key-major [kv][q], swizzled
+  __shared__ __attribute__((aligned(512))) float lds_ld[3][2][kTile];   // [stage][8 - LSE log2e, -Delta]
+  __shared__ __attribute__((aligned(256))) uint32_t lds_sc[3][64];      // [stage][Q, dO scale words]
+  __shared__ uint32_t lds_dscode[4];                                     // dS codes [key block] (byte: q block)
   __shared__ int64_t red[16];
 
   const int item = xcd_remap((int)blockIdx.x, p.total_items);
@@ -211,16 +227,16 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_kernel(BwdParams p) {
   const SeqOffsets qoff = seq_offsets(p.cu_q, s, red);
   const SeqOffsets koff = seq_offsets(p.cu_k, s, red);
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
-  const int kw = wave_s & 3;    // key block of this wave
-  const int half = wave_s >> 2;  // query half of every tile; 0: accumulates dV, 1: accumulates dK
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave_s = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kw = wave_s & 3;              // key block of this wave
+  const bool producer = wave_s < 4;      // waves 0-3: G1/G2 and the elementwise part; 4-7: G3/G4, loads
   const int r = lane & 31, hh = lane >> 5;
   const int C = p.H * kD;
   const int Cs = C >> 5;
   const int kv0 = kt * kTile;
-  const int kvrow = kv0 + 32 * kw + r;  // this lane's key row (B operands of S and dP)
-  const TileLane tl = tile_lane(wave, lane, C);
+  const int kvrow = kv0 + 32 * kw + r;  // this lane's key row
+  const TileLane<4> tl = tile_lane<4>(kw, lane, C);
 
   const int n_qtiles = (Lq + kTile - 1) / kTile;
   const int qt_begin = p.causal ? kt : 0;
@@ -229,28 +245,36 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_kernel(BwdParams p) {
   const uint8_t* qbase = (const uint8_t*)mx_uniform_ptr((void*)(p.q + q_start * (int64_t)C + h * kD));
   const uint8_t* dobase = (const uint8_t*)mx_uniform_ptr((void*)(p.dO + q_start * (int64_t)C + h * kD));
   const float* lse_base = (const float*)mx_uniform_ptr((void*)(p.pexp + (int64_t)h * p.Tq + q_start));
-  const float* del_base = (const float*)mx_uniform_ptr((void*)(p.delta + (int64_t)h * p.Tq + q_start));
-  // exponent offsets and Delta of a query tile: waves 0 and 1 each copy one 128-float vector (one
-  // 4-byte element per lane, two pieces of 64 lanes).
-  auto issue_ld_load = [&](int st, int q0) {
-    if (wave_s < 2) {
-      const float* src = wave_s == 0 ? lse_base : del_base;
+  const float* del_base = (const float*)mx_uniform_ptr((void*)(p.ndelta + (int64_t)h * p.Tq + q_start));
+  const uint8_t* qs_base = p.q_scale + (qoff.padded >> 5) * (int64_t)Cs + h * 4;
+  const uint8_t* ds_base = p.dO_scale + (qoff.padded >> 5) * (int64_t)Cs + h * 4;
+
+  // All global -> LDS copies are issued by the consumer waves: a query tile's Q and dO (four 1 KB
+  // pieces per wave each), its exponent offsets and -Delta (consumer waves 0 and 1, one 128-float
+  // vector each), its Q and dO scale words (consumer wave 2; lanes 0-3: Q blocks, 4-7: dO blocks).
+  auto issue_qtile = [&](int st, int qt) {
+    const int64_t q0 = (int64_t)qt * kTile;
+    issue_tile_load(lds_qd[st][0], (const uint8_t*)mx_uniform_ptr((void*)(qbase + q0 * C)), Lq - (int)q0, C, tl, kw);
+    issue_tile_load(lds_qd[st][1], (const uint8_t*)mx_uniform_ptr((void*)(dobase + q0 * C)), Lq - (int)q0, C, tl, kw);
+    if (kw < 2) {
+      const float* src = kw == 0 ? lse_base : del_base;
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const int row = min(q0 + c * 64 + lane, Lq - 1);
-        mx_lds_dma4((MX_LDS void*)(&lds_ld[st][wave_s][c * 64]), src, (uint32_t)row * 4u);
+        const int row = min((int)q0 + c * 64 + lane, Lq - 1);
+        mx_lds_dma4((MX_LDS void*)(&lds_ld[st][kw][c * 64]), src, (uint32_t)row * 4u);
       }
+    } else if (kw == 2) {
+      const int i = lane < 8 ? lane : 0;
+      const uint8_t* src = (i < 4 ? qs_base : ds_base) + (int64_t)((qt * 4 + (i & 3)) * Cs);
+      mx_lds_dma4_addr((MX_LDS void*)&lds_sc[st][0], src);
     }
   };
 
-  // prologue: K and V tiles, the first Q/dO tile and its LSE/Delta
-  issue_tile_load(lds_k, p.k + (k_start + kv0) * (int64_t)C + h * kD, Lk - kv0, C, tl, wave_s);
-  issue_tile_load(lds_v, p.v + (k_start + kv0) * (int64_t)C + h * kD, Lk - kv0, C, tl, wave_s);
-  if (qt_begin < n_qtiles) {
-    const int64_t q0 = (int64_t)qt_begin * kTile;
-    issue_tile_load(lds_qd[qt_begin & 1][0], qbase + q0 * C, Lq - (int)q0, C, tl, wave_s);
-    issue_tile_load(lds_qd[qt_begin & 1][1], dobase + q0 * C, Lq - (int)q0, C, tl, wave_s);
-    issue_ld_load(qt_begin & 1, (int)q0);
+  // prologue: K and V tiles into stage 2, the first query tile into stage 0
+  if (!producer) {
+    issue_tile_load(lds_qd[2][0], p.k + (k_start + kv0) * (int64_t)C + h * kD, Lk - kv0, C, tl, kw);
+    issue_tile_load(lds_qd[2][1], p.v + (k_start + kv0) * (int64_t)C + h * kD, Lk - kv0, C, tl, kw);
+    if (qt_begin < n_qtiles) issue_qtile(0, qt_begin);
   }
 
   // K (SQ32) and V (ROW32/SQ32) scales along D of this lane's key row: byte 0 = d-block hh, byte 2 =
@@ -260,31 +284,6 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_kernel(BwdParams p) {
   const uint32_t vsc_b =
       *reinterpret_cast<const uint32_t*>(p.v_scale + ((koff.padded + kvrow) >> p.v_row_shift) * (int64_t)Cs + h * 4) >>
       (8 * hh);
-  // K's scales for dQ = dS K (B operand: key block 2 ks + hh, d-block db): one word per key step
-  uint32_t kq_sc[2];
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
-    kq_sc[ks] =
-        *reinterpret_cast<const uint32_t*>(p.k_scale + ((koff.padded + kv0) / 32 + 2 * ks + hh) * (int64_t)Cs + h * 4);
-
-  // Q and dO scales of a query tile (SQ32): one word (4 d-blocks) per query block, raw. Wave 2 copies
-  // them into LDS with the tile (lanes 0-3: Q blocks, lanes 4-7: dO blocks, the rest repeat lane 0).
-  const uint8_t* qs_base = p.q_scale + (qoff.padded >> 5) * (int64_t)Cs + h * 4;
-  const uint8_t* ds_base = p.dO_scale + (qoff.padded >> 5) * (int64_t)Cs + h * 4;
-  auto issue_sc_load = [&](int st, int qt) {
-    if (wave_s == 2) {
-      const int i = lane < 8 ? lane : 0;
-      const uint8_t* src = (i < 4 ? qs_base : ds_base) + (int64_t)((qt * 4 + (i & 3)) * Cs);
-      mx_lds_dma4_addr((MX_LDS void*)&lds_sc[st][0], src);
-    }
-  };
-  if (qt_begin < n_qtiles) issue_sc_load(qt_begin & 1, qt_begin);
-  uint32_t qsc[4], dosc[4];
-
-  // dV (query-half-0 waves) or dK (query-half-1 waves) of this wave's 32 keys
-  mx_v16f kv_acc[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) kv_acc[i] = mx_v16f{};
 
   // per-lane constants of the transposed LDS reads
   const int grp = lane >> 4, gl = lane & 15;
@@ -296,210 +295,320 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_kernel(BwdParams p) {
   wait_vm();
   __syncthreads();
 
-  for (int qt = qt_begin; qt < n_qtiles; ++qt) {
-    const int q0 = qt * kTile;
-    const int st = qt & 1;
-    const uint8_t* lds_q = lds_qd[st][0];
-    const uint8_t* lds_do = lds_qd[st][1];
-    const float* pexp = lds_ld[st][0];
-    const float* dlt = lds_ld[st][1];
-    // prefetch the next query tile
-    // this tile's scale words (landed with the tile)
+  // Period k: the producers turn query tile k into P_q and dS_q, the consumers run G3 and G4 of tile
+  // k - 1 and fetch tile k + 1. Two workgroup barriers per period: B1 at the top (tile k has landed,
+  // everything of period k - 1 is done) and B2 once the consumers hold tile k - 1's P_q, dS_q and
+  // codes in registers (the producers may overwrite them). The two roles run separate loops with the
+  // same periods, so neither keeps the other's registers alive.
+  const int k_end = qt_begin < n_qtiles ? n_qtiles : qt_begin - 1;  // last period (none without tiles)
+  if (producer) {
+    // this wave's K and V rows, the B operands of S = Q K^T and dP = dO V^T, for the whole loop
+    const int krow = 32 * kw + r;
+    const mx_v8i kb0 = lds_row_operand(lds_qd[2][0], krow, 0, hh), kb1 = lds_row_operand(lds_qd[2][0], krow, 1, hh);
+    const mx_v8i vb0 = lds_row_operand(lds_qd[2][1], krow, 0, hh), vb1 = lds_row_operand(lds_qd[2][1], krow, 1, hh);
+    // The E8M0 code of a dS block from the exponent field of its |256 dS| maximum (wave-uniform, in
+    // scalar registers): code of 256 dS = efield - 8 (0 below, 255 for NaN/Inf), code of dS = that - 8;
+    // dS_q is E4M3 of 256 dS at scale 2^(cs - 127), cs = clamp(efield - 8, 8, 246) (the clamp only
+    // keeps the unused NaN-block values finite).
+    auto block_code = [](uint32_t efield, uint32_t& code, uint32_t& cs) {
+      asm("s_sub_u32 %1, %2, 8\n\t"      // cs = efield - 8 (wraps below 8)
+          "s_sub_u32 %0, %2, 16\n\t"     // code = efield - 16 ...
+          "s_cmp_lt_u32 %2, 16\n\t"
+          "s_cselect_b32 %0, 0, %0\n\t"  // ... 0 below 16
+          "s_cmp_ge_u32 %2, 255\n\t"
+          "s_cselect_b32 %0, 255, %0\n\t"  // NaN/Inf block
+          "s_max_u32 %1, %1, 8\n\t"
+          "s_cmp_lt_u32 %2, 8\n\t"
+          "s_cselect_b32 %1, 8, %1\n\t"
+          "s_min_u32 %1, %1, 246"
+          : "=&s"(code), "=&s"(cs)
+          : "s"(efield)
+          : "scc");
+    };
+    // Second half of block j's elementwise part: dS_q from 256 dS at the block's scale, and the LDS
+    // writes of P_q, dS_q (operand order) and of the dS_q image for the dQ kernel.
+    auto ew_b = [&](int j, const mx_v16f& dpacc, uint32_t code, uint32_t cs, const uint32_t (&pk)[4]) {
+      const float sc = __uint_as_float(cs << 23);
+      const float lim = __uint_as_float(((cs + 8u) << 23) | 0x600000u);  // 448 sc
+      uint32_t dsk[4];
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
-      qsc[qb] = lds_sc[st][qb];
-      dosc[qb] = lds_sc[st][4 + qb];
-    }
-    if (qt + 1 < n_qtiles) {
-      const int64_t nq0 = (int64_t)(q0 + kTile);
-      issue_sc_load(st ^ 1, qt + 1);
-      issue_tile_load(lds_qd[st ^ 1][0], (const uint8_t*)mx_uniform_ptr((void*)(qbase + nq0 * C)), Lq - (int)nq0, C,
-                      tl, wave_s);
-      issue_tile_load(lds_qd[st ^ 1][1], (const uint8_t*)mx_uniform_ptr((void*)(dobase + nq0 * C)), Lq - (int)nq0, C,
-                      tl, wave_s);
-      issue_ld_load(st ^ 1, (int)nq0);
-    }
-
-    // raw Q and dO scales for the B operands of G3 and G4 (query block 2 ks + hh, d-block db)
-    uint32_t qsc_t[2], dosc_t[2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      qsc_t[ks] = hh ? qsc[2 * ks + 1] : qsc[2 * ks];
-      dosc_t[ks] = hh ? dosc[2 * ks + 1] : dosc[2 * ks];
-    }
-    uint32_t qsc_c[2], dosc_c[2];  // this wave's query blocks' along-D scales for G1 and G2
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      qsc_c[j] = (half ? qsc[2 + j] : qsc[j]) >> (8 * hh);
-      dosc_c[j] = (half ? dosc[2 + j] : dosc[j]) >> (8 * hh);
-    }
-    const bool need_mask = (q0 + kTile > Lq) || (kv0 + kTile > Lk) || (p.causal && kv0 + kTile - 1 > q0);
-
-    // ---- per query block j of this wave's half: G1, G2 (S and dP), then 256 P, 256 dS ----
-    // (lane: key kvrow; queries 64 half + 32 j + 8 i + 4 hh + t). Two instantiations of the
-    // elementwise part behind one wave-uniform branch: interior tiles carry no mask code.
-    uint32_t pk[2][4], dsk[2][4], dscode[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int ql0 = 64 * half + 32 * j;  // first query of the block inside the tile
-      mx_v16f sacc, dpacc;
-      {
-        const int row = ql0 + r;       // query row (A operand)
-        const int krow = 32 * kw + r;  // key row (B operand), from the K and V tiles in LDS
-        mx_v8i qa0 = lds_row_operand(lds_q, row, 0, hh);
-        mx_v8i kb0 = lds_row_operand(lds_k, krow, 0, hh);
-        mx_v8i qa1 = lds_row_operand(lds_q, row, 1, hh);
-        mx_v8i kb1 = lds_row_operand(lds_k, krow, 1, hh);
-        sacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa0, kb0, mx_v16f{}, 0, 0, 0, (int)qsc_c[j], 0,
-                                                               (int)ksc_b);
-        sacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa1, kb1, sacc, 0, 0, 2, (int)qsc_c[j], 2, (int)ksc_b);
-        mx_v8i da0 = lds_row_operand(lds_do, row, 0, hh);
-        mx_v8i vb0 = lds_row_operand(lds_v, krow, 0, hh);
-        mx_v8i da1 = lds_row_operand(lds_do, row, 1, hh);
-        mx_v8i vb1 = lds_row_operand(lds_v, krow, 1, hh);
-        dpacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(da0, vb0, mx_v16f{}, 0, 0, 0, (int)dosc_c[j], 0,
-                                                                (int)vsc_b);
-        dpacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(da1, vb1, dpacc, 0, 0, 2, (int)dosc_c[j], 2,
-                                                                (int)vsc_b);
-        asm volatile("" : "+v"(sacc), "+v"(dpacc)::"memory");
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t w = mx_pack4_scaled(dpacc[4 * i], dpacc[4 * i + 1], dpacc[4 * i + 2], dpacc[4 * i + 3], sc, lim);
+        dsk[i] = code == 255u ? 0x7f7f7f7fu : w;
       }
-      auto elementwise = [&](auto masked) {
-        constexpr bool MASK = decltype(masked)::value;
-        float am = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          // the lane's 4 consecutive query rows ql0 + 8 i + 4 hh + (0..3)
-          const float4 pe4 = *reinterpret_cast<const float4*>(pexp + ql0 + 8 * i + 4 * hh);
-          const float4 dl4 = *reinterpret_cast<const float4*>(dlt + ql0 + 8 * i + 4 * hh);
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const int v = 4 * i + t;
-            const float pe = (&pe4.x)[t], dl = (&dl4.x)[t];
-            float e = __builtin_amdgcn_exp2f(fmaf(sacc[v], p.c2, pe));  // 256 P
-            if (MASK) {
-              const int qpos = q0 + ql0 + 8 * i + 4 * hh + t;
-              const bool ok = (kvrow < Lk) & (qpos < Lq) & ((p.causal == 0) | (kvrow <= qpos));
-              e = ok ? e : 0.0f;
-            }
-            const float dsv = e * (dpacc[v] - dl);  // 256 dS
-            sacc[v] = e;
-            dpacc[v] = dsv;
-          }
-          am = max3_abs(am, dpacc[4 * i], dpacc[4 * i + 1]);
-          am = max3_abs(am, dpacc[4 * i + 2], dpacc[4 * i + 3]);
-        }
-        // block maximum over the wave (one 32 x 32 block), code of dS = code of 256 dS - 8
-        const uint32_t c256 = mx_code_from_amax_bits(wave_max_dpp(__float_as_uint(am)));
-        dscode[j] = c256 == 255u ? 255u : (c256 > 8u ? c256 - 8u : 0u);
-        // 256 dS * 2^(127 - (code + 8)) = dS * 2^(127 - code)
-        const float inv = dscode[j] == 255u ? 0.0f : mx_inv_scale(dscode[j] + 8u);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pk[j][i] = mx_pack4_inrange(sacc[4 * i], sacc[4 * i + 1], sacc[4 * i + 2], sacc[4 * i + 3]);
-          const uint32_t w =
-              mx_pack4(dpacc[4 * i] * inv, dpacc[4 * i + 1] * inv, dpacc[4 * i + 2] * inv, dpacc[4 * i + 3] * inv);
-          dsk[j][i] = dscode[j] == 255u ? 0x7f7f7f7fu : w;
-        }
-      };
-      if (need_mask)
-        elementwise(std::true_type{});
-      else
-        elementwise(std::false_type{});
-    }
-
-    // ---- dS_q to LDS key-major [kv][q] (for dQ); the partner's operand; the block codes ----
-    {
-      const int kvl = 32 * kw + r;  // key row inside the tile
+      if (j == 0) __syncthreads();  // B2: the consumers hold their operands of tile k - 1 but block 3's
+      lds_pq[kw][j][lane] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+      lds_sq[kw][j][lane] = make_uint4(dsk[0], dsk[1], dsk[2], dsk[3]);
+      // the image: key row 32 kw + r, queries 32 j + 8 i + 4 hh .. +3
+      const int kvl = 32 * kw + r;
       const int sw = swz(kvl);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int ql = 64 * half + 32 * j + 8 * i + 4 * hh;
-          *reinterpret_cast<uint32_t*>(lds_ds + kvl * kD + 16 * ((ql >> 4) ^ sw) + (ql & 15)) = dsk[j][i];
-        }
-      // the dV wave (half 0) needs the other half's P_q, the dK wave (half 1) the other half's dS_q
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        lds_xchg[wave_s][j][lane] = half ? make_uint4(pk[j][0], pk[j][1], pk[j][2], pk[j][3])
-                                         : make_uint4(dsk[j][0], dsk[j][1], dsk[j][2], dsk[j][3]);
-      if (lane == 0) {
-        lds_dscode[kw][2 * half] = (uint8_t)dscode[0];
-        lds_dscode[kw][2 * half + 1] = (uint8_t)dscode[1];
+      for (int i = 0; i < 4; ++i) {
+        const int ql = 32 * j + 8 * i + 4 * hh;
+        *reinterpret_cast<uint32_t*>(lds_ds + kvl * kD + 16 * ((ql >> 4) ^ sw) + (ql & 15)) = dsk[i];
       }
-    }
-    __syncthreads();  // dS_q, the partner operands and the codes of all eight waves are in LDS
-
-    // ---- G3 (half-0 waves): dV += P_q^T dO;  G4 (half-1 waves): dK += dS_q^T Q; all 128 queries ----
-    {
-      const int partner = wave_s ^ 4;
-      const uint4 x0 = lds_xchg[partner][0][lane], x1 = lds_xchg[partner][1][lane];
-      const mx_v8i other{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-      if (half == 0) {
-        const mx_v8i own{(int)pk[0][0], (int)pk[0][1], (int)pk[0][2], (int)pk[0][3],
-                         (int)pk[1][0], (int)pk[1][1], (int)pk[1][2], (int)pk[1][3]};
+    };
+    // Block 3's second half is deferred into the next period, where it runs beside that tile's first
+    // loads and MFMAs (the consumers read block 3's operands and image chunks after B2).
+    mx_v16f ds3{};
+    uint32_t pk3[4] = {0u, 0u, 0u, 0u}, code3 = 0u, cs3 = 8u;
+    int st = 0;  // stage of tile k
+    for (int k = qt_begin; k <= k_end; ++k) {
+      __syncthreads();  // B1
+      if (k < n_qtiles) {
+        const int q0 = k * kTile;
+        const uint8_t* lds_q = lds_qd[st][0];
+        const uint8_t* lds_do = lds_qd[st][1];
+        const float* pexp = lds_ld[st][0];
+        const float* ndl = lds_ld[st][1];
+        uint32_t qsc[4], dosc[4];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const mx_v8i pa = ks == 0 ? own : other;
-#pragma unroll
-          for (int db = 0; db < 4; ++db) {
-            mx_v8i dob = lds_tr_operand(lds_do, ks, 32 * db, tr_row, tr_col, tr_swz);
-            kv_acc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(pa, dob, kv_acc[db], 0, 0, 0, 119, 0,
-                                                                         (int)(dosc_t[ks] >> (8 * db)));
-            asm volatile("" : "+v"(kv_acc[db])::"memory");
-          }
+        for (int qb = 0; qb < 4; ++qb) {
+          qsc[qb] = lds_sc[st][qb];
+          dosc[qb] = lds_sc[st][4 + qb];
         }
+        const bool need_mask = (q0 + kTile > Lq) || (kv0 + kTile > Lk) || (p.causal && kv0 + kTile - 1 > q0);
+
+        // Per query block j (lane: key kvrow; queries 32 j + 8 i + 4 hh + t): G1 and G2 (S and
+        // dP - Delta, the dP accumulator starting at -Delta), then 256 P and 256 dS with their E4M3
+        // codes. G1/G2 of block j + 1 are issued before block j's elementwise part. Two
+        // instantiations behind one wave-uniform branch: interior tiles carry no mask code.
+        auto tile_body = [&](auto masked) {
+          constexpr bool MASK = decltype(masked)::value;
+          // distinct first instructions keep the compiler from hoisting the two instantiations' common
+          // prologue above the branch (where it would hold registers across both)
+          if (MASK)
+            asm volatile("; masked tile" ::: "memory");
+          else
+            asm volatile("; interior tile" ::: "memory");
+          // Q and dO rows of block j (A operands of G1 and G2)
+          auto load_rows = [&](int j, mx_v8i (&a)[4]) {
+            const int row = 32 * j + r;
+            a[0] = lds_row_operand(lds_q, row, 0, hh);
+            a[1] = lds_row_operand(lds_q, row, 1, hh);
+            a[2] = lds_row_operand(lds_do, row, 0, hh);
+            a[3] = lds_row_operand(lds_do, row, 1, hh);
+          };
+          // exponent offsets of block j's 16 query rows, and -Delta as the dP accumulator's start
+          auto load_pe = [&](int j, float4 (&pe)[4]) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pe[i] = *reinterpret_cast<const float4*>(pexp + 32 * j + 8 * i + 4 * hh);
+          };
+          auto load_nd = [&](int j, mx_v16f& dpacc) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float4 nd4 = *reinterpret_cast<const float4*>(ndl + 32 * j + 8 * i + 4 * hh);
+              dpacc[4 * i] = nd4.x;
+              dpacc[4 * i + 1] = nd4.y;
+              dpacc[4 * i + 2] = nd4.z;
+              dpacc[4 * i + 3] = nd4.w;
+            }
+          };
+          auto g1 = [&](int j, const mx_v8i (&a)[4], mx_v16f& sacc) {
+            const uint32_t qs = qsc[j] >> (8 * hh);
+            sacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[0], kb0, mx_v16f{}, 0, 0, 0, (int)qs, 0,
+                                                                   (int)ksc_b);
+            sacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[1], kb1, sacc, 0, 0, 2, (int)qs, 2, (int)ksc_b);
+          };
+          auto g2 = [&](int j, const mx_v8i (&a)[4], mx_v16f& dpacc) {
+            const uint32_t dos = dosc[j] >> (8 * hh);
+            dpacc =
+                __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[2], vb0, dpacc, 0, 0, 0, (int)dos, 0, (int)vsc_b);
+            dpacc =
+                __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[3], vb1, dpacc, 0, 0, 2, (int)dos, 2, (int)vsc_b);
+          };
+          // first half of block j's elementwise part: 256 P (packed to pk), 256 dS (left in dpacc) and
+          // the block's code and scale exponent (wave-uniform)
+          uint32_t codes = 0;
+          auto ew_a = [&](int j, mx_v16f& sacc, mx_v16f& dpacc, const float4 (&pe)[4], uint32_t (&pk)[4]) {
+            const int ql0 = 32 * j;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+              for (int t = 0; t < 4; ++t) {
+                const int v = 4 * i + t;
+                float e = __builtin_amdgcn_exp2f(fmaf(sacc[v], p.c2, (&pe[i].x)[t]));  // 256 P
+                if (MASK) {
+                  const int qpos = q0 + ql0 + 8 * i + 4 * hh + t;
+                  const bool ok = (kvrow < Lk) & (qpos < Lq) & ((p.causal == 0) | (kvrow <= qpos));
+                  e = ok ? e : 0.0f;
+                }
+                sacc[v] = e;
+                dpacc[v] = e * dpacc[v];  // 256 dS
+              }
+            // |256 dS| maximum of the lane as a tree of max3, then over the wave
+            float m[6];
+#pragma unroll
+            for (int g = 0; g < 5; ++g) m[g] = max3_abs(__builtin_fabsf(dpacc[3 * g]), dpacc[3 * g + 1], dpacc[3 * g + 2]);
+            m[5] = __builtin_fabsf(dpacc[15]);
+            const float am = max3_abs(max3_abs(m[0], m[1], m[2]), m[3], m[4]);
+            const float am2 = fmaxf(am, m[5]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              pk[i] = mx_pack4_inrange(sacc[4 * i], sacc[4 * i + 1], sacc[4 * i + 2], sacc[4 * i + 3]);
+            const uint32_t efield =
+                (uint32_t)__builtin_amdgcn_readfirstlane((int)wave_max_dpp(__float_as_uint(am2))) >> 23;
+            uint32_t code, cs;
+            block_code(efield, code, cs);
+            codes |= code << (8 * j);
+            return make_uint2(code, cs);
+          };
+          // Software pipeline over the four blocks. Stage j issues block j + 1's G1/G2 and runs block
+          // j's first elementwise half beside block j - 1's second half (block 3's of the previous tile
+          // in stage 0), so one block's wave-wide maximum overlaps the other's arithmetic. dP's
+          // accumulator of block j + 1 (which starts at -Delta) reuses block j - 1's registers once
+          // its dS values are packed.
+          mx_v8i rows[4];
+          mx_v16f sacc[2], dpacc[2];
+          float4 pe[2][4];
+          uint32_t pk[2][4];
+          uint2 cc[2];
+          load_rows(0, rows);
+          load_pe(0, pe[0]);
+          load_nd(0, dpacc[0]);
+          g1(0, rows, sacc[0]);
+          g2(0, rows, dpacc[0]);
+          load_rows(1, rows);
+          load_pe(1, pe[1]);
+          load_nd(1, dpacc[1]);
+          __builtin_amdgcn_sched_barrier(0);
+          ew_b(3, ds3, code3, cs3, pk3);
+          g1(1, rows, sacc[1]);
+          g2(1, rows, dpacc[1]);
+          cc[0] = ew_a(0, sacc[0], dpacc[0], pe[0], pk[0]);
+          load_rows(2, rows);
+          __builtin_amdgcn_sched_barrier(0);
+          ew_b(0, dpacc[0], cc[0].x, cc[0].y, pk[0]);
+          load_pe(2, pe[0]);
+          load_nd(2, dpacc[0]);
+          g1(2, rows, sacc[0]);
+          g2(2, rows, dpacc[0]);
+          cc[1] = ew_a(1, sacc[1], dpacc[1], pe[1], pk[1]);
+          load_rows(3, rows);
+          __builtin_amdgcn_sched_barrier(0);
+          ew_b(1, dpacc[1], cc[1].x, cc[1].y, pk[1]);
+          load_pe(3, pe[1]);
+          load_nd(3, dpacc[1]);
+          g1(3, rows, sacc[1]);
+          g2(3, rows, dpacc[1]);
+          cc[0] = ew_a(2, sacc[0], dpacc[0], pe[0], pk[0]);
+          __builtin_amdgcn_sched_barrier(0);
+          ew_b(2, dpacc[0], cc[0].x, cc[0].y, pk[0]);
+          cc[1] = ew_a(3, sacc[1], dpacc[1], pe[1], pk[1]);
+          if (lane == 0) lds_dscode[kw] = codes;
+          ds3 = dpacc[1];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pk3[i] = pk[1][i];
+          code3 = cc[1].x;
+          cs3 = cc[1].y;
+        };
+        if (need_mask)
+          tile_body(std::true_type{});
+        else
+          tile_body(std::false_type{});
       } else {
-        const mx_v8i own{(int)dsk[0][0], (int)dsk[0][1], (int)dsk[0][2], (int)dsk[0][3],
-                         (int)dsk[1][0], (int)dsk[1][1], (int)dsk[1][2], (int)dsk[1][3]};
+        ew_b(3, ds3, code3, cs3, pk3);  // the last tile's block 3
+        __syncthreads();                // B2 (no tile left to produce)
+      }
+      st = st == 2 ? 0 : st + 1;
+    }
+  } else {
+    // dV and dK of the wave's 32 keys
+    mx_v16f dv_acc[4], dk_acc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      dv_acc[i] = mx_v16f{};
+      dk_acc[i] = mx_v16f{};
+    }
+    // which of the lane's four 16-byte image chunks (rows 32 kw + 8 c + lane / 8, stored chunk lane % 8)
+    // hold block 3's queries (logical chunks 6 and 7)
+    bool img_blk3[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) img_blk3[c] = (((lane & 7) ^ swz(32 * kw + 8 * c + (lane >> 3))) >> 1) == 3;
+    int st = 0;  // stage of tile k
+    for (int k = qt_begin; k <= k_end; ++k) {
+      const int st_prev = st == 0 ? 2 : st - 1, st_next = st == 2 ? 0 : st + 1;
+      __syncthreads();  // B1
+      // take tile k - 1's P_q, dS_q (blocks 0-2), codes and image chunks (but block 3's) to registers and
+      // global memory, fetch tile k + 1; after B2: block 3's operands and image chunks
+      mx_v8i pa[2], sa[2];
+      uint32_t codes = 0;
+      const int64_t tile = (((int64_t)h * p.nseq + s) * p.ntq_max + (k - 1)) * p.ntk_max + kt;
+      uint8_t* img = p.ds_img + tile * (kTile * kD) + kw * 4096;
+      if (k > qt_begin) {
+        const uint4 p0 = lds_pq[kw][0][lane], p1 = lds_pq[kw][1][lane], p2 = lds_pq[kw][2][lane];
+        const uint4 s0 = lds_sq[kw][0][lane], s1 = lds_sq[kw][1][lane], s2 = lds_sq[kw][2][lane];
+        pa[0] = mx_v8i{(int)p0.x, (int)p0.y, (int)p0.z, (int)p0.w, (int)p1.x, (int)p1.y, (int)p1.z, (int)p1.w};
+        sa[0] = mx_v8i{(int)s0.x, (int)s0.y, (int)s0.z, (int)s0.w, (int)s1.x, (int)s1.y, (int)s1.z, (int)s1.w};
+        pa[1] = mx_v8i{(int)p2.x, (int)p2.y, (int)p2.z, (int)p2.w, 0, 0, 0, 0};
+        sa[1] = mx_v8i{(int)s2.x, (int)s2.y, (int)s2.z, (int)s2.w, 0, 0, 0, 0};
+        codes = lds_dscode[kw];
+        if (lane == 0) *reinterpret_cast<uint32_t*>(p.ds_codes + tile * 16 + 4 * kw) = codes;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int o = c * 1024 + lane * 16;
+          const uint4 v = *reinterpret_cast<const uint4*>(lds_ds + kw * 4096 + o);
+          if (!img_blk3[c]) *reinterpret_cast<uint4*>(img + o) = v;
+        }
+      }
+      if (k + 1 < n_qtiles) issue_qtile(st_next, k + 1);
+      __syncthreads();  // B2
+      if (k > qt_begin) {
+        const uint4 p3 = lds_pq[kw][3][lane], s3 = lds_sq[kw][3][lane];
+        pa[1][4] = (int)p3.x;
+        pa[1][5] = (int)p3.y;
+        pa[1][6] = (int)p3.z;
+        pa[1][7] = (int)p3.w;
+        sa[1][4] = (int)s3.x;
+        sa[1][5] = (int)s3.y;
+        sa[1][6] = (int)s3.z;
+        sa[1][7] = (int)s3.w;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int o = c * 1024 + lane * 16;
+          if (img_blk3[c]) *reinterpret_cast<uint4*>(img + o) = *reinterpret_cast<const uint4*>(lds_ds + kw * 4096 + o);
+        }
+      }
+      if (k > qt_begin) {
+        // G3: dV += P_q^T dO; G4: dK += dS_q^T Q over the 128 queries of tile k - 1 (k-step ks: queries
+        // 64 ks .. +63; B scales: query block 2 ks + hh, d-block db; the A scale of dS_q likewise)
+        const uint8_t* lds_q = lds_qd[st_prev][0];
+        const uint8_t* lds_do = lds_qd[st_prev][1];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const mx_v8i sa = ks == 1 ? own : other;
-          // A-operand scale of dS_q: k-block hh of this step is query block 2 ks + hh
-          const uint32_t sa_sc = lds_dscode[kw][2 * ks + hh];
+          const uint32_t qsc_t = lds_sc[st_prev][2 * ks + hh];
+          const uint32_t dosc_t = lds_sc[st_prev][4 + 2 * ks + hh];
+          const uint32_t asc = (codes >> (8 * (2 * ks + hh))) & 0xffu;
 #pragma unroll
           for (int db = 0; db < 4; ++db) {
-            mx_v8i qbt = lds_tr_operand(lds_q, ks, 32 * db, tr_row, tr_col, tr_swz);
-            kv_acc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(sa, qbt, kv_acc[db], 0, 0, 0, (int)sa_sc, 0,
-                                                                         (int)(qsc_t[ks] >> (8 * db)));
-            asm volatile("" : "+v"(kv_acc[db])::"memory");
+            const mx_v8i dob = lds_tr_operand(lds_do, ks, 32 * db, tr_row, tr_col, tr_swz);
+            dv_acc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(pa[ks], dob, dv_acc[db], 0, 0, 0, 119, 0,
+                                                                         (int)(dosc_t >> (8 * db)));
+            const mx_v8i qbt = lds_tr_operand(lds_q, ks, 32 * db, tr_row, tr_col, tr_swz);
+            dk_acc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(sa[ks], qbt, dk_acc[db], 0, 0, 0, (int)asc,
+                                                                         0, (int)(qsc_t >> (8 * db)));
           }
         }
       }
+      wait_vm();  // this wave's part of tile k + 1 has landed (and its image stores are done)
+      st = st_next;
     }
 
-    // ---- dS_q of this (query tile, KV tile) pair to global memory for the dQ kernel: the 16 KB LDS
-    // image as it is (swizzled, key-major) and the 16 block codes; 2 KB per wave, 16 B per lane ----
-    {
-      const int64_t tile = (((int64_t)h * p.nseq + s) * p.ntq_max + qt) * p.ntk_max + kt;
-      uint8_t* img = p.ds_img + tile * (kTile * kD);
-      const int o0 = wave_s * 2048 + lane * 16;
-      const uint4 w0 = *reinterpret_cast<const uint4*>(lds_ds + o0);
-      const uint4 w1 = *reinterpret_cast<const uint4*>(lds_ds + o0 + 1024);
-      *reinterpret_cast<uint4*>(img + o0) = w0;
-      *reinterpret_cast<uint4*>(img + o0 + 1024) = w1;
-      if (wave_s == 0 && lane == 0)
-        *reinterpret_cast<uint4*>(p.ds_codes + tile * 16) = *reinterpret_cast<const uint4*>(lds_dscode);
-      // Wait for this thread's part of the next query tile (issued at the top of the iteration).
-      // Vector memory operations complete in issue order, so leaving the two stores issued since then
-      // in flight still covers the tile loads.
-      wait_vmcnt<2>();
-    }
-    __syncthreads();  // every thread's part of the next tile has landed; all reads of this stage,
-                      // of dS_q, of the partner operands and of the codes are done
+    // ---- epilogue: dV and dK = c dK of the wave's 32 keys (accumulator: column d = 32 db + r, rows
+    // kv 8 (v/4) + 4 hh + v%4 of the wave's key block) ----
+    const int64_t orow = (k_start + kv0 + 32 * kw) * (int64_t)C + h * kD;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int kr = 8 * (v >> 2) + 4 * hh + (v & 3);
+        if (kv0 + 32 * kw + kr < Lk) {
+          const uint32_t o = (uint32_t)(kr * C + 32 * db + r);
+          p.dv[orow + o] = (uint16_t)f32_to_bf16(dv_acc[db][v]);
+          p.dk[orow + o] = (uint16_t)f32_to_bf16(dk_acc[db][v] * p.c);
+        }
+      }
   }
-
-  // ---- epilogue: half-0 waves store dV, half-1 waves dK = c dK (accumulator: column d = 32 db + r,
-  // rows kv 8 (v/4) + 4 hh + v%4 of the wave's key block) ----
-  uint16_t* outb = (half ? p.dk : p.dv) + (k_start + kv0 + 32 * kw) * (int64_t)C + h * kD;
-  const float mult = half ? p.c : 1.0f;
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int kr = 8 * (v >> 2) + 4 * hh + (v & 3);
-      if (kv0 + 32 * kw + kr < Lk) outb[(uint32_t)(kr * C + 32 * db + r)] = (uint16_t)f32_to_bf16(kv_acc[db][v] * mult);
-    }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -529,7 +638,7 @@ struct DqParams {
 // workgroups share a CU, which measured faster than deeper prefetching with one workgroup per CU.
 constexpr int kDqStages = 2;
 
-__global__ void __launch_bounds__(512, 1) attn_dq_kernel(DqParams p) {
+__global__ void __launch_bounds__(64 * kDqWaves, 1) attn_dq_kernel(DqParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds_img[kDqStages][kTile * kD];
   __shared__ __attribute__((aligned(1024))) uint8_t lds_kt[kDqStages][kTile * kD];
   __shared__ __attribute__((aligned(256))) uint32_t lds_codes[kDqStages][64];
@@ -553,7 +662,7 @@ __global__ void __launch_bounds__(512, 1) attn_dq_kernel(DqParams p) {
   const int r = lane & 31, hh = lane >> 5;
   const int C = p.H * kD;
   const int Cs = C >> 5;
-  const TileLane tl = tile_lane(wave, lane, C);
+  const TileLane<kDqWaves> tl = tile_lane<kDqWaves>(wave, lane, C);
   int ntk = (Lk + kTile - 1) / kTile;
   if (p.causal) ntk = min(ntk, qt + 1);  // key tiles past the query tile are fully masked
 
@@ -565,9 +674,10 @@ __global__ void __launch_bounds__(512, 1) attn_dq_kernel(DqParams p) {
   auto issue_loads = [&](int kt, uint8_t* img, uint8_t* ktile, uint32_t* codes, uint32_t* kscw) {
     // the dS_q image is copied as it is (2 KB per wave, 16 B per lane)
 #pragma unroll
-    for (int c = 0; c < kPieces; ++c) {
-      const uint32_t off = (uint32_t)((wave_s * kPieces + c) * 1024 + lane * 16);
-      mx_lds_dma16((MX_LDS void*)(img + (wave_s * kPieces + c) * 1024), img_base + (int64_t)kt * (kTile * kD), off);
+    for (int c = 0; c < TileLane<kDqWaves>::kPieces; ++c) {
+      const int piece = wave_s * TileLane<kDqWaves>::kPieces + c;
+      mx_lds_dma16((MX_LDS void*)(img + piece * 1024), img_base + (int64_t)kt * (kTile * kD),
+                   (uint32_t)(piece * 1024 + lane * 16));
     }
     issue_tile_load(ktile, kbase + (int64_t)kt * kTile * C, Lk - kt * kTile, C, tl, wave_s);
     if (wave_s == 2) mx_lds_dma4_addr((MX_LDS void*)codes, code_base + (int64_t)kt * 16 + 4 * (lane & 3));
@@ -690,7 +800,7 @@ __global__ void __launch_bounds__(512, 1) attn_dq_kernel(DqParams p) {
 namespace mxfa {
 
 // Workspace: the dS_q images [H][nseq][ntq_max][ntk_max] (16 KB each), their block codes (16 B
-// each), then Delta [H][Tq] and the exponent offsets [H][Tq] (fp32), each region 256-byte aligned.
+// each), then -Delta [H][Tq] and the exponent offsets [H][Tq] (fp32), each region 256-byte aligned.
 struct BwdWorkspace {
   size_t img, codes, delta, pexp, total;
 };
@@ -739,14 +849,14 @@ hipError_t launch_attn_bwd(const AttnProblem& a, const MxOperand& v_d, const MxO
   p.total_items = p.n_ktiles * a.H * a.nseq;  // < 2^31, checked by the caller
   p.c2 = a.softmax_scale * kLog2e;
   p.causal = a.causal;
-  p.pexp = pexp; p.delta = delta; p.Tq = Tq;
+  p.pexp = pexp; p.ndelta = delta; p.Tq = Tq;
   p.ntq_max = ntq_max; p.ntk_max = ntk_max;
   p.ds_img = ws + w.img;
   p.ds_codes = ws + w.codes;
   p.c = a.softmax_scale;
   p.dk = dk; p.dv = dv;
   if (p.total_items > 0) {
-    hipLaunchKernelGGL(attn_bwd_kernel, dim3((unsigned)p.total_items), dim3(64 * kWaves), 0, stream, p);
+    hipLaunchKernelGGL(attn_bwd_kernel, dim3((unsigned)p.total_items), dim3(64 * kBwdWaves), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -767,7 +877,7 @@ hipError_t launch_attn_bwd(const AttnProblem& a, const MxOperand& v_d, const MxO
   d.mult = a.softmax_scale / (dq_fp16 ? sigma : 1.0f);
   d.dq = dq;
   if (d.total_items > 0) {
-    hipLaunchKernelGGL(attn_dq_kernel, dim3((unsigned)d.total_items), dim3(64 * kWaves), 0, stream, d);
+    hipLaunchKernelGGL(attn_dq_kernel, dim3((unsigned)d.total_items), dim3(64 * kDqWaves), 0, stream, d);
     return hipGetLastError();
   }
   return hipSuccess;

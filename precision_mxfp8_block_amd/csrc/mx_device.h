@@ -61,6 +61,21 @@ __device__ __forceinline__ uint32_t mx_pack4(float a, float b, float c, float d)
   return mx_pack2_hi(c, d, mx_pack2_lo(a, b, 0u));
 }
 
+// Four floats -> four E4M3 bytes of x / sc (sc a power of two, lim = 448 sc), round to nearest even,
+// saturating: the scaled conversion does not saturate, so the inputs are clamped to +-lim first.
+// Same bytes as clamping x / sc to +-448 and converting (x / sc is exact for a power-of-two sc).
+__device__ __forceinline__ uint32_t mx_pack4_scaled(float a, float b, float c, float d, float sc, float lim) {
+  typedef short v2s __attribute__((ext_vector_type(2)));
+  a = __builtin_amdgcn_fmed3f(a, -lim, lim);
+  b = __builtin_amdgcn_fmed3f(b, -lim, lim);
+  c = __builtin_amdgcn_fmed3f(c, -lim, lim);
+  d = __builtin_amdgcn_fmed3f(d, -lim, lim);
+  // the first conversion writes bytes 0-1, the second bytes 2-3: the initial value is irrelevant
+  v2s r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(__builtin_bit_cast(v2s, a), a, b, sc, false);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, c, d, sc, true);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
 
 // fp32 -> bf16 bits, round to nearest even (NaN kept quiet).
