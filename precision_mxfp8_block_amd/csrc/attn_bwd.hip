@@ -213,7 +213,6 @@ __global__ void __launch_bounds__(64 * kBwdWaves, 1) attn_bwd_kernel(BwdParams p
   __shared__ __attribute__((aligned(512))) float lds_ld[3][2][kTile];   // [stage][8 - LSE log2e, -Delta]
   __shared__ __attribute__((aligned(256))) uint32_t lds_sc[3][64];      // [stage][Q, dO scale words]
   __shared__ uint32_t lds_dscode[4];                                     // dS codes [key block] (byte: q block)
-  __shared__ int64_t red[16];
 
   const int item = xcd_remap((int)blockIdx.x, p.total_items);
   const int kt = item % p.n_ktiles;
@@ -224,8 +223,8 @@ __global__ void __launch_bounds__(64 * kBwdWaves, 1) attn_bwd_kernel(BwdParams p
   const int Lk = p.cu_k[s + 1] - (int)k_start;
   if (kt * kTile >= Lk) return;
 
-  const SeqOffsets qoff = seq_offsets(p.cu_q, s, red);
-  const SeqOffsets koff = seq_offsets(p.cu_k, s, red);
+  const SeqOffsets qoff = seq_offsets(p.cu_q, s);
+  const SeqOffsets koff = seq_offsets(p.cu_k, s);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave_s = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -643,7 +642,6 @@ __global__ void __launch_bounds__(64 * kDqWaves, 1) attn_dq_kernel(DqParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds_kt[kDqStages][kTile * kD];
   __shared__ __attribute__((aligned(256))) uint32_t lds_codes[kDqStages][64];
   __shared__ __attribute__((aligned(256))) uint32_t lds_ksc[kDqStages][64];
-  __shared__ int64_t red[16];
 
   const int item = xcd_remap((int)blockIdx.x, p.total_items);
   const int qt = item % p.ntq_max;
@@ -654,7 +652,7 @@ __global__ void __launch_bounds__(64 * kDqWaves, 1) attn_dq_kernel(DqParams p) {
   const int Lk = p.cu_k[s + 1] - (int)k_start;
   const int q0 = qt * kTile;
   if (q0 >= Lq) return;  // uniform over the workgroup
-  const SeqOffsets koff = seq_offsets(p.cu_k, s, red);
+  const SeqOffsets koff = seq_offsets(p.cu_k, s);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);

@@ -93,7 +93,6 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
   // with the tile
   __shared__ __attribute__((aligned(512))) uint32_t lds_ksc[2][kTile];
   __shared__ __attribute__((aligned(512))) uint32_t lds_vsc[2][kTile];
-  __shared__ int64_t red[16];
 
   const int item = xcd_remap((int)blockIdx.x, p.total_items);
   const int qt = p.n_qtiles - 1 - item % p.n_qtiles;  // heavy (late) query tiles first
@@ -104,8 +103,8 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
   const int Lk = p.cu_k[s + 1] - (int)k_start;
   if (qt * kTile >= Lq) return;  // uniform over the workgroup
 
-  const SeqOffsets qoff = seq_offsets(p.cu_q, s, red);
-  const SeqOffsets koff = seq_offsets(p.cu_k, s, red);
+  const SeqOffsets qoff = seq_offsets(p.cu_q, s);
+  const SeqOffsets koff = seq_offsets(p.cu_k, s);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r = lane & 31, hh = lane >> 5;

@@ -88,7 +88,6 @@ __device__ __forceinline__ uint32_t wave_max_dpp(uint32_t v) {
 
 __global__ void __launch_bounds__(256, 2) linear_quantize_kernel(LinearParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2][2][kTile * kChunk];  // stage x (X, W)
-  __shared__ int64_t red[16];
 
   const int item = xcd_remap((int)blockIdx.x, p.total_items);
   const int ct = item % p.n_coltiles;
@@ -99,8 +98,8 @@ __global__ void __launch_bounds__(256, 2) linear_quantize_kernel(LinearParams p)
   const int t0 = tt * kTile;
   if (t0 >= L) return;  // uniform over the workgroup
   const int valid = min(kTile, L - t0);
-  const int64_t br0 = seq_offsets(p.cu, s, red).blocks32 + (t0 >> 5);  // first 32-token block row
-  const int64_t nb_total = p.scale_t ? seq_offsets(p.cu, p.nseq, red).blocks32 : 0;
+  const int64_t br0 = seq_offsets(p.cu, s).blocks32 + (t0 >> 5);  // first 32-token block row
+  const int64_t nb_total = p.scale_t ? seq_offsets(p.cu, p.nseq).blocks32 : 0;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r = lane & 31, hh = lane >> 5;

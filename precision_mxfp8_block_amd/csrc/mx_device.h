@@ -158,18 +158,18 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 
 // Sum of a per-thread integer over a workgroup of `nthreads` (<= 1024) threads; every thread gets
 // the total. `red` is a workgroup-shared scratch of at least 16 ints.
-__device__ __forceinline__ int64_t block_sum_i64(int64_t v, int64_t* red) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int nw = (blockDim.x + 63) >> 6;
-  __syncthreads();
-  if (lane == 0) red[wid] = v;
-  __syncthreads();
-  int64_t t = 0;
-  for (int w = 0; w < nw; ++w) t += red[w];
-  __syncthreads();
-  return t;
+// Sum over the 64 lanes of a wave, returned in every lane: DPP within rows of 16 (after the quad
+// steps each group of lanes holds one value, so the mirrors add the partner group), then the
+// permlane16 and permlane32 swaps across rows. The wave must be fully active.
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0xB1, 0xF, 0xF, false);   // quad_perm 1,0,3,2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x4E, 0xF, 0xF, false);   // quad_perm 2,3,0,1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x141, 0xF, 0xF, false);  // row_half_mirror
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x140, 0xF, 0xF, false);  // row_mirror
+  auto s16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = (uint32_t)s16[0] + (uint32_t)s16[1];
+  auto s32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return (uint32_t)s32[0] + (uint32_t)s32[1];
 }
 
 // A 64-bit value the caller knows to be wave-uniform, moved to scalar registers (so that addresses
@@ -180,21 +180,24 @@ __device__ __forceinline__ int64_t mx_uniform_i64(int64_t v) {
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
-// Offsets of sequence s in the compact and padded layouts, computed by the whole workgroup from
-// the device cu_seqlens: blocks32 = sum_{r<s} ceil(L_r/32), padded = sum_{r<s} round_up(L_r,128).
+// Offsets of sequence s in the compact and padded layouts from the device cu_seqlens, computed by
+// every wave on its own (no barrier; the wave must be fully active): blocks32 = sum_{r<s}
+// ceil(L_r/32), padded = sum_{r<s} round_up(L_r,128). The sums fit 32 bits for any token count
+// whose data fits in device memory.
 struct SeqOffsets {
   int64_t blocks32;
   int64_t padded;
 };
-__device__ __forceinline__ SeqOffsets seq_offsets(const int32_t* cu, int s, int64_t* red) {
-  int64_t b = 0, p = 0;
-  for (int r = threadIdx.x; r < s; r += blockDim.x) {
-    int64_t L = (int64_t)cu[r + 1] - cu[r];
-    b += (L + 31) >> 5;
-    p += (L + 127) >> 7;
+__device__ __forceinline__ SeqOffsets seq_offsets(const int32_t* cu, int s) {
+  const int lane = threadIdx.x & 63;
+  uint32_t b = 0, p = 0;
+  for (int r = lane; r < s; r += 64) {
+    const uint32_t L = (uint32_t)(cu[r + 1] - cu[r]);
+    b += (L + 31u) >> 5;
+    p += (L + 127u) >> 7;
   }
   SeqOffsets o;
-  o.blocks32 = mx_uniform_i64(block_sum_i64(b, red));
-  o.padded = mx_uniform_i64(block_sum_i64(p, red)) << 7;
+  o.blocks32 = mx_uniform_i64((int64_t)wave_sum_u32(b));
+  o.padded = mx_uniform_i64((int64_t)wave_sum_u32(p)) << 7;
   return o;
 }

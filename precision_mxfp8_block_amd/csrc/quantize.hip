@@ -61,11 +61,10 @@ __global__ void __launch_bounds__(256) quantize_col32_kernel(const uint16_t* __r
                                                              const int32_t* __restrict__ cu,
                                                              uint8_t* __restrict__ data,
                                                              uint8_t* __restrict__ scale) {
-  __shared__ int64_t red[16];
   const int s = blockIdx.z, b = blockIdx.y;
   const int64_t t0 = cu[s], L = (int64_t)cu[s + 1] - t0;
   if ((int64_t)b * 32 >= L) return;  // uniform over the workgroup
-  const SeqOffsets off = seq_offsets(cu, s, red);
+  const SeqOffsets off = seq_offsets(cu, s);
   const int g = blockIdx.x * blockDim.x + threadIdx.x;
   if (g >= (C >> 2)) return;
   const int rows = (int)min<int64_t>(32, L - (int64_t)b * 32);
@@ -114,13 +113,12 @@ __global__ void __launch_bounds__(256) quantize_sq32_kernel(const uint16_t* __re
                                                             const int32_t* __restrict__ cu, int nseq,
                                                             uint8_t* __restrict__ data, uint8_t* __restrict__ scale,
                                                             uint8_t* __restrict__ scale_t) {
-  __shared__ int64_t red[16];
   const int s = blockIdx.z, b = blockIdx.y;
   const int64_t t0 = cu[s], L = (int64_t)cu[s + 1] - t0;
   if ((int64_t)b * 32 >= L) return;
-  const SeqOffsets off = seq_offsets(cu, s, red);
+  const SeqOffsets off = seq_offsets(cu, s);
   int64_t nb_total = 0;
-  if (scale_t) nb_total = seq_offsets(cu, nseq, red).blocks32;
+  if (scale_t) nb_total = seq_offsets(cu, nseq).blocks32;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int cb = blockIdx.x * 4 + wave;  // 32-column block
   if (cb >= (C >> 5)) return;            // whole wave leaves together
@@ -170,11 +168,10 @@ __global__ void __launch_bounds__(256) quantize_sq32_kernel(const uint16_t* __re
 __global__ void __launch_bounds__(256) scale_scatter_kernel(const uint8_t* __restrict__ compact,
                                                             const int32_t* __restrict__ cu, int C, int mode,
                                                             uint8_t* __restrict__ padded, int64_t padded_rows) {
-  __shared__ int64_t red[16];
   const int s = blockIdx.y, g = blockIdx.x;
   const int64_t L = (int64_t)cu[s + 1] - cu[s];
   if ((int64_t)g * 128 >= L) return;
-  const SeqOffsets off = seq_offsets(cu, s, red);
+  const SeqOffsets off = seq_offsets(cu, s);
   const int width = (mode == 1) ? C : (C >> 5);
   const int unit = (mode == 0) ? 1 : 32;                 // tokens per layout row
   const int rows_per_group = 128 / unit;
@@ -205,15 +202,14 @@ __global__ void __launch_bounds__(256) rmsnorm_quantize_kernel(const uint16_t* _
                                                                uint8_t* __restrict__ data,
                                                                uint8_t* __restrict__ scale,
                                                                uint8_t* __restrict__ scale_t) {
-  __shared__ int64_t red[16];
   __shared__ float rs[32];
   __shared__ uint32_t bmax[1024];  // up to C = 32768 columns
   const int s = blockIdx.y, b = blockIdx.x;
   const int64_t t0 = cu[s], L = (int64_t)cu[s + 1] - t0;
   if ((int64_t)b * 32 >= L) return;
-  const SeqOffsets off = seq_offsets(cu, s, red);
+  const SeqOffsets off = seq_offsets(cu, s);
   int64_t nb_total = 0;
-  if (scale_t) nb_total = seq_offsets(cu, nseq, red).blocks32;
+  if (scale_t) nb_total = seq_offsets(cu, nseq).blocks32;
   const int rows = (int)min<int64_t>(32, L - (int64_t)b * 32);
   const int64_t ta = t0 + (int64_t)b * 32;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
