@@ -105,10 +105,22 @@ __global__ void __launch_bounds__(256) quantize_col32_kernel(const uint16_t* __r
 }
 
 // ---------------------------------------------------------------------------------------------
-// SQ32: 32 x 32 blocks, one wave per block: lane l covers row l/2 and 16 columns (two 16-byte
-// loads). The block maximum is a wave-wide reduction. Four waves cover 128 adjacent columns.
-// Grid: x = C / 128 (rounded up), y = block index inside the sequence, z = sequence.
+// SQ32: 32 x 32 blocks. A wave covers 32 rows x 64 columns (two blocks): lane l reads the 16-byte
+// chunk l % 8 (8 bf16) of rows l / 8 + 8 i, i = 0..3, so every load and store instruction covers
+// whole 128-byte row segments. The lane's block is (l % 8) / 4; its maximum is taken over the 32
+// lanes that share lane bit 2 (DPP and lane swaps, no LDS). Four waves cover 256 columns.
+// Grid: x = C / 256 (rounded up), y = block row inside the sequence, z = sequence.
 // ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t max_over_block_lanes(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0xB1, 0xF, 0xF, false));   // lane bit 0
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x4E, 0xF, 0xF, false));   // lane bit 1
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x128, 0xF, 0xF, false));  // row_ror:8, lane bit 3
+  auto s16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);                   // lane bit 4
+  v = max((uint32_t)s16[0], (uint32_t)s16[1]);
+  auto s32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);                   // lane bit 5
+  return max((uint32_t)s32[0], (uint32_t)s32[1]);
+}
+
 __global__ void __launch_bounds__(256) quantize_sq32_kernel(const uint16_t* __restrict__ x, int64_t ld_x, int C,
                                                             const int32_t* __restrict__ cu, int nseq,
                                                             uint8_t* __restrict__ data, uint8_t* __restrict__ scale,
@@ -120,40 +132,46 @@ __global__ void __launch_bounds__(256) quantize_sq32_kernel(const uint16_t* __re
   int64_t nb_total = 0;
   if (scale_t) nb_total = seq_offsets(cu, nseq).blocks32;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int cb = blockIdx.x * 4 + wave;  // 32-column block
-  if (cb >= (C >> 5)) return;            // whole wave leaves together
-  const int r = lane >> 1, half = lane & 1;
+  const int cg = blockIdx.x * 4 + wave;  // 64-column group
+  if (cg * 64 >= C) return;              // whole wave leaves together
+  const int chunk = lane & 7, rl = lane >> 3;
+  const int col = cg * 64 + chunk * 8;
+  const bool col_ok = col < C;  // C % 64 == 32: the group's second block does not exist
   const int rows = (int)min<int64_t>(32, L - (int64_t)b * 32);
-  const int64_t t = t0 + (int64_t)b * 32 + r;
-  uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (r < rows) {
-    const uint4* src = reinterpret_cast<const uint4*>(x + t * ld_x + (int64_t)cb * 32 + half * 16);
-    uint4 a = src[0], c = src[1];
-    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w; w[4] = c.x; w[5] = c.y; w[6] = c.z; w[7] = c.w;
-  }
+  const int64_t tb = t0 + (int64_t)b * 32;
+  uint4 w[4];
   uint32_t amax = 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) amax = max(amax, max(w[i] & 0x7fffu, (w[i] >> 16) & 0x7fffu));
-  amax = wave_max_u32(amax);
-  const uint32_t code = mx_code_from_amax_bits(amax << 16);
-  if (r < rows) {
-    uint4 out;
-    if (code == 255u) {
-      out = make_uint4(0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu);
-    } else {
-      const float inv = mx_inv_scale(code);
-      uint32_t o[4];
+  for (int i = 0; i < 4; ++i) {
+    const int rr = rl + 8 * i;
+    w[i] = make_uint4(0u, 0u, 0u, 0u);
+    if (col_ok && rr < rows) w[i] = *reinterpret_cast<const uint4*>(x + (tb + rr) * ld_x + col);
+    const uint32_t q[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint32_t p = w[2 * i], q = w[2 * i + 1];
-        o[i] = mx_pack4(bf16_to_f32(p & 0xffffu) * inv, bf16_to_f32(p >> 16) * inv, bf16_to_f32(q & 0xffffu) * inv,
-                        bf16_to_f32(q >> 16) * inv);
-      }
-      out = make_uint4(o[0], o[1], o[2], o[3]);
-    }
-    *reinterpret_cast<uint4*>(data + t * C + (int64_t)cb * 32 + half * 16) = out;
+    for (int k = 0; k < 4; ++k) amax = max(amax, max(q[k] & 0x7fffu, (q[k] >> 16) & 0x7fffu));
   }
-  if (lane == 0) {
+  amax = max_over_block_lanes(amax);
+  const uint32_t code = mx_code_from_amax_bits(amax << 16);
+  const float inv = code == 255u ? 0.0f : mx_inv_scale(code);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rr = rl + 8 * i;
+    if (col_ok && rr < rows) {
+      uint2 out;
+      if (code == 255u) {
+        out = make_uint2(0x7f7f7f7fu, 0x7f7f7f7fu);
+      } else {
+        const uint32_t q[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+        out.x = mx_pack4(bf16_to_f32(q[0] & 0xffffu) * inv, bf16_to_f32(q[0] >> 16) * inv,
+                         bf16_to_f32(q[1] & 0xffffu) * inv, bf16_to_f32(q[1] >> 16) * inv);
+        out.y = mx_pack4(bf16_to_f32(q[2] & 0xffffu) * inv, bf16_to_f32(q[2] >> 16) * inv,
+                         bf16_to_f32(q[3] & 0xffffu) * inv, bf16_to_f32(q[3] >> 16) * inv);
+      }
+      *reinterpret_cast<uint2*>(data + (tb + rr) * C + col) = out;
+    }
+  }
+  if ((lane & 3) == 0 && lane < 8 && col_ok) {  // lanes 0 and 4: the group's two blocks
+    const int cb = col >> 5;
     const int64_t br = off.blocks32 + b;
     scale[br * (C >> 5) + cb] = (uint8_t)code;
     if (scale_t) scale_t[(int64_t)cb * nb_total + br] = (uint8_t)code;
@@ -302,7 +320,7 @@ hipError_t launch_quantize(const uint16_t* x, int64_t ld_x, int64_t T, int C, co
     dim3 grid((unsigned)(((C >> 2) + 255) / 256), (unsigned)((max_seqlen + 31) / 32), (unsigned)nseq);
     hipLaunchKernelGGL(quantize_col32_kernel, grid, dim3(256), 0, stream, x, ld_x, C, cu, data, scale);
   } else {
-    dim3 grid((unsigned)((C + 127) / 128), (unsigned)((max_seqlen + 31) / 32), (unsigned)nseq);
+    dim3 grid((unsigned)((C + 255) / 256), (unsigned)((max_seqlen + 31) / 32), (unsigned)nseq);
     hipLaunchKernelGGL(quantize_sq32_kernel, grid, dim3(256), 0, stream, x, ld_x, C, cu, nseq, data, scale,
                        scale_t);
   }

@@ -34,10 +34,11 @@ def _special_matrix(seed, T, C):
 
 @pytest.mark.parametrize("mode", [oracle.ROW32, oracle.COL32, oracle.SQ32])
 @pytest.mark.parametrize("lens", [[256], [37, 128, 1, 300, 95, 64]])
-def test_quantize_bit_exact(mode, lens):
-    say(f"quantize mode={mode} lens={lens}")
+@pytest.mark.parametrize("C", [384, 160])  # 160: the last 64-column group holds one 32-column block
+def test_quantize_bit_exact(mode, lens, C):
+    say(f"quantize mode={mode} lens={lens} C={C}")
     cu = synth.cu_seqlens(lens)
-    T, C = int(cu[-1]), 384
+    T = int(cu[-1])
     x = _special_matrix(3 + mode, T, C)
     d_ref, s_ref, st_ref = oracle.quantize(x, cu, mode)
     data, scale, scale_t = mx.quantize(to_dev_bf16(x), cu, cu_dev(cu), mode, want_scale_t=(mode == oracle.SQ32))
