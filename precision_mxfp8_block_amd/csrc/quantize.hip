@@ -69,17 +69,18 @@ __global__ void __launch_bounds__(256) quantize_col32_kernel(const uint16_t* __r
   if (g >= (C >> 2)) return;
   const int rows = (int)min<int64_t>(32, L - (int64_t)b * 32);
   const int64_t ta = t0 + (int64_t)b * 32;
+  // rows past the sequence end re-read its last row: every load is issued without a branch, and a
+  // repeated row does not change the block maximum
   uint2 v[32];
   uint32_t am[4] = {0, 0, 0, 0};
 #pragma unroll
+  for (int r = 0; r < 32; ++r) v[r] = *reinterpret_cast<const uint2*>(x + (ta + min(r, rows - 1)) * ld_x + (int64_t)g * 4);
+#pragma unroll
   for (int r = 0; r < 32; ++r) {
-    if (r < rows) {
-      v[r] = *reinterpret_cast<const uint2*>(x + (ta + r) * ld_x + (int64_t)g * 4);
-      am[0] = max(am[0], v[r].x & 0x7fffu);
-      am[1] = max(am[1], (v[r].x >> 16) & 0x7fffu);
-      am[2] = max(am[2], v[r].y & 0x7fffu);
-      am[3] = max(am[3], (v[r].y >> 16) & 0x7fffu);
-    }
+    am[0] = max(am[0], v[r].x & 0x7fffu);
+    am[1] = max(am[1], (v[r].x >> 16) & 0x7fffu);
+    am[2] = max(am[2], v[r].y & 0x7fffu);
+    am[3] = max(am[3], (v[r].y >> 16) & 0x7fffu);
   }
   uint32_t code[4];
   float inv[4];
@@ -139,13 +140,15 @@ __global__ void __launch_bounds__(256) quantize_sq32_kernel(const uint16_t* __re
   const bool col_ok = col < C;  // C % 64 == 32: the group's second block does not exist
   const int rows = (int)min<int64_t>(32, L - (int64_t)b * 32);
   const int64_t tb = t0 + (int64_t)b * 32;
+  // rows past the sequence end re-read its last row and a missing second block re-reads the first
+  // (neither changes a stored block maximum), so every load is issued without a branch
+  const int col_ld = col_ok ? col : col - 32;
   uint4 w[4];
   uint32_t amax = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int rr = rl + 8 * i;
-    w[i] = make_uint4(0u, 0u, 0u, 0u);
-    if (col_ok && rr < rows) w[i] = *reinterpret_cast<const uint4*>(x + (tb + rr) * ld_x + col);
+    const int rr = min(rl + 8 * i, rows - 1);
+    w[i] = *reinterpret_cast<const uint4*>(x + (tb + rr) * ld_x + col_ld);
     const uint32_t q[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
 #pragma unroll
     for (int k = 0; k < 4; ++k) amax = max(amax, max(q[k] & 0x7fffu, (q[k] >> 16) & 0x7fffu));
