@@ -12,15 +12,16 @@
 //   254), payload = E4M3_RNE_sat(Y 2^(127 - code)); scales [NB][C_out/32] and [C_out/32][NB].
 //
 // gfx950 design:
-//  * Workgroup = 4 waves = 128 tokens of one sequence x 128 output columns (one attention head when
-//    the head size is 128). Wave w owns token block w, so each of its four 32 x 32 accumulators is
-//    exactly one output scale block and the block maximum is a wave-wide reduction.
+//  * Workgroup = 8 waves = 256 tokens of one sequence x 256 output columns (the L2 traffic of X and W
+//    falls with the tile edge). Wave w owns token blocks 2 (w & 3), +1 and column blocks 4 (w >> 2)
+//    .. +3, so each of its eight 32 x 32 accumulators is exactly one output scale block and the block
+//    maximum is a wave-wide reduction.
 //  * The product is computed transposed, Y^T = W X^T (A = W rows, B = X rows, both read from LDS
 //    as 16-byte row pieces): the accumulator gives each lane one token and 4 x 4 consecutive
 //    output columns, i.e. four 4-byte payload stores per block.
-//  * X and W chunks of 128 x 128 bytes are double-buffered in LDS (direct global -> LDS loads,
-//    XOR-swizzled chunks) and fetched one chunk of C_in ahead; the E8M0 scales of the next chunk
-//    are fetched into registers at the same time.
+//  * X and W chunks of 256 x 128 bytes are double-buffered in LDS (128 KB; direct global -> LDS
+//    loads, XOR-swizzled chunks) and fetched one chunk of C_in ahead; the E8M0 scales of the next
+//    chunk are fetched into registers at the same time.
 //  * Items are (sequence, token tile, column tile) with the column tile fastest, remapped so that
 //    each XCD works on a contiguous item range: the column tiles of one token tile then share one
 //    L2, which serves the X tile to all of them.
@@ -29,8 +30,10 @@
 
 namespace {
 
-constexpr int kTile = 128;   // tokens and output columns per workgroup
+constexpr int kTok = 256;    // tokens per workgroup
+constexpr int kCol = 256;    // output columns per workgroup
 constexpr int kChunk = 128;  // bytes of C_in per LDS stage
+constexpr int kLinWaves = 8;
 
 struct LinearParams {
   const uint8_t* x;
@@ -52,17 +55,20 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
   return x * per + (x < rem ? x : rem) + slot;
 }
 
+// The direct LDS loads are inline asm (mx_lds_dma16) and so is their wait: with the compiler's own
+// direct-load builtin it waits for every outstanding load before the next LDS read, i.e. for the
+// next chunk's prefetch before the current chunk's MFMAs.
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Global -> LDS copy of a 128-row x 128-byte chunk (row stride ld bytes) into a swizzled LDS tile;
-// rows at or past `valid` re-fetch the last valid row (finite data, never stored).
+// Global -> LDS copy of a 256-row x 128-byte chunk (row stride ld bytes, `base` wave-uniform) into a
+// swizzled LDS tile, four 1 KB pieces per wave; rows at or past `valid` re-fetch the last valid row
+// (finite data, never stored).
 __device__ __forceinline__ void issue_chunk_load(uint8_t* lds_tile, const uint8_t* base, int valid, int ld,
                                                  const int* trow, const int* tcol, int wave_s) {
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const uint32_t off = (uint32_t)(min(trow[c], valid - 1) * ld + tcol[c]);
-    __builtin_amdgcn_global_load_lds((const void*)(base + off), (MX_LDS void*)(lds_tile + (wave_s * 4 + c) * 1024),
-                                     16, 0, 0);
+    mx_lds_dma16((MX_LDS void*)(lds_tile + (wave_s * 4 + c) * 1024), base, off);
   }
 }
 
@@ -75,19 +81,20 @@ __device__ __forceinline__ mx_v8i lds_row_operand(const uint8_t* lds, int row, i
   return mx_v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
-// Maximum over the 64 lanes of a wave (DPP inside rows of 16, then across rows and halves).
+// Maximum over the 64 lanes of a wave (DPP inside rows of 16, then lane swaps across rows).
 __device__ __forceinline__ uint32_t wave_max_dpp(uint32_t v) {
   v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
   v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
   v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x141, 0xF, 0xF, false));  // row_half_mirror
   v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x140, 0xF, 0xF, false));  // row_mirror
-  v = max(v, (uint32_t)__shfl_xor((int)v, 16, 64));
-  auto s = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-  return max((uint32_t)s[0], (uint32_t)s[1]);
+  auto s16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = max((uint32_t)s16[0], (uint32_t)s16[1]);
+  auto s32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return max((uint32_t)s32[0], (uint32_t)s32[1]);
 }
 
-__global__ void __launch_bounds__(256, 2) linear_quantize_kernel(LinearParams p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2][2][kTile * kChunk];  // stage x (X, W)
+__global__ void __launch_bounds__(64 * kLinWaves, 1) linear_quantize_kernel(LinearParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2][2][kTok * kChunk];  // stage x (X, W)
 
   const int item = xcd_remap((int)blockIdx.x, p.total_items);
   const int ct = item % p.n_coltiles;
@@ -95,116 +102,145 @@ __global__ void __launch_bounds__(256, 2) linear_quantize_kernel(LinearParams p)
   const int s = item / (p.n_coltiles * p.tiles_per_seq);
   const int64_t start = p.cu[s];
   const int L = p.cu[s + 1] - (int)start;
-  const int t0 = tt * kTile;
+  const int t0 = tt * kTok;
   if (t0 >= L) return;  // uniform over the workgroup
-  const int valid = min(kTile, L - t0);
+  const int valid = min(kTok, L - t0);
   const int64_t br0 = seq_offsets(p.cu, s).blocks32 + (t0 >> 5);  // first 32-token block row
   const int64_t nb_total = p.scale_t ? seq_offsets(p.cu, p.nseq).blocks32 : 0;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int r = lane & 31, hh = lane >> 5;
-  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
-  const int ldw = p.C_in;            // row stride of X and W in bytes
-  const int lds_s = p.C_in >> 5;     // scale row length in bytes (both X and W)
+  const int wave_s = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tq = wave_s & 3;   // token blocks 2 tq, 2 tq + 1 of the tile
+  const int cq = wave_s >> 2;  // column blocks 4 cq .. 4 cq + 3 of the tile
+  const int ldw = p.C_in;      // row stride of X and W in bytes
+  const int lds_s = p.C_in >> 5;  // scale row length in bytes (both X and W)
+  const int wrows = min(kCol, p.C_out - ct * kCol);  // 256, or 128 for a last half tile
+  const bool col_live = 128 * cq < wrows;           // wave-uniform
   int trow[4], tcol[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    const int pc = (wave * 4 + c) * 64 + lane;
+    const int pc = (wave_s * 4 + c) * 64 + lane;
     trow[c] = pc >> 3;
     tcol[c] = 16 * ((pc & 7) ^ lds_swz(pc >> 3));
   }
-  const uint8_t* xbase = p.x + (start + t0) * (int64_t)ldw;
-  const uint8_t* wbase = p.w + (int64_t)ct * kTile * ldw;
+  const uint8_t* xbase = (const uint8_t*)mx_uniform_ptr((void*)(p.x + (start + t0) * (int64_t)ldw));
+  const uint8_t* wbase = (const uint8_t*)mx_uniform_ptr((void*)(p.w + (int64_t)ct * kCol * ldw));
 
-  // Scale rows: W rows 32 j + r of this column tile; X: the wave's token block (SQ32) or the lane's
-  // token (ROW32), clamped into the sequence (clamped rows are never stored).
-  const int tok = min(wave * 32 + r, valid - 1);
-  const int64_t xs_row = p.x_row_shift ? br0 + (min(wave * 32, valid - 1) >> 5) : start + t0 + tok;
-  const uint32_t* xs_ptr = reinterpret_cast<const uint32_t*>(p.x_scale + xs_row * lds_s);
+  // Scale rows: X of the wave's two token blocks (SQ32) or the lane's tokens (ROW32), W rows of the
+  // wave's four column blocks, all clamped into range (clamped rows are never stored).
+  const uint32_t* xs_ptr[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int b0 = 64 * tq + 32 * i;
+    const int64_t row = p.x_row_shift ? br0 + (min(b0, valid - 1) >> 5) : start + t0 + min(b0 + r, valid - 1);
+    xs_ptr[i] = reinterpret_cast<const uint32_t*>(p.x_scale + row * lds_s);
+  }
   const uint32_t* ws_ptr[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    ws_ptr[j] = reinterpret_cast<const uint32_t*>(p.w_scale + ((int64_t)ct * kTile + 32 * j + r) * lds_s);
+    ws_ptr[j] = reinterpret_cast<const uint32_t*>(
+        p.w_scale + ((int64_t)ct * kCol + min(128 * cq + 32 * j + r, wrows - 1)) * lds_s);
 
   const int nchunks = p.C_in / kChunk;
-  uint32_t xsc = xs_ptr[0], wsc[4];
+  uint32_t xsc[2], wsc[4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) xsc[i] = xs_ptr[i][0];
 #pragma unroll
   for (int j = 0; j < 4; ++j) wsc[j] = ws_ptr[j][0];
   issue_chunk_load(lds[0][0], xbase, valid, ldw, trow, tcol, wave_s);
-  issue_chunk_load(lds[0][1], wbase, kTile, ldw, trow, tcol, wave_s);
+  issue_chunk_load(lds[0][1], wbase, wrows, ldw, trow, tcol, wave_s);
   wait_vm();
   __syncthreads();
 
-  mx_v16f acc[4];
+  // acc[i][j]: Y^T block of column block 4 cq + j and token block 2 tq + i (A = W rows, B = X rows)
+  mx_v16f acc[2][4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) acc[j] = mx_v16f{};
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = mx_v16f{};
 
   for (int c = 0; c < nchunks; ++c) {
     const int st = c & 1;
-    uint32_t xsn = 0, wsn[4] = {0, 0, 0, 0};
+    uint32_t xsn[2] = {0, 0}, wsn[4] = {0, 0, 0, 0};
     if (c + 1 < nchunks) {
-      xsn = xs_ptr[c + 1];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) xsn[i] = xs_ptr[i][c + 1];
 #pragma unroll
       for (int j = 0; j < 4; ++j) wsn[j] = ws_ptr[j][c + 1];
-      issue_chunk_load(lds[st ^ 1][0], xbase + (c + 1) * kChunk, valid, ldw, trow, tcol, wave_s);
-      issue_chunk_load(lds[st ^ 1][1], wbase + (c + 1) * kChunk, kTile, ldw, trow, tcol, wave_s);
+      issue_chunk_load(lds[st ^ 1][0], (const uint8_t*)mx_uniform_ptr((void*)(xbase + (c + 1) * kChunk)), valid, ldw,
+                       trow, tcol, wave_s);
+      issue_chunk_load(lds[st ^ 1][1], (const uint8_t*)mx_uniform_ptr((void*)(wbase + (c + 1) * kChunk)), wrows, ldw,
+                       trow, tcol, wave_s);
     }
-    const uint32_t xs_l = xsc >> (8 * hh);
 #pragma unroll
     for (int ds = 0; ds < 2; ++ds) {
-      const mx_v8i xb = lds_row_operand(lds[st][0], wave * 32 + r, ds, hh);
+      mx_v8i xb[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) xb[i] = lds_row_operand(lds[st][0], 64 * tq + 32 * i + r, ds, hh);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const mx_v8i wa = lds_row_operand(lds[st][1], 32 * j + r, ds, hh);
+        const mx_v8i wa = lds_row_operand(lds[st][1], 128 * cq + 32 * j + r, ds, hh);
         const uint32_t ws_l = wsc[j] >> (8 * hh);
-        if (ds == 0)
-          acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wa, xb, acc[j], 0, 0, 0, (int)ws_l, 0, (int)xs_l);
-        else
-          acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wa, xb, acc[j], 0, 0, 2, (int)ws_l, 2, (int)xs_l);
-        asm volatile("" : "+v"(acc[j])::"memory");
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const uint32_t xs_l = xsc[i] >> (8 * hh);
+          if (ds == 0)
+            acc[i][j] =
+                __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wa, xb[i], acc[i][j], 0, 0, 0, (int)ws_l, 0, (int)xs_l);
+          else
+            acc[i][j] =
+                __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wa, xb[i], acc[i][j], 0, 0, 2, (int)ws_l, 2, (int)xs_l);
+        }
       }
     }
     wait_vm();
     __syncthreads();
-    xsc = xsn;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) xsc[i] = xsn[i];
 #pragma unroll
     for (int j = 0; j < 4; ++j) wsc[j] = wsn[j];
   }
 
-  // ---- epilogue: one 32 x 32 output block per accumulator ----
-  if (wave * 32 >= valid) return;  // token block entirely past the sequence end (no barrier below)
-  const bool live = wave * 32 + r < valid;
-  const int64_t br = br0 + wave;
+  // ---- epilogue: one 32 x 32 output block per accumulator (no barrier below) ----
+  if (!col_live) return;
   const int ncs = p.C_out >> 5;
-  uint8_t* drow = p.data + (start + t0 + wave * 32 + r) * (int64_t)p.C_out + ct * kTile + 4 * hh;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    uint32_t m = 0;
-    if (live) {
+  for (int i = 0; i < 2; ++i) {
+    const int b0 = 64 * tq + 32 * i;  // first token of the block inside the tile
+    if (b0 >= valid) break;           // wave-uniform: this and the next token block are past the end
+    const bool live = b0 + r < valid;
+    const int64_t br = br0 + (b0 >> 5);
+    uint8_t* drow = p.data + (start + t0 + b0 + r) * (int64_t)p.C_out + ct * kCol + 128 * cq + 4 * hh;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) m = max(m, __float_as_uint(acc[j][v]) & 0x7fffffffu);
-    }
-    m = wave_max_dpp(m);
-    const uint32_t code = mx_code_from_amax_bits(m);
-    uint32_t words[4];
-    if (code == 255u) {
+    for (int j = 0; j < 4; ++j) {
+      uint32_t m = 0;
+      if (live) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) words[i] = 0x7f7f7f7fu;
-    } else {
-      const float inv = mx_inv_scale(code);
+        for (int v = 0; v < 16; ++v) m = max(m, __float_as_uint(acc[i][j][v]) & 0x7fffffffu);
+      }
+      m = wave_max_dpp(m);
+      const uint32_t code = mx_code_from_amax_bits(m);
+      uint32_t words[4];
+      if (code == 255u) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        words[i] = mx_pack4(acc[j][4 * i] * inv, acc[j][4 * i + 1] * inv, acc[j][4 * i + 2] * inv,
-                            acc[j][4 * i + 3] * inv);
-    }
-    if (live) {
+        for (int q = 0; q < 4; ++q) words[q] = 0x7f7f7f7fu;
+      } else {
+        const float inv = mx_inv_scale(code);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) *reinterpret_cast<uint32_t*>(drow + 32 * j + 8 * i) = words[i];
-    }
-    if (lane == 0) {
-      const int cb = ct * 4 + j;
-      p.scale[br * ncs + cb] = (uint8_t)code;
-      if (p.scale_t) p.scale_t[(int64_t)cb * nb_total + br] = (uint8_t)code;
+        for (int q = 0; q < 4; ++q)
+          words[q] = mx_pack4(acc[i][j][4 * q] * inv, acc[i][j][4 * q + 1] * inv, acc[i][j][4 * q + 2] * inv,
+                              acc[i][j][4 * q + 3] * inv);
+      }
+      if (live) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) *reinterpret_cast<uint32_t*>(drow + 32 * j + 8 * q) = words[q];
+      }
+      if (lane == 0) {
+        const int cb = (ct * kCol + 128 * cq) / 32 + j;
+        p.scale[br * ncs + cb] = (uint8_t)code;
+        if (p.scale_t) p.scale_t[(int64_t)cb * nb_total + br] = (uint8_t)code;
+      }
     }
   }
 }
@@ -224,8 +260,8 @@ hipError_t launch_linear_quantize(const MxOperand& x, const MxOperand& w, int64_
   p.w_scale = w.scale;
   p.cu = cu;
   p.nseq = nseq;
-  p.tiles_per_seq = (max_seqlen + kTile - 1) / kTile;
-  p.n_coltiles = C_out / kTile;
+  p.tiles_per_seq = (max_seqlen + kTok - 1) / kTok;
+  p.n_coltiles = (C_out + kCol - 1) / kCol;
   p.C_in = C_in;
   p.C_out = C_out;
   p.data = data;
@@ -234,7 +270,7 @@ hipError_t launch_linear_quantize(const MxOperand& x, const MxOperand& w, int64_
   const int64_t items = (int64_t)nseq * p.tiles_per_seq * p.n_coltiles;
   if (T == 0 || items == 0) return hipSuccess;
   p.total_items = (int)items;
-  hipLaunchKernelGGL(linear_quantize_kernel, dim3((unsigned)items), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(linear_quantize_kernel, dim3((unsigned)items), dim3(64 * kLinWaves), 0, stream, p);
   return hipGetLastError();
 }
 
