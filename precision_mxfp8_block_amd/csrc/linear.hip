@@ -151,6 +151,10 @@ __global__ void __launch_bounds__(64 * kLinWaves, 1) linear_quantize_kernel(Line
   issue_chunk_load(lds[0][0], xbase, valid, ldw, trow, tcol, wave_s);
   issue_chunk_load(lds[0][1], wbase, wrows, ldw, trow, tcol, wave_s);
   wait_vm();
+#pragma unroll
+  for (int i = 0; i < 2; ++i) asm volatile("" : "+v"(xsc[i]));  // loaded: see the loop's wait below
+#pragma unroll
+  for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(wsc[j]));
   __syncthreads();
 
   // acc[i][j]: Y^T block of column block 4 cq + j and token block 2 tq + i (A = W rows, B = X rows)
@@ -195,6 +199,14 @@ __global__ void __launch_bounds__(64 * kLinWaves, 1) linear_quantize_kernel(Line
       }
     }
     wait_vm();
+    // The next chunk's scale words were loaded before the direct loads above; their first use is
+    // pinned here, after the wait. Otherwise the compiler places its own wait for them among this
+    // chunk's MFMAs, and because the hardware counter retires in order, that wait also waits for
+    // the direct loads of the next chunk.
+#pragma unroll
+    for (int i = 0; i < 2; ++i) asm volatile("" : "+v"(xsn[i]));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(wsn[j]));
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < 2; ++i) xsc[i] = xsn[i];
@@ -202,46 +214,67 @@ __global__ void __launch_bounds__(64 * kLinWaves, 1) linear_quantize_kernel(Line
     for (int j = 0; j < 4; ++j) wsc[j] = wsn[j];
   }
 
-  // ---- epilogue: one 32 x 32 output block per accumulator (no barrier below) ----
-  if (!col_live) return;
+  // ---- epilogue: one 32 x 32 output block per accumulator ----
+  // The payload goes through LDS (the chunk buffers are free after the loop's last barrier): a
+  // lane's accumulator holds 4-byte pieces of 32 different token rows, which as direct stores would
+  // be partial-line writes; staged as a 256-token x 256-byte tile (16-byte pieces XOR-swizzled by
+  // row) it leaves as whole 256-byte row segments, 16 bytes per lane.
+  uint8_t* stage = &lds[0][0][0];
   const int ncs = p.C_out >> 5;
+  if (col_live) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int b0 = 64 * tq + 32 * i;  // first token of the block inside the tile
-    if (b0 >= valid) break;           // wave-uniform: this and the next token block are past the end
-    const bool live = b0 + r < valid;
-    const int64_t br = br0 + (b0 >> 5);
-    uint8_t* drow = p.data + (start + t0 + b0 + r) * (int64_t)p.C_out + ct * kCol + 128 * cq + 4 * hh;
+    for (int i = 0; i < 2; ++i) {
+      const int b0 = 64 * tq + 32 * i;  // first token of the block inside the tile
+      if (b0 >= valid) break;           // wave-uniform: this and the next token block are past the end
+      const int trow_l = b0 + r;
+      const bool live = trow_l < valid;
+      const int64_t br = br0 + (b0 >> 5);
+      uint8_t* srow = stage + trow_l * kCol;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint32_t m = 0;
-      if (live) {
+      for (int j = 0; j < 4; ++j) {
+        uint32_t m = 0;
+        if (live) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) m = max(m, __float_as_uint(acc[i][j][v]) & 0x7fffffffu);
-      }
-      m = wave_max_dpp(m);
-      const uint32_t code = mx_code_from_amax_bits(m);
-      uint32_t words[4];
-      if (code == 255u) {
+          for (int v = 0; v < 16; ++v) m = max(m, __float_as_uint(acc[i][j][v]) & 0x7fffffffu);
+        }
+        m = wave_max_dpp(m);
+        const uint32_t code = mx_code_from_amax_bits(m);
+        uint32_t words[4];
+        if (code == 255u) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) words[q] = 0x7f7f7f7fu;
-      } else {
-        const float inv = mx_inv_scale(code);
+          for (int q = 0; q < 4; ++q) words[q] = 0x7f7f7f7fu;
+        } else {
+          const float inv = mx_inv_scale(code);
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          words[q] = mx_pack4(acc[i][j][4 * q] * inv, acc[i][j][4 * q + 1] * inv, acc[i][j][4 * q + 2] * inv,
-                              acc[i][j][4 * q + 3] * inv);
-      }
-      if (live) {
+          for (int q = 0; q < 4; ++q)
+            words[q] = mx_pack4(acc[i][j][4 * q] * inv, acc[i][j][4 * q + 1] * inv, acc[i][j][4 * q + 2] * inv,
+                                acc[i][j][4 * q + 3] * inv);
+        }
+        if (live) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) *reinterpret_cast<uint32_t*>(drow + 32 * j + 8 * q) = words[q];
-      }
-      if (lane == 0) {
-        const int cb = (ct * kCol + 128 * cq) / 32 + j;
-        p.scale[br * ncs + cb] = (uint8_t)code;
-        if (p.scale_t) p.scale_t[(int64_t)cb * nb_total + br] = (uint8_t)code;
+          for (int q = 0; q < 4; ++q) {
+            const int cb = 128 * cq + 32 * j + 8 * q + 4 * hh;  // byte column inside the tile
+            *reinterpret_cast<uint32_t*>(srow + (((cb >> 4) ^ (trow_l & 15)) << 4) + (cb & 15)) = words[q];
+          }
+        }
+        if (lane == 0) {
+          const int cb = (ct * kCol + 128 * cq) / 32 + j;
+          p.scale[br * ncs + cb] = (uint8_t)code;
+          if (p.scale_t) p.scale_t[(int64_t)cb * nb_total + br] = (uint8_t)code;
+        }
       }
     }
+  }
+  __syncthreads();
+  const int kq = tid & 15;           // 16-byte piece of the row
+  const bool kq_live = 16 * kq < wrows;
+  uint8_t* dtile = p.data + (start + t0) * (int64_t)p.C_out + ct * kCol + 16 * kq;
+#pragma unroll
+  for (int pass = 0; pass < kTok / 32; ++pass) {
+    const int row = pass * 32 + (tid >> 4);
+    if (row < valid && kq_live)
+      *reinterpret_cast<uint4*>(dtile + row * (int64_t)p.C_out) =
+          *reinterpret_cast<const uint4*>(stage + row * kCol + ((kq ^ (row & 15)) << 4));
   }
 }
 
