@@ -58,6 +58,11 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
 // The direct LDS loads are inline asm (mx_lds_dma16) and so is their wait: with the compiler's own
 // direct-load builtin it waits for every outstanding load before the next LDS read, i.e. for the
 // next chunk's prefetch before the current chunk's MFMAs.
+template <int N>
+struct IntC {
+  static constexpr int value = N;
+};
+
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Global -> LDS copy of a 256-row x 128-byte chunk (row stride ld bytes, `base` wave-uniform) into a
@@ -81,16 +86,13 @@ __device__ __forceinline__ mx_v8i lds_row_operand(const uint8_t* lds, int row, i
   return mx_v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
-// Maximum over the 64 lanes of a wave (DPP inside rows of 16, then lane swaps across rows).
-__device__ __forceinline__ uint32_t wave_max_dpp(uint32_t v) {
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x141, 0xF, 0xF, false));  // row_half_mirror
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x140, 0xF, 0xF, false));  // row_mirror
-  auto s16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-  v = max((uint32_t)s16[0], (uint32_t)s16[1]);
-  auto s32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-  return max((uint32_t)s32[0], (uint32_t)s32[1]);
+// Four floats -> four E4M3 bytes of x / sc (sc a power of two) with no saturation: for callers that
+// know |x| / sc <= 448.
+__device__ __forceinline__ uint32_t pack4_div(float a, float b, float c, float d, float sc) {
+  typedef short v2s __attribute__((ext_vector_type(2)));
+  v2s r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(__builtin_bit_cast(v2s, a), a, b, sc, false);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, c, d, sc, true);
+  return __builtin_bit_cast(uint32_t, r);
 }
 
 __global__ void __launch_bounds__(64 * kLinWaves, 1) linear_quantize_kernel(LinearParams p) {
@@ -177,27 +179,44 @@ __global__ void __launch_bounds__(64 * kLinWaves, 1) linear_quantize_kernel(Line
       issue_chunk_load(lds[st ^ 1][1], (const uint8_t*)mx_uniform_ptr((void*)(wbase + (c + 1) * kChunk)), wrows, ldw,
                        trow, tcol, wave_s);
     }
+    // Operands are read from LDS two MFMA steps ahead of their use (a step = one W operand times
+    // both X operands, 2 MFMAs); the X operands of the second 64-byte half are read during the
+    // first half. The scheduling groups keep that order: LDS latency stays behind MFMA work.
+    const uint8_t* lx = lds[st][0];
+    const uint8_t* lw = lds[st][1];
+    mx_v8i xb[2][2], wa[8];
 #pragma unroll
-    for (int ds = 0; ds < 2; ++ds) {
-      mx_v8i xb[2];
+    for (int i = 0; i < 2; ++i) xb[0][i] = lds_row_operand(lx, 64 * tq + 32 * i + r, 0, hh);
+    wa[0] = lds_row_operand(lw, 128 * cq + r, 0, hh);
+    wa[1] = lds_row_operand(lw, 128 * cq + 32 + r, 0, hh);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // LDS reads
+    auto step = [&](auto S_) {
+      constexpr int s = decltype(S_)::value;
+      constexpr int ds = s >> 2, j = s & 3;
+      constexpr int nreads = (s + 2 < 8 ? 2 : 0) + (s == 2 ? 4 : 0);
+      if constexpr (s + 2 < 8) wa[s + 2] = lds_row_operand(lw, 128 * cq + 32 * ((s + 2) & 3) + r, (s + 2) >> 2, hh);
+      if constexpr (s == 2) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) xb[i] = lds_row_operand(lds[st][0], 64 * tq + 32 * i + r, ds, hh);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const mx_v8i wa = lds_row_operand(lds[st][1], 128 * cq + 32 * j + r, ds, hh);
-        const uint32_t ws_l = wsc[j] >> (8 * hh);
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const uint32_t xs_l = xsc[i] >> (8 * hh);
-          if (ds == 0)
-            acc[i][j] =
-                __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wa, xb[i], acc[i][j], 0, 0, 0, (int)ws_l, 0, (int)xs_l);
-          else
-            acc[i][j] =
-                __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wa, xb[i], acc[i][j], 0, 0, 2, (int)ws_l, 2, (int)xs_l);
-        }
+        for (int i = 0; i < 2; ++i) xb[1][i] = lds_row_operand(lx, 64 * tq + 32 * i + r, 1, hh);
       }
-    }
+      const uint32_t ws_l = wsc[j] >> (8 * hh);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const uint32_t xs_l = xsc[i] >> (8 * hh);
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wa[s], xb[ds][i], acc[i][j], 0, 0, 2 * ds, (int)ws_l,
+                                                                    2 * ds, (int)xs_l);
+      }
+      if constexpr (nreads > 0) __builtin_amdgcn_sched_group_barrier(0x100, nreads, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+    };
+    step(IntC<0>{});
+    step(IntC<1>{});
+    step(IntC<2>{});
+    step(IntC<3>{});
+    step(IntC<4>{});
+    step(IntC<5>{});
+    step(IntC<6>{});
+    step(IntC<7>{});
     wait_vm();
     // The next chunk's scale words were loaded before the direct loads above; their first use is
     // pinned here, after the wait. Otherwise the compiler places its own wait for them among this
@@ -221,48 +240,103 @@ __global__ void __launch_bounds__(64 * kLinWaves, 1) linear_quantize_kernel(Line
   // row) it leaves as whole 256-byte row segments, 16 bytes per lane.
   uint8_t* stage = &lds[0][0][0];
   const int ncs = p.C_out >> 5;
-  if (col_live) {
+  if (col_live) {  // wave-uniform
+    // Rows past the sequence end hold finite values (their X rows re-read the last valid row): they
+    // are converted and staged like the others but take no part in the block maximum and are never
+    // stored, so the block loop has no lane-dependent branches.
+    const bool live0 = 64 * tq + r < valid, live1 = 64 * tq + 32 + r < valid;
+    // |y| maximum of each lane's 16 values per block, on the bit patterns: the unsigned maximum is
+    // led by the negative value of largest magnitude (if any), the signed one by the largest
+    // positive value. v[4 i + j] = block (i, j).
+    uint32_t v[8];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t mu = 0;
+        int32_t mi = 0;
+#pragma unroll
+        for (int e = 0; e < 16; e += 2) {
+          const uint32_t b0 = __float_as_uint(acc[i][j][e]), b1 = __float_as_uint(acc[i][j][e + 1]);
+          mu = max(max(mu, b0), b1);
+          mi = max(max(mi, (int32_t)b0), (int32_t)b1);
+        }
+        v[4 * i + j] = (i ? live1 : live0) ? max(mu & 0x7fffffffu, (uint32_t)mi) : 0u;
+      }
+    // The eight wave-wide maxima in one pass: swapping lane halves pairs block k (lanes 0-31) with
+    // block k + 4 (lanes 32-63) in one register, swapping 16-lane rows then packs four blocks per
+    // register (v[0]: blocks 0, 1, 4, 5 in rows 0-3; v[2]: blocks 2, 3, 6, 7), and four DPP steps
+    // finish each row.
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      auto sw = __builtin_amdgcn_permlane32_swap(v[k], v[k + 4], false, false);
+      v[k] = max((uint32_t)sw[0], (uint32_t)sw[1]);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; k += 2) {
+      auto sw = __builtin_amdgcn_permlane16_swap(v[k], v[k + 1], false, false);
+      uint32_t x = max((uint32_t)sw[0], (uint32_t)sw[1]);
+      x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0u, x, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+      x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0u, x, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+      x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0u, x, 0x141, 0xF, 0xF, false));  // row_half_mirror
+      v[k] = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0u, x, 0x140, 0xF, 0xF, false));  // row_mirror
+    }
+    uint32_t amax[8];  // wave-uniform
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int reg = (k & 2) ? 2 : 0;                    // blocks 2, 3, 6, 7 in v[2]
+      const int row = (k & 1) | ((k >> 1) & 2);           // row of block k inside its register
+      amax[k] = __builtin_amdgcn_readlane(v[reg], 16 * row);
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int b0 = 64 * tq + 32 * i;  // first token of the block inside the tile
-      if (b0 >= valid) break;           // wave-uniform: this and the next token block are past the end
-      const int trow_l = b0 + r;
-      const bool live = trow_l < valid;
-      const int64_t br = br0 + (b0 >> 5);
+      const int trow_l = 64 * tq + 32 * i + r;
       uint8_t* srow = stage + trow_l * kCol;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        uint32_t m = 0;
-        if (live) {
-#pragma unroll
-          for (int v = 0; v < 16; ++v) m = max(m, __float_as_uint(acc[i][j][v]) & 0x7fffffffu);
-        }
-        m = wave_max_dpp(m);
+        const uint32_t m = amax[4 * i + j];
         const uint32_t code = mx_code_from_amax_bits(m);
+        const mx_v16f& y = acc[i][j];
         uint32_t words[4];
-        if (code == 255u) {
+        if (code == 255u) {  // scalar branches from here on
 #pragma unroll
           for (int q = 0; q < 4; ++q) words[q] = 0x7f7f7f7fu;
+        } else if (code >= 8u) {
+          // y / 2^(code - 127) in the converter; no clamp is needed when the block maximum's
+          // mantissa is at most 1.75 (then |y| / 2^(code - 127) <= 448)
+          const float sc = __uint_as_float(code << 23);
+          if ((m & 0x7fffffu) <= 0x600000u) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) words[q] = pack4_div(y[4 * q], y[4 * q + 1], y[4 * q + 2], y[4 * q + 3], sc);
+          } else {
+            const float lim = __uint_as_float(((code + 8u) << 23) | 0x600000u);  // 448 sc
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              words[q] = mx_pack4_scaled(y[4 * q], y[4 * q + 1], y[4 * q + 2], y[4 * q + 3], sc, lim);
+          }
         } else {
           const float inv = mx_inv_scale(code);
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            words[q] = mx_pack4(acc[i][j][4 * q] * inv, acc[i][j][4 * q + 1] * inv, acc[i][j][4 * q + 2] * inv,
-                                acc[i][j][4 * q + 3] * inv);
+            words[q] = mx_pack4(y[4 * q] * inv, y[4 * q + 1] * inv, y[4 * q + 2] * inv, y[4 * q + 3] * inv);
         }
-        if (live) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int cb = 128 * cq + 32 * j + 8 * q + 4 * hh;  // byte column inside the tile
-            *reinterpret_cast<uint32_t*>(srow + (((cb >> 4) ^ (trow_l & 15)) << 4) + (cb & 15)) = words[q];
-          }
-        }
-        if (lane == 0) {
-          const int cb = (ct * kCol + 128 * cq) / 32 + j;
-          p.scale[br * ncs + cb] = (uint8_t)code;
-          if (p.scale_t) p.scale_t[(int64_t)cb * nb_total + br] = (uint8_t)code;
+        for (int q = 0; q < 4; ++q) {
+          const int cb = 128 * cq + 32 * j + 8 * q + 4 * hh;  // byte column inside the tile
+          *reinterpret_cast<uint32_t*>(srow + (((cb >> 4) ^ (trow_l & 15)) << 4) + (cb & 15)) = words[q];
         }
       }
+    }
+    // lane k < 8 stores the code of block (k >> 2, k & 3) in both scale layouts
+    uint32_t mine = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) mine = lane == k ? mx_code_from_amax_bits(amax[k]) : mine;
+    const int bi = (lane >> 2) & 1, bj = lane & 3;
+    if (lane < 8 && 64 * tq + 32 * bi < valid) {
+      const int64_t br = br0 + 2 * tq + bi;
+      const int cb = (ct * kCol + 128 * cq) / 32 + bj;
+      p.scale[br * ncs + cb] = (uint8_t)mine;
+      if (p.scale_t) p.scale_t[(int64_t)cb * nb_total + br] = (uint8_t)mine;
     }
   }
   __syncthreads();

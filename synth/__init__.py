@@ -104,6 +104,15 @@ def normal_bf16(seed, stream, shape, std=1.0, outlier_p=0.0, outlier_mult=64.0, 
     return out.reshape(shape)
 
 
+def signs_bf16(seed, stream, shape, exp2):
+    """bf16 bits of +-2^exp2 (a normal bf16 power of two), the sign of element i from bit 0 of
+    draw i+1 of the stream."""
+    n = int(np.prod(shape))
+    mag = np.uint16((127 + int(exp2)) << 7)
+    neg = (raw_u64(seed, stream, n) & np.uint64(1)).astype(np.uint16) << np.uint16(15)
+    return (mag | neg).reshape(shape)
+
+
 def lengths(seed, n, lo, hi):
     """n integer sequence lengths, uniform in [lo, hi]."""
     u = uniform(seed, STREAM_LENGTHS, n)

@@ -245,16 +245,22 @@ class LinearCase:
     """Seeded projection: X bf16 ~ N(0,1) [T, C_in] quantized SQ32 (or ROW32), W bf16 ~ N(0, 0.02)
     [C_out, C_in] quantized ROW32. Quantization of the inputs is done by the oracle (inputs only)."""
 
-    def __init__(self, seed, lens, C_in, C_out, x_mode=None, nan_at=None):
+    def __init__(self, seed, lens, C_in, C_out, x_mode=None, nan_at=None, pm_exp2=None):
         self.cu = synth.cu_seqlens(lens)
         self.lens = list(lens)
         self.T = int(self.cu[-1])
         self.C_in, self.C_out = C_in, C_out
         self.x_mode = oracle.SQ32 if x_mode is None else x_mode
-        x = synth.normal_bf16(seed, synth.STREAM_ACT, (self.T, C_in))
+        if pm_exp2 is None:
+            x = synth.normal_bf16(seed, synth.STREAM_ACT, (self.T, C_in))
+            w = synth.normal_bf16(seed, synth.STREAM_WEIGHT, (C_out, C_in), std=0.02)
+        else:
+            # +-2^a and +-2^b entries: every product is +-2^(a+b), so Y is exact in FP32 whatever
+            # the summation order, and tiny exponents reach the smallest output scale codes
+            x = synth.signs_bf16(seed, synth.STREAM_ACT, (self.T, C_in), pm_exp2[0])
+            w = synth.signs_bf16(seed, synth.STREAM_WEIGHT, (C_out, C_in), pm_exp2[1])
         if nan_at is not None:
             x[nan_at] = 0x7fc0
-        w = synth.normal_bf16(seed, synth.STREAM_WEIGHT, (C_out, C_in), std=0.02)
         self.xd, self.xs, _ = oracle.quantize(x, self.cu, self.x_mode)
         self.wd, self.ws, _ = oracle.quantize(w, np.array([0, C_out], np.int32), oracle.ROW32)
 

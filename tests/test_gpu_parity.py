@@ -97,21 +97,28 @@ def test_rmsnorm_quantize_bit_exact(lens):
 
 
 LINEAR_CASES = [
-    # (label, seed, lens, C_in, C_out, x_mode, nan_at)
-    ("dense_T256_1024x1024", 21, [256], 1024, 1024, oracle.SQ32, None),
-    ("jagged_ragged_256x256", 22, [40, 300, 1, 129], 256, 256, oracle.SQ32, None),
-    ("row32_x_128x384", 23, [200], 128, 384, oracle.ROW32, None),
-    ("nan_block", 24, [64, 96], 256, 128, oracle.SQ32, (70, 5)),
+    # (label, seed, lens, C_in, C_out, x_mode, nan_at, pm_exp2)
+    ("dense_T256_1024x1024", 21, [256], 1024, 1024, oracle.SQ32, None, None),
+    ("jagged_ragged_256x256", 22, [40, 300, 1, 129], 256, 256, oracle.SQ32, None, None),
+    ("row32_x_128x384", 23, [200], 128, 384, oracle.ROW32, None, None),
+    ("nan_block", 24, [64, 96], 256, 128, oracle.SQ32, (70, 5), None),
+    # products of +-2^-60 entries: Y is exact and its block codes fall below 8
+    ("tiny_codes_exact", 25, [96, 200], 256, 384, oracle.SQ32, None, (-60, -60)),
 ]
 
 
 @pytest.mark.parametrize("case", LINEAR_CASES, ids=[c[0] for c in LINEAR_CASES])
 def test_linear_quantize_certified(case):
-    label, seed, lens, C_in, C_out, x_mode, nan_at = case
+    label, seed, lens, C_in, C_out, x_mode, nan_at, pm_exp2 = case
     say(f"linear {label}")
-    lc = LinearCase(seed, lens, C_in, C_out, x_mode=x_mode, nan_at=nan_at)
+    lc = LinearCase(seed, lens, C_in, C_out, x_mode=x_mode, nan_at=nan_at, pm_exp2=pm_exp2)
     dg, sg, stg = lc.run_gpu()
     do, so, sto, y, yabs = lc.run_oracle()
+    if pm_exp2 is not None:  # exact Y: bytes and codes must match exactly
+        assert int(so[so != 255].max()) < 8, "the case must reach output codes below 8"
+        np.testing.assert_array_equal(sg, so)
+        np.testing.assert_array_equal(stg, sto)
+        np.testing.assert_array_equal(dg, do)
     certify_linear(dg, sg, stg, do, so, y, yabs, lc.cu, label)
 
 
