@@ -32,7 +32,8 @@ namespace {
 
 constexpr int kTok = 256;    // tokens per workgroup
 constexpr int kCol = 256;    // output columns per workgroup
-constexpr int kChunk = 128;  // bytes of C_in per LDS stage
+constexpr int kHalf = 64;    // bytes of C_in per LDS stage
+constexpr int kStages = 4;   // stages in the LDS ring (three loads in flight)
 constexpr int kLinWaves = 8;
 
 struct LinearParams {
@@ -55,34 +56,46 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
   return x * per + (x < rem ? x : rem) + slot;
 }
 
-// The direct LDS loads are inline asm (mx_lds_dma16) and so is their wait: with the compiler's own
-// direct-load builtin it waits for every outstanding load before the next LDS read, i.e. for the
-// next chunk's prefetch before the current chunk's MFMAs.
+// The direct LDS loads are inline asm (mx_lds_dma16/4) and so are their waits and the stage
+// barriers: the compiler's own direct-load builtin makes it wait for every outstanding load before
+// the next LDS read, and its workgroup barrier waits for every outstanding load as well. The counts
+// are exact per wave (see the issue order in the kernel); loads retire in order.
+template <int N>
+__device__ __forceinline__ void wait_vm_n() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Every wave's LDS reads so far have completed and its loads up to the last wait are visible.
+__device__ __forceinline__ void stage_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 template <int N>
 struct IntC {
   static constexpr int value = N;
 };
 
-__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// XOR swizzle of the 16-byte piece inside a 64-byte LDS row: the 16 rows that one 16-lane group of
+// an operand read touches fall on 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int swz64(int row) { return (row >> 2) & 3; }
 
-// Global -> LDS copy of a 256-row x 128-byte chunk (row stride ld bytes, `base` wave-uniform) into a
-// swizzled LDS tile, four 1 KB pieces per wave; rows at or past `valid` re-fetch the last valid row
-// (finite data, never stored).
-__device__ __forceinline__ void issue_chunk_load(uint8_t* lds_tile, const uint8_t* base, int valid, int ld,
-                                                 const int* trow, const int* tcol, int wave_s) {
+// Global -> LDS copy of a 256-row x 64-byte stage tile (row stride ld bytes, `base` wave-uniform),
+// two 1 KB pieces per wave; rows at or past `valid` re-fetch the last valid row (finite data, never
+// stored). A dummy copy (every lane reads the first 16 bytes at `base`) keeps the number of loads per
+// stage fixed past the end of C_in; its destination is a free stage.
+__device__ __forceinline__ void issue_half_load(uint8_t* lds_tile, const uint8_t* base, int valid, int ld,
+                                                const int* trow, const int* tcol, int wave_s, bool dummy) {
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const uint32_t off = (uint32_t)(min(trow[c], valid - 1) * ld + tcol[c]);
-    mx_lds_dma16((MX_LDS void*)(lds_tile + (wave_s * 4 + c) * 1024), base, off);
+  for (int c = 0; c < 2; ++c) {
+    const uint32_t off = dummy ? 0u : (uint32_t)(min(trow[c], valid - 1) * ld + tcol[c]);
+    mx_lds_dma16((MX_LDS void*)(lds_tile + (wave_s * 2 + c) * 1024), base, off);
   }
 }
 
-// Operand of a 32x32x64 MFMA from row `row` of a swizzled LDS tile, 64-byte step ds.
-__device__ __forceinline__ mx_v8i lds_row_operand(const uint8_t* lds, int row, int ds, int hh) {
-  const uint8_t* p = lds + row * kChunk;
-  const int sw = lds_swz(row);
-  uint4 lo = *reinterpret_cast<const uint4*>(p + 16 * ((4 * ds + hh) ^ sw));
-  uint4 hi = *reinterpret_cast<const uint4*>(p + 16 * ((4 * ds + 2 + hh) ^ sw));
+// Operand of a 32x32x64 MFMA from row `row` of a swizzled 64-byte-row stage tile: lanes 0-31 take
+// bytes [0, 16) and [32, 48), lanes 32-63 bytes [16, 32) and [48, 64).
+__device__ __forceinline__ mx_v8i stage_operand(const uint8_t* lds, int row, int hh) {
+  const uint8_t* p = lds + row * kHalf;
+  const int sw = swz64(row);
+  uint4 lo = *reinterpret_cast<const uint4*>(p + 16 * (hh ^ sw));
+  uint4 hi = *reinterpret_cast<const uint4*>(p + 16 * ((2 + hh) ^ sw));
   return mx_v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
@@ -96,7 +109,8 @@ __device__ __forceinline__ uint32_t pack4_div(float a, float b, float c, float d
 }
 
 __global__ void __launch_bounds__(64 * kLinWaves, 1) linear_quantize_kernel(LinearParams p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2][2][kTok * kChunk];  // stage x (X, W)
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages][2][kTok * kHalf];  // stage x (X, W)
+  __shared__ __attribute__((aligned(16))) uint8_t lds_sc[kStages][2 * 256 * 4];    // scale words: X, W
 
   const int item = xcd_remap((int)blockIdx.x, p.total_items);
   const int ct = item % p.n_coltiles;
@@ -119,45 +133,60 @@ __global__ void __launch_bounds__(64 * kLinWaves, 1) linear_quantize_kernel(Line
   const int lds_s = p.C_in >> 5;  // scale row length in bytes (both X and W)
   const int wrows = min(kCol, p.C_out - ct * kCol);  // 256, or 128 for a last half tile
   const bool col_live = 128 * cq < wrows;           // wave-uniform
-  int trow[4], tcol[4];
+  int trow[2], tcol[2];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const int pc = (wave_s * 4 + c) * 64 + lane;
-    trow[c] = pc >> 3;
-    tcol[c] = 16 * ((pc & 7) ^ lds_swz(pc >> 3));
+  for (int c = 0; c < 2; ++c) {
+    const int pc = (wave_s * 2 + c) * 64 + lane;  // 16-byte piece of a 256 x 64-byte stage tile
+    trow[c] = pc >> 2;
+    tcol[c] = 16 * ((pc & 3) ^ swz64(pc >> 2));
   }
   const uint8_t* xbase = (const uint8_t*)mx_uniform_ptr((void*)(p.x + (start + t0) * (int64_t)ldw));
   const uint8_t* wbase = (const uint8_t*)mx_uniform_ptr((void*)(p.w + (int64_t)ct * kCol * ldw));
 
-  // Scale rows: X of the wave's two token blocks (SQ32) or the lane's tokens (ROW32), W rows of the
-  // wave's four column blocks, all clamped into range (clamped rows are never stored).
-  const uint32_t* xs_ptr[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int b0 = 64 * tq + 32 * i;
-    const int64_t row = p.x_row_shift ? br0 + (min(b0, valid - 1) >> 5) : start + t0 + min(b0 + r, valid - 1);
-    xs_ptr[i] = reinterpret_cast<const uint32_t*>(p.x_scale + row * lds_s);
+  // Scale words (4 codes = 128 bytes of C_in per row) reach LDS the same way as the payload: wave w
+  // copies 64 entries of the X part (w < 4) or W part (w >= 4) of a 2 KB ring slot per chunk. X
+  // entries are token rows (ROW32) or 32-token block rows (SQ32); rows are clamped into range
+  // (clamped rows are never stored).
+  const uint8_t* sbase;
+  uint32_t soff;
+  {
+    const int e = 64 * (wave_s & 3) + lane;
+    if (wave_s < 4) {
+      const int64_t row0 = p.x_row_shift ? br0 : start + t0;
+      sbase = p.x_scale + row0 * lds_s;
+      soff = (uint32_t)((p.x_row_shift ? min(e, (valid - 1) >> 5) : min(e, valid - 1)) * lds_s);
+    } else {
+      sbase = p.w_scale + (int64_t)ct * kCol * lds_s;
+      soff = (uint32_t)(min(e, wrows - 1) * lds_s);
+    }
+    sbase = (const uint8_t*)mx_uniform_ptr((void*)sbase);
   }
-  const uint32_t* ws_ptr[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    ws_ptr[j] = reinterpret_cast<const uint32_t*>(
-        p.w_scale + ((int64_t)ct * kCol + min(128 * cq + 32 * j + r, wrows - 1)) * lds_s);
-
-  const int nchunks = p.C_in / kChunk;
-  uint32_t xsc[2], wsc[4];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) xsc[i] = xs_ptr[i][0];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) wsc[j] = ws_ptr[j][0];
-  issue_chunk_load(lds[0][0], xbase, valid, ldw, trow, tcol, wave_s);
-  issue_chunk_load(lds[0][1], wbase, wrows, ldw, trow, tcol, wave_s);
-  wait_vm();
-#pragma unroll
-  for (int i = 0; i < 2; ++i) asm volatile("" : "+v"(xsc[i]));  // loaded: see the loop's wait below
-#pragma unroll
-  for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(wsc[j]));
-  __syncthreads();
+  const int nchunks = p.C_in >> 7;  // 128-byte chunks, two 64-byte stages each
+  const int nh = 2 * nchunks;
+  // Stage h of the ring holds C_in bytes [64 h, 64 h + 64) of the tile's X and W rows. Every wave
+  // issues, in this order: scale(0), stage 0, stage 1, scale(1), stage 2, then per chunk c stage
+  // 2c + 3 at its first barrier and scale(c + 2), stage 2c + 4 at its second. A stage is 4 direct
+  // loads per wave and a scale slot 1; past the end of C_in they are dummies, so every wait below
+  // leaves exactly 9 loads in flight and the loop body has no branches (the compiler could
+  // otherwise sink MFMAs past a wait).
+  auto issue_stage = [&](int h) {
+    const int sl = h & (kStages - 1);
+    const bool dummy = h >= nh;
+    const int hc = dummy ? 0 : h;
+    issue_half_load(lds[sl][0], (const uint8_t*)mx_uniform_ptr((void*)(xbase + hc * kHalf)), valid, ldw, trow, tcol,
+                    wave_s, dummy);
+    issue_half_load(lds[sl][1], (const uint8_t*)mx_uniform_ptr((void*)(wbase + hc * kHalf)), wrows, ldw, trow, tcol,
+                    wave_s, dummy);
+  };
+  auto issue_scales = [&](int c) {
+    mx_lds_dma4((MX_LDS void*)(lds_sc[c & (kStages - 1)] + 256 * wave_s), sbase,
+                soff + 4u * (uint32_t)min(c, nchunks - 1));
+  };
+  issue_scales(0);
+  issue_stage(0);
+  issue_stage(1);
+  issue_scales(1);
+  issue_stage(2);
 
   // acc[i][j]: Y^T block of column block 4 cq + j and token block 2 tq + i (A = W rows, B = X rows)
   mx_v16f acc[2][4];
@@ -166,72 +195,55 @@ __global__ void __launch_bounds__(64 * kLinWaves, 1) linear_quantize_kernel(Line
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = mx_v16f{};
 
-  for (int c = 0; c < nchunks; ++c) {
-    const int st = c & 1;
-    uint32_t xsn[2] = {0, 0}, wsn[4] = {0, 0, 0, 0};
-    if (c + 1 < nchunks) {
+  // MFMAs of one stage: operands read from LDS, X rows of the wave's two token blocks, W rows of its
+  // four column blocks; the scale codes of the stage's two 32-element K blocks are bytes 2 HF and
+  // 2 HF + 1 of the chunk's scale words (selected per lane half, then by op_sel).
+  auto stage_mfma = [&](auto HF_, int h, const uint32_t (&xsc)[2], const uint32_t (&wsc)[4]) {
+    constexpr int hf = decltype(HF_)::value;
+    const uint8_t* lx = lds[h & (kStages - 1)][0];
+    const uint8_t* lw = lds[h & (kStages - 1)][1];
+    mx_v8i xb[2], wa[4];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) xsn[i] = xs_ptr[i][c + 1];
+    for (int i = 0; i < 2; ++i) xb[i] = stage_operand(lx, 64 * tq + 32 * i + r, hh);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) wsn[j] = ws_ptr[j][c + 1];
-      issue_chunk_load(lds[st ^ 1][0], (const uint8_t*)mx_uniform_ptr((void*)(xbase + (c + 1) * kChunk)), valid, ldw,
-                       trow, tcol, wave_s);
-      issue_chunk_load(lds[st ^ 1][1], (const uint8_t*)mx_uniform_ptr((void*)(wbase + (c + 1) * kChunk)), wrows, ldw,
-                       trow, tcol, wave_s);
-    }
-    // Operands are read from LDS two MFMA steps ahead of their use (a step = one W operand times
-    // both X operands, 2 MFMAs); the X operands of the second 64-byte half are read during the
-    // first half. The scheduling groups keep that order: LDS latency stays behind MFMA work.
-    const uint8_t* lx = lds[st][0];
-    const uint8_t* lw = lds[st][1];
-    mx_v8i xb[2][2], wa[8];
+    for (int j = 0; j < 4; ++j) wa[j] = stage_operand(lw, 128 * cq + 32 * j + r, hh);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) xb[0][i] = lds_row_operand(lx, 64 * tq + 32 * i + r, 0, hh);
-    wa[0] = lds_row_operand(lw, 128 * cq + r, 0, hh);
-    wa[1] = lds_row_operand(lw, 128 * cq + 32 + r, 0, hh);
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // LDS reads
-    auto step = [&](auto S_) {
-      constexpr int s = decltype(S_)::value;
-      constexpr int ds = s >> 2, j = s & 3;
-      constexpr int nreads = (s + 2 < 8 ? 2 : 0) + (s == 2 ? 4 : 0);
-      if constexpr (s + 2 < 8) wa[s + 2] = lds_row_operand(lw, 128 * cq + 32 * ((s + 2) & 3) + r, (s + 2) >> 2, hh);
-      if constexpr (s == 2) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) xb[1][i] = lds_row_operand(lx, 64 * tq + 32 * i + r, 1, hh);
-      }
+    for (int j = 0; j < 4; ++j) {
       const uint32_t ws_l = wsc[j] >> (8 * hh);
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const uint32_t xs_l = xsc[i] >> (8 * hh);
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wa[s], xb[ds][i], acc[i][j], 0, 0, 2 * ds, (int)ws_l,
-                                                                    2 * ds, (int)xs_l);
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wa[j], xb[i], acc[i][j], 0, 0, 2 * hf, (int)ws_l,
+                                                                    2 * hf, (int)xs_l);
       }
-      if constexpr (nreads > 0) __builtin_amdgcn_sched_group_barrier(0x100, nreads, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
-    };
-    step(IntC<0>{});
-    step(IntC<1>{});
-    step(IntC<2>{});
-    step(IntC<3>{});
-    step(IntC<4>{});
-    step(IntC<5>{});
-    step(IntC<6>{});
-    step(IntC<7>{});
-    wait_vm();
-    // The next chunk's scale words were loaded before the direct loads above; their first use is
-    // pinned here, after the wait. Otherwise the compiler places its own wait for them among this
-    // chunk's MFMAs, and because the hardware counter retires in order, that wait also waits for
-    // the direct loads of the next chunk.
+    }
+    __builtin_amdgcn_sched_barrier(0);  // the stage's MFMAs are issued before the next wait
+  };
+
+  for (int c = 0; c < nchunks; ++c) {
+    // stage 2c and scale(c) have landed (in flight behind them: stage 2c+1, scale(c+1), stage 2c+2)
+    wait_vm_n<9>();
+    stage_barrier();
+    issue_stage(2 * c + 3);  // into the stage every wave finished reading before the barrier
+    uint32_t xsc[2], wsc[4];
+    {
+      const uint32_t* sx = reinterpret_cast<const uint32_t*>(lds_sc[c & (kStages - 1)]);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) asm volatile("" : "+v"(xsn[i]));
+      for (int i = 0; i < 2; ++i) xsc[i] = sx[p.x_row_shift ? 2 * tq + i : 64 * tq + 32 * i + r];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(wsn[j]));
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 2; ++i) xsc[i] = xsn[i];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) wsc[j] = wsn[j];
+      for (int j = 0; j < 4; ++j) wsc[j] = sx[256 + 128 * cq + 32 * j + r];
+    }
+    stage_mfma(IntC<0>{}, 2 * c, xsc, wsc);
+    // stage 2c+1 has landed (behind it: scale(c+1), stage 2c+2, stage 2c+3)
+    wait_vm_n<9>();
+    stage_barrier();
+    issue_scales(c + 2);
+    issue_stage(2 * c + 4);
+    stage_mfma(IntC<1>{}, 2 * c + 1, xsc, wsc);
   }
+  // the trailing dummy loads land before the epilogue reuses the ring
+  wait_vm_n<0>();
+  stage_barrier();
 
   // ---- epilogue: one 32 x 32 output block per accumulator ----
   // The payload goes through LDS (the chunk buffers are free after the loop's last barrier): a
