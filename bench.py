@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy first (reference kernel for HBM byte counters)")
+    ap.add_argument("--projection", action="store_true",
+                    help="time the module workload's projection GEMM+quantize producers instead of the attention "
+                         "step (one JSON line of its own)")
     return ap.parse_args()
 
 
@@ -108,11 +111,74 @@ def cpu_baseline(host, cu):
                       f"backward (FP32 dQ), {dt:.1f} s wall"}
 
 
+MODULE_SEED, MODULE_B, MODULE_DIM = 4, 64, 1024
+
+
+def bench_projection(args, torch, mx, synth):
+    """The cross-attention module's projection producers (GEMM + SQ32 quantize with both scale layouts):
+    X [T, 1024] (bf16 N(0,1) quantized SQ32) times W [1024, 1024] (bf16 N(0,0.02) quantized ROW32), for
+    the query side (64 samples x 256 tokens) and the key/value side (64 jagged lengths uniform in
+    [256, 2048]). value = FLOPs of the key/value-side call / its mean time over back-to-back calls (HIP
+    events on the launch stream)."""
+    stream = torch.cuda.current_stream()
+    C = MODULE_DIM
+    w_host = synth.normal_bf16(MODULE_SEED, synth.STREAM_WEIGHT, (C, C), std=0.02)
+    w_dev = torch.from_numpy(w_host.view(np.int16)).view(torch.bfloat16).cuda()
+    wd, ws, _ = mx.quantize(w_dev, np.array([0, C], np.int32), torch.tensor([0, C], dtype=torch.int32, device="cuda"),
+                            mx.ROW32)
+    wop = mx.MxOperand(wd, ws, mx.ROW32)
+    res = {}
+    for side, lens in (("q", [256] * MODULE_B), ("kv", [int(v) for v in synth.lengths(MODULE_SEED, MODULE_B, 256, 2048)])):
+        cu = synth.cu_seqlens(lens)
+        T = int(cu[-1])
+        cu_d = torch.from_numpy(cu).cuda()
+        x_host = synth.normal_bf16(MODULE_SEED, synth.STREAM_ACT, (T, C))
+        x_dev = torch.from_numpy(x_host.view(np.int16)).view(torch.bfloat16).cuda()
+        xd, xs, _ = mx.quantize(x_dev, cu, cu_d, mx.SQ32)
+        xop = mx.MxOperand(xd, xs, mx.SQ32)
+        nb = xs.shape[0]
+        d = torch.empty((T, C), dtype=torch.uint8, device="cuda")
+        sc = torch.empty((nb, C // 32), dtype=torch.uint8, device="cuda")
+        sct = torch.empty((C // 32, nb), dtype=torch.uint8, device="cuda")
+
+        def call():
+            mx.mxfa_linear_quantize(xop, wop, T, C, C, cu_d, len(lens), max(lens), d, sc, sct, stream)
+        for _ in range(args.warmup):
+            call()
+        torch.cuda.synchronize()
+        # the calls back to back between one pair of events: per-call event pairs would add their own
+        # gaps to a kernel of a few tens of microseconds
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3 / args.steps
+        flops = 2.0 * T * C * C
+        res[side] = {"T": T, "us": round(t * 1e6, 2), "pflops": round(flops / t / 1e15, 4),
+                     "frac_peak": round(flops / t / PEAK_MXFP8, 4)}
+        print(f"# projection {side}: T={T} {t * 1e6:.1f} us, {flops / t / 1e15:.3f} PF/s", file=sys.stderr, flush=True)
+    kv = res["kv"]
+    out = {
+        "metric": "MXFP8 projection GEMM+quantize PF/s and % of MI355X dense MXFP8 MFMA peak",
+        "value": kv["pflops"], "unit": "PF/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(kv["us"] / 1e3, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "mxfp8_e4m3 (fp32 accumulate)", "data": "synthetic",
+        "config": {"workload": "cross-attention module projection producers, model dim 1024 -> 1024",
+                   "kv_side": res["kv"], "q_side": res["q"]},
+        "roofline": {"bound": "mfma", "achieved": round(kv["pflops"] * 1e3, 2), "peak": PEAK_MXFP8 / 1e12,
+                     "unit": "TFLOP/s", "frac": kv["frac_peak"], "traffic": None,
+                     "kernel": "linear_quantize_kernel", "launch_us": kv["us"]},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); the per-GPU shard is the "
-              "single-GPU kernel at its real shape, see DESIGN.md for how the path would shard", file=sys.stderr)
+        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); each GPU's shard of a larger "
+              "job is this single-GPU workload at its real shape", file=sys.stderr)
         sys.exit(2)
     import torch
     import precision_mxfp8_block_amd as mx
@@ -127,6 +193,9 @@ def main():
         torch.cuda.synchronize()
         print("# copy calibration: 536870912 bytes read and written by one copy kernel", file=sys.stderr, flush=True)
         del src, dst
+    if args.projection:
+        bench_projection(args, torch, mx, synth)
+        return
     host, dev, cu, cu_d = make_inputs(torch, synth)
     T, C = B * N, H * D
     c = float(np.float32(1 / math.sqrt(D)))
