@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy first (reference kernel for HBM byte counters)")
+    ap.add_argument("--producers", action="store_true",
+                    help="time the fused RMSNorm+quantize producer at the module workload's shapes and the jagged "
+                         "scale scatter instead of the attention step (one JSON line of its own)")
     ap.add_argument("--projection", action="store_true",
                     help="time the module workload's projection GEMM+quantize producers instead of the attention "
                          "step (one JSON line of its own)")
@@ -174,6 +177,89 @@ def bench_projection(args, torch, mx, synth):
     print(json.dumps(out), flush=True)
 
 
+def _time_back_to_back(torch, stream, call, warmup, steps):
+    """Mean time of one call over `steps` calls issued back to back between one pair of HIP events on the
+    launch stream (per-call event pairs would add their own gaps to kernels of a few microseconds)."""
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / steps
+
+
+def bench_producers(args, torch, mx, synth):
+    """HBM-bound producers of the path, each against the 8 TB/s HBM peak:
+    * fused RMSNorm + SQ32 quantize with both scale layouts at the cross-attention module's shapes
+      (model dim 1024; query side 64 x 256 tokens, key/value side 64 jagged lengths uniform in
+      [256, 2048]); algorithmic bytes per element: 2 read (bf16) + 1 written (E4M3) + 2/1024 (the scale
+      grid twice), plus gamma;
+    * the jagged scale scatter at the 32-sequence self-attention shapes (lengths uniform in [128, 4096],
+      16 heads x 128 = 2048 columns) for the ROW32, COL32 and SQ32 scale layouts; algorithmic bytes:
+      the compact scale bytes read plus the padded scale bytes written.
+    value = the key/value-side RMSNorm+quantize GB/s."""
+    stream = torch.cuda.current_stream()
+    C = MODULE_DIM
+    gamma = torch.ones(C, dtype=torch.float32, device="cuda")
+    res = {}
+    for side, lens in (("q", [256] * MODULE_B), ("kv", [int(v) for v in synth.lengths(MODULE_SEED, MODULE_B, 256, 2048)])):
+        cu = synth.cu_seqlens(lens)
+        T = int(cu[-1])
+        cu_d = torch.from_numpy(cu).cuda()
+        x_host = synth.normal_bf16(MODULE_SEED, synth.STREAM_ACT, (T, C))
+        x = torch.from_numpy(x_host.view(np.int16)).view(torch.bfloat16).cuda()
+        nb = sum((L + 31) // 32 for L in lens)
+        d = torch.empty((T, C), dtype=torch.uint8, device="cuda")
+        sc = torch.empty((nb, C // 32), dtype=torch.uint8, device="cuda")
+        sct = torch.empty((C // 32, nb), dtype=torch.uint8, device="cuda")
+
+        def call():
+            mx.mxfa_rmsnorm_quantize(x, C, T, C, gamma, 1e-6, cu_d, len(lens), max(lens), d, sc, sct, stream)
+        t = _time_back_to_back(torch, stream, call, args.warmup, args.steps)
+        nbytes = T * C * 3 + 2 * nb * (C // 32) + 4 * C
+        res["rmsnorm_quantize_" + side] = {"T": T, "us": round(t * 1e6, 2), "gbps": round(nbytes / t / 1e9, 1),
+                                           "frac_hbm": round(nbytes / t / PEAK_HBM, 4)}
+        print(f"# rmsnorm_quantize {side}: T={T} {t * 1e6:.1f} us, {nbytes / t / 1e9:.0f} GB/s", file=sys.stderr,
+              flush=True)
+    lens = [int(v) for v in synth.lengths(4, 32, 128, 4096)]
+    cu = synth.cu_seqlens(lens)
+    cu_d = torch.from_numpy(cu).cuda()
+    T, Cj = int(cu[-1]), 16 * D
+    nb = sum((L + 31) // 32 for L in lens)
+    padded = sum((L + 127) // 128 * 128 for L in lens)
+    for name, mode, rows, prow, width in (("row32", mx.ROW32, T, padded, Cj // 32),
+                                          ("col32", mx.COL32, nb, padded // 32, Cj),
+                                          ("sq32", mx.SQ32, nb, padded // 32, Cj // 32)):
+        compact = torch.randint(0, 255, (rows, width), dtype=torch.uint8, device="cuda")
+        out = torch.empty((prow, width), dtype=torch.uint8, device="cuda")
+
+        def call():
+            mx.mxfa_varlen_scale_scatter(compact, cu_d, len(lens), max(lens), Cj, mode, out, prow, stream)
+        t = _time_back_to_back(torch, stream, call, args.warmup, args.steps)
+        nbytes = rows * width + prow * width
+        res["scale_scatter_" + name] = {"bytes": nbytes, "us": round(t * 1e6, 2), "gbps": round(nbytes / t / 1e9, 1),
+                                        "frac_hbm": round(nbytes / t / PEAK_HBM, 4)}
+        print(f"# scale_scatter {name}: {nbytes} B {t * 1e6:.1f} us, {nbytes / t / 1e9:.0f} GB/s", file=sys.stderr,
+              flush=True)
+    kv = res["rmsnorm_quantize_kv"]
+    out = {
+        "metric": "MXFP8 fused RMSNorm+quantize producer GB/s and % of MI355X HBM peak",
+        "value": kv["gbps"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(kv["us"] / 1e3, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 -> mxfp8_e4m3", "data": "synthetic",
+        "config": {"workload": "cross-attention module RMSNorm+quantize (model dim 1024) and jagged scale scatter "
+                               "(32 sequences, 16 heads)", **res},
+        "roofline": {"bound": "hbm", "achieved": kv["gbps"], "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                     "frac": kv["frac_hbm"], "traffic": None, "kernel": "rmsnorm_quantize_kernel",
+                     "launch_us": kv["us"]},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -195,6 +281,9 @@ def main():
         del src, dst
     if args.projection:
         bench_projection(args, torch, mx, synth)
+        return
+    if args.producers:
+        bench_producers(args, torch, mx, synth)
         return
     host, dev, cu, cu_d = make_inputs(torch, synth)
     T, C = B * N, H * D

@@ -65,20 +65,58 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
   return x * per + (x < rem ? x : rem) + slot;
 }
 
-// Issue the asynchronous global -> LDS copy of one 128 x 128-byte tile into a swizzled LDS tile.
-// `base` is the wave-uniform address of the tile's first row (this head's columns); each wave
-// writes four contiguous 1 KB pieces (64 lanes x 16 bytes), and the swizzle is applied by choosing
-// which logical chunk each lane fetches: lane piece c covers row trow[c], logical chunk offset
-// tcol[c]. Rows past the end of the sequence fetch the last valid row instead (finite data; the
-// scores of those rows are masked and their P is exactly 0).
-__device__ __forceinline__ void issue_tile_load(uint8_t* lds_tile, const uint8_t* base, int valid, int C,
-                                                const int* trow, const int* tcol, const uint32_t* toff,
-                                                int wave_s) {
+template <int V>
+struct Stage {
+  static constexpr int value = V;
+};
+
+// LDS image of one workgroup: two stages x (K tile, V tile), then per stage the tile's K scale words
+// (one per key row) and V scale bytes (4 key blocks x 128 columns).
+constexpr int kLdsTiles = 2 * 2 * kTile * kD;
+constexpr int kLdsKsc = kLdsTiles;               // 2 x 128 words
+constexpr int kLdsVsc = kLdsKsc + 2 * kTile * 4; // 2 x 512 bytes
+constexpr int kLdsBytes = kLdsVsc + 2 * kTile * 4;
+constexpr int lds_k_off(int st) { return (2 * st) * kTile * kD; }
+constexpr int lds_v_off(int st) { return (2 * st + 1) * kTile * kD; }
+
+// Direct global -> LDS copies whose LDS destination is a per-wave base register plus a compile-time
+// offset, added straight into M0 (so no per-destination scalar register stays live across the loop).
+// dma16_at: lane l's 16 bytes at base + voff land at wave_lds + IMM + 16 l. dma4_at: lane l's word
+// at addr lands at wave_lds + IMM + 4 l. The caller waits (s_waitcnt vmcnt) before reading them.
+template <int IMM>
+__device__ __forceinline__ void dma16_at(uint32_t wave_lds, const void* base, uint32_t voff) {
+  asm volatile("s_add_u32 m0, %0, %3\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(wave_lds), "v"(voff), "s"(base),
+               "i"(IMM)
+               : "memory", "scc");
+}
+template <int IMM>
+__device__ __forceinline__ void dma4_at(uint32_t wave_lds, const void* addr) {
+  asm volatile("s_add_u32 m0, %0, %2\n\tglobal_load_lds_dword %1, off" ::"s"(wave_lds), "v"(addr), "i"(IMM)
+               : "memory", "scc");
+}
+
+// Issue the asynchronous global -> LDS copy of one 128 x 128-byte tile into a swizzled LDS tile at
+// byte offset TILE of the workgroup's LDS image. `base` is the wave-uniform address of the tile's
+// first row (this head's columns); each wave writes four contiguous 1 KB pieces (64 lanes x 16
+// bytes) starting at wave_lds = 4 KB x wave, and the swizzle is applied by choosing which logical
+// chunk each lane fetches: lane piece c covers row trow[c], logical chunk offset tcol[c] (byte
+// offset toff[c] in a full tile). Rows past the end of the sequence fetch the last valid row
+// instead (finite data; the scores of those rows are masked and their P is exactly 0).
+template <int TILE>
+__device__ __forceinline__ void issue_tile_load(uint32_t wave_lds, const uint8_t* base, int valid, int C,
+                                                const int* trow, const int* tcol, const uint32_t* toff) {
+  uint32_t off[4];
+  if (valid >= kTile) {
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const uint32_t off = valid >= kTile ? toff[c] : (uint32_t)(min(trow[c], valid - 1) * C + tcol[c]);
-    mx_lds_dma16((MX_LDS void*)(lds_tile + (wave_s * 4 + c) * 1024), base, off);
+    for (int c = 0; c < 4; ++c) off[c] = toff[c];
+  } else {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) off[c] = (uint32_t)(min(trow[c], valid - 1) * C + tcol[c]);
   }
+  dma16_at<TILE + 0>(wave_lds, base, off[0]);
+  dma16_at<TILE + 1024>(wave_lds, base, off[1]);
+  dma16_at<TILE + 2048>(wave_lds, base, off[2]);
+  dma16_at<TILE + 3072>(wave_lds, base, off[3]);
 }
 
 // The direct LDS loads are inline asm (mx_lds_dma16/4): the compiler would otherwise wait for every
@@ -86,13 +124,23 @@ __device__ __forceinline__ void issue_tile_load(uint8_t* lds_tile, const uint8_t
 // tile right after issuing it. Their waits are asm as well.
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Two floats -> two E4M3 bytes in the low or high half of a word whose other half is kept.
+template <bool HI>
+__device__ __forceinline__ uint32_t cvt2(float a, float b, uint32_t old) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, HI);
+}
+// A register with unspecified contents (no instruction): the first conversion into a word starts
+// from it, and the second overwrites the other half, so no zeroing move is needed.
+__device__ __forceinline__ uint32_t undef_word() {
+  uint32_t u;
+  asm volatile("; unspecified %0" : "=v"(u));
+  return u;
+}
+
+template <bool VCOL32>
 __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
-  // two stages x (K tile, V tile)
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2][2][kTile * kD];
-  // the tile's K scale words (one per key row) and V scale bytes (4 key blocks x 128 columns), copied
-  // with the tile
-  __shared__ __attribute__((aligned(512))) uint32_t lds_ksc[2][kTile];
-  __shared__ __attribute__((aligned(512))) uint32_t lds_vsc[2][kTile];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[kLdsBytes];
+  MX_LDS uint8_t* const lds = (MX_LDS uint8_t*)lds_raw;
 
   const int item = xcd_remap((int)blockIdx.x, p.total_items);
   const int qt = p.n_qtiles - 1 - item % p.n_qtiles;  // heavy (late) query tiles first
@@ -128,9 +176,13 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
   }
   const uint8_t* kbase = (const uint8_t*)mx_uniform_ptr((void*)(p.k + k_start * (int64_t)C + h * kD));
   const uint8_t* vbase = (const uint8_t*)mx_uniform_ptr((void*)(p.v + k_start * (int64_t)C + h * kD));
+  // LDS byte address of this wave's pieces of a tile, and of its part of the scale areas
+  const uint32_t lds_addr = (uint32_t)(uintptr_t)lds;
+  const uint32_t wave_lds = lds_addr + (uint32_t)wave_s * 4096u;
+  const uint32_t scale_lds = lds_addr + 256u * (uint32_t)(wave_s & 1) + (wave_s < 2 ? kLdsKsc : kLdsVsc);
   if (n_ktiles > 0) {
-    issue_tile_load(lds[0][0], kbase, Lk, C, trow, tcol, toff, wave_s);
-    issue_tile_load(lds[0][1], vbase, Lk, C, trow, tcol, toff, wave_s);
+    issue_tile_load<lds_k_off(0)>(wave_lds, kbase, Lk, C, trow, tcol, toff);
+    issue_tile_load<lds_v_off(0)>(wave_lds, vbase, Lk, C, trow, tcol, toff);
   }
 
   // ---- Q tile rows of this wave, held as the B operand of S^T = K Q^T ----
@@ -154,27 +206,27 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
       *reinterpret_cast<const uint32_t*>(p.q_scale + ((qoff.padded + qrow) >> p.q_row_shift) * (int64_t)Cs + h * 4) >>
       (8 * hh);
 
-  // K and V scales of a key tile, copied into LDS with the tile: word l of lds_ksc is the K scale
-  // word (4 d-blocks) of key row kv0 + l (ROW32) or of its 32-row block (SQ32); lds_vsc holds, for
-  // key block vb = 0..3, the 128 V scale bytes of this head's columns (COL32) or its 4 d-block
-  // bytes (SQ32) at byte offset 128 vb. Waves 0-1 copy K, waves 2-3 copy V (64 words each).
+  // K and V scales of a key tile, copied into LDS with the tile: word l of the K scale area is the K
+  // scale word (4 d-blocks) of key row kv0 + l (ROW32) or of its 32-row block (SQ32); the V scale
+  // area holds, for key block vb = 0..3, the 128 V scale bytes of this head's columns (COL32) or its
+  // 4 d-block bytes (SQ32) at byte offset 128 vb. Waves 0-1 copy K, waves 2-3 copy V (64 words each).
   const uint8_t* ksbase = p.k_scale + (koff.padded >> p.k_row_shift) * (int64_t)Cs + h * 4;
-  const uint8_t* vsbase = p.v_scale + (koff.padded >> 5) * (int64_t)(C >> p.v_col_shift);
-  const int vcs = C >> p.v_col_shift;
-  auto issue_scale_load = [&](int kv0, int st) {
+  const uint8_t* vsbase = p.v_scale + (koff.padded >> 5) * (int64_t)(VCOL32 ? C : Cs);
+  constexpr int vcs_shift = VCOL32 ? 0 : 5;
+  auto issue_scale_load = [&](int kv0, auto stc) {
+    constexpr int st = decltype(stc)::value;
     const int l = 64 * (wave_s & 1) + lane;  // word index 0..127
+    const uint8_t* src;
     if (wave_s < 2) {
-      const uint8_t* src = ksbase + (int64_t)(((kv0 + l) >> p.k_row_shift) * Cs);
-      mx_lds_dma4_addr((MX_LDS void*)&lds_ksc[st][64 * wave_s], src);
+      src = ksbase + (int64_t)(((kv0 + l) >> p.k_row_shift) * Cs);
     } else {
       const int vb = l >> 5;
-      const int col = p.v_col_shift ? h * 4 : h * kD + 4 * (l & 31);
-      const uint8_t* src = vsbase + (int64_t)(((kv0 >> 5) + vb) * vcs + col);
-      mx_lds_dma4_addr((MX_LDS void*)&lds_vsc[st][64 * (wave_s & 1)], src);
+      const int col = VCOL32 ? h * kD + 4 * (l & 31) : h * 4;
+      src = vsbase + (int64_t)(((kv0 >> 5) + vb) * (C >> vcs_shift) + col);
     }
+    dma4_at<st * 512>(scale_lds, src);
   };
-  if (n_ktiles > 0) issue_scale_load(0, 0);
-  uint32_t ksc[4], vsc[8];
+  if (n_ktiles > 0) issue_scale_load(0, Stage<0>{});
 
   float m = -INFINITY;  // running max of raw scores for query row qrow
   float lsum = 0.0f;    // this lane's half of the row sum of P * 256
@@ -182,53 +234,72 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) oacc[i] = mx_v16f{};
 
-  // per-lane constants of the transposed V read (see the lane map in mx_device.h)
-  const int grp = lane >> 4, gl = lane & 15;
-  const int tb = gl >> 1, ts = gl & 1;
-  const int tr_row = 8 * (tb >> 2) + 4 * (grp >> 1) + (tb & 3);  // + 64 ks + 32 (c >> 1) + 16 (c & 1)
-  const int tr_col = 16 * (grp & 1) + 8 * ts;                    // + 32 dblk
-  const int tr_swz = swz(tr_row);
+  // Per-lane LDS byte offsets that do not change from tile to tile (the stage and the key/row
+  // block are compile-time offsets added to them):
+  //  * K rows: row 32 kb + r, d-step ds, half (lo: chunk 4 ds + hh, hi: chunk 4 ds + 2 + hh), swizzled
+  //    by swz(r) (adding 32 kb leaves the swizzle unchanged);
+  //  * V^T reads (see the lane map in mx_device.h): row tr_row (+ 64 ks + 32 (cc >> 1) + 16 (cc & 1),
+  //    which leave the swizzle unchanged), column 32 db + tr_col;
+  //  * scales: K scale word 32 kb + r; V scale byte 128 (2 ks + hh) + (COL32: 32 db + r, SQ32: db).
+  uint32_t koffs[2][2];
+  {
+    const int sw = swz(r);
+#pragma unroll
+    for (int ds = 0; ds < 2; ++ds) {
+      koffs[ds][0] = (uint32_t)(r * kD + 16 * ((4 * ds + hh) ^ sw));
+      koffs[ds][1] = (uint32_t)(r * kD + 16 * ((4 * ds + 2 + hh) ^ sw));
+    }
+  }
+  uint32_t voffs[4];
+  {
+    const int grp = lane >> 4, gl = lane & 15;
+    const int tb = gl >> 1, ts = gl & 1;
+    const int tr_row = 8 * (tb >> 2) + 4 * (grp >> 1) + (tb & 3);
+    const int tr_col = 16 * (grp & 1) + 8 * ts;
+    const int tr_swz = swz(tr_row);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int col = 32 * db + tr_col;
+      voffs[db] = (uint32_t)(tr_row * kD + 16 * ((col >> 4) ^ tr_swz) + (col & 15));
+    }
+  }
+  const uint32_t ksc_off = (uint32_t)(kLdsKsc + 4 * r);
+  const uint32_t vsc_off = (uint32_t)(kLdsVsc + 128 * hh + (VCOL32 ? r : 0));
 
   wait_vm();
   __syncthreads();
 
-  for (int kt = 0; kt < n_ktiles; ++kt) {
+  auto step = [&](int kt, auto stc) {
+    constexpr int st = decltype(stc)::value;
     const int kv0 = kt * kTile;
-    const int st = kt & 1;
-    const uint8_t* lds_k = lds[st][0];
-    const uint8_t* lds_v = lds[st][1];
     // this tile's scales (landed with the tile)
+    uint32_t ksc[4], vsc[8];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) ksc[kb] = lds_ksc[st][32 * kb + r];
-    {
-      const uint8_t* vb8 = reinterpret_cast<const uint8_t*>(lds_vsc[st]);
+    for (int kb = 0; kb < 4; ++kb) ksc[kb] = *(const MX_LDS uint32_t*)(lds + ksc_off + st * 512 + 128 * kb);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
-          vsc[ks * 4 + db] = vb8[128 * (2 * ks + hh) + (p.v_col_shift ? db : 32 * db + r)];
-    }
+      for (int db = 0; db < 4; ++db)
+        vsc[ks * 4 + db] = lds[vsc_off + st * 512 + 256 * ks + (VCOL32 ? 32 * db : db)];
     // prefetch the next tile (data and scales straight into the other LDS stage)
     if (kt + 1 < n_ktiles) {
       const int64_t next = (int64_t)(kv0 + kTile) * C;
-      issue_tile_load(lds[st ^ 1][0], kbase + next, Lk - kv0 - kTile, C, trow, tcol, toff, wave_s);
-      issue_tile_load(lds[st ^ 1][1], vbase + next, Lk - kv0 - kTile, C, trow, tcol, toff, wave_s);
-      issue_scale_load(kv0 + kTile, st ^ 1);
+      issue_tile_load<lds_k_off(st ^ 1)>(wave_lds, kbase + next, Lk - kv0 - kTile, C, trow, tcol, toff);
+      issue_tile_load<lds_v_off(st ^ 1)>(wave_lds, vbase + next, Lk - kv0 - kTile, C, trow, tcol, toff);
+      issue_scale_load(kv0 + kTile, Stage<st ^ 1>{});
     }
 
     // ---- S^T = K Q^T : 4 key blocks of 32 x 2 D-steps of 64 ----
     mx_v16f sacc[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      const int row = 32 * kb + r;
       sacc[kb] = mx_v16f{};
-      const uint8_t* krow = lds_k + row * kD;
-      const int sw = swz(row);
 #pragma unroll
       for (int ds = 0; ds < 2; ++ds) {
-        uint4 lo = *reinterpret_cast<const uint4*>(krow + 16 * ((4 * ds + hh) ^ sw));
-        uint4 hi = *reinterpret_cast<const uint4*>(krow + 16 * ((4 * ds + 2 + hh) ^ sw));
-        mx_v8i ka{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        const MX_LDS uint8_t* t = lds + lds_k_off(st) + 32 * kb * kD;
+        const mx_v4i lo = *(const MX_LDS mx_v4i*)(t + koffs[ds][0]);
+        const mx_v4i hi = *(const MX_LDS mx_v4i*)(t + koffs[ds][1]);
+        mx_v8i ka{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
         const uint32_t kscb = ksc[kb] >> (8 * hh);
         if (ds == 0)
           sacc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qa[0], sacc[kb], 0, 0, 0, (int)kscb, 0,
@@ -244,26 +315,32 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
     // ---- mask (ragged tail, causal diagonal) ----
     const bool need_mask = (kv0 + kTile > Lk) || (p.causal && kv0 + kTile - 1 > qt * kTile + wave * 32);
     if (need_mask) {
+      // key kv0 + 32 kb + 8 (v >> 2) + 4 hh + (v & 3) is masked when its offset in the tile reaches
+      // lim + 4 hh: past the sequence end, or (causal) past this lane's query row
+      const int lim = min(Lk - kv0, p.causal ? qrow - kv0 + 1 : kTile) - 4 * hh;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int kvpos = kv0 + 32 * kb + 8 * (v >> 2) + 4 * hh + (v & 3);
-          if (kvpos >= Lk || (p.causal && kvpos > qrow)) sacc[kb][v] = -INFINITY;
-        }
+        for (int v = 0; v < 16; ++v)
+          if (32 * kb + 8 * (v >> 2) + (v & 3) >= lim) sacc[kb][v] = -INFINITY;
     }
 
     // ---- online softmax (FP32) ----
-    float mx = -INFINITY;
+    // two independent max chains (one per pair of key blocks), joined at the end
+    float mx0 = m, mx1 = m;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int v = 0; v < 16; v += 2) mx = max3f(mx, sacc[kb][v], sacc[kb][v + 1]);
+      for (int v = 0; v < 16; v += 2) {
+        mx0 = max3f(mx0, sacc[kb][v], sacc[kb][v + 1]);
+        mx1 = max3f(mx1, sacc[kb + 2][v], sacc[kb + 2][v + 1]);
+      }
+    float m_new;
     {
+      const float mx = fmaxf(mx0, mx1);
       auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = fmaxf(__uint_as_float(sw2[0]), __uint_as_float(sw2[1]));
+      m_new = fmaxf(__uint_as_float(sw2[0]), __uint_as_float(sw2[1]));
     }
-    const float m_new = fmaxf(m, mx);
     const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
     const float base = m_use * p.c2 - 8.0f;  // exp2(S c2 - base) = 256 P
     // O and l need rescaling only where the row max moved; skip the multiplies when no row of the
@@ -283,14 +360,16 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float e0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][4 * i + 0], p.c2, -base));
-        float e1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][4 * i + 1], p.c2, -base));
-        float e2 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][4 * i + 2], p.c2, -base));
-        float e3 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][4 * i + 3], p.c2, -base));
+        const float e0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][4 * i + 0], p.c2, -base));
+        const float e1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][4 * i + 1], p.c2, -base));
+        const float e2 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][4 * i + 2], p.c2, -base));
+        const float e3 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][4 * i + 3], p.c2, -base));
         ps += (e0 + e1) + (e2 + e3);
-        pk[kb][i] = mx_pack4_inrange(e0, e1, e2, e3);
+        // all four lie in [0, 256]: no clamp needed before the conversion
+        pk[kb][i] = cvt2<true>(e2, e3, cvt2<false>(e0, e1, undef_word()));
       }
     lsum += ps;
+    asm volatile("" : "+v"(lsum));  // keep the row sum here (not sunk past the PV products)
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- O^T += V^T P^T : 2 key steps of 64 x 4 D-blocks of 32 ----
@@ -307,10 +386,8 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
         mx_v2i part[4];
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) {
-          const int row = 64 * ks + 32 * (cc >> 1) + 16 * (cc & 1) + tr_row;
-          const int col = 32 * db + tr_col;
-          const int off = row * kD + 16 * ((col >> 4) ^ tr_swz) + (col & 15);
-          part[cc] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((MX_LDS mx_v2i*)(lds_v + off));
+          const int rowoff = (64 * ks + 32 * (cc >> 1) + 16 * (cc & 1)) * kD;
+          part[cc] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((MX_LDS mx_v2i*)(lds + lds_v_off(st) + rowoff + voffs[db]));
         }
         return mx_v8i{part[0].x, part[0].y, part[1].x, part[1].y, part[2].x, part[2].y, part[3].x, part[3].y};
       };
@@ -328,6 +405,12 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
 
     wait_vm();        // this thread's part of the next tile has landed in LDS
     __syncthreads();  // ... everyone's, and nobody still reads the stage the next prefetch overwrites
+  };
+
+  // two tiles per iteration so that each stage's LDS addresses are compile-time offsets
+  for (int kt = 0; kt < n_ktiles; kt += 2) {
+    step(kt, Stage<0>{});
+    if (kt + 1 < n_ktiles) step(kt + 1, Stage<1>{});
   }
 
   // ---- epilogue: O / l -> bf16, LSE ----
@@ -372,7 +455,10 @@ hipError_t launch_attn_fwd(const AttnProblem& a, uint16_t* o, float* lse, hipStr
   p.causal = a.causal;
   p.o = o; p.lse = lse; p.Tq = a.total_q;
   if (p.total_items == 0) return hipSuccess;
-  hipLaunchKernelGGL(attn_fwd_kernel, dim3((unsigned)p.total_items), dim3(256), 0, stream, p);
+  if (p.v_col_shift == 0)
+    hipLaunchKernelGGL(attn_fwd_kernel<true>, dim3((unsigned)p.total_items), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(attn_fwd_kernel<false>, dim3((unsigned)p.total_items), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
