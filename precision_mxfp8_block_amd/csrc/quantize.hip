@@ -199,13 +199,28 @@ __global__ void __launch_bounds__(256) scale_scatter_kernel(const uint8_t* __res
   const int64_t valid_rows = (L + unit - 1) / unit;      // rows of this sequence in the compact tensor
   const int64_t src_row0 = (mode == 0) ? (int64_t)cu[s] : off.blocks32;
   const int64_t dst_row0 = off.padded / unit;
-  const int64_t nbytes = (int64_t)rows_per_group * width;
-  for (int64_t i = threadIdx.x; i < nbytes; i += blockDim.x) {
-    const int64_t rr = (int64_t)g * rows_per_group + i / width;  // row inside the sequence
-    const int64_t col = i % width;
-    uint8_t v = 0;
-    if (rr < valid_rows) v = compact[(src_row0 + rr) * width + col];
-    if (dst_row0 + rr < padded_rows) padded[(dst_row0 + rr) * width + col] = v;  // never past the buffer
+  const int64_t grow0 = (int64_t)g * rows_per_group;     // first row of this group inside the sequence
+  // rows of the group that hold data, and rows that exist in the padded buffer
+  const int nvalid = (int)max<int64_t>(0, min<int64_t>(rows_per_group, valid_rows - grow0));
+  const int nrows = (int)max<int64_t>(0, min<int64_t>(rows_per_group, padded_rows - dst_row0 - grow0));
+  const uint8_t* src = compact + (src_row0 + grow0) * width;
+  uint8_t* dst = padded + (dst_row0 + grow0) * width;
+  if ((width & 15) == 0) {
+    // 16-byte pieces (the row width and both row starts are multiples of 16 bytes)
+    const int wv = width >> 4;
+    const int n = nrows * wv;
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+      const int rr = i / wv;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (rr < nvalid) v = reinterpret_cast<const uint4*>(src)[i];
+      reinterpret_cast<uint4*>(dst)[i] = v;
+    }
+  } else {
+    const int n = nrows * width;
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+      const int rr = i / width;
+      dst[i] = rr < nvalid ? src[i] : (uint8_t)0;
+    }
   }
 }
 
@@ -306,6 +321,125 @@ __global__ void __launch_bounds__(256) rmsnorm_quantize_kernel(const uint16_t* _
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Fused RMSNorm + SQ32 quantize for C = 512 SEGS (SEGS = 1..4) with the 32 x C tile held in
+// registers: one read of the input, one write of the payload. Workgroup = 8 waves per (sequence,
+// 32-token block); wave w owns rows 4w..4w+3, lane l columns 512 j + 8 l .. + 7 of segment j
+// (16-byte loads and 8-byte stores cover whole 1 KB / 512 B row segments per instruction).
+// Per row: sum of squares in FP64 (exact bf16 squares), lane sum by butterfly, one rounding to
+// fp32; r = 1 / sqrtf(ss / C + eps). y = (x r) gamma; the maximum |y| of each 32 x 32 block is
+// taken over the lane's 4 rows x 8 columns, the 4 lanes of the block (DPP) and the 8 waves (LDS).
+// Rows past the sequence end re-read the block's last row (no branch on the loads; a repeated
+// row leaves every block maximum unchanged) and are not stored.
+// ---------------------------------------------------------------------------------------------
+template <int SEGS>
+__global__ void __launch_bounds__(512) rmsnorm_quantize_regs_kernel(const uint16_t* __restrict__ x, int64_t ld_x,
+                                                                    const float* __restrict__ gamma, float eps,
+                                                                    const int32_t* __restrict__ cu, int nseq,
+                                                                    uint8_t* __restrict__ data,
+                                                                    uint8_t* __restrict__ scale,
+                                                                    uint8_t* __restrict__ scale_t) {
+  constexpr int C = 512 * SEGS;
+  constexpr int NCB = C / 32;
+  __shared__ uint32_t bm[8][NCB];
+  const int s = blockIdx.y, b = blockIdx.x;
+  const int64_t t0 = cu[s], L = (int64_t)cu[s + 1] - t0;
+  if ((int64_t)b * 32 >= L) return;  // uniform over the workgroup
+  const SeqOffsets off = seq_offsets(cu, s);
+  int64_t nb_total = 0;
+  if (scale_t) nb_total = seq_offsets(cu, nseq).blocks32;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int rows = (int)min<int64_t>(32, L - (int64_t)b * 32);
+  const int64_t tb = t0 + (int64_t)b * 32;
+
+  uint4 v[4][SEGS];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rr = min(4 * wave + i, rows - 1);
+#pragma unroll
+    for (int j = 0; j < SEGS; ++j)
+      v[i][j] = *reinterpret_cast<const uint4*>(x + (tb + rr) * ld_x + 512 * j + 8 * lane);
+  }
+  float g[SEGS][8];
+#pragma unroll
+  for (int j = 0; j < SEGS; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) g[j][e] = gamma[512 * j + 8 * lane + e];
+
+  float r[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    double ss = 0.0;
+#pragma unroll
+    for (int j = 0; j < SEGS; ++j) {
+      const uint32_t w[4] = {v[i][j].x, v[i][j].y, v[i][j].z, v[i][j].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float a = bf16_to_f32(w[k] & 0xffffu), c = bf16_to_f32(w[k] >> 16);
+        ss += (double)(a * a) + (double)(c * c);  // squares of bf16 values are exact in fp32
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
+    const float ms = (float)ss / (float)C;
+    r[i] = 1.0f / __fsqrt_rn(ms + eps);
+  }
+
+  auto yval = [&](int i, int j, int e) {
+    const uint32_t w = (e >> 1) == 0 ? v[i][j].x : (e >> 1) == 1 ? v[i][j].y : (e >> 1) == 2 ? v[i][j].z : v[i][j].w;
+    const float xv = bf16_to_f32((e & 1) ? (w >> 16) : (w & 0xffffu));
+    return __fmul_rn(__fmul_rn(xv, r[i]), g[j][e]);
+  };
+  // block maxima (magnitude bit patterns; NaN and Inf order above every finite value)
+#pragma unroll
+  for (int j = 0; j < SEGS; ++j) {
+    uint32_t am = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) am = max(am, __float_as_uint(yval(i, j, e)) & 0x7fffffffu);
+    am = max(am, (uint32_t)__builtin_amdgcn_update_dpp(0u, am, 0xB1, 0xF, 0xF, false));  // lane bit 0
+    am = max(am, (uint32_t)__builtin_amdgcn_update_dpp(0u, am, 0x4E, 0xF, 0xF, false));  // lane bit 1
+    if ((lane & 3) == 0) bm[wave][16 * j + (lane >> 2)] = am;
+  }
+  __syncthreads();
+  uint32_t code[SEGS];
+#pragma unroll
+  for (int j = 0; j < SEGS; ++j) {
+    uint32_t am = 0;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) am = max(am, bm[w][16 * j + (lane >> 2)]);
+    code[j] = mx_code_from_amax_bits(am);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rr = 4 * wave + i;
+    if (rr < rows) {
+#pragma unroll
+      for (int j = 0; j < SEGS; ++j) {
+        uint2 out;
+        if (code[j] == 255u) {
+          out = make_uint2(0x7f7f7f7fu, 0x7f7f7f7fu);
+        } else {
+          const float inv = mx_inv_scale(code[j]);
+          out.x = mx_pack4(yval(i, j, 0) * inv, yval(i, j, 1) * inv, yval(i, j, 2) * inv, yval(i, j, 3) * inv);
+          out.y = mx_pack4(yval(i, j, 4) * inv, yval(i, j, 5) * inv, yval(i, j, 6) * inv, yval(i, j, 7) * inv);
+        }
+        *reinterpret_cast<uint2*>(data + (tb + rr) * C + 512 * j + 8 * lane) = out;
+      }
+    }
+  }
+  if (wave == 0 && (lane & 3) == 0) {
+    const int64_t br = off.blocks32 + b;
+#pragma unroll
+    for (int j = 0; j < SEGS; ++j) {
+      const int cb = 16 * j + (lane >> 2);
+      scale[br * NCB + cb] = (uint8_t)code[j];
+      if (scale_t) scale_t[(int64_t)cb * nb_total + br] = (uint8_t)code[j];
+    }
+  }
+}
+
 }  // namespace
 
 namespace mxfa {
@@ -343,8 +477,27 @@ hipError_t launch_rmsnorm_quantize(const uint16_t* x, int64_t ld_x, int C, const
                                    uint8_t* scale_t, hipStream_t stream) {
   if (max_seqlen == 0) return hipSuccess;
   dim3 grid((unsigned)((max_seqlen + 31) / 32), (unsigned)nseq);
-  hipLaunchKernelGGL(rmsnorm_quantize_kernel, grid, dim3(256), 0, stream, x, ld_x, C, gamma, eps, cu, nseq, data,
-                     scale, scale_t);
+  switch (C) {
+    case 512:
+      hipLaunchKernelGGL(rmsnorm_quantize_regs_kernel<1>, grid, dim3(512), 0, stream, x, ld_x, gamma, eps, cu, nseq,
+                         data, scale, scale_t);
+      break;
+    case 1024:
+      hipLaunchKernelGGL(rmsnorm_quantize_regs_kernel<2>, grid, dim3(512), 0, stream, x, ld_x, gamma, eps, cu, nseq,
+                         data, scale, scale_t);
+      break;
+    case 1536:
+      hipLaunchKernelGGL(rmsnorm_quantize_regs_kernel<3>, grid, dim3(512), 0, stream, x, ld_x, gamma, eps, cu, nseq,
+                         data, scale, scale_t);
+      break;
+    case 2048:
+      hipLaunchKernelGGL(rmsnorm_quantize_regs_kernel<4>, grid, dim3(512), 0, stream, x, ld_x, gamma, eps, cu, nseq,
+                         data, scale, scale_t);
+      break;
+    default:
+      hipLaunchKernelGGL(rmsnorm_quantize_kernel, grid, dim3(256), 0, stream, x, ld_x, C, gamma, eps, cu, nseq, data,
+                         scale, scale_t);
+  }
   return hipGetLastError();
 }
 

@@ -65,12 +65,14 @@ def test_quantize_strided_rows():
     np.testing.assert_array_equal(scale.cpu().numpy(), s_ref)
 
 
+@pytest.mark.parametrize("C", [256, 2048])
 @pytest.mark.parametrize("mode", [oracle.ROW32, oracle.COL32, oracle.SQ32])
-def test_scale_scatter_bit_exact(mode):
+def test_scale_scatter_bit_exact(mode, C):
+    # C = 256: ROW32/SQ32 scale rows of 8 bytes (byte copies); C = 2048: every layout in 16-byte pieces
     lens = [37, 128, 1, 300, 95, 256]
-    say(f"scatter mode={mode}")
+    say(f"scatter mode={mode} C={C}")
     cu = synth.cu_seqlens(lens)
-    T, C = int(cu[-1]), 256
+    T = int(cu[-1])
     x = synth.normal_bf16(5, 1, (T, C))
     _, s_ref, _ = oracle.quantize(x, cu, mode)
     p_ref = oracle.scale_scatter(s_ref, cu, C, mode)
@@ -81,12 +83,29 @@ def test_scale_scatter_bit_exact(mode):
     np.testing.assert_array_equal(padded.cpu().numpy(), p_ref)
 
 
-@pytest.mark.parametrize("lens", [[64], [37, 128, 1, 95]])
-def test_rmsnorm_quantize_bit_exact(lens):
-    say(f"rmsnorm lens={lens}")
+RMSNORM_CASES = [
+    # (lens, C, NaN position or None): C = 512..2048 in steps of 512 take the register-resident
+    # kernel, other multiples of 32 the general one
+    ([64], 1024, None),
+    ([37, 128, 1, 95], 1024, None),
+    ([37, 128, 1, 95], 512, None),
+    ([40, 33], 1536, None),
+    ([37, 1, 70], 2048, None),
+    ([37, 64, 1], 1024, (40, 100)),
+    ([37, 128, 1, 95], 800, None),
+    ([5, 64], 96, (6, 3)),
+]
+
+
+@pytest.mark.parametrize("lens,C,nan_at", RMSNORM_CASES, ids=[f"{c[1]}-{len(c[0])}seq-{'nan' if c[2] else 'fin'}"
+                                                             for c in RMSNORM_CASES])
+def test_rmsnorm_quantize_bit_exact(lens, C, nan_at):
+    say(f"rmsnorm lens={lens} C={C} nan_at={nan_at}")
     cu = synth.cu_seqlens(lens)
-    T, C = int(cu[-1]), 1024
+    T = int(cu[-1])
     x = synth.normal_bf16(6, synth.STREAM_ACT, (T, C))
+    if nan_at is not None:
+        x[nan_at] = 0x7FC0  # a quiet bf16 NaN: its row's blocks get code 255 and payload 0x7F
     gamma = (1.0 + 0.1 * synth.normal(6, synth.STREAM_WEIGHT, C)).astype(np.float32)
     d_ref, s_ref, st_ref, _ = oracle.rmsnorm_quantize(x, gamma, 1e-6, cu)
     data, scale, scale_t = mx.rmsnorm_quantize(to_dev_bf16(x), torch.from_numpy(gamma).cuda(), 1e-6, cu, cu_dev(cu))
