@@ -65,6 +65,17 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
   return x * per + (x < rem ? x : rem) + slot;
 }
 
+// x if off < lim, else -inf. One compare into VCC and one select (inline asm so that the 64 compares
+// of a masked tile do not each occupy a scalar register pair).
+__device__ __forceinline__ float keep_below(float x, int off, int lim, float ninf) {
+  float y;
+  asm("v_cmp_lt_i32_e32 vcc, %2, %3\n\tv_cndmask_b32_e32 %0, %4, %1, vcc"
+      : "=v"(y)
+      : "v"(x), "i"(off), "v"(lim), "v"(ninf)
+      : "vcc");
+  return y;
+}
+
 template <int V>
 struct Stage {
   static constexpr int value = V;
@@ -179,11 +190,6 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
   // LDS byte address of this wave's pieces of a tile, and of its part of the scale areas
   const uint32_t lds_addr = (uint32_t)(uintptr_t)lds;
   const uint32_t wave_lds = lds_addr + (uint32_t)wave_s * 4096u;
-  const uint32_t scale_lds = lds_addr + 256u * (uint32_t)(wave_s & 1) + (wave_s < 2 ? kLdsKsc : kLdsVsc);
-  if (n_ktiles > 0) {
-    issue_tile_load<lds_k_off(0)>(wave_lds, kbase, Lk, C, trow, tcol, toff);
-    issue_tile_load<lds_v_off(0)>(wave_lds, vbase, Lk, C, trow, tcol, toff);
-  }
 
   // ---- Q tile rows of this wave, held as the B operand of S^T = K Q^T ----
   const int qrow = qt * kTile + wave * 32 + r;  // position in the sequence
@@ -206,27 +212,41 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
       *reinterpret_cast<const uint32_t*>(p.q_scale + ((qoff.padded + qrow) >> p.q_row_shift) * (int64_t)Cs + h * 4) >>
       (8 * hh);
 
-  // K and V scales of a key tile, copied into LDS with the tile: word l of the K scale area is the K
-  // scale word (4 d-blocks) of key row kv0 + l (ROW32) or of its 32-row block (SQ32); the V scale
-  // area holds, for key block vb = 0..3, the 128 V scale bytes of this head's columns (COL32) or its
-  // 4 d-block bytes (SQ32) at byte offset 128 vb. Waves 0-1 copy K, waves 2-3 copy V (64 words each).
+  // K and V scales of a key tile, copied into LDS with the tile: word l of a K scale stage is the K
+  // scale word (4 d-blocks) of key row kv0 + l (ROW32) or of its 32-row block (SQ32); a V scale
+  // stage holds, for key block vb = 0..3, the 128 V scale bytes of this head's columns (COL32) or
+  // its 4 d-block bytes (SQ32) at byte offset 128 vb. Waves 0-1 copy K scales, waves 2-3 V scales
+  // (64 words each).
   const uint8_t* ksbase = p.k_scale + (koff.padded >> p.k_row_shift) * (int64_t)Cs + h * 4;
   const uint8_t* vsbase = p.v_scale + (koff.padded >> 5) * (int64_t)(VCOL32 ? C : Cs);
   constexpr int vcs_shift = VCOL32 ? 0 : 5;
-  auto issue_scale_load = [&](int kv0, auto stc) {
+  const uint32_t scale_lds = lds_addr + 256u * (uint32_t)(wave_s & 1);
+  auto issue_kscale_load = [&](int kv0, auto stc) {  // waves 0-1
     constexpr int st = decltype(stc)::value;
-    const int l = 64 * (wave_s & 1) + lane;  // word index 0..127
-    const uint8_t* src;
-    if (wave_s < 2) {
-      src = ksbase + (int64_t)(((kv0 + l) >> p.k_row_shift) * Cs);
-    } else {
-      const int vb = l >> 5;
-      const int col = VCOL32 ? h * kD + 4 * (l & 31) : h * 4;
-      src = vsbase + (int64_t)(((kv0 >> 5) + vb) * (C >> vcs_shift) + col);
-    }
-    dma4_at<st * 512>(scale_lds, src);
+    const int l = 64 * (wave_s & 1) + lane;
+    dma4_at<kLdsKsc + st * 512>(scale_lds, ksbase + (int64_t)(((kv0 + l) >> p.k_row_shift) * Cs));
   };
-  if (n_ktiles > 0) issue_scale_load(0, Stage<0>{});
+  auto issue_vscale_load = [&](int kv0, auto stc) {  // waves 2-3
+    constexpr int st = decltype(stc)::value;
+    const int l = 64 * (wave_s & 1) + lane;
+    const int col = VCOL32 ? h * kD + 4 * (l & 31) : h * 4;
+    dma4_at<kLdsVsc + st * 512>(scale_lds, vsbase + (int64_t)(((kv0 >> 5) + (l >> 5)) * (C >> vcs_shift) + col));
+  };
+  // Prologue loads: K, V and their scales of tile 0 into stage 0, K and its scales of tile 1 into
+  // stage 1. In the loop, the loads issued in the middle of step t bring K of tile t + 2 and V of
+  // tile t + 1 (with their scales): K one step before its scores are computed, V one and a half.
+  if (n_ktiles > 0) {
+    issue_tile_load<lds_k_off(0)>(wave_lds, kbase, Lk, C, trow, tcol, toff);
+    issue_tile_load<lds_v_off(0)>(wave_lds, vbase, Lk, C, trow, tcol, toff);
+    if (wave_s < 2)
+      issue_kscale_load(0, Stage<0>{});
+    else
+      issue_vscale_load(0, Stage<0>{});
+  }
+  if (n_ktiles > 1) {
+    issue_tile_load<lds_k_off(1)>(wave_lds, kbase + (int64_t)kTile * C, Lk - kTile, C, trow, tcol, toff);
+    if (wave_s < 2) issue_kscale_load(kTile, Stage<1>{});
+  }
 
   float m = -INFINITY;  // running max of raw scores for query row qrow
   float lsum = 0.0f;    // this lane's half of the row sum of P * 256
@@ -266,41 +286,21 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
   const uint32_t ksc_off = (uint32_t)(kLdsKsc + 4 * r);
   const uint32_t vsc_off = (uint32_t)(kLdsVsc + 128 * hh + (VCOL32 ? r : 0));
 
-  wait_vm();
-  __syncthreads();
-
-  auto step = [&](int kt, auto stc) {
-    constexpr int st = decltype(stc)::value;
-    const int kv0 = kt * kTile;
-    // this tile's scales (landed with the tile)
-    uint32_t ksc[4], vsc[8];
+  // S^T = K Q^T for key blocks [KB0, KB1) of the tile in K stage SK: 4 key blocks of 32 x 2 D-steps
+  // of 64, the K scale words read from the tile's scale stage
+  mx_v16f sacc[4];
+  auto issue_s = [&](auto skc, auto kb0c, auto kb1c) {
+    constexpr int sk = decltype(skc)::value, kb0 = decltype(kb0c)::value, kb1 = decltype(kb1c)::value;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) ksc[kb] = *(const MX_LDS uint32_t*)(lds + ksc_off + st * 512 + 128 * kb);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-        vsc[ks * 4 + db] = lds[vsc_off + st * 512 + 256 * ks + (VCOL32 ? 32 * db : db)];
-    // prefetch the next tile (data and scales straight into the other LDS stage)
-    if (kt + 1 < n_ktiles) {
-      const int64_t next = (int64_t)(kv0 + kTile) * C;
-      issue_tile_load<lds_k_off(st ^ 1)>(wave_lds, kbase + next, Lk - kv0 - kTile, C, trow, tcol, toff);
-      issue_tile_load<lds_v_off(st ^ 1)>(wave_lds, vbase + next, Lk - kv0 - kTile, C, trow, tcol, toff);
-      issue_scale_load(kv0 + kTile, Stage<st ^ 1>{});
-    }
-
-    // ---- S^T = K Q^T : 4 key blocks of 32 x 2 D-steps of 64 ----
-    mx_v16f sacc[4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int kb = kb0; kb < kb1; ++kb) {
+      const uint32_t kscb = *(const MX_LDS uint32_t*)(lds + ksc_off + sk * 512 + 128 * kb) >> (8 * hh);
       sacc[kb] = mx_v16f{};
 #pragma unroll
       for (int ds = 0; ds < 2; ++ds) {
-        const MX_LDS uint8_t* t = lds + lds_k_off(st) + 32 * kb * kD;
+        const MX_LDS uint8_t* t = lds + lds_k_off(sk) + 32 * kb * kD;
         const mx_v4i lo = *(const MX_LDS mx_v4i*)(t + koffs[ds][0]);
         const mx_v4i hi = *(const MX_LDS mx_v4i*)(t + koffs[ds][1]);
         mx_v8i ka{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-        const uint32_t kscb = ksc[kb] >> (8 * hh);
         if (ds == 0)
           sacc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qa[0], sacc[kb], 0, 0, 0, (int)kscb, 0,
                                                                      (int)qsc);
@@ -309,10 +309,33 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
                                                                      (int)qsc);
       }
     }
+  };
+  using KB0 = Stage<0>;
+  using KB2 = Stage<2>;
+  using KB4 = Stage<4>;
 
-    __builtin_amdgcn_sched_barrier(0);
+  wait_vm();
+  __syncthreads();
+  if (n_ktiles > 0) issue_s(Stage<0>{}, KB0{}, KB4{});
 
-    // ---- mask (ragged tail, causal diagonal) ----
+  // One step per key tile t (stage st = t % 2). Software pipeline: the scores of tile t + 1 are
+  // computed by MFMAs issued in the middle and at the end of step t, into the registers that the
+  // exponentials of tile t have just consumed, so the matrix cores work while this wave runs the
+  // softmax:
+  //   1. mask, row max, base of the exponent (tile t's scores are complete)
+  //   2. rescale O and l where the row max moved (skipped, exactly, when none did)
+  //   3. P of key blocks 0-1 -> E4M3
+  //   4. wait for the loads issued one step ago (K of t + 1, V of t, their scales), barrier; issue
+  //      the loads of K of t + 2 and V of t + 1 into the stages of K of t and V of t - 1, which every
+  //      wave has finished reading
+  //   5. O^T += V^T P^T for keys 0-63; scores of tile t + 1, key blocks 0-1
+  //   6. P of key blocks 2-3 -> E4M3 (while the MFMAs of 5 run)
+  //   7. scores of tile t + 1, key blocks 2-3; O^T += V^T P^T for keys 64-127
+  auto step = [&](int kt, auto stc) {
+    constexpr int st = decltype(stc)::value;
+    const int kv0 = kt * kTile;
+
+    // ---- 1. mask (ragged tail, causal diagonal) ----
     const bool need_mask = (kv0 + kTile > Lk) || (p.causal && kv0 + kTile - 1 > qt * kTile + wave * 32);
     if (need_mask) {
       // key kv0 + 32 kb + 8 (v >> 2) + 4 hh + (v & 3) is masked when its offset in the tile reaches
@@ -322,19 +345,22 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int v = 0; v < 16; ++v)
-          if (32 * kb + 8 * (v >> 2) + (v & 3) >= lim) sacc[kb][v] = -INFINITY;
+          sacc[kb][v] = keep_below(sacc[kb][v], 32 * kb + 8 * (v >> 2) + (v & 3), lim, -INFINITY);
     }
 
-    // ---- online softmax (FP32) ----
-    // two independent max chains (one per pair of key blocks), joined at the end
+    // online softmax (FP32): two independent max chains (key blocks 0-1 first: their MFMAs were
+    // issued first), joined at the end
     float mx0 = m, mx1 = m;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int v = 0; v < 16; v += 2) {
+      mx0 = max3f(mx0, sacc[0][v], sacc[0][v + 1]);
+      mx1 = max3f(mx1, sacc[1][v], sacc[1][v + 1]);
+    }
 #pragma unroll
-      for (int v = 0; v < 16; v += 2) {
-        mx0 = max3f(mx0, sacc[kb][v], sacc[kb][v + 1]);
-        mx1 = max3f(mx1, sacc[kb + 2][v], sacc[kb + 2][v + 1]);
-      }
+    for (int v = 0; v < 16; v += 2) {
+      mx0 = max3f(mx0, sacc[2][v], sacc[2][v + 1]);
+      mx1 = max3f(mx1, sacc[3][v], sacc[3][v + 1]);
+    }
     float m_new;
     {
       const float mx = fmaxf(mx0, mx1);
@@ -343,8 +369,8 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
     }
     const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
     const float base = m_use * p.c2 - 8.0f;  // exp2(S c2 - base) = 256 P
-    // O and l need rescaling only where the row max moved; skip the multiplies when no row of the
-    // wave moved (exact either way)
+
+    // ---- 2. ----
     if (__builtin_amdgcn_ballot_w64(m_new > m)) {
       const float alpha = __builtin_amdgcn_exp2f((m - m_use) * p.c2);
       lsum *= alpha;
@@ -354,10 +380,11 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
         for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
     }
     m = m_new;
+
+    // ---- 3. P = exp2(S c2 - base) = 256 P in [0, 256] (no clamp needed), packed to E4M3 ----
     uint32_t pk[4][4];
     float ps = 0.0f;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    auto exp_pack = [&](int kb) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float e0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][4 * i + 0], p.c2, -base));
@@ -365,46 +392,69 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
         const float e2 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][4 * i + 2], p.c2, -base));
         const float e3 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][4 * i + 3], p.c2, -base));
         ps += (e0 + e1) + (e2 + e3);
-        // all four lie in [0, 256]: no clamp needed before the conversion
         pk[kb][i] = cvt2<true>(e2, e3, cvt2<false>(e0, e1, undef_word()));
       }
+    };
+    exp_pack(0);
+    exp_pack(1);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- 4. loads of the next stages ----
+    wait_vm();
+    __syncthreads();
+    if (kt + 2 < n_ktiles) {
+      issue_tile_load<lds_k_off(st)>(wave_lds, kbase + (int64_t)(kv0 + 2 * kTile) * C, Lk - kv0 - 2 * kTile, C, trow,
+                                     tcol, toff);
+      if (wave_s < 2) issue_kscale_load(kv0 + 2 * kTile, Stage<st>{});
+    }
+    const bool more = kt + 1 < n_ktiles;
+    if (more) {
+      issue_tile_load<lds_v_off(st ^ 1)>(wave_lds, vbase + (int64_t)(kv0 + kTile) * C, Lk - kv0 - kTile, C, trow,
+                                         tcol, toff);
+      if (wave_s >= 2) issue_vscale_load(kv0 + kTile, Stage<st ^ 1>{});
+    }
+
+    // O^T += V^T P^T for key step ks (64 keys) x 4 D-blocks of 32; the transposed V reads are issued
+    // one MFMA ahead, and an empty asm statement that uses the MFMA result and clobbers memory pins
+    // each MFMA and keeps later LDS reads below it
+    auto read_v = [&](int ks, int db) {
+      mx_v2i part[4];
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        const int rowoff = (64 * ks + 32 * (cc >> 1) + 16 * (cc & 1)) * kD;
+        part[cc] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((MX_LDS mx_v2i*)(lds + lds_v_off(st) + rowoff + voffs[db]));
+      }
+      return mx_v8i{part[0].x, part[0].y, part[1].x, part[1].y, part[2].x, part[2].y, part[3].x, part[3].y};
+    };
+    auto pv = [&](int ks) {
+      const mx_v8i pb{(int)pk[2 * ks][0], (int)pk[2 * ks][1], (int)pk[2 * ks][2], (int)pk[2 * ks][3],
+                      (int)pk[2 * ks + 1][0], (int)pk[2 * ks + 1][1], (int)pk[2 * ks + 1][2], (int)pk[2 * ks + 1][3]};
+      mx_v8i va_next = read_v(ks, 0);
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const uint32_t vsc = lds[vsc_off + st * 512 + 256 * ks + (VCOL32 ? 32 * db : db)];
+        const mx_v8i va = va_next;
+        if (db < 3) va_next = read_v(ks, db + 1);
+        oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, oacc[db], 0, 0, 0, (int)vsc, 0, 119);
+        asm volatile("" : "+v"(oacc[db])::"memory");
+      }
+    };
+
+    // ---- 5. ----
+    pv(0);
+    if (more) issue_s(Stage<st ^ 1>{}, KB0{}, KB2{});
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- 6. ----
+    exp_pack(2);
+    exp_pack(3);
     lsum += ps;
     asm volatile("" : "+v"(lsum));  // keep the row sum here (not sunk past the PV products)
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- O^T += V^T P^T : 2 key steps of 64 x 4 D-blocks of 32 ----
-    // Software-pipelined one step ahead: the transposed V reads of step i+1 are issued before the
-    // MFMA of step i; an empty asm statement that uses the MFMA result and clobbers memory keeps
-    // the compiler from hoisting further reads (which would hold all eight V operands in VGPRs).
-    {
-      mx_v8i pb[2];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-        pb[ks] = mx_v8i{(int)pk[2 * ks][0], (int)pk[2 * ks][1], (int)pk[2 * ks][2], (int)pk[2 * ks][3],
-                        (int)pk[2 * ks + 1][0], (int)pk[2 * ks + 1][1], (int)pk[2 * ks + 1][2], (int)pk[2 * ks + 1][3]};
-      auto read_v = [&](int ks, int db) {
-        mx_v2i part[4];
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-          const int rowoff = (64 * ks + 32 * (cc >> 1) + 16 * (cc & 1)) * kD;
-          part[cc] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((MX_LDS mx_v2i*)(lds + lds_v_off(st) + rowoff + voffs[db]));
-        }
-        return mx_v8i{part[0].x, part[0].y, part[1].x, part[1].y, part[2].x, part[2].y, part[3].x, part[3].y};
-      };
-      mx_v8i va_next = read_v(0, 0);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int ks = i >> 2, db = i & 3;
-        const mx_v8i va = va_next;
-        if (i + 1 < 8) va_next = read_v((i + 1) >> 2, (i + 1) & 3);
-        oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb[ks], oacc[db], 0, 0, 0, (int)vsc[i], 0, 119);
-        // pin the MFMA here and keep later LDS reads below it
-        asm volatile("" : "+v"(oacc[db])::"memory");
-      }
-    }
-
-    wait_vm();        // this thread's part of the next tile has landed in LDS
-    __syncthreads();  // ... everyone's, and nobody still reads the stage the next prefetch overwrites
+    // ---- 7. ----
+    if (more) issue_s(Stage<st ^ 1>{}, KB2{}, KB4{});
+    pv(1);
   };
 
   // two tiles per iteration so that each stage's LDS addresses are compile-time offsets
