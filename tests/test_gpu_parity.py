@@ -148,6 +148,10 @@ FWD_CASES = [
     ("ragged_train", 3, [200, 77, 384, 1], None, 2, False, 0.0, "train"),
     ("ragged_causal_outliers", 4, [300, 129, 512], None, 1, True, 0.005, "train"),
     ("cross_lens", 5, [256, 64], [1000, 33], 1, False, 0.0, "fwd"),
+    # an empty sequence between two others (offsets of the compact and padded layouts skip it);
+    # 640 keys: an odd number of key tiles, 1 and 2 tiles in the others
+    ("empty_seq_middle", 6, [128, 0, 200, 640], None, 2, False, 0.0, "train"),
+    ("causal_5_tiles", 10, [640, 130], None, 1, True, 0.0, "train"),
 ]
 
 
@@ -178,6 +182,7 @@ BWD_CASES = [
     ("ragged", 3, [200, 77, 384, 1], 2, False, 0.0, 1.0),
     # x64 outliers make |dQ / c| reach ~1.5e5: sigma = 2^-4 keeps the FP16 accumulator finite
     ("ragged_causal_outliers", 4, [300, 129, 512], 1, True, 0.005, 0.0625),
+    ("empty_seq_middle", 6, [128, 0, 200, 640], 2, False, 0.0, 1.0),
 ]
 
 
