@@ -53,9 +53,11 @@ __global__ void __launch_bounds__(256) quantize_row32_kernel(const uint16_t* __r
 }
 
 // ---------------------------------------------------------------------------------------------
-// COL32: 32 x 1 blocks along the tokens. A thread owns 4 adjacent columns of one 32-token block
-// (8-byte loads, 64 lanes cover 512 contiguous bytes of a row).
-// Grid: x = column groups / 256, y = block index inside the sequence, z = sequence.
+// COL32: 32 x 1 blocks along the tokens. A wave covers 32 rows x 128 columns: lane l owns columns
+// 4 (l % 32) .. +3 (8-byte loads) of rows 16 (l / 32) + i, i = 0..15; a column's maximum joins the
+// two half-waves with one lane swap. Every load instruction covers two 256-byte row segments and
+// every store two whole 128-byte output row segments; four waves cover 512 columns.
+// Grid: x = C / 512 (rounded up), y = block index inside the sequence, z = sequence.
 // ---------------------------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) quantize_col32_kernel(const uint16_t* __restrict__ x, int64_t ld_x, int C,
                                                              const int32_t* __restrict__ cu,
@@ -65,44 +67,54 @@ __global__ void __launch_bounds__(256) quantize_col32_kernel(const uint16_t* __r
   const int64_t t0 = cu[s], L = (int64_t)cu[s + 1] - t0;
   if ((int64_t)b * 32 >= L) return;  // uniform over the workgroup
   const SeqOffsets off = seq_offsets(cu, s);
-  const int g = blockIdx.x * blockDim.x + threadIdx.x;
-  if (g >= (C >> 2)) return;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int cg = blockIdx.x * 4 + wave;  // 128-column group
+  if (cg * 128 >= C) return;             // whole wave leaves together
+  const int col = cg * 128 + 4 * (lane & 31);
+  const bool col_ok = col < C;
+  const int col_ld = col_ok ? col : cg * 128;  // lanes past C re-read the group's first columns
+  const int half = lane >> 5;
   const int rows = (int)min<int64_t>(32, L - (int64_t)b * 32);
   const int64_t ta = t0 + (int64_t)b * 32;
   // rows past the sequence end re-read its last row: every load is issued without a branch, and a
   // repeated row does not change the block maximum
-  uint2 v[32];
+  uint2 v[16];
   uint32_t am[4] = {0, 0, 0, 0};
 #pragma unroll
-  for (int r = 0; r < 32; ++r) v[r] = *reinterpret_cast<const uint2*>(x + (ta + min(r, rows - 1)) * ld_x + (int64_t)g * 4);
+  for (int i = 0; i < 16; ++i)
+    v[i] = *reinterpret_cast<const uint2*>(x + (ta + min(16 * half + i, rows - 1)) * ld_x + col_ld);
 #pragma unroll
-  for (int r = 0; r < 32; ++r) {
-    am[0] = max(am[0], v[r].x & 0x7fffu);
-    am[1] = max(am[1], (v[r].x >> 16) & 0x7fffu);
-    am[2] = max(am[2], v[r].y & 0x7fffu);
-    am[3] = max(am[3], (v[r].y >> 16) & 0x7fffu);
+  for (int i = 0; i < 16; ++i) {
+    am[0] = max(am[0], v[i].x & 0x7fffu);
+    am[1] = max(am[1], (v[i].x >> 16) & 0x7fffu);
+    am[2] = max(am[2], v[i].y & 0x7fffu);
+    am[3] = max(am[3], (v[i].y >> 16) & 0x7fffu);
   }
   uint32_t code[4];
   float inv[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    code[i] = mx_code_from_amax_bits(am[i] << 16);
-    inv[i] = code[i] == 255u ? 0.0f : mx_inv_scale(code[i]);
+  for (int k = 0; k < 4; ++k) {
+    auto sw = __builtin_amdgcn_permlane32_swap(am[k], am[k], false, false);  // the other half-wave
+    const uint32_t m = max((uint32_t)sw[0], (uint32_t)sw[1]);
+    code[k] = mx_code_from_amax_bits(m << 16);
+    inv[k] = code[k] == 255u ? 0.0f : mx_inv_scale(code[k]);
   }
 #pragma unroll
-  for (int r = 0; r < 32; ++r) {
-    if (r < rows) {
-      uint32_t o = mx_pack4(bf16_to_f32(v[r].x & 0xffffu) * inv[0], bf16_to_f32(v[r].x >> 16) * inv[1],
-                            bf16_to_f32(v[r].y & 0xffffu) * inv[2], bf16_to_f32(v[r].y >> 16) * inv[3]);
+  for (int i = 0; i < 16; ++i) {
+    const int r = 16 * half + i;
+    if (col_ok && r < rows) {
+      uint32_t o = mx_pack4(bf16_to_f32(v[i].x & 0xffffu) * inv[0], bf16_to_f32(v[i].x >> 16) * inv[1],
+                            bf16_to_f32(v[i].y & 0xffffu) * inv[2], bf16_to_f32(v[i].y >> 16) * inv[3]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (code[i] == 255u) o = (o & ~(0xffu << (8 * i))) | (0x7fu << (8 * i));
-      *reinterpret_cast<uint32_t*>(data + (ta + r) * C + (int64_t)g * 4) = o;
+      for (int k = 0; k < 4; ++k)
+        if (code[k] == 255u) o = (o & ~(0xffu << (8 * k))) | (0x7fu << (8 * k));
+      *reinterpret_cast<uint32_t*>(data + (ta + r) * C + col) = o;
     }
   }
-  const int64_t br = off.blocks32 + b;
-  *reinterpret_cast<uint32_t*>(scale + br * C + (int64_t)g * 4) =
-      code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
+  if (half == 0 && col_ok) {
+    const int64_t br = off.blocks32 + b;
+    *reinterpret_cast<uint32_t*>(scale + br * C + col) = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
+  }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -454,7 +466,7 @@ hipError_t launch_quantize(const uint16_t* x, int64_t ld_x, int64_t T, int C, co
     hipLaunchKernelGGL(quantize_row32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, ld_x, T, C, data,
                        scale);
   } else if (mode == 1) {
-    dim3 grid((unsigned)(((C >> 2) + 255) / 256), (unsigned)((max_seqlen + 31) / 32), (unsigned)nseq);
+    dim3 grid((unsigned)((C + 511) / 512), (unsigned)((max_seqlen + 31) / 32), (unsigned)nseq);
     hipLaunchKernelGGL(quantize_col32_kernel, grid, dim3(256), 0, stream, x, ld_x, C, cu, data, scale);
   } else {
     dim3 grid((unsigned)((C + 255) / 256), (unsigned)((max_seqlen + 31) / 32), (unsigned)nseq);

@@ -34,7 +34,7 @@ def _special_matrix(seed, T, C):
 
 @pytest.mark.parametrize("mode", [oracle.ROW32, oracle.COL32, oracle.SQ32])
 @pytest.mark.parametrize("lens", [[256], [37, 128, 1, 300, 95, 64]])
-@pytest.mark.parametrize("C", [384, 160])  # 160: the last 64-column group holds one 32-column block
+@pytest.mark.parametrize("C", [384, 160, 224, 96])  # C % 128 = 32, 96 and C < 128: partial column groups
 def test_quantize_bit_exact(mode, lens, C):
     say(f"quantize mode={mode} lens={lens} C={C}")
     cu = synth.cu_seqlens(lens)
