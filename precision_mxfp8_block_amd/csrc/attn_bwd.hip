@@ -338,14 +338,15 @@ __global__ void __launch_bounds__(64 * kBwdWaves, 1) attn_bwd_kernel(BwdParams p
       if (j == 0) __syncthreads();  // B2: the consumers hold their operands of tile k - 1 but block 3's
       lds_pq[kw][j][lane] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
       lds_sq[kw][j][lane] = make_uint4(dsk[0], dsk[1], dsk[2], dsk[3]);
-      // the image: key row 32 kw + r, queries 32 j + 8 i + 4 hh .. +3
+      // the image: key row 32 kw + r. Lane (r, hh) holds the 4-query groups 32 j + 8 i + 4 hh; two
+      // half-wave swaps give lane (r, 0) queries 32 j + 0..15 and lane (r, 1) queries 32 j + 16..31
+      // (words: hh = 0 group i, hh = 1 group i, hh = 0 group i + 1, hh = 1 group i + 1), which it
+      // writes as one 16-byte chunk
       const int kvl = 32 * kw + r;
-      const int sw = swz(kvl);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int ql = 32 * j + 8 * i + 4 * hh;
-        *reinterpret_cast<uint32_t*>(lds_ds + kvl * kD + 16 * ((ql >> 4) ^ sw) + (ql & 15)) = dsk[i];
-      }
+      const auto x02 = __builtin_amdgcn_permlane32_swap(dsk[0], dsk[2], false, false);
+      const auto x13 = __builtin_amdgcn_permlane32_swap(dsk[1], dsk[3], false, false);
+      const uint4 chunk = make_uint4(x02[0], x02[1], x13[0], x13[1]);
+      *reinterpret_cast<uint4*>(lds_ds + kvl * kD + 16 * ((2 * j + hh) ^ swz(kvl))) = chunk;
     };
     // Block 3's second half is deferred into the next period, where it runs beside that tile's first
     // loads and MFMAs (the consumers read block 3's operands and image chunks after B2).
@@ -534,6 +535,9 @@ __global__ void __launch_bounds__(64 * kBwdWaves, 1) attn_bwd_kernel(BwdParams p
       uint32_t codes = 0;
       const int64_t tile = (((int64_t)h * p.nseq + s) * p.ntq_max + (k - 1)) * p.ntk_max + kt;
       uint8_t* img = p.ds_img + tile * (kTile * kD) + kw * 4096;
+      // the wave's four 16-byte chunks of tile k - 1's dS_q image: taken from LDS now (blocks 0-2) and
+      // after B2 (block 3), stored to global memory after this period's load wait (see below)
+      uint4 imgv[4];
       if (k > qt_begin) {
         const uint4 p0 = lds_pq[kw][0][lane], p1 = lds_pq[kw][1][lane], p2 = lds_pq[kw][2][lane];
         const uint4 s0 = lds_sq[kw][0][lane], s1 = lds_sq[kw][1][lane], s2 = lds_sq[kw][2][lane];
@@ -542,13 +546,8 @@ __global__ void __launch_bounds__(64 * kBwdWaves, 1) attn_bwd_kernel(BwdParams p
         pa[1] = mx_v8i{(int)p2.x, (int)p2.y, (int)p2.z, (int)p2.w, 0, 0, 0, 0};
         sa[1] = mx_v8i{(int)s2.x, (int)s2.y, (int)s2.z, (int)s2.w, 0, 0, 0, 0};
         codes = lds_dscode[kw];
-        if (lane == 0) *reinterpret_cast<uint32_t*>(p.ds_codes + tile * 16 + 4 * kw) = codes;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int o = c * 1024 + lane * 16;
-          const uint4 v = *reinterpret_cast<const uint4*>(lds_ds + kw * 4096 + o);
-          if (!img_blk3[c]) *reinterpret_cast<uint4*>(img + o) = v;
-        }
+        for (int c = 0; c < 4; ++c) imgv[c] = *reinterpret_cast<const uint4*>(lds_ds + kw * 4096 + c * 1024 + lane * 16);
       }
       if (k + 1 < n_qtiles) issue_qtile(st_next, k + 1);
       __syncthreads();  // B2
@@ -562,10 +561,15 @@ __global__ void __launch_bounds__(64 * kBwdWaves, 1) attn_bwd_kernel(BwdParams p
         sa[1][5] = (int)s3.y;
         sa[1][6] = (int)s3.z;
         sa[1][7] = (int)s3.w;
+        // block 3's chunks again, now written (the others may already hold tile k's image: keep the
+        // values read before B2 for them)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const int o = c * 1024 + lane * 16;
-          if (img_blk3[c]) *reinterpret_cast<uint4*>(img + o) = *reinterpret_cast<const uint4*>(lds_ds + kw * 4096 + o);
+          const uint4 v = *reinterpret_cast<const uint4*>(lds_ds + kw * 4096 + c * 1024 + lane * 16);
+          imgv[c].x = img_blk3[c] ? v.x : imgv[c].x;
+          imgv[c].y = img_blk3[c] ? v.y : imgv[c].y;
+          imgv[c].z = img_blk3[c] ? v.z : imgv[c].z;
+          imgv[c].w = img_blk3[c] ? v.w : imgv[c].w;
         }
       }
       if (k > qt_begin) {
@@ -589,7 +593,15 @@ __global__ void __launch_bounds__(64 * kBwdWaves, 1) attn_bwd_kernel(BwdParams p
           }
         }
       }
-      wait_vm();  // this wave's part of tile k + 1 has landed (and its image stores are done)
+      // This wave's part of tile k + 1 has landed. The vector memory counter also counts stores, so
+      // the image and code stores are issued only now: they complete during the next period instead
+      // of holding up this wait.
+      wait_vm();
+      if (k > qt_begin) {
+        if (lane == 0) *reinterpret_cast<uint32_t*>(p.ds_codes + tile * 16 + 4 * kw) = codes;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) *reinterpret_cast<uint4*>(img + c * 1024 + lane * 16) = imgv[c];
+      }
       st = st_next;
     }
 
