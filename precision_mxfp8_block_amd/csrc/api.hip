@@ -58,7 +58,8 @@ mxfa_status check_jagged(const int32_t* cu, int nseq, int max_seqlen, int64_t T,
 mxfa_status check_attn(const mxfa_attn_args* a, const char* fn) {
   if (!a) return fail(MXFA_ERR_INVALID, "%s: args is NULL", fn);
   if (a->head_dim != 128) return fail(MXFA_ERR_UNSUPPORTED, "%s: head_dim=%d (only 128 is implemented)", fn, a->head_dim);
-  if (a->num_heads < 1) return fail(MXFA_ERR_INVALID, "%s: num_heads=%d", fn, a->num_heads);
+  if (a->num_heads < 1 || a->num_heads > kMaxGridY)
+    return fail(MXFA_ERR_INVALID, "%s: num_heads=%d out of [1, %d]", fn, a->num_heads, kMaxGridY);
   if (a->nseq < 1) return fail(MXFA_ERR_INVALID, "%s: nseq=%d", fn, a->nseq);
   if (a->total_q < 0 || a->total_k < 0) return fail(MXFA_ERR_INVALID, "%s: negative total tokens", fn);
   if (a->max_seqlen_q < 0 || a->max_seqlen_q > a->total_q || a->max_seqlen_k < 0 || a->max_seqlen_k > a->total_k)

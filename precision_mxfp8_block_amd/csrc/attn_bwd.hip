@@ -154,31 +154,38 @@ __device__ __forceinline__ uint32_t wave_max_dpp(uint32_t v) {
 // Preprocess: the negated row sums -Delta[h][t] = -sum_d dO[t, h, d] * O[t, h, d] (fp32, the
 // initial value of the dP accumulator) and the exponent offset of 256 P, b[h][t] = 8 - LSE[h][t]
 // log2(e) (so 256 P = exp2(c log2(e) S + b)).
-// Sixteen lanes per (token, head) row of 128: eight bf16 of O and of dO per lane.
+// A workgroup covers 64 consecutive tokens of one head: four lanes per (token, head) row of 128,
+// lane g reading 16-byte pieces g, g + 4, g + 8, g + 12 of O and of dO (every load instruction
+// covers whole 64-byte row segments), so each wave writes 16 consecutive outputs per array.
+// Grid: x = tokens / 64 (rounded up), y = head.
 // ---------------------------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) bwd_preprocess_kernel(const uint16_t* __restrict__ o,
                                                              const uint16_t* __restrict__ dout,
                                                              const float* __restrict__ lse, int64_t T, int H,
                                                              float* __restrict__ ndelta, float* __restrict__ pexp) {
-  // 16 lanes per (token, head) row of 128: 8 bf16 of O and of dO per lane (16-byte loads)
-  const int64_t row = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 4;
-  const int g = threadIdx.x & 15;
-  const bool valid = row < T * H;
+  const int h = blockIdx.y;
+  const int g = threadIdx.x & 3;
+  const int64_t t = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 2);
+  const bool valid = t < T;
+  const int64_t row = (valid ? t : T - 1) * H + h;  // rows past the end re-read the last one
+  uint4 a[4], b[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    a[c] = *reinterpret_cast<const uint4*>(o + row * kD + 8 * (g + 4 * c));
+    b[c] = *reinterpret_cast<const uint4*>(dout + row * kD + 8 * (g + 4 * c));
+  }
   float sum = 0.0f;
-  if (valid) {
-    const uint4 a = *reinterpret_cast<const uint4*>(o + row * kD + 8 * g);
-    const uint4 b = *reinterpret_cast<const uint4*>(dout + row * kD + 8 * g);
-    const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const uint32_t aw[4] = {a[c].x, a[c].y, a[c].z, a[c].w}, bw[4] = {b[c].x, b[c].y, b[c].z, b[c].w};
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       sum += bf16_to_f32(aw[i] & 0xffffu) * bf16_to_f32(bw[i] & 0xffffu) +
              bf16_to_f32(aw[i] >> 16) * bf16_to_f32(bw[i] >> 16);
   }
-#pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 16);
+  sum += __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(sum), 0xB1, 0xF, 0xF, false));  // lane bit 0
+  sum += __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(sum), 0x4E, 0xF, 0xF, false));  // lane bit 1
   if (valid && g == 0) {
-    const int64_t t = row / H;
-    const int h = (int)(row % H);
     ndelta[(int64_t)h * T + t] = -sum;
     pexp[(int64_t)h * T + t] = 8.0f - lse[(int64_t)h * T + t] * kLog2e;
   }
@@ -842,9 +849,8 @@ hipError_t launch_attn_bwd(const AttnProblem& a, const MxOperand& v_d, const MxO
   const int ntq_max = (a.max_seqlen_q + kTile - 1) / kTile;
   const int ntk_max = (a.max_seqlen_k + kTile - 1) / kTile;
   if (Tq > 0) {
-    const int64_t rows = Tq * a.H;  // 16 lanes per row
-    const int64_t blocks = (rows + 15) / 16;
-    hipLaunchKernelGGL(bwd_preprocess_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, o, dout_bf16, lse, Tq,
+    hipLaunchKernelGGL(bwd_preprocess_kernel, dim3((unsigned)((Tq + 63) / 64), (unsigned)a.H), dim3(256), 0, stream, o,
+                       dout_bf16, lse, Tq,
                        a.H, delta, pexp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -80,6 +80,7 @@ def _args(**kw):
 @pytest.mark.parametrize("kw,expect", [
     (dict(D=64), UNSUPPORTED),
     (dict(H=0), INVALID),
+    (dict(H=65536), INVALID),           # a grid dimension of the backward's preprocess
     (dict(nseq=0), INVALID),
     (dict(max_q=300), INVALID),         # > total_q
     (dict(cu_q=0), INVALID),
