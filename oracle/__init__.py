@@ -59,7 +59,7 @@ def _load():
     lib.orc_dequantize.argtypes = [P, P, i64, i32, P, i32, i32, P]
     lib.orc_scale_scatter.argtypes = [P, P, i32, i32, i32, P, i64]
     lib.orc_attn_fwd_f64.argtypes = [P, P, P, P, P, i32, i32, i32, f32, i32, i32, i32, P, P, P, i32]
-    lib.orc_attn_fwd_mx.argtypes = [P, P, i32, P, P, i32, P, P, i32, P, P, i32, i32, i32, f32, i32, P, P, P, i32]
+    lib.orc_attn_fwd_mx.argtypes = [P, P, i32, P, P, i32, P, P, i32, P, P, i32, i32, i32, f32, i32, i32, P, P, P, i32]
     lib.orc_attn_bwd_f64.argtypes = [P, P, P, P, P, P, P, P, P, i32, i32, i32, f32, i32, i32, i32, f32,
                                      P, P, P, P, P, P, P, i32]
     lib.orc_attn_bwd_mx.argtypes = [P, P, P, P, P, P, i32, P, P, P, P, P, P, P, i32, i32, i32, f32, i32, i32, f32,
@@ -186,8 +186,12 @@ def scale_scatter(compact, cu, C, mode):
 
 # ---- attention -----------------------------------------------------------------------------
 
+P_NONE, P_STATIC, P_DYNAMIC = 0, 1, 2  # P quantization modes of the forward
+
 def attn_fwd_f64(q, k, v, cu_q, cu_k, H, D, softmax_scale, causal=False, quant_p=True, kv_tile=128, nthreads=None):
-    """q, k, v: float64 [T, H*D]. Returns (o_bf16 uint16 [Tq, H*D], o_f32 [Tq, H*D], lse [H, Tq])."""
+    """q, k, v: float64 [T, H*D]. Returns (o_bf16 uint16 [Tq, H*D], o_f32 [Tq, H*D], lse [H, Tq]).
+    quant_p: P_NONE / False (no P quantization), P_STATIC / True (scale 2^-8 on every block) or
+    P_DYNAMIC (each 32-key block scaled by the MX rule on its largest P)."""
     lib = _load()
     cu_q, cu_k = _c(cu_q, np.int32), _c(cu_k, np.int32)
     q, k, v = _c(q, np.float64), _c(k, np.float64), _c(v, np.float64)
@@ -203,8 +207,9 @@ def attn_fwd_f64(q, k, v, cu_q, cu_k, H, D, softmax_scale, causal=False, quant_p
 
 
 def attn_fwd_mx(q, q_scale, q_mode, k, k_scale, k_mode, v, v_scale, v_mode, cu_q, cu_k, H, D, softmax_scale,
-                causal=False, nthreads=None):
-    """MX inputs in compact layouts. Returns (o_bf16 [Tq, H*D] uint16, o_f32, lse [H, Tq])."""
+                causal=False, p_scale=1, nthreads=None):
+    """MX inputs in compact layouts. Returns (o_bf16 [Tq, H*D] uint16, o_f32, lse [H, Tq]).
+    p_scale: P_STATIC (1) or P_DYNAMIC (2), as for attn_fwd_f64."""
     lib = _load()
     cu_q, cu_k = _c(cu_q, np.int32), _c(cu_k, np.int32)
     arrs = [_c(a, np.uint8) for a in (q, q_scale, k, k_scale, v, v_scale)]
@@ -214,7 +219,7 @@ def attn_fwd_mx(q, q_scale, q_mode, k, k_scale, k_mode, v, v_scale, v_mode, cu_q
     lse = np.empty((H, Tq), np.float32)
     rc = lib.orc_attn_fwd_mx(_p(arrs[0]), _p(arrs[1]), q_mode, _p(arrs[2]), _p(arrs[3]), k_mode, _p(arrs[4]),
                              _p(arrs[5]), v_mode, _p(cu_q), _p(cu_k), cu_q.size - 1, H, D, softmax_scale,
-                             int(causal), _p(o16), _p(o32), _p(lse), nthreads or default_threads())
+                             int(causal), int(p_scale), _p(o16), _p(o32), _p(lse), nthreads or default_threads())
     _check(rc, "attn_fwd_mx")
     return o16, o32, lse
 

@@ -299,14 +299,22 @@ const int TILE = 128;  // Q and KV tile rows [TC paragraph 2: [128, 128] tiles, 
 //   S  = Q K^T, accumulated exactly and rounded to fp32 (the MMA accumulates in FP32).
 //   online softmax in FP32 [TC paragraph 1: softmax runs in FP32, then P is converted]:
 //     m' = max(m, rowmax S);  alpha = exp(c (m - m'));  P = exp(c (S - m'));  l = alpha l + rowsum P
-//   P is quantized to E4M3 with the static scale 2^-8 (E8M0 code 119) on every 32-block: P <= 1
-//     because the row max m' is the reference point [BR item 4: constant scale, P in [0,1];
-//     AE TMEM: the softmax row max is reused, so no extra max pass] (READING A5).
+//   quant_p = 1: P is quantized to E4M3 with the static scale 2^-8 (E8M0 code 119) on every
+//     32-block: P <= 1 because the row max m' is the reference point [BR item 4: constant scale,
+//     P in [0,1]; AE TMEM: the softmax row max is reused, so no extra max pass] (READING A5).
+//   quant_p = 2: dynamic block scale. Each row's keys of the tile are split into blocks of 32
+//     starting at the tile's first key; a block's scale is the MX scale rule applied to its largest
+//     P (code = e8m0_code(amax), so that element lands in [256, 512)), and its P values are
+//     quantized as E4M3(P 2^(127-code)) [AE TMEM / TC: 32-element blocks with one E8M0 scale, the
+//     scale taken from the block maximum; the alternative to the constant P scale of BR item 4].
+//     A block holding the row maximum gets code 119, the static scale.
+//   quant_p = 0 skips the P quantization (pinning mode).
 //   O  = alpha O + deq(P_q) V, rounded to fp32 per tile.
 //   At the end: O_out = bf16(fl32(O / l)), LSE = fl32(c m + ln l).
-// quant_p = 0 skips the P quantization (pinning mode).
 // Pinned by: FP64 brute-force softmax attention (no-quant mode), one-tile == many tiles,
-// closed forms (K = 0, causal row 0, one-hot scores), the quantization error bound.
+// closed forms (K = 0, causal row 0, one-hot scores), the quantization error bound; the dynamic
+// mode by a worked single-row example (block codes from floor(log2 amax), identity V), its K = 0
+// closed form and its accuracy against the static mode.
 void attn_fwd_unit(const double* q, const double* k, const double* v, int64_t q0, int64_t Lq, int64_t k0,
                    int64_t Lk, int H, int D, int h, double c, int causal, int quant_p, int kv_tile,
                    uint16_t* o_bf16, float* o_f32, float* lse, int64_t lse_stride) {
@@ -344,16 +352,29 @@ void attn_fwd_unit(const double* q, const double* k, const double* v, int64_t q0
         if (mnew == -std::numeric_limits<double>::infinity()) continue;  // no key seen yet
         double alpha = (m[i] == -std::numeric_limits<double>::infinity()) ? 0.0 : fl32(std::exp(c * (m[i] - mnew)));
         double psum = 0.0;
-        std::vector<double> pv(D, 0.0);
+        std::vector<double> p(nk, 0.0);  // masked keys keep P = 0
         for (int64_t j = 0; j < nk; ++j) {
           double s = S[i * kv_tile + j];
           if (s == -std::numeric_limits<double>::infinity()) continue;
-          double p = fl32(std::exp(c * (s - mnew)));
-          psum += p;
-          double pd = p;
-          if (quant_p) pd = e4m3_decode(e4m3_encode(p * 256.0)) * e8m0_value(119);
-          const double* vj = v + (k0 + kt + j) * C + (int64_t)h * D;
-          for (int d = 0; d < D; ++d) pv[d] += pd * vj[d];
+          p[j] = fl32(std::exp(c * (s - mnew)));
+          psum += p[j];
+        }
+        std::vector<double> pv(D, 0.0);
+        for (int64_t b0 = 0; b0 < nk; b0 += 32) {  // 32-key blocks from the tile start
+          const int64_t b1 = std::min<int64_t>(b0 + 32, nk);
+          int code = 119;
+          if (quant_p == 2) {
+            double amax = 0.0;
+            for (int64_t j = b0; j < b1; ++j) amax = std::max(amax, p[j]);
+            code = e8m0_code(amax);
+          }
+          for (int64_t j = b0; j < b1; ++j) {
+            if (p[j] == 0.0) continue;
+            double pd = p[j];
+            if (quant_p) pd = e4m3_decode(e4m3_encode(p[j] * pow2(127 - code))) * e8m0_value(code);
+            const double* vj = v + (k0 + kt + j) * C + (int64_t)h * D;
+            for (int d = 0; d < D; ++d) pv[d] += pd * vj[d];
+          }
         }
         l[i] = fl32(alpha * l[i] + psum);
         for (int d = 0; d < D; ++d) O[i * D + d] = fl32(alpha * O[i * D + d] + pv[d]);
@@ -610,7 +631,8 @@ int orc_scale_scatter(const uint8_t* compact, const int32_t* cu, int nseq, int C
 int orc_attn_fwd_f64(const double* q, const double* k, const double* v, const int32_t* cu_q, const int32_t* cu_k,
                      int nseq, int H, int D, float softmax_scale, int causal, int quant_p, int kv_tile,
                      uint16_t* o_bf16, float* o_f32, float* lse, int nthreads) {
-  if (!cu_q || !cu_k || nseq < 1 || H < 1 || D < 1 || kv_tile < 1 || kv_tile > 4096) return -1;
+  if (!cu_q || !cu_k || nseq < 1 || H < 1 || D < 1 || kv_tile < 1 || kv_tile > 4096 || quant_p < 0 || quant_p > 2)
+    return -1;
   int64_t Tq = cu_q[nseq];
   parallel_units(nseq * H, nthreads, [&](int u) {
     int s = u / H, h = u % H;
@@ -623,16 +645,16 @@ int orc_attn_fwd_f64(const double* q, const double* k, const double* v, const in
 // Forward on MX inputs in the compact layout (payload [T, H*D], scales per mode).
 int orc_attn_fwd_mx(const uint8_t* q, const uint8_t* q_scale, int q_mode, const uint8_t* k, const uint8_t* k_scale,
                     int k_mode, const uint8_t* v, const uint8_t* v_scale, int v_mode, const int32_t* cu_q,
-                    const int32_t* cu_k, int nseq, int H, int D, float softmax_scale, int causal, uint16_t* o_bf16,
-                    float* o_f32, float* lse, int nthreads) {
-  if (!cu_q || !cu_k || nseq < 1 || (H * D) % 32) return -1;
+                    const int32_t* cu_k, int nseq, int H, int D, float softmax_scale, int causal, int quant_p,
+                    uint16_t* o_bf16, float* o_f32, float* lse, int nthreads) {
+  if (!cu_q || !cu_k || nseq < 1 || (H * D) % 32 || quant_p < 0 || quant_p > 2) return -1;
   int64_t Tq = cu_q[nseq], Tk = cu_k[nseq];
   int C = H * D;
   std::vector<double> qd((size_t)Tq * C), kd((size_t)Tk * C), vd((size_t)Tk * C);
   dequantize_matrix(q, q_scale, Tq, C, cu_q, nseq, q_mode, qd.data());
   dequantize_matrix(k, k_scale, Tk, C, cu_k, nseq, k_mode, kd.data());
   dequantize_matrix(v, v_scale, Tk, C, cu_k, nseq, v_mode, vd.data());
-  return orc_attn_fwd_f64(qd.data(), kd.data(), vd.data(), cu_q, cu_k, nseq, H, D, softmax_scale, causal, 1, TILE,
+  return orc_attn_fwd_f64(qd.data(), kd.data(), vd.data(), cu_q, cu_k, nseq, H, D, softmax_scale, causal, quant_p, TILE,
                           o_bf16, o_f32, lse, nthreads);
 }
 

@@ -368,6 +368,78 @@ def test_fwd_quantized_error_bound():
     assert np.max(np.abs(oq - ob)) <= 2.0 ** -4 * np.max(np.abs(v)) + 384 * 2.0 ** -18 * np.max(np.abs(v))
 
 
+def test_fwd_dynamic_p_worked_example():
+    """Dynamic P scale on one query row against 100 keys (blocks of 32, 32, 32 and a ragged 4).
+    Scores s_j = -0.5 pi(j), pi permuting keys inside each block so the block maximum is not its
+    first key; with c = 1/sqrt(128) the block maxima are P = 1, exp(-16c), exp(-32c), exp(-48c),
+    so floor(log2 amax) + 119 gives the codes 119, 116, 114, 112 (worked by hand). With V the
+    identity, O_d = deq(P_q)_d / l exposes every quantized P."""
+    nk, D = 100, 128
+    nb = [min(32, nk - 32 * (j // 32)) for j in range(nk)]  # size of key j's block
+    perm = np.array([32 * (j // 32) + ((j % 32) * 7 + 3) % nb[j] for j in range(nk)])
+    assert sorted(perm) == list(range(nk)) and all(perm[32 * b] != 32 * b for b in range(4))
+    s = -0.5 * perm
+    q = np.zeros((1, D)); q[0, 0] = 1.0
+    k = np.zeros((nk, D)); k[:, 0] = s
+    v = np.zeros((nk, D)); v[np.arange(nk), np.arange(nk)] = 1.0
+    c = float(np.float32(1 / math.sqrt(128)))
+    cu_q, cu_k = synth.cu_seqlens([1]), synth.cu_seqlens([nk])
+    _, o_dyn, _ = oracle.attn_fwd_f64(q, k, v, cu_q, cu_k, 1, D, c, quant_p=oracle.P_DYNAMIC)
+    _, o_sta, _ = oracle.attn_fwd_f64(q, k, v, cu_q, cu_k, 1, D, c, quant_p=oracle.P_STATIC)
+
+    p_ = np.array([np.float32(math.exp(c * sj)) for sj in s], dtype=np.float64)
+    l = 0.0
+    for x in p_:
+        l += x
+    l = np.float32(l)
+    codes = [int(np.floor(np.log2(p_[b:b + 32].max()))) + 119 for b in range(0, nk, 32)]
+    assert codes == [119, 116, 114, 112]
+    deq = np.empty(nk)
+    for j in range(nk):
+        e = codes[j // 32] - 127
+        deq[j] = oracle.e4m3_decode(oracle.e4m3_encode(p_[j] * 2.0 ** -e)) * 2.0 ** e
+    expect = np.zeros(D, np.float32)
+    expect[:nk] = (deq / np.float64(l)).astype(np.float32)
+    np.testing.assert_array_equal(o_dyn[0], expect)
+    assert np.any(o_dyn[0] != o_sta[0])  # the blocks below the row maximum are rounded differently
+
+
+def test_fwd_dynamic_p_closed_form_zero_keys():
+    """K = 0: every P is 1, each block's maximum is 1, so every block takes code 119 and the dynamic
+    mode reduces to O = mean of the V rows (ragged last tile and block included)."""
+    cu = synth.cu_seqlens([200])
+    H, D = 1, 128
+    q = _rand(4, 1, (200, D))
+    k = np.zeros((200, D))
+    v = _rand(4, 3, (200, D))
+    _, o, lse = oracle.attn_fwd_f64(q, k, v, cu, cu, H, D, 0.0884, quant_p=oracle.P_DYNAMIC)
+    np.testing.assert_allclose(o, np.broadcast_to(v.mean(axis=0), o.shape), rtol=0, atol=1e-6)
+    np.testing.assert_allclose(lse, math.log(200), rtol=1e-6)
+
+
+def test_fwd_dynamic_p_accuracy_on_small_blocks():
+    """Key 0 scores highest and the rest of its 32-key block has c s = -200 (P = 0 exactly in FP32,
+    so that block is exact in both modes); the 480 keys of the later blocks have c s in
+    [-16, -12], so 256 P < 2^-10 for all of them: the static scale
+    2^-8 rounds every one to zero (the smallest E4M3 subnormal is 2^-9), while a per-block scale
+    keeps them normal. The dynamic mode must then be much closer to exact attention than the
+    static one, and inside the 2^-4 relative bound."""
+    N, D, nq = 512, 64, 4
+    rng = np.random.default_rng(11)
+    c = 0.125
+    s = np.concatenate([[0.0], np.full(31, -200.0), rng.uniform(-16.0, -12.0, N - 32)]) / c
+    q = np.zeros((nq, D)); q[:, 0] = 1.0
+    k = np.zeros((N, D)); k[:, 0] = s
+    v = _rand(8, 3, (N, D))
+    cu_q, cu_k = synth.cu_seqlens([nq]), synth.cu_seqlens([N])
+    _, o_dyn, _ = oracle.attn_fwd_f64(q, k, v, cu_q, cu_k, 1, D, c, quant_p=oracle.P_DYNAMIC)
+    _, o_sta, _ = oracle.attn_fwd_f64(q, k, v, cu_q, cu_k, 1, D, c, quant_p=oracle.P_STATIC)
+    ob, _ = _brute_attention(q, k, v, cu_q, cu_k, 1, D, c, False)
+    err_dyn, err_sta = np.max(np.abs(o_dyn - ob)), np.max(np.abs(o_sta - ob))
+    assert err_dyn < 0.1 * err_sta
+    assert err_dyn <= 2.0 ** -4 * np.max(np.abs(v))
+
+
 # ---------------------------------------------------------------------------------------------
 # Attention backward
 # ---------------------------------------------------------------------------------------------
