@@ -356,6 +356,20 @@ def main():
     torch.cuda.synchronize()
     bwd32_s = float(np.median([e[0].elapsed_time(e[1]) * 1e-3 for e in e32]))
 
+    # the forward once more with the dynamic per-block P scale (same inputs and stream), for the
+    # comparison of the two P scales
+    edyn = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n32)]
+    o_dyn = torch.empty_like(o)
+    lse_dyn = torch.empty_like(lse)
+    for i in range(n32 + 1):
+        if i:
+            edyn[i - 1][0].record(stream)
+        mx.mxfa_fwd_p_scale(attn, mx.P_BLOCK_DYNAMIC, o_dyn, lse_dyn, stream)
+        if i:
+            edyn[i - 1][1].record(stream)
+    torch.cuda.synchronize()
+    fwd_dyn_s = float(np.median([e[0].elapsed_time(e[1]) * 1e-3 for e in edyn]))
+
     times = {n: [e[0].elapsed_time(e[1]) * 1e-3 for e in ev[n]] for n in names}
     med = {n: float(np.median(v)) for n, v in times.items()}
     f_fwd = 4.0 * N * N * D * B * H
@@ -384,6 +398,7 @@ def main():
         "bwd_pflops": round(bwd_pf, 4), "bwd_frac_peak": round(bwd_pf * 1e15 / PEAK_MXFP8, 4),
         "fwd_us": round(med["fwd"] * 1e6, 2), "bwd_us": round(med["bwd"] * 1e6, 2),
         "bwd_fp32dq_us": round(bwd32_s * 1e6, 2), "bwd_fp32dq_pflops": round(f_bwd / bwd32_s / 1e15, 4),
+        "fwd_dynamic_p_us": round(fwd_dyn_s * 1e6, 2), "fwd_dynamic_p_pflops": round(f_fwd / fwd_dyn_s / 1e15, 4),
         "quant_us": round(med["quant"] * 1e6, 2),
         "quant_gbps": round(quant_bytes / med["quant"] / 1e9, 1),
         "roofline": roof,

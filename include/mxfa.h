@@ -133,6 +133,24 @@ int64_t mxfa_padded_token_rows(const int32_t* cu_seqlens_host, int nseq);
  *   lse: fp32 [H][T_q]; rows of a sequence with no keys get O = 0 and LSE = -inf. */
 mxfa_status mxfa_fwd(const mxfa_attn_args* a, uint16_t* o, float* lse, void* stream);
 
+/* How the forward scales each 32-key block of P before the E4M3 pack. */
+typedef enum {
+  MXFA_P_STATIC = 0,        /* 2^-8 on every block (code 119): P <= 1, so 1.0 maps to 256
+                               [BR item 4: constant scale because softmax output lies in [0, 1]] */
+  MXFA_P_BLOCK_DYNAMIC = 1  /* per (query row, 32-key block of the tile): the MX scale rule applied to
+                               the block's largest P, code = floor(log2 max P) - 8 + 127 clamped at 0,
+                               payload E4M3(P 2^(127-code)) saturated at 448; a block holding the row
+                               maximum gets code 119 [AE-TMEM: per-block scales from the block maximum,
+                               which the row-max pass of the online softmax already visits] */
+} mxfa_p_scale;
+
+/* Attention forward with a choice of P scale; mxfa_fwd(a, o, lse, s) is
+ * mxfa_fwd_p_scale(a, MXFA_P_STATIC, o, lse, s). The dynamic scale keeps small probabilities out of
+ * the E4M3 subnormal range (a block whose largest P is far below the row maximum gets a finer
+ * scale); the row sum l still adds the FP32 P. Same arguments, layouts and errors as mxfa_fwd;
+ * MXFA_ERR_INVALID for any other p_scale value. */
+mxfa_status mxfa_fwd_p_scale(const mxfa_attn_args* a, mxfa_p_scale p_scale, uint16_t* o, float* lse, void* stream);
+
 /* Workspace bytes mxfa_bwd needs for problem `a` (host struct; only nseq, max_seqlen_q/k, total_q and
  * num_heads are read): one 16 KB FP8 dS tile plus 16 bytes of block codes per (head, sequence,
  * 128-query tile, 128-key tile) of the longest sequences, i.e. H * nseq * ceil(max_q/128) *

@@ -12,8 +12,8 @@ import os
 import torch
 
 __all__ = [
-    "ROW32", "COL32", "SQ32", "DQ_FP32", "DQ_FP16_STATIC", "MxfaError",
-    "mxfa_quantize", "mxfa_varlen_scale_scatter", "mxfa_padded_token_rows", "mxfa_fwd", "mxfa_bwd",
+    "ROW32", "COL32", "SQ32", "DQ_FP32", "DQ_FP16_STATIC", "P_STATIC", "P_BLOCK_DYNAMIC", "MxfaError",
+    "mxfa_quantize", "mxfa_varlen_scale_scatter", "mxfa_padded_token_rows", "mxfa_fwd", "mxfa_fwd_p_scale", "mxfa_bwd",
     "mxfa_bwd_workspace_size", "mxfa_rmsnorm_quantize", "mxfa_linear_quantize", "mxfa_status_string",
     "mxfa_last_error_message", "MxOperand", "AttnArgs", "quantize", "scale_scatter", "fwd", "bwd",
     "rmsnorm_quantize", "linear_quantize",
@@ -22,6 +22,7 @@ __all__ = [
 
 ROW32, COL32, SQ32 = 0, 1, 2
 DQ_FP32, DQ_FP16_STATIC = 0, 1
+P_STATIC, P_BLOCK_DYNAMIC = 0, 1
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmxfa.so")
 _lib = None
@@ -62,6 +63,7 @@ def _load():
     lib.mxfa_padded_token_rows.argtypes = [P, i32]
     lib.mxfa_padded_token_rows.restype = i64
     lib.mxfa_fwd.argtypes = [ctypes.POINTER(_AttnArgs), P, P, P]
+    lib.mxfa_fwd_p_scale.argtypes = [ctypes.POINTER(_AttnArgs), i32, P, P, P]
     lib.mxfa_bwd_workspace_size.argtypes = [ctypes.POINTER(_AttnArgs), i32]
     lib.mxfa_bwd_workspace_size.restype = ctypes.c_size_t
     lib.mxfa_bwd.argtypes = [ctypes.POINTER(_AttnArgs), _Mx, _Mx, P, P, P, i32, f32, P, ctypes.c_size_t, P, P, P, P]
@@ -71,7 +73,8 @@ def _load():
     lib.mxfa_status_string.restype = ctypes.c_char_p
     lib.mxfa_last_error_message.argtypes = []
     lib.mxfa_last_error_message.restype = ctypes.c_char_p
-    for n in ("mxfa_quantize", "mxfa_varlen_scale_scatter", "mxfa_fwd", "mxfa_bwd", "mxfa_rmsnorm_quantize",
+    for n in ("mxfa_quantize", "mxfa_varlen_scale_scatter", "mxfa_fwd", "mxfa_fwd_p_scale", "mxfa_bwd",
+              "mxfa_rmsnorm_quantize",
               "mxfa_linear_quantize"):
         getattr(lib, n).restype = i32
     _lib = lib
@@ -166,6 +169,13 @@ def mxfa_fwd(args, o, lse, stream=None):
     _check(_load().mxfa_fwd(ctypes.byref(a), _ptr(o), _ptr(lse), _stream(stream)), "mxfa_fwd")
 
 
+def mxfa_fwd_p_scale(args, p_scale, o, lse, stream=None):
+    """p_scale: P_STATIC or P_BLOCK_DYNAMIC."""
+    a = args._c()
+    _check(_load().mxfa_fwd_p_scale(ctypes.byref(a), int(p_scale), _ptr(o), _ptr(lse), _stream(stream)),
+           "mxfa_fwd_p_scale")
+
+
 def mxfa_bwd_workspace_size(args, dq_mode):
     """args: AttnArgs (or the ctypes struct)."""
     a = args._c() if hasattr(args, "_c") else args
@@ -225,12 +235,15 @@ def scale_scatter(compact, cu_host, cu_dev, C, mode, stream=None):
     return out
 
 
-def fwd(args, stream=None):
+def fwd(args, stream=None, p_scale=P_STATIC):
     """Returns (o bf16 [T_q, H*D], lse fp32 [H, T_q])."""
     dev = args.q.data.device
     o = torch.empty((args.total_q, args.num_heads * args.head_dim), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((args.num_heads, args.total_q), dtype=torch.float32, device=dev)
-    mxfa_fwd(args, o, lse, stream)
+    if p_scale == P_STATIC:
+        mxfa_fwd(args, o, lse, stream)
+    else:
+        mxfa_fwd_p_scale(args, p_scale, o, lse, stream)
     return o, lse
 
 

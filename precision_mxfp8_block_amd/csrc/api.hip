@@ -171,14 +171,21 @@ mxfa_status mxfa_varlen_scale_scatter(const uint8_t* compact, const int32_t* cu_
 }
 
 mxfa_status mxfa_fwd(const mxfa_attn_args* a, uint16_t* o, float* lse, void* stream) {
-  const char* fn = "mxfa_fwd";
+  return mxfa_fwd_p_scale(a, MXFA_P_STATIC, o, lse, stream);
+}
+
+mxfa_status mxfa_fwd_p_scale(const mxfa_attn_args* a, mxfa_p_scale p_scale, uint16_t* o, float* lse, void* stream) {
+  const char* fn = p_scale == MXFA_P_STATIC ? "mxfa_fwd" : "mxfa_fwd_p_scale";
+  if (p_scale != MXFA_P_STATIC && p_scale != MXFA_P_BLOCK_DYNAMIC)
+    return fail(MXFA_ERR_INVALID, "%s: bad p_scale %d", fn, (int)p_scale);
   mxfa_status st = check_attn(a, fn);
   if (st != MXFA_OK) return st;
   if (a->v.mode != MXFA_COL32 && a->v.mode != MXFA_SQ32)
     return fail(MXFA_ERR_INVALID, "%s: v.mode must be COL32 or SQ32", fn);
   if (!o || !lse) return fail(MXFA_ERR_INVALID, "%s: NULL o/lse", fn);
   if (!aligned(o, 16) || !aligned(lse, 4)) return fail(MXFA_ERR_INVALID, "%s: o/lse misaligned", fn);
-  return hip_status(mxfa::launch_attn_fwd(to_problem(a), o, lse, (hipStream_t)stream), fn);
+  return hip_status(
+      mxfa::launch_attn_fwd(to_problem(a), p_scale == MXFA_P_BLOCK_DYNAMIC ? 1 : 0, o, lse, (hipStream_t)stream), fn);
 }
 
 size_t mxfa_bwd_workspace_size(const mxfa_attn_args* a, mxfa_dq_mode dq_mode) {

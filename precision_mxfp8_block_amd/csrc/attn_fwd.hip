@@ -148,7 +148,7 @@ __device__ __forceinline__ uint32_t undef_word() {
   return u;
 }
 
-template <bool VCOL32>
+template <bool VCOL32, bool PDYN>
 __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[kLdsBytes];
   MX_LDS uint8_t* const lds = (MX_LDS uint8_t*)lds_raw;
@@ -322,15 +322,16 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
   // computed by MFMAs issued in the middle and at the end of step t, into the registers that the
   // exponentials of tile t have just consumed, so the matrix cores work while this wave runs the
   // softmax:
-  //   1. mask, row max, base of the exponent (tile t's scores are complete)
-  //   2. rescale O and l where the row max moved (skipped, exactly, when none did)
-  //   3. P of key blocks 0-1 -> E4M3
+  //   1. mask, row max (and, with the dynamic P scale, the block maxima and codes), exponent
+  //      offsets (tile t's scores are complete)
+  //   2. P of key blocks 0-1 -> E4M3
+  //   3. rescale O and l where the row max moved (skipped, exactly, when none did)
   //   4. wait for the loads issued one step ago (K of t + 1, V of t, their scales), barrier; issue
   //      the loads of K of t + 2 and V of t + 1 into the stages of K of t and V of t - 1, which every
   //      wave has finished reading
-  //   5. O^T += V^T P^T for keys 0-63; scores of tile t + 1, key blocks 0-1
+  //   5. scores of tile t + 1, key blocks 0-1; O^T += V^T P^T for keys 0-63
   //   6. P of key blocks 2-3 -> E4M3 (while the MFMAs of 5 run)
-  //   7. scores of tile t + 1, key blocks 2-3; O^T += V^T P^T for keys 64-127
+  //   7. O^T += V^T P^T for keys 64-127; scores of tile t + 1, key blocks 2-3
   auto step = [&](int kt, auto stc) {
     constexpr int st = decltype(stc)::value;
     const int kv0 = kt * kTile;
@@ -348,29 +349,97 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
           sacc[kb][v] = keep_below(sacc[kb][v], 32 * kb + 8 * (v >> 2) + (v & 3), lim, -INFINITY);
     }
 
-    // online softmax (FP32): two independent max chains (key blocks 0-1 first: their MFMAs were
-    // issued first), joined at the end
-    float mx0 = m, mx1 = m;
-#pragma unroll
-    for (int v = 0; v < 16; v += 2) {
-      mx0 = max3f(mx0, sacc[0][v], sacc[0][v + 1]);
-      mx1 = max3f(mx1, sacc[1][v], sacc[1][v + 1]);
-    }
-#pragma unroll
-    for (int v = 0; v < 16; v += 2) {
-      mx0 = max3f(mx0, sacc[2][v], sacc[2][v + 1]);
-      mx1 = max3f(mx1, sacc[3][v], sacc[3][v + 1]);
-    }
+    // online softmax (FP32)
     float m_new;
-    {
+    float bmx[4];  // dynamic P scale: largest score of each 32-key block (both lane halves)
+    if constexpr (!PDYN) {
+      // two independent max chains (key blocks 0-1 first: their MFMAs were issued first), joined
+      // at the end
+      float mx0 = m, mx1 = m;
+#pragma unroll
+      for (int v = 0; v < 16; v += 2) {
+        mx0 = max3f(mx0, sacc[0][v], sacc[0][v + 1]);
+        mx1 = max3f(mx1, sacc[1][v], sacc[1][v + 1]);
+      }
+#pragma unroll
+      for (int v = 0; v < 16; v += 2) {
+        mx0 = max3f(mx0, sacc[2][v], sacc[2][v + 1]);
+        mx1 = max3f(mx1, sacc[3][v], sacc[3][v + 1]);
+      }
       const float mx = fmaxf(mx0, mx1);
       auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
       m_new = fmaxf(__uint_as_float(sw2[0]), __uint_as_float(sw2[1]));
+    } else {
+      // one chain per key block, each joined with the other lane half (which holds the block's
+      // other 16 keys); the row maximum is the largest block maximum
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        float x = max3f(sacc[kb][0], sacc[kb][1], sacc[kb][2]);
+#pragma unroll
+        for (int v = 3; v < 15; v += 2) x = max3f(x, sacc[kb][v], sacc[kb][v + 1]);
+        x = fmaxf(x, sacc[kb][15]);
+        auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        bmx[kb] = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      }
+      m_new = fmaxf(max3f(m, bmx[0], bmx[1]), fmaxf(bmx[2], bmx[3]));
     }
     const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
     const float base = m_use * p.c2 - 8.0f;  // exp2(S c2 - base) = 256 P
 
-    // ---- 2. ----
+    // Exponent offset of each key block: P_q = E4M3(exp2(S c2 - pbase)). Static scale: pbase =
+    // base for every block (256 P, code 119). Dynamic scale: the MX rule on the block's largest P,
+    // code = exponent field of max P - 8 (clamped at 0), so that P lands in [256, 512) relative to
+    // the block scale 2^(code - 127): pbase = base + code - 119. max P is taken as
+    // exp2((block max - m) c2), which is exactly 1 for the block holding the row maximum: going
+    // through base instead (exp2(block max c2 - base) / 256) would put it just below 1 whenever
+    // base rounds up, and give that block code 118 and a saturated largest element. The row sum
+    // collects each block's exponentials with the weight 2^(code - 119).
+    float pbase[4];
+    uint32_t pcode[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      if constexpr (PDYN) {
+        const float pmax = __builtin_amdgcn_exp2f((bmx[kb] - m_use) * p.c2);
+        const int code = max((int)(__float_as_uint(pmax) >> 23) - 8, 0);
+        pcode[kb] = (uint32_t)code;
+        pbase[kb] = base + (float)(code - 119);
+      } else {
+        pcode[kb] = 119u;
+        pbase[kb] = base;
+      }
+    }
+
+
+    // ---- 2. P = exp2(S c2 - pbase), packed to E4M3. Static scale: 256 P in [0, 256], no clamp
+    // needed. Dynamic scale: up to 512, saturated at 448 (the converter gives NaN beyond) ----
+    uint32_t pk[4][4];
+    float ps = 0.0f;
+    auto exp_pack = [&](int kb) {
+      float psk = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float e0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][4 * i + 0], p.c2, -pbase[kb]));
+        float e1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][4 * i + 1], p.c2, -pbase[kb]));
+        float e2 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][4 * i + 2], p.c2, -pbase[kb]));
+        float e3 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][4 * i + 3], p.c2, -pbase[kb]));
+        if constexpr (PDYN) {
+          psk += (e0 + e1) + (e2 + e3);
+          e0 = fminf(e0, 448.0f);
+          e1 = fminf(e1, 448.0f);
+          e2 = fminf(e2, 448.0f);
+          e3 = fminf(e3, 448.0f);
+        } else {
+          ps += (e0 + e1) + (e2 + e3);
+        }
+        pk[kb][i] = cvt2<true>(e2, e3, cvt2<false>(e0, e1, undef_word()));
+      }
+      if constexpr (PDYN) ps = fmaf(psk, __uint_as_float((pcode[kb] + 8u) << 23), ps);
+    };
+    exp_pack(0);
+    exp_pack(1);
+
+    // ---- 3. rescale O and l where the row max moved (skipped, exactly, when none did); after the
+    // exponentials so that the wait for the last PV products of the previous step is short ----
     if (__builtin_amdgcn_ballot_w64(m_new > m)) {
       const float alpha = __builtin_amdgcn_exp2f((m - m_use) * p.c2);
       lsum *= alpha;
@@ -380,23 +449,6 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
         for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
     }
     m = m_new;
-
-    // ---- 3. P = exp2(S c2 - base) = 256 P in [0, 256] (no clamp needed), packed to E4M3 ----
-    uint32_t pk[4][4];
-    float ps = 0.0f;
-    auto exp_pack = [&](int kb) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float e0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][4 * i + 0], p.c2, -base));
-        const float e1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][4 * i + 1], p.c2, -base));
-        const float e2 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][4 * i + 2], p.c2, -base));
-        const float e3 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][4 * i + 3], p.c2, -base));
-        ps += (e0 + e1) + (e2 + e3);
-        pk[kb][i] = cvt2<true>(e2, e3, cvt2<false>(e0, e1, undef_word()));
-      }
-    };
-    exp_pack(0);
-    exp_pack(1);
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- 4. loads of the next stages ----
@@ -427,6 +479,8 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
       return mx_v8i{part[0].x, part[0].y, part[1].x, part[1].y, part[2].x, part[2].y, part[3].x, part[3].y};
     };
     auto pv = [&](int ks) {
+      // P scale of this lane's K block: lane half hh supplies key block 2 ks + hh
+      const uint32_t psc = PDYN ? (hh ? pcode[2 * ks + 1] : pcode[2 * ks]) : 119u;
       const mx_v8i pb{(int)pk[2 * ks][0], (int)pk[2 * ks][1], (int)pk[2 * ks][2], (int)pk[2 * ks][3],
                       (int)pk[2 * ks + 1][0], (int)pk[2 * ks + 1][1], (int)pk[2 * ks + 1][2], (int)pk[2 * ks + 1][3]};
       mx_v8i va_next = read_v(ks, 0);
@@ -435,14 +489,14 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
         const uint32_t vsc = lds[vsc_off + st * 512 + 256 * ks + (VCOL32 ? 32 * db : db)];
         const mx_v8i va = va_next;
         if (db < 3) va_next = read_v(ks, db + 1);
-        oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, oacc[db], 0, 0, 0, (int)vsc, 0, 119);
+        oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, oacc[db], 0, 0, 0, (int)vsc, 0, (int)psc);
         asm volatile("" : "+v"(oacc[db])::"memory");
       }
     };
 
     // ---- 5. ----
-    pv(0);
     if (more) issue_s(Stage<st ^ 1>{}, KB0{}, KB2{});
+    pv(0);
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- 6. ----
@@ -453,8 +507,8 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- 7. ----
-    if (more) issue_s(Stage<st ^ 1>{}, KB2{}, KB4{});
     pv(1);
+    if (more) issue_s(Stage<st ^ 1>{}, KB2{}, KB4{});
   };
 
   // two tiles per iteration so that each stage's LDS addresses are compile-time offsets
@@ -489,7 +543,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
 
 namespace mxfa {
 
-hipError_t launch_attn_fwd(const AttnProblem& a, uint16_t* o, float* lse, hipStream_t stream) {
+hipError_t launch_attn_fwd(const AttnProblem& a, int p_dynamic, uint16_t* o, float* lse, hipStream_t stream) {
   FwdParams p;
   p.q = a.q.data; p.k = a.k.data; p.v = a.v.data;
   p.q_scale = a.q.scale; p.k_scale = a.k.scale; p.v_scale = a.v.scale;
@@ -505,10 +559,18 @@ hipError_t launch_attn_fwd(const AttnProblem& a, uint16_t* o, float* lse, hipStr
   p.causal = a.causal;
   p.o = o; p.lse = lse; p.Tq = a.total_q;
   if (p.total_items == 0) return hipSuccess;
-  if (p.v_col_shift == 0)
-    hipLaunchKernelGGL(attn_fwd_kernel<true>, dim3((unsigned)p.total_items), dim3(256), 0, stream, p);
-  else
-    hipLaunchKernelGGL(attn_fwd_kernel<false>, dim3((unsigned)p.total_items), dim3(256), 0, stream, p);
+  const dim3 grid((unsigned)p.total_items), block(256);
+  if (p.v_col_shift == 0) {
+    if (p_dynamic)
+      hipLaunchKernelGGL((attn_fwd_kernel<true, true>), grid, block, 0, stream, p);
+    else
+      hipLaunchKernelGGL((attn_fwd_kernel<true, false>), grid, block, 0, stream, p);
+  } else {
+    if (p_dynamic)
+      hipLaunchKernelGGL((attn_fwd_kernel<false, true>), grid, block, 0, stream, p);
+    else
+      hipLaunchKernelGGL((attn_fwd_kernel<false, false>), grid, block, 0, stream, p);
+  }
   return hipGetLastError();
 }
 

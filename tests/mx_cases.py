@@ -39,6 +39,11 @@ LSE_REL = 1e-3
 # method); every other workload uses the bounds above.
 O_OUTLIER_MAX_ABS, O_OUTLIER_REL_FRO = 6e-2, 1e-2
 GRAD_OUTLIER_REL_FRO = 8e-2
+# A peaked softmax (scores with standard deviation ~11) puts a row's weight on one or two keys. At an
+# E4M3 rounding midpoint the kernel's FP32 exp2 and the oracle's FP64 exp can round such a key's P
+# to neighbouring codes, and one E4M3 step is at most 1/8 of the value, so a single such key moves
+# O by up to max|V| / 8; the relative Frobenius bound stays O_REL_FRO.
+O_PEAKED_MAX_ABS = 1.0 / 8.0
 
 
 def say(msg):
@@ -81,7 +86,8 @@ def gpu_quantize_padded(x_dev, cu, cu_d, mode):
 class AttnCase:
     """Seeded attention problem: bf16 Q, K, V, dO [T, H*128], per-sequence lengths."""
 
-    def __init__(self, seed, lens_q, lens_k=None, H=1, causal=False, outlier_p=0.0, fwd_modes="train"):
+    def __init__(self, seed, lens_q, lens_k=None, H=1, causal=False, outlier_p=0.0, fwd_modes="train",
+                 softmax_scale=None):
         self.seed, self.H, self.D, self.causal = seed, H, 128, causal
         self.lens_q = list(lens_q)
         self.lens_k = list(lens_k if lens_k is not None else lens_q)
@@ -95,12 +101,12 @@ class AttnCase:
         self.k = synth.normal_bf16(seed, synth.STREAM_K, (self.Tk, C), **kw)
         self.v = synth.normal_bf16(seed, synth.STREAM_V, (self.Tk, C), **kw)
         self.do = synth.normal_bf16(seed, synth.STREAM_DO, (self.Tq, C), **kw)
-        self.c = float(np.float32(1.0 / math.sqrt(128)))
+        self.c = float(np.float32(1.0 / math.sqrt(128) if softmax_scale is None else softmax_scale))
         # operand modes: training (Q, K SQ32; V COL32 fwd, ROW32 bwd) or forward-only (Q, K ROW32)
         self.qk_mode = oracle.SQ32 if fwd_modes == "train" else oracle.ROW32
 
     # ---------------- GPU path ----------------
-    def run_gpu_fwd(self):
+    def run_gpu_fwd(self, p_scale=mx.P_STATIC):
         self.cu_q_d, self.cu_k_d = cu_dev(self.cu_q), cu_dev(self.cu_k)
         self.q_d, self.k_d = to_dev_bf16(self.q), to_dev_bf16(self.k)
         self.v_d, self.do_d = to_dev_bf16(self.v), to_dev_bf16(self.do)
@@ -112,7 +118,7 @@ class AttnCase:
                                 mx.MxOperand(self.gv[0], self.gv[1], mx.COL32),
                                 self.cu_q_d, self.cu_k_d, len(self.lens_q), max(self.lens_q), max(self.lens_k),
                                 self.Tq, self.Tk, self.H, 128, self.c, self.causal)
-        o, lse = mx.fwd(self.args)
+        o, lse = mx.fwd(self.args, p_scale=p_scale)
         torch.cuda.synchronize()
         self.o_dev, self.lse_dev = o, lse
         return to_host_bf16_bits(o), lse.cpu().numpy()
@@ -126,13 +132,13 @@ class AttnCase:
         return tuple(to_host_bf16_bits(t) for t in (dq, dk, dv))
 
     # ---------------- oracle ----------------
-    def run_oracle_fwd(self):
+    def run_oracle_fwd(self, p_scale=oracle.P_STATIC):
         self.oq = oracle.quantize(self.q, self.cu_q, self.qk_mode)
         self.ok = oracle.quantize(self.k, self.cu_k, self.qk_mode)
         self.ov = oracle.quantize(self.v, self.cu_k, oracle.COL32)
         o16, o32, lse = oracle.attn_fwd_mx(self.oq[0], self.oq[1], self.qk_mode, self.ok[0], self.ok[1], self.qk_mode,
                                            self.ov[0], self.ov[1], oracle.COL32, self.cu_q, self.cu_k, self.H, 128,
-                                           self.c, self.causal)
+                                           self.c, self.causal, p_scale=p_scale)
         self.o16_ref, self.lse_ref = o16, lse
         return o16, o32, lse
 
@@ -145,7 +151,7 @@ class AttnCase:
                                   128, self.c, self.causal, dq_mode, sigma)
 
 
-def check_o(o_gpu_bits, o_ref32, lse_gpu, lse_ref, label="", qk_outliers_full_length=False):
+def check_o(o_gpu_bits, o_ref32, lse_gpu, lse_ref, label="", qk_outliers_full_length=False, peaked=False):
     o = bf16_bits_to_f64(o_gpu_bits)
     ref = np.asarray(o_ref32, np.float64)
     max_abs = float(np.max(np.abs(o - ref))) if o.size else 0.0
@@ -157,6 +163,8 @@ def check_o(o_gpu_bits, o_ref32, lse_gpu, lse_ref, label="", qk_outliers_full_le
     say(f"  {label} O max_abs={max_abs:.3e} (scale {scale:.3g}) rel_fro={fro:.3e} lse_rel={lse_err:.3e}")
     assert np.all(np.isfinite(o)), "non-finite O"
     tol_abs, tol_fro = (O_OUTLIER_MAX_ABS, O_OUTLIER_REL_FRO) if qk_outliers_full_length else (O_MAX_ABS, O_REL_FRO)
+    if peaked:
+        tol_abs = O_PEAKED_MAX_ABS
     assert max_abs <= tol_abs * scale and fro <= tol_fro, (max_abs, scale, fro)
     assert lse_err <= LSE_REL, lse_err
     assert np.all(np.isneginf(lse_gpu[~fin])), "rows without keys must have LSE = -inf"

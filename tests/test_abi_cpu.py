@@ -26,7 +26,8 @@ def _declared_functions():
 
 def test_header_declares_the_abi():
     names = _declared_functions()
-    for n in ["mxfa_quantize", "mxfa_fwd", "mxfa_bwd", "mxfa_varlen_scale_scatter", "mxfa_rmsnorm_quantize",
+    for n in ["mxfa_quantize", "mxfa_fwd", "mxfa_fwd_p_scale", "mxfa_bwd", "mxfa_varlen_scale_scatter",
+              "mxfa_rmsnorm_quantize",
               "mxfa_linear_quantize",
               "mxfa_bwd_workspace_size", "mxfa_status_string", "mxfa_last_error_message"]:
         assert n in names
@@ -101,6 +102,20 @@ def test_fwd_null_outputs():
     a = _args()
     assert _lib().mxfa_fwd(ctypes.byref(a), 0, P, 0) == INVALID
     assert _lib().mxfa_fwd(None, P, P, 0) == INVALID
+
+
+@pytest.mark.parametrize("p_scale", [-1, 2, 7])
+def test_fwd_p_scale_rejects_unknown_mode(p_scale):
+    a = _args()
+    assert _lib().mxfa_fwd_p_scale(ctypes.byref(a), p_scale, P, P, 0) == INVALID
+    assert "p_scale" in _last()
+
+
+@pytest.mark.parametrize("kw", [dict(H=0), dict(v=(P, P, 0)), dict(scale=float("inf"))])
+def test_fwd_p_scale_checks_the_problem_like_fwd(kw):
+    a = _args(**kw)
+    for mode in (mx.P_STATIC, mx.P_BLOCK_DYNAMIC):
+        assert _lib().mxfa_fwd_p_scale(ctypes.byref(a), mode, P, P, 0) == INVALID
 
 
 @pytest.mark.parametrize("kw,expect", [

@@ -12,7 +12,7 @@ import torch
 import oracle
 import precision_mxfp8_block_amd as mx
 import synth
-from mx_cases import AttnCase, LinearCase, certify_linear, check_grads, check_o, cu_dev, say, to_dev_bf16
+from mx_cases import AttnCase, LinearCase, certify_linear, check_grads, check_o, cu_dev, rel_fro, say, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -163,6 +163,37 @@ def test_fwd_parity(case):
     o_gpu, lse_gpu = c.run_gpu_fwd()
     _, o32, lse = c.run_oracle_fwd()
     check_o(o_gpu, o32, lse_gpu, lse, label)
+
+
+@pytest.mark.parametrize("case", FWD_CASES, ids=[c[0] for c in FWD_CASES])
+def test_fwd_parity_dynamic_p(case):
+    """The per-block dynamic P scale against the oracle's dynamic mode on the same cases."""
+    label, seed, lq, lk, H, causal, op, modes = case
+    say(f"fwd dynamic P {label}")
+    c = AttnCase(seed, lq, lk, H=H, causal=causal, outlier_p=op, fwd_modes=modes)
+    o_gpu, lse_gpu = c.run_gpu_fwd(mx.P_BLOCK_DYNAMIC)
+    _, o32, lse = c.run_oracle_fwd(oracle.P_DYNAMIC)
+    check_o(o_gpu, o32, lse_gpu, lse, label)
+
+
+def test_fwd_dynamic_p_peaky_softmax():
+    """Softmax scale 1 (scores with standard deviation ~11): most 32-key blocks lie far below their
+    row maximum, so their codes drop below 119 and, at the static scale, their P would fall among
+    E4M3 subnormals or to zero. Both P scales must match the oracle's corresponding mode (under the
+    peaked-softmax bound), and the dynamic scale must change the result."""
+    say("fwd dynamic P peaky softmax")
+    c = AttnCase(21, [384, 200, 640], None, H=2, fwd_modes="train", softmax_scale=1.0)
+    o_sta, lse_sta = c.run_gpu_fwd(mx.P_STATIC)
+    _, o32, lse = c.run_oracle_fwd(oracle.P_STATIC)
+    check_o(o_sta, o32, lse_sta, lse, "peaky_static", peaked=True)
+    o_dyn, lse_dyn = c.run_gpu_fwd(mx.P_BLOCK_DYNAMIC)
+    _, o32, lse = c.run_oracle_fwd(oracle.P_DYNAMIC)
+    check_o(o_dyn, o32, lse_dyn, lse, "peaky_dynamic", peaked=True)
+    assert np.any(o_dyn != o_sta)
+    _, o_exact, _ = c.run_oracle_fwd(oracle.P_NONE)
+    err_dyn = rel_fro(synth.bf16_bits_to_f32(o_dyn), o_exact)
+    err_sta = rel_fro(synth.bf16_bits_to_f32(o_sta), o_exact)
+    say(f"  rel_fro vs unquantized P: dynamic {err_dyn:.3e}, static {err_sta:.3e}")
 
 
 def test_fwd_empty_key_sequence():
