@@ -71,7 +71,7 @@ class FullAttn:
         self.dev = {n: to_dev_bf16(a) for n, a in self.x.items()}
         self.cu_q_d, self.cu_k_d = cu_dev(self.cu_q), cu_dev(self.cu_k)
 
-    def gpu_fwd(self):
+    def gpu_fwd(self, p_scale=mx.P_STATIC):
         self.gq = gpu_quantize_padded(self.dev["q"], self.cu_q, self.cu_q_d, self.qk_mode)
         self.gk = gpu_quantize_padded(self.dev["k"], self.cu_k, self.cu_k_d, self.qk_mode)
         self.gv = gpu_quantize_padded(self.dev["v"], self.cu_k, self.cu_k_d, mx.COL32)
@@ -80,7 +80,7 @@ class FullAttn:
                                 mx.MxOperand(self.gv[0], self.gv[1], mx.COL32),
                                 self.cu_q_d, self.cu_k_d, len(self.lens_q), max(self.lens_q), max(self.lens_k),
                                 self.Tq, self.Tk, self.H, D, C_SCALE, self.causal)
-        self.o, self.lse = mx.fwd(self.args)
+        self.o, self.lse = mx.fwd(self.args, p_scale=p_scale)
         torch.cuda.synchronize()
 
     def gpu_bwd(self, dq_mode, sigma):
@@ -102,7 +102,7 @@ class FullAttn:
         np.testing.assert_array_equal(host(gpu[0][rows, h * D:(h + 1) * D]), ref[0], err_msg=f"{name} payload")
         np.testing.assert_array_equal(scale_slice(host(gpu[2]), mode, cu, boff, s, h), ref[1], err_msg=f"{name} scale")
 
-    def oracle_fwd_slice(self, s, h):
+    def oracle_fwd_slice(self, s, h, p_scale=oracle.P_STATIC):
         Lq, Lk = self.lens_q[s], self.lens_k[s]
         cq, ck = np.array([0, Lq], np.int32), np.array([0, Lk], np.int32)
         self.rq = oracle.quantize(self._xs("q", s, h), cq, self.qk_mode)
@@ -112,7 +112,8 @@ class FullAttn:
         self._check_quant("k", self.gk, self.qk_mode, s, h, self.rk)
         self._check_quant("v", self.gv, mx.COL32, s, h, rv)
         o16, o32, lse = oracle.attn_fwd_mx(self.rq[0], self.rq[1], self.qk_mode, self.rk[0], self.rk[1], self.qk_mode,
-                                           rv[0], rv[1], oracle.COL32, cq, ck, 1, D, C_SCALE, self.causal)
+                                           rv[0], rv[1], oracle.COL32, cq, ck, 1, D, C_SCALE, self.causal,
+                                           p_scale=p_scale)
         rows = slice(int(self.cu_q[s]), int(self.cu_q[s + 1]))
         o_g = to_host_bf16_bits(self.o[rows, h * D:(h + 1) * D])
         lse_g = host(self.lse[h, rows])[None, :]
@@ -154,6 +155,15 @@ def test_training_step_B4_H16_N4096(dq_mode, sigma):
     for s, h in [(0, 0), (2, 11)]:
         o16, lse = fa.oracle_fwd_slice(s, h)
         fa.oracle_bwd_slice(s, h, o16, lse, g, dq_mode, sigma)
+
+
+def test_training_forward_dynamic_p_B4_H16_N4096():
+    """The forward with the dynamic per-block P scale, as the benchmark times it (training modes)."""
+    say("full-size forward, dynamic P scale: B=4 H=16 N=4096, Q/K SQ32, V COL32")
+    fa = FullAttn(2, [4096] * 4, [4096] * 4, 16)
+    fa.gpu_fwd(mx.P_BLOCK_DYNAMIC)
+    for s, h in [(0, 3), (3, 14)]:
+        fa.oracle_fwd_slice(s, h, oracle.P_DYNAMIC)
 
 
 def test_causal_outliers_B4_H16_N8192():
