@@ -370,6 +370,19 @@ def main():
     torch.cuda.synchronize()
     fwd_dyn_s = float(np.median([e[0].elapsed_time(e[1]) * 1e-3 for e in edyn]))
 
+    # the forward writing O as MXFP8 only (ROW32 blocks along D, for the next projection)
+    emx = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n32)]
+    o_mxd = torch.empty((T, C), dtype=torch.uint8, device=o.device)
+    o_mxs = torch.empty((T, C // 32), dtype=torch.uint8, device=o.device)
+    for i in range(n32 + 1):
+        if i:
+            emx[i - 1][0].record(stream)
+        mx.mxfa_fwd_mx_out(attn, mx.P_STATIC, None, o_mxd, o_mxs, lse_dyn, stream)
+        if i:
+            emx[i - 1][1].record(stream)
+    torch.cuda.synchronize()
+    fwd_mx_s = float(np.median([e[0].elapsed_time(e[1]) * 1e-3 for e in emx]))
+
     times = {n: [e[0].elapsed_time(e[1]) * 1e-3 for e in ev[n]] for n in names}
     med = {n: float(np.median(v)) for n, v in times.items()}
     f_fwd = 4.0 * N * N * D * B * H
@@ -399,6 +412,7 @@ def main():
         "fwd_us": round(med["fwd"] * 1e6, 2), "bwd_us": round(med["bwd"] * 1e6, 2),
         "bwd_fp32dq_us": round(bwd32_s * 1e6, 2), "bwd_fp32dq_pflops": round(f_bwd / bwd32_s / 1e15, 4),
         "fwd_dynamic_p_us": round(fwd_dyn_s * 1e6, 2), "fwd_dynamic_p_pflops": round(f_fwd / fwd_dyn_s / 1e15, 4),
+        "fwd_mx_out_us": round(fwd_mx_s * 1e6, 2), "fwd_mx_out_pflops": round(f_fwd / fwd_mx_s / 1e15, 4),
         "quant_us": round(med["quant"] * 1e6, 2),
         "quant_gbps": round(quant_bytes / med["quant"] / 1e9, 1),
         "roofline": roof,

@@ -151,6 +151,18 @@ typedef enum {
  * MXFA_ERR_INVALID for any other p_scale value. */
 mxfa_status mxfa_fwd_p_scale(const mxfa_attn_args* a, mxfa_p_scale p_scale, uint16_t* o, float* lse, void* stream);
 
+/* Attention forward with O written as MXFP8 for the next projection [AE-TMEM: FP8 outputs with their
+ * scales, quantized in the epilogue of the kernel that produces them; TC paragraph 3: scales along the
+ * next GEMM's contraction dimension, here D]. O = O_acc / l in FP32 is quantized in ROW32 blocks
+ * (32 of D per token and head) by the rule of mxfa_quantize; bf16 O can be written in the same pass
+ * (the backward needs it for Delta).
+ *   o       : bf16 [T_q, H*D], or NULL to skip it
+ *   o_data  : E4M3 [T_q, H*D], 4-byte aligned, or NULL to skip it (not both NULL)
+ *   o_scale : E8M0 [T_q, H*D/32] (the ROW32 layout of mxfa_quantize), 4-byte aligned; required with o_data
+ *   p_scale, lse, stream: as mxfa_fwd_p_scale. Same problem checks and errors as mxfa_fwd. */
+mxfa_status mxfa_fwd_mx_out(const mxfa_attn_args* a, mxfa_p_scale p_scale, uint16_t* o, uint8_t* o_data,
+                            uint8_t* o_scale, float* lse, void* stream);
+
 /* Workspace bytes mxfa_bwd needs for problem `a` (host struct; only nseq, max_seqlen_q/k, total_q and
  * num_heads are read): one 16 KB FP8 dS tile plus 16 bytes of block codes per (head, sequence,
  * 128-query tile, 128-key tile) of the longest sequences, i.e. H * nseq * ceil(max_q/128) *

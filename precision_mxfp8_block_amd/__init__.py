@@ -13,7 +13,8 @@ import torch
 
 __all__ = [
     "ROW32", "COL32", "SQ32", "DQ_FP32", "DQ_FP16_STATIC", "P_STATIC", "P_BLOCK_DYNAMIC", "MxfaError",
-    "mxfa_quantize", "mxfa_varlen_scale_scatter", "mxfa_padded_token_rows", "mxfa_fwd", "mxfa_fwd_p_scale", "mxfa_bwd",
+    "mxfa_quantize", "mxfa_varlen_scale_scatter", "mxfa_padded_token_rows", "mxfa_fwd", "mxfa_fwd_p_scale",
+    "mxfa_fwd_mx_out", "mxfa_bwd", "fwd_mx_out",
     "mxfa_bwd_workspace_size", "mxfa_rmsnorm_quantize", "mxfa_linear_quantize", "mxfa_status_string",
     "mxfa_last_error_message", "MxOperand", "AttnArgs", "quantize", "scale_scatter", "fwd", "bwd",
     "rmsnorm_quantize", "linear_quantize",
@@ -64,6 +65,7 @@ def _load():
     lib.mxfa_padded_token_rows.restype = i64
     lib.mxfa_fwd.argtypes = [ctypes.POINTER(_AttnArgs), P, P, P]
     lib.mxfa_fwd_p_scale.argtypes = [ctypes.POINTER(_AttnArgs), i32, P, P, P]
+    lib.mxfa_fwd_mx_out.argtypes = [ctypes.POINTER(_AttnArgs), i32, P, P, P, P, P]
     lib.mxfa_bwd_workspace_size.argtypes = [ctypes.POINTER(_AttnArgs), i32]
     lib.mxfa_bwd_workspace_size.restype = ctypes.c_size_t
     lib.mxfa_bwd.argtypes = [ctypes.POINTER(_AttnArgs), _Mx, _Mx, P, P, P, i32, f32, P, ctypes.c_size_t, P, P, P, P]
@@ -73,7 +75,7 @@ def _load():
     lib.mxfa_status_string.restype = ctypes.c_char_p
     lib.mxfa_last_error_message.argtypes = []
     lib.mxfa_last_error_message.restype = ctypes.c_char_p
-    for n in ("mxfa_quantize", "mxfa_varlen_scale_scatter", "mxfa_fwd", "mxfa_fwd_p_scale", "mxfa_bwd",
+    for n in ("mxfa_quantize", "mxfa_varlen_scale_scatter", "mxfa_fwd", "mxfa_fwd_p_scale", "mxfa_fwd_mx_out", "mxfa_bwd",
               "mxfa_rmsnorm_quantize",
               "mxfa_linear_quantize"):
         getattr(lib, n).restype = i32
@@ -176,6 +178,13 @@ def mxfa_fwd_p_scale(args, p_scale, o, lse, stream=None):
            "mxfa_fwd_p_scale")
 
 
+def mxfa_fwd_mx_out(args, p_scale, o, o_data, o_scale, lse, stream=None):
+    """o (bf16) and o_data (E4M3, ROW32 codes in o_scale) may each be None, not both."""
+    a = args._c()
+    _check(_load().mxfa_fwd_mx_out(ctypes.byref(a), int(p_scale), _ptr(o), _ptr(o_data), _ptr(o_scale), _ptr(lse),
+                                   _stream(stream)), "mxfa_fwd_mx_out")
+
+
 def mxfa_bwd_workspace_size(args, dq_mode):
     """args: AttnArgs (or the ctypes struct)."""
     a = args._c() if hasattr(args, "_c") else args
@@ -233,6 +242,19 @@ def scale_scatter(compact, cu_host, cu_dev, C, mode, stream=None):
     out = torch.empty((rows, width), dtype=torch.uint8, device=compact.device)
     mxfa_varlen_scale_scatter(compact, cu_dev, len(lens), max(lens) if lens else 0, C, mode, out, rows, stream)
     return out
+
+
+def fwd_mx_out(args, stream=None, p_scale=P_STATIC, with_bf16=True):
+    """Forward writing O as MXFP8 (ROW32 blocks along D). Returns (o bf16 or None, o_data u8 [T_q, H*D],
+    o_scale u8 [T_q, H*D/32], lse fp32 [H, T_q])."""
+    dev = args.q.data.device
+    C = args.num_heads * args.head_dim
+    o = torch.empty((args.total_q, C), dtype=torch.bfloat16, device=dev) if with_bf16 else None
+    o_data = torch.empty((args.total_q, C), dtype=torch.uint8, device=dev)
+    o_scale = torch.empty((args.total_q, C // 32), dtype=torch.uint8, device=dev)
+    lse = torch.empty((args.num_heads, args.total_q), dtype=torch.float32, device=dev)
+    mxfa_fwd_mx_out(args, p_scale, o, o_data, o_scale, lse, stream)
+    return o, o_data, o_scale, lse
 
 
 def fwd(args, stream=None, p_scale=P_STATIC):

@@ -175,17 +175,27 @@ mxfa_status mxfa_fwd(const mxfa_attn_args* a, uint16_t* o, float* lse, void* str
 }
 
 mxfa_status mxfa_fwd_p_scale(const mxfa_attn_args* a, mxfa_p_scale p_scale, uint16_t* o, float* lse, void* stream) {
-  const char* fn = p_scale == MXFA_P_STATIC ? "mxfa_fwd" : "mxfa_fwd_p_scale";
+  if (!o) return fail(MXFA_ERR_INVALID, "%s: NULL o", p_scale == MXFA_P_STATIC ? "mxfa_fwd" : "mxfa_fwd_p_scale");
+  return mxfa_fwd_mx_out(a, p_scale, o, nullptr, nullptr, lse, stream);
+}
+
+mxfa_status mxfa_fwd_mx_out(const mxfa_attn_args* a, mxfa_p_scale p_scale, uint16_t* o, uint8_t* o_data,
+                            uint8_t* o_scale, float* lse, void* stream) {
+  const char* fn = o_data ? "mxfa_fwd_mx_out" : p_scale == MXFA_P_STATIC ? "mxfa_fwd" : "mxfa_fwd_p_scale";
   if (p_scale != MXFA_P_STATIC && p_scale != MXFA_P_BLOCK_DYNAMIC)
     return fail(MXFA_ERR_INVALID, "%s: bad p_scale %d", fn, (int)p_scale);
   mxfa_status st = check_attn(a, fn);
   if (st != MXFA_OK) return st;
   if (a->v.mode != MXFA_COL32 && a->v.mode != MXFA_SQ32)
     return fail(MXFA_ERR_INVALID, "%s: v.mode must be COL32 or SQ32", fn);
-  if (!o || !lse) return fail(MXFA_ERR_INVALID, "%s: NULL o/lse", fn);
-  if (!aligned(o, 16) || !aligned(lse, 4)) return fail(MXFA_ERR_INVALID, "%s: o/lse misaligned", fn);
-  return hip_status(
-      mxfa::launch_attn_fwd(to_problem(a), p_scale == MXFA_P_BLOCK_DYNAMIC ? 1 : 0, o, lse, (hipStream_t)stream), fn);
+  if (!lse) return fail(MXFA_ERR_INVALID, "%s: NULL lse", fn);
+  if (!o && !o_data) return fail(MXFA_ERR_INVALID, "%s: neither o nor o_data given", fn);
+  if (o_data && !o_scale) return fail(MXFA_ERR_INVALID, "%s: o_data without o_scale", fn);
+  if ((o && !aligned(o, 16)) || !aligned(lse, 4) || (o_data && (!aligned(o_data, 4) || !aligned(o_scale, 4))))
+    return fail(MXFA_ERR_INVALID, "%s: misaligned output", fn);
+  return hip_status(mxfa::launch_attn_fwd(to_problem(a), p_scale == MXFA_P_BLOCK_DYNAMIC ? 1 : 0, o, o_data,
+                                          o_data ? o_scale : nullptr, lse, (hipStream_t)stream),
+                    fn);
 }
 
 size_t mxfa_bwd_workspace_size(const mxfa_attn_args* a, mxfa_dq_mode dq_mode) {

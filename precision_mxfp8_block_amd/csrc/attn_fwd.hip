@@ -51,7 +51,9 @@ struct FwdParams {
   float c;   // softmax scale
   float c2;  // softmax scale * log2(e)
   int causal;
-  uint16_t* o;
+  uint16_t* o;          // bf16 O, or null
+  uint8_t* o_mx;        // E4M3 O in ROW32 blocks (32 of D per token and head), or null
+  uint8_t* o_mx_scale;  // its E8M0 codes [T_q][H*D/32]
   float* lse;
   int64_t Tq;
 };
@@ -523,18 +525,52 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
     lsum = __uint_as_float(sw2[0]) + __uint_as_float(sw2[1]);
   }
   const float l = lsum * (1.0f / 256.0f);
+  const float inv_l = l > 0.0f ? 1.0f / l : 0.0f;
+  // MX output: O = O_acc / l in FP32, quantized in ROW32 blocks (the MX scale rule of the operand
+  // quantizer). Lane (r, hh) holds 16 of block db's 32 values (d = 32 db + 8 i + 4 hh + j), the
+  // other lane half the other 16, so the block maximum is joined across the halves. Every lane
+  // runs this part (the swap reads the partner lane); only rows inside the sequence store.
+  uint32_t mx_words[4][4];
+  uint32_t mx_codes = 0;
+  if (p.o_mx) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      uint32_t amax = 0;  // largest sign-cleared bit pattern: orders NaN > Inf > finite magnitudes
+#pragma unroll
+      for (int v = 0; v < 16; ++v) amax = max(amax, __float_as_uint(oacc[db][v] * inv_l) & 0x7fffffffu);
+      const auto sw = __builtin_amdgcn_permlane32_swap(amax, amax, false, false);
+      amax = max((uint32_t)sw[0], (uint32_t)sw[1]);
+      const uint32_t code = mx_code_from_amax_bits(amax);
+      mx_codes |= code << (8 * db);
+      const float inv = mx_inv_scale(code == 255u ? 127u : code);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        mx_words[db][i] = code == 255u ? 0x7f7f7f7fu
+                                       : mx_pack4(oacc[db][4 * i + 0] * inv_l * inv, oacc[db][4 * i + 1] * inv_l * inv,
+                                                  oacc[db][4 * i + 2] * inv_l * inv, oacc[db][4 * i + 3] * inv_l * inv);
+    }
+  }
   if (qrow < Lq) {
-    const float inv_l = l > 0.0f ? 1.0f / l : 0.0f;
-    uint16_t* dst = p.o + (q_start + qrow) * (int64_t)C + h * kD;
+    if (p.o) {
+      uint16_t* dst = p.o + (q_start + qrow) * (int64_t)C + h * kD;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int d = 32 * db + 8 * i + 4 * hh;
-        uint32_t w0 = f32_to_bf16(oacc[db][4 * i + 0] * inv_l) | (f32_to_bf16(oacc[db][4 * i + 1] * inv_l) << 16);
-        uint32_t w1 = f32_to_bf16(oacc[db][4 * i + 2] * inv_l) | (f32_to_bf16(oacc[db][4 * i + 3] * inv_l) << 16);
-        *reinterpret_cast<uint2*>(dst + d) = make_uint2(w0, w1);
-      }
+        for (int i = 0; i < 4; ++i) {
+          const int d = 32 * db + 8 * i + 4 * hh;
+          uint32_t w0 = f32_to_bf16(oacc[db][4 * i + 0] * inv_l) | (f32_to_bf16(oacc[db][4 * i + 1] * inv_l) << 16);
+          uint32_t w1 = f32_to_bf16(oacc[db][4 * i + 2] * inv_l) | (f32_to_bf16(oacc[db][4 * i + 3] * inv_l) << 16);
+          *reinterpret_cast<uint2*>(dst + d) = make_uint2(w0, w1);
+        }
+    }
+    if (p.o_mx) {
+      uint8_t* dst = p.o_mx + (q_start + qrow) * (int64_t)C + h * kD;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *reinterpret_cast<uint32_t*>(dst + 32 * db + 8 * i + 4 * hh) = mx_words[db][i];
+      if (hh == 0) *reinterpret_cast<uint32_t*>(p.o_mx_scale + (q_start + qrow) * (int64_t)Cs + h * 4) = mx_codes;
+    }
     if (hh == 0) p.lse[(int64_t)h * p.Tq + q_start + qrow] = l > 0.0f ? m * p.c + logf(l) : -INFINITY;
   }
 }
@@ -543,7 +579,8 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
 
 namespace mxfa {
 
-hipError_t launch_attn_fwd(const AttnProblem& a, int p_dynamic, uint16_t* o, float* lse, hipStream_t stream) {
+hipError_t launch_attn_fwd(const AttnProblem& a, int p_dynamic, uint16_t* o, uint8_t* o_mx, uint8_t* o_mx_scale,
+                           float* lse, hipStream_t stream) {
   FwdParams p;
   p.q = a.q.data; p.k = a.k.data; p.v = a.v.data;
   p.q_scale = a.q.scale; p.k_scale = a.k.scale; p.v_scale = a.v.scale;
@@ -557,7 +594,7 @@ hipError_t launch_attn_fwd(const AttnProblem& a, int p_dynamic, uint16_t* o, flo
   p.c = a.softmax_scale;
   p.c2 = a.softmax_scale * kLog2e;
   p.causal = a.causal;
-  p.o = o; p.lse = lse; p.Tq = a.total_q;
+  p.o = o; p.o_mx = o_mx; p.o_mx_scale = o_mx_scale; p.lse = lse; p.Tq = a.total_q;
   if (p.total_items == 0) return hipSuccess;
   const dim3 grid((unsigned)p.total_items), block(256);
   if (p.v_col_shift == 0) {

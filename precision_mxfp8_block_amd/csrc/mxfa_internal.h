@@ -34,7 +34,9 @@ hipError_t launch_rmsnorm_quantize(const uint16_t* x, int64_t ld_x, int C, const
 hipError_t launch_linear_quantize(const MxOperand& x, const MxOperand& w, int64_t T, int C_in, int C_out,
                                   const int32_t* cu, int nseq, int max_seqlen, uint8_t* data, uint8_t* scale,
                                   uint8_t* scale_t, hipStream_t stream);
-hipError_t launch_attn_fwd(const AttnProblem& a, int p_dynamic, uint16_t* o, float* lse, hipStream_t stream);
+// o and o_mx may each be null (not both): bf16 O and/or E4M3 O in ROW32 blocks with its codes.
+hipError_t launch_attn_fwd(const AttnProblem& a, int p_dynamic, uint16_t* o, uint8_t* o_mx, uint8_t* o_mx_scale,
+                           float* lse, hipStream_t stream);
 size_t bwd_workspace_bytes(int64_t Tq, int H, int nseq, int max_q, int max_k);
 hipError_t launch_attn_bwd(const AttnProblem& a, const MxOperand& v_d, const MxOperand& dout, const uint16_t* o,
                            const uint16_t* dout_bf16, const float* lse, int dq_fp16, float sigma, void* workspace,

@@ -111,6 +111,20 @@ def test_fwd_p_scale_rejects_unknown_mode(p_scale):
     assert "p_scale" in _last()
 
 
+@pytest.mark.parametrize("o,o_data,o_scale,lse", [
+    (0, 0, 0, P),         # neither output
+    (0, P, 0, P),         # MX payload without its scales
+    (P, P + 2, P, P),     # payload not 4-byte aligned
+    (0, P, P + 1, P),     # scales not 4-byte aligned
+    (P + 8, 0, 0, P),     # bf16 O not 16-byte aligned
+    (P, P, P, 0),         # no LSE
+])
+def test_fwd_mx_out_argument_errors(o, o_data, o_scale, lse):
+    a = _args()
+    assert _lib().mxfa_fwd_mx_out(ctypes.byref(a), mx.P_STATIC, o, o_data, o_scale, lse, 0) == INVALID
+    assert _last() != ""
+
+
 @pytest.mark.parametrize("kw", [dict(H=0), dict(v=(P, P, 0)), dict(scale=float("inf"))])
 def test_fwd_p_scale_checks_the_problem_like_fwd(kw):
     a = _args(**kw)

@@ -12,7 +12,8 @@ import torch
 import oracle
 import precision_mxfp8_block_amd as mx
 import synth
-from mx_cases import AttnCase, LinearCase, certify_linear, check_grads, check_o, cu_dev, rel_fro, say, to_dev_bf16
+from mx_cases import (O_MAX_ABS, O_REL_FRO, AttnCase, LinearCase, certify_linear, check_grads, check_o, cu_dev,
+                      rel_fro, say, to_dev_bf16)
 
 pytestmark = pytest.mark.gpu
 
@@ -194,6 +195,60 @@ def test_fwd_dynamic_p_peaky_softmax():
     err_dyn = rel_fro(synth.bf16_bits_to_f32(o_dyn), o_exact)
     err_sta = rel_fro(synth.bf16_bits_to_f32(o_sta), o_exact)
     say(f"  rel_fro vs unquantized P: dynamic {err_dyn:.3e}, static {err_sta:.3e}")
+
+
+MX_OUT_CASES = [FWD_CASES[i] for i in (0, 2, 3, 4, 5)]
+
+
+@pytest.mark.parametrize("case", MX_OUT_CASES, ids=[c[0] for c in MX_OUT_CASES])
+def test_fwd_mx_out_parity(case):
+    """O written as MXFP8 (ROW32 blocks along D) in the forward's epilogue.
+    * Against the GPU's own O (the bf16 O written in the same pass, within 2^-8 relative of the FP32 O
+      that was quantized): every block code is the MX rule's code of a value within 2^-8 of the block's
+      bf16 maximum, and every dequantized value is within one E4M3 step of the block's top binade
+      (amax / 8, saturation included) plus the bf16 rounding.
+    * Against the oracle (its FP32 O, which differs from the GPU's by the attention tolerance): the
+      dequantized output is within the O tolerance plus amax / 8, and within 2^-4 + the O tolerance in
+      relative Frobenius norm; the fractions of equal codes and bytes with the oracle's quantization
+      of its own O are printed.
+    * The bf16 O written in the same pass equals mxfa_fwd's bit for bit, and O_data does not depend on
+      whether bf16 O is written."""
+    label, seed, lq, lk, H, causal, op, modes = case
+    say(f"fwd MX O {label}")
+    c = AttnCase(seed, lq, lk, H=H, causal=causal, outlier_p=op, fwd_modes=modes)
+    o_bits, lse_g = c.run_gpu_fwd()
+    o16, od, osc, lse2 = mx.fwd_mx_out(c.args)
+    _, od_only, osc_only, _ = mx.fwd_mx_out(c.args, with_bf16=False)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(o16.view(torch.int16).cpu().numpy().view(np.uint16), o_bits)
+    np.testing.assert_array_equal(lse2.cpu().numpy(), lse_g)
+    gd, gs = od.cpu().numpy(), osc.cpu().numpy()
+    np.testing.assert_array_equal(od_only.cpu().numpy(), gd)
+    np.testing.assert_array_equal(osc_only.cpu().numpy(), gs)
+    _, o32, _ = c.run_oracle_fwd()
+    o32 = np.asarray(o32, np.float32)
+    rd, rs, _ = oracle.quantize(o32, c.cu_q, oracle.ROW32)
+    dc = gs.astype(np.int64) - rs.astype(np.int64)
+    same_code, same_byte = float(np.mean(dc == 0)), float(np.mean(gd == rd))
+    deq = oracle.dequantize(gd, gs, c.cu_q, oracle.ROW32)
+    T, C = o32.shape
+    amax = np.repeat(np.abs(o32).reshape(T, C // 32, 32).max(axis=2), 32, axis=1)
+    scale = max(1.0, float(np.abs(o32).max()))
+    err = np.abs(deq - o32)
+    say(f"  {label} codes equal {same_code:.4f}, payload bytes equal {same_byte:.4f}, "
+        f"max err / (amax/8) {float(np.max(err / np.maximum(amax / 8, 1e-30))):.3f}, rel_fro {rel_fro(deq, o32):.3e}")
+    # against the GPU's own O
+    ob = synth.bf16_bits_to_f32(o_bits).astype(np.float64)
+    amax_b = np.abs(ob).reshape(T, C // 32, 32).max(axis=2)
+    code_lo = np.array([[oracle.e8m0_code(x * (1 - 2.0 ** -8)) for x in row] for row in amax_b])
+    code_hi = np.array([[oracle.e8m0_code(x * (1 + 2.0 ** -8)) for x in row] for row in amax_b])
+    assert np.all((gs >= code_lo) & (gs <= code_hi)), "block code not the MX code of the block maximum"
+    amax_bf = np.repeat(amax_b, 32, axis=1)
+    assert np.all(np.abs(deq - ob) <= amax_bf / 8 + 2.0 ** -8 * np.abs(ob))
+    # against the oracle
+    assert np.abs(dc).max() <= 1
+    assert np.all(err <= O_MAX_ABS * scale + amax / 8)
+    assert rel_fro(deq, o32) <= 2.0 ** -4 + O_REL_FRO
 
 
 def test_fwd_empty_key_sequence():
