@@ -383,6 +383,21 @@ def main():
     torch.cuda.synchronize()
     fwd_mx_s = float(np.median([e[0].elapsed_time(e[1]) * 1e-3 for e in emx]))
 
+    # the backward writing the gradients as MXFP8 only (SQ32 blocks, compact codes), FP16 dQ as in the step
+    nb = T // 32
+    u8 = lambda *shape: torch.empty(shape, dtype=torch.uint8, device=o.device)
+    gmx = (u8(T, C), u8(nb, C // 32), u8(T, C), u8(nb, C // 32), u8(T, C), u8(nb, C // 32))
+    ebm = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n32)]
+    for i in range(n32 + 1):
+        if i:
+            ebm[i - 1][0].record(stream)
+        mx.mxfa_bwd_mx_out(attn, vop, doop, o, dev["do"], lse, args.dq_mode, 1.0, ws, ws_bytes, None, None, None, gmx,
+                           stream)
+        if i:
+            ebm[i - 1][1].record(stream)
+    torch.cuda.synchronize()
+    bwd_mx_s = float(np.median([e[0].elapsed_time(e[1]) * 1e-3 for e in ebm]))
+
     times = {n: [e[0].elapsed_time(e[1]) * 1e-3 for e in ev[n]] for n in names}
     med = {n: float(np.median(v)) for n, v in times.items()}
     f_fwd = 4.0 * N * N * D * B * H
@@ -413,6 +428,7 @@ def main():
         "bwd_fp32dq_us": round(bwd32_s * 1e6, 2), "bwd_fp32dq_pflops": round(f_bwd / bwd32_s / 1e15, 4),
         "fwd_dynamic_p_us": round(fwd_dyn_s * 1e6, 2), "fwd_dynamic_p_pflops": round(f_fwd / fwd_dyn_s / 1e15, 4),
         "fwd_mx_out_us": round(fwd_mx_s * 1e6, 2), "fwd_mx_out_pflops": round(f_fwd / fwd_mx_s / 1e15, 4),
+        "bwd_mx_out_us": round(bwd_mx_s * 1e6, 2), "bwd_mx_out_pflops": round(f_bwd / bwd_mx_s / 1e15, 4),
         "quant_us": round(med["quant"] * 1e6, 2),
         "quant_gbps": round(quant_bytes / med["quant"] / 1e9, 1),
         "roofline": roof,

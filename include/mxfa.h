@@ -190,6 +190,30 @@ mxfa_status mxfa_bwd(const mxfa_attn_args* a, mxfa_mx v_d, mxfa_mx dout, const u
                      void* workspace, size_t workspace_bytes, uint16_t* dq, uint16_t* dk, uint16_t* dv,
                      void* stream);
 
+/* MXFP8 gradient outputs (E4M3 payloads with their E8M0 codes). */
+typedef struct {
+  uint8_t* dq;        /* [T_q, H*D] */
+  uint8_t* dq_scale;  /* SQ32 codes, compact layout of mxfa_quantize: [sum_s ceil(Lq_s/32)][H*D/32] */
+  uint8_t* dk;        /* [T_k, H*D] */
+  uint8_t* dk_scale;  /* [sum_s ceil(Lk_s/32)][H*D/32] */
+  uint8_t* dv;        /* [T_k, H*D] */
+  uint8_t* dv_scale;  /* [sum_s ceil(Lk_s/32)][H*D/32] */
+} mxfa_grad_mx;
+
+/* Attention backward with the gradients written as MXFP8 [BR item 8 / AE-TMEM: quantized gradients
+ * exposed to the next layer, quantized in the epilogue of the kernel that produces them]. Each
+ * gradient (the FP32 value whose bf16 rounding mxfa_bwd writes) is quantized in square 32 x 32
+ * blocks (32 tokens from each sequence start x 32 of D) by the rule of mxfa_quantize, so one payload
+ * serves the next products along D (the projection's input gradient) and along the tokens (its
+ * weight gradient); a partial last block takes its maximum over the rows inside the sequence.
+ *   dq, dk, dv : bf16 outputs as in mxfa_bwd, all set or all NULL
+ *   mx_out     : host struct of six device pointers (all set; payloads 4-byte aligned), or NULL
+ *   at least one of the two sets; everything else as mxfa_bwd. */
+mxfa_status mxfa_bwd_mx_out(const mxfa_attn_args* a, mxfa_mx v_d, mxfa_mx dout, const uint16_t* o,
+                            const uint16_t* dout_bf16, const float* lse, mxfa_dq_mode dq_mode, float dq_static_scale,
+                            void* workspace, size_t workspace_bytes, uint16_t* dq, uint16_t* dk, uint16_t* dv,
+                            const mxfa_grad_mx* mx_out, void* stream);
+
 /* Fused RMSNorm + quantize producer [AE-TMEM: quantization fused into RMSNorm, no separate
  * global-memory pass; BR item 7: FP8 output with dual scale layouts in one pass].
  * y = fl32(fl32(x * r) * gamma[c]), r = 1 / sqrtf(ss / C + eps), ss = sum of x^2 over the row

@@ -14,7 +14,7 @@ import torch
 __all__ = [
     "ROW32", "COL32", "SQ32", "DQ_FP32", "DQ_FP16_STATIC", "P_STATIC", "P_BLOCK_DYNAMIC", "MxfaError",
     "mxfa_quantize", "mxfa_varlen_scale_scatter", "mxfa_padded_token_rows", "mxfa_fwd", "mxfa_fwd_p_scale",
-    "mxfa_fwd_mx_out", "mxfa_bwd", "fwd_mx_out",
+    "mxfa_fwd_mx_out", "mxfa_bwd", "mxfa_bwd_mx_out", "fwd_mx_out", "bwd_mx_out",
     "mxfa_bwd_workspace_size", "mxfa_rmsnorm_quantize", "mxfa_linear_quantize", "mxfa_status_string",
     "mxfa_last_error_message", "MxOperand", "AttnArgs", "quantize", "scale_scatter", "fwd", "bwd",
     "rmsnorm_quantize", "linear_quantize",
@@ -39,6 +39,10 @@ def library_path():
 
 class _Mx(ctypes.Structure):
     _fields_ = [("data", ctypes.c_void_p), ("scale", ctypes.c_void_p), ("mode", ctypes.c_int)]
+
+
+class _GradMx(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("dq", "dq_scale", "dk", "dk_scale", "dv", "dv_scale")]
 
 
 class _AttnArgs(ctypes.Structure):
@@ -69,6 +73,8 @@ def _load():
     lib.mxfa_bwd_workspace_size.argtypes = [ctypes.POINTER(_AttnArgs), i32]
     lib.mxfa_bwd_workspace_size.restype = ctypes.c_size_t
     lib.mxfa_bwd.argtypes = [ctypes.POINTER(_AttnArgs), _Mx, _Mx, P, P, P, i32, f32, P, ctypes.c_size_t, P, P, P, P]
+    lib.mxfa_bwd_mx_out.argtypes = [ctypes.POINTER(_AttnArgs), _Mx, _Mx, P, P, P, i32, f32, P, ctypes.c_size_t, P, P, P,
+                                    ctypes.POINTER(_GradMx), P]
     lib.mxfa_rmsnorm_quantize.argtypes = [P, i64, i64, i32, P, f32, P, i32, i32, P, P, P, P]
     lib.mxfa_linear_quantize.argtypes = [_Mx, _Mx, i64, i32, i32, P, i32, i32, P, P, P, P]
     lib.mxfa_status_string.argtypes = [i32]
@@ -76,7 +82,7 @@ def _load():
     lib.mxfa_last_error_message.argtypes = []
     lib.mxfa_last_error_message.restype = ctypes.c_char_p
     for n in ("mxfa_quantize", "mxfa_varlen_scale_scatter", "mxfa_fwd", "mxfa_fwd_p_scale", "mxfa_fwd_mx_out", "mxfa_bwd",
-              "mxfa_rmsnorm_quantize",
+              "mxfa_bwd_mx_out", "mxfa_rmsnorm_quantize",
               "mxfa_linear_quantize"):
         getattr(lib, n).restype = i32
     _lib = lib
@@ -282,6 +288,38 @@ def bwd(args, v_d, dout, o, dout_bf16, lse, dq_mode=DQ_FP32, dq_static_scale=1.0
     mxfa_bwd(args, v_d, dout, o, dout_bf16, lse, dq_mode, dq_static_scale, workspace, workspace.numel(), dq, dk, dv,
              stream)
     return dq, dk, dv
+
+
+def mxfa_bwd_mx_out(args, v_d, dout, o, dout_bf16, lse, dq_mode, dq_static_scale, workspace, workspace_bytes, dq, dk,
+                    dv, mx_out, stream=None):
+    """dq, dk, dv: bf16 tensors or None (all or none); mx_out: sequence of the six tensors
+    (dq, dq_scale, dk, dk_scale, dv, dv_scale) or None."""
+    a = args._c()
+    g = ctypes.byref(_GradMx(*[_ptr(t) for t in mx_out])) if mx_out is not None else None
+    _check(_load().mxfa_bwd_mx_out(ctypes.byref(a), v_d._c(), dout._c(), _ptr(o), _ptr(dout_bf16), _ptr(lse), dq_mode,
+                                   dq_static_scale, _ptr(workspace), workspace_bytes, _ptr(dq), _ptr(dk), _ptr(dv), g,
+                                   _stream(stream)), "mxfa_bwd_mx_out")
+
+
+def bwd_mx_out(args, v_d, dout, o, dout_bf16, lse, cu_q_host, cu_k_host, dq_mode=DQ_FP32, dq_static_scale=1.0,
+               with_bf16=True, stream=None):
+    """Backward with MXFP8 gradients (SQ32, compact codes). Returns ((dq, dk, dv) bf16 or None,
+    (dq, dq_scale, dk, dk_scale, dv, dv_scale))."""
+    dev = args.q.data.device
+    C = args.num_heads * args.head_dim
+    workspace = torch.empty(mxfa_bwd_workspace_size(args, dq_mode), dtype=torch.uint8, device=dev)
+    nbq, nbk = _blockrows(_lens(cu_q_host)), _blockrows(_lens(cu_k_host))
+    u8 = lambda *shape: torch.empty(shape, dtype=torch.uint8, device=dev)
+    mx_out = (u8(args.total_q, C), u8(nbq, C // 32), u8(args.total_k, C), u8(nbk, C // 32), u8(args.total_k, C),
+              u8(nbk, C // 32))
+    bf = None
+    if with_bf16:
+        bf = (torch.empty((args.total_q, C), dtype=torch.bfloat16, device=dev),
+              torch.empty((args.total_k, C), dtype=torch.bfloat16, device=dev),
+              torch.empty((args.total_k, C), dtype=torch.bfloat16, device=dev))
+    mxfa_bwd_mx_out(args, v_d, dout, o, dout_bf16, lse, dq_mode, dq_static_scale, workspace, workspace.numel(),
+                    *(bf if bf else (None, None, None)), mx_out, stream)
+    return bf, mx_out
 
 
 def rmsnorm_quantize(x_bf16, gamma, eps, cu_host, cu_dev, want_scale_t=True, stream=None):

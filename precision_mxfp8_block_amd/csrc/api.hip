@@ -208,7 +208,16 @@ mxfa_status mxfa_bwd(const mxfa_attn_args* a, mxfa_mx v_d, mxfa_mx dout, const u
                      const uint16_t* dout_bf16, const float* lse, mxfa_dq_mode dq_mode, float dq_static_scale,
                      void* workspace, size_t workspace_bytes, uint16_t* dq, uint16_t* dk, uint16_t* dv,
                      void* stream) {
-  const char* fn = "mxfa_bwd";
+  if (!dq || !dk || !dv) return fail(MXFA_ERR_INVALID, "mxfa_bwd: NULL tensor argument");
+  return mxfa_bwd_mx_out(a, v_d, dout, o, dout_bf16, lse, dq_mode, dq_static_scale, workspace, workspace_bytes, dq, dk,
+                         dv, nullptr, stream);
+}
+
+mxfa_status mxfa_bwd_mx_out(const mxfa_attn_args* a, mxfa_mx v_d, mxfa_mx dout, const uint16_t* o,
+                            const uint16_t* dout_bf16, const float* lse, mxfa_dq_mode dq_mode, float dq_static_scale,
+                            void* workspace, size_t workspace_bytes, uint16_t* dq, uint16_t* dk, uint16_t* dv,
+                            const mxfa_grad_mx* mx_out, void* stream) {
+  const char* fn = mx_out ? "mxfa_bwd_mx_out" : "mxfa_bwd";
   mxfa_status st = check_attn(a, fn);
   if (st != MXFA_OK) return st;
   if (a->q.mode != MXFA_SQ32 || a->k.mode != MXFA_SQ32)
@@ -220,10 +229,20 @@ mxfa_status mxfa_bwd(const mxfa_attn_args* a, mxfa_mx v_d, mxfa_mx dout, const u
     return fail(MXFA_ERR_INVALID, "%s: NULL v_d/dout data or scale", fn);
   if (!aligned(v_d.data, 16) || !aligned(v_d.scale, 16) || !aligned(dout.data, 16) || !aligned(dout.scale, 16))
     return fail(MXFA_ERR_INVALID, "%s: v_d/dout not 16-byte aligned", fn);
-  if (!o || !dout_bf16 || !lse || !dq || !dk || !dv) return fail(MXFA_ERR_INVALID, "%s: NULL tensor argument", fn);
-  if (!aligned(o, 16) || !aligned(dout_bf16, 16) || !aligned(lse, 4) || !aligned(dq, 16) || !aligned(dk, 16) ||
-      !aligned(dv, 16))
+  if (!o || !dout_bf16 || !lse) return fail(MXFA_ERR_INVALID, "%s: NULL tensor argument", fn);
+  const bool bf16_out = dq || dk || dv;
+  if (bf16_out && !(dq && dk && dv)) return fail(MXFA_ERR_INVALID, "%s: dq, dk, dv must be all set or all NULL", fn);
+  if (!bf16_out && !mx_out) return fail(MXFA_ERR_INVALID, "%s: no gradient output", fn);
+  if (!aligned(o, 16) || !aligned(dout_bf16, 16) || !aligned(lse, 4) ||
+      (bf16_out && (!aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))))
     return fail(MXFA_ERR_INVALID, "%s: misaligned tensor argument", fn);
+  if (mx_out) {
+    const mxfa_grad_mx& g = *mx_out;
+    if (!g.dq || !g.dq_scale || !g.dk || !g.dk_scale || !g.dv || !g.dv_scale)
+      return fail(MXFA_ERR_INVALID, "%s: every MXFP8 gradient payload and scale pointer must be set", fn);
+    if (!aligned(g.dq, 4) || !aligned(g.dk, 4) || !aligned(g.dv, 4))
+      return fail(MXFA_ERR_INVALID, "%s: MXFP8 gradient payloads must be 4-byte aligned", fn);
+  }
   if (dq_mode != MXFA_DQ_FP32 && dq_mode != MXFA_DQ_FP16_STATIC)
     return fail(MXFA_ERR_INVALID, "%s: bad dq_mode %d", fn, (int)dq_mode);
   if (dq_mode == MXFA_DQ_FP16_STATIC && !is_pow2(dq_static_scale))
@@ -232,12 +251,14 @@ mxfa_status mxfa_bwd(const mxfa_attn_args* a, mxfa_mx v_d, mxfa_mx dout, const u
   const size_t need = mxfa_bwd_workspace_size(a, dq_mode);
   if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
     return fail(MXFA_ERR_INVALID, "%s: workspace NULL, misaligned or smaller than %zu bytes", fn, need);
+  mxfa::GradMxOut gm{};
+  if (mx_out) gm = {mx_out->dq, mx_out->dq_scale, mx_out->dk, mx_out->dk_scale, mx_out->dv, mx_out->dv_scale};
   mxfa::MxOperand vv{v_d.data, v_d.scale, (int)v_d.mode};
   mxfa::MxOperand dd{dout.data, dout.scale, (int)dout.mode};
   return hip_status(mxfa::launch_attn_bwd(to_problem(a), vv, dd, o, dout_bf16, lse,
                                           dq_mode == MXFA_DQ_FP16_STATIC ? 1 : 0,
                                           dq_mode == MXFA_DQ_FP16_STATIC ? dq_static_scale : 1.0f, workspace, dq, dk,
-                                          dv, (hipStream_t)stream),
+                                          dv, mx_out ? &gm : nullptr, (hipStream_t)stream),
                     fn);
 }
 

@@ -150,6 +150,30 @@ __device__ __forceinline__ uint32_t wave_max_dpp(uint32_t v) {
   return max((uint32_t)s32[0], (uint32_t)s32[1]);
 }
 
+// SQ32 quantization (the MX scale rule of the operand quantizer) of one 32 x 32 gradient block that
+// a wave holds in the MFMA accumulator layout: lane (r, hh) holds column r and rows
+// 8 (v / 4) + 4 hh + v % 4, v = 0..15. Rows at or past `valid` lie outside the sequence: they are
+// left out of the block maximum and not stored. Payload bytes go to dst[row * C] (dst already at
+// the lane's column), the E8M0 code to *code_dst (lane 0). Every lane of the wave must take part.
+__device__ __forceinline__ void store_grad_sq32(const float (&x)[16], int valid, uint8_t* dst, int C,
+                                                uint8_t* code_dst, int lane, int hh) {
+  uint32_t am = 0;  // largest sign-cleared bit pattern: orders NaN > Inf > finite magnitudes
+#pragma unroll
+  for (int v = 0; v < 16; ++v)
+    if (8 * (v >> 2) + 4 * hh + (v & 3) < valid) am = max(am, __float_as_uint(x[v]) & 0x7fffffffu);
+  am = wave_max_dpp(am);
+  const uint32_t code = mx_code_from_amax_bits(am);
+  const float inv = mx_inv_scale(code == 255u ? 127u : code);
+#pragma unroll
+  for (int v = 0; v < 16; v += 2) {
+    const uint32_t w = code == 255u ? 0x7f7fu : mx_pack2_lo(x[v] * inv, x[v + 1] * inv, 0u);
+    const int r0 = 8 * (v >> 2) + 4 * hh + (v & 3);
+    if (r0 < valid) dst[(uint32_t)(r0 * C)] = (uint8_t)w;
+    if (r0 + 1 < valid) dst[(uint32_t)((r0 + 1) * C)] = (uint8_t)(w >> 8);
+  }
+  if (lane == 0) *code_dst = (uint8_t)code;
+}
+
 // ---------------------------------------------------------------------------------------------
 // Preprocess: the negated row sums -Delta[h][t] = -sum_d dO[t, h, d] * O[t, h, d] (fp32, the
 // initial value of the dP accumulator) and the exponent offset of 256 P, b[h][t] = 8 - LSE[h][t]
@@ -207,7 +231,9 @@ struct BwdParams {
   uint8_t* ds_img;       // [H][nseq][ntq_max][ntk_max] 16 KB dS_q images
   uint8_t* ds_codes;     // [H][nseq][ntq_max][ntk_max] 16 E8M0 codes
   float c;
-  uint16_t *dk, *dv;
+  uint16_t *dk, *dv;                  // bf16 gradients, or null
+  uint8_t *dk_mx, *dk_mx_scale;       // E4M3 SQ32 gradients (compact codes [blocks][C/32]), or null
+  uint8_t *dv_mx, *dv_mx_scale;
 };
 
 __global__ void __launch_bounds__(64 * kBwdWaves, 1) attn_bwd_kernel(BwdParams p) {
@@ -615,17 +641,35 @@ __global__ void __launch_bounds__(64 * kBwdWaves, 1) attn_bwd_kernel(BwdParams p
     // ---- epilogue: dV and dK = c dK of the wave's 32 keys (accumulator: column d = 32 db + r, rows
     // kv 8 (v/4) + 4 hh + v%4 of the wave's key block) ----
     const int64_t orow = (k_start + kv0 + 32 * kw) * (int64_t)C + h * kD;
+    if (p.dv) {
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int kr = 8 * (v >> 2) + 4 * hh + (v & 3);
-        if (kv0 + 32 * kw + kr < Lk) {
-          const uint32_t o = (uint32_t)(kr * C + 32 * db + r);
-          p.dv[orow + o] = (uint16_t)f32_to_bf16(dv_acc[db][v]);
-          p.dk[orow + o] = (uint16_t)f32_to_bf16(dk_acc[db][v] * p.c);
+        for (int v = 0; v < 16; ++v) {
+          const int kr = 8 * (v >> 2) + 4 * hh + (v & 3);
+          if (kv0 + 32 * kw + kr < Lk) {
+            const uint32_t o = (uint32_t)(kr * C + 32 * db + r);
+            p.dv[orow + o] = (uint16_t)f32_to_bf16(dv_acc[db][v]);
+            p.dk[orow + o] = (uint16_t)f32_to_bf16(dk_acc[db][v] * p.c);
+          }
         }
+    }
+    // MXFP8 gradients: the wave's 32 keys x 4 blocks of 32 columns are four SQ32 blocks each (key
+    // blocks start at the sequence start); block row koff.blocks32 + (kv0 + 32 kw) / 32
+    const int kvalid = Lk - (kv0 + 32 * kw);
+    if (p.dv_mx && kvalid > 0) {
+      const int64_t brow = koff.blocks32 + ((kv0 + 32 * kw) >> 5);
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        float x[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) x[v] = dv_acc[db][v];
+        store_grad_sq32(x, kvalid, p.dv_mx + orow + 32 * db + r, C, p.dv_mx_scale + brow * Cs + h * 4 + db, lane, hh);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) x[v] = dk_acc[db][v] * p.c;
+        store_grad_sq32(x, kvalid, p.dk_mx + orow + 32 * db + r, C, p.dk_mx_scale + brow * Cs + h * 4 + db, lane, hh);
       }
+    }
   }
 }
 
@@ -649,7 +693,8 @@ struct DqParams {
   int dq_fp16;
   int log2_sigma;  // sigma = 2^log2_sigma (0 in FP32 mode)
   float mult;      // c / sigma
-  uint16_t* dq;
+  uint16_t* dq;    // bf16 dQ, or null
+  uint8_t *dq_mx, *dq_mx_scale;  // E4M3 SQ32 dQ (compact codes [blocks][C/32]), or null
 };
 
 // LDS ring of (dS image, K tile) stages (a power of two). Two stages keep the LDS at 66 KB so two
@@ -793,22 +838,33 @@ __global__ void __launch_bounds__(64 * kDqWaves, 1) attn_dq_kernel(DqParams p) {
   }
 
   // ---- epilogue: dQ = bf16(c acc / sigma); block rows 8 (v/4) + 4 hh + v%4, column 32 db + r ----
-  uint16_t* dqb = p.dq + (q_start + q0 + 32 * qb) * (int64_t)C + h * kD;
+  const int64_t orow = (q_start + q0 + 32 * qb) * (int64_t)C + h * kD;
+  const int qvalid = Lq - (q0 + 32 * qb);
+  int64_t brow = 0;
+  if (p.dq_mx) brow = seq_offsets(p.cu_q, s).blocks32 + ((q0 + 32 * qb) >> 5);
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
     const int db = 2 * half + e;
+    float x[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      float x;
       if (p.dq_fp16) {
         const float2 f = __half22float2(__builtin_bit_cast(__half2, acc16[e][v >> 1]));
-        x = (v & 1) ? f.y : f.x;
+        x[v] = ((v & 1) ? f.y : f.x) * p.mult;
       } else {
-        x = acc32[e][v];
+        x[v] = acc32[e][v] * p.mult;
       }
-      const int qr = 8 * (v >> 2) + 4 * hh + (v & 3);
-      if (q0 + 32 * qb + qr < Lq) dqb[(uint32_t)(qr * C + 32 * db + r)] = (uint16_t)f32_to_bf16(x * p.mult);
     }
+    if (p.dq) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int qr = 8 * (v >> 2) + 4 * hh + (v & 3);
+        if (qr < qvalid) p.dq[orow + (uint32_t)(qr * C + 32 * db + r)] = (uint16_t)f32_to_bf16(x[v]);
+      }
+    }
+    // MXFP8 dQ: one SQ32 block (32 queries from the sequence start x 32 columns) per (e, wave)
+    if (p.dq_mx && qvalid > 0)
+      store_grad_sq32(x, qvalid, p.dq_mx + orow + 32 * db + r, C, p.dq_mx_scale + brow * Cs + h * 4 + db, lane, hh);
   }
 }
 
@@ -839,7 +895,7 @@ size_t bwd_workspace_bytes(int64_t Tq, int H, int nseq, int max_q, int max_k) {
 
 hipError_t launch_attn_bwd(const AttnProblem& a, const MxOperand& v_d, const MxOperand& dout, const uint16_t* o,
                            const uint16_t* dout_bf16, const float* lse, int dq_fp16, float sigma, void* workspace,
-                           uint16_t* dq, uint16_t* dk, uint16_t* dv, hipStream_t stream) {
+                           uint16_t* dq, uint16_t* dk, uint16_t* dv, const GradMxOut* mx_out, hipStream_t stream) {
   const int64_t Tq = a.total_q;
   const int C = a.H * kD;
   const BwdWorkspace w = bwd_workspace_layout(Tq, a.H, a.nseq, a.max_seqlen_q, a.max_seqlen_k);
@@ -871,6 +927,10 @@ hipError_t launch_attn_bwd(const AttnProblem& a, const MxOperand& v_d, const MxO
   p.ds_codes = ws + w.codes;
   p.c = a.softmax_scale;
   p.dk = dk; p.dv = dv;
+  p.dk_mx = mx_out ? mx_out->dk : nullptr;
+  p.dk_mx_scale = mx_out ? mx_out->dk_scale : nullptr;
+  p.dv_mx = mx_out ? mx_out->dv : nullptr;
+  p.dv_mx_scale = mx_out ? mx_out->dv_scale : nullptr;
   if (p.total_items > 0) {
     hipLaunchKernelGGL(attn_bwd_kernel, dim3((unsigned)p.total_items), dim3(64 * kBwdWaves), 0, stream, p);
     hipError_t e = hipGetLastError();
@@ -892,6 +952,8 @@ hipError_t launch_attn_bwd(const AttnProblem& a, const MxOperand& v_d, const MxO
   }
   d.mult = a.softmax_scale / (dq_fp16 ? sigma : 1.0f);
   d.dq = dq;
+  d.dq_mx = mx_out ? mx_out->dq : nullptr;
+  d.dq_mx_scale = mx_out ? mx_out->dq_scale : nullptr;
   if (d.total_items > 0) {
     hipLaunchKernelGGL(attn_dq_kernel, dim3((unsigned)d.total_items), dim3(64 * kDqWaves), 0, stream, d);
     return hipGetLastError();

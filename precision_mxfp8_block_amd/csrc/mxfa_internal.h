@@ -38,8 +38,13 @@ hipError_t launch_linear_quantize(const MxOperand& x, const MxOperand& w, int64_
 hipError_t launch_attn_fwd(const AttnProblem& a, int p_dynamic, uint16_t* o, uint8_t* o_mx, uint8_t* o_mx_scale,
                            float* lse, hipStream_t stream);
 size_t bwd_workspace_bytes(int64_t Tq, int H, int nseq, int max_q, int max_k);
+// MXFP8 gradient outputs: E4M3 payloads [T, H*D] and compact SQ32 codes [blocks][H*D/32].
+struct GradMxOut {
+  uint8_t *dq, *dq_scale, *dk, *dk_scale, *dv, *dv_scale;
+};
+// dq, dk, dv (bf16) are all null or all set; mx_out (all six pointers set) may be null.
 hipError_t launch_attn_bwd(const AttnProblem& a, const MxOperand& v_d, const MxOperand& dout, const uint16_t* o,
                            const uint16_t* dout_bf16, const float* lse, int dq_fp16, float sigma, void* workspace,
-                           uint16_t* dq, uint16_t* dk, uint16_t* dv, hipStream_t stream);
+                           uint16_t* dq, uint16_t* dk, uint16_t* dv, const GradMxOut* mx_out, hipStream_t stream);
 
 }  // namespace mxfa

@@ -131,6 +131,18 @@ class AttnCase:
         torch.cuda.synchronize()
         return tuple(to_host_bf16_bits(t) for t in (dq, dk, dv))
 
+    def run_gpu_bwd_mx_out(self, dq_mode, sigma=1.0, with_bf16=True):
+        """mxfa_bwd_mx_out on the same operands: ((dq, dk, dv) bf16 bits or None, six numpy arrays:
+        dq, dq_scale, dk, dk_scale, dv, dv_scale)."""
+        gvd = gpu_quantize_padded(self.v_d, self.cu_k, self.cu_k_d, mx.ROW32)
+        gdo = gpu_quantize_padded(self.do_d, self.cu_q, self.cu_q_d, mx.SQ32)
+        bf, mxo = mx.bwd_mx_out(self.args, mx.MxOperand(gvd[0], gvd[1], mx.ROW32),
+                                mx.MxOperand(gdo[0], gdo[1], mx.SQ32), self.o_dev, self.do_d, self.lse_dev, self.cu_q,
+                                self.cu_k, dq_mode, sigma, with_bf16=with_bf16)
+        torch.cuda.synchronize()
+        bits = tuple(to_host_bf16_bits(t) for t in bf) if bf is not None else None
+        return bits, tuple(t.cpu().numpy() for t in mxo)
+
     # ---------------- oracle ----------------
     def run_oracle_fwd(self, p_scale=oracle.P_STATIC):
         self.oq = oracle.quantize(self.q, self.cu_q, self.qk_mode)

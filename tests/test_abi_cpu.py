@@ -26,7 +26,8 @@ def _declared_functions():
 
 def test_header_declares_the_abi():
     names = _declared_functions()
-    for n in ["mxfa_quantize", "mxfa_fwd", "mxfa_fwd_p_scale", "mxfa_bwd", "mxfa_varlen_scale_scatter",
+    for n in ["mxfa_quantize", "mxfa_fwd", "mxfa_fwd_p_scale", "mxfa_fwd_mx_out", "mxfa_bwd", "mxfa_bwd_mx_out",
+              "mxfa_varlen_scale_scatter",
               "mxfa_rmsnorm_quantize",
               "mxfa_linear_quantize",
               "mxfa_bwd_workspace_size", "mxfa_status_string", "mxfa_last_error_message"]:
@@ -149,6 +150,23 @@ def test_bwd_argument_errors(kw, expect):
                          P, kw.get("dq_mode", 0), kw.get("sigma", 1.0), kw.get("ws", P), kw.get("ws_bytes", need), P,
                          P, P, 0)
     assert st == expect, _last()
+
+
+@pytest.mark.parametrize("bf16,mxp", [
+    ((0, 0, 0), None),                      # no gradient output at all
+    ((P, 0, 0), None),                      # bf16 gradients only partly given
+    ((0, 0, 0), (P, P, P, 0, P, P)),        # an MXFP8 scale pointer missing
+    ((0, 0, 0), (P, P, P + 2, P, P, P)),    # an MXFP8 payload not 4-byte aligned
+    ((P, P, P + 8, ), (P, P, P, P, P, P)),  # bf16 dv misaligned
+])
+def test_bwd_mx_out_argument_errors(bf16, mxp):
+    a = _args()
+    need = mx.mxfa_bwd_workspace_size(a, 0)
+    bf16 = tuple(bf16) + (0,) * (3 - len(bf16))
+    g = ctypes.byref(mx._GradMx(*mxp)) if mxp is not None else None
+    st = _lib().mxfa_bwd_mx_out(ctypes.byref(a), mx._Mx(P, P, 0), mx._Mx(P, P, 2), P, P, P, 0, 1.0, P, need, *bf16, g, 0)
+    assert st == INVALID, _last()
+    assert _last() != ""
 
 
 def test_scatter_and_rmsnorm_argument_errors():

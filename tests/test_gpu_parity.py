@@ -12,7 +12,7 @@ import torch
 import oracle
 import precision_mxfp8_block_amd as mx
 import synth
-from mx_cases import (O_MAX_ABS, O_REL_FRO, AttnCase, LinearCase, certify_linear, check_grads, check_o, cu_dev,
+from mx_cases import (GRAD_REL_FRO, O_MAX_ABS, O_REL_FRO, AttnCase, LinearCase, certify_linear, check_grads, check_o, cu_dev,
                       rel_fro, say, to_dev_bf16)
 
 pytestmark = pytest.mark.gpu
@@ -197,6 +197,39 @@ def test_fwd_dynamic_p_peaky_softmax():
     say(f"  rel_fro vs unquantized P: dynamic {err_dyn:.3e}, static {err_sta:.3e}")
 
 
+def check_mx_sq32_output(label, gd, gs, own_bits, ref_f, cu, rel_tol):
+    """An SQ32 MXFP8 output against the GPU's own bf16 output written in the same pass (codes are the MX
+    codes of a value within bf16 rounding of each block's maximum; values within one E4M3 step of the
+    block's top binade, amax / 8, plus bf16 rounding) and against the oracle's FP32 result (codes
+    within one, relative Frobenius error within 2^-4 + the stated tolerance)."""
+    T, C = own_bits.shape
+    own = synth.bf16_bits_to_f32(own_bits).astype(np.float64)
+    lens = np.diff(np.asarray(cu, np.int64))
+    nb = int(np.sum((lens + 31) // 32))
+    # the block maximum of each (sequence-aligned 32-token block, 32 columns)
+    amax_b = np.zeros((nb, C // 32))
+    row_block = np.empty(T, np.int64)
+    b0 = 0
+    for s0, L in zip(cu[:-1], lens):
+        row_block[s0:s0 + L] = b0 + np.arange(L) // 32
+        b0 += (L + 31) // 32
+    np.maximum.at(amax_b, row_block, np.abs(own).reshape(T, C // 32, 32).max(axis=2))
+    code_lo = np.array([[oracle.e8m0_code(x * (1 - 2.0 ** -8)) for x in row] for row in amax_b])
+    code_hi = np.array([[oracle.e8m0_code(x * (1 + 2.0 ** -8)) for x in row] for row in amax_b])
+    assert gs.shape == (nb, C // 32)
+    assert np.all((gs >= code_lo) & (gs <= code_hi)), f"{label}: block code not the MX code of its maximum"
+    deq = oracle.dequantize(gd, gs, cu, oracle.SQ32)
+    amax_el = np.repeat(amax_b[row_block], 32, axis=1)
+    assert np.all(np.abs(deq - own) <= amax_el / 8 + 2.0 ** -8 * np.abs(own)), label
+    rd, rs, _ = oracle.quantize(np.asarray(ref_f, np.float32), cu, oracle.SQ32)
+    dc = gs.astype(np.int64) - rs.astype(np.int64)
+    fro = rel_fro(deq, ref_f)
+    say(f"  {label}: codes equal {float(np.mean(dc == 0)):.4f}, bytes equal {float(np.mean(gd == rd)):.4f}, "
+        f"rel_fro vs oracle {fro:.3e}")
+    assert np.abs(dc).max() <= 1, label
+    assert fro <= 2.0 ** -4 + rel_tol, label
+
+
 MX_OUT_CASES = [FWD_CASES[i] for i in (0, 2, 3, 4, 5)]
 
 
@@ -308,3 +341,30 @@ def test_bwd_deterministic():
         b = c.run_gpu_bwd(mode, sigma)
         for x, y in zip(a, b):
             np.testing.assert_array_equal(x, y)
+
+
+MX_GRAD_CASES = [(BWD_CASES[2], mx.DQ_FP32), (BWD_CASES[3], mx.DQ_FP16_STATIC), (BWD_CASES[4], mx.DQ_FP16_STATIC)]
+
+
+@pytest.mark.parametrize("case,dq_mode", MX_GRAD_CASES, ids=[f"{c[0]}-dq{m}" for c, m in MX_GRAD_CASES])
+def test_bwd_mx_out_parity(case, dq_mode):
+    """dQ, dK, dV written as MXFP8 (SQ32 blocks from each sequence start, compact codes) in the
+    backward's epilogues; the bf16 gradients of the same pass equal mxfa_bwd's bit for bit, and the
+    MXFP8 payloads do not depend on whether bf16 gradients are written."""
+    label, seed, lens, H, causal, op, sigma = case
+    say(f"bwd MX gradients {label} dq_mode={dq_mode}")
+    c = AttnCase(seed, lens, None, H=H, causal=causal, outlier_p=op, fwd_modes="train")
+    c.run_gpu_fwd()
+    c.run_oracle_fwd()
+    g_bits = c.run_gpu_bwd(dq_mode, sigma)
+    bits, mxo = c.run_gpu_bwd_mx_out(dq_mode, sigma)
+    _, mxo_only = c.run_gpu_bwd_mx_out(dq_mode, sigma, with_bf16=False)
+    for a, b in zip(bits, g_bits):
+        np.testing.assert_array_equal(a, b)
+    for a, b in zip(mxo, mxo_only):
+        np.testing.assert_array_equal(a, b)
+    ref = c.run_oracle_bwd(dq_mode, sigma)
+    for i, name in enumerate(("dq", "dk", "dv")):
+        cu = c.cu_q if name == "dq" else c.cu_k
+        check_mx_sq32_output(f"{label} {name}", mxo[2 * i], mxo[2 * i + 1], bits[i], ref[name + "_f"], cu,
+                             GRAD_REL_FRO)
