@@ -18,7 +18,8 @@
 //
 // Style: plain loops, FP64 wherever the pages do not fix a precision, FP32 rounding exactly at
 // the points where the pages put FP32 (softmax, the FP32 accumulators), one function per step.
-// Readings of points the pages leave open are marked READING and listed in the design doc.
+// Readings of points the pages leave open are marked READING where they apply, each with the
+// choice it makes.
 //
 // Parity status of each function is stated at its definition ("pinned by ..." names the
 // non-oracle fact each one is checked against in tests/test_oracle_pins.py).
@@ -85,8 +86,8 @@ uint8_t e4m3_code_of_magnitude(double y) {
 
 // Encode with round-to-nearest-even at every exponent (subnormals included) and saturation of
 // magnitudes above 448 to 448. A value that rounds to zero keeps its sign. NaN -> 0x7F.
-// READING (the pages name only "E4M3"; the saturating round-to-nearest-even pack is fixed by the
-// method's statement of the quantizer): see DESIGN.md, "Readings".
+// READING: the pages name only "E4M3"; the saturating round-to-nearest-even pack follows the
+// method's statement of the quantizer.
 // Pinned by: brute-force nearest-even search over all 127 non-negative finite codes.
 uint8_t e4m3_encode(double v) {
   if (std::isnan(v)) return 0x7f;
@@ -114,7 +115,7 @@ uint8_t e4m3_encode(double v) {
 // Scale rule [AE TMEM: "bit extraction instead of logarithms or division"]: the block's scale
 // exponent is floor(log2(amax)) minus the largest E4M3 exponent (8), so the largest element lands
 // in [256, 512). In fp32 bits this is (exponent field of amax) - 8. Clamped to [0, 254]; a block
-// with no non-zero element gets 0; a block holding NaN or Inf gets 255 (READING A1).
+// with no non-zero element gets 0; a block holding NaN or Inf gets 255 (READING).
 // Pinned by: code(1.0) = 119, code(448) = 127, code(512) = 128, clamps, specials.
 int e8m0_code(double amax) {
   if (!std::isfinite(amax)) return 255;
@@ -155,7 +156,7 @@ double fp16_round(double v) {
 enum Mode { ROW32 = 0, COL32 = 1, SQ32 = 2 };
 
 // Token blocks of 32 start at each sequence start; the last block of a sequence may be partial
-// (READING A3: a block never straddles two sequences, because the scale tensors are padded per
+// (READING: a block never straddles two sequences, because the scale tensors are padded per
 // sequence [AE TMEM, jagged handling]).
 int64_t blockrow_offset(const int32_t* cu, int s) {
   int64_t off = 0;
@@ -301,7 +302,7 @@ const int TILE = 128;  // Q and KV tile rows [TC paragraph 2: [128, 128] tiles, 
 //     m' = max(m, rowmax S);  alpha = exp(c (m - m'));  P = exp(c (S - m'));  l = alpha l + rowsum P
 //   quant_p = 1: P is quantized to E4M3 with the static scale 2^-8 (E8M0 code 119) on every
 //     32-block: P <= 1 because the row max m' is the reference point [BR item 4: constant scale,
-//     P in [0,1]; AE TMEM: the softmax row max is reused, so no extra max pass] (READING A5).
+//     P in [0,1]; AE TMEM: the softmax row max is reused, so no extra max pass] (READING).
 //   quant_p = 2: dynamic block scale. Each row's keys of the tile are split into blocks of 32
 //     starting at the tile's first key; a block's scale is the MX scale rule applied to its largest
 //     P (code = e8m0_code(amax), so that element lands in [256, 512)), and its P values are
@@ -406,7 +407,7 @@ void attn_fwd_unit(const double* q, const double* k, const double* v, int64_t q0
 //   P_q = E4M3(P 2^8), static code 119 [BR item 4]
 //   dV += deq(P_q)^T deq(dO_q)                                 GEMM 2
 //   dP  = deq(dO_q) deq(V)^T (fp32)                            GEMM 3
-//   dS  = P (dP - Delta) (fp32),  Delta_i = sum_d dO_id O_id   (READING A8)
+//   dS  = P (dP - Delta) (fp32),  Delta_i = sum_d dO_id O_id   (READING)
 //   dS_q: 32 x 32 square blocks of the tile, dynamic E8M0 scale from the block's absolute
 //         maximum [AE TMEM: dS quantized once per square block with a warp-wide abs-max]
 //   dK += deq(dS_q)^T deq(Q_q)                                 GEMM 4
@@ -728,7 +729,7 @@ int orc_attn_bwd_mx(const uint8_t* q, const uint8_t* q_scale, const uint8_t* k, 
 }
 
 // Fused RMSNorm + quantize producer [AE TMEM: quantization fused into RMSNorm; BR item 7: FP8
-// output with dual scale layouts in one pass]. READING A11:
+// output with dual scale layouts in one pass]. READING:
 //   ss = fl32(sum_c x^2) (exact sum, one rounding), r = 1 / sqrtf(ss / C + eps) in fp32 with IEEE
 //   division and square root, y = fl32(fl32(x r) gamma); then SQ32 quantization of y with token
 //   blocks aligned to sequence starts; scale written in [NB][C/32] and transposed [C/32][NB].
@@ -760,7 +761,7 @@ int orc_rmsnorm_quantize(const uint16_t* x, int64_t ld, int64_t T, int C, const 
 }
 
 // Fused projection GEMM + quantize producer [AE TMEM: quantization fused into the projection GEMM
-// epilogue; BR item 7: FP8 output with dual scale layouts in one pass]. READING A12:
+// epilogue; BR item 7: FP8 output with dual scale layouts in one pass]. READING:
 //   Y = fl32(sum_k deq(X)_tk deq(W)_nk)  (X [T, C_in] SQ32 compact or ROW32, W [C_out, C_in] ROW32
 //   along C_in)
 //   then SQ32 quantization of Y with token blocks aligned to sequence starts; scales written in
