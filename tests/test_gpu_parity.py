@@ -2,7 +2,9 @@
 
 Bit-exact for the quantizer, the scale scatter and the RMSNorm+quantize producer; certified
 mismatches only for the projection GEMM + quantize producer; tolerances of
-tests/mx_cases.py for attention. Sizes here finish in seconds on the oracle and still span several
+tests/mx_cases.py for attention (both P scales). The MXFP8 outputs of the forward (O) and the backward
+(dQ, dK, dV) are checked against the GPU's own bf16 results of the same pass (codes certified, values
+within one E4M3 step) and against the oracle's FP32 results through its quantizer. Sizes here finish in seconds on the oracle and still span several
 tiles and ragged tails; full-size sampled checks are in test_gpu_fullsize.py.
 """
 import numpy as np
