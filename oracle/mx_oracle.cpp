@@ -134,6 +134,8 @@ double e8m0_value(int code) {
 }
 
 // binary16 rounding (nearest even), overflow to infinity; used for the FP16 dQ accumulator.
+// Pinned by: numpy's float16 conversion (subnormals, ties in every binade, 65504 / 65520) and the
+// worked FP16 dQ accumulation example.
 double fp16_round(double v) {
   if (std::isnan(v) || std::isinf(v) || v == 0.0) return v;
   double a = std::fabs(v);
@@ -313,7 +315,8 @@ const int TILE = 128;  // Q and KV tile rows [TC paragraph 2: [128, 128] tiles, 
 //   O  = alpha O + deq(P_q) V, rounded to fp32 per tile.
 //   At the end: O_out = bf16(fl32(O / l)), LSE = fl32(c m + ln l).
 // Pinned by: FP64 brute-force softmax attention (no-quant mode), one-tile == many tiles,
-// closed forms (K = 0, causal row 0, one-hot scores), the quantization error bound; the dynamic
+// closed forms (K = 0, causal row 0, one-hot scores), the quantization error bound, a worked
+// static-scale example whose P lie in E4M3's subnormal band at 2^-8 (codes derived by hand); the dynamic
 // mode by a worked single-row example (block codes from floor(log2 amax), identity V), its K = 0
 // closed form and its accuracy against the static mode.
 void attn_fwd_unit(const double* q, const double* k, const double* v, int64_t q0, int64_t Lq, int64_t k0,
@@ -417,7 +420,9 @@ void attn_fwd_unit(const double* q, const double* k, const double* v, int64_t q0
 // Outputs: dQ = bf16(c acc / sigma), dK = bf16(c dK), dV = bf16(dV).
 // quant = 0 skips the P and dS quantization (pinning mode).
 // Pinned by: FP64 central finite differences of the no-quant mode on tiny inputs; FP16 vs FP32
-// accumulator bound.
+// accumulator bound; worked examples with hand-derived results for the static P scale of the
+// recomputed P (dV), Delta from the bf16 dO, dS quantized per 32 x 32 block and used quantized in dK,
+// and the FP32 / FP16 dQ accumulators with the static scale sigma.
 struct BwdArgs {
   const double *q, *k, *v, *dO_mm, *o_delta, *do_delta;
   const float* lse;
