@@ -88,7 +88,9 @@ def _check(rc, name):
 
 
 def default_threads():
-    return max(1, min(os.cpu_count() or 1, 64))
+    """At most 16 threads: the CPU share of one GPU on the machines this runs on, whatever the core
+    count the OS reports."""
+    return max(1, min(os.cpu_count() or 1, 16))
 
 
 # ---- scalars ------------------------------------------------------------------------------

@@ -73,21 +73,157 @@ def cu_dev(cu):
     return torch.from_numpy(np.asarray(cu, np.int32)).cuda()
 
 
+GUARD_BYTES = 4096
+GUARD_FILL = 0xA5   # the guard bytes around every output
+PREFILL = 0xFF      # every output byte before the call: bf16/fp32 NaN, E4M3 NaN, E8M0 NaN
+
+
+class Guarded:
+    """A GPU output tensor `t` prefilled with 0xFF bytes inside a larger buffer whose GUARD_BYTES before
+    and after it hold GUARD_FILL; check() fails if any guard byte changed (a store out of bounds). An
+    output element the kernels never write keeps the prefill (NaN in every float format), so a
+    comparison with the oracle or with an earlier call cannot pass on stale memory."""
+
+    def __init__(self, shape, dtype, prefill=PREFILL):
+        n = int(np.prod(shape)) * torch.empty((), dtype=dtype).element_size()
+        self.n = n
+        self.buf = torch.full((GUARD_BYTES + n + GUARD_BYTES,), GUARD_FILL, dtype=torch.uint8, device="cuda")
+        self.buf[GUARD_BYTES:GUARD_BYTES + n].fill_(prefill)
+        self.t = self.buf[GUARD_BYTES:GUARD_BYTES + n].view(dtype).view(shape)
+
+    def check(self, label=""):
+        g = torch.cat([self.buf[:GUARD_BYTES], self.buf[GUARD_BYTES + self.n:]])
+        bad = int((g != GUARD_FILL).sum())
+        assert bad == 0, f"{label}: {bad} guard bytes around the output were overwritten"
+
+
+def gpu_quantize(x_dev, cu, cu_d, mode, want_scale_t=False):
+    """mxfa_quantize through the ABI into guarded, 0xFF-prefilled outputs (compact layout)."""
+    T, C = x_dev.shape
+    lens = np.diff(np.asarray(cu, np.int64))
+    nb = int(np.sum((lens + 31) // 32))
+    data = Guarded((T, C), torch.uint8)
+    scale = Guarded({mx.ROW32: (T, C // 32), mx.COL32: (nb, C), mx.SQ32: (nb, C // 32)}[mode], torch.uint8)
+    scale_t = Guarded((C // 32, nb), torch.uint8) if want_scale_t else None
+    mx.mxfa_quantize(x_dev, x_dev.stride(0), T, C, cu_d, len(lens), int(lens.max()) if lens.size else 0, mode,
+                     data.t, scale.t, scale_t.t if scale_t else None)
+    torch.cuda.synchronize()
+    for g in (data, scale, scale_t):
+        if g is not None:
+            g.check("quantize output")
+    return data.t, scale.t, scale_t.t if scale_t else None
+
+
+def gpu_scale_scatter(compact, cu, cu_d, C, mode):
+    lens = [int(v) for v in np.diff(np.asarray(cu, np.int64))]
+    P = sum((L + 127) // 128 * 128 for L in lens)
+    rows = P if mode == mx.ROW32 else P // 32
+    width = C if mode == mx.COL32 else C // 32
+    out = Guarded((rows, width), torch.uint8)
+    mx.mxfa_varlen_scale_scatter(compact, cu_d, len(lens), max(lens) if lens else 0, C, mode, out.t, rows)
+    torch.cuda.synchronize()
+    out.check("scale scatter output")
+    return out.t
+
+
 def gpu_quantize_padded(x_dev, cu, cu_d, mode):
     """Quantize on the GPU (compact) and scatter the scales to the padded layout when needed."""
-    data, scale, _ = mx.quantize(x_dev, cu, cu_d, mode)
+    data, scale, _ = gpu_quantize(x_dev, cu, cu_d, mode)
     lens = np.diff(cu)
     if np.all(lens % 128 == 0):
         return data, scale, scale
-    padded = mx.scale_scatter(scale, cu, cu_d, x_dev.shape[1], mode)
+    padded = gpu_scale_scatter(scale, cu, cu_d, x_dev.shape[1], mode)
     return data, padded, scale
 
 
+def token_blocks(lens):
+    """(start, stop) token rows of every 32-token block, counted from each sequence start."""
+    out, t0 = [], 0
+    for L in lens:
+        for b in range(0, L, 32):
+            out.append((t0 + b, t0 + min(L, b + 32)))
+        t0 += L
+    return out
+
+
+def block_rel_errors(g, ref, lens, H, D=128):
+    """Relative Frobenius error of every (32-token block, head) of a [T, H*D] gradient; a block whose
+    reference is exactly zero gives 0 if the GPU block is zero too and inf otherwise."""
+    g, ref = np.asarray(g, np.float64), np.asarray(ref, np.float64)
+    errs = []
+    for a, b in token_blocks(lens):
+        for h in range(H):
+            x, r = g[a:b, h * D:(h + 1) * D], ref[a:b, h * D:(h + 1) * D]
+            nr = np.linalg.norm(r)
+            if nr == 0:
+                errs.append(0.0 if not np.any(x) else float("inf"))
+            else:
+                errs.append(float(np.linalg.norm(x - r) / nr))
+    return np.array(errs)
+
+
+def bf16_rounding_interval(bits):
+    """The closed interval of real values that bf16 round-to-nearest-even sends to each bf16 value:
+    b - ulp/2 .. b + ulp/2 (a superset at the bottom of a binade, where the spacing below halves)."""
+    b = synth.bf16_bits_to_f32(bits).astype(np.float64)
+    mag = np.abs(b)
+    e = np.floor(np.log2(np.where(mag > 0, mag, 1.0)))
+    e = np.maximum(e, -126.0)
+    half = np.where(mag > 0, np.ldexp(1.0, (e - 8).astype(np.int64)), 2.0 ** -134)
+    return b - half, b + half
+
+
+def certify_mx_output(gd, gs, own_bits, cu, mode, label=""):
+    """Certify every E8M0 code and E4M3 byte of an MXFP8 output that was quantized from FP32 values y
+    whose bf16 rounding the same pass wrote (own_bits): y lies in the bf16 rounding interval [lo, hi] of
+    its own bf16 value, so
+      * each block code must be the MX code (exponent of the block maximum minus 8) of some block
+        maximum in [max lo, max hi] of the block's magnitudes;
+      * each byte must decode, at that code, to a value between E4M3(lo 2^(127-code)) and
+        E4M3(hi 2^(127-code)) (round to nearest even, saturating at 448): a truncating pack or an
+        off-by-one byte falls outside that range whenever the interval does not straddle a midpoint.
+    mode: ROW32 (1 x 32 along the columns, codes [T][C/32]) or SQ32 (32 x 32 from each sequence start,
+    codes [NB][C/32])."""
+    dec = e4m3_table()
+    T, C = own_bits.shape
+    lo, hi = bf16_rounding_interval(own_bits)
+    mag_lo = np.where((lo <= 0) & (hi >= 0), 0.0, np.minimum(np.abs(lo), np.abs(hi)))
+    mag_hi = np.maximum(np.abs(lo), np.abs(hi))
+    lens = [int(v) for v in np.diff(np.asarray(cu, np.int64))]
+    if mode == oracle.ROW32:
+        row_block = np.arange(T)
+        nb = T
+    else:
+        row_block = np.empty(T, np.int64)
+        for i, (a, b) in enumerate(token_blocks(lens)):
+            row_block[a:b] = i
+        nb = len(token_blocks(lens))
+    assert gs.shape == (nb, C // 32), (gs.shape, nb)
+    amax_lo = np.zeros((nb, C // 32))
+    amax_hi = np.zeros((nb, C // 32))
+    np.maximum.at(amax_lo, row_block, mag_lo.reshape(T, C // 32, 32).max(axis=2))
+    np.maximum.at(amax_hi, row_block, mag_hi.reshape(T, C // 32, 32).max(axis=2))
+    code_lo = np.vectorize(oracle.e8m0_code)(amax_lo)
+    code_hi = np.vectorize(oracle.e8m0_code)(amax_hi)
+    bad = np.argwhere((gs < code_lo) | (gs > code_hi))
+    assert bad.size == 0, f"{label}: {len(bad)} block codes outside the MX codes of their maxima, e.g. {bad[:3]}"
+    code = gs[row_block][:, np.repeat(np.arange(C // 32), 32)].astype(np.int64)
+    inv = np.ldexp(1.0, 127 - code)
+    elo = oracle.e4m3_encode_array((lo * inv).astype(np.float32)).reshape(T, C)
+    ehi = oracle.e4m3_encode_array((hi * inv).astype(np.float32)).reshape(T, C)
+    v = dec[gd]
+    ok = (v >= dec[elo]) & (v <= dec[ehi])
+    assert ok.all(), (f"{label}: {int((~ok).sum())} of {ok.size} E4M3 bytes are not the rounding of a value in "
+                      f"their bf16 interval, e.g. at {np.argwhere(~ok)[:3].tolist()}")
+    say(f"  {label}: {gd.size} bytes and {gs.size} codes certified against the same pass's bf16 values")
+
+
 class AttnCase:
-    """Seeded attention problem: bf16 Q, K, V, dO [T, H*128], per-sequence lengths."""
+    """Seeded attention problem: bf16 Q, K, V, dO [T, H*128], per-sequence lengths. `inputs` (a dict of
+    bf16 bit arrays q, k, v, do) replaces the seeded normal draws for structured cases."""
 
     def __init__(self, seed, lens_q, lens_k=None, H=1, causal=False, outlier_p=0.0, fwd_modes="train",
-                 softmax_scale=None):
+                 softmax_scale=None, inputs=None):
         self.seed, self.H, self.D, self.causal = seed, H, 128, causal
         self.lens_q = list(lens_q)
         self.lens_k = list(lens_k if lens_k is not None else lens_q)
@@ -96,17 +232,22 @@ class AttnCase:
         self.Tq, self.Tk = int(self.cu_q[-1]), int(self.cu_k[-1])
         C = H * 128
         self.C = C
-        kw = dict(outlier_p=outlier_p)
-        self.q = synth.normal_bf16(seed, synth.STREAM_Q, (self.Tq, C), **kw)
-        self.k = synth.normal_bf16(seed, synth.STREAM_K, (self.Tk, C), **kw)
-        self.v = synth.normal_bf16(seed, synth.STREAM_V, (self.Tk, C), **kw)
-        self.do = synth.normal_bf16(seed, synth.STREAM_DO, (self.Tq, C), **kw)
+        if inputs is not None:
+            self.q, self.k, self.v, self.do = (np.ascontiguousarray(inputs[n], np.uint16) for n in ("q", "k", "v", "do"))
+            assert self.q.shape == (self.Tq, C) and self.k.shape == (self.Tk, C)
+        else:
+            kw = dict(outlier_p=outlier_p)
+            self.q = synth.normal_bf16(seed, synth.STREAM_Q, (self.Tq, C), **kw)
+            self.k = synth.normal_bf16(seed, synth.STREAM_K, (self.Tk, C), **kw)
+            self.v = synth.normal_bf16(seed, synth.STREAM_V, (self.Tk, C), **kw)
+            self.do = synth.normal_bf16(seed, synth.STREAM_DO, (self.Tq, C), **kw)
         self.c = float(np.float32(1.0 / math.sqrt(128) if softmax_scale is None else softmax_scale))
         # operand modes: training (Q, K SQ32; V COL32 fwd, ROW32 bwd) or forward-only (Q, K ROW32)
         self.qk_mode = oracle.SQ32 if fwd_modes == "train" else oracle.ROW32
 
     # ---------------- GPU path ----------------
     def run_gpu_fwd(self, p_scale=mx.P_STATIC):
+        """mxfa_fwd / mxfa_fwd_p_scale through the ABI into NaN-prefilled, guarded outputs."""
         self.cu_q_d, self.cu_k_d = cu_dev(self.cu_q), cu_dev(self.cu_k)
         self.q_d, self.k_d = to_dev_bf16(self.q), to_dev_bf16(self.k)
         self.v_d, self.do_d = to_dev_bf16(self.v), to_dev_bf16(self.do)
@@ -118,49 +259,76 @@ class AttnCase:
                                 mx.MxOperand(self.gv[0], self.gv[1], mx.COL32),
                                 self.cu_q_d, self.cu_k_d, len(self.lens_q), max(self.lens_q), max(self.lens_k),
                                 self.Tq, self.Tk, self.H, 128, self.c, self.causal)
-        o, lse = mx.fwd(self.args, p_scale=p_scale)
+        o, lse = Guarded((self.Tq, self.C), torch.bfloat16), Guarded((self.H, self.Tq), torch.float32)
+        if p_scale == mx.P_STATIC:
+            mx.mxfa_fwd(self.args, o.t, lse.t)
+        else:
+            mx.mxfa_fwd_p_scale(self.args, p_scale, o.t, lse.t)
         torch.cuda.synchronize()
-        self.o_dev, self.lse_dev = o, lse
-        return to_host_bf16_bits(o), lse.cpu().numpy()
+        o.check("O"), lse.check("LSE")
+        self.o_dev, self.lse_dev = o.t, lse.t
+        return to_host_bf16_bits(o.t), lse.t.cpu().numpy()
 
-    def run_gpu_bwd(self, dq_mode, sigma=1.0):
+    def bwd_operands(self):
         gvd = gpu_quantize_padded(self.v_d, self.cu_k, self.cu_k_d, mx.ROW32)
         gdo = gpu_quantize_padded(self.do_d, self.cu_q, self.cu_q_d, mx.SQ32)
-        dq, dk, dv = mx.bwd(self.args, mx.MxOperand(gvd[0], gvd[1], mx.ROW32), mx.MxOperand(gdo[0], gdo[1], mx.SQ32),
-                            self.o_dev, self.do_d, self.lse_dev, dq_mode, sigma)
+        return mx.MxOperand(gvd[0], gvd[1], mx.ROW32), mx.MxOperand(gdo[0], gdo[1], mx.SQ32)
+
+    def run_gpu_bwd(self, dq_mode, sigma=1.0, o=None, lse=None):
+        """mxfa_bwd through the ABI: NaN-prefilled, guarded gradients and a guarded workspace. o and lse
+        default to the GPU forward's outputs."""
+        vop, doop = self.bwd_operands()
+        need = mx.mxfa_bwd_workspace_size(self.args, dq_mode)
+        ws = Guarded((need,), torch.uint8)
+        g = [Guarded((T, self.C), torch.bfloat16) for T in (self.Tq, self.Tk, self.Tk)]
+        mx.mxfa_bwd(self.args, vop, doop, self.o_dev if o is None else o, self.do_d,
+                    self.lse_dev if lse is None else lse, dq_mode, sigma, ws.t, need, *(x.t for x in g))
         torch.cuda.synchronize()
-        return tuple(to_host_bf16_bits(t) for t in (dq, dk, dv))
+        ws.check("workspace")
+        for x, n in zip(g, ("dQ", "dK", "dV")):
+            x.check(n)
+        return tuple(to_host_bf16_bits(x.t) for x in g)
 
     def run_gpu_bwd_mx_out(self, dq_mode, sigma=1.0, with_bf16=True):
-        """mxfa_bwd_mx_out on the same operands: ((dq, dk, dv) bf16 bits or None, six numpy arrays:
-        dq, dq_scale, dk, dk_scale, dv, dv_scale)."""
-        gvd = gpu_quantize_padded(self.v_d, self.cu_k, self.cu_k_d, mx.ROW32)
-        gdo = gpu_quantize_padded(self.do_d, self.cu_q, self.cu_q_d, mx.SQ32)
-        bf, mxo = mx.bwd_mx_out(self.args, mx.MxOperand(gvd[0], gvd[1], mx.ROW32),
-                                mx.MxOperand(gdo[0], gdo[1], mx.SQ32), self.o_dev, self.do_d, self.lse_dev, self.cu_q,
-                                self.cu_k, dq_mode, sigma, with_bf16=with_bf16)
+        """mxfa_bwd_mx_out on the same operands, guarded and NaN-prefilled outputs: ((dq, dk, dv) bf16 bits or
+        None, six numpy arrays: dq, dq_scale, dk, dk_scale, dv, dv_scale)."""
+        vop, doop = self.bwd_operands()
+        need = mx.mxfa_bwd_workspace_size(self.args, dq_mode)
+        ws = Guarded((need,), torch.uint8)
+        nbq, nbk = int(np.sum((np.array(self.lens_q) + 31) // 32)), int(np.sum((np.array(self.lens_k) + 31) // 32))
+        mxo = [Guarded(shape, torch.uint8) for shape in ((self.Tq, self.C), (nbq, self.C // 32), (self.Tk, self.C),
+                                                          (nbk, self.C // 32), (self.Tk, self.C), (nbk, self.C // 32))]
+        bf = [Guarded((T, self.C), torch.bfloat16) for T in (self.Tq, self.Tk, self.Tk)] if with_bf16 else None
+        mx.mxfa_bwd_mx_out(self.args, vop, doop, self.o_dev, self.do_d, self.lse_dev, dq_mode, sigma, ws.t, need,
+                           *((x.t for x in bf) if bf else (None, None, None)), [x.t for x in mxo])
         torch.cuda.synchronize()
-        bits = tuple(to_host_bf16_bits(t) for t in bf) if bf is not None else None
-        return bits, tuple(t.cpu().numpy() for t in mxo)
+        ws.check("workspace")
+        for x in mxo + (bf or []):
+            x.check("MXFP8 backward output")
+        bits = tuple(to_host_bf16_bits(x.t) for x in bf) if bf is not None else None
+        return bits, tuple(x.t.cpu().numpy() for x in mxo)
 
     # ---------------- oracle ----------------
-    def run_oracle_fwd(self, p_scale=oracle.P_STATIC):
-        self.oq = oracle.quantize(self.q, self.cu_q, self.qk_mode)
-        self.ok = oracle.quantize(self.k, self.cu_k, self.qk_mode)
-        self.ov = oracle.quantize(self.v, self.cu_k, oracle.COL32)
-        o16, o32, lse = oracle.attn_fwd_mx(self.oq[0], self.oq[1], self.qk_mode, self.ok[0], self.ok[1], self.qk_mode,
-                                           self.ov[0], self.ov[1], oracle.COL32, self.cu_q, self.cu_k, self.H, 128,
-                                           self.c, self.causal, p_scale=p_scale)
+    def run_oracle_fwd(self, p_scale=oracle.P_STATIC, orc=oracle):
+        self.oq = orc.quantize(self.q, self.cu_q, self.qk_mode)
+        self.ok = orc.quantize(self.k, self.cu_k, self.qk_mode)
+        self.ov = orc.quantize(self.v, self.cu_k, orc.COL32)
+        o16, o32, lse = orc.attn_fwd_mx(self.oq[0], self.oq[1], self.qk_mode, self.ok[0], self.ok[1], self.qk_mode,
+                                        self.ov[0], self.ov[1], orc.COL32, self.cu_q, self.cu_k, self.H, 128,
+                                        self.c, self.causal, p_scale=p_scale)
         self.o16_ref, self.lse_ref = o16, lse
         return o16, o32, lse
 
-    def run_oracle_bwd(self, dq_mode, sigma=1.0):
-        """The oracle's backward from the oracle's own forward outputs (O in bf16 and LSE)."""
-        ovd = oracle.quantize(self.v, self.cu_k, oracle.ROW32)
-        odo = oracle.quantize(self.do, self.cu_q, oracle.SQ32)
-        return oracle.attn_bwd_mx(self.oq[0], self.oq[1], self.ok[0], self.ok[1], ovd[0], ovd[1], oracle.ROW32,
-                                  odo[0], odo[1], self.o16_ref, self.do, self.lse_ref, self.cu_q, self.cu_k, self.H,
-                                  128, self.c, self.causal, dq_mode, sigma)
+    def run_oracle_bwd(self, dq_mode, sigma=1.0, orc=oracle, o16=None, lse=None):
+        """The oracle's backward, by default from the oracle's own forward outputs (O in bf16 and LSE)."""
+        ovd = orc.quantize(self.v, self.cu_k, orc.ROW32)
+        odo = orc.quantize(self.do, self.cu_q, orc.SQ32)
+        oq = orc.quantize(self.q, self.cu_q, orc.SQ32)
+        ok = orc.quantize(self.k, self.cu_k, orc.SQ32)
+        return orc.attn_bwd_mx(oq[0], oq[1], ok[0], ok[1], ovd[0], ovd[1], orc.ROW32,
+                               odo[0], odo[1], self.o16_ref if o16 is None else o16, self.do,
+                               self.lse_ref if lse is None else lse, self.cu_q, self.cu_k, self.H,
+                               128, self.c, self.causal, dq_mode, sigma)
 
 
 def check_o(o_gpu_bits, o_ref32, lse_gpu, lse_ref, label="", qk_outliers_full_length=False, peaked=False):
@@ -287,9 +455,15 @@ class LinearCase:
     def run_gpu(self):
         xo = mx.MxOperand(torch.from_numpy(self.xd).cuda(), torch.from_numpy(self.xs).cuda(), self.x_mode)
         wo = mx.MxOperand(torch.from_numpy(self.wd).cuda(), torch.from_numpy(self.ws).cuda(), mx.ROW32)
-        data, scale, scale_t = mx.linear_quantize(xo, wo, self.cu, cu_dev(self.cu))
+        nb = int(np.sum((np.array(self.lens) + 31) // 32))
+        data, scale, scale_t = (Guarded((self.T, self.C_out), torch.uint8), Guarded((nb, self.C_out // 32), torch.uint8),
+                                Guarded((self.C_out // 32, nb), torch.uint8))
+        mx.mxfa_linear_quantize(xo, wo, self.T, self.C_in, self.C_out, cu_dev(self.cu), len(self.lens), max(self.lens),
+                                data.t, scale.t, scale_t.t)
         torch.cuda.synchronize()
-        return data.cpu().numpy(), scale.cpu().numpy(), scale_t.cpu().numpy()
+        for g in (data, scale, scale_t):
+            g.check("linear_quantize output")
+        return data.t.cpu().numpy(), scale.t.cpu().numpy(), scale_t.t.cpu().numpy()
 
     def run_oracle(self):
         """(data, scale, scale_t, y, yabs) with yabs = sum_k |deq(X)_tk deq(W)_nk|."""

@@ -24,7 +24,7 @@ import torch
 import oracle
 import precision_mxfp8_block_amd as mx
 import synth
-from mx_cases import (LinearCase, certify_linear, check_grads, check_o, cu_dev, gpu_quantize_padded, say,
+from mx_cases import (Guarded, LinearCase, certify_linear, check_grads, check_o, cu_dev, gpu_quantize_padded, say,
                       to_dev_bf16, to_host_bf16_bits)
 
 pytestmark = pytest.mark.gpu
@@ -51,8 +51,29 @@ def host(t):
     return t.detach().cpu().numpy()
 
 
+def xcd_slices(nseq, H, ntiles_per_pair=1, n=8):
+    """One (sequence, head) pair from each of the 8 contiguous ranges of (sequence, head) items the
+    attention kernels' grid remap gives the 8 XCDs (items are ordered sequence, head, tile), at a
+    different offset inside each range."""
+    pairs = nseq * H
+    per = pairs // n
+    out = []
+    for x in range(n):
+        p = x * per + (3 * x + 1) % max(per, 1)
+        out.append((p // H, p % H))
+    return out
+
+
+def all_written(t, label):
+    """Outputs are NaN-prefilled: a non-finite element anywhere in the full tensor is one the kernels
+    never wrote (the inputs here produce finite outputs)."""
+    bad = int((~torch.isfinite(t.float())).sum())
+    assert bad == 0, f"{label}: {bad} elements not written (still NaN) or non-finite"
+
+
 class FullAttn:
-    """Full-size attention problem on the GPU plus per-slice oracle checks."""
+    """Full-size attention problem on the GPU plus oracle checks of sampled (sequence, head) slices, all
+    slices in one oracle call (one sequence per slice, so they run on parallel threads)."""
 
     def __init__(self, seed, lens_q, lens_k, H, causal=False, outlier_p=0.0, qk_mode=mx.SQ32):
         self.outliers = outlier_p > 0
@@ -62,6 +83,7 @@ class FullAttn:
         self.Tq, self.Tk = int(self.cu_q[-1]), int(self.cu_k[-1])
         self.H, self.causal, self.qk_mode = H, causal, qk_mode
         C = H * D
+        self.C = C
         kw = dict(outlier_p=outlier_p)
         say(f"  generating inputs Tq={self.Tq} Tk={self.Tk} C={C}")
         self.x = {"q": synth.normal_bf16(seed, synth.STREAM_Q, (self.Tq, C), **kw),
@@ -80,70 +102,102 @@ class FullAttn:
                                 mx.MxOperand(self.gv[0], self.gv[1], mx.COL32),
                                 self.cu_q_d, self.cu_k_d, len(self.lens_q), max(self.lens_q), max(self.lens_k),
                                 self.Tq, self.Tk, self.H, D, C_SCALE, self.causal)
-        self.o, self.lse = mx.fwd(self.args, p_scale=p_scale)
+        o, lse = Guarded((self.Tq, self.C), torch.bfloat16), Guarded((self.H, self.Tq), torch.float32)
+        if p_scale == mx.P_STATIC:
+            mx.mxfa_fwd(self.args, o.t, lse.t)
+        else:
+            mx.mxfa_fwd_p_scale(self.args, p_scale, o.t, lse.t)
         torch.cuda.synchronize()
+        o.check("O"), lse.check("LSE")
+        all_written(o.t, "O")
+        self.o, self.lse = o.t, lse.t
 
     def gpu_bwd(self, dq_mode, sigma):
         self.gvd = gpu_quantize_padded(self.dev["v"], self.cu_k, self.cu_k_d, mx.ROW32)
         self.gdo = gpu_quantize_padded(self.dev["do"], self.cu_q, self.cu_q_d, mx.SQ32)
-        g = mx.bwd(self.args, mx.MxOperand(self.gvd[0], self.gvd[1], mx.ROW32),
-                   mx.MxOperand(self.gdo[0], self.gdo[1], mx.SQ32), self.o, self.dev["do"], self.lse, dq_mode, sigma)
+        need = mx.mxfa_bwd_workspace_size(self.args, dq_mode)
+        ws = Guarded((need,), torch.uint8)
+        g = [Guarded((T, self.C), torch.bfloat16) for T in (self.Tq, self.Tk, self.Tk)]
+        mx.mxfa_bwd(self.args, mx.MxOperand(self.gvd[0], self.gvd[1], mx.ROW32),
+                    mx.MxOperand(self.gdo[0], self.gdo[1], mx.SQ32), self.o, self.dev["do"], self.lse, dq_mode, sigma,
+                    ws.t, need, *(x.t for x in g))
         torch.cuda.synchronize()
-        return g
+        ws.check("workspace")
+        for x, n in zip(g, ("dQ", "dK", "dV")):
+            x.check(n)
+            all_written(x.t, n)
+        return tuple(x.t for x in g)
 
-    def _xs(self, name, s, h):
+    def _stack(self, name, slices):
+        """The (sequence, head) slices of one input stacked as the sequences of a one-head batch."""
         cu = self.cu_q if name in ("q", "do") else self.cu_k
-        return np.ascontiguousarray(self.x[name][int(cu[s]):int(cu[s + 1]), h * D:(h + 1) * D])
+        return np.ascontiguousarray(np.concatenate(
+            [self.x[name][int(cu[s]):int(cu[s + 1]), h * D:(h + 1) * D] for s, h in slices]))
 
-    def _check_quant(self, name, gpu, mode, s, h, ref):
-        """The GPU's full-size quantization, sliced, equals the oracle's quantization of the slice."""
+    def _stack_cu(self, slices, side):
+        lens = self.lens_q if side == "q" else self.lens_k
+        return synth.cu_seqlens([lens[s] for s, _ in slices])
+
+    def _check_quant(self, name, gpu, mode, slices, ref):
+        """The GPU's full-size quantization, sliced, equals the oracle's quantization of the slices."""
         cu, boff = (self.cu_q, self.bq) if name in ("q", "do") else (self.cu_k, self.bk)
-        rows = slice(int(cu[s]), int(cu[s + 1]))
-        np.testing.assert_array_equal(host(gpu[0][rows, h * D:(h + 1) * D]), ref[0], err_msg=f"{name} payload")
-        np.testing.assert_array_equal(scale_slice(host(gpu[2]), mode, cu, boff, s, h), ref[1], err_msg=f"{name} scale")
+        cs = self._stack_cu(slices, "q" if name in ("q", "do") else "k")
+        bs = block_offsets(np.diff(cs))
+        for i, (s, h) in enumerate(slices):
+            rows = slice(int(cu[s]), int(cu[s + 1]))
+            np.testing.assert_array_equal(host(gpu[0][rows, h * D:(h + 1) * D]), ref[0][int(cs[i]):int(cs[i + 1])],
+                                          err_msg=f"{name} payload, slice {s, h}")
+            rrows = slice(int(cs[i]), int(cs[i + 1])) if mode == mx.ROW32 else slice(int(bs[i]), int(bs[i + 1]))
+            np.testing.assert_array_equal(scale_slice(host(gpu[2]), mode, cu, boff, s, h), ref[1][rrows],
+                                          err_msg=f"{name} scale, slice {s, h}")
 
-    def oracle_fwd_slice(self, s, h, p_scale=oracle.P_STATIC):
-        Lq, Lk = self.lens_q[s], self.lens_k[s]
-        cq, ck = np.array([0, Lq], np.int32), np.array([0, Lk], np.int32)
-        self.rq = oracle.quantize(self._xs("q", s, h), cq, self.qk_mode)
-        self.rk = oracle.quantize(self._xs("k", s, h), ck, self.qk_mode)
-        rv = oracle.quantize(self._xs("v", s, h), ck, oracle.COL32)
-        self._check_quant("q", self.gq, self.qk_mode, s, h, self.rq)
-        self._check_quant("k", self.gk, self.qk_mode, s, h, self.rk)
-        self._check_quant("v", self.gv, mx.COL32, s, h, rv)
+    def oracle_fwd_slices(self, slices, p_scale=oracle.P_STATIC):
+        cq, ck = self._stack_cu(slices, "q"), self._stack_cu(slices, "k")
+        say(f"  oracle forward on {len(slices)} slices {slices}")
+        self.rq = oracle.quantize(self._stack("q", slices), cq, self.qk_mode)
+        self.rk = oracle.quantize(self._stack("k", slices), ck, self.qk_mode)
+        rv = oracle.quantize(self._stack("v", slices), ck, oracle.COL32)
+        self._check_quant("q", self.gq, self.qk_mode, slices, self.rq)
+        self._check_quant("k", self.gk, self.qk_mode, slices, self.rk)
+        self._check_quant("v", self.gv, mx.COL32, slices, rv)
         o16, o32, lse = oracle.attn_fwd_mx(self.rq[0], self.rq[1], self.qk_mode, self.rk[0], self.rk[1], self.qk_mode,
                                            rv[0], rv[1], oracle.COL32, cq, ck, 1, D, C_SCALE, self.causal,
                                            p_scale=p_scale)
-        rows = slice(int(self.cu_q[s]), int(self.cu_q[s + 1]))
-        o_g = to_host_bf16_bits(self.o[rows, h * D:(h + 1) * D])
-        lse_g = host(self.lse[h, rows])[None, :]
-        check_o(o_g, o32, lse_g, lse, f"seq {s} head {h}", qk_outliers_full_length=self.outliers)
+        for i, (s, h) in enumerate(slices):
+            rows = slice(int(self.cu_q[s]), int(self.cu_q[s + 1]))
+            r = slice(int(cq[i]), int(cq[i + 1]))
+            o_g = to_host_bf16_bits(self.o[rows, h * D:(h + 1) * D])
+            lse_g = host(self.lse[h, rows])[None, :]
+            check_o(o_g, o32[r], lse_g, lse[:, r], f"seq {s} head {h}", qk_outliers_full_length=self.outliers)
         return o16, lse
 
-    def oracle_bwd_slice(self, s, h, o16, lse, g, dq_mode, sigma):
-        Lq, Lk = self.lens_q[s], self.lens_k[s]
-        cq, ck = np.array([0, Lq], np.int32), np.array([0, Lk], np.int32)
-        rvd = oracle.quantize(self._xs("v", s, h), ck, oracle.ROW32)
-        rdo = oracle.quantize(self._xs("do", s, h), cq, oracle.SQ32)
-        self._check_quant("v", self.gvd, mx.ROW32, s, h, rvd)
-        self._check_quant("do", self.gdo, mx.SQ32, s, h, rdo)
+    def oracle_bwd_slices(self, slices, o16, lse, g, dq_mode, sigma):
+        cq, ck = self._stack_cu(slices, "q"), self._stack_cu(slices, "k")
+        say(f"  oracle backward on {len(slices)} slices, dq_mode {dq_mode}")
+        rvd = oracle.quantize(self._stack("v", slices), ck, oracle.ROW32)
+        rdo = oracle.quantize(self._stack("do", slices), cq, oracle.SQ32)
+        self._check_quant("v", self.gvd, mx.ROW32, slices, rvd)
+        self._check_quant("do", self.gdo, mx.SQ32, slices, rdo)
         ref = oracle.attn_bwd_mx(self.rq[0], self.rq[1], self.rk[0], self.rk[1], rvd[0], rvd[1], oracle.ROW32,
-                                 rdo[0], rdo[1], o16, self._xs("do", s, h), lse, cq, ck, 1, D, C_SCALE, self.causal,
-                                 dq_mode, sigma)
+                                 rdo[0], rdo[1], o16, self._stack("do", slices), lse, cq, ck, 1, D, C_SCALE,
+                                 self.causal, dq_mode, sigma)
         assert ref["overflow"] == 0, "oracle FP16 accumulator overflowed: sigma too large for this input"
-        qr = slice(int(self.cu_q[s]), int(self.cu_q[s + 1]))
-        kr = slice(int(self.cu_k[s]), int(self.cu_k[s + 1]))
-        cols = slice(h * D, (h + 1) * D)
-        gs = (to_host_bf16_bits(g[0][qr, cols]), to_host_bf16_bits(g[1][kr, cols]), to_host_bf16_bits(g[2][kr, cols]))
-        check_grads(gs, ref, f"seq {s} head {h} dq_mode {dq_mode}", qk_outliers_full_length=self.outliers)
+        for i, (s, h) in enumerate(slices):
+            qr = slice(int(self.cu_q[s]), int(self.cu_q[s + 1]))
+            kr = slice(int(self.cu_k[s]), int(self.cu_k[s + 1]))
+            rq_, rk_ = slice(int(cq[i]), int(cq[i + 1])), slice(int(ck[i]), int(ck[i + 1]))
+            cols = slice(h * D, (h + 1) * D)
+            gs = (to_host_bf16_bits(g[0][qr, cols]), to_host_bf16_bits(g[1][kr, cols]),
+                  to_host_bf16_bits(g[2][kr, cols]))
+            sub = {"dq_f": ref["dq_f"][rq_], "dk_f": ref["dk_f"][rk_], "dv_f": ref["dv_f"][rk_]}
+            check_grads(gs, sub, f"seq {s} head {h} dq_mode {dq_mode}", qk_outliers_full_length=self.outliers)
 
 
 def test_llm_forward_B4_H16_N4096():
     say("full-size forward: B=4 H=16 N=4096, Q/K ROW32, V COL32")
     fa = FullAttn(2, [4096] * 4, [4096] * 4, 16, qk_mode=mx.ROW32)
     fa.gpu_fwd()
-    for s, h in [(0, 0), (3, 15), (1, 9)]:
-        fa.oracle_fwd_slice(s, h)
+    fa.oracle_fwd_slices(xcd_slices(4, 16))
 
 
 @pytest.mark.parametrize("dq_mode,sigma", [(mx.DQ_FP16_STATIC, 1.0), (mx.DQ_FP32, 1.0)])
@@ -152,9 +206,9 @@ def test_training_step_B4_H16_N4096(dq_mode, sigma):
     fa = FullAttn(2, [4096] * 4, [4096] * 4, 16)
     fa.gpu_fwd()
     g = fa.gpu_bwd(dq_mode, sigma)
-    for s, h in [(0, 0), (2, 11)]:
-        o16, lse = fa.oracle_fwd_slice(s, h)
-        fa.oracle_bwd_slice(s, h, o16, lse, g, dq_mode, sigma)
+    slices = xcd_slices(4, 16)
+    o16, lse = fa.oracle_fwd_slices(slices)
+    fa.oracle_bwd_slices(slices, o16, lse, g, dq_mode, sigma)
 
 
 def test_training_forward_dynamic_p_B4_H16_N4096():
@@ -162,20 +216,18 @@ def test_training_forward_dynamic_p_B4_H16_N4096():
     say("full-size forward, dynamic P scale: B=4 H=16 N=4096, Q/K SQ32, V COL32")
     fa = FullAttn(2, [4096] * 4, [4096] * 4, 16)
     fa.gpu_fwd(mx.P_BLOCK_DYNAMIC)
-    for s, h in [(0, 3), (3, 14)]:
-        fa.oracle_fwd_slice(s, h, oracle.P_DYNAMIC)
+    fa.oracle_fwd_slices(xcd_slices(4, 16)[::2], oracle.P_DYNAMIC)
 
 
-def test_causal_outliers_B4_H16_N8192():
-    say("full-size causal: B=4 H=16 N=8192, 0.5% x64 outliers, FP16 (sigma 2^-4) and FP32 dQ")
+@pytest.mark.parametrize("dq_mode,sigma", [(mx.DQ_FP16_STATIC, 0.0625), (mx.DQ_FP32, 1.0)])
+def test_causal_outliers_B4_H16_N8192(dq_mode, sigma):
+    say(f"full-size causal: B=4 H=16 N=8192, 0.5% x64 outliers, dq_mode={dq_mode} sigma={sigma}")
     fa = FullAttn(3, [8192] * 4, [8192] * 4, 16, causal=True, outlier_p=0.005)
     fa.gpu_fwd()
-    g16 = fa.gpu_bwd(mx.DQ_FP16_STATIC, 0.0625)
-    g32 = fa.gpu_bwd(mx.DQ_FP32, 1.0)
-    s, h = 1, 6
-    o16, lse = fa.oracle_fwd_slice(s, h)
-    fa.oracle_bwd_slice(s, h, o16, lse, g16, mx.DQ_FP16_STATIC, 0.0625)
-    fa.oracle_bwd_slice(s, h, o16, lse, g32, mx.DQ_FP32, 1.0)
+    g = fa.gpu_bwd(dq_mode, sigma)
+    slices = xcd_slices(4, 16)[::2]
+    o16, lse = fa.oracle_fwd_slices(slices)
+    fa.oracle_bwd_slices(slices, o16, lse, g, dq_mode, sigma)
 
 
 def test_jagged_32_sequences_H16():
@@ -185,10 +237,10 @@ def test_jagged_32_sequences_H16():
     fa.gpu_fwd()
     g = fa.gpu_bwd(mx.DQ_FP16_STATIC, 1.0)
     longest = int(np.argmax(lens))
-    ragged = next(i for i, L in enumerate(lens) if L % 128 and i != longest)
-    for s, h in [(longest, 3), (ragged, 12)]:
-        o16, lse = fa.oracle_fwd_slice(s, h)
-        fa.oracle_bwd_slice(s, h, o16, lse, g, mx.DQ_FP16_STATIC, 1.0)
+    ragged = [i for i, L in enumerate(lens) if L % 128 and i != longest]
+    slices = [(longest, 3), (ragged[0], 12), (ragged[len(ragged) // 2], 7), (ragged[-1], 0)]
+    o16, lse = fa.oracle_fwd_slices(slices)
+    fa.oracle_bwd_slices(slices, o16, lse, g, mx.DQ_FP16_STATIC, 1.0)
 
 
 # ---------------------------------------------------------------------------------------------

@@ -3,9 +3,12 @@
 Bit-exact for the quantizer, the scale scatter and the RMSNorm+quantize producer; certified
 mismatches only for the projection GEMM + quantize producer; tolerances of
 tests/mx_cases.py for attention (both P scales). The MXFP8 outputs of the forward (O) and the backward
-(dQ, dK, dV) are checked against the GPU's own bf16 results of the same pass (codes certified, values
-within one E4M3 step) and against the oracle's FP32 results through its quantizer. Sizes here finish in seconds on the oracle and still span several
-tiles and ragged tails; full-size sampled checks are in test_gpu_fullsize.py.
+(dQ, dK, dV) are certified byte by byte against the GPU's own bf16 results of the same pass and compared
+with the oracle's FP32 results through its quantizer. Every output is written into a NaN-prefilled
+buffer between guard bytes (mx_cases.Guarded). Sizes here finish in seconds on the oracle and still
+span several tiles and ragged tails; full-size sampled checks are in test_gpu_fullsize.py, the
+structure-sensitive backward cases in test_gpu_structure.py and the exhaustive quantizer sweep in
+test_gpu_quantize_sweep.py.
 """
 import numpy as np
 import pytest
@@ -14,8 +17,9 @@ import torch
 import oracle
 import precision_mxfp8_block_amd as mx
 import synth
-from mx_cases import (GRAD_REL_FRO, O_MAX_ABS, O_REL_FRO, AttnCase, LinearCase, certify_linear, check_grads, check_o, cu_dev,
-                      rel_fro, say, to_dev_bf16)
+from mx_cases import (GRAD_REL_FRO, O_MAX_ABS, O_REL_FRO, AttnCase, Guarded, LinearCase, certify_linear,
+                      certify_mx_output, check_grads, check_o, cu_dev, gpu_quantize, gpu_scale_scatter, rel_fro, say,
+                      to_dev_bf16, to_host_bf16_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -44,8 +48,7 @@ def test_quantize_bit_exact(mode, lens, C):
     T = int(cu[-1])
     x = _special_matrix(3 + mode, T, C)
     d_ref, s_ref, st_ref = oracle.quantize(x, cu, mode)
-    data, scale, scale_t = mx.quantize(to_dev_bf16(x), cu, cu_dev(cu), mode, want_scale_t=(mode == oracle.SQ32))
-    torch.cuda.synchronize()
+    data, scale, scale_t = gpu_quantize(to_dev_bf16(x), cu, cu_dev(cu), mode, want_scale_t=(mode == oracle.SQ32))
     np.testing.assert_array_equal(data.cpu().numpy(), d_ref)
     np.testing.assert_array_equal(scale.cpu().numpy(), s_ref)
     if mode == oracle.SQ32:
@@ -60,12 +63,12 @@ def test_quantize_strided_rows():
     cu = synth.cu_seqlens([T])
     d_ref, s_ref, _ = oracle.quantize(np.ascontiguousarray(full[:, :C]), cu, oracle.SQ32)
     xd = to_dev_bf16(full)
-    data = torch.empty((T, C), dtype=torch.uint8, device="cuda")
-    scale = torch.empty((2, C // 32), dtype=torch.uint8, device="cuda")
-    mx.mxfa_quantize(xd, ld, T, C, cu_dev(cu), 1, T, mx.SQ32, data, scale)
+    data, scale = Guarded((T, C), torch.uint8), Guarded((2, C // 32), torch.uint8)
+    mx.mxfa_quantize(xd, ld, T, C, cu_dev(cu), 1, T, mx.SQ32, data.t, scale.t)
     torch.cuda.synchronize()
-    np.testing.assert_array_equal(data.cpu().numpy(), d_ref)
-    np.testing.assert_array_equal(scale.cpu().numpy(), s_ref)
+    data.check("data"), scale.check("scale")
+    np.testing.assert_array_equal(data.t.cpu().numpy(), d_ref)
+    np.testing.assert_array_equal(scale.t.cpu().numpy(), s_ref)
 
 
 @pytest.mark.parametrize("C", [256, 2048])
@@ -80,9 +83,8 @@ def test_scale_scatter_bit_exact(mode, C):
     _, s_ref, _ = oracle.quantize(x, cu, mode)
     p_ref = oracle.scale_scatter(s_ref, cu, C, mode)
     cud = cu_dev(cu)
-    _, scale, _ = mx.quantize(to_dev_bf16(x), cu, cud, mode)
-    padded = mx.scale_scatter(scale, cu, cud, C, mode)
-    torch.cuda.synchronize()
+    _, scale, _ = gpu_quantize(to_dev_bf16(x), cu, cud, mode)
+    padded = gpu_scale_scatter(scale, cu, cud, C, mode)
     np.testing.assert_array_equal(padded.cpu().numpy(), p_ref)
 
 
@@ -111,11 +113,17 @@ def test_rmsnorm_quantize_bit_exact(lens, C, nan_at):
         x[nan_at] = 0x7FC0  # a quiet bf16 NaN: its row's blocks get code 255 and payload 0x7F
     gamma = (1.0 + 0.1 * synth.normal(6, synth.STREAM_WEIGHT, C)).astype(np.float32)
     d_ref, s_ref, st_ref, _ = oracle.rmsnorm_quantize(x, gamma, 1e-6, cu)
-    data, scale, scale_t = mx.rmsnorm_quantize(to_dev_bf16(x), torch.from_numpy(gamma).cuda(), 1e-6, cu, cu_dev(cu))
+    nb = s_ref.shape[0]
+    data, scale, scale_t = Guarded((T, C), torch.uint8), Guarded((nb, C // 32), torch.uint8), Guarded((C // 32, nb),
+                                                                                                      torch.uint8)
+    mx.mxfa_rmsnorm_quantize(to_dev_bf16(x), C, T, C, torch.from_numpy(gamma).cuda(), 1e-6, cu_dev(cu), len(lens),
+                             max(lens), data.t, scale.t, scale_t.t)
     torch.cuda.synchronize()
-    np.testing.assert_array_equal(data.cpu().numpy(), d_ref)
-    np.testing.assert_array_equal(scale.cpu().numpy(), s_ref)
-    np.testing.assert_array_equal(scale_t.cpu().numpy(), st_ref)
+    for g in (data, scale, scale_t):
+        g.check("rmsnorm output")
+    np.testing.assert_array_equal(data.t.cpu().numpy(), d_ref)
+    np.testing.assert_array_equal(scale.t.cpu().numpy(), s_ref)
+    np.testing.assert_array_equal(scale_t.t.cpu().numpy(), st_ref)
 
 
 LINEAR_CASES = [
@@ -200,29 +208,12 @@ def test_fwd_dynamic_p_peaky_softmax():
 
 
 def check_mx_sq32_output(label, gd, gs, own_bits, ref_f, cu, rel_tol):
-    """An SQ32 MXFP8 output against the GPU's own bf16 output written in the same pass (codes are the MX
-    codes of a value within bf16 rounding of each block's maximum; values within one E4M3 step of the
-    block's top binade, amax / 8, plus bf16 rounding) and against the oracle's FP32 result (codes
-    within one, relative Frobenius error within 2^-4 + the stated tolerance)."""
-    T, C = own_bits.shape
-    own = synth.bf16_bits_to_f32(own_bits).astype(np.float64)
-    lens = np.diff(np.asarray(cu, np.int64))
-    nb = int(np.sum((lens + 31) // 32))
-    # the block maximum of each (sequence-aligned 32-token block, 32 columns)
-    amax_b = np.zeros((nb, C // 32))
-    row_block = np.empty(T, np.int64)
-    b0 = 0
-    for s0, L in zip(cu[:-1], lens):
-        row_block[s0:s0 + L] = b0 + np.arange(L) // 32
-        b0 += (L + 31) // 32
-    np.maximum.at(amax_b, row_block, np.abs(own).reshape(T, C // 32, 32).max(axis=2))
-    code_lo = np.array([[oracle.e8m0_code(x * (1 - 2.0 ** -8)) for x in row] for row in amax_b])
-    code_hi = np.array([[oracle.e8m0_code(x * (1 + 2.0 ** -8)) for x in row] for row in amax_b])
-    assert gs.shape == (nb, C // 32)
-    assert np.all((gs >= code_lo) & (gs <= code_hi)), f"{label}: block code not the MX code of its maximum"
+    """An SQ32 MXFP8 output, certified byte by byte against the GPU's own bf16 output written in the same
+    pass (mx_cases.certify_mx_output), and against the oracle's FP32 result (codes within one, relative
+    Frobenius error within 2^-4 + the stated tolerance; the fractions of equal codes and bytes with the
+    oracle's quantization of its own result are printed)."""
+    certify_mx_output(gd, gs, own_bits, cu, oracle.SQ32, label)
     deq = oracle.dequantize(gd, gs, cu, oracle.SQ32)
-    amax_el = np.repeat(amax_b[row_block], 32, axis=1)
-    assert np.all(np.abs(deq - own) <= amax_el / 8 + 2.0 ** -8 * np.abs(own)), label
     rd, rs, _ = oracle.quantize(np.asarray(ref_f, np.float32), cu, oracle.SQ32)
     dc = gs.astype(np.int64) - rs.astype(np.int64)
     fro = rel_fro(deq, ref_f)
@@ -238,49 +229,46 @@ MX_OUT_CASES = [FWD_CASES[i] for i in (0, 2, 3, 4, 5)]
 @pytest.mark.parametrize("case", MX_OUT_CASES, ids=[c[0] for c in MX_OUT_CASES])
 def test_fwd_mx_out_parity(case):
     """O written as MXFP8 (ROW32 blocks along D) in the forward's epilogue.
-    * Against the GPU's own O (the bf16 O written in the same pass, within 2^-8 relative of the FP32 O
-      that was quantized): every block code is the MX rule's code of a value within 2^-8 of the block's
-      bf16 maximum, and every dequantized value is within one E4M3 step of the block's top binade
-      (amax / 8, saturation included) plus the bf16 rounding.
-    * Against the oracle (its FP32 O, which differs from the GPU's by the attention tolerance): the
-      dequantized output is within the O tolerance plus amax / 8, and within 2^-4 + the O tolerance in
-      relative Frobenius norm; the fractions of equal codes and bytes with the oracle's quantization
-      of its own O are printed.
+    * Against the GPU's own O (the bf16 O written in the same pass rounds the FP32 O that was quantized):
+      every block code and every byte certified by mx_cases.certify_mx_output.
+    * Against the oracle (its FP32 O, which differs from the GPU's by the attention tolerance): codes
+      within one, the dequantized output within the O tolerance plus amax / 8, and within 2^-4 + the O
+      tolerance in relative Frobenius norm; the fractions of equal codes and bytes are printed.
     * The bf16 O written in the same pass equals mxfa_fwd's bit for bit, and O_data does not depend on
-      whether bf16 O is written."""
+      whether bf16 O is written. Outputs are guarded and NaN-prefilled."""
     label, seed, lq, lk, H, causal, op, modes = case
     say(f"fwd MX O {label}")
     c = AttnCase(seed, lq, lk, H=H, causal=causal, outlier_p=op, fwd_modes=modes)
     o_bits, lse_g = c.run_gpu_fwd()
-    o16, od, osc, lse2 = mx.fwd_mx_out(c.args)
-    _, od_only, osc_only, _ = mx.fwd_mx_out(c.args, with_bf16=False)
-    torch.cuda.synchronize()
-    np.testing.assert_array_equal(o16.view(torch.int16).cpu().numpy().view(np.uint16), o_bits)
-    np.testing.assert_array_equal(lse2.cpu().numpy(), lse_g)
-    gd, gs = od.cpu().numpy(), osc.cpu().numpy()
-    np.testing.assert_array_equal(od_only.cpu().numpy(), gd)
-    np.testing.assert_array_equal(osc_only.cpu().numpy(), gs)
+    T, C = c.Tq, c.C
+
+    def run(with_bf16):
+        o16 = Guarded((T, C), torch.bfloat16) if with_bf16 else None
+        od, osc, lse2 = Guarded((T, C), torch.uint8), Guarded((T, C // 32), torch.uint8), Guarded((c.H, T), torch.float32)
+        mx.mxfa_fwd_mx_out(c.args, mx.P_STATIC, o16.t if o16 else None, od.t, osc.t, lse2.t)
+        torch.cuda.synchronize()
+        for g in (o16, od, osc, lse2):
+            if g is not None:
+                g.check("fwd_mx_out output")
+        return (to_host_bf16_bits(o16.t) if o16 else None), od.t.cpu().numpy(), osc.t.cpu().numpy(), lse2.t.cpu().numpy()
+    o16, gd, gs, lse2 = run(True)
+    _, od_only, osc_only, _ = run(False)
+    np.testing.assert_array_equal(o16, o_bits)
+    np.testing.assert_array_equal(lse2, lse_g)
+    np.testing.assert_array_equal(od_only, gd)
+    np.testing.assert_array_equal(osc_only, gs)
+    certify_mx_output(gd, gs, o_bits, c.cu_q, oracle.ROW32, f"{label} O")
     _, o32, _ = c.run_oracle_fwd()
     o32 = np.asarray(o32, np.float32)
     rd, rs, _ = oracle.quantize(o32, c.cu_q, oracle.ROW32)
     dc = gs.astype(np.int64) - rs.astype(np.int64)
     same_code, same_byte = float(np.mean(dc == 0)), float(np.mean(gd == rd))
     deq = oracle.dequantize(gd, gs, c.cu_q, oracle.ROW32)
-    T, C = o32.shape
     amax = np.repeat(np.abs(o32).reshape(T, C // 32, 32).max(axis=2), 32, axis=1)
     scale = max(1.0, float(np.abs(o32).max()))
     err = np.abs(deq - o32)
     say(f"  {label} codes equal {same_code:.4f}, payload bytes equal {same_byte:.4f}, "
         f"max err / (amax/8) {float(np.max(err / np.maximum(amax / 8, 1e-30))):.3f}, rel_fro {rel_fro(deq, o32):.3e}")
-    # against the GPU's own O
-    ob = synth.bf16_bits_to_f32(o_bits).astype(np.float64)
-    amax_b = np.abs(ob).reshape(T, C // 32, 32).max(axis=2)
-    code_lo = np.array([[oracle.e8m0_code(x * (1 - 2.0 ** -8)) for x in row] for row in amax_b])
-    code_hi = np.array([[oracle.e8m0_code(x * (1 + 2.0 ** -8)) for x in row] for row in amax_b])
-    assert np.all((gs >= code_lo) & (gs <= code_hi)), "block code not the MX code of the block maximum"
-    amax_bf = np.repeat(amax_b, 32, axis=1)
-    assert np.all(np.abs(deq - ob) <= amax_bf / 8 + 2.0 ** -8 * np.abs(ob))
-    # against the oracle
     assert np.abs(dc).max() <= 1
     assert np.all(err <= O_MAX_ABS * scale + amax / 8)
     assert rel_fro(deq, o32) <= 2.0 ** -4 + O_REL_FRO

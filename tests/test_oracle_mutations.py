@@ -13,6 +13,7 @@ import os
 import shutil
 import subprocess
 
+import numpy as np
 import pytest
 
 import test_oracle_worked_examples as worked
@@ -90,3 +91,46 @@ def test_pin_catches_mutant(name, mutant_modules):
     pin = worked.PINS[MUTANTS[name][1]]
     with pytest.raises(AssertionError):
         pin(mutant_modules[name])
+
+
+# ---------------------------------------------------------------------------------------------
+# The GPU structure cases can fail: each planted mistake moves some (32-token block, head) of a
+# gradient by more than ten times the stated tolerance on the inputs test_gpu_structure.py uses.
+# ---------------------------------------------------------------------------------------------
+
+SENSITIVITY = [
+    # (structured case, mutant, gradient that must move)
+    ("delta_sensitive", "delta_from_quantized_do", "dk"),
+    ("delta_sensitive", "delta_from_quantized_do", "dq"),
+    ("ds_block_range", "ds_blocks_32x128", "dk"),
+    ("p_subnormal_band", "bwd_p_scale_1", "dv"),
+]
+
+
+@pytest.mark.parametrize("case_name,mutant,grad", SENSITIVITY)
+def test_structured_case_separates_mutant(case_name, mutant, grad, mutant_modules):
+    import oracle
+    from mx_cases import GRAD_REL_FRO, AttnCase, block_rel_errors
+    from synth import structured
+    case = getattr(structured, case_name)()
+    lens, H = case["lens"], case["inputs"]["q"].shape[1] // 128
+    c = AttnCase(0, lens, None, H=H, softmax_scale=case["softmax_scale"], inputs=case["inputs"])
+    c.run_oracle_fwd()
+    good = c.run_oracle_bwd(1, 1.0)
+    bad = c.run_oracle_bwd(1, 1.0, orc=mutant_modules[mutant])
+    errs = block_rel_errors(bad[grad + "_f"], good[grad + "_f"], lens, H)
+    assert errs.max() >= 10 * GRAD_REL_FRO, (case_name, mutant, grad, errs.max())
+
+
+def test_fp16_rounding_case_separates_truncation(mutant_modules):
+    from mx_cases import AttnCase
+    from synth import structured
+    case = structured.dq_fp16_rounding()
+    vals = {}
+    import oracle
+    for name, orc in (("good", oracle), ("bad", mutant_modules["fp16_truncates"])):
+        c = AttnCase(0, case["lens_q"], case["lens_k"], H=1, softmax_scale=case["softmax_scale"], inputs=case["inputs"])
+        c.run_oracle_fwd(orc=orc)
+        r = c.run_oracle_bwd(1, 2.0 ** -23, orc=orc, o16=np.zeros((1, 128), np.uint16), lse=np.zeros((1, 1), np.float32))
+        vals[name] = float(r["dq_f"][0, 1])
+    assert vals == {"good": 1.5, "bad": 1.0}
