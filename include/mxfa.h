@@ -190,6 +190,23 @@ mxfa_status mxfa_bwd(const mxfa_attn_args* a, mxfa_mx v_d, mxfa_mx dout, const u
                      void* workspace, size_t workspace_bytes, uint16_t* dq, uint16_t* dk, uint16_t* dv,
                      void* stream);
 
+/* mxfa_bwd without a workspace argument, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). The workspace lives in a
+ * fixed array of mxfa_bwd_no_alloc_max_workspace() bytes (64 MiB) that the library holds on each GPU
+ * it runs on until the process ends; the call itself allocates and frees nothing.
+ *   Arguments, layouts and results as mxfa_bwd (dq, dk, dv required).
+ *   MXFA_ERR_INVALID (nothing enqueued) when mxfa_bwd_workspace_size(a, dq_mode) exceeds the array:
+ *   such problems need mxfa_bwd with a caller-owned workspace.
+ *   Every call on one GPU uses that GPU's array: calls that overlap in time on the same GPU (other
+ *   streams, other threads) race and give wrong results. Every byte the kernels read from the array is
+ *   written earlier in the same call, so nothing needs clearing between calls. */
+mxfa_status mxfa_bwd_no_alloc(const mxfa_attn_args* a, mxfa_mx v_d, mxfa_mx dout, const uint16_t* o,
+                              const uint16_t* dout_bf16, const float* lse, mxfa_dq_mode dq_mode, float dq_static_scale,
+                              uint16_t* dq, uint16_t* dk, uint16_t* dv, void* stream);
+
+/* Size in bytes of the fixed workspace array behind mxfa_bwd_no_alloc (host only). */
+size_t mxfa_bwd_no_alloc_max_workspace(void);
+
 /* MXFP8 gradient outputs (E4M3 payloads with their E8M0 codes). */
 typedef struct {
   uint8_t* dq;        /* [T_q, H*D] */

@@ -14,7 +14,8 @@ import torch
 __all__ = [
     "ROW32", "COL32", "SQ32", "DQ_FP32", "DQ_FP16_STATIC", "P_STATIC", "P_BLOCK_DYNAMIC", "MxfaError",
     "mxfa_quantize", "mxfa_varlen_scale_scatter", "mxfa_padded_token_rows", "mxfa_fwd", "mxfa_fwd_p_scale",
-    "mxfa_fwd_mx_out", "mxfa_bwd", "mxfa_bwd_mx_out", "fwd_mx_out", "bwd_mx_out",
+    "mxfa_fwd_mx_out", "mxfa_bwd", "mxfa_bwd_mx_out", "mxfa_bwd_no_alloc", "mxfa_bwd_no_alloc_max_workspace",
+    "fwd_mx_out", "bwd_mx_out",
     "mxfa_bwd_workspace_size", "mxfa_rmsnorm_quantize", "mxfa_linear_quantize", "mxfa_status_string",
     "mxfa_last_error_message", "MxOperand", "AttnArgs", "quantize", "scale_scatter", "fwd", "bwd",
     "rmsnorm_quantize", "linear_quantize",
@@ -75,6 +76,9 @@ def _load():
     lib.mxfa_bwd.argtypes = [ctypes.POINTER(_AttnArgs), _Mx, _Mx, P, P, P, i32, f32, P, ctypes.c_size_t, P, P, P, P]
     lib.mxfa_bwd_mx_out.argtypes = [ctypes.POINTER(_AttnArgs), _Mx, _Mx, P, P, P, i32, f32, P, ctypes.c_size_t, P, P, P,
                                     ctypes.POINTER(_GradMx), P]
+    lib.mxfa_bwd_no_alloc.argtypes = [ctypes.POINTER(_AttnArgs), _Mx, _Mx, P, P, P, i32, f32, P, P, P, P]
+    lib.mxfa_bwd_no_alloc_max_workspace.argtypes = []
+    lib.mxfa_bwd_no_alloc_max_workspace.restype = ctypes.c_size_t
     lib.mxfa_rmsnorm_quantize.argtypes = [P, i64, i64, i32, P, f32, P, i32, i32, P, P, P, P]
     lib.mxfa_linear_quantize.argtypes = [_Mx, _Mx, i64, i32, i32, P, i32, i32, P, P, P, P]
     lib.mxfa_status_string.argtypes = [i32]
@@ -82,7 +86,7 @@ def _load():
     lib.mxfa_last_error_message.argtypes = []
     lib.mxfa_last_error_message.restype = ctypes.c_char_p
     for n in ("mxfa_quantize", "mxfa_varlen_scale_scatter", "mxfa_fwd", "mxfa_fwd_p_scale", "mxfa_fwd_mx_out", "mxfa_bwd",
-              "mxfa_bwd_mx_out", "mxfa_rmsnorm_quantize",
+              "mxfa_bwd_mx_out", "mxfa_bwd_no_alloc", "mxfa_rmsnorm_quantize",
               "mxfa_linear_quantize"):
         getattr(lib, n).restype = i32
     _lib = lib
@@ -203,6 +207,18 @@ def mxfa_bwd(args, v_d, dout, o, dout_bf16, lse, dq_mode, dq_static_scale, works
     _check(_load().mxfa_bwd(ctypes.byref(a), v_d._c(), dout._c(), _ptr(o), _ptr(dout_bf16), _ptr(lse), dq_mode,
                             dq_static_scale, _ptr(workspace), workspace_bytes, _ptr(dq), _ptr(dk), _ptr(dv),
                             _stream(stream)), "mxfa_bwd")
+
+
+def mxfa_bwd_no_alloc(args, v_d, dout, o, dout_bf16, lse, dq_mode, dq_static_scale, dq, dk, dv, stream=None):
+    """mxfa_bwd with the library's fixed per-GPU workspace array (no workspace argument)."""
+    a = args._c()
+    _check(_load().mxfa_bwd_no_alloc(ctypes.byref(a), v_d._c(), dout._c(), _ptr(o), _ptr(dout_bf16), _ptr(lse),
+                                     dq_mode, dq_static_scale, _ptr(dq), _ptr(dk), _ptr(dv), _stream(stream)),
+           "mxfa_bwd_no_alloc")
+
+
+def mxfa_bwd_no_alloc_max_workspace():
+    return int(_load().mxfa_bwd_no_alloc_max_workspace())
 
 
 def mxfa_rmsnorm_quantize(x, ld_x, T, C, gamma, eps, cu_seqlens, nseq, max_seqlen, data_out, scale_out,

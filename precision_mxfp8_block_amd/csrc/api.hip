@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "mxfa.h"
@@ -84,6 +85,34 @@ mxfa_status check_attn(const mxfa_attn_args* a, const char* fn) {
   return MXFA_OK;
 }
 
+// Workspace of mxfa_bwd_no_alloc: one fixed array per GPU, resident until the process ends. In host
+// code `scratch` names a host-side stand-in, never the device memory: kernels get the device address
+// that hipGetSymbolAddress returns for the current device, fetched once per device and kept below.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (looked up on the first call per device).
+hipError_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return hipSuccess;
+}
+
 mxfa::AttnProblem to_problem(const mxfa_attn_args* a) {
   mxfa::AttnProblem p;
   p.q = {a->q.data, a->q.scale, (int)a->q.mode};
@@ -100,6 +129,69 @@ mxfa::AttnProblem to_problem(const mxfa_attn_args* a) {
   p.softmax_scale = a->softmax_scale;
   p.causal = a->causal ? 1 : 0;
   return p;
+}
+
+// Every argument check of the backward entry points (host only). workspace may be NULL only when
+// `library_workspace` is set (the fixed array of mxfa_bwd_no_alloc, whose size is checked here).
+mxfa_status check_bwd(const mxfa_attn_args* a, mxfa_mx v_d, mxfa_mx dout, const uint16_t* o, const uint16_t* dout_bf16,
+                      const float* lse, mxfa_dq_mode dq_mode, float dq_static_scale, const void* workspace,
+                      size_t workspace_bytes, const uint16_t* dq, const uint16_t* dk, const uint16_t* dv,
+                      const mxfa_grad_mx* mx_out, bool library_workspace, const char* fn) {
+  mxfa_status st = check_attn(a, fn);
+  if (st != MXFA_OK) return st;
+  if (a->q.mode != MXFA_SQ32 || a->k.mode != MXFA_SQ32)
+    return fail(MXFA_ERR_INVALID, "%s: q and k must be SQ32 (square blocks serve both GEMM directions)", fn);
+  if (v_d.mode != MXFA_ROW32 && v_d.mode != MXFA_SQ32)
+    return fail(MXFA_ERR_INVALID, "%s: v_d.mode must be ROW32 or SQ32", fn);
+  if (dout.mode != MXFA_SQ32) return fail(MXFA_ERR_INVALID, "%s: dout.mode must be SQ32", fn);
+  if (!v_d.data || !v_d.scale || !dout.data || !dout.scale)
+    return fail(MXFA_ERR_INVALID, "%s: NULL v_d/dout data or scale", fn);
+  if (!aligned(v_d.data, 16) || !aligned(v_d.scale, 16) || !aligned(dout.data, 16) || !aligned(dout.scale, 16))
+    return fail(MXFA_ERR_INVALID, "%s: v_d/dout not 16-byte aligned", fn);
+  if (!o || !dout_bf16 || !lse) return fail(MXFA_ERR_INVALID, "%s: NULL tensor argument", fn);
+  const bool bf16_out = dq || dk || dv;
+  if (bf16_out && !(dq && dk && dv)) return fail(MXFA_ERR_INVALID, "%s: dq, dk, dv must be all set or all NULL", fn);
+  if (!bf16_out && !mx_out) return fail(MXFA_ERR_INVALID, "%s: no gradient output", fn);
+  if (!aligned(o, 16) || !aligned(dout_bf16, 16) || !aligned(lse, 4) ||
+      (bf16_out && (!aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))))
+    return fail(MXFA_ERR_INVALID, "%s: misaligned tensor argument", fn);
+  if (mx_out) {
+    const mxfa_grad_mx& g = *mx_out;
+    if (!g.dq || !g.dq_scale || !g.dk || !g.dk_scale || !g.dv || !g.dv_scale)
+      return fail(MXFA_ERR_INVALID, "%s: every MXFP8 gradient payload and scale pointer must be set", fn);
+    if (!aligned(g.dq, 4) || !aligned(g.dk, 4) || !aligned(g.dv, 4))
+      return fail(MXFA_ERR_INVALID, "%s: MXFP8 gradient payloads must be 4-byte aligned", fn);
+  }
+  if (dq_mode != MXFA_DQ_FP32 && dq_mode != MXFA_DQ_FP16_STATIC)
+    return fail(MXFA_ERR_INVALID, "%s: bad dq_mode %d", fn, (int)dq_mode);
+  if (dq_mode == MXFA_DQ_FP16_STATIC && !is_pow2(dq_static_scale))
+    return fail(MXFA_ERR_INVALID, "%s: dq_static_scale=%g must be a positive power of two", fn,
+                (double)dq_static_scale);
+  const size_t need = mxfa_bwd_workspace_size(a, dq_mode);
+  if (library_workspace) {
+    if (need > kScratchBytes)
+      return fail(MXFA_ERR_INVALID,
+                  "%s: the problem needs %zu workspace bytes, more than the %zu of the fixed array; call mxfa_bwd "
+                  "with a caller-owned workspace", fn, need, kScratchBytes);
+  } else if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) {
+    return fail(MXFA_ERR_INVALID, "%s: workspace NULL, misaligned or smaller than %zu bytes", fn, need);
+  }
+  return MXFA_OK;
+}
+
+mxfa_status launch_bwd(const mxfa_attn_args* a, mxfa_mx v_d, mxfa_mx dout, const uint16_t* o,
+                       const uint16_t* dout_bf16, const float* lse, mxfa_dq_mode dq_mode, float dq_static_scale,
+                       void* workspace, uint16_t* dq, uint16_t* dk, uint16_t* dv, const mxfa_grad_mx* mx_out,
+                       void* stream, const char* fn) {
+  mxfa::GradMxOut gm{};
+  if (mx_out) gm = {mx_out->dq, mx_out->dq_scale, mx_out->dk, mx_out->dk_scale, mx_out->dv, mx_out->dv_scale};
+  mxfa::MxOperand vv{v_d.data, v_d.scale, (int)v_d.mode};
+  mxfa::MxOperand dd{dout.data, dout.scale, (int)dout.mode};
+  return hip_status(mxfa::launch_attn_bwd(to_problem(a), vv, dd, o, dout_bf16, lse,
+                                          dq_mode == MXFA_DQ_FP16_STATIC ? 1 : 0,
+                                          dq_mode == MXFA_DQ_FP16_STATIC ? dq_static_scale : 1.0f, workspace, dq, dk,
+                                          dv, mx_out ? &gm : nullptr, (hipStream_t)stream),
+                    fn);
 }
 
 }  // namespace
@@ -213,53 +305,31 @@ mxfa_status mxfa_bwd(const mxfa_attn_args* a, mxfa_mx v_d, mxfa_mx dout, const u
                          dv, nullptr, stream);
 }
 
+size_t mxfa_bwd_no_alloc_max_workspace(void) { return kScratchBytes; }
+
+mxfa_status mxfa_bwd_no_alloc(const mxfa_attn_args* a, mxfa_mx v_d, mxfa_mx dout, const uint16_t* o,
+                              const uint16_t* dout_bf16, const float* lse, mxfa_dq_mode dq_mode, float dq_static_scale,
+                              uint16_t* dq, uint16_t* dk, uint16_t* dv, void* stream) {
+  const char* fn = "mxfa_bwd_no_alloc";
+  if (!dq || !dk || !dv) return fail(MXFA_ERR_INVALID, "%s: NULL tensor argument", fn);
+  mxfa_status st = check_bwd(a, v_d, dout, o, dout_bf16, lse, dq_mode, dq_static_scale, nullptr, 0, dq, dk, dv,
+                             nullptr, true, fn);
+  if (st != MXFA_OK) return st;
+  void* ws = nullptr;
+  st = hip_status(scratch_address(&ws), fn);
+  if (st != MXFA_OK) return st;
+  return launch_bwd(a, v_d, dout, o, dout_bf16, lse, dq_mode, dq_static_scale, ws, dq, dk, dv, nullptr, stream, fn);
+}
+
 mxfa_status mxfa_bwd_mx_out(const mxfa_attn_args* a, mxfa_mx v_d, mxfa_mx dout, const uint16_t* o,
                             const uint16_t* dout_bf16, const float* lse, mxfa_dq_mode dq_mode, float dq_static_scale,
                             void* workspace, size_t workspace_bytes, uint16_t* dq, uint16_t* dk, uint16_t* dv,
                             const mxfa_grad_mx* mx_out, void* stream) {
   const char* fn = mx_out ? "mxfa_bwd_mx_out" : "mxfa_bwd";
-  mxfa_status st = check_attn(a, fn);
+  mxfa_status st = check_bwd(a, v_d, dout, o, dout_bf16, lse, dq_mode, dq_static_scale, workspace, workspace_bytes, dq,
+                             dk, dv, mx_out, false, fn);
   if (st != MXFA_OK) return st;
-  if (a->q.mode != MXFA_SQ32 || a->k.mode != MXFA_SQ32)
-    return fail(MXFA_ERR_INVALID, "%s: q and k must be SQ32 (square blocks serve both GEMM directions)", fn);
-  if (v_d.mode != MXFA_ROW32 && v_d.mode != MXFA_SQ32)
-    return fail(MXFA_ERR_INVALID, "%s: v_d.mode must be ROW32 or SQ32", fn);
-  if (dout.mode != MXFA_SQ32) return fail(MXFA_ERR_INVALID, "%s: dout.mode must be SQ32", fn);
-  if (!v_d.data || !v_d.scale || !dout.data || !dout.scale)
-    return fail(MXFA_ERR_INVALID, "%s: NULL v_d/dout data or scale", fn);
-  if (!aligned(v_d.data, 16) || !aligned(v_d.scale, 16) || !aligned(dout.data, 16) || !aligned(dout.scale, 16))
-    return fail(MXFA_ERR_INVALID, "%s: v_d/dout not 16-byte aligned", fn);
-  if (!o || !dout_bf16 || !lse) return fail(MXFA_ERR_INVALID, "%s: NULL tensor argument", fn);
-  const bool bf16_out = dq || dk || dv;
-  if (bf16_out && !(dq && dk && dv)) return fail(MXFA_ERR_INVALID, "%s: dq, dk, dv must be all set or all NULL", fn);
-  if (!bf16_out && !mx_out) return fail(MXFA_ERR_INVALID, "%s: no gradient output", fn);
-  if (!aligned(o, 16) || !aligned(dout_bf16, 16) || !aligned(lse, 4) ||
-      (bf16_out && (!aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))))
-    return fail(MXFA_ERR_INVALID, "%s: misaligned tensor argument", fn);
-  if (mx_out) {
-    const mxfa_grad_mx& g = *mx_out;
-    if (!g.dq || !g.dq_scale || !g.dk || !g.dk_scale || !g.dv || !g.dv_scale)
-      return fail(MXFA_ERR_INVALID, "%s: every MXFP8 gradient payload and scale pointer must be set", fn);
-    if (!aligned(g.dq, 4) || !aligned(g.dk, 4) || !aligned(g.dv, 4))
-      return fail(MXFA_ERR_INVALID, "%s: MXFP8 gradient payloads must be 4-byte aligned", fn);
-  }
-  if (dq_mode != MXFA_DQ_FP32 && dq_mode != MXFA_DQ_FP16_STATIC)
-    return fail(MXFA_ERR_INVALID, "%s: bad dq_mode %d", fn, (int)dq_mode);
-  if (dq_mode == MXFA_DQ_FP16_STATIC && !is_pow2(dq_static_scale))
-    return fail(MXFA_ERR_INVALID, "%s: dq_static_scale=%g must be a positive power of two", fn,
-                (double)dq_static_scale);
-  const size_t need = mxfa_bwd_workspace_size(a, dq_mode);
-  if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
-    return fail(MXFA_ERR_INVALID, "%s: workspace NULL, misaligned or smaller than %zu bytes", fn, need);
-  mxfa::GradMxOut gm{};
-  if (mx_out) gm = {mx_out->dq, mx_out->dq_scale, mx_out->dk, mx_out->dk_scale, mx_out->dv, mx_out->dv_scale};
-  mxfa::MxOperand vv{v_d.data, v_d.scale, (int)v_d.mode};
-  mxfa::MxOperand dd{dout.data, dout.scale, (int)dout.mode};
-  return hip_status(mxfa::launch_attn_bwd(to_problem(a), vv, dd, o, dout_bf16, lse,
-                                          dq_mode == MXFA_DQ_FP16_STATIC ? 1 : 0,
-                                          dq_mode == MXFA_DQ_FP16_STATIC ? dq_static_scale : 1.0f, workspace, dq, dk,
-                                          dv, mx_out ? &gm : nullptr, (hipStream_t)stream),
-                    fn);
+  return launch_bwd(a, v_d, dout, o, dout_bf16, lse, dq_mode, dq_static_scale, workspace, dq, dk, dv, mx_out, stream, fn);
 }
 
 mxfa_status mxfa_rmsnorm_quantize(const uint16_t* x, int64_t ld_x, int64_t T, int C, const float* gamma, float eps,

@@ -226,3 +226,19 @@ def test_linear_quantize_argument_errors(kw, expect):
                                      a["nseq"], a["max_seqlen"], a["data"], a["scale"], a["scale_t"], 0)
     assert st == expect, _last()
     assert _last() != ""
+
+
+def test_bwd_no_alloc_argument_errors():
+    """The allocation-free backward rejects, before any HIP call, missing outputs and problems whose
+    workspace exceeds its fixed array (B=4, H=16, N=4096 needs about 1 GB); the limit is 64 MiB."""
+    lib = _lib()
+    assert mx.mxfa_bwd_no_alloc_max_workspace() == 64 << 20
+    big = _args(nseq=4, max_q=4096, max_k=4096, total_q=16384, total_k=16384, H=16)
+    assert mx.mxfa_bwd_workspace_size(big, 1) > mx.mxfa_bwd_no_alloc_max_workspace()
+    st = lib.mxfa_bwd_no_alloc(ctypes.byref(big), mx._Mx(P, P, 0), mx._Mx(P, P, 2), P, P, P, 1, 1.0, P, P, P, 0)
+    assert st == INVALID and "mxfa_bwd_no_alloc" in _last() and "workspace" in _last()
+    small = _args()
+    assert lib.mxfa_bwd_no_alloc(ctypes.byref(small), mx._Mx(P, P, 0), mx._Mx(P, P, 2), P, P, P, 1, 1.0, 0, P, P,
+                                 0) == INVALID
+    assert lib.mxfa_bwd_no_alloc(ctypes.byref(small), mx._Mx(P, P, 0), mx._Mx(P, P, 1), P, P, P, 1, 1.0, P, P, P,
+                                 0) == INVALID  # dO must be SQ32
