@@ -12,6 +12,12 @@ peak (5.03 PF/s = 256 CU x 4 SIMD x 2048 FLOP/clk x 2.4 GHz).
 
 cpu_baseline: the CPU oracle, as it is, on a bounded sample of the same workload (batch element 0,
 6 of the 16 heads, N = 4096, forward + backward) on this host's cores.
+
+Before the headline line (which stays last), one JSON line per further workload, each with its own
+roofline entry and oracle sample (--headline-only skips them): causal B=4 H=16 N=8192 with 0.5% x64
+outliers (fwd + bwd, FP16 dQ at sigma 2^-4 and FP32 dQ); the jagged batch of 32 sequences with lengths
+uniform in [128, 4096] beside a uniform batch of the same total tokens; the forward-only LLM shape
+(Q/K ROW32, V COL32); the cross-attention module step (producers, scatter, attention fwd + bwd).
 """
 import argparse
 import json
@@ -27,6 +33,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_MXFP8 = 5.03e15  # FLOP/s
 PEAK_HBM = 8.0e12     # B/s
+synth_mod = None  # the synth module, set in main()
 B, H, N, D = 4, 16, 4096, 128
 SEED = 2
 
@@ -38,6 +45,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--dq-mode", type=int, default=1, help="0 = FP32 dQ, 1 = FP16 static-scale dQ")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="skip the per-workload lines (causal outliers, jagged vs uniform, module, forward-only) "
+                         "printed before the headline line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy first (reference kernel for HBM byte counters)")
     ap.add_argument("--producers", action="store_true",
@@ -109,9 +119,11 @@ def cpu_baseline(host, cu):
                        False, 0, 1.0, nthreads=nthreads)
     dt = time.perf_counter() - t0
     flops = 3.5 * 4.0 * N * N * D * hs
-    return {"value": flops / dt / 1e15, "unit": "PF/s", "cores": nthreads, "kind": "oracle",
+    model, nproc, _ = host_cpu()
+    return {"value": flops / dt / 1e15, "unit": "PF/s", "cores": min(nthreads, hs), "kind": "oracle",
+            "cpu_model": model, "nproc": nproc,
             "sample": f"batch element 0 of the step, heads 0-{hs - 1} of {H} (N={N}): quantize + forward + "
-                      f"backward (FP32 dQ), {dt:.1f} s wall"}
+                      f"backward (FP32 dQ), one thread per head, {dt:.1f} s wall"}
 
 
 MODULE_SEED, MODULE_B, MODULE_DIM = 4, 64, 1024
@@ -260,6 +272,314 @@ def bench_producers(args, torch, mx, synth):
     print(json.dumps(out), flush=True)
 
 
+def host_cpu():
+    """CPU model and the number of cores the oracle may use here (the box's share, at most 16)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, os.cpu_count() or 1, max(1, min(16, os.cpu_count() or 1))
+
+
+def oracle_slices(slices, backward, c, causal, qk_mode=2):
+    """The oracle, as it is, on (sequence, head) slices given as bf16 arrays {q, k, v, do}: each slice one
+    sequence of a one-head batch, so the slices run on parallel threads. Returns wall seconds."""
+    import oracle
+    cq = synth_mod.cu_seqlens([x["q"].shape[0] for x in slices])
+    ck = synth_mod.cu_seqlens([x["k"].shape[0] for x in slices])
+    cat = {n: np.ascontiguousarray(np.concatenate([x[n] for x in slices])) for n in ("q", "k", "v", "do")}
+    nthreads = max(1, min(16, os.cpu_count() or 1))
+    t0 = time.perf_counter()
+    q = oracle.quantize(cat["q"], cq, qk_mode)
+    k = oracle.quantize(cat["k"], ck, qk_mode)
+    v = oracle.quantize(cat["v"], ck, oracle.COL32)
+    o16, _, lse = oracle.attn_fwd_mx(q[0], q[1], qk_mode, k[0], k[1], qk_mode, v[0], v[1], oracle.COL32, cq, ck, 1, D,
+                                     c, causal, nthreads=nthreads)
+    if backward:
+        vd = oracle.quantize(cat["v"], ck, oracle.ROW32)
+        do = oracle.quantize(cat["do"], cq, oracle.SQ32)
+        oracle.attn_bwd_mx(q[0], q[1], k[0], k[1], vd[0], vd[1], oracle.ROW32, do[0], do[1], o16, cat["do"], lse, cq,
+                           ck, 1, D, c, causal, 0, 1.0, nthreads=nthreads)
+    return time.perf_counter() - t0, min(nthreads, len(slices))
+
+
+def attn_flops(lens_q, lens_k, H, causal):
+    """Forward FLOPs (4 D per visible (query, key) pair; top-left causal: the pairs j <= i)."""
+    pairs = 0
+    for lq, lk in zip(lens_q, lens_k):
+        pairs += (min(lq, lk) * (min(lq, lk) + 1) // 2 + max(0, lq - lk) * lk) if causal else lq * lk
+    return 4.0 * D * H * pairs
+
+
+def bench_attention_workload(args, torch, mx, label, workload, lens_q, lens_k, H, causal, outlier_p, seed,
+                             fwd_only=False, qk_mode=None, dq_modes=((1, 1.0), (0, 1.0)), cpu_slices=4,
+                             cpu_backward=False, extra_config=None):
+    """One attention workload at its full size: quantize, forward and backward (each dQ mode) timed over
+    back-to-back calls with HIP events on the launch stream. Returns the JSON dict (not printed)."""
+    stream = torch.cuda.current_stream()
+    qk_mode = (mx.ROW32 if fwd_only else mx.SQ32) if qk_mode is None else qk_mode
+    cu_q, cu_k = synth_mod.cu_seqlens(lens_q), synth_mod.cu_seqlens(lens_k)
+    Tq, Tk, C = int(cu_q[-1]), int(cu_k[-1]), H * D
+    kw = dict(outlier_p=outlier_p)
+    host = {"q": synth_mod.normal_bf16(seed, synth_mod.STREAM_Q, (Tq, C), **kw),
+            "k": synth_mod.normal_bf16(seed, synth_mod.STREAM_K, (Tk, C), **kw),
+            "v": synth_mod.normal_bf16(seed, synth_mod.STREAM_V, (Tk, C), **kw),
+            "do": synth_mod.normal_bf16(seed, synth_mod.STREAM_DO, (Tq, C), **kw)}
+    dev = {n: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda() for n, a in host.items()}
+    cq_d, ck_d = torch.from_numpy(cu_q).cuda(), torch.from_numpy(cu_k).cuda()
+    c = float(np.float32(1 / math.sqrt(D)))
+    nbq, nbk = int(np.sum((np.array(lens_q) + 31) // 32)), int(np.sum((np.array(lens_k) + 31) // 32))
+    Pq, Pk = mx.mxfa_padded_token_rows(cu_q), mx.mxfa_padded_token_rows(cu_k)
+    u8 = lambda *shape: torch.empty(shape, dtype=torch.uint8, device="cuda")
+    srows = {mx.ROW32: (lambda T, nb, P: (T, C // 32), lambda T, nb, P: (P, C // 32)),
+             mx.COL32: (lambda T, nb, P: (nb, C), lambda T, nb, P: (P // 32, C)),
+             mx.SQ32: (lambda T, nb, P: (nb, C // 32), lambda T, nb, P: (P // 32, C // 32))}
+    jag_q, jag_k = any(L % 128 for L in lens_q), any(L % 128 for L in lens_k)
+
+    def operand(name, mode, T, nb, P, cu_d, lens, jag):
+        d, sc = u8(T, C), u8(*srows[mode][0](T, nb, P))
+        pad = u8(*srows[mode][1](T, nb, P)) if jag else sc
+
+        def run():
+            mx.mxfa_quantize(dev[name], C, T, C, cu_d, len(lens), max(lens), mode, d, sc, None, stream)
+            if jag:
+                mx.mxfa_varlen_scale_scatter(sc, cu_d, len(lens), max(lens), C, mode, pad, pad.shape[0], stream)
+        return mx.MxOperand(d, pad, mode), run
+    qop, rq = operand("q", qk_mode, Tq, nbq, Pq, cq_d, lens_q, jag_q)
+    kop, rk = operand("k", qk_mode, Tk, nbk, Pk, ck_d, lens_k, jag_k)
+    vop, rv = operand("v", mx.COL32, Tk, nbk, Pk, ck_d, lens_k, jag_k)
+    runs = [rq, rk, rv]
+    if not fwd_only:
+        vdop, rvd = operand("v", mx.ROW32, Tk, nbk, Pk, ck_d, lens_k, jag_k)
+        doop, rdo = operand("do", mx.SQ32, Tq, nbq, Pq, cq_d, lens_q, jag_q)
+        runs += [rvd, rdo]
+
+    def quant():
+        for r in runs:
+            r()
+    attn = mx.AttnArgs(qop, kop, vop, cq_d, ck_d, len(lens_q), max(lens_q), max(lens_k), Tq, Tk, H, D, c, causal)
+    o = torch.empty((Tq, C), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((H, Tq), dtype=torch.float32, device="cuda")
+    quant()
+    t_quant = _time_back_to_back(torch, stream, quant, 2, max(3, args.steps // 4))
+    t_fwd = _time_back_to_back(torch, stream, lambda: mx.mxfa_fwd(attn, o, lse, stream), 2, args.steps)
+    f_fwd = attn_flops(lens_q, lens_k, H, causal)
+    res = {"fwd_us": round(t_fwd * 1e6, 2), "fwd_pflops": round(f_fwd / t_fwd / 1e15, 4),
+           "quant_us": round(t_quant * 1e6, 2)}
+    dom_t, dom_f, dom_name = t_fwd, f_fwd, "attn_fwd_kernel"
+    if not fwd_only:
+        ws_bytes = mx.mxfa_bwd_workspace_size(attn, 1)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+        dq, dk, dv = (torch.empty((T, C), dtype=torch.bfloat16, device="cuda") for T in (Tq, Tk, Tk))
+        for dq_mode, sigma in dq_modes:
+            t = _time_back_to_back(torch, stream, lambda: mx.mxfa_bwd(attn, vdop, doop, o, dev["do"], lse, dq_mode, sigma,
+                                                                     ws, ws_bytes, dq, dk, dv, stream), 2, args.steps)
+            key = "bwd_fp16dq" if dq_mode == 1 else "bwd_fp32dq"
+            res[key + "_us"] = round(t * 1e6, 2)
+            res[key + "_pflops"] = round(2.5 * f_fwd / t / 1e15, 4)
+            res[key + "_sigma"] = sigma
+        t_bwd = res["bwd_fp16dq_us"] * 1e-6
+        dom_t, dom_f, dom_name = (t_bwd, 2.5 * f_fwd, "mxfa_bwd call (FP16 dQ)") if t_bwd > t_fwd else (dom_t, dom_f,
+                                                                                                       dom_name)
+        res["step_us"] = round((t_quant + t_fwd + t_bwd) * 1e6, 2)
+        value = 3.5 * f_fwd / (t_fwd + t_bwd) / 1e15
+    else:
+        value = f_fwd / t_fwd / 1e15
+    print(f"# {label}: " + ", ".join(f"{k}={v}" for k, v in res.items()), file=sys.stderr, flush=True)
+    cfg = {"workload": workload, "H": H, "D": D, "causal": bool(causal), "nseq": len(lens_q), "tokens_q": Tq,
+           "tokens_k": Tk, "max_len": max(lens_k), "outlier_p": outlier_p, **(extra_config or {}), **res}
+    out = {
+        "metric": "MXFP8 attention fwd/bwd PF/s and % of MI355X dense MXFP8 MFMA peak",
+        "value": round(value, 4), "unit": "PF/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round((res.get("step_us", res["fwd_us"])) / 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "mxfp8_e4m3 (fp32 accumulate)", "data": "synthetic",
+        "config": cfg,
+        "roofline": {"bound": "mfma", "achieved": round(dom_f / dom_t / 1e12, 2), "peak": PEAK_MXFP8 / 1e12,
+                     "unit": "TFLOP/s", "frac": round(dom_f / dom_t / PEAK_MXFP8, 4), "traffic": None,
+                     "kernel": dom_name, "launch_us": round(dom_t * 1e6, 2)},
+    }
+    if not args.no_cpu_baseline and cpu_slices:
+        picks = [(s, (7 * s + 3) % H) for s in np.argsort(lens_k)[::-1][:cpu_slices]]
+        sl = [{n: np.ascontiguousarray(host[n][int((cu_q if n in ("q", "do") else cu_k)[s]):
+                                               int((cu_q if n in ("q", "do") else cu_k)[s + 1]), h * D:(h + 1) * D])
+               for n in ("q", "k", "v", "do")} for s, h in picks]
+        dt, cores = oracle_slices(sl, cpu_backward, c, causal, qk_mode)
+        f = sum(attn_flops([lens_q[s]], [lens_k[s]], 1, causal) for s, _ in picks) * (3.5 if cpu_backward else 1.0)
+        model, nproc, _ = host_cpu()
+        out["cpu_baseline"] = {"value": round(f / dt / 1e15, 8), "unit": "PF/s", "cores": cores, "kind": "oracle",
+                               "cpu_model": model, "nproc": nproc,
+                               "sample": f"{len(picks)} (sequence, head) slices of the longest sequences, quantize + "
+                                         f"forward{' + backward' if cpu_backward else ''}, one thread per slice, "
+                                         f"{dt:.1f} s wall"}
+    del dev
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_workloads(args, torch, mx):
+    """The per-workload lines: causal N=8192 with outliers, jagged 32 sequences beside a uniform batch of
+    the same total tokens, and the forward-only LLM shape (Q/K ROW32)."""
+    lines = []
+    lines.append(bench_attention_workload(
+        args, torch, mx, "causal outliers", "causal B=4 H=16 N=8192, 0.5% of entries x64, fwd + bwd",
+        [8192] * 4, [8192] * 4, 16, True, 0.005, 3, dq_modes=((1, 0.0625), (0, 1.0)), cpu_slices=4))
+    lens = [int(v) for v in synth_mod.lengths(4, 32, 128, 4096)]
+    jag = bench_attention_workload(
+        args, torch, mx, "jagged", "jagged self-attention, 32 sequences with lengths uniform in [128, 4096], fwd + bwd",
+        lens, lens, 16, False, 0.0, 4, cpu_slices=4)
+    L = int(round(sum(lens) / len(lens) / 128.0)) * 128
+    uni = bench_attention_workload(
+        args, torch, mx, "uniform", f"uniform self-attention, 32 sequences of {L} tokens, fwd + bwd",
+        [L] * 32, [L] * 32, 16, False, 0.0, 4, cpu_slices=0)
+    jag["config"]["uniform_same_batch"] = {k: uni["config"][k] for k in uni["config"] if k.endswith(("us", "pflops"))}
+    jag["config"]["uniform_same_batch"]["len"] = L
+    lines.append(jag)
+    lines.append(bench_attention_workload(
+        args, torch, mx, "forward-only", "LLM forward B=4 H=16 N=4096, Q/K ROW32, V COL32",
+        [N] * B, [N] * B, H, False, 0.0, SEED, fwd_only=True, cpu_slices=4))
+    for line in lines:
+        print(json.dumps(line), flush=True)
+
+
+def bench_module(args, torch, mx):
+    """The cross-attention module step at its full size: RMSNorm+quantize of the query- and key/value-side
+    activations (model dim 1024), the three projection GEMM+quantize producers (SQ32 outputs, both scale
+    layouts), the jagged scale scatter of K and V, attention forward, quantize of dO, attention backward
+    (FP16 dQ). The weights are quantized once, outside the step. Step and phases timed with HIP events."""
+    stream = torch.cuda.current_stream()
+    Bm, NQ, Hm, CM = MODULE_B, 256, 8, MODULE_DIM
+    lens_q = [NQ] * Bm
+    lens_k = [int(v) for v in synth_mod.lengths(5, Bm, 256, 2048)]
+    cu_q, cu_k = synth_mod.cu_seqlens(lens_q), synth_mod.cu_seqlens(lens_k)
+    Tq, Tk = int(cu_q[-1]), int(cu_k[-1])
+    cq_d, ck_d = torch.from_numpy(cu_q).cuda(), torch.from_numpy(cu_k).cuda()
+    xq_h = synth_mod.normal_bf16(5, synth_mod.STREAM_ACT, (Tq, CM))
+    xkv_h = synth_mod.normal_bf16(5, synth_mod.STREAM_ACT + 1, (Tk, CM))
+    w_h = {n: synth_mod.normal_bf16(5, synth_mod.STREAM_WEIGHT + i, (CM, CM), std=0.02) for i, n in enumerate("qkv")}
+    do_h = synth_mod.normal_bf16(5, synth_mod.STREAM_DO, (Tq, Hm * D))
+    bf = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    xq, xkv, dout = bf(xq_h), bf(xkv_h), bf(do_h)
+    gamma = torch.ones(CM, dtype=torch.float32, device="cuda")
+    wcu = np.array([0, CM], np.int32)
+    w_hat = {n: mx.quantize(bf(w_h[n]), wcu, torch.from_numpy(wcu).cuda(), mx.ROW32) for n in "qkv"}
+    u8 = lambda *shape: torch.empty(shape, dtype=torch.uint8, device="cuda")
+    nbq, nbk = Tq // 32, int(np.sum((np.array(lens_k) + 31) // 32))
+    Pk = mx.mxfa_padded_token_rows(cu_k)
+    xqh = (u8(Tq, CM), u8(nbq, CM // 32), u8(CM // 32, nbq))
+    xkvh = (u8(Tk, CM), u8(nbk, CM // 32), u8(CM // 32, nbk))
+    C = Hm * D
+    gq = (u8(Tq, C), u8(nbq, C // 32), u8(C // 32, nbq))
+    gk = (u8(Tk, C), u8(nbk, C // 32), u8(C // 32, nbk))
+    gv = (u8(Tk, C), u8(nbk, C // 32), u8(C // 32, nbk))
+    pk_, pv_ = u8(Pk // 32, C // 32), u8(Pk // 32, C // 32)
+    gdo = (u8(Tq, C), u8(nbq, C // 32))
+    c = float(np.float32(1 / math.sqrt(D)))
+    attn = mx.AttnArgs(mx.MxOperand(gq[0], gq[1], mx.SQ32), mx.MxOperand(gk[0], pk_, mx.SQ32),
+                       mx.MxOperand(gv[0], pv_, mx.SQ32), cq_d, ck_d, Bm, NQ, max(lens_k), Tq, Tk, Hm, D, c, False)
+    o = torch.empty((Tq, C), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((Hm, Tq), dtype=torch.float32, device="cuda")
+    ws_bytes = mx.mxfa_bwd_workspace_size(attn, 1)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    dq, dk, dv = (torch.empty((T, C), dtype=torch.bfloat16, device="cuda") for T in (Tq, Tk, Tk))
+    wop = {n: mx.MxOperand(w_hat[n][0], w_hat[n][1], mx.ROW32) for n in "qkv"}
+    phases = ["producers", "scatter", "fwd", "bwd"]
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+        mark(0)
+        mx.mxfa_rmsnorm_quantize(xq, CM, Tq, CM, gamma, 1e-6, cq_d, Bm, NQ, *xqh, stream)
+        mx.mxfa_rmsnorm_quantize(xkv, CM, Tk, CM, gamma, 1e-6, ck_d, Bm, max(lens_k), *xkvh, stream)
+        mx.mxfa_linear_quantize(mx.MxOperand(xqh[0], xqh[1], mx.SQ32), wop["q"], Tq, CM, C, cq_d, Bm, NQ, *gq, stream)
+        for n, g in (("k", gk), ("v", gv)):
+            mx.mxfa_linear_quantize(mx.MxOperand(xkvh[0], xkvh[1], mx.SQ32), wop[n], Tk, CM, C, ck_d, Bm, max(lens_k),
+                                    *g, stream)
+        mark(1)
+        mx.mxfa_varlen_scale_scatter(gk[1], ck_d, Bm, max(lens_k), C, mx.SQ32, pk_, pk_.shape[0], stream)
+        mx.mxfa_varlen_scale_scatter(gv[1], ck_d, Bm, max(lens_k), C, mx.SQ32, pv_, pv_.shape[0], stream)
+        mark(2)
+        mx.mxfa_fwd(attn, o, lse, stream)
+        mark(3)
+        mx.mxfa_quantize(dout, C, Tq, C, cq_d, Bm, NQ, mx.SQ32, gdo[0], gdo[1], None, stream)
+        mx.mxfa_bwd(attn, mx.MxOperand(gv[0], pv_, mx.SQ32), mx.MxOperand(gdo[0], gdo[1], mx.SQ32), o, dout, lse, 1,
+                    1.0, ws, ws_bytes, dq, dk, dv, stream)
+        mark(4)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    ph = {n: float(np.median([e[i].elapsed_time(e[i + 1]) * 1e-3 for e in evs])) for i, n in enumerate(phases)}
+    t_step = float(np.median([e[0].elapsed_time(e[4]) * 1e-3 for e in evs]))
+    f_attn = attn_flops(lens_q, lens_k, Hm, False)
+    f_proj = 2.0 * CM * C * (Tq + 2 * Tk)
+    total = 3.5 * f_attn + f_proj
+    res = {k + "_us": round(v * 1e6, 2) for k, v in ph.items()}
+    res.update({"module_step_us": round(t_step * 1e6, 2), "attn_fwd_pflops": round(f_attn / ph["fwd"] / 1e15, 4),
+                "attn_bwd_pflops": round(2.5 * f_attn / ph["bwd"] / 1e15, 4),
+                "projection_pflops": round(f_proj / ph["producers"] / 1e15, 4)})
+    print("# module: " + ", ".join(f"{k}={v}" for k, v in res.items()), file=sys.stderr, flush=True)
+    dom = max(ph, key=ph.get)
+    dom_f = {"producers": f_proj, "fwd": f_attn, "bwd": 2.5 * f_attn, "scatter": 0.0}[dom]
+    out = {
+        "metric": "MXFP8 cross-attention module step PF/s (projections + attention fwd/bwd) and % of MI355X dense "
+                  "MXFP8 MFMA peak",
+        "value": round(total / t_step / 1e15, 4), "unit": "PF/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(t_step * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "mxfp8_e4m3 (fp32 accumulate)", "data": "synthetic",
+        "config": {"workload": "cross-attention module: 64 samples x 256 queries, 64 key sequences with lengths "
+                               "uniform in [256, 2048], H=8, model dim 1024; RMSNorm+quantize -> projection+quantize "
+                               "-> scale scatter -> attention fwd -> quantize dO -> attention bwd (FP16 dQ)",
+                   "tokens_q": Tq, "tokens_k": Tk, **res},
+        "roofline": {"bound": "mfma", "achieved": round(dom_f / ph[dom] / 1e12, 2), "peak": PEAK_MXFP8 / 1e12,
+                     "unit": "TFLOP/s", "frac": round(dom_f / ph[dom] / PEAK_MXFP8, 4), "traffic": None,
+                     "kernel": {"producers": "rmsnorm_quantize + linear_quantize (phase)", "fwd": "attn_fwd_kernel",
+                                "bwd": "mxfa_bwd call", "scatter": "scale_scatter_kernel"}[dom],
+                     "launch_us": round(ph[dom] * 1e6, 2)},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        picks = [int(s) for s in np.argsort(lens_k)[::-1][:2]]
+        t0 = time.perf_counter()
+        fl = 0.0
+        for s in picks:
+            h = 3
+            rq, rk = slice(int(cu_q[s]), int(cu_q[s + 1])), slice(int(cu_k[s]), int(cu_k[s + 1]))
+            cq1, ck1 = np.array([0, NQ], np.int32), np.array([0, lens_k[s]], np.int32)
+            ones = np.ones(CM, np.float32)
+            xq1 = oracle.rmsnorm_quantize(np.ascontiguousarray(xq_h[rq]), ones, 1e-6, cq1)
+            xk1 = oracle.rmsnorm_quantize(np.ascontiguousarray(xkv_h[rk]), ones, 1e-6, ck1)
+            outs = {}
+            for n, x1, cu1 in (("q", xq1, cq1), ("k", xk1, ck1), ("v", xk1, ck1)):
+                wd, ws1, _ = oracle.quantize(np.ascontiguousarray(w_h[n][h * D:(h + 1) * D]), np.array([0, D], np.int32),
+                                             oracle.ROW32)
+                outs[n] = oracle.linear_quantize(x1[0], x1[1], wd, ws1, cu1)
+            o16, _, lse1 = oracle.attn_fwd_mx(outs["q"][0], outs["q"][1], 2, outs["k"][0], outs["k"][1], 2, outs["v"][0],
+                                              outs["v"][1], 2, cq1, ck1, 1, D, c, False)
+            do1 = np.ascontiguousarray(do_h[rq, h * D:(h + 1) * D])
+            rdo = oracle.quantize(do1, cq1, oracle.SQ32)
+            oracle.attn_bwd_mx(outs["q"][0], outs["q"][1], outs["k"][0], outs["k"][1], outs["v"][0], outs["v"][1], 2,
+                               rdo[0], rdo[1], o16, do1, lse1, cq1, ck1, 1, D, c, False, 1, 1.0)
+            fl += 3.5 * attn_flops([NQ], [lens_k[s]], 1, False) + 2.0 * CM * D * (NQ + 2 * lens_k[s])
+        dt = time.perf_counter() - t0
+        model, nproc, _ = host_cpu()
+        out["cpu_baseline"] = {"value": round(fl / dt / 1e15, 8), "unit": "PF/s", "cores": 16 if nproc >= 16 else nproc,
+                               "kind": "oracle", "cpu_model": model, "nproc": nproc,
+                               "sample": f"head 3 of the 2 samples with the longest key sequences: RMSNorm+quantize, "
+                                         f"the three projections (that head's 128 columns), attention fwd + bwd, "
+                                         f"{dt:.1f} s wall"}
+    print(json.dumps(out), flush=True)
+    torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -269,6 +589,8 @@ def main():
     import torch
     import precision_mxfp8_block_amd as mx
     import synth
+    global synth_mod
+    synth_mod = synth
 
     torch.cuda.set_device(0)
     if args.copy_calibration:
@@ -285,6 +607,9 @@ def main():
     if args.producers:
         bench_producers(args, torch, mx, synth)
         return
+    if not args.headline_only:
+        bench_workloads(args, torch, mx)
+        bench_module(args, torch, mx)
     host, dev, cu, cu_d = make_inputs(torch, synth)
     T, C = B * N, H * D
     c = float(np.float32(1 / math.sqrt(D)))

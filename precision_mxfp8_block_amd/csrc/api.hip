@@ -80,7 +80,8 @@ mxfa_status check_attn(const mxfa_attn_args* a, const char* fn) {
   if (a->k.mode != MXFA_ROW32 && a->k.mode != MXFA_SQ32)
     return fail(MXFA_ERR_INVALID, "%s: k.mode must be ROW32 or SQ32", fn);
   const int64_t qtiles = ((int64_t)a->max_seqlen_q + 127) / 128, ktiles = ((int64_t)a->max_seqlen_k + 127) / 128;
-  const int64_t items = (qtiles > ktiles ? qtiles : ktiles) * a->num_heads * a->nseq;
+  const int64_t pairs = (int64_t)a->num_heads * a->nseq;
+  const int64_t items = (qtiles > ktiles ? qtiles : ktiles) * ((pairs + 7) / 8 * 8);  // the largest grid
   if (items >= (int64_t)1 << 31) return fail(MXFA_ERR_INVALID, "%s: problem too large for one launch", fn);
   return MXFA_OK;
 }

@@ -58,12 +58,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ int swz(int row) { return lds_swz(row); }
 
-__device__ __forceinline__ int xcd_remap(int bid, int total) {
-  const int per = total >> 3, rem = total & 7;
-  const int x = bid & 7, slot = bid >> 3;
-  return x * per + (x < rem ? x : rem) + slot;
-}
-
 // Waits on the vector memory counter, written as asm: the direct LDS loads are asm too, so the
 // compiler does not see them and would drop a builtin wait it believes to be redundant.
 template <int N>
@@ -247,7 +241,8 @@ __global__ void __launch_bounds__(64 * kBwdWaves, 1) attn_bwd_kernel(BwdParams p
   __shared__ __attribute__((aligned(256))) uint32_t lds_sc[3][64];      // [stage][Q, dO scale words]
   __shared__ uint32_t lds_dscode[4];                                     // dS codes [key block] (byte: q block)
 
-  const int item = xcd_remap((int)blockIdx.x, p.total_items);
+  const int item = mx_pair_item((int)blockIdx.x, p.n_ktiles, p.nseq * p.H);
+  if (item < 0) return;
   const int kt = item % p.n_ktiles;
   const int h = (item / p.n_ktiles) % p.H;
   const int s = item / (p.n_ktiles * p.H);
@@ -707,7 +702,8 @@ __global__ void __launch_bounds__(64 * kDqWaves, 1) attn_dq_kernel(DqParams p) {
   __shared__ __attribute__((aligned(256))) uint32_t lds_codes[kDqStages][64];
   __shared__ __attribute__((aligned(256))) uint32_t lds_ksc[kDqStages][64];
 
-  const int item = xcd_remap((int)blockIdx.x, p.total_items);
+  const int item = mx_pair_item((int)blockIdx.x, p.ntq_max, p.nseq * p.H);
+  if (item < 0) return;
   const int qt = item % p.ntq_max;
   const int h = (item / p.ntq_max) % p.H;
   const int s = item / (p.ntq_max * p.H);
@@ -918,7 +914,7 @@ hipError_t launch_attn_bwd(const AttnProblem& a, const MxOperand& v_d, const MxO
   p.cu_q = a.cu_q; p.cu_k = a.cu_k;
   p.nseq = a.nseq; p.H = a.H;
   p.n_ktiles = ntk_max;
-  p.total_items = p.n_ktiles * a.H * a.nseq;  // < 2^31, checked by the caller
+  p.total_items = (int)mx_pair_grid((int64_t)a.H * a.nseq, p.n_ktiles);  // < 2^31, checked by the caller
   p.c2 = a.softmax_scale * kLog2e;
   p.causal = a.causal;
   p.pexp = pexp; p.ndelta = delta; p.Tq = Tq;
@@ -940,7 +936,7 @@ hipError_t launch_attn_bwd(const AttnProblem& a, const MxOperand& v_d, const MxO
   d.k = a.k.data; d.k_scale = a.k.scale;
   d.cu_q = a.cu_q; d.cu_k = a.cu_k;
   d.nseq = a.nseq; d.H = a.H; d.ntq_max = ntq_max; d.ntk_max = ntk_max;
-  d.total_items = ntq_max * a.H * a.nseq;
+  d.total_items = (int)mx_pair_grid((int64_t)a.H * a.nseq, ntq_max);
   d.causal = a.causal;
   d.ds_img = ws + w.img;
   d.ds_codes = ws + w.codes;

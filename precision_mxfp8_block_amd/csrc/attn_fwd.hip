@@ -22,9 +22,9 @@
 //    read), in exactly that key order.
 //  * LDS tiles are 128 rows x 128 bytes with the 16-byte chunk index XOR-swizzled (lds_swz):
 //    conflict-free for the row reads of K and the transposed reads of V.
-//  * Grid order is XCD-aware: consecutive workgroup IDs land on different XCDs, so IDs are remapped
-//    to give each XCD a contiguous range of (sequence, head, tile) items; the query tiles of one
-//    head then share one XCD's L2, which holds that head's K and V.
+//  * Grid order is XCD-aware (mx_pair_item): the query tiles of one (sequence, head) pair run on one
+//    XCD, whose L2 holds that head's K and V, and the pairs are dealt to the XCDs in turn, so every
+//    XCD gets the same share of a jagged batch's long and short sequences.
 #include "mx_device.h"
 #include "mxfa_internal.h"
 
@@ -59,13 +59,6 @@ struct FwdParams {
 };
 
 __device__ __forceinline__ int swz(int row) { return lds_swz(row); }
-
-// XCD-aware mapping of a linear workgroup id to a work item (bijective for any total < 2^31).
-__device__ __forceinline__ int xcd_remap(int bid, int total) {
-  const int per = total >> 3, rem = total & 7;
-  const int x = bid & 7, slot = bid >> 3;
-  return x * per + (x < rem ? x : rem) + slot;
-}
 
 // x if off < lim, else -inf. One compare into VCC and one select (inline asm so that the 64 compares
 // of a masked tile do not each occupy a scalar register pair).
@@ -155,7 +148,8 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[kLdsBytes];
   MX_LDS uint8_t* const lds = (MX_LDS uint8_t*)lds_raw;
 
-  const int item = xcd_remap((int)blockIdx.x, p.total_items);
+  const int item = mx_pair_item((int)blockIdx.x, p.n_qtiles, p.nseq * p.H);
+  if (item < 0) return;
   const int qt = p.n_qtiles - 1 - item % p.n_qtiles;  // heavy (late) query tiles first
   const int h = (item / p.n_qtiles) % p.H;
   const int s = item / (p.n_qtiles * p.H);
@@ -590,7 +584,7 @@ hipError_t launch_attn_fwd(const AttnProblem& a, int p_dynamic, uint16_t* o, uin
   p.cu_q = a.cu_q; p.cu_k = a.cu_k;
   p.nseq = a.nseq; p.H = a.H;
   p.n_qtiles = (a.max_seqlen_q + kTile - 1) / kTile;
-  p.total_items = p.n_qtiles * a.H * a.nseq;  // < 2^31, checked by the caller
+  p.total_items = (int)mx_pair_grid((int64_t)a.H * a.nseq, p.n_qtiles);  // < 2^31, checked by the caller
   p.c = a.softmax_scale;
   p.c2 = a.softmax_scale * kLog2e;
   p.causal = a.causal;

@@ -184,6 +184,22 @@ __device__ __forceinline__ int64_t mx_uniform_i64(int64_t v) {
 // every wave on its own (no barrier; the wave must be fully active): blocks32 = sum_{r<s}
 // ceil(L_r/32), padded = sum_{r<s} round_up(L_r,128). The sums fit 32 bits for any token count
 // whose data fits in device memory.
+// Workgroup id -> work item of the attention kernels, items being (pair, tile) with pair = sequence *
+// heads + head. Consecutive workgroup ids are dispatched to the 8 XCDs in turn (id % 8); XCD x takes
+// the pairs x, x + 8, x + 16, ... and runs each pair's tiles back to back, so one head's K and V (or Q
+// and dO) stay in one XCD's L2, and the heads of every sequence spread over all XCDs: a jagged batch
+// gives each XCD the same share of long and short sequences. The grid is mx_pair_grid(pairs, tiles);
+// ids that fall past the last pair give -1.
+__host__ __device__ __forceinline__ int64_t mx_pair_grid(int64_t pairs, int64_t tiles) {
+  return (pairs + 7) / 8 * 8 * tiles;
+}
+__device__ __forceinline__ int mx_pair_item(int bid, int tiles, int pairs) {
+  const int x = bid & 7, slot = bid >> 3;
+  const int pl = slot / tiles, t = slot - pl * tiles;
+  const int pair = pl * 8 + x;
+  return pair < pairs ? pair * tiles + t : -1;
+}
+
 struct SeqOffsets {
   int64_t blocks32;
   int64_t padded;

@@ -51,15 +51,14 @@ def host(t):
     return t.detach().cpu().numpy()
 
 
-def xcd_slices(nseq, H, ntiles_per_pair=1, n=8):
-    """One (sequence, head) pair from each of the 8 contiguous ranges of (sequence, head) items the
-    attention kernels' grid remap gives the 8 XCDs (items are ordered sequence, head, tile), at a
-    different offset inside each range."""
+def xcd_slices(nseq, H, n=8):
+    """One (sequence, head) pair from each XCD's share of the attention kernels' grid, at a different
+    position in each share: XCD x runs the pairs p = x, x + 8, x + 16, ... (p = sequence * H + head)."""
     pairs = nseq * H
     per = pairs // n
     out = []
     for x in range(n):
-        p = x * per + (3 * x + 1) % max(per, 1)
+        p = x + 8 * ((3 * x + 1) % max(per, 1))
         out.append((p // H, p % H))
     return out
 
@@ -168,7 +167,7 @@ class FullAttn:
             r = slice(int(cq[i]), int(cq[i + 1]))
             o_g = to_host_bf16_bits(self.o[rows, h * D:(h + 1) * D])
             lse_g = host(self.lse[h, rows])[None, :]
-            check_o(o_g, o32[r], lse_g, lse[:, r], f"seq {s} head {h}", qk_outliers_full_length=self.outliers)
+            check_o(o_g, o32[r], lse_g, lse[:, r], f"seq {s} head {h}", outliers=self.outliers)
         return o16, lse
 
     def oracle_bwd_slices(self, slices, o16, lse, g, dq_mode, sigma):
@@ -190,7 +189,7 @@ class FullAttn:
             gs = (to_host_bf16_bits(g[0][qr, cols]), to_host_bf16_bits(g[1][kr, cols]),
                   to_host_bf16_bits(g[2][kr, cols]))
             sub = {"dq_f": ref["dq_f"][rq_], "dk_f": ref["dk_f"][rk_], "dv_f": ref["dv_f"][rk_]}
-            check_grads(gs, sub, f"seq {s} head {h} dq_mode {dq_mode}", qk_outliers_full_length=self.outliers)
+            check_grads(gs, sub, f"seq {s} head {h} dq_mode {dq_mode}", qk_outliers=self.outliers)
 
 
 def test_llm_forward_B4_H16_N4096():
@@ -225,7 +224,7 @@ def test_causal_outliers_B4_H16_N8192(dq_mode, sigma):
     fa = FullAttn(3, [8192] * 4, [8192] * 4, 16, causal=True, outlier_p=0.005)
     fa.gpu_fwd()
     g = fa.gpu_bwd(dq_mode, sigma)
-    slices = xcd_slices(4, 16)[::2]
+    slices = xcd_slices(4, 16)
     o16, lse = fa.oracle_fwd_slices(slices)
     fa.oracle_bwd_slices(slices, o16, lse, g, dq_mode, sigma)
 

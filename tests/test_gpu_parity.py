@@ -358,3 +358,4 @@ def test_bwd_mx_out_parity(case, dq_mode):
         cu = c.cu_q if name == "dq" else c.cu_k
         check_mx_sq32_output(f"{label} {name}", mxo[2 * i], mxo[2 * i + 1], bits[i], ref[name + "_f"], cu,
                              GRAD_REL_FRO)
+
