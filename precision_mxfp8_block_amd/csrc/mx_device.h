@@ -156,8 +156,6 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return v;
 }
 
-// Sum of a per-thread integer over a workgroup of `nthreads` (<= 1024) threads; every thread gets
-// the total. `red` is a workgroup-shared scratch of at least 16 ints.
 // Sum over the 64 lanes of a wave, returned in every lane: DPP within rows of 16 (after the quad
 // steps each group of lanes holds one value, so the mirrors add the partner group), then the
 // permlane16 and permlane32 swaps across rows. The wave must be fully active.
@@ -180,10 +178,6 @@ __device__ __forceinline__ int64_t mx_uniform_i64(int64_t v) {
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
-// Offsets of sequence s in the compact and padded layouts from the device cu_seqlens, computed by
-// every wave on its own (no barrier; the wave must be fully active): blocks32 = sum_{r<s}
-// ceil(L_r/32), padded = sum_{r<s} round_up(L_r,128). The sums fit 32 bits for any token count
-// whose data fits in device memory.
 // Workgroup id -> work item of the attention kernels, items being (pair, tile) with pair = sequence *
 // heads + head. Consecutive workgroup ids are dispatched to the 8 XCDs in turn (id % 8); XCD x takes
 // the pairs x, x + 8, x + 16, ... and runs each pair's tiles back to back, so one head's K and V (or Q
@@ -200,6 +194,10 @@ __device__ __forceinline__ int mx_pair_item(int bid, int tiles, int pairs) {
   return pair < pairs ? pair * tiles + t : -1;
 }
 
+// Offsets of sequence s in the compact and padded layouts from the device cu_seqlens, computed by
+// every wave on its own (no barrier; the wave must be fully active): blocks32 = sum_{r<s}
+// ceil(L_r/32), padded = sum_{r<s} round_up(L_r,128). The sums fit 32 bits for any token count
+// whose data fits in device memory.
 struct SeqOffsets {
   int64_t blocks32;
   int64_t padded;
