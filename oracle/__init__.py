@@ -66,6 +66,9 @@ def _load():
                                     P, P, P, P, P, P, P, i32]
     lib.orc_rmsnorm_quantize.argtypes = [P, i64, i64, i32, P, f32, P, i32, P, P, P, P]
     lib.orc_linear_quantize.argtypes = [P, P, i32, P, P, i64, i32, i32, P, i32, P, P, P, P, i32]
+    lib.orc_linear_bwd_data.argtypes = [P, P, P, P, i64, i32, i32, P, i32, P, P, i32]
+    lib.orc_linear_bwd_weight.argtypes = [P, P, P, P, i64, i32, i32, P, i32, P, i32]
+    lib.orc_rmsnorm_bwd.argtypes = [P, i64, i64, i32, P, f32, P, P, P, P]
     for name in ["orc_quantize_bf16", "orc_quantize_f32", "orc_dequantize", "orc_scale_scatter",
                  "orc_attn_fwd_f64", "orc_attn_fwd_mx", "orc_attn_bwd_f64", "orc_attn_bwd_mx",
                  "orc_rmsnorm_quantize", "orc_linear_quantize"]:
@@ -304,3 +307,49 @@ def linear_quantize(x, x_scale, w, w_scale, cu, x_mode=SQ32, nthreads=None):
                                  _p(scale), _p(scale_t), _p(y), nthreads or default_threads())
     _check(rc, "linear_quantize")
     return data, scale, scale_t, y
+
+
+def linear_bwd_data(dy, dy_scale, wt, wt_scale, cu, nthreads=None):
+    """dX = dY W: dy [T, C_out] SQ32 payload with compact scales [NB, C_out/32]; wt = W^T [C_in, C_out]
+    payload with ROW32 scales [C_in, C_out/32]. Returns (dx bf16 bits uint16 [T, C_in], dx float32)."""
+    lib = _load()
+    cu = _c(cu, np.int32)
+    dy, dys, wt, wts = (_c(a, np.uint8) for a in (dy, dy_scale, wt, wt_scale))
+    T, C_out = dy.shape
+    C_in = wt.shape[0]
+    dx = np.empty((T, C_in), np.uint16)
+    dxf = np.empty((T, C_in), np.float32)
+    rc = lib.orc_linear_bwd_data(_p(dy), _p(dys), _p(wt), _p(wts), T, C_out, C_in, _p(cu), cu.size - 1, _p(dx),
+                                 _p(dxf), nthreads or default_threads())
+    _check(rc, "linear_bwd_data")
+    return dx, dxf
+
+
+def linear_bwd_weight(dy, dy_scale_t, x, x_scale_t, cu, nthreads=None):
+    """dW = dY^T X over all tokens: dy [T, C_out] and x [T, C_in] SQ32 payloads with their transposed scale
+    grids [C_out/32, NB] and [C_in/32, NB]. Returns dw float32 [C_out, C_in]."""
+    lib = _load()
+    cu = _c(cu, np.int32)
+    dy, dyst, x, xst = (_c(a, np.uint8) for a in (dy, dy_scale_t, x, x_scale_t))
+    T, C_out = dy.shape
+    C_in = x.shape[1]
+    dw = np.empty((C_out, C_in), np.float32)
+    rc = lib.orc_linear_bwd_weight(_p(dy), _p(dyst), _p(x), _p(xst), T, C_out, C_in, _p(cu), cu.size - 1, _p(dw),
+                                   nthreads or default_threads())
+    _check(rc, "linear_bwd_weight")
+    return dw
+
+
+def rmsnorm_bwd(x_bf16, gamma, eps, dy_bf16):
+    """x_bf16, dy_bf16: uint16 [T, C]. Returns (dx bf16 bits uint16 [T, C], dx float32, dgamma float32 [C])."""
+    lib = _load()
+    x = _c(x_bf16, np.uint16)
+    dy = _c(dy_bf16, np.uint16)
+    gamma = _c(gamma, np.float32)
+    T, C = x.shape
+    dx = np.empty((T, C), np.uint16)
+    dxf = np.empty((T, C), np.float32)
+    dg = np.empty(C, np.float32)
+    rc = lib.orc_rmsnorm_bwd(_p(x), C, T, C, _p(gamma), eps, _p(dy), _p(dx), _p(dxf), _p(dg))
+    _check(rc, "rmsnorm_bwd")
+    return dx, dxf, dg

@@ -1,5 +1,6 @@
 // CPU oracle for MXFP8 block-scaled attention (forward and backward), the MX quantizer,
-// the jagged scale scatter and the RMSNorm+quantize producer.
+// the jagged scale scatter, the RMSNorm+quantize and projection+quantize producers and their
+// backward (data and weight gradients of the projection, RMSNorm backward).
 //
 // TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the benchmark's CPU
 // baseline may load this library. The product path (the HIP library) never calls it, and
@@ -794,6 +795,120 @@ int orc_linear_quantize(const uint8_t* x, const uint8_t* x_scale, int x_mode, co
   if (y_out)
     for (int64_t i = 0; i < T * C_out; ++i) y_out[i] = (float)y[i];
   quantize_matrix(y.data(), T, C_out, cu, nseq, SQ32, data, scale, scale_t);
+  return 0;
+}
+
+
+// ---------------------------------------------------------------------------------------------
+// Producer backward (the module's training step past the attention backward)
+// ---------------------------------------------------------------------------------------------
+//
+// [BR item 7]: the producers write FP8 with the scale grid in two layouts, [NB][C/32] and its
+// transpose [C/32][NB], so that one square-block payload feeds both the forward GEMM (contraction
+// along the channels) and the weight-gradient GEMM (contraction along the tokens) [AE TMEM: square
+// blocks serve the plain and the transposed product]. READING of the backward of Y = X W^T with
+// X [T, C_in], W [C_out, C_in], given the output gradient dY [T, C_out]:
+//   data gradient   dX = dY W        contraction over C_out
+//   weight gradient dW = dY^T X      contraction over the tokens of every sequence
+// and of the RMSNorm y = x r gamma with r = (sum_c x_c^2 / C + eps)^(-1/2):
+//   dx_k = r gamma_k dy_k - x_k r^3 (sum_c gamma_c dy_c x_c) / C,   dgamma_c = sum_t dy_tc x_tc r_t
+// with the quantizers treated as identities in the backward (straight through).
+
+// Value of element (t, c) of an SQ32 payload read through the transposed scale grid [C/32][NB]
+// (the layout the weight-gradient GEMM consumes): decode(data) * 2^(code - 127) with the code of
+// (channel block c / 32, token block of t).
+static void dequantize_sq32_transposed(const uint8_t* data, const uint8_t* scale_t, int64_t T, int C,
+                                       const int32_t* cu, int nseq, double* out) {
+  const int64_t nb = blockrow_offset(cu, nseq);
+  for (int s = 0; s < nseq; ++s) {
+    const int64_t b0 = blockrow_offset(cu, s);
+    for (int64_t t = cu[s]; t < cu[s + 1]; ++t) {
+      const int64_t br = b0 + (t - cu[s]) / 32;
+      for (int c = 0; c < C; ++c)
+        out[t * C + c] = e4m3_decode(data[t * C + c]) * e8m0_value(scale_t[(int64_t)(c / 32) * nb + br]);
+    }
+  }
+}
+
+// Data gradient: dx = fl32(sum_o deq(dy)_to deq(wt)_io), dy [T, C_out] SQ32 with compact scales
+// [NB][C_out/32], wt = W^T [C_in, C_out] quantized ROW32 (1 x 32 along C_out, the contraction
+// dimension: [TC paragraph 3]); dx_bf16 = bf16 of dx (either output may be NULL).
+// Pinned by: wt = I (exact) gives dx = deq(dy); small-integer operands give the exact integer
+// product; the adjoint identity <dY, X W^T> = <dX, X> with exactly representable W.
+int orc_linear_bwd_data(const uint8_t* dy, const uint8_t* dy_scale, const uint8_t* wt, const uint8_t* wt_scale,
+                        int64_t T, int C_out, int C_in, const int32_t* cu, int nseq, uint16_t* dx_bf16, float* dx_f32,
+                        int nthreads) {
+  if (C_in % 32 || C_out % 32 || !valid_cu(cu, nseq, T)) return -1;
+  std::vector<double> dyd((size_t)T * C_out), wtd((size_t)C_in * C_out);
+  dequantize_matrix(dy, dy_scale, T, C_out, cu, nseq, SQ32, dyd.data());
+  const int32_t wcu[2] = {0, C_in};
+  dequantize_matrix(wt, wt_scale, C_in, C_out, wcu, 1, ROW32, wtd.data());
+  parallel_units((int)T, nthreads, [&](int t) {
+    for (int i = 0; i < C_in; ++i) {
+      double acc = 0.0;
+      for (int o = 0; o < C_out; ++o) acc += dyd[(size_t)t * C_out + o] * wtd[(size_t)i * C_out + o];
+      const float f = (float)acc;
+      if (dx_f32) dx_f32[(size_t)t * C_in + i] = f;
+      if (dx_bf16) dx_bf16[(size_t)t * C_in + i] = bf16_round(f);
+    }
+  });
+  return 0;
+}
+
+// Weight gradient: dw = fl32(sum over all tokens t of deq(dy)_to deq(x)_ti), dy [T, C_out] and
+// x [T, C_in] both SQ32 payloads read through their transposed scale grids [C/32][NB].
+// Pinned by: small-integer operands with a different power-of-two scale per (token block, channel
+// block) give the exact integer sums (a misread scale grid moves them); jagged = sum of per-sequence
+// dense results.
+int orc_linear_bwd_weight(const uint8_t* dy, const uint8_t* dy_scale_t, const uint8_t* x, const uint8_t* x_scale_t,
+                          int64_t T, int C_out, int C_in, const int32_t* cu, int nseq, float* dw, int nthreads) {
+  if (C_in % 32 || C_out % 32 || !valid_cu(cu, nseq, T)) return -1;
+  std::vector<double> dyd((size_t)T * C_out), xd((size_t)T * C_in);
+  dequantize_sq32_transposed(dy, dy_scale_t, T, C_out, cu, nseq, dyd.data());
+  dequantize_sq32_transposed(x, x_scale_t, T, C_in, cu, nseq, xd.data());
+  parallel_units(C_out, nthreads, [&](int o) {
+    for (int i = 0; i < C_in; ++i) {
+      double acc = 0.0;
+      for (int64_t t = 0; t < T; ++t) acc += dyd[(size_t)t * C_out + o] * xd[(size_t)t * C_in + i];
+      dw[(size_t)o * C_in + i] = (float)acc;
+    }
+  });
+  return 0;
+}
+
+// RMSNorm backward. x bf16 [T, ld] (first C columns), dy bf16 [T, C] (the gradient of y), gamma
+// fp32 [C]. r_t is the forward's own fp32 value (same formula as orc_rmsnorm_quantize); the
+// derivative is evaluated in FP64 at that r:
+//   dx_tk = r gamma_k dy_k - x_k r^3 S / C,  S = sum_c gamma_c dy_c x_c
+//   dgamma_c = fl32(sum_t dy_tc x_tc r_t)
+// dx_f32 = fl32(dx), dx_bf16 = bf16(dx_f32) (either may be NULL).
+// Pinned by: central finite differences of the FP64 forward (dx and dgamma); the scale-invariance
+// identity sum_k dx_k x_k = eps r^3 S.
+int orc_rmsnorm_bwd(const uint16_t* x, int64_t ld, int64_t T, int C, const float* gamma, float eps, const uint16_t* dy,
+                    uint16_t* dx_bf16, float* dx_f32, float* dgamma) {
+  if (C % 32 || ld < C || !gamma || T < 0) return -1;
+  std::vector<double> dg((size_t)C, 0.0);
+  for (int64_t t = 0; t < T; ++t) {
+    double ss = 0.0;
+    for (int c = 0; c < C; ++c) {
+      const double xv = bf16_value(x[t * ld + c]);
+      ss += xv * xv;
+    }
+    const float ss32 = (float)ss;
+    const float r32 = 1.0f / std::sqrt(ss32 / (float)C + eps);
+    const double r = (double)r32;
+    double S = 0.0;
+    for (int c = 0; c < C; ++c) S += (double)gamma[c] * bf16_value(dy[t * C + c]) * bf16_value(x[t * ld + c]);
+    for (int k = 0; k < C; ++k) {
+      const double xk = bf16_value(x[t * ld + k]), dyk = bf16_value(dy[t * C + k]);
+      const double d = r * (double)gamma[k] * dyk - xk * r * r * r * S / (double)C;
+      const float f = (float)d;
+      if (dx_f32) dx_f32[t * C + k] = f;
+      if (dx_bf16) dx_bf16[t * C + k] = bf16_round(f);
+      dg[k] += dyk * xk * r;
+    }
+  }
+  for (int c = 0; c < C; ++c) dgamma[c] = (float)dg[c];
   return 0;
 }
 

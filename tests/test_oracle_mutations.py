@@ -2,7 +2,7 @@
 
 Each mutant is a copy of oracle/mx_oracle.cpp with one plausible mistake planted by a text
 replacement, built with g++ into a temporary directory next to a copy of the oracle's Python binding.
-The pin named for it (tests/test_oracle_worked_examples.py) must fail on the mutant, and the test
+The pin named for it (tests/test_oracle_worked_examples.py, tests/test_oracle_producer_bwd.py) must fail on the mutant, and the test
 first checks that the replacement really changed the source (exactly one match), so a mutant can
 never silently be the unchanged oracle. The unmutated oracle passes every pin (the worked-example
 tests themselves).
@@ -16,7 +16,10 @@ import subprocess
 import numpy as np
 import pytest
 
+import test_oracle_producer_bwd as producer
 import test_oracle_worked_examples as worked
+
+PINS = {**worked.PINS, **producer.PINS}
 
 ORACLE_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
 
@@ -50,6 +53,25 @@ MUTANTS = {
                         "cell = fp16_round(cell + fp16_round(acc));"),
                        ("double sig = (dq_mode == 1) ? (double)dq_sigma : 1.0;", "double sig = 1.0;")],
                       "dq_accumulators"),
+    # the weight gradient reads the scale grid untransposed ([NB][C/32] instead of [C/32][NB])
+    "wgrad_grid_untransposed": ([("e8m0_value(scale_t[(int64_t)(c / 32) * nb + br])",
+                                  "e8m0_value(scale_t[br * (C / 32) + c / 32])")], "linear_bwd_weight_scaled_blocks"),
+    # the data gradient multiplies by W^T's transpose (W read as [C_out, C_in])
+    "dgrad_w_untransposed": ([("acc += dyd[(size_t)t * C_out + o] * wtd[(size_t)i * C_out + o];",
+                               "acc += dyd[(size_t)t * C_out + o] * wtd[(size_t)o * C_in + i];")],
+                             "linear_bwd_data_exact"),
+    # the weight gradient sums over the first sequence only
+    "wgrad_first_sequence": ([("for (int64_t t = 0; t < T; ++t) acc += dyd",
+                               "for (int64_t t = 0; t < cu[1]; ++t) acc += dyd")], "linear_bwd_adjoint"),
+    # RMSNorm backward with r^2 in place of r^3
+    "rms_bwd_r_squared": ([("xk * r * r * r * S", "xk * r * r * S")], "rmsnorm_bwd_finite_differences"),
+    # RMSNorm backward without gamma on the direct term
+    "rms_bwd_gamma_missing": ([("r * (double)gamma[k] * dyk", "r * dyk")], "rmsnorm_bwd_finite_differences"),
+    # dgamma without the row's r
+    "dgamma_without_r": ([("dg[k] += dyk * xk * r;", "dg[k] += dyk * xk;")], "rmsnorm_bwd_finite_differences"),
+    # the projection term of the RMSNorm backward with the wrong sign
+    "rms_bwd_sign": ([("r * (double)gamma[k] * dyk - xk", "r * (double)gamma[k] * dyk + xk")],
+                     "rmsnorm_bwd_scale_invariance"),
 }
 
 
@@ -88,7 +110,7 @@ def mutant_modules(tmp_path_factory):
 
 @pytest.mark.parametrize("name", list(MUTANTS))
 def test_pin_catches_mutant(name, mutant_modules):
-    pin = worked.PINS[MUTANTS[name][1]]
+    pin = PINS[MUTANTS[name][1]]
     with pytest.raises(AssertionError):
         pin(mutant_modules[name])
 
