@@ -258,6 +258,55 @@ mxfa_status mxfa_linear_quantize(mxfa_mx x, mxfa_mx w, int64_t T, int C_in, int 
                                  int nseq, int max_seqlen, uint8_t* data_out, uint8_t* scale_out,
                                  uint8_t* scale_t_out, void* stream);
 
+/* Backward of the projection, data gradient [BR item 7; AE-TMEM: square 32 x 32 blocks serve the
+ * plain and the transposed product]: dX = dY W accumulated in FP32, written as bf16 (accumulate = 0)
+ * or added in FP32 to the bf16 dx already there (accumulate = 1: an input that feeds two projections,
+ * such as the key and value projections of one activation, gets the sum of both products). It is
+ * the projection kernel with dY as its input and W^T as its weight.
+ *   dy     : [T, C_out] payload with compact SQ32 (or ROW32) scales, e.g. the MXFP8 gradients of
+ *            mxfa_bwd_mx_out
+ *   wt     : W^T [C_in, C_out] payload with ROW32 scales [C_in][C_out/32] (1 x 32 along C_out, the
+ *            contraction dimension), i.e. mxfa_quantize of the transposed weight
+ *   C_out  : multiple of 128 in [128, 65536]; C_in: positive multiple of 128
+ *   cu_seqlens, nseq, max_seqlen : as mxfa_quantize
+ *   dx     : bf16 [T, C_in], 16-byte aligned. No workspace. */
+mxfa_status mxfa_linear_bwd_data(mxfa_mx dy, mxfa_mx wt, int64_t T, int C_out, int C_in, const int32_t* cu_seqlens,
+                                 int nseq, int max_seqlen, int accumulate, uint16_t* dx, void* stream);
+
+/* Workspace bytes of mxfa_linear_bwd_weight (host only; 0 for invalid sizes). */
+size_t mxfa_linear_bwd_weight_workspace_size(int64_t T, int nseq, int C_out, int C_in);
+
+/* Backward of the projection, weight gradient [BR item 7: the producers' second, transposed scale
+ * layout exists for this product; AE-TMEM: square blocks]: dW[o, i] = sum over every token of every
+ * sequence of deq(dY)[t, o] deq(X)[t, i], FP32. Both operands are SQ32 payloads read through their
+ * transposed scale grids, whose rows run along the tokens (the contraction).
+ *   dy, dy_scale_t : [T, C_out] E4M3 and its transposed SQ32 codes [C_out/32][NB]
+ *   x, x_scale_t   : [T, C_in] E4M3 and [C_in/32][NB] (e.g. mxfa_rmsnorm_quantize's outputs)
+ *   NB = sum over sequences of ceil(L/32); C_out, C_in positive multiples of 128; T x C below 2^32
+ *   workspace      : device, 16-byte aligned, >= mxfa_linear_bwd_weight_workspace_size(...) bytes
+ *                    (token block table and one FP32 partial dW per token chunk, summed in order)
+ *   dw             : FP32 [C_out, C_in], 16-byte aligned
+ * The FP32 accumulation order is the hardware's (parity by tolerance). */
+mxfa_status mxfa_linear_bwd_weight(const uint8_t* dy, const uint8_t* dy_scale_t, const uint8_t* x,
+                                   const uint8_t* x_scale_t, int64_t T, int C_out, int C_in,
+                                   const int32_t* cu_seqlens, int nseq, int max_seqlen, void* workspace,
+                                   size_t workspace_bytes, float* dw, void* stream);
+
+/* Workspace bytes of mxfa_rmsnorm_bwd (host only; 0 for invalid sizes). */
+size_t mxfa_rmsnorm_bwd_workspace_size(int64_t T, int C);
+
+/* RMSNorm backward (the producer mxfa_rmsnorm_quantize differentiated with its quantizer passed
+ * straight through): with r = 1 / sqrt(mean_c x_c^2 + eps) per token (computed as the forward does),
+ *   dx_k = r gamma_k dy_k - x_k r^3 (sum_c gamma_c dy_c x_c) / C     -> bf16 [T, C]
+ *   dgamma_c = sum_t dy_tc x_tc r_t                                  -> FP32 [C]
+ *   x: bf16 [T, ld_x] (16-byte aligned, ld_x >= C, multiple of 8); dy: bf16 [T, C]; gamma: FP32 [C]
+ *   C: multiple of 32 in [32, 2048]
+ *   workspace: device, 16-byte aligned, >= mxfa_rmsnorm_bwd_workspace_size(T, C) bytes (per-wave
+ *   partial dgamma rows, summed in order) */
+mxfa_status mxfa_rmsnorm_bwd(const uint16_t* x, int64_t ld_x, int64_t T, int C, const float* gamma, float eps,
+                             const uint16_t* dy, void* workspace, size_t workspace_bytes, uint16_t* dx, float* dgamma,
+                             void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* mxfa_status_string(mxfa_status s);
 

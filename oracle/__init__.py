@@ -66,7 +66,7 @@ def _load():
                                     P, P, P, P, P, P, P, i32]
     lib.orc_rmsnorm_quantize.argtypes = [P, i64, i64, i32, P, f32, P, i32, P, P, P, P]
     lib.orc_linear_quantize.argtypes = [P, P, i32, P, P, i64, i32, i32, P, i32, P, P, P, P, i32]
-    lib.orc_linear_bwd_data.argtypes = [P, P, P, P, i64, i32, i32, P, i32, P, P, i32]
+    lib.orc_linear_bwd_data.argtypes = [P, P, P, P, i64, i32, i32, P, i32, P, P, P, i32]
     lib.orc_linear_bwd_weight.argtypes = [P, P, P, P, i64, i32, i32, P, i32, P, i32]
     lib.orc_rmsnorm_bwd.argtypes = [P, i64, i64, i32, P, f32, P, P, P, P]
     for name in ["orc_quantize_bf16", "orc_quantize_f32", "orc_dequantize", "orc_scale_scatter",
@@ -309,18 +309,20 @@ def linear_quantize(x, x_scale, w, w_scale, cu, x_mode=SQ32, nthreads=None):
     return data, scale, scale_t, y
 
 
-def linear_bwd_data(dy, dy_scale, wt, wt_scale, cu, nthreads=None):
-    """dX = dY W: dy [T, C_out] SQ32 payload with compact scales [NB, C_out/32]; wt = W^T [C_in, C_out]
-    payload with ROW32 scales [C_in, C_out/32]. Returns (dx bf16 bits uint16 [T, C_in], dx float32)."""
+def linear_bwd_data(dy, dy_scale, wt, wt_scale, cu, dx_in=None, nthreads=None):
+    """dX = dY W (+ dx_in): dy [T, C_out] SQ32 payload with compact scales [NB, C_out/32]; wt = W^T
+    [C_in, C_out] payload with ROW32 scales [C_in, C_out/32]; dx_in optional bf16 bits [T, C_in] the
+    product is added to. Returns (dx bf16 bits uint16 [T, C_in], dx float32)."""
     lib = _load()
     cu = _c(cu, np.int32)
     dy, dys, wt, wts = (_c(a, np.uint8) for a in (dy, dy_scale, wt, wt_scale))
     T, C_out = dy.shape
     C_in = wt.shape[0]
+    dxi = None if dx_in is None else _c(dx_in, np.uint16)
     dx = np.empty((T, C_in), np.uint16)
     dxf = np.empty((T, C_in), np.float32)
-    rc = lib.orc_linear_bwd_data(_p(dy), _p(dys), _p(wt), _p(wts), T, C_out, C_in, _p(cu), cu.size - 1, _p(dx),
-                                 _p(dxf), nthreads or default_threads())
+    rc = lib.orc_linear_bwd_data(_p(dy), _p(dys), _p(wt), _p(wts), T, C_out, C_in, _p(cu), cu.size - 1, _p(dxi),
+                                 _p(dx), _p(dxf), nthreads or default_threads())
     _check(rc, "linear_bwd_data")
     return dx, dxf
 

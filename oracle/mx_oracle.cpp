@@ -832,12 +832,16 @@ static void dequantize_sq32_transposed(const uint8_t* data, const uint8_t* scale
 
 // Data gradient: dx = fl32(sum_o deq(dy)_to deq(wt)_io), dy [T, C_out] SQ32 with compact scales
 // [NB][C_out/32], wt = W^T [C_in, C_out] quantized ROW32 (1 x 32 along C_out, the contraction
-// dimension: [TC paragraph 3]); dx_bf16 = bf16 of dx (either output may be NULL).
+// dimension: [TC paragraph 3]); dx_bf16 = bf16 of dx (either output may be NULL). With dx_in (bf16,
+// may be NULL) the product is added to it: dx = fl32(fl32(sum) + dx_in), so that a layer whose input
+// feeds two projections (the key and value projections of one activation) gets dY_k W_k + dY_v W_v
+// from two calls (READING: the sum of the gradients of a shared input).
 // Pinned by: wt = I (exact) gives dx = deq(dy); small-integer operands give the exact integer
-// product; the adjoint identity <dY, X W^T> = <dX, X> with exactly representable W.
+// product, and two accumulated products their exact sum; the adjoint identity <dY, X W^T> = <dX, X>
+// with exactly representable W.
 int orc_linear_bwd_data(const uint8_t* dy, const uint8_t* dy_scale, const uint8_t* wt, const uint8_t* wt_scale,
-                        int64_t T, int C_out, int C_in, const int32_t* cu, int nseq, uint16_t* dx_bf16, float* dx_f32,
-                        int nthreads) {
+                        int64_t T, int C_out, int C_in, const int32_t* cu, int nseq, const uint16_t* dx_in,
+                        uint16_t* dx_bf16, float* dx_f32, int nthreads) {
   if (C_in % 32 || C_out % 32 || !valid_cu(cu, nseq, T)) return -1;
   std::vector<double> dyd((size_t)T * C_out), wtd((size_t)C_in * C_out);
   dequantize_matrix(dy, dy_scale, T, C_out, cu, nseq, SQ32, dyd.data());
@@ -847,7 +851,8 @@ int orc_linear_bwd_data(const uint8_t* dy, const uint8_t* dy_scale, const uint8_
     for (int i = 0; i < C_in; ++i) {
       double acc = 0.0;
       for (int o = 0; o < C_out; ++o) acc += dyd[(size_t)t * C_out + o] * wtd[(size_t)i * C_out + o];
-      const float f = (float)acc;
+      float f = (float)acc;
+      if (dx_in) f = (float)((double)f + bf16_value(dx_in[(size_t)t * C_in + i]));
       if (dx_f32) dx_f32[(size_t)t * C_in + i] = f;
       if (dx_bf16) dx_bf16[(size_t)t * C_in + i] = bf16_round(f);
     }

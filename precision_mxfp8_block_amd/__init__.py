@@ -4,7 +4,8 @@ The functions named mxfa_* are the C ABI of include/mxfa.h, one to one: they onl
 tensors (device memory) and Python numbers into pointers and integers and raise MxfaError on a
 non-OK status. Every step of the computation runs in the HIP kernels of libmxfa.so; there is no
 fallback path. The allocate-and-call helpers at the end (quantize, scale_scatter, fwd, bwd,
-rmsnorm_quantize, linear_quantize) size the output tensors with torch and call the same entry points.
+rmsnorm_quantize, linear_quantize, linear_bwd_data, linear_bwd_weight, rmsnorm_bwd) size the output tensors
+and workspaces with torch and call the same entry points.
 """
 import ctypes
 import os
@@ -19,6 +20,8 @@ __all__ = [
     "mxfa_bwd_workspace_size", "mxfa_rmsnorm_quantize", "mxfa_linear_quantize", "mxfa_status_string",
     "mxfa_last_error_message", "MxOperand", "AttnArgs", "quantize", "scale_scatter", "fwd", "bwd",
     "rmsnorm_quantize", "linear_quantize",
+    "mxfa_linear_bwd_data", "mxfa_linear_bwd_weight", "mxfa_linear_bwd_weight_workspace_size", "mxfa_rmsnorm_bwd",
+    "mxfa_rmsnorm_bwd_workspace_size", "linear_bwd_data", "linear_bwd_weight", "rmsnorm_bwd",
     "library_path",
 ]
 
@@ -81,13 +84,20 @@ def _load():
     lib.mxfa_bwd_no_alloc_max_workspace.restype = ctypes.c_size_t
     lib.mxfa_rmsnorm_quantize.argtypes = [P, i64, i64, i32, P, f32, P, i32, i32, P, P, P, P]
     lib.mxfa_linear_quantize.argtypes = [_Mx, _Mx, i64, i32, i32, P, i32, i32, P, P, P, P]
+    lib.mxfa_linear_bwd_data.argtypes = [_Mx, _Mx, i64, i32, i32, P, i32, i32, i32, P, P]
+    lib.mxfa_linear_bwd_weight_workspace_size.argtypes = [i64, i32, i32, i32]
+    lib.mxfa_linear_bwd_weight_workspace_size.restype = ctypes.c_size_t
+    lib.mxfa_linear_bwd_weight.argtypes = [P, P, P, P, i64, i32, i32, P, i32, i32, P, ctypes.c_size_t, P, P]
+    lib.mxfa_rmsnorm_bwd_workspace_size.argtypes = [i64, i32]
+    lib.mxfa_rmsnorm_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.mxfa_rmsnorm_bwd.argtypes = [P, i64, i64, i32, P, f32, P, P, ctypes.c_size_t, P, P, P]
     lib.mxfa_status_string.argtypes = [i32]
     lib.mxfa_status_string.restype = ctypes.c_char_p
     lib.mxfa_last_error_message.argtypes = []
     lib.mxfa_last_error_message.restype = ctypes.c_char_p
     for n in ("mxfa_quantize", "mxfa_varlen_scale_scatter", "mxfa_fwd", "mxfa_fwd_p_scale", "mxfa_fwd_mx_out", "mxfa_bwd",
               "mxfa_bwd_mx_out", "mxfa_bwd_no_alloc", "mxfa_rmsnorm_quantize",
-              "mxfa_linear_quantize"):
+              "mxfa_linear_quantize", "mxfa_linear_bwd_data", "mxfa_linear_bwd_weight", "mxfa_rmsnorm_bwd"):
         getattr(lib, n).restype = i32
     _lib = lib
     return lib
@@ -372,3 +382,69 @@ def linear_quantize(x, w, cu_host, cu_dev, want_scale_t=True, stream=None):
     mxfa_linear_quantize(x, w, T, C_in, C_out, cu_dev, len(lens), max(lens) if lens else 0, data, scale, scale_t,
                          stream)
     return data, scale, scale_t
+
+
+def mxfa_linear_bwd_data(dy, wt, T, C_out, C_in, cu_seqlens, nseq, max_seqlen, accumulate, dx, stream=None):
+    """dy: MxOperand [T, C_out] (SQ32 or ROW32 compact scales); wt: MxOperand W^T [C_in, C_out] ROW32;
+    accumulate 1 adds to dx."""
+    _check(_load().mxfa_linear_bwd_data(dy._c(), wt._c(), T, C_out, C_in, _ptr(cu_seqlens), nseq, max_seqlen,
+                                        int(accumulate), _ptr(dx), _stream(stream)), "mxfa_linear_bwd_data")
+
+
+def mxfa_linear_bwd_weight_workspace_size(T, nseq, C_out, C_in):
+    return int(_load().mxfa_linear_bwd_weight_workspace_size(T, nseq, C_out, C_in))
+
+
+def mxfa_linear_bwd_weight(dy, dy_scale_t, x, x_scale_t, T, C_out, C_in, cu_seqlens, nseq, max_seqlen, workspace,
+                           workspace_bytes, dw, stream=None):
+    _check(_load().mxfa_linear_bwd_weight(_ptr(dy), _ptr(dy_scale_t), _ptr(x), _ptr(x_scale_t), T, C_out, C_in,
+                                          _ptr(cu_seqlens), nseq, max_seqlen, _ptr(workspace), workspace_bytes,
+                                          _ptr(dw), _stream(stream)), "mxfa_linear_bwd_weight")
+
+
+def mxfa_rmsnorm_bwd_workspace_size(T, C):
+    return int(_load().mxfa_rmsnorm_bwd_workspace_size(T, C))
+
+
+def mxfa_rmsnorm_bwd(x, ld_x, T, C, gamma, eps, dy, workspace, workspace_bytes, dx, dgamma, stream=None):
+    _check(_load().mxfa_rmsnorm_bwd(_ptr(x), ld_x, T, C, _ptr(gamma), eps, _ptr(dy), _ptr(workspace), workspace_bytes,
+                                    _ptr(dx), _ptr(dgamma), _stream(stream)), "mxfa_rmsnorm_bwd")
+
+
+def linear_bwd_data(dy, wt, cu_host, cu_dev, dx=None, stream=None):
+    """dX = dY W as bf16 [T, C_in] (dy: MxOperand [T, C_out]; wt: MxOperand W^T [C_in, C_out] ROW32); with
+    dx given, the product is added to it."""
+    T, C_out = dy.data.shape
+    C_in = wt.data.shape[0]
+    lens = _lens(cu_host)
+    acc = dx is not None
+    if dx is None:
+        dx = torch.empty((T, C_in), dtype=torch.bfloat16, device=dy.data.device)
+    mxfa_linear_bwd_data(dy, wt, T, C_out, C_in, cu_dev, len(lens), max(lens) if lens else 0, acc, dx, stream)
+    return dx
+
+
+def linear_bwd_weight(dy, dy_scale_t, x, x_scale_t, cu_host, cu_dev, workspace=None, stream=None):
+    """dW = dY^T X as FP32 [C_out, C_in] from SQ32 payloads and their transposed scale grids."""
+    T, C_out = dy.shape
+    C_in = x.shape[1]
+    lens = _lens(cu_host)
+    need = mxfa_linear_bwd_weight_workspace_size(T, len(lens), C_out, C_in)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dy.device)
+    dw = torch.empty((C_out, C_in), dtype=torch.float32, device=dy.device)
+    mxfa_linear_bwd_weight(dy, dy_scale_t, x, x_scale_t, T, C_out, C_in, cu_dev, len(lens), max(lens) if lens else 0,
+                           workspace, workspace.numel(), dw, stream)
+    return dw
+
+
+def rmsnorm_bwd(x_bf16, gamma, eps, dy_bf16, workspace=None, stream=None):
+    """RMSNorm backward: returns (dx bf16 [T, C], dgamma FP32 [C])."""
+    T, C = x_bf16.shape
+    need = mxfa_rmsnorm_bwd_workspace_size(T, C)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x_bf16.device)
+    dx = torch.empty((T, C), dtype=torch.bfloat16, device=x_bf16.device)
+    dg = torch.empty(C, dtype=torch.float32, device=x_bf16.device)
+    mxfa_rmsnorm_bwd(x_bf16, x_bf16.stride(0), T, C, gamma, eps, dy_bf16, workspace, workspace.numel(), dx, dg, stream)
+    return dx, dg

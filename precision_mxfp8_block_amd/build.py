@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmxfa.so")
-SOURCES = ["api.hip", "quantize.hip", "attn_fwd.hip", "attn_bwd.hip", "linear.hip"]
+SOURCES = ["api.hip", "quantize.hip", "attn_fwd.hip", "attn_bwd.hip", "linear.hip", "linear_bwd.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

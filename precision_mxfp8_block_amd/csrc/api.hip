@@ -1,6 +1,7 @@
 // C ABI of the MXFP8 attention library: argument validation (host only, before any launch) and
 // dispatch to the kernel launchers. Declarations and the contract of every entry point are in
 // include/mxfa.h.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -374,7 +375,86 @@ mxfa_status mxfa_linear_quantize(mxfa_mx x, mxfa_mx w, int64_t T, int C_in, int 
   mxfa::MxOperand xx{x.data, x.scale, (int)x.mode};
   mxfa::MxOperand ww{w.data, w.scale, (int)w.mode};
   return hip_status(mxfa::launch_linear_quantize(xx, ww, T, C_in, C_out, cu_seqlens, nseq, max_seqlen, data_out,
-                                                 scale_out, scale_t_out, (hipStream_t)stream),
+                                                 scale_out, scale_t_out, nullptr, 0, (hipStream_t)stream),
+                    fn);
+}
+
+mxfa_status mxfa_linear_bwd_data(mxfa_mx dy, mxfa_mx wt, int64_t T, int C_out, int C_in, const int32_t* cu_seqlens,
+                                 int nseq, int max_seqlen, int accumulate, uint16_t* dx, void* stream) {
+  const char* fn = "mxfa_linear_bwd_data";
+  if (T < 0) return fail(MXFA_ERR_INVALID, "%s: T < 0", fn);
+  if (C_out <= 0 || C_out % 128 || C_out > 65536)
+    return fail(MXFA_ERR_INVALID, "%s: C_out=%d must be a multiple of 128 in [128, 65536]", fn, C_out);
+  if (C_in <= 0 || C_in % 128) return fail(MXFA_ERR_INVALID, "%s: C_in=%d must be a positive multiple of 128", fn, C_in);
+  if (dy.mode != MXFA_SQ32 && dy.mode != MXFA_ROW32) return fail(MXFA_ERR_INVALID, "%s: dy.mode must be SQ32 or ROW32", fn);
+  if (wt.mode != MXFA_ROW32) return fail(MXFA_ERR_INVALID, "%s: wt.mode must be ROW32 (scales along C_out)", fn);
+  if (!dy.data || !dy.scale || !wt.data || !wt.scale || !dx) return fail(MXFA_ERR_INVALID, "%s: NULL argument", fn);
+  if (!aligned(dy.data, 16) || !aligned(dy.scale, 16) || !aligned(wt.data, 16) || !aligned(wt.scale, 16) ||
+      !aligned(dx, 16))
+    return fail(MXFA_ERR_INVALID, "%s: misaligned argument", fn);
+  if (accumulate != 0 && accumulate != 1) return fail(MXFA_ERR_INVALID, "%s: accumulate must be 0 or 1", fn);
+  mxfa_status st = check_jagged(cu_seqlens, nseq, max_seqlen, T, fn);
+  if (st != MXFA_OK) return st;
+  if ((int64_t)nseq * ((max_seqlen + 127) / 128) * (C_in / 128) >= ((int64_t)1 << 31))
+    return fail(MXFA_ERR_INVALID, "%s: problem too large for one launch", fn);
+  // the projection kernel with dY as its input (contraction over C_out) and W^T as its weight
+  mxfa::MxOperand dd{dy.data, dy.scale, (int)dy.mode};
+  mxfa::MxOperand ww{wt.data, wt.scale, (int)wt.mode};
+  return hip_status(mxfa::launch_linear_quantize(dd, ww, T, C_out, C_in, cu_seqlens, nseq, max_seqlen, nullptr, nullptr,
+                                                 nullptr, dx, accumulate, (hipStream_t)stream),
+                    fn);
+}
+
+size_t mxfa_linear_bwd_weight_workspace_size(int64_t T, int nseq, int C_out, int C_in) {
+  if (T < 0 || nseq < 1 || C_out <= 0 || C_in <= 0) return 0;
+  return mxfa::wgrad_workspace_bytes(T, nseq, C_out, C_in);
+}
+
+mxfa_status mxfa_linear_bwd_weight(const uint8_t* dy, const uint8_t* dy_scale_t, const uint8_t* x,
+                                   const uint8_t* x_scale_t, int64_t T, int C_out, int C_in,
+                                   const int32_t* cu_seqlens, int nseq, int max_seqlen, void* workspace,
+                                   size_t workspace_bytes, float* dw, void* stream) {
+  const char* fn = "mxfa_linear_bwd_weight";
+  if (T < 0) return fail(MXFA_ERR_INVALID, "%s: T < 0", fn);
+  if (C_out <= 0 || C_out % 128 || C_in <= 0 || C_in % 128)
+    return fail(MXFA_ERR_INVALID, "%s: C_out=%d and C_in=%d must be positive multiples of 128", fn, C_out, C_in);
+  if (T * (int64_t)std::max(C_out, C_in) >= ((int64_t)1 << 32))
+    return fail(MXFA_ERR_UNSUPPORTED, "%s: T x C must stay below 2^32 bytes per operand", fn);
+  if (!dy || !dy_scale_t || !x || !x_scale_t || !dw || !workspace) return fail(MXFA_ERR_INVALID, "%s: NULL argument", fn);
+  if (!aligned(dy, 16) || !aligned(x, 16) || !aligned(dw, 16) || !aligned(workspace, 16))
+    return fail(MXFA_ERR_INVALID, "%s: misaligned argument", fn);
+  mxfa_status st = check_jagged(cu_seqlens, nseq, max_seqlen, T, fn);
+  if (st != MXFA_OK) return st;
+  if (workspace_bytes < mxfa::wgrad_workspace_bytes(T, nseq, C_out, C_in))
+    return fail(MXFA_ERR_INVALID, "%s: workspace too small (%zu < %zu bytes)", fn, workspace_bytes,
+                mxfa::wgrad_workspace_bytes(T, nseq, C_out, C_in));
+  return hip_status(mxfa::launch_linear_wgrad(dy, dy_scale_t, x, x_scale_t, T, C_out, C_in, cu_seqlens, nseq,
+                                              max_seqlen, workspace, dw, (hipStream_t)stream),
+                    fn);
+}
+
+size_t mxfa_rmsnorm_bwd_workspace_size(int64_t T, int C) {
+  if (T < 0 || C <= 0) return 0;
+  return mxfa::rmsnorm_bwd_workspace_bytes(T, C);
+}
+
+mxfa_status mxfa_rmsnorm_bwd(const uint16_t* x, int64_t ld_x, int64_t T, int C, const float* gamma, float eps,
+                             const uint16_t* dy, void* workspace, size_t workspace_bytes, uint16_t* dx, float* dgamma,
+                             void* stream) {
+  const char* fn = "mxfa_rmsnorm_bwd";
+  if (T < 0) return fail(MXFA_ERR_INVALID, "%s: T < 0", fn);
+  if (C <= 0 || C % 32 || C > 2048)
+    return fail(MXFA_ERR_UNSUPPORTED, "%s: C=%d must be a multiple of 32 in [32, 2048]", fn, C);
+  if (ld_x < C || ld_x % 8) return fail(MXFA_ERR_INVALID, "%s: bad ld_x", fn);
+  if (!x || !gamma || !dy || !dx || !dgamma || !workspace) return fail(MXFA_ERR_INVALID, "%s: NULL argument", fn);
+  if (!aligned(x, 16) || !aligned(dy, 16) || !aligned(dx, 16) || !aligned(gamma, 4) || !aligned(dgamma, 16) ||
+      !aligned(workspace, 16))
+    return fail(MXFA_ERR_INVALID, "%s: misaligned argument", fn);
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(MXFA_ERR_INVALID, "%s: eps must be finite and >= 0", fn);
+  if (workspace_bytes < mxfa::rmsnorm_bwd_workspace_bytes(T, C))
+    return fail(MXFA_ERR_INVALID, "%s: workspace too small (%zu < %zu bytes)", fn, workspace_bytes,
+                mxfa::rmsnorm_bwd_workspace_bytes(T, C));
+  return hip_status(mxfa::launch_rmsnorm_bwd(x, ld_x, T, C, gamma, eps, dy, workspace, dx, dgamma, (hipStream_t)stream),
                     fn);
 }
 

@@ -53,6 +53,8 @@ struct LinearParams {
   uint8_t* data;
   uint8_t* scale;
   uint8_t* scale_t;
+  uint16_t* out_bf16;  // set: Y is written as bf16 [T, C_out] instead of quantized
+  int accumulate;      // with out_bf16: Y is added to the bf16 values already there (FP32 add)
 };
 
 // The direct LDS loads are inline asm (mx_lds_dma16/4) and so are their waits and the stage
@@ -409,7 +411,36 @@ __global__ void __launch_bounds__(64 * kLinWaves, 1) linear_quantize_kernel(Line
       const LinPlace pl = place(n);  // the list still holds item n (a refill keeps the current item)
       const int valid = pl.valid, wrows = cur.wrows, ct = pl.ct;
       const int ncs = p.C_out >> 5;
-      if (128 * cq < wrows) {  // wave-uniform: the wave's column half exists
+      if (p.out_bf16) {
+        // bf16 output: each lane writes its token's four runs of 4 consecutive columns per block
+        // (8-byte stores; the two lane halves complete 16-byte runs)
+        if (128 * cq < wrows) {
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const int trow_l = 64 * tq + 32 * i + r;
+            if (trow_l < valid) {
+              uint16_t* orow = p.out_bf16 + (pl.row0 + trow_l) * (int64_t)p.C_out + ct * kCol + 128 * cq;
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                  const mx_v16f& y = acc[i][j];
+                  uint2* dst = reinterpret_cast<uint2*>(orow + 32 * j + 8 * q + 4 * hh);
+                  float v[4] = {y[4 * q], y[4 * q + 1], y[4 * q + 2], y[4 * q + 3]};
+                  if (p.accumulate) {
+                    const uint2 old = *dst;
+                    v[0] += bf16_to_f32(old.x & 0xffffu);
+                    v[1] += bf16_to_f32(old.x >> 16);
+                    v[2] += bf16_to_f32(old.y & 0xffffu);
+                    v[3] += bf16_to_f32(old.y >> 16);
+                  }
+                  *dst = make_uint2(f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16),
+                                    f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16));
+                }
+            }
+          }
+        }
+      } else if (128 * cq < wrows) {  // wave-uniform: the wave's column half exists
         // Rows past the sequence end hold finite values (their X rows re-read the last valid row):
         // they are converted and staged like the others but take no part in the block maximum and
         // are never stored, so the block loop has no lane-dependent branches.
@@ -482,15 +513,17 @@ __global__ void __launch_bounds__(64 * kLinWaves, 1) linear_quantize_kernel(Line
         }
       }
       __syncthreads();
-      const int kq = tid & 15;  // 16-byte piece of the row
-      const bool kq_live = 16 * kq < wrows;
-      uint8_t* dtile = p.data + pl.row0 * (int64_t)p.C_out + ct * kCol + 16 * kq;
+      if (!p.out_bf16) {
+        const int kq = tid & 15;  // 16-byte piece of the row
+        const bool kq_live = 16 * kq < wrows;
+        uint8_t* dtile = p.data + pl.row0 * (int64_t)p.C_out + ct * kCol + 16 * kq;
 #pragma unroll
-      for (int pass = 0; pass < kTok / 32; ++pass) {
-        const int row = pass * 32 + (tid >> 4);
-        if (row < valid && kq_live)
-          *reinterpret_cast<uint4*>(dtile + row * (int64_t)p.C_out) =
-              *reinterpret_cast<const uint4*>(stage + row * kCol + ((kq ^ (row & 15)) << 4));
+        for (int pass = 0; pass < kTok / 32; ++pass) {
+          const int row = pass * 32 + (tid >> 4);
+          if (row < valid && kq_live)
+            *reinterpret_cast<uint4*>(dtile + row * (int64_t)p.C_out) =
+                *reinterpret_cast<const uint4*>(stage + row * kCol + ((kq ^ (row & 15)) << 4));
+        }
       }
     }
     if (n + 1 == count) break;
@@ -518,7 +551,8 @@ namespace mxfa {
 
 hipError_t launch_linear_quantize(const MxOperand& x, const MxOperand& w, int64_t T, int C_in, int C_out,
                                   const int32_t* cu, int nseq, int max_seqlen, uint8_t* data,
-                                  uint8_t* scale, uint8_t* scale_t, hipStream_t stream) {
+                                  uint8_t* scale, uint8_t* scale_t, uint16_t* out_bf16, int accumulate,
+                                  hipStream_t stream) {
   LinearParams p;
   p.x = x.data;
   p.x_scale = x.scale;
@@ -533,6 +567,8 @@ hipError_t launch_linear_quantize(const MxOperand& x, const MxOperand& w, int64_
   p.data = data;
   p.scale = scale;
   p.scale_t = scale_t;
+  p.out_bf16 = out_bf16;
+  p.accumulate = accumulate;
   // an upper bound on the items (every sequence at max_seqlen)
   const int64_t items = (int64_t)nseq * ((max_seqlen + kTok - 1) / kTok) * p.n_coltiles;
   if (T == 0 || items == 0) return hipSuccess;

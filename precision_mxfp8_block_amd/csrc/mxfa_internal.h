@@ -31,9 +31,19 @@ hipError_t launch_scale_scatter(const uint8_t* compact, const int32_t* cu, int n
 hipError_t launch_rmsnorm_quantize(const uint16_t* x, int64_t ld_x, int C, const float* gamma, float eps,
                                    const int32_t* cu, int nseq, int max_seqlen, uint8_t* data, uint8_t* scale,
                                    uint8_t* scale_t, hipStream_t stream);
+// out_bf16 set: Y written as bf16 [T, C_out] (data, scale and scale_t unused) instead of quantized,
+// added to the bf16 values already there when accumulate is set.
 hipError_t launch_linear_quantize(const MxOperand& x, const MxOperand& w, int64_t T, int C_in, int C_out,
                                   const int32_t* cu, int nseq, int max_seqlen, uint8_t* data, uint8_t* scale,
-                                  uint8_t* scale_t, hipStream_t stream);
+                                  uint8_t* scale_t, uint16_t* out_bf16, int accumulate, hipStream_t stream);
+// Producer backward (linear_bwd.hip).
+size_t wgrad_workspace_bytes(int64_t T, int nseq, int C_out, int C_in);
+hipError_t launch_linear_wgrad(const uint8_t* dy, const uint8_t* dy_st, const uint8_t* x, const uint8_t* x_st,
+                               int64_t T, int C_out, int C_in, const int32_t* cu, int nseq, int max_seqlen,
+                               void* workspace, float* dw, hipStream_t stream);
+size_t rmsnorm_bwd_workspace_bytes(int64_t T, int C);
+hipError_t launch_rmsnorm_bwd(const uint16_t* x, int64_t ld_x, int64_t T, int C, const float* gamma, float eps,
+                              const uint16_t* dy, void* workspace, uint16_t* dx, float* dgamma, hipStream_t stream);
 // o and o_mx may each be null (not both): bf16 O and/or E4M3 O in ROW32 blocks with its codes.
 hipError_t launch_attn_fwd(const AttnProblem& a, int p_dynamic, uint16_t* o, uint8_t* o_mx, uint8_t* o_mx_scale,
                            float* lse, hipStream_t stream);

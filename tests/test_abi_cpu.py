@@ -29,7 +29,8 @@ def test_header_declares_the_abi():
     for n in ["mxfa_quantize", "mxfa_fwd", "mxfa_fwd_p_scale", "mxfa_fwd_mx_out", "mxfa_bwd", "mxfa_bwd_mx_out",
               "mxfa_varlen_scale_scatter",
               "mxfa_rmsnorm_quantize",
-              "mxfa_linear_quantize",
+              "mxfa_linear_quantize", "mxfa_linear_bwd_data", "mxfa_linear_bwd_weight",
+              "mxfa_linear_bwd_weight_workspace_size", "mxfa_rmsnorm_bwd", "mxfa_rmsnorm_bwd_workspace_size",
               "mxfa_bwd_workspace_size", "mxfa_status_string", "mxfa_last_error_message"]:
         assert n in names
 
@@ -242,3 +243,78 @@ def test_bwd_no_alloc_argument_errors():
                                  0) == INVALID
     assert lib.mxfa_bwd_no_alloc(ctypes.byref(small), mx._Mx(P, P, 0), mx._Mx(P, P, 1), P, P, P, 1, 1.0, P, P, P,
                                  0) == INVALID  # dO must be SQ32
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(C_out=96), INVALID),           # C_out (the contraction) must be a multiple of 128
+    (dict(C_in=160), INVALID),           # C_in must be a multiple of 128
+    (dict(dy=(P, P, 1)), INVALID),       # dy must be SQ32 or ROW32
+    (dict(wt=(P, P, 2)), INVALID),       # W^T must be ROW32 (scales along C_out)
+    (dict(dy=(0, P, 2)), INVALID),
+    (dict(wt=(P, P + 4, 0)), INVALID),   # misaligned scale
+    (dict(dx=P + 2), INVALID),           # misaligned output
+    (dict(dx=0), INVALID),
+    (dict(nseq=0), INVALID),
+    (dict(T=-1), INVALID),
+    (dict(accumulate=2), INVALID),
+])
+def test_linear_bwd_data_argument_errors(kw, expect):
+    a = dict(dy=(P, P, 2), wt=(P, P, 0), T=256, C_out=1024, C_in=1024, cu=P, nseq=1, max_seqlen=256, accumulate=0,
+             dx=P)
+    a.update(kw)
+    st = _lib().mxfa_linear_bwd_data(mx._Mx(*a["dy"]), mx._Mx(*a["wt"]), a["T"], a["C_out"], a["C_in"], a["cu"],
+                                     a["nseq"], a["max_seqlen"], a["accumulate"], a["dx"], 0)
+    assert st == expect, _last()
+    assert "mxfa_linear_bwd_data" in _last()
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(C_out=96), INVALID),
+    (dict(C_in=160), INVALID),
+    (dict(T=1 << 23), UNSUPPORTED),      # T x C reaches 2^32 bytes (32-bit load offsets)
+    (dict(dy=0), INVALID),
+    (dict(x_st=0), INVALID),
+    (dict(dw=P + 4), INVALID),           # misaligned
+    (dict(workspace=0), INVALID),
+    (dict(workspace_bytes=16), INVALID),  # too small
+    (dict(max_seqlen=300), INVALID),
+])
+def test_linear_bwd_weight_argument_errors(kw, expect):
+    a = dict(dy=P, dy_st=P, x=P, x_st=P, T=256, C_out=1024, C_in=1024, cu=P, nseq=1, max_seqlen=256, workspace=P,
+             workspace_bytes=1 << 40, dw=P)
+    a.update(kw)
+    st = _lib().mxfa_linear_bwd_weight(a["dy"], a["dy_st"], a["x"], a["x_st"], a["T"], a["C_out"], a["C_in"], a["cu"],
+                                       a["nseq"], a["max_seqlen"], a["workspace"], a["workspace_bytes"], a["dw"], 0)
+    assert st == expect, _last()
+    assert "mxfa_linear_bwd_weight" in _last()
+
+
+def test_linear_bwd_weight_workspace_size():
+    """Block table (one int2 per token block, bounded by T/32 + nseq) plus one FP32 partial dW per token
+    chunk; at least one partial, growing with T."""
+    small = mx.mxfa_linear_bwd_weight_workspace_size(256, 1, 1024, 1024)
+    big = mx.mxfa_linear_bwd_weight_workspace_size(75659, 64, 1024, 1024)
+    assert small >= 1024 * 1024 * 4 and big > small
+    assert big % 4 == 0
+    assert mx.mxfa_linear_bwd_weight_workspace_size(-1, 1, 1024, 1024) == 0
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(C=48), UNSUPPORTED),           # multiple of 32
+    (dict(C=4096), UNSUPPORTED),         # above 2048
+    (dict(ld_x=100), INVALID),
+    (dict(x=P + 8), INVALID),
+    (dict(dgamma=P + 4), INVALID),       # float4 stores
+    (dict(eps=float("nan")), INVALID),
+    (dict(workspace_bytes=64), INVALID),
+    (dict(dy=0), INVALID),
+    (dict(T=-1), INVALID),
+])
+def test_rmsnorm_bwd_argument_errors(kw, expect):
+    a = dict(x=P, ld_x=1024, T=128, C=1024, gamma=P, eps=1e-6, dy=P, workspace=P, workspace_bytes=1 << 40, dx=P,
+             dgamma=P)
+    a.update(kw)
+    st = _lib().mxfa_rmsnorm_bwd(a["x"], a["ld_x"], a["T"], a["C"], a["gamma"], a["eps"], a["dy"], a["workspace"],
+                                 a["workspace_bytes"], a["dx"], a["dgamma"], 0)
+    assert st == expect, _last()
+    assert "mxfa_rmsnorm_bwd" in _last()

@@ -63,6 +63,9 @@ MUTANTS = {
     # the weight gradient sums over the first sequence only
     "wgrad_first_sequence": ([("for (int64_t t = 0; t < T; ++t) acc += dyd",
                                "for (int64_t t = 0; t < cu[1]; ++t) acc += dyd")], "linear_bwd_adjoint"),
+    # the accumulated data gradient drops the earlier one
+    "dgrad_accumulate_ignored": ([("if (dx_in) f = (float)((double)f + bf16_value(dx_in[(size_t)t * C_in + i]));",
+                                   "if (dx_in) f = (float)((double)f);")], "linear_bwd_data_accumulate"),
     # RMSNorm backward with r^2 in place of r^3
     "rms_bwd_r_squared": ([("xk * r * r * r * S", "xk * r * r * S")], "rmsnorm_bwd_finite_differences"),
     # RMSNorm backward without gamma on the direct term

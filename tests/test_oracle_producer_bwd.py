@@ -82,6 +82,26 @@ def pin_linear_bwd_data_exact(orc):
     np.testing.assert_array_equal(dx_bf, bf16_bits(expect))
 
 
+def pin_linear_bwd_data_accumulate(orc):
+    """Two data gradients into one input (the key and value projections of one activation): the second
+    call adds its product to the first call's bf16 output. With exactly representable operands whose
+    products and sums stay exact in bf16 (integers below 2^8), the result is dY1 W1 + dY2 W2 exactly."""
+    rng = np.random.default_rng(15)
+    C_out, C_in = 64, 96
+    cu = _cu(LENS)
+    dys = [np.clip(rng.integers(-2, 3, size=(int(cu[-1]), C_out)), -2, 2).astype(np.float64) for _ in range(2)]
+    wts = [rng.integers(-1, 2, size=(C_in, C_out)).astype(np.float64) for _ in range(2)]
+    q = [(orc.quantize(d.astype(np.float32), cu, orc.SQ32), orc.quantize(w.astype(np.float32),
+                                                                          np.array([0, C_in], np.int32), orc.ROW32))
+         for d, w in zip(dys, wts)]
+    dx1, _ = orc.linear_bwd_data(q[0][0][0], q[0][0][1], q[0][1][0], q[0][1][1], cu)
+    dx2, dx2f = orc.linear_bwd_data(q[1][0][0], q[1][0][1], q[1][1][0], q[1][1][1], cu, dx_in=dx1)
+    expect = dys[0] @ wts[0].T + dys[1] @ wts[1].T
+    assert np.abs(expect).max() < 256
+    np.testing.assert_array_equal(dx2f.astype(np.float64), expect)
+    np.testing.assert_array_equal(dx2, bf16_bits(expect))
+
+
 def pin_linear_bwd_data_identity(orc):
     """W = I (exactly representable): dX = deq(dY), bit for bit."""
     rng = np.random.default_rng(12)
@@ -193,6 +213,7 @@ def pin_rmsnorm_bwd_scale_invariance(orc):
 PINS = {
     "linear_bwd_data_exact": pin_linear_bwd_data_exact,
     "linear_bwd_data_identity": pin_linear_bwd_data_identity,
+    "linear_bwd_data_accumulate": pin_linear_bwd_data_accumulate,
     "linear_bwd_weight_scaled_blocks": pin_linear_bwd_weight_scaled_blocks,
     "linear_bwd_adjoint": pin_linear_bwd_adjoint,
     "rmsnorm_bwd_finite_differences": pin_rmsnorm_bwd_finite_differences,
@@ -202,6 +223,10 @@ PINS = {
 
 def test_linear_bwd_data_exact():
     pin_linear_bwd_data_exact(oracle)
+
+
+def test_linear_bwd_data_accumulate():
+    pin_linear_bwd_data_accumulate(oracle)
 
 
 def test_linear_bwd_data_identity():
