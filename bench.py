@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--producers", action="store_true",
                     help="time the fused RMSNorm+quantize producer at the module workload's shapes and the jagged "
                          "scale scatter instead of the attention step (one JSON line of its own)")
+    ap.add_argument("--module", action="store_true",
+                    help="time only the cross-attention module training step (the config-5 shape, then module "
+                         "latency at 4k, 8k and 16k key/value tokens), one JSON line each")
     ap.add_argument("--projection", action="store_true",
                     help="time the module workload's projection GEMM+quantize producers instead of the attention "
                          "step (one JSON line of its own)")
@@ -446,138 +449,232 @@ def bench_workloads(args, torch, mx):
         print(json.dumps(line), flush=True)
 
 
-def bench_module(args, torch, mx):
-    """The cross-attention module step at its full size: RMSNorm+quantize of the query- and key/value-side
-    activations (model dim 1024), the three projection GEMM+quantize producers (SQ32 outputs, both scale
-    layouts), the jagged scale scatter of K and V, attention forward, quantize of dO, attention backward
-    (FP16 dQ). The weights are quantized once, outside the step. Step and phases timed with HIP events."""
-    stream = torch.cuda.current_stream()
-    Bm, NQ, Hm, CM = MODULE_B, 256, 8, MODULE_DIM
+def module_step_setup(torch, mx, lens_k, seed, NQ=256, Hm=8, CM=None):
+    """Buffers of one cross-attention module training step: query side len(lens_k) samples x NQ tokens,
+    key/value side the given jagged lengths, H=Hm heads of 128, model dim CM; bf16 N(0,1) activations,
+    N(0, 0.02) weights quantized once (W along C_in for the forward, W^T along C_out for the data
+    gradient), dO N(0,1)."""
+    CM = CM or MODULE_DIM
+    Bm = len(lens_k)
     lens_q = [NQ] * Bm
-    lens_k = [int(v) for v in synth_mod.lengths(5, Bm, 256, 2048)]
     cu_q, cu_k = synth_mod.cu_seqlens(lens_q), synth_mod.cu_seqlens(lens_k)
     Tq, Tk = int(cu_q[-1]), int(cu_k[-1])
-    cq_d, ck_d = torch.from_numpy(cu_q).cuda(), torch.from_numpy(cu_k).cuda()
-    xq_h = synth_mod.normal_bf16(5, synth_mod.STREAM_ACT, (Tq, CM))
-    xkv_h = synth_mod.normal_bf16(5, synth_mod.STREAM_ACT + 1, (Tk, CM))
-    w_h = {n: synth_mod.normal_bf16(5, synth_mod.STREAM_WEIGHT + i, (CM, CM), std=0.02) for i, n in enumerate("qkv")}
-    do_h = synth_mod.normal_bf16(5, synth_mod.STREAM_DO, (Tq, Hm * D))
-    bf = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
-    xq, xkv, dout = bf(xq_h), bf(xkv_h), bf(do_h)
-    gamma = torch.ones(CM, dtype=torch.float32, device="cuda")
-    wcu = np.array([0, CM], np.int32)
-    w_hat = {n: mx.quantize(bf(w_h[n]), wcu, torch.from_numpy(wcu).cuda(), mx.ROW32) for n in "qkv"}
-    u8 = lambda *shape: torch.empty(shape, dtype=torch.uint8, device="cuda")
-    nbq, nbk = Tq // 32, int(np.sum((np.array(lens_k) + 31) // 32))
-    Pk = mx.mxfa_padded_token_rows(cu_k)
-    xqh = (u8(Tq, CM), u8(nbq, CM // 32), u8(CM // 32, nbq))
-    xkvh = (u8(Tk, CM), u8(nbk, CM // 32), u8(CM // 32, nbk))
+    m = dict(Bm=Bm, NQ=NQ, Hm=Hm, CM=CM, lens_q=lens_q, lens_k=lens_k, cu_q=cu_q, cu_k=cu_k, Tq=Tq, Tk=Tk,
+             cq_d=torch.from_numpy(cu_q).cuda(), ck_d=torch.from_numpy(cu_k).cuda())
+    m["xq_h"] = synth_mod.normal_bf16(seed, synth_mod.STREAM_ACT, (Tq, CM))
+    m["xkv_h"] = synth_mod.normal_bf16(seed, synth_mod.STREAM_ACT + 1, (Tk, CM))
+    m["w_h"] = {n: synth_mod.normal_bf16(seed, synth_mod.STREAM_WEIGHT + i, (CM, CM), std=0.02) for i, n in enumerate("qkv")}
     C = Hm * D
-    gq = (u8(Tq, C), u8(nbq, C // 32), u8(C // 32, nbq))
-    gk = (u8(Tk, C), u8(nbk, C // 32), u8(C // 32, nbk))
-    gv = (u8(Tk, C), u8(nbk, C // 32), u8(C // 32, nbk))
-    pk_, pv_ = u8(Pk // 32, C // 32), u8(Pk // 32, C // 32)
-    gdo = (u8(Tq, C), u8(nbq, C // 32))
+    m["do_h"] = synth_mod.normal_bf16(seed, synth_mod.STREAM_DO, (Tq, C))
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    m["xq"], m["xkv"], m["dout"] = bf(m["xq_h"]), bf(m["xkv_h"]), bf(m["do_h"])
+    m["gamma"] = torch.ones(CM, dtype=torch.float32, device="cuda")
+    wcu, tcu = np.array([0, C], np.int32), np.array([0, CM], np.int32)
+    w_hat = {n: mx.quantize(bf(m["w_h"][n]), wcu, torch.from_numpy(wcu).cuda(), mx.ROW32) for n in "qkv"}
+    wt_hat = {n: mx.quantize(bf(m["w_h"][n].T), tcu, torch.from_numpy(tcu).cuda(), mx.ROW32) for n in "qkv"}
+    m["wop"] = {n: mx.MxOperand(w_hat[n][0], w_hat[n][1], mx.ROW32) for n in "qkv"}
+    m["wtop"] = {n: mx.MxOperand(wt_hat[n][0], wt_hat[n][1], mx.ROW32) for n in "qkv"}
+    u8 = lambda *shape: torch.empty(shape, dtype=torch.uint8, device="cuda")
+    bf16 = lambda *shape: torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+    f32 = lambda *shape: torch.empty(shape, dtype=torch.float32, device="cuda")
+    nbq, nbk = int(np.sum((np.array(lens_q) + 31) // 32)), int(np.sum((np.array(lens_k) + 31) // 32))
+    Pk = mx.mxfa_padded_token_rows(cu_k)
+    sq = lambda T, nb, w: (u8(T, w), u8(nb, w // 32), u8(w // 32, nb))
+    m["xqh"], m["xkvh"] = sq(Tq, nbq, CM), sq(Tk, nbk, CM)
+    m["gq"], m["gk"], m["gv"] = sq(Tq, nbq, C), sq(Tk, nbk, C), sq(Tk, nbk, C)
+    m["pk"], m["pv"] = u8(Pk // 32, C // 32), u8(Pk // 32, C // 32)
+    m["gdo"] = (u8(Tq, C), u8(nbq, C // 32))
     c = float(np.float32(1 / math.sqrt(D)))
-    attn = mx.AttnArgs(mx.MxOperand(gq[0], gq[1], mx.SQ32), mx.MxOperand(gk[0], pk_, mx.SQ32),
-                       mx.MxOperand(gv[0], pv_, mx.SQ32), cq_d, ck_d, Bm, NQ, max(lens_k), Tq, Tk, Hm, D, c, False)
-    o = torch.empty((Tq, C), dtype=torch.bfloat16, device="cuda")
-    lse = torch.empty((Hm, Tq), dtype=torch.float32, device="cuda")
-    ws_bytes = mx.mxfa_bwd_workspace_size(attn, 1)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
-    dq, dk, dv = (torch.empty((T, C), dtype=torch.bfloat16, device="cuda") for T in (Tq, Tk, Tk))
-    wop = {n: mx.MxOperand(w_hat[n][0], w_hat[n][1], mx.ROW32) for n in "qkv"}
-    phases = ["producers", "scatter", "fwd", "bwd"]
+    m["c"] = c
+    m["attn"] = mx.AttnArgs(mx.MxOperand(m["gq"][0], m["gq"][1], mx.SQ32), mx.MxOperand(m["gk"][0], m["pk"], mx.SQ32),
+                            mx.MxOperand(m["gv"][0], m["pv"], mx.SQ32), m["cq_d"], m["ck_d"], Bm, NQ, max(lens_k), Tq,
+                            Tk, Hm, D, c, False)
+    m["o"], m["lse"] = bf16(Tq, C), f32(Hm, Tq)
+    m["ws_bytes"] = mx.mxfa_bwd_workspace_size(m["attn"], 1)
+    m["ws"] = u8(m["ws_bytes"])
+    m["qdq"], m["qdk"], m["qdv"] = sq(Tq, nbq, C), sq(Tk, nbk, C), sq(Tk, nbk, C)
+    m["dxq"], m["dxkv"] = bf16(Tq, CM), bf16(Tk, CM)
+    m["dxq_in"], m["dxkv_in"] = bf16(Tq, CM), bf16(Tk, CM)
+    m["dgq"], m["dgkv"] = f32(CM), f32(CM)
+    m["dw"] = {n: f32(C, CM) for n in "qkv"}
+    m["wg_bytes"] = max(mx.mxfa_linear_bwd_weight_workspace_size(T, Bm, C, CM) for T in (Tq, Tk))
+    m["wg_ws"] = u8(m["wg_bytes"])
+    m["rb_bytes"] = max(mx.mxfa_rmsnorm_bwd_workspace_size(T, CM) for T in (Tq, Tk))
+    m["rb_ws"] = u8(m["rb_bytes"])
+    return m
 
-    def step(ev=None):
-        def mark(i):
-            if ev is not None:
-                ev[i].record(stream)
-        mark(0)
-        mx.mxfa_rmsnorm_quantize(xq, CM, Tq, CM, gamma, 1e-6, cq_d, Bm, NQ, *xqh, stream)
-        mx.mxfa_rmsnorm_quantize(xkv, CM, Tk, CM, gamma, 1e-6, ck_d, Bm, max(lens_k), *xkvh, stream)
-        mx.mxfa_linear_quantize(mx.MxOperand(xqh[0], xqh[1], mx.SQ32), wop["q"], Tq, CM, C, cq_d, Bm, NQ, *gq, stream)
-        for n, g in (("k", gk), ("v", gv)):
-            mx.mxfa_linear_quantize(mx.MxOperand(xkvh[0], xkvh[1], mx.SQ32), wop[n], Tk, CM, C, ck_d, Bm, max(lens_k),
-                                    *g, stream)
-        mark(1)
-        mx.mxfa_varlen_scale_scatter(gk[1], ck_d, Bm, max(lens_k), C, mx.SQ32, pk_, pk_.shape[0], stream)
-        mx.mxfa_varlen_scale_scatter(gv[1], ck_d, Bm, max(lens_k), C, mx.SQ32, pv_, pv_.shape[0], stream)
-        mark(2)
-        mx.mxfa_fwd(attn, o, lse, stream)
-        mark(3)
-        mx.mxfa_quantize(dout, C, Tq, C, cq_d, Bm, NQ, mx.SQ32, gdo[0], gdo[1], None, stream)
-        mx.mxfa_bwd(attn, mx.MxOperand(gv[0], pv_, mx.SQ32), mx.MxOperand(gdo[0], gdo[1], mx.SQ32), o, dout, lse, 1,
-                    1.0, ws, ws_bytes, dq, dk, dv, stream)
-        mark(4)
+
+MODULE_PHASES = ["producers", "scatter", "attn_fwd", "attn_bwd", "producer_bwd"]
+
+
+def module_step(mx, m, stream, ev=None):
+    """One training step of the module; ev: 6 events marking the phase boundaries (or None)."""
+    def mark(i):
+        if ev is not None:
+            ev[i].record(stream)
+    Bm, NQ, CM, Tq, Tk, C = m["Bm"], m["NQ"], m["CM"], m["Tq"], m["Tk"], m["Hm"] * D
+    mk = max(m["lens_k"])
+    cq_d, ck_d = m["cq_d"], m["ck_d"]
+    SQ = mx.SQ32
+    mark(0)
+    mx.mxfa_rmsnorm_quantize(m["xq"], CM, Tq, CM, m["gamma"], 1e-6, cq_d, Bm, NQ, *m["xqh"], stream)
+    mx.mxfa_rmsnorm_quantize(m["xkv"], CM, Tk, CM, m["gamma"], 1e-6, ck_d, Bm, mk, *m["xkvh"], stream)
+    mx.mxfa_linear_quantize(mx.MxOperand(m["xqh"][0], m["xqh"][1], SQ), m["wop"]["q"], Tq, CM, C, cq_d, Bm, NQ,
+                            *m["gq"], stream)
+    for n in "kv":
+        mx.mxfa_linear_quantize(mx.MxOperand(m["xkvh"][0], m["xkvh"][1], SQ), m["wop"][n], Tk, CM, C, ck_d, Bm, mk,
+                                *m["g" + n], stream)
+    mark(1)
+    mx.mxfa_varlen_scale_scatter(m["gk"][1], ck_d, Bm, mk, C, SQ, m["pk"], m["pk"].shape[0], stream)
+    mx.mxfa_varlen_scale_scatter(m["gv"][1], ck_d, Bm, mk, C, SQ, m["pv"], m["pv"].shape[0], stream)
+    mark(2)
+    mx.mxfa_fwd(m["attn"], m["o"], m["lse"], stream)
+    mark(3)
+    mx.mxfa_quantize(m["dout"], C, Tq, C, cq_d, Bm, NQ, SQ, m["gdo"][0], m["gdo"][1], None, stream)
+    # the gradients leave the attention backward as SQ32 MXFP8 with both code layouts (the producers'
+    # format), which the projections' backward consumes directly
+    qdq, qdk, qdv = m["qdq"], m["qdk"], m["qdv"]
+    mx.mxfa_bwd_mx_out(m["attn"], mx.MxOperand(m["gv"][0], m["pv"], SQ), mx.MxOperand(m["gdo"][0], m["gdo"][1], SQ),
+                       m["o"], m["dout"], m["lse"], 1, 1.0, m["ws"], m["ws_bytes"], None, None, None,
+                       [qdq[0], qdq[1], qdk[0], qdk[1], qdv[0], qdv[1], qdq[2], qdk[2], qdv[2]], stream)
+    mark(4)
+    # projection data gradients (the key/value input sums its two), RMSNorm backward, weight gradients
+    mx.mxfa_linear_bwd_data(mx.MxOperand(m["qdq"][0], m["qdq"][1], SQ), m["wtop"]["q"], Tq, C, CM, cq_d, Bm, NQ, 0,
+                            m["dxq"], stream)
+    mx.mxfa_linear_bwd_data(mx.MxOperand(m["qdk"][0], m["qdk"][1], SQ), m["wtop"]["k"], Tk, C, CM, ck_d, Bm, mk, 0,
+                            m["dxkv"], stream)
+    mx.mxfa_linear_bwd_data(mx.MxOperand(m["qdv"][0], m["qdv"][1], SQ), m["wtop"]["v"], Tk, C, CM, ck_d, Bm, mk, 1,
+                            m["dxkv"], stream)
+    mx.mxfa_rmsnorm_bwd(m["xq"], CM, Tq, CM, m["gamma"], 1e-6, m["dxq"], m["rb_ws"], m["rb_bytes"], m["dxq_in"],
+                        m["dgq"], stream)
+    mx.mxfa_rmsnorm_bwd(m["xkv"], CM, Tk, CM, m["gamma"], 1e-6, m["dxkv"], m["rb_ws"], m["rb_bytes"], m["dxkv_in"],
+                        m["dgkv"], stream)
+    for n, qg, xh, T, cu, ms in (("q", m["qdq"], m["xqh"], Tq, cq_d, NQ), ("k", m["qdk"], m["xkvh"], Tk, ck_d, mk),
+                                 ("v", m["qdv"], m["xkvh"], Tk, ck_d, mk)):
+        mx.mxfa_linear_bwd_weight(qg[0], qg[2], xh[0], xh[2], T, C, CM, cu, Bm, ms, m["wg_ws"], m["wg_bytes"],
+                                  m["dw"][n], stream)
+    mark(5)
+
+
+def module_cpu_baseline(m, picks):
+    """The oracle on head 3 of the picked samples: RMSNorm+quantize, the three projections (that head's 128
+    columns), attention fwd + bwd, and the projections' data and weight gradients and the RMSNorm
+    backward of that head's slice."""
+    import oracle
+    D_, CM, NQ = D, m["CM"], m["NQ"]
+    c = m["c"]
+    t0 = time.perf_counter()
+    fl = 0.0
+    h = 3
+    ones = np.ones(CM, np.float32)
+    for s in picks:
+        Lk = m["lens_k"][s]
+        rq = slice(int(m["cu_q"][s]), int(m["cu_q"][s + 1]))
+        rk = slice(int(m["cu_k"][s]), int(m["cu_k"][s + 1]))
+        cq1, ck1 = np.array([0, NQ], np.int32), np.array([0, Lk], np.int32)
+        xq1 = oracle.rmsnorm_quantize(np.ascontiguousarray(m["xq_h"][rq]), ones, 1e-6, cq1)
+        xk1 = oracle.rmsnorm_quantize(np.ascontiguousarray(m["xkv_h"][rk]), ones, 1e-6, ck1)
+        outs, wts = {}, {}
+        for n, x1, cu1 in (("q", xq1, cq1), ("k", xk1, ck1), ("v", xk1, ck1)):
+            wslice = np.ascontiguousarray(m["w_h"][n][h * D_:(h + 1) * D_])
+            wd, ws1, _ = oracle.quantize(wslice, np.array([0, D_], np.int32), oracle.ROW32)
+            wts[n] = oracle.quantize(np.ascontiguousarray(wslice.T), np.array([0, CM], np.int32), oracle.ROW32)
+            outs[n] = oracle.linear_quantize(x1[0], x1[1], wd, ws1, cu1)
+        o16, _, lse1 = oracle.attn_fwd_mx(outs["q"][0], outs["q"][1], 2, outs["k"][0], outs["k"][1], 2, outs["v"][0],
+                                          outs["v"][1], 2, cq1, ck1, 1, D_, c, False)
+        do1 = np.ascontiguousarray(m["do_h"][rq, h * D_:(h + 1) * D_])
+        rdo = oracle.quantize(do1, cq1, oracle.SQ32)
+        g = oracle.attn_bwd_mx(outs["q"][0], outs["q"][1], outs["k"][0], outs["k"][1], outs["v"][0], outs["v"][1], 2,
+                               rdo[0], rdo[1], o16, do1, lse1, cq1, ck1, 1, D_, c, False, 1, 1.0)
+        for n, gname, x1, cu1, xsrc, rows in (("q", "dq", xq1, cq1, m["xq_h"], rq), ("k", "dk", xk1, ck1, m["xkv_h"], rk),
+                                              ("v", "dv", xk1, ck1, m["xkv_h"], rk)):
+            gq = oracle.quantize(g[gname], cu1, oracle.SQ32)
+            dx, _ = oracle.linear_bwd_data(gq[0], gq[1], wts[n][0], wts[n][1], cu1)
+            oracle.rmsnorm_bwd(np.ascontiguousarray(xsrc[rows]), ones, 1e-6, dx)
+            oracle.linear_bwd_weight(gq[0], gq[2], x1[0], x1[2], cu1)
+        fl += 3.5 * attn_flops([NQ], [Lk], 1, False) + 3 * 2.0 * CM * D_ * (NQ + 2 * Lk)
+    return fl, time.perf_counter() - t0
+
+
+def bench_module(args, torch, mx, lens_k=None, seed=5, label=None, cpu_picks=2):
+    """One cross-attention module training step at full size: forward (RMSNorm+quantize of the query- and
+    key/value-side activations, the three projection GEMM+quantize producers with SQ32 outputs in both
+    scale layouts, the jagged scale scatter of K and V, attention forward), backward (quantize dO,
+    attention backward with FP16 dQ writing the gradients as SQ32 MXFP8 with both code layouts, the
+    projections' data gradients (W^T along C_out; the key/value input sums its two), the RMSNorm
+    backward on both sides, the projections' weight gradients over all tokens through the transposed
+    scale grids). The weights are quantized once, outside the step. Step and phases timed with HIP
+    events (median over the timed steps)."""
+    stream = torch.cuda.current_stream()
+    if lens_k is None:
+        lens_k = [int(v) for v in synth_mod.lengths(5, MODULE_B, 256, 2048)]
+    m = module_step_setup(torch, mx, lens_k, seed)
     for _ in range(args.warmup):
-        step()
+        module_step(mx, m, stream)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(MODULE_PHASES) + 1)] for _ in range(args.steps)]
     for i in range(args.steps):
-        step(evs[i])
+        module_step(mx, m, stream, evs[i])
     torch.cuda.synchronize()
-    ph = {n: float(np.median([e[i].elapsed_time(e[i + 1]) * 1e-3 for e in evs])) for i, n in enumerate(phases)}
-    t_step = float(np.median([e[0].elapsed_time(e[4]) * 1e-3 for e in evs]))
-    f_attn = attn_flops(lens_q, lens_k, Hm, False)
+    ph = {n: float(np.median([e[i].elapsed_time(e[i + 1]) * 1e-3 for e in evs])) for i, n in enumerate(MODULE_PHASES)}
+    t_step = float(np.median([e[0].elapsed_time(e[-1]) * 1e-3 for e in evs]))
+    Tq, Tk, CM, C = m["Tq"], m["Tk"], m["CM"], m["Hm"] * D
+    f_attn = attn_flops(m["lens_q"], lens_k, m["Hm"], False)
     f_proj = 2.0 * CM * C * (Tq + 2 * Tk)
-    total = 3.5 * f_attn + f_proj
+    total = 3.5 * f_attn + 3 * f_proj
     res = {k + "_us": round(v * 1e6, 2) for k, v in ph.items()}
-    res.update({"module_step_us": round(t_step * 1e6, 2), "attn_fwd_pflops": round(f_attn / ph["fwd"] / 1e15, 4),
-                "attn_bwd_pflops": round(2.5 * f_attn / ph["bwd"] / 1e15, 4),
-                "projection_pflops": round(f_proj / ph["producers"] / 1e15, 4)})
+    res.update({"module_step_us": round(t_step * 1e6, 2), "fwd_us": round(sum(ph[k] for k in MODULE_PHASES[:3]) * 1e6, 2),
+                "bwd_us": round(sum(ph[k] for k in MODULE_PHASES[3:]) * 1e6, 2),
+                "attn_fwd_pflops": round(f_attn / ph["attn_fwd"] / 1e15, 4),
+                "attn_bwd_pflops": round(2.5 * f_attn / ph["attn_bwd"] / 1e15, 4),
+                "projection_pflops": round(f_proj / ph["producers"] / 1e15, 4),
+                "producer_bwd_pflops": round(2 * f_proj / ph["producer_bwd"] / 1e15, 4)})
     print("# module: " + ", ".join(f"{k}={v}" for k, v in res.items()), file=sys.stderr, flush=True)
     dom = max(ph, key=ph.get)
-    dom_f = {"producers": f_proj, "fwd": f_attn, "bwd": 2.5 * f_attn, "scatter": 0.0}[dom]
+    dom_f = {"producers": f_proj, "attn_fwd": f_attn, "attn_bwd": 2.5 * f_attn, "scatter": 0.0,
+             "producer_bwd": 2 * f_proj}[dom]
+    workload = label or ("cross-attention module training step: 64 samples x 256 queries, 64 key sequences with "
+                         "lengths uniform in [256, 2048], H=8, model dim 1024")
     out = {
-        "metric": "MXFP8 cross-attention module step PF/s (projections + attention fwd/bwd) and % of MI355X dense "
-                  "MXFP8 MFMA peak",
+        "metric": "MXFP8 cross-attention module training step PF/s (projections, their backward, attention fwd/bwd) "
+                  "and % of MI355X dense MXFP8 MFMA peak",
         "value": round(total / t_step / 1e15, 4), "unit": "PF/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(t_step * 1e3, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "mxfp8_e4m3 (fp32 accumulate)", "data": "synthetic",
-        "config": {"workload": "cross-attention module: 64 samples x 256 queries, 64 key sequences with lengths "
-                               "uniform in [256, 2048], H=8, model dim 1024; RMSNorm+quantize -> projection+quantize "
-                               "-> scale scatter -> attention fwd -> quantize dO -> attention bwd (FP16 dQ)",
+        "config": {"workload": workload + "; RMSNorm+quantize -> projection+quantize -> scale scatter -> attention "
+                                          "fwd -> quantize dO -> attention bwd (FP16 dQ, MXFP8 gradients) -> "
+                                          "projection data/weight gradients -> RMSNorm bwd",
                    "tokens_q": Tq, "tokens_k": Tk, **res},
         "roofline": {"bound": "mfma", "achieved": round(dom_f / ph[dom] / 1e12, 2), "peak": PEAK_MXFP8 / 1e12,
                      "unit": "TFLOP/s", "frac": round(dom_f / ph[dom] / PEAK_MXFP8, 4), "traffic": None,
-                     "kernel": {"producers": "rmsnorm_quantize + linear_quantize (phase)", "fwd": "attn_fwd_kernel",
-                                "bwd": "mxfa_bwd call", "scatter": "scale_scatter_kernel"}[dom],
+                     "kernel": {"producers": "rmsnorm_quantize + linear_quantize (phase)", "attn_fwd": "attn_fwd_kernel",
+                                "attn_bwd": "quantize dO + mxfa_bwd_mx_out call", "scatter": "scale_scatter_kernel",
+                                "producer_bwd": "linear_bwd_data x3 + rmsnorm_bwd x2 + linear_bwd_weight x3 (phase)"}[dom],
                      "launch_us": round(ph[dom] * 1e6, 2)},
     }
-    if not args.no_cpu_baseline:
-        import oracle
-        picks = [int(s) for s in np.argsort(lens_k)[::-1][:2]]
-        t0 = time.perf_counter()
-        fl = 0.0
-        for s in picks:
-            h = 3
-            rq, rk = slice(int(cu_q[s]), int(cu_q[s + 1])), slice(int(cu_k[s]), int(cu_k[s + 1]))
-            cq1, ck1 = np.array([0, NQ], np.int32), np.array([0, lens_k[s]], np.int32)
-            ones = np.ones(CM, np.float32)
-            xq1 = oracle.rmsnorm_quantize(np.ascontiguousarray(xq_h[rq]), ones, 1e-6, cq1)
-            xk1 = oracle.rmsnorm_quantize(np.ascontiguousarray(xkv_h[rk]), ones, 1e-6, ck1)
-            outs = {}
-            for n, x1, cu1 in (("q", xq1, cq1), ("k", xk1, ck1), ("v", xk1, ck1)):
-                wd, ws1, _ = oracle.quantize(np.ascontiguousarray(w_h[n][h * D:(h + 1) * D]), np.array([0, D], np.int32),
-                                             oracle.ROW32)
-                outs[n] = oracle.linear_quantize(x1[0], x1[1], wd, ws1, cu1)
-            o16, _, lse1 = oracle.attn_fwd_mx(outs["q"][0], outs["q"][1], 2, outs["k"][0], outs["k"][1], 2, outs["v"][0],
-                                              outs["v"][1], 2, cq1, ck1, 1, D, c, False)
-            do1 = np.ascontiguousarray(do_h[rq, h * D:(h + 1) * D])
-            rdo = oracle.quantize(do1, cq1, oracle.SQ32)
-            oracle.attn_bwd_mx(outs["q"][0], outs["q"][1], outs["k"][0], outs["k"][1], outs["v"][0], outs["v"][1], 2,
-                               rdo[0], rdo[1], o16, do1, lse1, cq1, ck1, 1, D, c, False, 1, 1.0)
-            fl += 3.5 * attn_flops([NQ], [lens_k[s]], 1, False) + 2.0 * CM * D * (NQ + 2 * lens_k[s])
-        dt = time.perf_counter() - t0
+    if not args.no_cpu_baseline and cpu_picks:
+        picks = [int(s) for s in np.argsort(lens_k)[::-1][:cpu_picks]]
+        fl, dt = module_cpu_baseline(m, picks)
         model, nproc, _ = host_cpu()
         out["cpu_baseline"] = {"value": round(fl / dt / 1e15, 8), "unit": "PF/s", "cores": 16 if nproc >= 16 else nproc,
                                "kind": "oracle", "cpu_model": model, "nproc": nproc,
-                               "sample": f"head 3 of the 2 samples with the longest key sequences: RMSNorm+quantize, "
-                                         f"the three projections (that head's 128 columns), attention fwd + bwd, "
-                                         f"{dt:.1f} s wall"}
+                               "sample": f"head 3 of the {len(picks)} samples with the longest key sequences: the whole "
+                                         f"training step on that head's slice, {dt:.1f} s wall"}
     print(json.dumps(out), flush=True)
+    del m
     torch.cuda.empty_cache()
+
+
+def bench_module_latency(args, torch, mx):
+    """Module training-step latency at 4,096, 8,192 and 16,384 key/value tokens (64 samples x 256 queries,
+    key lengths uniform around total / 64), one JSON line each."""
+    for total in (4096, 8192, 16384):
+        L = total // MODULE_B
+        lens = [int(v) for v in synth_mod.lengths(6, MODULE_B, L // 2, L + L // 2)]
+        bench_module(args, torch, mx, lens_k=lens, seed=6,
+                     label=f"cross-attention module training step at {total} key/value tokens (actual {sum(lens)}): "
+                           f"64 samples x 256 queries, key lengths uniform in [{L // 2}, {L + L // 2}], H=8, "
+                           f"model dim 1024", cpu_picks=1)
 
 
 def main():
@@ -607,9 +704,14 @@ def main():
     if args.producers:
         bench_producers(args, torch, mx, synth)
         return
+    if args.module:
+        bench_module(args, torch, mx)
+        bench_module_latency(args, torch, mx)
+        return
     if not args.headline_only:
         bench_workloads(args, torch, mx)
         bench_module(args, torch, mx)
+        bench_module_latency(args, torch, mx)
     host, dev, cu, cu_d = make_inputs(torch, synth)
     T, C = B * N, H * D
     c = float(np.float32(1 / math.sqrt(D)))

@@ -215,6 +215,12 @@ typedef struct {
   uint8_t* dk_scale;  /* [sum_s ceil(Lk_s/32)][H*D/32] */
   uint8_t* dv;        /* [T_k, H*D] */
   uint8_t* dv_scale;  /* [sum_s ceil(Lk_s/32)][H*D/32] */
+  /* Optional (each may be NULL): the same codes in the transposed layout [H*D/32][NB] (NB the
+   * block rows above), the second layout of the producers' format [BR item 7], which the weight
+   * gradient of the projection consumes (mxfa_linear_bwd_weight). */
+  uint8_t* dq_scale_t;
+  uint8_t* dk_scale_t;
+  uint8_t* dv_scale_t;
 } mxfa_grad_mx;
 
 /* Attention backward with the gradients written as MXFP8 [BR item 8 / AE-TMEM: quantized gradients
@@ -224,7 +230,8 @@ typedef struct {
  * serves the next products along D (the projection's input gradient) and along the tokens (its
  * weight gradient); a partial last block takes its maximum over the rows inside the sequence.
  *   dq, dk, dv : bf16 outputs as in mxfa_bwd, all set or all NULL
- *   mx_out     : host struct of six device pointers (all set; payloads 4-byte aligned), or NULL
+ *   mx_out     : host struct of device pointers (the six payloads and codes all set, payloads 4-byte
+ *                aligned; the three transposed code grids each optional), or NULL
  *   at least one of the two sets; everything else as mxfa_bwd. */
 mxfa_status mxfa_bwd_mx_out(const mxfa_attn_args* a, mxfa_mx v_d, mxfa_mx dout, const uint16_t* o,
                             const uint16_t* dout_bf16, const float* lse, mxfa_dq_mode dq_mode, float dq_static_scale,

@@ -46,7 +46,8 @@ class _Mx(ctypes.Structure):
 
 
 class _GradMx(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in ("dq", "dq_scale", "dk", "dk_scale", "dv", "dv_scale")]
+    _fields_ = [(n, ctypes.c_void_p) for n in ("dq", "dq_scale", "dk", "dk_scale", "dv", "dv_scale", "dq_scale_t",
+                                               "dk_scale_t", "dv_scale_t")]
 
 
 class _AttnArgs(ctypes.Structure):
@@ -319,7 +320,8 @@ def bwd(args, v_d, dout, o, dout_bf16, lse, dq_mode=DQ_FP32, dq_static_scale=1.0
 def mxfa_bwd_mx_out(args, v_d, dout, o, dout_bf16, lse, dq_mode, dq_static_scale, workspace, workspace_bytes, dq, dk,
                     dv, mx_out, stream=None):
     """dq, dk, dv: bf16 tensors or None (all or none); mx_out: sequence of the six tensors
-    (dq, dq_scale, dk, dk_scale, dv, dv_scale) or None."""
+    (dq, dq_scale, dk, dk_scale, dv, dv_scale), optionally followed by the three transposed code grids
+    (dq_scale_t, dk_scale_t, dv_scale_t; each may be None), or None."""
     a = args._c()
     g = ctypes.byref(_GradMx(*[_ptr(t) for t in mx_out])) if mx_out is not None else None
     _check(_load().mxfa_bwd_mx_out(ctypes.byref(a), v_d._c(), dout._c(), _ptr(o), _ptr(dout_bf16), _ptr(lse), dq_mode,

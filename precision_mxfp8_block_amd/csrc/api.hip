@@ -186,7 +186,9 @@ mxfa_status launch_bwd(const mxfa_attn_args* a, mxfa_mx v_d, mxfa_mx dout, const
                        void* workspace, uint16_t* dq, uint16_t* dk, uint16_t* dv, const mxfa_grad_mx* mx_out,
                        void* stream, const char* fn) {
   mxfa::GradMxOut gm{};
-  if (mx_out) gm = {mx_out->dq, mx_out->dq_scale, mx_out->dk, mx_out->dk_scale, mx_out->dv, mx_out->dv_scale};
+  if (mx_out)
+    gm = {mx_out->dq,         mx_out->dq_scale,   mx_out->dk,        mx_out->dk_scale, mx_out->dv,
+          mx_out->dv_scale,   mx_out->dq_scale_t, mx_out->dk_scale_t, mx_out->dv_scale_t};
   mxfa::MxOperand vv{v_d.data, v_d.scale, (int)v_d.mode};
   mxfa::MxOperand dd{dout.data, dout.scale, (int)dout.mode};
   return hip_status(mxfa::launch_attn_bwd(to_problem(a), vv, dd, o, dout_bf16, lse,

@@ -150,7 +150,7 @@ __device__ __forceinline__ uint32_t wave_max_dpp(uint32_t v) {
 // left out of the block maximum and not stored. Payload bytes go to dst[row * C] (dst already at
 // the lane's column), the E8M0 code to *code_dst (lane 0). Every lane of the wave must take part.
 __device__ __forceinline__ void store_grad_sq32(const float (&x)[16], int valid, uint8_t* dst, int C,
-                                                uint8_t* code_dst, int lane, int hh) {
+                                                uint8_t* code_dst, uint8_t* code_t_dst, int lane, int hh) {
   uint32_t am = 0;  // largest sign-cleared bit pattern: orders NaN > Inf > finite magnitudes
 #pragma unroll
   for (int v = 0; v < 16; ++v)
@@ -165,7 +165,10 @@ __device__ __forceinline__ void store_grad_sq32(const float (&x)[16], int valid,
     if (r0 < valid) dst[(uint32_t)(r0 * C)] = (uint8_t)w;
     if (r0 + 1 < valid) dst[(uint32_t)((r0 + 1) * C)] = (uint8_t)(w >> 8);
   }
-  if (lane == 0) *code_dst = (uint8_t)code;
+  if (lane == 0) {
+    *code_dst = (uint8_t)code;
+    if (code_t_dst) *code_t_dst = (uint8_t)code;
+  }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -227,6 +230,7 @@ struct BwdParams {
   float c;
   uint16_t *dk, *dv;                  // bf16 gradients, or null
   uint8_t *dk_mx, *dk_mx_scale;       // E4M3 SQ32 gradients (compact codes [blocks][C/32]), or null
+  uint8_t *dk_mx_scale_t, *dv_mx_scale_t;  // the codes transposed [C/32][blocks], each nullable
   uint8_t *dv_mx, *dv_mx_scale;
 };
 
@@ -652,17 +656,20 @@ __global__ void __launch_bounds__(64 * kBwdWaves, 1) attn_bwd_kernel(BwdParams p
     // MXFP8 gradients: the wave's 32 keys x 4 blocks of 32 columns are four SQ32 blocks each (key
     // blocks start at the sequence start); block row koff.blocks32 + (kv0 + 32 kw) / 32
     const int kvalid = Lk - (kv0 + 32 * kw);
-    if (p.dv_mx && kvalid > 0) {
+    if (p.dv_mx && kvalid > 0) {  // wave-uniform
       const int64_t brow = koff.blocks32 + ((kv0 + 32 * kw) >> 5);
+      const int64_t nbk = (p.dk_mx_scale_t || p.dv_mx_scale_t) ? seq_offsets(p.cu_k, p.nseq).blocks32 : 0;
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         float x[16];
 #pragma unroll
         for (int v = 0; v < 16; ++v) x[v] = dv_acc[db][v];
-        store_grad_sq32(x, kvalid, p.dv_mx + orow + 32 * db + r, C, p.dv_mx_scale + brow * Cs + h * 4 + db, lane, hh);
+        store_grad_sq32(x, kvalid, p.dv_mx + orow + 32 * db + r, C, p.dv_mx_scale + brow * Cs + h * 4 + db,
+                        p.dv_mx_scale_t ? p.dv_mx_scale_t + (int64_t)(h * 4 + db) * nbk + brow : nullptr, lane, hh);
 #pragma unroll
         for (int v = 0; v < 16; ++v) x[v] = dk_acc[db][v] * p.c;
-        store_grad_sq32(x, kvalid, p.dk_mx + orow + 32 * db + r, C, p.dk_mx_scale + brow * Cs + h * 4 + db, lane, hh);
+        store_grad_sq32(x, kvalid, p.dk_mx + orow + 32 * db + r, C, p.dk_mx_scale + brow * Cs + h * 4 + db,
+                        p.dk_mx_scale_t ? p.dk_mx_scale_t + (int64_t)(h * 4 + db) * nbk + brow : nullptr, lane, hh);
       }
     }
   }
@@ -690,6 +697,7 @@ struct DqParams {
   float mult;      // c / sigma
   uint16_t* dq;    // bf16 dQ, or null
   uint8_t *dq_mx, *dq_mx_scale;  // E4M3 SQ32 dQ (compact codes [blocks][C/32]), or null
+  uint8_t* dq_mx_scale_t;         // the codes transposed [C/32][blocks], or null
 };
 
 // LDS ring of (dS image, K tile) stages (a power of two). Two stages keep the LDS at 66 KB so two
@@ -836,8 +844,9 @@ __global__ void __launch_bounds__(64 * kDqWaves, 1) attn_dq_kernel(DqParams p) {
   // ---- epilogue: dQ = bf16(c acc / sigma); block rows 8 (v/4) + 4 hh + v%4, column 32 db + r ----
   const int64_t orow = (q_start + q0 + 32 * qb) * (int64_t)C + h * kD;
   const int qvalid = Lq - (q0 + 32 * qb);
-  int64_t brow = 0;
+  int64_t brow = 0, nbq = 0;
   if (p.dq_mx) brow = seq_offsets(p.cu_q, s).blocks32 + ((q0 + 32 * qb) >> 5);
+  if (p.dq_mx_scale_t) nbq = seq_offsets(p.cu_q, p.nseq).blocks32;
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
     const int db = 2 * half + e;
@@ -860,7 +869,8 @@ __global__ void __launch_bounds__(64 * kDqWaves, 1) attn_dq_kernel(DqParams p) {
     }
     // MXFP8 dQ: one SQ32 block (32 queries from the sequence start x 32 columns) per (e, wave)
     if (p.dq_mx && qvalid > 0)
-      store_grad_sq32(x, qvalid, p.dq_mx + orow + 32 * db + r, C, p.dq_mx_scale + brow * Cs + h * 4 + db, lane, hh);
+      store_grad_sq32(x, qvalid, p.dq_mx + orow + 32 * db + r, C, p.dq_mx_scale + brow * Cs + h * 4 + db,
+                      p.dq_mx_scale_t ? p.dq_mx_scale_t + (int64_t)(h * 4 + db) * nbq + brow : nullptr, lane, hh);
   }
 }
 
@@ -927,6 +937,8 @@ hipError_t launch_attn_bwd(const AttnProblem& a, const MxOperand& v_d, const MxO
   p.dk_mx_scale = mx_out ? mx_out->dk_scale : nullptr;
   p.dv_mx = mx_out ? mx_out->dv : nullptr;
   p.dv_mx_scale = mx_out ? mx_out->dv_scale : nullptr;
+  p.dk_mx_scale_t = mx_out ? mx_out->dk_scale_t : nullptr;
+  p.dv_mx_scale_t = mx_out ? mx_out->dv_scale_t : nullptr;
   if (p.total_items > 0) {
     hipLaunchKernelGGL(attn_bwd_kernel, dim3((unsigned)p.total_items), dim3(64 * kBwdWaves), 0, stream, p);
     hipError_t e = hipGetLastError();
@@ -950,6 +962,7 @@ hipError_t launch_attn_bwd(const AttnProblem& a, const MxOperand& v_d, const MxO
   d.dq = dq;
   d.dq_mx = mx_out ? mx_out->dq : nullptr;
   d.dq_mx_scale = mx_out ? mx_out->dq_scale : nullptr;
+  d.dq_mx_scale_t = mx_out ? mx_out->dq_scale_t : nullptr;
   if (d.total_items > 0) {
     hipLaunchKernelGGL(attn_dq_kernel, dim3((unsigned)d.total_items), dim3(64 * kDqWaves), 0, stream, d);
     return hipGetLastError();

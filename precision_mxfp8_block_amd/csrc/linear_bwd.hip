@@ -41,6 +41,7 @@ constexpr int kWgWaves = 8;
 constexpr int kWgSlots = 4;     // LDS ring slots (K steps)
 constexpr int kWgMaxChunk = 256;  // token blocks per chunk, at most
 constexpr int kRmsWaves = 8;
+constexpr int kRmsMaxC = 2048;  // widest row of the RMSNorm backward
 
 template <int N>
 __device__ __forceinline__ void wait_vm_n() {
@@ -63,21 +64,25 @@ __global__ void __launch_bounds__(256) block_table_kernel(const int32_t* __restr
 }
 
 // ---------------------------------------------------------------------------------------------
-// Ordered sum of FP32 partial arrays: out[e] = sum_{k < n_parts} part[k * n + e], k ascending.
+// Ordered sums of FP32 partial arrays: group g = blockIdx.y adds parts g * per_group .. (g + 1) *
+// per_group - 1 (k ascending): out[g * n + e] = sum_k part[k * n + e]. One group gives the total;
+// many partials are summed in two passes (groups, then the group sums) so that no thread walks a long
+// chain of dependent loads.
 // ---------------------------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) sum_parts_kernel(const float* __restrict__ part, int n_parts, int64_t n,
-                                                        float* __restrict__ out) {
+__global__ void __launch_bounds__(256) sum_parts_kernel(const float* __restrict__ part, int n_parts, int per_group,
+                                                        int64_t n, float* __restrict__ out) {
   const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (e >= n) return;
-  float4 acc = *reinterpret_cast<const float4*>(part + e);
-  for (int k = 1; k < n_parts; ++k) {
+  const int k0 = blockIdx.y * per_group, k1 = min(n_parts, k0 + per_group);
+  float4 acc = *reinterpret_cast<const float4*>(part + (int64_t)k0 * n + e);
+  for (int k = k0 + 1; k < k1; ++k) {
     const float4 v = *reinterpret_cast<const float4*>(part + (int64_t)k * n + e);
     acc.x += v.x;
     acc.y += v.y;
     acc.z += v.z;
     acc.w += v.w;
   }
-  *reinterpret_cast<float4*>(out + e) = acc;
+  *reinterpret_cast<float4*>(out + (int64_t)blockIdx.y * n + e) = acc;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -270,16 +275,17 @@ __global__ void __launch_bounds__(64 * kWgWaves, 1) wgrad_kernel(WgradParams p) 
 // RMSNorm backward: one wave per token row (rows strided over all waves of the grid); lane l covers
 // columns 8 l + 512 k (16-byte pieces of x and dy), K = ceil(C / 512) <= 4 pieces per lane (C <= 2048). r is
 // recomputed as the forward computes it (FP64 sum of squares, one fp32 rounding, 1 / sqrt in fp32);
-// each wave accumulates its rows' dy x r per column and writes them as one partial row for the
-// ordered reduction.
+// each wave accumulates its rows' dy x r per column; the workgroup adds its 8 waves' sums in wave order
+// (through LDS) and writes one partial row for the ordered reduction.
 // ---------------------------------------------------------------------------------------------
 template <int K>
 __global__ void __launch_bounds__(64 * kRmsWaves) rmsnorm_bwd_kernel(const uint16_t* __restrict__ x, int64_t ld_x,
                                                                   int64_t T, int C, const float* __restrict__ gamma,
                                                                   float eps, const uint16_t* __restrict__ dy,
                                                                   uint16_t* __restrict__ dx, float* __restrict__ dg_part) {
-  const int lane = threadIdx.x & 63;
-  const int64_t gw = (int64_t)blockIdx.x * kRmsWaves + (threadIdx.x >> 6);
+  __shared__ float lds_dg[kRmsWaves][kRmsMaxC];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t gw = (int64_t)blockIdx.x * kRmsWaves + wave;
   const int64_t nw = (int64_t)gridDim.x * kRmsWaves;
   float g[K][8], dgacc[K][8];
 #pragma unroll
@@ -343,9 +349,16 @@ __global__ void __launch_bounds__(64 * kRmsWaves) rmsnorm_bwd_kernel(const uint1
   for (int k = 0; k < K; ++k) {
     const int c0 = 512 * k + 8 * lane;
     if (c0 >= C) continue;
-    float* dst = dg_part + gw * C + c0;
+    float* dst = &lds_dg[wave][c0];
     *reinterpret_cast<float4*>(dst) = make_float4(dgacc[k][0], dgacc[k][1], dgacc[k][2], dgacc[k][3]);
     *reinterpret_cast<float4*>(dst + 4) = make_float4(dgacc[k][4], dgacc[k][5], dgacc[k][6], dgacc[k][7]);
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < C; c += 64 * kRmsWaves) {
+    float v = lds_dg[0][c];
+#pragma unroll
+    for (int w = 1; w < kRmsWaves; ++w) v += lds_dg[w][c];
+    dg_part[(int64_t)blockIdx.x * C + c] = v;
   }
 }
 
@@ -416,8 +429,8 @@ hipError_t launch_linear_wgrad(const uint8_t* dy, const uint8_t* dy_st, const ui
   const int64_t grid = mx_pair_grid(w.chunks, n_ot * n_it);
   hipLaunchKernelGGL(wgrad_kernel, dim3((unsigned)grid), dim3(64 * kWgWaves), 0, stream, p);
   const int64_t n = (int64_t)C_out * C_in;
-  hipLaunchKernelGGL(sum_parts_kernel, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, stream, part, w.chunks, n,
-                     dw);
+  hipLaunchKernelGGL(sum_parts_kernel, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, stream, part, w.chunks,
+                     w.chunks, n, dw);
   return hipGetLastError();
 }
 
@@ -427,9 +440,12 @@ static int rms_grid(int64_t T) {
   return (int)std::max<int64_t>(1, std::min<int64_t>(kRmsGridMax, (waves + kRmsWaves - 1) / kRmsWaves));
 }
 
+constexpr int kRmsPerGroup = 32;  // partial rows per group of the first reduction pass
+
 size_t rmsnorm_bwd_workspace_bytes(int64_t T, int C) {
   (void)T;
-  return (size_t)kRmsGridMax * kRmsWaves * C * sizeof(float);
+  const size_t parts = kRmsGridMax;
+  return (parts + (parts + kRmsPerGroup - 1) / kRmsPerGroup) * C * sizeof(float);
 }
 
 hipError_t launch_rmsnorm_bwd(const uint16_t* x, int64_t ld_x, int64_t T, int C, const float* gamma, float eps,
@@ -447,8 +463,14 @@ hipError_t launch_rmsnorm_bwd(const uint16_t* x, int64_t ld_x, int64_t T, int C,
   else
     hipLaunchKernelGGL(rmsnorm_bwd_kernel<4>, dim3(grid), dim3(64 * kRmsWaves), 0, stream, x, ld_x, T, C, gamma, eps, dy,
                        dx, part);
-  hipLaunchKernelGGL(sum_parts_kernel, dim3((unsigned)(((int64_t)C / 4 + 255) / 256)), dim3(256), 0, stream, part,
-                     grid * kRmsWaves, (int64_t)C, dgamma);
+  // per-workgroup partial rows -> group sums -> dgamma, each in ascending order
+  const int parts = grid, groups = (parts + kRmsPerGroup - 1) / kRmsPerGroup;
+  float* level2 = part + (int64_t)kRmsGridMax * C;
+  const unsigned cblocks = (unsigned)(((int64_t)C / 4 + 255) / 256);
+  hipLaunchKernelGGL(sum_parts_kernel, dim3(cblocks, (unsigned)groups), dim3(256), 0, stream, part, parts, kRmsPerGroup,
+                     (int64_t)C, level2);
+  hipLaunchKernelGGL(sum_parts_kernel, dim3(cblocks, 1), dim3(256), 0, stream, level2, groups, groups, (int64_t)C,
+                     dgamma);
   return hipGetLastError();
 }
 

@@ -51,6 +51,7 @@ size_t bwd_workspace_bytes(int64_t Tq, int H, int nseq, int max_q, int max_k);
 // MXFP8 gradient outputs: E4M3 payloads [T, H*D] and compact SQ32 codes [blocks][H*D/32].
 struct GradMxOut {
   uint8_t *dq, *dq_scale, *dk, *dk_scale, *dv, *dv_scale;
+  uint8_t *dq_scale_t, *dk_scale_t, *dv_scale_t;  // transposed code grids [C/32][NB], each nullable
 };
 // dq, dk, dv (bf16) are all null or all set; mx_out (all six pointers set) may be null.
 hipError_t launch_attn_bwd(const AttnProblem& a, const MxOperand& v_d, const MxOperand& dout, const uint16_t* o,

@@ -277,22 +277,28 @@ class AttnCase:
 
     def run_gpu_bwd_mx_out(self, dq_mode, sigma=1.0, with_bf16=True):
         """mxfa_bwd_mx_out on the same operands, guarded and NaN-prefilled outputs: ((dq, dk, dv) bf16 bits or
-        None, six numpy arrays: dq, dq_scale, dk, dk_scale, dv, dv_scale)."""
+        None, six numpy arrays: dq, dq_scale, dk, dk_scale, dv, dv_scale). The transposed code grids are
+        requested too and must equal the transposes of the compact ones."""
         vop, doop = self.bwd_operands()
         need = mx.mxfa_bwd_workspace_size(self.args, dq_mode)
         ws = Guarded((need,), torch.uint8)
         nbq, nbk = int(np.sum((np.array(self.lens_q) + 31) // 32)), int(np.sum((np.array(self.lens_k) + 31) // 32))
         mxo = [Guarded(shape, torch.uint8) for shape in ((self.Tq, self.C), (nbq, self.C // 32), (self.Tk, self.C),
                                                           (nbk, self.C // 32), (self.Tk, self.C), (nbk, self.C // 32))]
+        # the codes also in the transposed layout [C/32][NB] (the weight gradient's operand layout)
+        mxt = [Guarded(shape, torch.uint8) for shape in ((self.C // 32, nbq), (self.C // 32, nbk), (self.C // 32, nbk))]
         bf = [Guarded((T, self.C), torch.bfloat16) for T in (self.Tq, self.Tk, self.Tk)] if with_bf16 else None
         mx.mxfa_bwd_mx_out(self.args, vop, doop, self.o_dev, self.do_d, self.lse_dev, dq_mode, sigma, ws.t, need,
-                           *((x.t for x in bf) if bf else (None, None, None)), [x.t for x in mxo])
+                           *((x.t for x in bf) if bf else (None, None, None)), [x.t for x in mxo] + [x.t for x in mxt])
         torch.cuda.synchronize()
         ws.check("workspace")
-        for x in mxo + (bf or []):
+        for x in mxo + mxt + (bf or []):
             x.check("MXFP8 backward output")
+        out = tuple(x.t.cpu().numpy() for x in mxo)
+        for i, t in enumerate(mxt):
+            np.testing.assert_array_equal(t.t.cpu().numpy(), out[2 * i + 1].T)
         bits = tuple(to_host_bf16_bits(x.t) for x in bf) if bf is not None else None
-        return bits, tuple(x.t.cpu().numpy() for x in mxo)
+        return bits, out
 
     # ---------------- oracle ----------------
     def run_oracle_fwd(self, p_scale=oracle.P_STATIC, orc=oracle):
