@@ -230,7 +230,7 @@ typedef struct {
  * serves the next products along D (the projection's input gradient) and along the tokens (its
  * weight gradient); a partial last block takes its maximum over the rows inside the sequence.
  *   dq, dk, dv : bf16 outputs as in mxfa_bwd, all set or all NULL
- *   mx_out     : host struct of device pointers (the six payloads and codes all set, payloads 4-byte
+ *   mx_out     : host struct of device pointers (the six payloads and codes all set, payloads 16-byte
  *                aligned; the three transposed code grids each optional), or NULL
  *   at least one of the two sets; everything else as mxfa_bwd. */
 mxfa_status mxfa_bwd_mx_out(const mxfa_attn_args* a, mxfa_mx v_d, mxfa_mx dout, const uint16_t* o,

@@ -161,8 +161,8 @@ mxfa_status check_bwd(const mxfa_attn_args* a, mxfa_mx v_d, mxfa_mx dout, const 
     const mxfa_grad_mx& g = *mx_out;
     if (!g.dq || !g.dq_scale || !g.dk || !g.dk_scale || !g.dv || !g.dv_scale)
       return fail(MXFA_ERR_INVALID, "%s: every MXFP8 gradient payload and scale pointer must be set", fn);
-    if (!aligned(g.dq, 4) || !aligned(g.dk, 4) || !aligned(g.dv, 4))
-      return fail(MXFA_ERR_INVALID, "%s: MXFP8 gradient payloads must be 4-byte aligned", fn);
+    if (!aligned(g.dq, 16) || !aligned(g.dk, 16) || !aligned(g.dv, 16))
+      return fail(MXFA_ERR_INVALID, "%s: MXFP8 gradient payloads must be 16-byte aligned", fn);
   }
   if (dq_mode != MXFA_DQ_FP32 && dq_mode != MXFA_DQ_FP16_STATIC)
     return fail(MXFA_ERR_INVALID, "%s: bad dq_mode %d", fn, (int)dq_mode);

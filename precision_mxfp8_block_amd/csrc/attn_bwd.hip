@@ -147,10 +147,14 @@ __device__ __forceinline__ uint32_t wave_max_dpp(uint32_t v) {
 // SQ32 quantization (the MX scale rule of the operand quantizer) of one 32 x 32 gradient block that
 // a wave holds in the MFMA accumulator layout: lane (r, hh) holds column r and rows
 // 8 (v / 4) + 4 hh + v % 4, v = 0..15. Rows at or past `valid` lie outside the sequence: they are
-// left out of the block maximum and not stored. Payload bytes go to dst[row * C] (dst already at
-// the lane's column), the E8M0 code to *code_dst (lane 0). Every lane of the wave must take part.
+// left out of the block maximum and not stored. The payload goes through the wave's 1 KB of LDS
+// (`stage`, [32 rows][32 bytes]) so that it leaves as 16-byte row pieces (lane l: row l / 2, bytes
+// 16 (l % 2) ..), to dst + row * C (dst at the block's row 0, column 0); the E8M0 code to *code_dst
+// and, when set, *code_t_dst (lane 0). Every lane of the wave must take part; LDS operations of one
+// wave execute in order, so the reads see the wave's own writes.
 __device__ __forceinline__ void store_grad_sq32(const float (&x)[16], int valid, uint8_t* dst, int C,
-                                                uint8_t* code_dst, uint8_t* code_t_dst, int lane, int hh) {
+                                                uint8_t* code_dst, uint8_t* code_t_dst, uint8_t* stage, int lane,
+                                                int hh) {
   uint32_t am = 0;  // largest sign-cleared bit pattern: orders NaN > Inf > finite magnitudes
 #pragma unroll
   for (int v = 0; v < 16; ++v)
@@ -158,13 +162,17 @@ __device__ __forceinline__ void store_grad_sq32(const float (&x)[16], int valid,
   am = wave_max_dpp(am);
   const uint32_t code = mx_code_from_amax_bits(am);
   const float inv = mx_inv_scale(code == 255u ? 127u : code);
+  const int r = lane & 31;
 #pragma unroll
   for (int v = 0; v < 16; v += 2) {
     const uint32_t w = code == 255u ? 0x7f7fu : mx_pack2_lo(x[v] * inv, x[v + 1] * inv, 0u);
     const int r0 = 8 * (v >> 2) + 4 * hh + (v & 3);
-    if (r0 < valid) dst[(uint32_t)(r0 * C)] = (uint8_t)w;
-    if (r0 + 1 < valid) dst[(uint32_t)((r0 + 1) * C)] = (uint8_t)(w >> 8);
+    stage[r0 * 32 + r] = (uint8_t)w;
+    stage[(r0 + 1) * 32 + r] = (uint8_t)(w >> 8);
   }
+  const int row = lane >> 1;
+  const uint4 piece = *reinterpret_cast<const uint4*>(stage + row * 32 + 16 * (lane & 1));
+  if (row < valid) *reinterpret_cast<uint4*>(dst + (int64_t)row * C + 16 * (lane & 1)) = piece;
   if (lane == 0) {
     *code_dst = (uint8_t)code;
     if (code_t_dst) *code_t_dst = (uint8_t)code;
@@ -659,17 +667,22 @@ __global__ void __launch_bounds__(64 * kBwdWaves, 1) attn_bwd_kernel(BwdParams p
     if (p.dv_mx && kvalid > 0) {  // wave-uniform
       const int64_t brow = koff.blocks32 + ((kv0 + 32 * kw) >> 5);
       const int64_t nbk = (p.dk_mx_scale_t || p.dv_mx_scale_t) ? seq_offsets(p.cu_k, p.nseq).blocks32 : 0;
+      // staging for the payload: 1 KB of this wave's own part of the dS image buffer, which nothing
+      // reads after the last period (this wave read its image chunks before its last stores)
+      uint8_t* stage = lds_ds + kw * 4096;
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         float x[16];
 #pragma unroll
         for (int v = 0; v < 16; ++v) x[v] = dv_acc[db][v];
-        store_grad_sq32(x, kvalid, p.dv_mx + orow + 32 * db + r, C, p.dv_mx_scale + brow * Cs + h * 4 + db,
-                        p.dv_mx_scale_t ? p.dv_mx_scale_t + (int64_t)(h * 4 + db) * nbk + brow : nullptr, lane, hh);
+        store_grad_sq32(x, kvalid, p.dv_mx + orow + 32 * db, C, p.dv_mx_scale + brow * Cs + h * 4 + db,
+                        p.dv_mx_scale_t ? p.dv_mx_scale_t + (int64_t)(h * 4 + db) * nbk + brow : nullptr, stage, lane,
+                        hh);
 #pragma unroll
         for (int v = 0; v < 16; ++v) x[v] = dk_acc[db][v] * p.c;
-        store_grad_sq32(x, kvalid, p.dk_mx + orow + 32 * db + r, C, p.dk_mx_scale + brow * Cs + h * 4 + db,
-                        p.dk_mx_scale_t ? p.dk_mx_scale_t + (int64_t)(h * 4 + db) * nbk + brow : nullptr, lane, hh);
+        store_grad_sq32(x, kvalid, p.dk_mx + orow + 32 * db, C, p.dk_mx_scale + brow * Cs + h * 4 + db,
+                        p.dk_mx_scale_t ? p.dk_mx_scale_t + (int64_t)(h * 4 + db) * nbk + brow : nullptr, stage, lane,
+                        hh);
       }
     }
   }
@@ -845,7 +858,10 @@ __global__ void __launch_bounds__(64 * kDqWaves, 1) attn_dq_kernel(DqParams p) {
   const int64_t orow = (q_start + q0 + 32 * qb) * (int64_t)C + h * kD;
   const int qvalid = Lq - (q0 + 32 * qb);
   int64_t brow = 0, nbq = 0;
-  if (p.dq_mx) brow = seq_offsets(p.cu_q, s).blocks32 + ((q0 + 32 * qb) >> 5);
+  if (p.dq_mx) {
+    brow = seq_offsets(p.cu_q, s).blocks32 + ((q0 + 32 * qb) >> 5);
+    __syncthreads();  // every wave is done with the image stages; 1 KB of stage 0 per wave stages dQ
+  }
   if (p.dq_mx_scale_t) nbq = seq_offsets(p.cu_q, p.nseq).blocks32;
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
@@ -869,8 +885,9 @@ __global__ void __launch_bounds__(64 * kDqWaves, 1) attn_dq_kernel(DqParams p) {
     }
     // MXFP8 dQ: one SQ32 block (32 queries from the sequence start x 32 columns) per (e, wave)
     if (p.dq_mx && qvalid > 0)
-      store_grad_sq32(x, qvalid, p.dq_mx + orow + 32 * db + r, C, p.dq_mx_scale + brow * Cs + h * 4 + db,
-                      p.dq_mx_scale_t ? p.dq_mx_scale_t + (int64_t)(h * 4 + db) * nbq + brow : nullptr, lane, hh);
+      store_grad_sq32(x, qvalid, p.dq_mx + orow + 32 * db, C, p.dq_mx_scale + brow * Cs + h * 4 + db,
+                      p.dq_mx_scale_t ? p.dq_mx_scale_t + (int64_t)(h * 4 + db) * nbq + brow : nullptr,
+                      &lds_img[0][wave_s * 1024], lane, hh);
   }
 }
 

@@ -157,7 +157,7 @@ def test_bwd_argument_errors(kw, expect):
     ((0, 0, 0), None),                      # no gradient output at all
     ((P, 0, 0), None),                      # bf16 gradients only partly given
     ((0, 0, 0), (P, P, P, 0, P, P)),        # an MXFP8 scale pointer missing
-    ((0, 0, 0), (P, P, P + 2, P, P, P)),    # an MXFP8 payload not 4-byte aligned
+    ((0, 0, 0), (P, P, P + 8, P, P, P)),    # an MXFP8 payload not 16-byte aligned
     ((P, P, P + 8, ), (P, P, P, P, P, P)),  # bf16 dv misaligned
 ])
 def test_bwd_mx_out_argument_errors(bf16, mxp):
