@@ -227,6 +227,7 @@ struct BwdParams {
   const int32_t *cu_q, *cu_k;
   int nseq, H, n_ktiles;
   int total_items;
+  int contiguous;  // item order (mx_item)
   float c2;  // c * log2(e)
   int causal;
   const float* pexp;    // [H][Tq]: 8 - LSE log2(e)
@@ -253,7 +254,7 @@ __global__ void __launch_bounds__(64 * kBwdWaves, 1) attn_bwd_kernel(BwdParams p
   __shared__ __attribute__((aligned(256))) uint32_t lds_sc[3][64];      // [stage][Q, dO scale words]
   __shared__ uint32_t lds_dscode[4];                                     // dS codes [key block] (byte: q block)
 
-  const int item = mx_pair_item((int)blockIdx.x, p.n_ktiles, p.nseq * p.H);
+  const int item = mx_item(p.contiguous, (int)blockIdx.x, p.total_items, p.n_ktiles, p.nseq * p.H);
   if (item < 0) return;
   const int kt = item % p.n_ktiles;
   const int h = (item / p.n_ktiles) % p.H;
@@ -702,6 +703,7 @@ struct DqParams {
   const int32_t *cu_q, *cu_k;
   int nseq, H, ntq_max, ntk_max;
   int total_items;
+  int contiguous;
   int causal;
   const uint8_t* ds_img;
   const uint8_t* ds_codes;
@@ -723,7 +725,8 @@ __global__ void __launch_bounds__(64 * kDqWaves, 1) attn_dq_kernel(DqParams p) {
   __shared__ __attribute__((aligned(256))) uint32_t lds_codes[kDqStages][64];
   __shared__ __attribute__((aligned(256))) uint32_t lds_ksc[kDqStages][64];
 
-  const int item = mx_pair_item((int)blockIdx.x, p.ntq_max, p.nseq * p.H);
+  // pairs in the reverse of the main pass's order: the images it wrote last are read first
+  const int item = mx_item(p.contiguous, (int)blockIdx.x, p.total_items, p.ntq_max, p.nseq * p.H, true);
   if (item < 0) return;
   const int qt = item % p.ntq_max;
   const int h = (item / p.ntq_max) % p.H;
@@ -941,7 +944,10 @@ hipError_t launch_attn_bwd(const AttnProblem& a, const MxOperand& v_d, const MxO
   p.cu_q = a.cu_q; p.cu_k = a.cu_k;
   p.nseq = a.nseq; p.H = a.H;
   p.n_ktiles = ntk_max;
-  p.total_items = (int)mx_pair_grid((int64_t)a.H * a.nseq, p.n_ktiles);  // < 2^31, checked by the caller
+  const MxItemOrder ord = mx_item_order(a.total_q, a.total_k, a.nseq, a.max_seqlen_q, a.max_seqlen_k,
+                                       (int64_t)a.H * a.nseq, p.n_ktiles);
+  p.contiguous = ord.contiguous;
+  p.total_items = (int)ord.grid;  // < 2^31, checked by the caller
   p.c2 = a.softmax_scale * kLog2e;
   p.causal = a.causal;
   p.pexp = pexp; p.ndelta = delta; p.Tq = Tq;
@@ -965,7 +971,10 @@ hipError_t launch_attn_bwd(const AttnProblem& a, const MxOperand& v_d, const MxO
   d.k = a.k.data; d.k_scale = a.k.scale;
   d.cu_q = a.cu_q; d.cu_k = a.cu_k;
   d.nseq = a.nseq; d.H = a.H; d.ntq_max = ntq_max; d.ntk_max = ntk_max;
-  d.total_items = (int)mx_pair_grid((int64_t)a.H * a.nseq, ntq_max);
+  const MxItemOrder dord = mx_item_order(a.total_q, a.total_k, a.nseq, a.max_seqlen_q, a.max_seqlen_k,
+                                        (int64_t)a.H * a.nseq, ntq_max);
+  d.contiguous = dord.contiguous;
+  d.total_items = (int)dord.grid;
   d.causal = a.causal;
   d.ds_img = ws + w.img;
   d.ds_codes = ws + w.codes;

@@ -183,15 +183,44 @@ __device__ __forceinline__ int64_t mx_uniform_i64(int64_t v) {
 // the pairs x, x + 8, x + 16, ... and runs each pair's tiles back to back, so one head's K and V (or Q
 // and dO) stay in one XCD's L2, and the heads of every sequence spread over all XCDs: a jagged batch
 // gives each XCD the same share of long and short sequences. The grid is mx_pair_grid(pairs, tiles);
-// ids that fall past the last pair give -1.
+// ids that fall past the last pair give -1. reverse runs each XCD's pairs last to first.
+//
+// For a uniform batch (every sequence at the maximum length) every pair carries the same work, and the
+// backward launcher takes the contiguous order instead (mx_item_order): XCD x runs one contiguous
+// range of about total / 8 items, a pair's tiles still back to back; the grid is the item count.
+// Measured on MI355X (B=4 H=16 N=4096, D=128): with both backward passes in this order the dQ pass
+// takes 270 us instead of 311 us (causal: 160 instead of 193 us); the main pass and the forward do not
+// change. The choice never affects results: both orders visit every item once.
 __host__ __device__ __forceinline__ int64_t mx_pair_grid(int64_t pairs, int64_t tiles) {
   return (pairs + 7) / 8 * 8 * tiles;
 }
-__device__ __forceinline__ int mx_pair_item(int bid, int tiles, int pairs) {
+__device__ __forceinline__ int mx_pair_item(int bid, int tiles, int pairs, bool reverse = false) {
   const int x = bid & 7, slot = bid >> 3;
   const int pl = slot / tiles, t = slot - pl * tiles;
-  const int pair = pl * 8 + x;
+  const int pair = (reverse ? (pairs + 7) / 8 - 1 - pl : pl) * 8 + x;
   return pair < pairs ? pair * tiles + t : -1;
+}
+__device__ __forceinline__ int mx_range_item(int bid, int total, bool reverse = false) {
+  const int per = total >> 3, rem = total & 7;
+  const int x = bid & 7, slot = bid >> 3;
+  const int cnt = per + (x < rem ? 1 : 0);  // ids x, x + 8, ... below total
+  return x * per + (x < rem ? x : rem) + (reverse ? cnt - 1 - slot : slot);
+}
+// Item order and grid of an attention launch: contiguous ranges for a uniform batch (every sequence at
+// the maximum length: total tokens = sequences x maximum, on both sides), else pairs dealt to XCDs.
+struct MxItemOrder {
+  int contiguous;
+  int64_t grid;
+};
+__host__ __forceinline__ MxItemOrder mx_item_order(int64_t total_q, int64_t total_k, int nseq, int max_q, int max_k,
+                                                   int64_t pairs, int64_t tiles) {
+  MxItemOrder o;
+  o.contiguous = total_q == (int64_t)nseq * max_q && total_k == (int64_t)nseq * max_k;
+  o.grid = o.contiguous ? pairs * tiles : mx_pair_grid(pairs, tiles);
+  return o;
+}
+__device__ __forceinline__ int mx_item(int contiguous, int bid, int total, int tiles, int pairs, bool reverse = false) {
+  return contiguous ? mx_range_item(bid, total, reverse) : mx_pair_item(bid, tiles, pairs, reverse);
 }
 
 // Offsets of sequence s in the compact and padded layouts from the device cu_seqlens, computed by
