@@ -641,7 +641,12 @@ __global__ void __launch_bounds__(64 * kBwdWaves, 1) attn_bwd_kernel(BwdParams p
       if (k > qt_begin) {
         if (lane == 0) *reinterpret_cast<uint32_t*>(p.ds_codes + tile * 16 + 4 * kw) = codes;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) *reinterpret_cast<uint4*>(img + c * 1024 + lane * 16) = imgv[c];
+        // non-temporal: the dQ pass reads each image once, and stores that do not stay dirty in the
+        // caches leave its reads without write-backs to wait behind (dQ pass 268 -> 250 us measured)
+        for (int c = 0; c < 4; ++c) {
+          const mx_u32x4 v4 = {imgv[c].x, imgv[c].y, imgv[c].z, imgv[c].w};
+          __builtin_nontemporal_store(v4, reinterpret_cast<mx_u32x4*>(img + c * 1024 + lane * 16));
+        }
       }
       st = st_next;
     }
@@ -754,11 +759,11 @@ __global__ void __launch_bounds__(64 * kDqWaves, 1) attn_dq_kernel(DqParams p) {
   const uint8_t* code_base = p.ds_codes + tile0 * 16;
   const uint8_t* ksc_base = p.k_scale + (koff.padded / 32) * (int64_t)Cs + h * 4;
   auto issue_loads = [&](int kt, uint8_t* img, uint8_t* ktile, uint32_t* codes, uint32_t* kscw) {
-    // the dS_q image is copied as it is (2 KB per wave, 16 B per lane)
+    // the dS_q image is copied as it is (2 KB per wave, 16 B per lane), read once: non-temporal
 #pragma unroll
     for (int c = 0; c < TileLane<kDqWaves>::kPieces; ++c) {
       const int piece = wave_s * TileLane<kDqWaves>::kPieces + c;
-      mx_lds_dma16((MX_LDS void*)(img + piece * 1024), img_base + (int64_t)kt * (kTile * kD),
+      mx_lds_dma16_nt((MX_LDS void*)(img + piece * 1024), img_base + (int64_t)kt * (kTile * kD),
                    (uint32_t)(piece * 1024 + lane * 16));
     }
     issue_tile_load(ktile, kbase + (int64_t)kt * kTile * C, Lk - kt * kTile, C, tl, wave_s);

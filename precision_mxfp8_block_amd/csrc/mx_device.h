@@ -23,6 +23,7 @@ typedef int mx_v4i __attribute__((ext_vector_type(4)));
 typedef int mx_v2i __attribute__((ext_vector_type(2)));
 typedef float mx_v16f __attribute__((ext_vector_type(16)));
 typedef float mx_v4f __attribute__((ext_vector_type(4)));
+typedef unsigned int mx_u32x4 __attribute__((ext_vector_type(4)));
 
 #define MX_LDS __attribute__((address_space(3)))
 
@@ -119,6 +120,14 @@ __device__ __forceinline__ void* mx_uniform_ptr(void* p) {
 __device__ __forceinline__ void mx_lds_dma16(MX_LDS void* lds_dst, const void* base, uint32_t voff) {
   const uint32_t m = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)lds_dst);
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m), "v"(voff), "s"(mx_uniform_ptr((void*)base))
+               : "memory");
+}
+
+// mx_lds_dma16 with the non-temporal hint, for data read exactly once (it is not kept in the caches
+// for reuse).
+__device__ __forceinline__ void mx_lds_dma16_nt(MX_LDS void* lds_dst, const void* base, uint32_t voff) {
+  const uint32_t m = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)lds_dst);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt" ::"s"(m), "v"(voff), "s"(mx_uniform_ptr((void*)base))
                : "memory");
 }
 
