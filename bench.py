@@ -13,7 +13,8 @@ peak (5.03 PF/s = 256 CU x 4 SIMD x 2048 FLOP/clk x 2.4 GHz).
 cpu_baseline: the CPU oracle, as it is, on a bounded sample of the same workload (batch element 0,
 6 of the 16 heads, N = 4096, forward + backward) on this host's cores.
 
-Before the headline line (which stays last), one JSON line per further workload, each with its own
+The headline step is timed first, on a GPU that has run nothing else in the process; then one JSON
+line per further workload (the headline line is printed last), each with its own
 roofline entry and oracle sample (--headline-only skips them): causal B=4 H=16 N=8192 with 0.5% x64
 outliers (fwd + bwd, FP16 dQ at sigma 2^-4 and FP32 dQ); the jagged batch of 32 sequences with lengths
 uniform in [128, 4096] beside a uniform batch of the same total tokens; the forward-only LLM shape
@@ -708,10 +709,6 @@ def main():
         bench_module(args, torch, mx)
         bench_module_latency(args, torch, mx)
         return
-    if not args.headline_only:
-        bench_workloads(args, torch, mx)
-        bench_module(args, torch, mx)
-        bench_module_latency(args, torch, mx)
     host, dev, cu, cu_d = make_inputs(torch, synth)
     T, C = B * N, H * D
     c = float(np.float32(1 / math.sqrt(D)))
@@ -860,6 +857,12 @@ def main():
         "quant_gbps": round(quant_bytes / med["quant"] / 1e9, 1),
         "roofline": roof,
     }
+    # the headline step is measured first, on a GPU that has run nothing else; the per-workload lines
+    # follow, and the headline line is printed last
+    if not args.headline_only:
+        bench_workloads(args, torch, mx)
+        bench_module(args, torch, mx)
+        bench_module_latency(args, torch, mx)
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(host, cu)
