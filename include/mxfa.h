@@ -64,11 +64,19 @@ typedef enum {
                               [AE-TMEM: dQ reduction in FP16 with static scaling; BR item 6] */
 } mxfa_dq_mode;
 
-/* One MX operand: payload [T, C] (row stride C bytes) and its scale tensor in `mode`'s layout. */
+/* Element format of an MX payload. E4M3 (MXFP8) everywhere; E2M1 (MXFP4: two elements per byte,
+ * element 2i in the low nibble of byte i, magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6) only for the
+ * forward's q and k, in ROW32 blocks [brifing.si "Future directions": MXFP6 and MXFP4 as the next
+ * precisions; TC paragraph 1: the block-scaled matrix units run MXFP8, MXFP6 and MXFP4]. */
+typedef enum { MXFA_E4M3 = 0, MXFA_E2M1 = 1 } mxfa_elem;
+
+/* One MX operand: payload [T, C] (row stride C bytes; C/2 bytes for E2M1) and its scale tensor in
+ * `mode`'s layout. A zero-initialised struct has elem = MXFA_E4M3. */
 typedef struct {
   const uint8_t* data;
   const uint8_t* scale;
   mxfa_block mode;
+  mxfa_elem elem;
 } mxfa_mx;
 
 /* Attention problem shared by the forward and the backward.
@@ -76,6 +84,9 @@ typedef struct {
  * Allowed modes (scales along the MMA contraction dimension [TC paragraph 3]):
  *   q, k : ROW32 (along D) or SQ32 (square; one payload serves both GEMM directions [AE-TMEM])
  *   v    : COL32 (along the keys, for O = P V) or SQ32.
+ * Element formats: E4M3 for all three, or (forward entry points only) q and k both E2M1 in ROW32
+ * with v E4M3: S = Q K^T then runs on the FP4 form of the scaled MMA; the backward entry points
+ * return MXFA_ERR_UNSUPPORTED for E2M1 operands.
  * Causal masking is top-left aligned (key j visible to query i iff j <= i, positions counted
  * from each sequence start). head_dim must be 128. */
 typedef struct {
@@ -108,6 +119,18 @@ typedef struct {
 mxfa_status mxfa_quantize(const uint16_t* x, int64_t ld_x, int64_t T, int C, const int32_t* cu_seqlens, int nseq,
                           int max_seqlen, mxfa_block mode, uint8_t* data_out, uint8_t* scale_out,
                           uint8_t* scale_t_out, void* stream);
+
+/* MXFP4 quantization of a bf16 matrix in ROW32 blocks (1 x 32 along the columns), by the OCP MX rule
+ * for E2M1 [brifing.si "Future directions"; the rule of mxfa_quantize with E2M1's largest exponent]:
+ * scale code e = clamp(exponent_field(amax) - 2, 0, 254), 255 if the block holds NaN or Inf; element
+ * = the E2M1 magnitude nearest to |x| * 2^(127-e) (ties to the even code, saturating at 6) with x's
+ * sign bit (NaN blocks: payload 0).
+ *   x          : bf16 bits [T, ld_x] (first C columns used); C a multiple of 32
+ *   data_out   : [T, C/2] payload, element 2i in the low nibble of byte i
+ *   scale_out  : [T][C/32] (the ROW32 layout; scatter it with mxfa_varlen_scale_scatter as for
+ *                E4M3 payloads). x, data_out and scale_out 16-byte aligned. */
+mxfa_status mxfa_quantize_e2m1(const uint16_t* x, int64_t ld_x, int64_t T, int C, uint8_t* data_out,
+                               uint8_t* scale_out, void* stream);
 
 /* Jagged zero-gather scale path [AE-TMEM: split addressing; BR item 5: lightweight scatter that
  * moves scale factors without changing values]. Copies compact scales (as written by

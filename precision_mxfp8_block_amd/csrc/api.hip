@@ -39,6 +39,9 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 bool valid_mode(int m) { return m == MXFA_ROW32 || m == MXFA_COL32 || m == MXFA_SQ32; }
 
+// Operands of every entry point but the forward's Q and K must be E4M3.
+bool e4m3(const mxfa_mx& m) { return m.elem == MXFA_E4M3; }
+
 bool is_pow2(float x) {
   if (!(x > 0.0f) || !std::isfinite(x)) return false;
   int e;
@@ -76,6 +79,13 @@ mxfa_status check_attn(const mxfa_attn_args* a, const char* fn) {
     if (!aligned(ops[i]->data, 16) || !aligned(ops[i]->scale, 16))
       return fail(MXFA_ERR_INVALID, "%s: %s data/scale not 16-byte aligned", fn, names[i]);
   }
+  for (int i = 0; i < 3; ++i)
+    if (ops[i]->elem != MXFA_E4M3 && ops[i]->elem != MXFA_E2M1)
+      return fail(MXFA_ERR_INVALID, "%s: %s.elem=%d is not an element format", fn, names[i], (int)ops[i]->elem);
+  if (a->q.elem != a->k.elem) return fail(MXFA_ERR_INVALID, "%s: q and k must share one element format", fn);
+  if (!e4m3(a->v)) return fail(MXFA_ERR_UNSUPPORTED, "%s: v must be E4M3 (MXFP4 is for q and k only)", fn);
+  if (a->q.elem == MXFA_E2M1 && (a->q.mode != MXFA_ROW32 || a->k.mode != MXFA_ROW32))
+    return fail(MXFA_ERR_UNSUPPORTED, "%s: MXFP4 q and k must be ROW32", fn);
   if (a->q.mode != MXFA_ROW32 && a->q.mode != MXFA_SQ32)
     return fail(MXFA_ERR_INVALID, "%s: q.mode must be ROW32 or SQ32", fn);
   if (a->k.mode != MXFA_ROW32 && a->k.mode != MXFA_SQ32)
@@ -117,9 +127,9 @@ hipError_t scratch_address(void** out) {
 
 mxfa::AttnProblem to_problem(const mxfa_attn_args* a) {
   mxfa::AttnProblem p;
-  p.q = {a->q.data, a->q.scale, (int)a->q.mode};
-  p.k = {a->k.data, a->k.scale, (int)a->k.mode};
-  p.v = {a->v.data, a->v.scale, (int)a->v.mode};
+  p.q = {a->q.data, a->q.scale, (int)a->q.mode, (int)a->q.elem};
+  p.k = {a->k.data, a->k.scale, (int)a->k.mode, (int)a->k.elem};
+  p.v = {a->v.data, a->v.scale, (int)a->v.mode, (int)a->v.elem};
   p.cu_q = a->cu_seqlens_q;
   p.cu_k = a->cu_seqlens_k;
   p.nseq = a->nseq;
@@ -141,6 +151,8 @@ mxfa_status check_bwd(const mxfa_attn_args* a, mxfa_mx v_d, mxfa_mx dout, const 
                       const mxfa_grad_mx* mx_out, bool library_workspace, const char* fn) {
   mxfa_status st = check_attn(a, fn);
   if (st != MXFA_OK) return st;
+  if (!e4m3(a->q) || !e4m3(v_d) || !e4m3(dout))
+    return fail(MXFA_ERR_UNSUPPORTED, "%s: the backward takes E4M3 operands only", fn);
   if (a->q.mode != MXFA_SQ32 || a->k.mode != MXFA_SQ32)
     return fail(MXFA_ERR_INVALID, "%s: q and k must be SQ32 (square blocks serve both GEMM directions)", fn);
   if (v_d.mode != MXFA_ROW32 && v_d.mode != MXFA_SQ32)
@@ -243,6 +255,19 @@ mxfa_status mxfa_quantize(const uint16_t* x, int64_t ld_x, int64_t T, int C, con
   return hip_status(mxfa::launch_quantize(x, ld_x, T, C, cu_seqlens, nseq, max_seqlen, (int)mode, data_out, scale_out,
                                           scale_t_out, (hipStream_t)stream),
                     fn);
+}
+
+mxfa_status mxfa_quantize_e2m1(const uint16_t* x, int64_t ld_x, int64_t T, int C, uint8_t* data_out,
+                               uint8_t* scale_out, void* stream) {
+  const char* fn = "mxfa_quantize_e2m1";
+  if (T < 0) return fail(MXFA_ERR_INVALID, "%s: T=%lld < 0", fn, (long long)T);
+  if (C <= 0 || C % 32) return fail(MXFA_ERR_INVALID, "%s: C=%d must be a positive multiple of 32", fn, C);
+  if (ld_x < C || ld_x % 8) return fail(MXFA_ERR_INVALID, "%s: ld_x=%lld must be >= C and a multiple of 8", fn, (long long)ld_x);
+  if (!x || !data_out || !scale_out) return fail(MXFA_ERR_INVALID, "%s: NULL x/data_out/scale_out", fn);
+  if (!aligned(x, 16) || !aligned(data_out, 16) || !aligned(scale_out, 16))
+    return fail(MXFA_ERR_INVALID, "%s: x/data_out/scale_out not 16-byte aligned", fn);
+  if (T * (C / 16) / 256 >= ((int64_t)1 << 31)) return fail(MXFA_ERR_INVALID, "%s: tensor too large for one launch", fn);
+  return hip_status(mxfa::launch_quantize_e2m1(x, ld_x, T, C, data_out, scale_out, (hipStream_t)stream), fn);
 }
 
 mxfa_status mxfa_varlen_scale_scatter(const uint8_t* compact, const int32_t* cu_seqlens, int nseq, int max_seqlen,
@@ -363,6 +388,7 @@ mxfa_status mxfa_linear_quantize(mxfa_mx x, mxfa_mx w, int64_t T, int C_in, int 
   if (C_in <= 0 || C_in % 128 || C_in > 65536)
     return fail(MXFA_ERR_INVALID, "%s: C_in=%d must be a multiple of 128 in [128, 65536]", fn, C_in);
   if (C_out <= 0 || C_out % 128) return fail(MXFA_ERR_INVALID, "%s: C_out=%d must be a positive multiple of 128", fn, C_out);
+  if (!e4m3(x) || !e4m3(w)) return fail(MXFA_ERR_UNSUPPORTED, "%s: x and w must be E4M3", fn);
   if (x.mode != MXFA_SQ32 && x.mode != MXFA_ROW32) return fail(MXFA_ERR_INVALID, "%s: x.mode must be SQ32 or ROW32", fn);
   if (w.mode != MXFA_ROW32) return fail(MXFA_ERR_INVALID, "%s: w.mode must be ROW32 (scales along C_in)", fn);
   if (!x.data || !x.scale || !w.data || !w.scale || !data_out || !scale_out)
@@ -388,6 +414,7 @@ mxfa_status mxfa_linear_bwd_data(mxfa_mx dy, mxfa_mx wt, int64_t T, int C_out, i
   if (C_out <= 0 || C_out % 128 || C_out > 65536)
     return fail(MXFA_ERR_INVALID, "%s: C_out=%d must be a multiple of 128 in [128, 65536]", fn, C_out);
   if (C_in <= 0 || C_in % 128) return fail(MXFA_ERR_INVALID, "%s: C_in=%d must be a positive multiple of 128", fn, C_in);
+  if (!e4m3(dy) || !e4m3(wt)) return fail(MXFA_ERR_UNSUPPORTED, "%s: dy and wt must be E4M3", fn);
   if (dy.mode != MXFA_SQ32 && dy.mode != MXFA_ROW32) return fail(MXFA_ERR_INVALID, "%s: dy.mode must be SQ32 or ROW32", fn);
   if (wt.mode != MXFA_ROW32) return fail(MXFA_ERR_INVALID, "%s: wt.mode must be ROW32 (scales along C_out)", fn);
   if (!dy.data || !dy.scale || !wt.data || !wt.scale || !dx) return fail(MXFA_ERR_INVALID, "%s: NULL argument", fn);

@@ -143,7 +143,10 @@ __device__ __forceinline__ uint32_t undef_word() {
   return u;
 }
 
-template <bool VCOL32, bool PDYN>
+// QK4: Q and K in MXFP4 (E2M1, two elements per byte, ROW32 scales), S computed by the scaled MFMA
+// in its FP4 format (twice the FP8 rate). The K tile then takes 64 bytes per key: LDS row R of the
+// K stage holds keys 2R (logical chunks 0-3) and 2R + 1 (chunks 4-7), swizzled like the FP8 tiles.
+template <bool VCOL32, bool PDYN, bool QK4>
 __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[kLdsBytes];
   MX_LDS uint8_t* const lds = (MX_LDS uint8_t*)lds_raw;
@@ -181,22 +184,57 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
     tcol[c] = 16 * ((pchunk & 7) ^ swz(pchunk >> 3));
     toff[c] = (uint32_t)(trow[c] * C + tcol[c]);
   }
-  const uint8_t* kbase = (const uint8_t*)mx_uniform_ptr((void*)(p.k + k_start * (int64_t)C + h * kD));
+  // row stride of Q and K in bytes, and the K tile pieces of QK4 (two 1 KB pieces per wave: piece c
+  // of wave w covers LDS row R = 8 (2 w + c) + l / 8, physical chunk l % 8, i.e. key 2 R + lc / 4,
+  // bytes 16 (lc % 4) of its 64, lc = (l % 8) ^ swz(R) the logical chunk)
+  constexpr int kQKBytes = QK4 ? kD / 2 : kD;
+  const int ldqk = QK4 ? C / 2 : C;
+  int k4row[2];
+  uint32_t k4col[2];
+  if constexpr (QK4) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int pchunk = (wave * 2 + c) * 64 + lane;
+      const int R = pchunk >> 3, lc = (pchunk & 7) ^ swz(pchunk >> 3);
+      k4row[c] = 2 * R + (lc >> 2);
+      k4col[c] = (uint32_t)(16 * (lc & 3));
+    }
+  }
+  const uint8_t* kbase = (const uint8_t*)mx_uniform_ptr((void*)(p.k + k_start * (int64_t)ldqk + h * kQKBytes));
   const uint8_t* vbase = (const uint8_t*)mx_uniform_ptr((void*)(p.v + k_start * (int64_t)C + h * kD));
   // LDS byte address of this wave's pieces of a tile, and of its part of the scale areas
   const uint32_t lds_addr = (uint32_t)(uintptr_t)lds;
   const uint32_t wave_lds = lds_addr + (uint32_t)wave_s * 4096u;
+  const uint32_t wave_lds_k4 = lds_addr + (uint32_t)wave_s * 2048u;  // QK4 K tile pieces
+  // K tile of key rows kv0.. into K stage TILE: FP8 tiles as V's, FP4 tiles in 8 KB
+  auto issue_k_load = [&](auto tilec, int kv0) {
+    constexpr int TILE = decltype(tilec)::value;
+    const uint8_t* base = kbase + (int64_t)kv0 * ldqk;
+    const int valid = Lk - kv0;
+    if constexpr (QK4) {
+      uint32_t off[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) off[c] = (uint32_t)(min(k4row[c], valid - 1) * ldqk) + k4col[c];
+      dma16_at<TILE + 0>(wave_lds_k4, base, off[0]);
+      dma16_at<TILE + 1024>(wave_lds_k4, base, off[1]);
+    } else {
+      issue_tile_load<TILE>(wave_lds, base, valid, C, trow, tcol, toff);
+    }
+  };
 
   // ---- Q tile rows of this wave, held as the B operand of S^T = K Q^T ----
   const int qrow = qt * kTile + wave * 32 + r;  // position in the sequence
   mx_v8i qa[2];
   {
     const bool valid = qrow < Lq;
-    const uint8_t* src = p.q + (q_start + qrow) * (int64_t)C + h * kD;
+    const uint8_t* src = p.q + (q_start + qrow) * (int64_t)ldqk + h * kQKBytes;
 #pragma unroll
     for (int ds = 0; ds < 2; ++ds) {
       uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
-      if (valid) {
+      if constexpr (QK4) {
+        // FP4: the lane's 32 elements of d-block 2 ds + hh, 16 bytes (the upper operand half unused)
+        if (valid) lo = *reinterpret_cast<const uint4*>(src + 32 * ds + 16 * hh);
+      } else if (valid) {
         lo = *reinterpret_cast<const uint4*>(src + 64 * ds + 16 * hh);
         hi = *reinterpret_cast<const uint4*>(src + 64 * ds + 32 + 16 * hh);
       }
@@ -232,7 +270,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
   // stage 1. In the loop, the loads issued in the middle of step t bring K of tile t + 2 and V of
   // tile t + 1 (with their scales): K one step before its scores are computed, V one and a half.
   if (n_ktiles > 0) {
-    issue_tile_load<lds_k_off(0)>(wave_lds, kbase, Lk, C, trow, tcol, toff);
+    issue_k_load(Stage<lds_k_off(0)>{}, 0);
     issue_tile_load<lds_v_off(0)>(wave_lds, vbase, Lk, C, trow, tcol, toff);
     if (wave_s < 2)
       issue_kscale_load(0, Stage<0>{});
@@ -240,7 +278,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
       issue_vscale_load(0, Stage<0>{});
   }
   if (n_ktiles > 1) {
-    issue_tile_load<lds_k_off(1)>(wave_lds, kbase + (int64_t)kTile * C, Lk - kTile, C, trow, tcol, toff);
+    issue_k_load(Stage<lds_k_off(1)>{}, kTile);
     if (wave_s < 2) issue_kscale_load(kTile, Stage<1>{});
   }
 
@@ -257,8 +295,17 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
   //  * V^T reads (see the lane map in mx_device.h): row tr_row (+ 64 ks + 32 (cc >> 1) + 16 (cc & 1),
   //    which leave the swizzle unchanged), column 32 db + tr_col;
   //  * scales: K scale word 32 kb + r; V scale byte 128 (2 ks + hh) + (COL32: 32 db + r, SQ32: db).
+  //  * QK4 K rows: key 32 kb + r is in LDS row 16 kb + r / 2 (its swizzle does not depend on kb),
+  //    logical chunk 4 (r % 2) + 2 ds + hh: the 32 elements of d-block 2 ds + hh;
   uint32_t koffs[2][2];
-  {
+  if constexpr (QK4) {
+    const int R = r >> 1, sw = swz(R);
+#pragma unroll
+    for (int ds = 0; ds < 2; ++ds) {
+      koffs[ds][0] = (uint32_t)(R * kD + 16 * ((4 * (r & 1) + 2 * ds + hh) ^ sw));
+      koffs[ds][1] = koffs[ds][0];
+    }
+  } else {
     const int sw = swz(r);
 #pragma unroll
     for (int ds = 0; ds < 2; ++ds) {
@@ -293,15 +340,18 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
       sacc[kb] = mx_v16f{};
 #pragma unroll
       for (int ds = 0; ds < 2; ++ds) {
-        const MX_LDS uint8_t* t = lds + lds_k_off(sk) + 32 * kb * kD;
+        // operand format: 0 = E4M3, 4 = E2M1 (the FP4 operand fills the low four registers)
+        constexpr int fmt = QK4 ? 4 : 0;
+        const MX_LDS uint8_t* t = lds + lds_k_off(sk) + 32 * kb * kQKBytes;
         const mx_v4i lo = *(const MX_LDS mx_v4i*)(t + koffs[ds][0]);
-        const mx_v4i hi = *(const MX_LDS mx_v4i*)(t + koffs[ds][1]);
+        mx_v4i hi = mx_v4i{0, 0, 0, 0};
+        if constexpr (!QK4) hi = *(const MX_LDS mx_v4i*)(t + koffs[ds][1]);
         mx_v8i ka{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
         if (ds == 0)
-          sacc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qa[0], sacc[kb], 0, 0, 0, (int)kscb, 0,
+          sacc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qa[0], sacc[kb], fmt, fmt, 0, (int)kscb, 0,
                                                                      (int)qsc);
         else
-          sacc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qa[1], sacc[kb], 0, 0, 2, (int)kscb, 2,
+          sacc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qa[1], sacc[kb], fmt, fmt, 2, (int)kscb, 2,
                                                                      (int)qsc);
       }
     }
@@ -451,8 +501,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
     wait_vm();
     __syncthreads();
     if (kt + 2 < n_ktiles) {
-      issue_tile_load<lds_k_off(st)>(wave_lds, kbase + (int64_t)(kv0 + 2 * kTile) * C, Lk - kv0 - 2 * kTile, C, trow,
-                                     tcol, toff);
+      issue_k_load(Stage<lds_k_off(st)>{}, kv0 + 2 * kTile);
       if (wave_s < 2) issue_kscale_load(kv0 + 2 * kTile, Stage<st>{});
     }
     const bool more = kt + 1 < n_ktiles;
@@ -591,16 +640,28 @@ hipError_t launch_attn_fwd(const AttnProblem& a, int p_dynamic, uint16_t* o, uin
   p.o = o; p.o_mx = o_mx; p.o_mx_scale = o_mx_scale; p.lse = lse; p.Tq = a.total_q;
   if (p.total_items == 0) return hipSuccess;
   const dim3 grid((unsigned)p.total_items), block(256);
-  if (p.v_col_shift == 0) {
+  if (a.q.elem == 1) {  // Q and K in MXFP4 (checked by the caller: both ROW32, V COL32 or SQ32 in E4M3)
+    if (p.v_col_shift == 0) {
+      if (p_dynamic)
+        hipLaunchKernelGGL((attn_fwd_kernel<true, true, true>), grid, block, 0, stream, p);
+      else
+        hipLaunchKernelGGL((attn_fwd_kernel<true, false, true>), grid, block, 0, stream, p);
+    } else {
+      if (p_dynamic)
+        hipLaunchKernelGGL((attn_fwd_kernel<false, true, true>), grid, block, 0, stream, p);
+      else
+        hipLaunchKernelGGL((attn_fwd_kernel<false, false, true>), grid, block, 0, stream, p);
+    }
+  } else if (p.v_col_shift == 0) {
     if (p_dynamic)
-      hipLaunchKernelGGL((attn_fwd_kernel<true, true>), grid, block, 0, stream, p);
+      hipLaunchKernelGGL((attn_fwd_kernel<true, true, false>), grid, block, 0, stream, p);
     else
-      hipLaunchKernelGGL((attn_fwd_kernel<true, false>), grid, block, 0, stream, p);
+      hipLaunchKernelGGL((attn_fwd_kernel<true, false, false>), grid, block, 0, stream, p);
   } else {
     if (p_dynamic)
-      hipLaunchKernelGGL((attn_fwd_kernel<false, true>), grid, block, 0, stream, p);
+      hipLaunchKernelGGL((attn_fwd_kernel<false, true, false>), grid, block, 0, stream, p);
     else
-      hipLaunchKernelGGL((attn_fwd_kernel<false, false>), grid, block, 0, stream, p);
+      hipLaunchKernelGGL((attn_fwd_kernel<false, false, false>), grid, block, 0, stream, p);
   }
   return hipGetLastError();
 }

@@ -53,6 +53,56 @@ __global__ void __launch_bounds__(256) quantize_row32_kernel(const uint16_t* __r
 }
 
 // ---------------------------------------------------------------------------------------------
+// ROW32 in MXFP4: E2M1 elements (OCP MX: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6) with the scale code
+// clamp(exponent_field(amax) - 2, 0, 254), 2 being the exponent of E2M1's largest magnitude; 255 and
+// a zero payload for blocks holding NaN or Inf. Two lanes share a block, 16 bf16 each; a lane writes
+// 8 bytes (element 2i in the low nibble of byte i).
+// ---------------------------------------------------------------------------------------------
+// Nearest E2M1 code of v (already scaled), ties to the even code, saturating at 6, sign kept: the
+// magnitude code counts the midpoints between consecutive magnitudes that |v| passes, a midpoint
+// whose upper neighbour has the even code (0.75, 1.75, 3.5) counting when reached, the others
+// (0.25, 1.25, 2.5, 5) when exceeded.
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  const float a = fabsf(v);
+  const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
+  return c | ((__float_as_uint(v) >> 28) & 8u);
+}
+
+__global__ void __launch_bounds__(256) quantize_row32_e2m1_kernel(const uint16_t* __restrict__ x, int64_t ld_x,
+                                                                  int64_t T, int C, uint8_t* __restrict__ data,
+                                                                  uint8_t* __restrict__ scale) {
+  const int64_t chunks_per_row = C >> 4;
+  const int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (u >= T * chunks_per_row) return;  // pairs of lanes leave together (chunks_per_row is even)
+  const int64_t t = u / chunks_per_row;
+  const int j = (int)(u - t * chunks_per_row);
+  const uint4* src = reinterpret_cast<const uint4*>(x + t * ld_x + (int64_t)j * 16);
+  const uint4 a = src[0], b = src[1];
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  uint32_t amax = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = max(amax, max(w[i] & 0x7fffu, (w[i] >> 16) & 0x7fffu));
+  amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1, 64));
+  const uint32_t e = amax >> 7;  // biased exponent field of the bf16 (= fp32) maximum
+  const uint32_t code = e >= 255u ? 255u : (e > 2u ? e - 2u : 0u);
+  uint2 out = make_uint2(0u, 0u);
+  if (code != 255u) {
+    const float inv = mx_inv_scale(code);
+    uint32_t o[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t lo = e2m1_code(bf16_to_f32(w[i] & 0xffffu) * inv);
+      const uint32_t hi = e2m1_code(bf16_to_f32(w[i] >> 16) * inv);
+      o[i >> 2] |= (lo | (hi << 4)) << (8 * (i & 3));
+    }
+    out = make_uint2(o[0], o[1]);
+  }
+  *reinterpret_cast<uint2*>(data + t * (C >> 1) + (int64_t)j * 8) = out;
+  if ((j & 1) == 0) scale[t * (C >> 5) + (j >> 1)] = (uint8_t)code;
+}
+
+// ---------------------------------------------------------------------------------------------
 // COL32: 32 x 1 blocks along the tokens. A wave covers 32 rows x 128 columns: lane l owns columns
 // 4 (l % 32) .. +3 (8-byte loads) of rows 16 (l / 32) + i, i = 0..15; a column's maximum joins the
 // two half-waves with one lane swap. Every load instruction covers two 256-byte row segments and
@@ -473,6 +523,15 @@ hipError_t launch_quantize(const uint16_t* x, int64_t ld_x, int64_t T, int C, co
     hipLaunchKernelGGL(quantize_sq32_kernel, grid, dim3(256), 0, stream, x, ld_x, C, cu, nseq, data, scale,
                        scale_t);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_e2m1(const uint16_t* x, int64_t ld_x, int64_t T, int C, uint8_t* data, uint8_t* scale,
+                               hipStream_t stream) {
+  const int64_t units = T * (C >> 4);
+  if (units == 0) return hipSuccess;
+  hipLaunchKernelGGL(quantize_row32_e2m1_kernel, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, stream, x, ld_x,
+                     T, C, data, scale);
   return hipGetLastError();
 }
 

@@ -26,7 +26,7 @@ def _declared_functions():
 
 def test_header_declares_the_abi():
     names = _declared_functions()
-    for n in ["mxfa_quantize", "mxfa_fwd", "mxfa_fwd_p_scale", "mxfa_fwd_mx_out", "mxfa_bwd", "mxfa_bwd_mx_out",
+    for n in ["mxfa_quantize", "mxfa_quantize_e2m1", "mxfa_fwd", "mxfa_fwd_p_scale", "mxfa_fwd_mx_out", "mxfa_bwd", "mxfa_bwd_mx_out",
               "mxfa_varlen_scale_scatter",
               "mxfa_rmsnorm_quantize",
               "mxfa_linear_quantize", "mxfa_linear_bwd_data", "mxfa_linear_bwd_weight",
@@ -92,12 +92,42 @@ def _args(**kw):
     (dict(k=(0, P, 2)), INVALID),
     (dict(k=(P + 4, P, 2)), INVALID),
     (dict(scale=float("inf")), INVALID),
+    # element formats: MXFP4 only for q and k together, ROW32, with an E4M3 v
+    (dict(q=(P, P, 0, 1), k=(P, P, 0, 0)), INVALID),      # q and k in different formats
+    (dict(q=(P, P, 2, 1), k=(P, P, 2, 1)), UNSUPPORTED),  # MXFP4 in SQ32
+    (dict(q=(P, P, 0, 1), k=(P, P, 0, 1), v=(P, P, 1, 1)), UNSUPPORTED),  # MXFP4 v
+    (dict(q=(P, P, 0, 3), k=(P, P, 0, 3)), INVALID),      # not an element format
 ])
 def test_fwd_argument_errors(kw, expect):
     a = _args(**kw)
     st = _lib().mxfa_fwd(ctypes.byref(a), P, P, 0)
     assert st == expect, _last()
     assert _last() != ""
+
+
+def test_bwd_rejects_mxfp4_operands():
+    a = _args(q=(P, P, 0, 1), k=(P, P, 0, 1))
+    need = mx.mxfa_bwd_workspace_size(a, 0)
+    st = _lib().mxfa_bwd(ctypes.byref(a), mx._Mx(P, P, 0), mx._Mx(P, P, 2), P, P, P, 0, 1.0, P, need, P, P, P, 0)
+    assert st == UNSUPPORTED and "E4M3" in _last()
+    a = _args()
+    st = _lib().mxfa_bwd(ctypes.byref(a), mx._Mx(P, P, 0, 1), mx._Mx(P, P, 2), P, P, P, 0, 1.0, P, need, P, P, P, 0)
+    assert st == UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(C=48), INVALID),
+    (dict(ld_x=100), INVALID),
+    (dict(ld_x=132), INVALID),
+    (dict(x=0), INVALID),
+    (dict(data=P + 8), INVALID),
+    (dict(T=-1), INVALID),
+])
+def test_quantize_e2m1_argument_errors(kw, expect):
+    a = dict(x=P, ld_x=128, T=256, C=128, data=P, scale=P)
+    a.update(kw)
+    st = _lib().mxfa_quantize_e2m1(a["x"], a["ld_x"], a["T"], a["C"], a["data"], a["scale"], 0)
+    assert st == expect and _last() != ""
 
 
 def test_fwd_null_outputs():
