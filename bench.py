@@ -18,7 +18,8 @@ line per further workload (the headline line is printed last), each with its own
 roofline entry and oracle sample (--headline-only skips them): causal B=4 H=16 N=8192 with 0.5% x64
 outliers (fwd + bwd, FP16 dQ at sigma 2^-4 and FP32 dQ); the jagged batch of 32 sequences with lengths
 uniform in [128, 4096] beside a uniform batch of the same total tokens; the forward-only LLM shape
-(Q/K ROW32, V COL32); the cross-attention module step (producers, scatter, attention fwd + bwd).
+(Q/K ROW32, V COL32) and the same forward with Q and K in MXFP4 (E2M1); the cross-attention module
+step (producers, scatter, attention fwd + bwd).
 """
 import argparse
 import json
@@ -33,6 +34,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_MXFP8 = 5.03e15  # FLOP/s
+PEAK_MXFP4 = 10.1e15  # FLOP/s, dense FP4 scaled MFMA
+# forward with Q/K in MXFP4: S = Q K^T (half the FLOPs) at the FP4 rate, O = P V at the FP8 rate
+PEAK_FWD_QK4 = 1.0 / (0.5 / PEAK_MXFP4 + 0.5 / PEAK_MXFP8)
 PEAK_HBM = 8.0e12     # B/s
 synth_mod = None  # the synth module, set in main()
 B, H, N, D = 4, 16, 4096, 128
@@ -54,6 +58,8 @@ def parse():
     ap.add_argument("--producers", action="store_true",
                     help="time the fused RMSNorm+quantize producer at the module workload's shapes and the jagged "
                          "scale scatter instead of the attention step (one JSON line of its own)")
+    ap.add_argument("--forward-only", action="store_true",
+                    help="only the forward-only LLM shape, with Q/K in MXFP8 and in MXFP4 (two JSON lines)")
     ap.add_argument("--module", action="store_true",
                     help="time only the cross-attention module training step (the config-5 shape, then module "
                          "latency at 4k, 8k and 16k key/value tokens), one JSON line each")
@@ -290,7 +296,7 @@ def host_cpu():
     return model, os.cpu_count() or 1, max(1, min(16, os.cpu_count() or 1))
 
 
-def oracle_slices(slices, backward, c, causal, qk_mode=2):
+def oracle_slices(slices, backward, c, causal, qk_mode=2, qk_e2m1=False):
     """The oracle, as it is, on (sequence, head) slices given as bf16 arrays {q, k, v, do}: each slice one
     sequence of a one-head batch, so the slices run on parallel threads. Returns wall seconds."""
     import oracle
@@ -299,6 +305,12 @@ def oracle_slices(slices, backward, c, causal, qk_mode=2):
     cat = {n: np.ascontiguousarray(np.concatenate([x[n] for x in slices])) for n in ("q", "k", "v", "do")}
     nthreads = max(1, min(16, os.cpu_count() or 1))
     t0 = time.perf_counter()
+    if qk_e2m1:  # forward with Q and K in MXFP4
+        from oracle import mxfp4
+        q4, k4 = mxfp4.quantize_row32(cat["q"]), mxfp4.quantize_row32(cat["k"])
+        v = oracle.quantize(cat["v"], ck, oracle.COL32)
+        mxfp4.attn_fwd_qk_fp4(q4[0], q4[1], k4[0], k4[1], v[0], v[1], cq, ck, 1, D, c, causal)
+        return time.perf_counter() - t0, min(nthreads, len(slices))
     q = oracle.quantize(cat["q"], cq, qk_mode)
     k = oracle.quantize(cat["k"], ck, qk_mode)
     v = oracle.quantize(cat["v"], ck, oracle.COL32)
@@ -322,7 +334,7 @@ def attn_flops(lens_q, lens_k, H, causal):
 
 def bench_attention_workload(args, torch, mx, label, workload, lens_q, lens_k, H, causal, outlier_p, seed,
                              fwd_only=False, qk_mode=None, dq_modes=((1, 1.0), (0, 1.0)), cpu_slices=4,
-                             cpu_backward=False, extra_config=None):
+                             cpu_backward=False, extra_config=None, qk_e2m1=False):
     """One attention workload at its full size: quantize, forward and backward (each dQ mode) timed over
     back-to-back calls with HIP events on the launch stream. Returns the JSON dict (not printed)."""
     stream = torch.cuda.current_stream()
@@ -354,8 +366,22 @@ def bench_attention_workload(args, torch, mx, label, workload, lens_q, lens_k, H
             if jag:
                 mx.mxfa_varlen_scale_scatter(sc, cu_d, len(lens), max(lens), C, mode, pad, pad.shape[0], stream)
         return mx.MxOperand(d, pad, mode), run
-    qop, rq = operand("q", qk_mode, Tq, nbq, Pq, cq_d, lens_q, jag_q)
-    kop, rk = operand("k", qk_mode, Tk, nbk, Pk, ck_d, lens_k, jag_k)
+    def operand_e2m1(name, T, P, cu_d, lens, jag):
+        d, sc = u8(T, C // 2), u8(T, C // 32)
+        pad = u8(P, C // 32) if jag else sc
+
+        def run():
+            mx.mxfa_quantize_e2m1(dev[name], C, T, C, d, sc, stream)
+            if jag:
+                mx.mxfa_varlen_scale_scatter(sc, cu_d, len(lens), max(lens), C, mx.ROW32, pad, pad.shape[0], stream)
+        return mx.MxOperand(d, pad, mx.ROW32, mx.E2M1), run
+    if qk_e2m1:
+        assert fwd_only and qk_mode == mx.ROW32
+        qop, rq = operand_e2m1("q", Tq, Pq, cq_d, lens_q, jag_q)
+        kop, rk = operand_e2m1("k", Tk, Pk, ck_d, lens_k, jag_k)
+    else:
+        qop, rq = operand("q", qk_mode, Tq, nbq, Pq, cq_d, lens_q, jag_q)
+        kop, rk = operand("k", qk_mode, Tk, nbk, Pk, ck_d, lens_k, jag_k)
     vop, rv = operand("v", mx.COL32, Tk, nbk, Pk, ck_d, lens_k, jag_k)
     runs = [rq, rk, rv]
     if not fwd_only:
@@ -397,14 +423,17 @@ def bench_attention_workload(args, torch, mx, label, workload, lens_q, lens_k, H
     print(f"# {label}: " + ", ".join(f"{k}={v}" for k, v in res.items()), file=sys.stderr, flush=True)
     cfg = {"workload": workload, "H": H, "D": D, "causal": bool(causal), "nseq": len(lens_q), "tokens_q": Tq,
            "tokens_k": Tk, "max_len": max(lens_k), "outlier_p": outlier_p, **(extra_config or {}), **res}
+    peak = PEAK_FWD_QK4 if qk_e2m1 else PEAK_MXFP8
     out = {
-        "metric": "MXFP8 attention fwd/bwd PF/s and % of MI355X dense MXFP8 MFMA peak",
+        "metric": ("MXFP4-QK attention forward PF/s and % of the MI355X dense MFMA peak of its mix (S in FP4, "
+                   "P V in FP8)") if qk_e2m1 else "MXFP8 attention fwd/bwd PF/s and % of MI355X dense MXFP8 MFMA peak",
         "value": round(value, 4), "unit": "PF/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round((res.get("step_us", res["fwd_us"])) / 1e3, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "mxfp8_e4m3 (fp32 accumulate)", "data": "synthetic",
-        "config": cfg,
-        "roofline": {"bound": "mfma", "achieved": round(dom_f / dom_t / 1e12, 2), "peak": PEAK_MXFP8 / 1e12,
-                     "unit": "TFLOP/s", "frac": round(dom_f / dom_t / PEAK_MXFP8, 4), "traffic": None,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "mxfp4_e2m1 Q/K, mxfp8_e4m3 V/P (fp32 accumulate)" if qk_e2m1 else "mxfp8_e4m3 (fp32 accumulate)",
+        "data": "synthetic", "config": cfg,
+        "roofline": {"bound": "mfma", "achieved": round(dom_f / dom_t / 1e12, 2), "peak": round(peak / 1e12, 1),
+                     "unit": "TFLOP/s", "frac": round(dom_f / dom_t / peak, 4), "traffic": None,
                      "kernel": dom_name, "launch_us": round(dom_t * 1e6, 2)},
     }
     if not args.no_cpu_baseline and cpu_slices:
@@ -412,7 +441,7 @@ def bench_attention_workload(args, torch, mx, label, workload, lens_q, lens_k, H
         sl = [{n: np.ascontiguousarray(host[n][int((cu_q if n in ("q", "do") else cu_k)[s]):
                                                int((cu_q if n in ("q", "do") else cu_k)[s + 1]), h * D:(h + 1) * D])
                for n in ("q", "k", "v", "do")} for s, h in picks]
-        dt, cores = oracle_slices(sl, cpu_backward, c, causal, qk_mode)
+        dt, cores = oracle_slices(sl, cpu_backward, c, causal, qk_mode, qk_e2m1)
         f = sum(attn_flops([lens_q[s]], [lens_k[s]], 1, causal) for s, _ in picks) * (3.5 if cpu_backward else 1.0)
         model, nproc, _ = host_cpu()
         out["cpu_baseline"] = {"value": round(f / dt / 1e15, 8), "unit": "PF/s", "cores": cores, "kind": "oracle",
@@ -443,11 +472,24 @@ def bench_workloads(args, torch, mx):
     jag["config"]["uniform_same_batch"] = {k: uni["config"][k] for k in uni["config"] if k.endswith(("us", "pflops"))}
     jag["config"]["uniform_same_batch"]["len"] = L
     lines.append(jag)
-    lines.append(bench_attention_workload(
-        args, torch, mx, "forward-only", "LLM forward B=4 H=16 N=4096, Q/K ROW32, V COL32",
-        [N] * B, [N] * B, H, False, 0.0, SEED, fwd_only=True, cpu_slices=4))
+    lines += bench_forward_only(args, torch, mx)
     for line in lines:
         print(json.dumps(line), flush=True)
+
+
+def bench_forward_only(args, torch, mx):
+    """The forward-only LLM shape with Q/K in MXFP8 and, on the same inputs, in MXFP4."""
+    lines = []
+    fo = bench_attention_workload(
+        args, torch, mx, "forward-only", "LLM forward B=4 H=16 N=4096, Q/K ROW32, V COL32",
+        [N] * B, [N] * B, H, False, 0.0, SEED, fwd_only=True, cpu_slices=4)
+    lines.append(fo)
+    f4 = bench_attention_workload(
+        args, torch, mx, "forward-only MXFP4 Q/K", "LLM forward B=4 H=16 N=4096, Q/K MXFP4 (E2M1) ROW32, V E4M3 COL32",
+        [N] * B, [N] * B, H, False, 0.0, SEED, fwd_only=True, cpu_slices=2, qk_e2m1=True)
+    f4["config"]["mxfp8_qk_same_shape"] = {k: fo["config"][k] for k in ("fwd_us", "fwd_pflops", "quant_us")}
+    lines.append(f4)
+    return lines
 
 
 def module_step_setup(torch, mx, lens_k, seed, NQ=256, Hm=8, CM=None):
@@ -704,6 +746,10 @@ def main():
         return
     if args.producers:
         bench_producers(args, torch, mx, synth)
+        return
+    if args.forward_only:
+        for line in bench_forward_only(args, torch, mx):
+            print(json.dumps(line), flush=True)
         return
     if args.module:
         bench_module(args, torch, mx)
