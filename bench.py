@@ -18,7 +18,7 @@ line per further workload (the headline line is printed last), each with its own
 roofline entry and oracle sample (--headline-only skips them): causal B=4 H=16 N=8192 with 0.5% x64
 outliers (fwd + bwd, FP16 dQ at sigma 2^-4 and FP32 dQ); the jagged batch of 32 sequences with lengths
 uniform in [128, 4096] beside a uniform batch of the same total tokens; the forward-only LLM shape
-(Q/K ROW32, V COL32) and the same forward with Q and K in MXFP4 (E2M1); the cross-attention module
+(Q/K ROW32, V COL32) and the same forward with Q and K in MXFP4 (E2M1) and MXFP6 (E2M3); the cross-attention module
 step (producers, scatter, attention fwd + bwd).
 """
 import argparse
@@ -34,8 +34,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_MXFP8 = 5.03e15  # FLOP/s
-PEAK_MXFP4 = 10.1e15  # FLOP/s, dense FP4 scaled MFMA
-# forward with Q/K in MXFP4: S = Q K^T (half the FLOPs) at the FP4 rate, O = P V at the FP8 rate
+PEAK_MXFP4 = 10.1e15  # FLOP/s, dense FP4 and FP6 scaled MFMA
+# forward with Q/K in MXFP4 or MXFP6: S = Q K^T (half the FLOPs) at the FP4/FP6 rate, O = P V at the FP8 rate
 PEAK_FWD_QK4 = 1.0 / (0.5 / PEAK_MXFP4 + 0.5 / PEAK_MXFP8)
 PEAK_HBM = 8.0e12     # B/s
 synth_mod = None  # the synth module, set in main()
@@ -59,7 +59,7 @@ def parse():
                     help="time the fused RMSNorm+quantize producer at the module workload's shapes and the jagged "
                          "scale scatter instead of the attention step (one JSON line of its own)")
     ap.add_argument("--forward-only", action="store_true",
-                    help="only the forward-only LLM shape, with Q/K in MXFP8 and in MXFP4 (two JSON lines)")
+                    help="only the forward-only LLM shape, with Q/K in MXFP8, MXFP4 and MXFP6 (three JSON lines)")
     ap.add_argument("--module", action="store_true",
                     help="time only the cross-attention module training step (the config-5 shape, then module "
                          "latency at 4k, 8k and 16k key/value tokens), one JSON line each")
@@ -296,7 +296,7 @@ def host_cpu():
     return model, os.cpu_count() or 1, max(1, min(16, os.cpu_count() or 1))
 
 
-def oracle_slices(slices, backward, c, causal, qk_mode=2, qk_e2m1=False):
+def oracle_slices(slices, backward, c, causal, qk_mode=2, qk_small=None):
     """The oracle, as it is, on (sequence, head) slices given as bf16 arrays {q, k, v, do}: each slice one
     sequence of a one-head batch, so the slices run on parallel threads. Returns wall seconds."""
     import oracle
@@ -305,11 +305,12 @@ def oracle_slices(slices, backward, c, causal, qk_mode=2, qk_e2m1=False):
     cat = {n: np.ascontiguousarray(np.concatenate([x[n] for x in slices])) for n in ("q", "k", "v", "do")}
     nthreads = max(1, min(16, os.cpu_count() or 1))
     t0 = time.perf_counter()
-    if qk_e2m1:  # forward with Q and K in MXFP4
-        from oracle import mxfp4
-        q4, k4 = mxfp4.quantize_row32(cat["q"]), mxfp4.quantize_row32(cat["k"])
+    if qk_small:  # forward with Q and K in MXFP4 ("e2m1") or MXFP6 ("e2m3")
+        from oracle import mxfp4, mxfp6
+        mod, fwd = (mxfp4, mxfp4.attn_fwd_qk_fp4) if qk_small == "e2m1" else (mxfp6, mxfp6.attn_fwd_qk_fp6)
+        q4, k4 = mod.quantize_row32(cat["q"]), mod.quantize_row32(cat["k"])
         v = oracle.quantize(cat["v"], ck, oracle.COL32)
-        mxfp4.attn_fwd_qk_fp4(q4[0], q4[1], k4[0], k4[1], v[0], v[1], cq, ck, 1, D, c, causal)
+        fwd(q4[0], q4[1], k4[0], k4[1], v[0], v[1], cq, ck, 1, D, c, causal)
         return time.perf_counter() - t0, min(nthreads, len(slices))
     q = oracle.quantize(cat["q"], cq, qk_mode)
     k = oracle.quantize(cat["k"], ck, qk_mode)
@@ -334,7 +335,7 @@ def attn_flops(lens_q, lens_k, H, causal):
 
 def bench_attention_workload(args, torch, mx, label, workload, lens_q, lens_k, H, causal, outlier_p, seed,
                              fwd_only=False, qk_mode=None, dq_modes=((1, 1.0), (0, 1.0)), cpu_slices=4,
-                             cpu_backward=False, extra_config=None, qk_e2m1=False):
+                             cpu_backward=False, extra_config=None, qk_small=None):
     """One attention workload at its full size: quantize, forward and backward (each dQ mode) timed over
     back-to-back calls with HIP events on the launch stream. Returns the JSON dict (not printed)."""
     stream = torch.cuda.current_stream()
@@ -366,19 +367,22 @@ def bench_attention_workload(args, torch, mx, label, workload, lens_q, lens_k, H
             if jag:
                 mx.mxfa_varlen_scale_scatter(sc, cu_d, len(lens), max(lens), C, mode, pad, pad.shape[0], stream)
         return mx.MxOperand(d, pad, mode), run
-    def operand_e2m1(name, T, P, cu_d, lens, jag):
-        d, sc = u8(T, C // 2), u8(T, C // 32)
+    def operand_small(name, T, P, cu_d, lens, jag):
+        # MXFP4 (16 B per 32 elements) or MXFP6 (24 B), ROW32 scales
+        nbytes, quant, elem = {"e2m1": (16, mx.mxfa_quantize_e2m1, mx.E2M1),
+                               "e2m3": (24, mx.mxfa_quantize_e2m3, mx.E2M3)}[qk_small]
+        d, sc = u8(T, C // 32 * nbytes), u8(T, C // 32)
         pad = u8(P, C // 32) if jag else sc
 
         def run():
-            mx.mxfa_quantize_e2m1(dev[name], C, T, C, d, sc, stream)
+            quant(dev[name], C, T, C, d, sc, stream)
             if jag:
                 mx.mxfa_varlen_scale_scatter(sc, cu_d, len(lens), max(lens), C, mx.ROW32, pad, pad.shape[0], stream)
-        return mx.MxOperand(d, pad, mx.ROW32, mx.E2M1), run
-    if qk_e2m1:
+        return mx.MxOperand(d, pad, mx.ROW32, elem), run
+    if qk_small:
         assert fwd_only and qk_mode == mx.ROW32
-        qop, rq = operand_e2m1("q", Tq, Pq, cq_d, lens_q, jag_q)
-        kop, rk = operand_e2m1("k", Tk, Pk, ck_d, lens_k, jag_k)
+        qop, rq = operand_small("q", Tq, Pq, cq_d, lens_q, jag_q)
+        kop, rk = operand_small("k", Tk, Pk, ck_d, lens_k, jag_k)
     else:
         qop, rq = operand("q", qk_mode, Tq, nbq, Pq, cq_d, lens_q, jag_q)
         kop, rk = operand("k", qk_mode, Tk, nbk, Pk, ck_d, lens_k, jag_k)
@@ -423,14 +427,16 @@ def bench_attention_workload(args, torch, mx, label, workload, lens_q, lens_k, H
     print(f"# {label}: " + ", ".join(f"{k}={v}" for k, v in res.items()), file=sys.stderr, flush=True)
     cfg = {"workload": workload, "H": H, "D": D, "causal": bool(causal), "nseq": len(lens_q), "tokens_q": Tq,
            "tokens_k": Tk, "max_len": max(lens_k), "outlier_p": outlier_p, **(extra_config or {}), **res}
-    peak = PEAK_FWD_QK4 if qk_e2m1 else PEAK_MXFP8
+    peak = PEAK_FWD_QK4 if qk_small else PEAK_MXFP8
+    small = {"e2m1": ("MXFP4", "FP4", "mxfp4_e2m1"), "e2m3": ("MXFP6", "FP6", "mxfp6_e2m3")}.get(qk_small)
     out = {
-        "metric": ("MXFP4-QK attention forward PF/s and % of the MI355X dense MFMA peak of its mix (S in FP4, "
-                   "P V in FP8)") if qk_e2m1 else "MXFP8 attention fwd/bwd PF/s and % of MI355X dense MXFP8 MFMA peak",
+        "metric": (f"{small[0]}-QK attention forward PF/s and % of the MI355X dense MFMA peak of its mix (S in "
+                   f"{small[1]}, P V in FP8)") if small else
+                  "MXFP8 attention fwd/bwd PF/s and % of MI355X dense MXFP8 MFMA peak",
         "value": round(value, 4), "unit": "PF/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round((res.get("step_us", res["fwd_us"])) / 1e3, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
-        "dtype": "mxfp4_e2m1 Q/K, mxfp8_e4m3 V/P (fp32 accumulate)" if qk_e2m1 else "mxfp8_e4m3 (fp32 accumulate)",
+        "dtype": f"{small[2]} Q/K, mxfp8_e4m3 V/P (fp32 accumulate)" if small else "mxfp8_e4m3 (fp32 accumulate)",
         "data": "synthetic", "config": cfg,
         "roofline": {"bound": "mfma", "achieved": round(dom_f / dom_t / 1e12, 2), "peak": round(peak / 1e12, 1),
                      "unit": "TFLOP/s", "frac": round(dom_f / dom_t / peak, 4), "traffic": None,
@@ -441,7 +447,7 @@ def bench_attention_workload(args, torch, mx, label, workload, lens_q, lens_k, H
         sl = [{n: np.ascontiguousarray(host[n][int((cu_q if n in ("q", "do") else cu_k)[s]):
                                                int((cu_q if n in ("q", "do") else cu_k)[s + 1]), h * D:(h + 1) * D])
                for n in ("q", "k", "v", "do")} for s, h in picks]
-        dt, cores = oracle_slices(sl, cpu_backward, c, causal, qk_mode, qk_e2m1)
+        dt, cores = oracle_slices(sl, cpu_backward, c, causal, qk_mode, qk_small)
         f = sum(attn_flops([lens_q[s]], [lens_k[s]], 1, causal) for s, _ in picks) * (3.5 if cpu_backward else 1.0)
         model, nproc, _ = host_cpu()
         out["cpu_baseline"] = {"value": round(f / dt / 1e15, 8), "unit": "PF/s", "cores": cores, "kind": "oracle",
@@ -478,7 +484,7 @@ def bench_workloads(args, torch, mx):
 
 
 def bench_forward_only(args, torch, mx):
-    """The forward-only LLM shape with Q/K in MXFP8 and, on the same inputs, in MXFP4."""
+    """The forward-only LLM shape with Q/K in MXFP8 and, on the same inputs, in MXFP4 and MXFP6."""
     lines = []
     fo = bench_attention_workload(
         args, torch, mx, "forward-only", "LLM forward B=4 H=16 N=4096, Q/K ROW32, V COL32",
@@ -486,9 +492,13 @@ def bench_forward_only(args, torch, mx):
     lines.append(fo)
     f4 = bench_attention_workload(
         args, torch, mx, "forward-only MXFP4 Q/K", "LLM forward B=4 H=16 N=4096, Q/K MXFP4 (E2M1) ROW32, V E4M3 COL32",
-        [N] * B, [N] * B, H, False, 0.0, SEED, fwd_only=True, cpu_slices=2, qk_e2m1=True)
-    f4["config"]["mxfp8_qk_same_shape"] = {k: fo["config"][k] for k in ("fwd_us", "fwd_pflops", "quant_us")}
-    lines.append(f4)
+        [N] * B, [N] * B, H, False, 0.0, SEED, fwd_only=True, cpu_slices=2, qk_small="e2m1")
+    f6 = bench_attention_workload(
+        args, torch, mx, "forward-only MXFP6 Q/K", "LLM forward B=4 H=16 N=4096, Q/K MXFP6 (E2M3) ROW32, V E4M3 COL32",
+        [N] * B, [N] * B, H, False, 0.0, SEED, fwd_only=True, cpu_slices=2, qk_small="e2m3")
+    for f in (f4, f6):
+        f["config"]["mxfp8_qk_same_shape"] = {k: fo["config"][k] for k in ("fwd_us", "fwd_pflops", "quant_us")}
+        lines.append(f)
     return lines
 
 

@@ -64,13 +64,15 @@ typedef enum {
                               [AE-TMEM: dQ reduction in FP16 with static scaling; BR item 6] */
 } mxfa_dq_mode;
 
-/* Element format of an MX payload. E4M3 (MXFP8) everywhere; E2M1 (MXFP4: two elements per byte,
- * element 2i in the low nibble of byte i, magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6) only for the
- * forward's q and k, in ROW32 blocks [brifing.si "Future directions": MXFP6 and MXFP4 as the next
- * precisions; TC paragraph 1: the block-scaled matrix units run MXFP8, MXFP6 and MXFP4]. */
-typedef enum { MXFA_E4M3 = 0, MXFA_E2M1 = 1 } mxfa_elem;
+/* Element format of an MX payload. E4M3 (MXFP8) everywhere; for the forward's q and k only, in ROW32
+ * blocks, also E2M1 (MXFP4: two elements per byte, element 2i in the low nibble of byte i, magnitudes
+ * 0, 0.5, 1, 1.5, 2, 3, 4, 6) or E2M3 (MXFP6: a block's 32 six-bit codes in 24 bytes, code j at bits
+ * 6j..6j+5 of a little-endian bit string; magnitudes f/8 below 1, then 2^e (1 + f/8) up to 7.5)
+ * [brifing.si "Future directions": MXFP6 and MXFP4 as the next precisions; TC paragraph 1: the
+ * block-scaled matrix units run MXFP8, MXFP6 and MXFP4]. */
+typedef enum { MXFA_E4M3 = 0, MXFA_E2M1 = 1, MXFA_E2M3 = 2 } mxfa_elem;
 
-/* One MX operand: payload [T, C] (row stride C bytes; C/2 bytes for E2M1) and its scale tensor in
+/* One MX operand: payload [T, C] (row stride C bytes; C/2 for E2M1, 3C/4 for E2M3) and its scale tensor in
  * `mode`'s layout. A zero-initialised struct has elem = MXFA_E4M3. */
 typedef struct {
   const uint8_t* data;
@@ -84,9 +86,9 @@ typedef struct {
  * Allowed modes (scales along the MMA contraction dimension [TC paragraph 3]):
  *   q, k : ROW32 (along D) or SQ32 (square; one payload serves both GEMM directions [AE-TMEM])
  *   v    : COL32 (along the keys, for O = P V) or SQ32.
- * Element formats: E4M3 for all three, or (forward entry points only) q and k both E2M1 in ROW32
- * with v E4M3: S = Q K^T then runs on the FP4 form of the scaled MMA; the backward entry points
- * return MXFA_ERR_UNSUPPORTED for E2M1 operands.
+ * Element formats: E4M3 for all three, or (forward entry points only) q and k both E2M1 or both
+ * E2M3 in ROW32 with v E4M3: S = Q K^T then runs on the FP4 / FP6 form of the scaled MMA; the
+ * backward entry points return MXFA_ERR_UNSUPPORTED for such operands.
  * Causal masking is top-left aligned (key j visible to query i iff j <= i, positions counted
  * from each sequence start). head_dim must be 128. */
 typedef struct {
@@ -130,6 +132,16 @@ mxfa_status mxfa_quantize(const uint16_t* x, int64_t ld_x, int64_t T, int C, con
  *   scale_out  : [T][C/32] (the ROW32 layout; scatter it with mxfa_varlen_scale_scatter as for
  *                E4M3 payloads). x, data_out and scale_out 16-byte aligned. */
 mxfa_status mxfa_quantize_e2m1(const uint16_t* x, int64_t ld_x, int64_t T, int C, uint8_t* data_out,
+                               uint8_t* scale_out, void* stream);
+
+/* MXFP6 quantization of a bf16 matrix in ROW32 blocks, by the same rule with E2M3 elements
+ * [brifing.si "Future directions"]: scale code e = clamp(exponent_field(amax) - 2, 0, 254) (7.5 =
+ * 1.875 * 2^2), 255 for NaN/Inf blocks; element = the E2M3 magnitude nearest to |x| * 2^(127-e), ties
+ * to the even code, saturating at 7.5, with x's sign bit (NaN blocks: payload 0).
+ *   data_out  : [T, 3C/4] payload, block b of a row at bytes 24b .. 24b + 23 (code j of the block at
+ *               bits 6j .. 6j + 5, little-endian)
+ *   scale_out : [T][C/32]; other arguments as mxfa_quantize_e2m1. */
+mxfa_status mxfa_quantize_e2m3(const uint16_t* x, int64_t ld_x, int64_t T, int C, uint8_t* data_out,
                                uint8_t* scale_out, void* stream);
 
 /* Jagged zero-gather scale path [AE-TMEM: split addressing; BR item 5: lightweight scatter that

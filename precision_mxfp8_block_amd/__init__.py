@@ -19,7 +19,8 @@ __all__ = [
     "fwd_mx_out", "bwd_mx_out",
     "mxfa_bwd_workspace_size", "mxfa_rmsnorm_quantize", "mxfa_linear_quantize", "mxfa_status_string",
     "mxfa_last_error_message", "MxOperand", "AttnArgs", "quantize", "scale_scatter", "fwd", "bwd",
-    "rmsnorm_quantize", "linear_quantize", "E4M3", "E2M1", "mxfa_quantize_e2m1", "quantize_e2m1",
+    "rmsnorm_quantize", "linear_quantize", "E4M3", "E2M1", "E2M3", "mxfa_quantize_e2m1",
+    "quantize_e2m1", "mxfa_quantize_e2m3", "quantize_e2m3",
     "mxfa_linear_bwd_data", "mxfa_linear_bwd_weight", "mxfa_linear_bwd_weight_workspace_size", "mxfa_rmsnorm_bwd",
     "mxfa_rmsnorm_bwd_workspace_size", "linear_bwd_data", "linear_bwd_weight", "rmsnorm_bwd",
     "library_path",
@@ -28,7 +29,7 @@ __all__ = [
 ROW32, COL32, SQ32 = 0, 1, 2
 DQ_FP32, DQ_FP16_STATIC = 0, 1
 P_STATIC, P_BLOCK_DYNAMIC = 0, 1
-E4M3, E2M1 = 0, 1  # element formats (mxfa_elem)
+E4M3, E2M1, E2M3 = 0, 1, 2  # element formats (mxfa_elem)
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmxfa.so")
 _lib = None
@@ -72,6 +73,7 @@ def _load():
     lib.mxfa_quantize.argtypes = [P, i64, i64, i32, P, i32, i32, i32, P, P, P, P]
     lib.mxfa_varlen_scale_scatter.argtypes = [P, P, i32, i32, i32, i32, P, i64, P]
     lib.mxfa_quantize_e2m1.argtypes = [P, i64, i64, i32, P, P, P]
+    lib.mxfa_quantize_e2m3.argtypes = [P, i64, i64, i32, P, P, P]
     lib.mxfa_padded_token_rows.argtypes = [P, i32]
     lib.mxfa_padded_token_rows.restype = i64
     lib.mxfa_fwd.argtypes = [ctypes.POINTER(_AttnArgs), P, P, P]
@@ -98,7 +100,7 @@ def _load():
     lib.mxfa_status_string.restype = ctypes.c_char_p
     lib.mxfa_last_error_message.argtypes = []
     lib.mxfa_last_error_message.restype = ctypes.c_char_p
-    for n in ("mxfa_quantize", "mxfa_quantize_e2m1", "mxfa_varlen_scale_scatter", "mxfa_fwd", "mxfa_fwd_p_scale", "mxfa_fwd_mx_out", "mxfa_bwd",
+    for n in ("mxfa_quantize", "mxfa_quantize_e2m1", "mxfa_quantize_e2m3", "mxfa_varlen_scale_scatter", "mxfa_fwd", "mxfa_fwd_p_scale", "mxfa_fwd_mx_out", "mxfa_bwd",
               "mxfa_bwd_mx_out", "mxfa_bwd_no_alloc", "mxfa_rmsnorm_quantize",
               "mxfa_linear_quantize", "mxfa_linear_bwd_data", "mxfa_linear_bwd_weight", "mxfa_rmsnorm_bwd"):
         getattr(lib, n).restype = i32
@@ -150,6 +152,11 @@ def mxfa_quantize(x, ld_x, T, C, cu_seqlens, nseq, max_seqlen, mode, data_out, s
 def mxfa_quantize_e2m1(x, ld_x, T, C, data_out, scale_out, stream=None):
     _check(_load().mxfa_quantize_e2m1(_ptr(x), ld_x, T, C, _ptr(data_out), _ptr(scale_out), _stream(stream)),
            "mxfa_quantize_e2m1")
+
+
+def mxfa_quantize_e2m3(x, ld_x, T, C, data_out, scale_out, stream=None):
+    _check(_load().mxfa_quantize_e2m3(_ptr(x), ld_x, T, C, _ptr(data_out), _ptr(scale_out), _stream(stream)),
+           "mxfa_quantize_e2m3")
 
 
 def mxfa_varlen_scale_scatter(compact, cu_seqlens, nseq, max_seqlen, C, mode, padded_out, padded_rows, stream=None):
@@ -280,6 +287,15 @@ def quantize_e2m1(x_bf16, stream=None):
     data = torch.empty((T, C // 2), dtype=torch.uint8, device=x_bf16.device)
     scale = torch.empty((T, C // 32), dtype=torch.uint8, device=x_bf16.device)
     mxfa_quantize_e2m1(x_bf16, x_bf16.stride(0), T, C, data, scale, stream)
+    return data, scale
+
+
+def quantize_e2m3(x_bf16, stream=None):
+    """x_bf16: torch.bfloat16 [T, C] on the GPU. Returns (data [T, 3C/4], scale [T, C/32]): MXFP6 ROW32."""
+    T, C = x_bf16.shape
+    data = torch.empty((T, 3 * C // 4), dtype=torch.uint8, device=x_bf16.device)
+    scale = torch.empty((T, C // 32), dtype=torch.uint8, device=x_bf16.device)
+    mxfa_quantize_e2m3(x_bf16, x_bf16.stride(0), T, C, data, scale, stream)
     return data, scale
 
 

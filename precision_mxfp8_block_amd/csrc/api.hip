@@ -80,12 +80,12 @@ mxfa_status check_attn(const mxfa_attn_args* a, const char* fn) {
       return fail(MXFA_ERR_INVALID, "%s: %s data/scale not 16-byte aligned", fn, names[i]);
   }
   for (int i = 0; i < 3; ++i)
-    if (ops[i]->elem != MXFA_E4M3 && ops[i]->elem != MXFA_E2M1)
+    if (ops[i]->elem != MXFA_E4M3 && ops[i]->elem != MXFA_E2M1 && ops[i]->elem != MXFA_E2M3)
       return fail(MXFA_ERR_INVALID, "%s: %s.elem=%d is not an element format", fn, names[i], (int)ops[i]->elem);
   if (a->q.elem != a->k.elem) return fail(MXFA_ERR_INVALID, "%s: q and k must share one element format", fn);
-  if (!e4m3(a->v)) return fail(MXFA_ERR_UNSUPPORTED, "%s: v must be E4M3 (MXFP4 is for q and k only)", fn);
-  if (a->q.elem == MXFA_E2M1 && (a->q.mode != MXFA_ROW32 || a->k.mode != MXFA_ROW32))
-    return fail(MXFA_ERR_UNSUPPORTED, "%s: MXFP4 q and k must be ROW32", fn);
+  if (!e4m3(a->v)) return fail(MXFA_ERR_UNSUPPORTED, "%s: v must be E4M3 (MXFP4/MXFP6 are for q and k only)", fn);
+  if (!e4m3(a->q) && (a->q.mode != MXFA_ROW32 || a->k.mode != MXFA_ROW32))
+    return fail(MXFA_ERR_UNSUPPORTED, "%s: MXFP4/MXFP6 q and k must be ROW32", fn);
   if (a->q.mode != MXFA_ROW32 && a->q.mode != MXFA_SQ32)
     return fail(MXFA_ERR_INVALID, "%s: q.mode must be ROW32 or SQ32", fn);
   if (a->k.mode != MXFA_ROW32 && a->k.mode != MXFA_SQ32)
@@ -268,6 +268,19 @@ mxfa_status mxfa_quantize_e2m1(const uint16_t* x, int64_t ld_x, int64_t T, int C
     return fail(MXFA_ERR_INVALID, "%s: x/data_out/scale_out not 16-byte aligned", fn);
   if (T * (C / 16) / 256 >= ((int64_t)1 << 31)) return fail(MXFA_ERR_INVALID, "%s: tensor too large for one launch", fn);
   return hip_status(mxfa::launch_quantize_e2m1(x, ld_x, T, C, data_out, scale_out, (hipStream_t)stream), fn);
+}
+
+mxfa_status mxfa_quantize_e2m3(const uint16_t* x, int64_t ld_x, int64_t T, int C, uint8_t* data_out,
+                               uint8_t* scale_out, void* stream) {
+  const char* fn = "mxfa_quantize_e2m3";
+  if (T < 0) return fail(MXFA_ERR_INVALID, "%s: T=%lld < 0", fn, (long long)T);
+  if (C <= 0 || C % 32) return fail(MXFA_ERR_INVALID, "%s: C=%d must be a positive multiple of 32", fn, C);
+  if (ld_x < C || ld_x % 8) return fail(MXFA_ERR_INVALID, "%s: ld_x=%lld must be >= C and a multiple of 8", fn, (long long)ld_x);
+  if (!x || !data_out || !scale_out) return fail(MXFA_ERR_INVALID, "%s: NULL x/data_out/scale_out", fn);
+  if (!aligned(x, 16) || !aligned(data_out, 16) || !aligned(scale_out, 16))
+    return fail(MXFA_ERR_INVALID, "%s: x/data_out/scale_out not 16-byte aligned", fn);
+  if (T * (C / 16) / 256 >= ((int64_t)1 << 31)) return fail(MXFA_ERR_INVALID, "%s: tensor too large for one launch", fn);
+  return hip_status(mxfa::launch_quantize_e2m3(x, ld_x, T, C, data_out, scale_out, (hipStream_t)stream), fn);
 }
 
 mxfa_status mxfa_varlen_scale_scatter(const uint8_t* compact, const int32_t* cu_seqlens, int nseq, int max_seqlen,

@@ -143,11 +143,16 @@ __device__ __forceinline__ uint32_t undef_word() {
   return u;
 }
 
-// QK4: Q and K in MXFP4 (E2M1, two elements per byte, ROW32 scales), S computed by the scaled MFMA
-// in its FP4 format (twice the FP8 rate). The K tile then takes 64 bytes per key: LDS row R of the
-// K stage holds keys 2R (logical chunks 0-3) and 2R + 1 (chunks 4-7), swizzled like the FP8 tiles.
-template <bool VCOL32, bool PDYN, bool QK4>
+// QKF: the element format of Q and K, as the scaled MFMA's format code: 0 E4M3; 4 E2M1 (MXFP4, two
+// elements per byte); 2 E2M3 (MXFP6, a block's 32 codes in 24 bytes). Both low-precision forms run
+// S at twice the FP8 rate with ROW32 scales; a lane's operand is then the 32 elements of one d-block
+// (16 or 24 bytes). The MXFP4 K tile takes 64 bytes per key: LDS row R of the K stage holds keys 2R
+// (logical chunks 0-3) and 2R + 1 (chunks 4-7). The MXFP6 K tile keeps one key per 128-byte row
+// (96 bytes used; the copy of logical chunks 6 and 7 re-reads chunks 0 and 1). Both are swizzled
+// like the FP8 tiles.
+template <bool VCOL32, bool PDYN, int QKF>
 __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
+  constexpr bool QK4 = QKF == 4, QK6 = QKF == 2;
   __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[kLdsBytes];
   MX_LDS uint8_t* const lds = (MX_LDS uint8_t*)lds_raw;
 
@@ -187,8 +192,8 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
   // row stride of Q and K in bytes, and the K tile pieces of QK4 (two 1 KB pieces per wave: piece c
   // of wave w covers LDS row R = 8 (2 w + c) + l / 8, physical chunk l % 8, i.e. key 2 R + lc / 4,
   // bytes 16 (lc % 4) of its 64, lc = (l % 8) ^ swz(R) the logical chunk)
-  constexpr int kQKBytes = QK4 ? kD / 2 : kD;
-  const int ldqk = QK4 ? C / 2 : C;
+  constexpr int kQKBytes = QK4 ? kD / 2 : QK6 ? 3 * kD / 4 : kD;
+  const int ldqk = QK4 ? C / 2 : QK6 ? 3 * C / 4 : C;
   int k4row[2];
   uint32_t k4col[2];
   if constexpr (QK4) {
@@ -198,6 +203,15 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
       const int R = pchunk >> 3, lc = (pchunk & 7) ^ swz(pchunk >> 3);
       k4row[c] = 2 * R + (lc >> 2);
       k4col[c] = (uint32_t)(16 * (lc & 3));
+    }
+  }
+  // MXFP6 K tile pieces: as the FP8 tile's, 96-byte rows (logical chunks 6 and 7 re-read 0 and 1)
+  uint32_t k6col[4];
+  if constexpr (QK6) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int lc = tcol[c] >> 4;
+      k6col[c] = (uint32_t)(16 * (lc < 6 ? lc : lc - 6));
     }
   }
   const uint8_t* kbase = (const uint8_t*)mx_uniform_ptr((void*)(p.k + k_start * (int64_t)ldqk + h * kQKBytes));
@@ -217,6 +231,14 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
       for (int c = 0; c < 2; ++c) off[c] = (uint32_t)(min(k4row[c], valid - 1) * ldqk) + k4col[c];
       dma16_at<TILE + 0>(wave_lds_k4, base, off[0]);
       dma16_at<TILE + 1024>(wave_lds_k4, base, off[1]);
+    } else if constexpr (QK6) {
+      uint32_t off[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) off[c] = (uint32_t)(min(trow[c], valid - 1) * ldqk) + k6col[c];
+      dma16_at<TILE + 0>(wave_lds, base, off[0]);
+      dma16_at<TILE + 1024>(wave_lds, base, off[1]);
+      dma16_at<TILE + 2048>(wave_lds, base, off[2]);
+      dma16_at<TILE + 3072>(wave_lds, base, off[3]);
     } else {
       issue_tile_load<TILE>(wave_lds, base, valid, C, trow, tcol, toff);
     }
@@ -234,6 +256,15 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
       if constexpr (QK4) {
         // FP4: the lane's 32 elements of d-block 2 ds + hh, 16 bytes (the upper operand half unused)
         if (valid) lo = *reinterpret_cast<const uint4*>(src + 32 * ds + 16 * hh);
+      } else if constexpr (QK6) {
+        // FP6: the 24 bytes of d-block 2 ds + hh (registers 0-5)
+        if (valid) {
+          const uint2 a0 = *reinterpret_cast<const uint2*>(src + 48 * ds + 24 * hh);
+          const uint2 a1 = *reinterpret_cast<const uint2*>(src + 48 * ds + 24 * hh + 8);
+          const uint2 a2 = *reinterpret_cast<const uint2*>(src + 48 * ds + 24 * hh + 16);
+          lo = make_uint4(a0.x, a0.y, a1.x, a1.y);
+          hi = make_uint4(a2.x, a2.y, 0u, 0u);
+        }
       } else if (valid) {
         lo = *reinterpret_cast<const uint4*>(src + 64 * ds + 16 * hh);
         hi = *reinterpret_cast<const uint4*>(src + 64 * ds + 32 + 16 * hh);
@@ -297,7 +328,20 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
   //  * scales: K scale word 32 kb + r; V scale byte 128 (2 ks + hh) + (COL32: 32 db + r, SQ32: db).
   //  * QK4 K rows: key 32 kb + r is in LDS row 16 kb + r / 2 (its swizzle does not depend on kb),
   //    logical chunk 4 (r % 2) + 2 ds + hh: the 32 elements of d-block 2 ds + hh;
+  //  * QK6 K rows: key row r, the 24 bytes of d-block 2 ds + hh as three 8-byte reads at logical bytes
+  //    48 ds + 24 hh + 8 i, each inside one 16-byte chunk (koffs6);
   uint32_t koffs[2][2];
+  uint32_t koffs6[2][3];
+  if constexpr (QK6) {
+    const int sw = swz(r);
+#pragma unroll
+    for (int ds = 0; ds < 2; ++ds)
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        const int o = 48 * ds + 24 * hh + 8 * i;
+        koffs6[ds][i] = (uint32_t)(r * kD + 16 * ((o >> 4) ^ sw) + (o & 15));
+      }
+  }
   if constexpr (QK4) {
     const int R = r >> 1, sw = swz(R);
 #pragma unroll
@@ -340,13 +384,22 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
       sacc[kb] = mx_v16f{};
 #pragma unroll
       for (int ds = 0; ds < 2; ++ds) {
-        // operand format: 0 = E4M3, 4 = E2M1 (the FP4 operand fills the low four registers)
-        constexpr int fmt = QK4 ? 4 : 0;
-        const MX_LDS uint8_t* t = lds + lds_k_off(sk) + 32 * kb * kQKBytes;
-        const mx_v4i lo = *(const MX_LDS mx_v4i*)(t + koffs[ds][0]);
-        mx_v4i hi = mx_v4i{0, 0, 0, 0};
-        if constexpr (!QK4) hi = *(const MX_LDS mx_v4i*)(t + koffs[ds][1]);
-        mx_v8i ka{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        // operand format: the MFMA's code (the FP4 operand fills registers 0-3, the FP6 one 0-5)
+        constexpr int fmt = QKF;
+        mx_v8i ka;
+        if constexpr (QK6) {
+          const MX_LDS uint8_t* t = lds + lds_k_off(sk) + 32 * kb * kD;
+          const mx_v2i a0 = *(const MX_LDS mx_v2i*)(t + koffs6[ds][0]);
+          const mx_v2i a1 = *(const MX_LDS mx_v2i*)(t + koffs6[ds][1]);
+          const mx_v2i a2 = *(const MX_LDS mx_v2i*)(t + koffs6[ds][2]);
+          ka = mx_v8i{a0.x, a0.y, a1.x, a1.y, a2.x, a2.y, 0, 0};
+        } else {
+          const MX_LDS uint8_t* t = lds + lds_k_off(sk) + 32 * kb * kQKBytes;
+          const mx_v4i lo = *(const MX_LDS mx_v4i*)(t + koffs[ds][0]);
+          mx_v4i hi = mx_v4i{0, 0, 0, 0};
+          if constexpr (!QK4) hi = *(const MX_LDS mx_v4i*)(t + koffs[ds][1]);
+          ka = mx_v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        }
         if (ds == 0)
           sacc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qa[0], sacc[kb], fmt, fmt, 0, (int)kscb, 0,
                                                                      (int)qsc);
@@ -640,29 +693,27 @@ hipError_t launch_attn_fwd(const AttnProblem& a, int p_dynamic, uint16_t* o, uin
   p.o = o; p.o_mx = o_mx; p.o_mx_scale = o_mx_scale; p.lse = lse; p.Tq = a.total_q;
   if (p.total_items == 0) return hipSuccess;
   const dim3 grid((unsigned)p.total_items), block(256);
-  if (a.q.elem == 1) {  // Q and K in MXFP4 (checked by the caller: both ROW32, V COL32 or SQ32 in E4M3)
+  // Q and K in MXFP4 (elem 1) or MXFP6 (elem 2): checked by the caller (both ROW32, V in E4M3)
+  auto launch = [&](auto qkf) {
+    constexpr int F = decltype(qkf)::value;
     if (p.v_col_shift == 0) {
       if (p_dynamic)
-        hipLaunchKernelGGL((attn_fwd_kernel<true, true, true>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((attn_fwd_kernel<true, true, F>), grid, block, 0, stream, p);
       else
-        hipLaunchKernelGGL((attn_fwd_kernel<true, false, true>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((attn_fwd_kernel<true, false, F>), grid, block, 0, stream, p);
     } else {
       if (p_dynamic)
-        hipLaunchKernelGGL((attn_fwd_kernel<false, true, true>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((attn_fwd_kernel<false, true, F>), grid, block, 0, stream, p);
       else
-        hipLaunchKernelGGL((attn_fwd_kernel<false, false, true>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((attn_fwd_kernel<false, false, F>), grid, block, 0, stream, p);
     }
-  } else if (p.v_col_shift == 0) {
-    if (p_dynamic)
-      hipLaunchKernelGGL((attn_fwd_kernel<true, true, false>), grid, block, 0, stream, p);
-    else
-      hipLaunchKernelGGL((attn_fwd_kernel<true, false, false>), grid, block, 0, stream, p);
-  } else {
-    if (p_dynamic)
-      hipLaunchKernelGGL((attn_fwd_kernel<false, true, false>), grid, block, 0, stream, p);
-    else
-      hipLaunchKernelGGL((attn_fwd_kernel<false, false, false>), grid, block, 0, stream, p);
-  }
+  };
+  if (a.q.elem == 1)
+    launch(Stage<4>{});
+  else if (a.q.elem == 2)
+    launch(Stage<2>{});
+  else
+    launch(Stage<0>{});
   return hipGetLastError();
 }
 

@@ -10,7 +10,7 @@ struct MxOperand {
   const uint8_t* data;
   const uint8_t* scale;
   int mode;      // 0 ROW32, 1 COL32, 2 SQ32
-  int elem = 0;  // 0 E4M3 (one byte per element), 1 E2M1 (two elements per byte)
+  int elem = 0;  // 0 E4M3 (one byte per element), 1 E2M1 (two elements per byte), 2 E2M3 (4 per 3 bytes)
 };
 
 struct AttnProblem {
@@ -29,6 +29,9 @@ hipError_t launch_quantize(const uint16_t* x, int64_t ld_x, int64_t T, int C, co
                            hipStream_t stream);
 // MXFP4 (E2M1) ROW32 quantization: payload [T, C/2], scales [T][C/32].
 hipError_t launch_quantize_e2m1(const uint16_t* x, int64_t ld_x, int64_t T, int C, uint8_t* data, uint8_t* scale,
+                               hipStream_t stream);
+// MXFP6 (E2M3) ROW32 quantization: payload [T, 3C/4] (24 bytes per block), scales [T][C/32].
+hipError_t launch_quantize_e2m3(const uint16_t* x, int64_t ld_x, int64_t T, int C, uint8_t* data, uint8_t* scale,
                                hipStream_t stream);
 hipError_t launch_scale_scatter(const uint8_t* compact, const int32_t* cu, int nseq, int max_seqlen, int C, int mode,
                                 uint8_t* padded, int64_t padded_rows, hipStream_t stream);

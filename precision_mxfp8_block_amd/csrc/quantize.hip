@@ -103,6 +103,67 @@ __global__ void __launch_bounds__(256) quantize_row32_e2m1_kernel(const uint16_t
 }
 
 // ---------------------------------------------------------------------------------------------
+// ROW32 in MXFP6: E2M3 elements (OCP MX: f/8 below 1, then 2^e (1 + f/8) up to 7.5) with the scale
+// code clamp(exponent_field(amax) - 2, 0, 254); 255 and a zero payload for blocks holding NaN or Inf.
+// A block's 32 six-bit codes form a 24-byte little-endian bit string (code j at bits 6j .. 6j + 5).
+// Two lanes share a block, 16 bf16 each; a lane writes its 12 bytes (bits 96 h .. 96 h + 95).
+// ---------------------------------------------------------------------------------------------
+// Nearest E2M3 code of v (already scaled), ties to the even code, saturating at 7.5, sign kept: below
+// 1 the step is 1/8 (q = rne(8 a) is the code; q = 8 is 1.0, the first normal); in binade [2^e,
+// 2^(e+1)), e = 0..2, the step is 2^(e-3) and the code (e + 1) 8 + rne(a 2^(3-e)) - 8 (a rounding up
+// to the next binade gives that binade's first code); codes past 31 (a >= 7.75) saturate.
+__device__ __forceinline__ uint32_t e2m3_code(float v) {
+  const float a = fabsf(v);
+  uint32_t c;
+  if (a < 1.0f) {
+    c = (uint32_t)__builtin_rintf(a * 8.0f);
+  } else if (a >= 8.0f) {
+    c = 31u;
+  } else {
+    const int e = (int)(__float_as_uint(a) >> 23) - 127;  // 0, 1 or 2
+    const float q = __builtin_rintf(a * __uint_as_float((uint32_t)(130 - e) << 23));  // a 2^(3-e)
+    c = min((uint32_t)((e + 1) * 8) + (uint32_t)q - 8u, 31u);
+  }
+  return c | ((__float_as_uint(v) >> 26) & 32u);
+}
+
+__global__ void __launch_bounds__(256) quantize_row32_e2m3_kernel(const uint16_t* __restrict__ x, int64_t ld_x,
+                                                                  int64_t T, int C, uint8_t* __restrict__ data,
+                                                                  uint8_t* __restrict__ scale) {
+  const int64_t chunks_per_row = C >> 4;
+  const int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (u >= T * chunks_per_row) return;  // pairs of lanes leave together (chunks_per_row is even)
+  const int64_t t = u / chunks_per_row;
+  const int j = (int)(u - t * chunks_per_row);
+  const uint4* src = reinterpret_cast<const uint4*>(x + t * ld_x + (int64_t)j * 16);
+  const uint4 a = src[0], b = src[1];
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  uint32_t amax = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = max(amax, max(w[i] & 0x7fffu, (w[i] >> 16) & 0x7fffu));
+  amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1, 64));
+  const uint32_t e = amax >> 7;
+  const uint32_t code = e >= 255u ? 255u : (e > 2u ? e - 2u : 0u);
+  uint32_t o[3] = {0u, 0u, 0u};
+  if (code != 255u) {
+    const float inv = mx_inv_scale(code);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t h = (w[i >> 1] >> (16 * (i & 1))) & 0xffffu;
+      const uint32_t c = e2m3_code(bf16_to_f32(h) * inv);
+      const int bit = 6 * i;  // compile-time after unrolling
+      o[bit >> 5] |= c << (bit & 31);
+      if ((bit & 31) > 26) o[(bit >> 5) + 1] |= c >> (32 - (bit & 31));
+    }
+  }
+  uint32_t* dst = reinterpret_cast<uint32_t*>(data + t * (3 * (int64_t)C / 4) + (int64_t)j * 12);
+  dst[0] = o[0];
+  dst[1] = o[1];
+  dst[2] = o[2];
+  if ((j & 1) == 0) scale[t * (C >> 5) + (j >> 1)] = (uint8_t)code;
+}
+
+// ---------------------------------------------------------------------------------------------
 // COL32: 32 x 1 blocks along the tokens. A wave covers 32 rows x 128 columns: lane l owns columns
 // 4 (l % 32) .. +3 (8-byte loads) of rows 16 (l / 32) + i, i = 0..15; a column's maximum joins the
 // two half-waves with one lane swap. Every load instruction covers two 256-byte row segments and
@@ -531,6 +592,15 @@ hipError_t launch_quantize_e2m1(const uint16_t* x, int64_t ld_x, int64_t T, int 
   const int64_t units = T * (C >> 4);
   if (units == 0) return hipSuccess;
   hipLaunchKernelGGL(quantize_row32_e2m1_kernel, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, stream, x, ld_x,
+                     T, C, data, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_e2m3(const uint16_t* x, int64_t ld_x, int64_t T, int C, uint8_t* data, uint8_t* scale,
+                               hipStream_t stream) {
+  const int64_t units = T * (C >> 4);
+  if (units == 0) return hipSuccess;
+  hipLaunchKernelGGL(quantize_row32_e2m3_kernel, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, stream, x, ld_x,
                      T, C, data, scale);
   return hipGetLastError();
 }

@@ -26,7 +26,7 @@ def _declared_functions():
 
 def test_header_declares_the_abi():
     names = _declared_functions()
-    for n in ["mxfa_quantize", "mxfa_quantize_e2m1", "mxfa_fwd", "mxfa_fwd_p_scale", "mxfa_fwd_mx_out", "mxfa_bwd", "mxfa_bwd_mx_out",
+    for n in ["mxfa_quantize", "mxfa_quantize_e2m1", "mxfa_quantize_e2m3", "mxfa_fwd", "mxfa_fwd_p_scale", "mxfa_fwd_mx_out", "mxfa_bwd", "mxfa_bwd_mx_out",
               "mxfa_varlen_scale_scatter",
               "mxfa_rmsnorm_quantize",
               "mxfa_linear_quantize", "mxfa_linear_bwd_data", "mxfa_linear_bwd_weight",
@@ -97,6 +97,8 @@ def _args(**kw):
     (dict(q=(P, P, 2, 1), k=(P, P, 2, 1)), UNSUPPORTED),  # MXFP4 in SQ32
     (dict(q=(P, P, 0, 1), k=(P, P, 0, 1), v=(P, P, 1, 1)), UNSUPPORTED),  # MXFP4 v
     (dict(q=(P, P, 0, 3), k=(P, P, 0, 3)), INVALID),      # not an element format
+    (dict(q=(P, P, 0, 2), k=(P, P, 0, 1)), INVALID),      # MXFP6 q with MXFP4 k
+    (dict(q=(P, P, 2, 2), k=(P, P, 2, 2)), UNSUPPORTED),  # MXFP6 in SQ32
 ])
 def test_fwd_argument_errors(kw, expect):
     a = _args(**kw)
@@ -126,8 +128,9 @@ def test_bwd_rejects_mxfp4_operands():
 def test_quantize_e2m1_argument_errors(kw, expect):
     a = dict(x=P, ld_x=128, T=256, C=128, data=P, scale=P)
     a.update(kw)
-    st = _lib().mxfa_quantize_e2m1(a["x"], a["ld_x"], a["T"], a["C"], a["data"], a["scale"], 0)
-    assert st == expect and _last() != ""
+    for fn in (_lib().mxfa_quantize_e2m1, _lib().mxfa_quantize_e2m3):
+        st = fn(a["x"], a["ld_x"], a["T"], a["C"], a["data"], a["scale"], 0)
+        assert st == expect and _last() != ""
 
 
 def test_fwd_null_outputs():

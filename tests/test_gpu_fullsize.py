@@ -7,6 +7,7 @@ inputs.
 
 Workloads (shapes, value distributions and seeds of the five workload descriptions):
   LLM forward     B=4, H=16, N=4096: Q/K ROW32, V COL32, forward only; the same with Q/K in MXFP4
+                  and in MXFP6
   training step   same shape: Q/K/dO SQ32, V COL32 (forward) + ROW32 (backward), FP16 dQ with
                   sigma = 1 (the benchmark's step) and FP32 dQ
   causal          B=4, H=16, N=8192, causal, 0.5% of entries x64, both dQ modes
@@ -201,16 +202,20 @@ def test_llm_forward_B4_H16_N4096():
     fa.oracle_fwd_slices(xcd_slices(4, 16))
 
 
-def test_llm_forward_mxfp4_qk_B4_H16_N4096():
-    """The forward with Q and K in MXFP4 (E2M1, ROW32) at the benchmark's size: the GPU's E2M1 payloads and
-    scales of the sampled slices equal the oracle's, and the slices' O and LSE match the oracle's forward."""
-    from oracle import mxfp4
-    say("full-size forward: B=4 H=16 N=4096, Q/K MXFP4 ROW32, V E4M3 COL32")
+@pytest.mark.parametrize("fmt", ["e2m1", "e2m3"])
+def test_llm_forward_small_qk_B4_H16_N4096(fmt):
+    """The forward with Q and K in MXFP4 (E2M1) or MXFP6 (E2M3), ROW32, at the benchmark's size: the GPU's
+    payloads and scales of the sampled slices equal the oracle's, and the slices' O and LSE match the
+    oracle's forward."""
+    from oracle import mxfp4, mxfp6
+    mod, fwd, quant, elem, nb = ((mxfp4, mxfp4.attn_fwd_qk_fp4, mx.quantize_e2m1, mx.E2M1, D // 2) if fmt == "e2m1"
+                                 else (mxfp6, mxfp6.attn_fwd_qk_fp6, mx.quantize_e2m3, mx.E2M3, 3 * D // 4))
+    say(f"full-size forward: B=4 H=16 N=4096, Q/K {fmt} ROW32, V E4M3 COL32")
     fa = FullAttn(2, [4096] * 4, [4096] * 4, 16, qk_mode=mx.ROW32)
-    q4, qs = mx.quantize_e2m1(fa.dev["q"])
-    k4, ks = mx.quantize_e2m1(fa.dev["k"])
+    q4, qs = quant(fa.dev["q"])
+    k4, ks = quant(fa.dev["k"])
     gv = gpu_quantize_padded(fa.dev["v"], fa.cu_k, fa.cu_k_d, mx.COL32)
-    args = mx.AttnArgs(mx.MxOperand(q4, qs, mx.ROW32, mx.E2M1), mx.MxOperand(k4, ks, mx.ROW32, mx.E2M1),
+    args = mx.AttnArgs(mx.MxOperand(q4, qs, mx.ROW32, elem), mx.MxOperand(k4, ks, mx.ROW32, elem),
                        mx.MxOperand(gv[0], gv[1], mx.COL32), fa.cu_q_d, fa.cu_k_d, 4, 4096, 4096, fa.Tq, fa.Tk, 16, D,
                        C_SCALE, False)
     o, lse = Guarded((fa.Tq, fa.C), torch.bfloat16), Guarded((16, fa.Tq), torch.float32)
@@ -220,18 +225,18 @@ def test_llm_forward_mxfp4_qk_B4_H16_N4096():
     all_written(o.t, "O")
     slices = xcd_slices(4, 16)
     cq, ck = fa._stack_cu(slices, "q"), fa._stack_cu(slices, "k")
-    rq = mxfp4.quantize_row32(fa._stack("q", slices))
-    rk = mxfp4.quantize_row32(fa._stack("k", slices))
+    rq = mod.quantize_row32(fa._stack("q", slices))
+    rk = mod.quantize_row32(fa._stack("k", slices))
     rv = oracle.quantize(fa._stack("v", slices), ck, oracle.COL32)
     for i, (s, h) in enumerate(slices):
         rows = slice(int(fa.cu_q[s]), int(fa.cu_q[s + 1]))
         r = slice(int(cq[i]), int(cq[i + 1]))
-        np.testing.assert_array_equal(host(q4[rows, h * D // 2:(h + 1) * D // 2]), rq[0][r])
+        np.testing.assert_array_equal(host(q4[rows, h * nb:(h + 1) * nb]), rq[0][r])
         np.testing.assert_array_equal(host(qs[rows, h * 4:(h + 1) * 4]), rq[1][r])
-        np.testing.assert_array_equal(host(k4[rows, h * D // 2:(h + 1) * D // 2]), rk[0][r])
+        np.testing.assert_array_equal(host(k4[rows, h * nb:(h + 1) * nb]), rk[0][r])
         np.testing.assert_array_equal(host(ks[rows, h * 4:(h + 1) * 4]), rk[1][r])
-    say(f"  oracle MXFP4 forward on {len(slices)} slices {slices}")
-    _, o32, lse_r = mxfp4.attn_fwd_qk_fp4(rq[0], rq[1], rk[0], rk[1], rv[0], rv[1], cq, ck, 1, D, C_SCALE)
+    say(f"  oracle {fmt} forward on {len(slices)} slices {slices}")
+    _, o32, lse_r = fwd(rq[0], rq[1], rk[0], rk[1], rv[0], rv[1], cq, ck, 1, D, C_SCALE)
     for i, (s, h) in enumerate(slices):
         rows = slice(int(fa.cu_q[s]), int(fa.cu_q[s + 1]))
         r = slice(int(cq[i]), int(cq[i + 1]))

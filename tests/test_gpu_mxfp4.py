@@ -1,6 +1,6 @@
-"""MXFP4 (E2M1) path on the GPU against the oracle: the ROW32 quantizer bit for bit, the forward
-with Q and K in MXFP4 (V in E4M3 COL32) to the forward's O and LSE tolerances, and its SQNR against
-exact attention next to the MXFP8 forward's on the same inputs."""
+"""MXFP4 (E2M1) and MXFP6 (E2M3) paths on the GPU against the oracle: the ROW32 quantizers bit for
+bit, the forward with Q and K in MXFP4 or MXFP6 (V in E4M3 COL32) to the forward's O and LSE
+tolerances, and their SQNR against exact attention next to the MXFP8 forward's on the same inputs."""
 import math
 
 import numpy as np
@@ -10,25 +10,52 @@ import torch
 import oracle
 import precision_mxfp8_block_amd as mx
 import synth
-from oracle import mxfp4
+from oracle import mxfp4, mxfp6
 from mx_cases import (Guarded, bf16_bits_to_f64, check_o, cu_dev, gpu_quantize_padded, gpu_scale_scatter, say,
                       to_dev_bf16, to_host_bf16_bits)
 
 pytestmark = pytest.mark.gpu
 
 
-def gpu_quantize_e2m1(x_dev, ld_cols=None):
+# element format -> (payload bytes per 32 elements, GPU entry point, oracle module)
+FORMATS = {"e2m1": (16, mx.mxfa_quantize_e2m1, mxfp4), "e2m3": (24, mx.mxfa_quantize_e2m3, mxfp6)}
+
+
+def gpu_quantize_small(x_dev, fmt="e2m1"):
     T, C = x_dev.shape
-    data, scale = Guarded((T, C // 2), torch.uint8), Guarded((T, C // 32), torch.uint8)
-    mx.mxfa_quantize_e2m1(x_dev, x_dev.stride(0), T, C, data.t, scale.t)
+    nbytes, fn, _ = FORMATS[fmt]
+    data, scale = Guarded((T, C // 32 * nbytes), torch.uint8), Guarded((T, C // 32), torch.uint8)
+    fn(x_dev, x_dev.stride(0), T, C, data.t, scale.t)
     torch.cuda.synchronize()
-    data.check("E2M1 payload"), scale.check("E2M1 scales")
+    data.check(f"{fmt} payload"), scale.check(f"{fmt} scales")
     return data.t.cpu().numpy(), scale.t.cpu().numpy()
 
 
 def bf16_bits(vals):
     a = np.asarray(vals, np.float32).view(np.uint32)
     return (a >> 16).astype(np.uint16)
+
+
+def crafted_rows_e2m3():
+    """Rows of 64 columns at block maximum 4 (code 127, scale 1): every E2M3 midpoint, both signs;
+    saturation; subnormal range; NaN/Inf and zero blocks."""
+    grid = list(np.arange(0, 1, 1 / 8)) + list(np.arange(1, 2, 1 / 8)) + list(np.arange(2, 4, 1 / 4)) + \
+        list(np.arange(4, 8, 1 / 2))
+    mids = [(grid[c] + grid[c + 1]) / 2 for c in range(24)]  # midpoints up to 3.875 (block max stays 4)
+    rows = []
+    r = np.zeros(64, np.float32)
+    r[:24] = mids
+    r[24] = 4.0
+    r[32:56] = -np.array(mids, np.float32)
+    r[56] = -4.0
+    rows.append(bf16_bits(r))
+    r = np.zeros(64, np.float32)
+    r[:6] = [7.25, 7.5, 7.75, 7.875, -7.625, 4.25]   # block max 7.875 (code 127): saturation and ties
+    r[32:38] = [4.75, 5.25, 5.75, 6.25, 6.75, 7.25]  # midpoints of the top binade
+    rows.append(bf16_bits(r))
+    for extra in crafted_rows()[2:]:
+        rows.append(extra)
+    return np.stack(rows)
 
 
 def crafted_rows():
@@ -62,9 +89,10 @@ def crafted_rows():
     return np.stack(rows)
 
 
+@pytest.mark.parametrize("fmt", ["e2m1", "e2m3"])
 @pytest.mark.parametrize("case", ["normal_300x256", "normal_77x2048_ld", "crafted", "scaled_wide"])
-def test_quantize_e2m1_bit_exact(case):
-    say(f"E2M1 quantize case {case}")
+def test_quantize_small_formats_bit_exact(case, fmt):
+    say(f"{fmt} quantize case {case}")
     if case == "normal_300x256":
         x = synth.normal_bf16(41, 1, (300, 256))
         xd = to_dev_bf16(x)
@@ -73,7 +101,7 @@ def test_quantize_e2m1_bit_exact(case):
         x = np.ascontiguousarray(full[:, :2048])
         xd = to_dev_bf16(full)[:, :2048]  # row stride 2112 elements
     elif case == "crafted":
-        x = crafted_rows()
+        x = crafted_rows() if fmt == "e2m1" else crafted_rows_e2m3()
         xd = to_dev_bf16(x)
     else:
         # magnitudes spread over many binades per block
@@ -81,17 +109,17 @@ def test_quantize_e2m1_bit_exact(case):
         f = (rng.normal(size=(64, 512)) * np.exp2(rng.integers(-60, 60, (64, 512)))).astype(np.float32)
         x = bf16_bits(f.view(np.uint32) & 0xFFFF0000)
         xd = to_dev_bf16(x)
-    d, s = gpu_quantize_e2m1(xd)
-    d_ref, s_ref = mxfp4.quantize_row32(x)
+    d, s = gpu_quantize_small(xd, fmt)
+    d_ref, s_ref = FORMATS[fmt][2].quantize_row32(x)
     np.testing.assert_array_equal(s, s_ref)
     np.testing.assert_array_equal(d, d_ref)
 
 
 class Fp4Case:
-    """Attention problem whose Q and K are quantized to MXFP4 (ROW32) and V to MXFP8 COL32."""
+    """Attention problem whose Q and K are quantized to MXFP4 or MXFP6 (ROW32) and V to MXFP8 COL32."""
 
-    def __init__(self, seed, lens_q, lens_k=None, H=2, causal=False):
-        self.H, self.causal = H, causal
+    def __init__(self, seed, lens_q, lens_k=None, H=2, causal=False, fmt="e2m1"):
+        self.H, self.causal, self.fmt = H, causal, fmt
         self.lens_q, self.lens_k = list(lens_q), list(lens_k or lens_q)
         self.cu_q, self.cu_k = synth.cu_seqlens(self.lens_q), synth.cu_seqlens(self.lens_k)
         self.Tq, self.Tk = int(self.cu_q[-1]), int(self.cu_k[-1])
@@ -105,12 +133,14 @@ class Fp4Case:
     def run_gpu(self, p_scale=mx.P_STATIC):
         cq, ck = cu_dev(self.cu_q), cu_dev(self.cu_k)
         qd, kd, vd = to_dev_bf16(self.q), to_dev_bf16(self.k), to_dev_bf16(self.v)
-        q4, qs = mx.quantize_e2m1(qd)
-        k4, ks = mx.quantize_e2m1(kd)
+        quant = mx.quantize_e2m1 if self.fmt == "e2m1" else mx.quantize_e2m3
+        elem = mx.E2M1 if self.fmt == "e2m1" else mx.E2M3
+        q4, qs = quant(qd)
+        k4, ks = quant(kd)
         qsp = qs if all(L % 128 == 0 for L in self.lens_q) else gpu_scale_scatter(qs, self.cu_q, cq, self.C, mx.ROW32)
         ksp = ks if all(L % 128 == 0 for L in self.lens_k) else gpu_scale_scatter(ks, self.cu_k, ck, self.C, mx.ROW32)
         gv = gpu_quantize_padded(vd, self.cu_k, ck, mx.COL32)
-        args = mx.AttnArgs(mx.MxOperand(q4, qsp, mx.ROW32, mx.E2M1), mx.MxOperand(k4, ksp, mx.ROW32, mx.E2M1),
+        args = mx.AttnArgs(mx.MxOperand(q4, qsp, mx.ROW32, elem), mx.MxOperand(k4, ksp, mx.ROW32, elem),
                            mx.MxOperand(gv[0], gv[1], mx.COL32), cq, ck, len(self.lens_q), max(self.lens_q),
                            max(self.lens_k), self.Tq, self.Tk, self.H, 128, self.c, self.causal)
         o, lse = Guarded((self.Tq, self.C), torch.bfloat16), Guarded((self.H, self.Tq), torch.float32)
@@ -124,12 +154,13 @@ class Fp4Case:
         return to_host_bf16_bits(o.t), lse.t.cpu().numpy()
 
     def run_oracle(self, p_scale=oracle.P_STATIC):
-        q4, qs = mxfp4.quantize_row32(self.q)
-        k4, ks = mxfp4.quantize_row32(self.k)
+        mod = FORMATS[self.fmt][2]
+        q4, qs = mod.quantize_row32(self.q)
+        k4, ks = mod.quantize_row32(self.k)
         v8, vs, _ = oracle.quantize(self.v, self.cu_k, oracle.COL32)
         self.q4_ref, self.k4_ref = q4, k4
-        return mxfp4.attn_fwd_qk_fp4(q4, qs, k4, ks, v8, vs, self.cu_q, self.cu_k, self.H, 128, self.c, self.causal,
-                                     p_scale=p_scale)
+        fwd = mxfp4.attn_fwd_qk_fp4 if self.fmt == "e2m1" else mxfp6.attn_fwd_qk_fp6
+        return fwd(q4, qs, k4, ks, v8, vs, self.cu_q, self.cu_k, self.H, 128, self.c, self.causal, p_scale=p_scale)
 
 
 FWD_CASES = [
@@ -141,10 +172,11 @@ FWD_CASES = [
 ]
 
 
+@pytest.mark.parametrize("fmt", ["e2m1", "e2m3"])
 @pytest.mark.parametrize("label,seed,lq,lk,H,causal,p_scale", FWD_CASES, ids=[c[0] for c in FWD_CASES])
-def test_fwd_mxfp4_qk_parity(label, seed, lq, lk, H, causal, p_scale):
-    say(f"MXFP4 forward case {label}: seed {seed}, lengths {lq} / {lk or lq}, H={H}, causal={causal}")
-    case = Fp4Case(seed, lq, lk, H, causal)
+def test_fwd_small_qk_parity(label, seed, lq, lk, H, causal, p_scale, fmt):
+    say(f"{fmt} Q/K forward case {label}: seed {seed}, lengths {lq} / {lk or lq}, H={H}, causal={causal}")
+    case = Fp4Case(seed, lq, lk, H, causal, fmt)
     o_g, lse_g = case.run_gpu(p_scale)
     _, o32, lse = case.run_oracle(oracle.P_STATIC if p_scale == mx.P_STATIC else oracle.P_DYNAMIC)
     np.testing.assert_array_equal(case.q4_gpu, case.q4_ref)
@@ -156,24 +188,30 @@ def sqnr_db(x, ref):
     return 10.0 * math.log10(float(np.sum(ref * ref)) / float(np.sum((x - ref) ** 2)))
 
 
-def test_fwd_mxfp4_sqnr_next_to_mxfp8():
-    """O's SQNR against exact attention for Q/K in MXFP4 and in MXFP8 (same inputs, V E4M3 COL32 in both):
-    the GPU's value matches the oracle's replay within 0.25 dB in both formats."""
+def test_fwd_small_qk_sqnr_next_to_mxfp8():
+    """O's SQNR against exact attention for Q/K in MXFP4, MXFP6 and MXFP8 (same inputs, V E4M3 COL32 in
+    all): the GPU's value matches the oracle's replay within 0.25 dB in each format."""
     case = Fp4Case(56, [1024, 1024], None, 2, False)
     o_g, _ = case.run_gpu()
     o16_ref, _, _ = case.run_oracle()
+    c6 = Fp4Case(56, [1024, 1024], None, 2, False, "e2m3")
+    o6_g, _ = c6.run_gpu()
+    o6_ref, _, _ = c6.run_oracle()
     f = {n: bf16_bits_to_f64(getattr(case, n)) for n in ("q", "k", "v")}
     _, ex, _ = oracle.attn_fwd_f64(f["q"], f["k"], f["v"], case.cu_q, case.cu_k, case.H, 128, case.c, False,
                                    quant_p=False)
     ex = ex.astype(np.float64)
     s4_gpu, s4_orc = sqnr_db(bf16_bits_to_f64(o_g), ex), sqnr_db(bf16_bits_to_f64(o16_ref), ex)
+    s6_gpu, s6_orc = sqnr_db(bf16_bits_to_f64(o6_g), ex), sqnr_db(bf16_bits_to_f64(o6_ref), ex)
     # the MXFP8 forward on the same inputs (Q, K ROW32)
     from mx_cases import AttnCase
     c8 = AttnCase(56, [1024, 1024], H=2, fwd_modes="infer")
     o8_g, _ = c8.run_gpu_fwd()
     o8_ref, _, _ = c8.run_oracle_fwd()
     s8_gpu, s8_orc = sqnr_db(bf16_bits_to_f64(o8_g), ex), sqnr_db(bf16_bits_to_f64(o8_ref), ex)
-    say(f"O SQNR vs exact: Q/K MXFP4 {s4_gpu:.2f} dB (oracle {s4_orc:.2f}), Q/K MXFP8 {s8_gpu:.2f} dB "
-        f"(oracle {s8_orc:.2f})")
-    assert abs(s4_gpu - s4_orc) <= 0.25 and abs(s8_gpu - s8_orc) <= 0.25
-    assert s8_gpu > s4_gpu  # fewer mantissa bits cost accuracy
+    say(f"O SQNR vs exact: Q/K MXFP4 {s4_gpu:.2f} dB (oracle {s4_orc:.2f}), Q/K MXFP6 {s6_gpu:.2f} dB "
+        f"(oracle {s6_orc:.2f}), Q/K MXFP8 {s8_gpu:.2f} dB (oracle {s8_orc:.2f})")
+    assert abs(s4_gpu - s4_orc) <= 0.25 and abs(s6_gpu - s6_orc) <= 0.25 and abs(s8_gpu - s8_orc) <= 0.25
+    # E2M3 keeps E4M3's three mantissa bits (only the exponent range shrinks, which a 32-element block
+    # of N(0,1) values hardly uses): MXFP6 Q/K lands within 1 dB of MXFP8; E2M1's single bit costs ~9 dB
+    assert abs(s6_gpu - s8_gpu) < 1.0 and min(s6_gpu, s8_gpu) > s4_gpu + 5.0
