@@ -67,7 +67,8 @@ typedef enum {
 /* Element format of an MX payload. E4M3 (MXFP8) everywhere; for the forward's q and k only, in ROW32
  * blocks, also E2M1 (MXFP4: two elements per byte, element 2i in the low nibble of byte i, magnitudes
  * 0, 0.5, 1, 1.5, 2, 3, 4, 6) or E2M3 (MXFP6: a block's 32 six-bit codes in 24 bytes, code j at bits
- * 6j..6j+5 of a little-endian bit string; magnitudes f/8 below 1, then 2^e (1 + f/8) up to 7.5)
+ * 6j..6j+5 of a little-endian bit string, blocks in pairs as mxfa_quantize_e2m3 describes; magnitudes
+ * f/8 below 1, then 2^e (1 + f/8) up to 7.5)
  * [brifing.si "Future directions": MXFP6 and MXFP4 as the next precisions; TC paragraph 1: the
  * block-scaled matrix units run MXFP8, MXFP6 and MXFP4]. */
 typedef enum { MXFA_E4M3 = 0, MXFA_E2M1 = 1, MXFA_E2M3 = 2 } mxfa_elem;
@@ -138,8 +139,11 @@ mxfa_status mxfa_quantize_e2m1(const uint16_t* x, int64_t ld_x, int64_t T, int C
  * [brifing.si "Future directions"]: scale code e = clamp(exponent_field(amax) - 2, 0, 254) (7.5 =
  * 1.875 * 2^2), 255 for NaN/Inf blocks; element = the E2M3 magnitude nearest to |x| * 2^(127-e), ties
  * to the even code, saturating at 7.5, with x's sign bit (NaN blocks: payload 0).
- *   data_out  : [T, 3C/4] payload, block b of a row at bytes 24b .. 24b + 23 (code j of the block at
- *               bits 6j .. 6j + 5, little-endian)
+ *   C         : columns, a multiple of 64
+ *   data_out  : [T, 3C/4] payload. A block's codes form a 24-byte little-endian bit string (code j at
+ *               bits 6j .. 6j + 5); the blocks of a row go in pairs (2p, 2p + 1) of 48 bytes at 48p:
+ *               bytes 0-15 of block 2p, bytes 0-15 of block 2p + 1, bytes 16-23 of block 2p, bytes
+ *               16-23 of block 2p + 1 (each block one 16-byte and one 8-byte piece)
  *   scale_out : [T][C/32]; other arguments as mxfa_quantize_e2m1. */
 mxfa_status mxfa_quantize_e2m3(const uint16_t* x, int64_t ld_x, int64_t T, int C, uint8_t* data_out,
                                uint8_t* scale_out, void* stream);

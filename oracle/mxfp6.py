@@ -15,7 +15,10 @@ ones, as for MXFP8 (kongchang.com, "Why MXFP8") and MXFP4 (mxfp4.py):
   * Element: the magnitude nearest to |x| * 2^(127 - code), ties to the even code, saturated at 7.5;
     the sign bit is x's sign bit. A NaN block's payload is 0.
 Layout: a block's 32 six-bit codes fill 24 bytes as one little-endian bit string (code j at bits
-6j .. 6j + 5), blocks in order along the row: payload [T, 3 C / 4], scales [T, C / 32] (ROW32).
+6j .. 6j + 5); the blocks of a row go in pairs (2p, 2p + 1), 48 bytes per pair: bytes 0-15 of block 2p,
+bytes 0-15 of block 2p + 1, bytes 16-23 of block 2p, bytes 16-23 of block 2p + 1 (so that each block
+is one 16-byte piece and one 8-byte piece). Payload [T, 3 C / 4] (C a multiple of 64), scales
+[T, C / 32] (ROW32).
 """
 import numpy as np
 
@@ -86,12 +89,18 @@ def unpack_block(b):
     return [(bits >> (6 * j)) & 0x3F for j in range(32)]
 
 
+def block_bytes(b):
+    """Byte positions, in a row's payload, of block b's 24-byte bit string (in bit-string order)."""
+    p, a = divmod(b, 2)
+    return list(range(48 * p + 16 * a, 48 * p + 16 * a + 16)) + list(range(48 * p + 32 + 8 * a, 48 * p + 40 + 8 * a))
+
+
 def quantize_row32(x_bf16):
-    """x_bf16: uint16 bf16 bits [T, C], C a multiple of 32. Returns (payload uint8 [T, 3C/4],
+    """x_bf16: uint16 bf16 bits [T, C], C a multiple of 64. Returns (payload uint8 [T, 3C/4],
     scale uint8 [T, C/32])."""
     x = _bf16_to_f64(x_bf16)
     T, C = x.shape
-    assert C % 32 == 0
+    assert C % 64 == 0
     data = np.zeros((T, 3 * C // 4), np.uint8)
     scale = np.zeros((T, C // 32), np.uint8)
     for t in range(T):
@@ -100,7 +109,7 @@ def quantize_row32(x_bf16):
             code = scale_code(blk)
             scale[t, b] = code
             if code != 255:  # a NaN block keeps payload 0
-                data[t, 24 * b:24 * b + 24] = pack_block(e2m3_encode_array(blk * 2.0 ** (127 - code)))
+                data[t, block_bytes(b)] = pack_block(e2m3_encode_array(blk * 2.0 ** (127 - code)))
     return data, scale
 
 
@@ -111,7 +120,7 @@ def dequantize_row32(data, scale):
     for t in range(T):
         for b in range(C // 32):
             code = int(scale[t, b])
-            codes = unpack_block(data[t, 24 * b:24 * b + 24])
+            codes = unpack_block(data[t, block_bytes(b)])
             out[t, 32 * b:32 * b + 32] = (np.nan if code == 255 else
                                          np.array([e2m3_value(c) for c in codes]) * 2.0 ** (code - 127))
     return out

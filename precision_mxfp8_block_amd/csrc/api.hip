@@ -274,7 +274,7 @@ mxfa_status mxfa_quantize_e2m3(const uint16_t* x, int64_t ld_x, int64_t T, int C
                                uint8_t* scale_out, void* stream) {
   const char* fn = "mxfa_quantize_e2m3";
   if (T < 0) return fail(MXFA_ERR_INVALID, "%s: T=%lld < 0", fn, (long long)T);
-  if (C <= 0 || C % 32) return fail(MXFA_ERR_INVALID, "%s: C=%d must be a positive multiple of 32", fn, C);
+  if (C <= 0 || C % 64) return fail(MXFA_ERR_INVALID, "%s: C=%d must be a positive multiple of 64", fn, C);
   if (ld_x < C || ld_x % 8) return fail(MXFA_ERR_INVALID, "%s: ld_x=%lld must be >= C and a multiple of 8", fn, (long long)ld_x);
   if (!x || !data_out || !scale_out) return fail(MXFA_ERR_INVALID, "%s: NULL x/data_out/scale_out", fn);
   if (!aligned(x, 16) || !aligned(data_out, 16) || !aligned(scale_out, 16))

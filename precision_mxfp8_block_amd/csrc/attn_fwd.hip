@@ -144,7 +144,8 @@ __device__ __forceinline__ uint32_t undef_word() {
 }
 
 // QKF: the element format of Q and K, as the scaled MFMA's format code: 0 E4M3; 4 E2M1 (MXFP4, two
-// elements per byte); 2 E2M3 (MXFP6, a block's 32 codes in 24 bytes). Both low-precision forms run
+// elements per byte); 2 E2M3 (MXFP6, a block's 32 codes in 24 bytes, the two blocks of each 64-element
+// d-step stored as their two 16-byte pieces, then their two 8-byte pieces). Both low-precision forms run
 // S at twice the FP8 rate with ROW32 scales; a lane's operand is then the 32 elements of one d-block
 // (16 or 24 bytes). The MXFP4 K tile takes 64 bytes per key: LDS row R of the K stage holds keys 2R
 // (logical chunks 0-3) and 2R + 1 (chunks 4-7). The MXFP6 K tile keeps one key per 128-byte row
@@ -257,13 +258,11 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
         // FP4: the lane's 32 elements of d-block 2 ds + hh, 16 bytes (the upper operand half unused)
         if (valid) lo = *reinterpret_cast<const uint4*>(src + 32 * ds + 16 * hh);
       } else if constexpr (QK6) {
-        // FP6: the 24 bytes of d-block 2 ds + hh (registers 0-5)
+        // FP6: the 24 bytes of d-block 2 ds + hh (registers 0-5): its 16-byte piece, then its 8-byte one
         if (valid) {
-          const uint2 a0 = *reinterpret_cast<const uint2*>(src + 48 * ds + 24 * hh);
-          const uint2 a1 = *reinterpret_cast<const uint2*>(src + 48 * ds + 24 * hh + 8);
-          const uint2 a2 = *reinterpret_cast<const uint2*>(src + 48 * ds + 24 * hh + 16);
-          lo = make_uint4(a0.x, a0.y, a1.x, a1.y);
-          hi = make_uint4(a2.x, a2.y, 0u, 0u);
+          lo = *reinterpret_cast<const uint4*>(src + 48 * ds + 16 * hh);
+          const uint2 t8 = *reinterpret_cast<const uint2*>(src + 48 * ds + 32 + 8 * hh);
+          hi = make_uint4(t8.x, t8.y, 0u, 0u);
         }
       } else if (valid) {
         lo = *reinterpret_cast<const uint4*>(src + 64 * ds + 16 * hh);
@@ -328,19 +327,17 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
   //  * scales: K scale word 32 kb + r; V scale byte 128 (2 ks + hh) + (COL32: 32 db + r, SQ32: db).
   //  * QK4 K rows: key 32 kb + r is in LDS row 16 kb + r / 2 (its swizzle does not depend on kb),
   //    logical chunk 4 (r % 2) + 2 ds + hh: the 32 elements of d-block 2 ds + hh;
-  //  * QK6 K rows: key row r, the 24 bytes of d-block 2 ds + hh as three 8-byte reads at logical bytes
-  //    48 ds + 24 hh + 8 i, each inside one 16-byte chunk (koffs6);
+  //  * QK6 K rows: key row r, the 24 bytes of d-block 2 ds + hh: logical chunk 3 ds + hh (16 bytes)
+  //    and the half hh of logical chunk 3 ds + 2 (8 bytes) (koffs6);
   uint32_t koffs[2][2];
-  uint32_t koffs6[2][3];
+  uint32_t koffs6[2][2];
   if constexpr (QK6) {
     const int sw = swz(r);
 #pragma unroll
-    for (int ds = 0; ds < 2; ++ds)
-#pragma unroll
-      for (int i = 0; i < 3; ++i) {
-        const int o = 48 * ds + 24 * hh + 8 * i;
-        koffs6[ds][i] = (uint32_t)(r * kD + 16 * ((o >> 4) ^ sw) + (o & 15));
-      }
+    for (int ds = 0; ds < 2; ++ds) {
+      koffs6[ds][0] = (uint32_t)(r * kD + 16 * ((3 * ds + hh) ^ sw));
+      koffs6[ds][1] = (uint32_t)(r * kD + 16 * ((3 * ds + 2) ^ sw) + 8 * hh);
+    }
   }
   if constexpr (QK4) {
     const int R = r >> 1, sw = swz(R);
@@ -389,10 +386,9 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
         mx_v8i ka;
         if constexpr (QK6) {
           const MX_LDS uint8_t* t = lds + lds_k_off(sk) + 32 * kb * kD;
-          const mx_v2i a0 = *(const MX_LDS mx_v2i*)(t + koffs6[ds][0]);
-          const mx_v2i a1 = *(const MX_LDS mx_v2i*)(t + koffs6[ds][1]);
-          const mx_v2i a2 = *(const MX_LDS mx_v2i*)(t + koffs6[ds][2]);
-          ka = mx_v8i{a0.x, a0.y, a1.x, a1.y, a2.x, a2.y, 0, 0};
+          const mx_v4i a16 = *(const MX_LDS mx_v4i*)(t + koffs6[ds][0]);
+          const mx_v2i a8 = *(const MX_LDS mx_v2i*)(t + koffs6[ds][1]);
+          ka = mx_v8i{a16.x, a16.y, a16.z, a16.w, a8.x, a8.y, 0, 0};
         } else {
           const MX_LDS uint8_t* t = lds + lds_k_off(sk) + 32 * kb * kQKBytes;
           const mx_v4i lo = *(const MX_LDS mx_v4i*)(t + koffs[ds][0]);

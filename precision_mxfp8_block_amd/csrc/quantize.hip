@@ -106,7 +106,10 @@ __global__ void __launch_bounds__(256) quantize_row32_e2m1_kernel(const uint16_t
 // ROW32 in MXFP6: E2M3 elements (OCP MX: f/8 below 1, then 2^e (1 + f/8) up to 7.5) with the scale
 // code clamp(exponent_field(amax) - 2, 0, 254); 255 and a zero payload for blocks holding NaN or Inf.
 // A block's 32 six-bit codes form a 24-byte little-endian bit string (code j at bits 6j .. 6j + 5).
-// Two lanes share a block, 16 bf16 each; a lane writes its 12 bytes (bits 96 h .. 96 h + 95).
+// Blocks go in pairs (2p, 2p + 1) of 48 bytes: bytes 0-15 of block 2p, bytes 0-15 of block 2p + 1,
+// then the two blocks' bytes 16-23, so that a block is one 16-byte and one 8-byte piece (the forward
+// reads an FP6 operand as exactly these two pieces). Two lanes share a block, 16 bf16 each; lane h
+// has the block's bytes 12 h .. 12 h + 11.
 // ---------------------------------------------------------------------------------------------
 // Nearest E2M3 code of v (already scaled), ties to the even code, saturating at 7.5, sign kept: below
 // 1 the step is 1/8 (q = rne(8 a) is the code; q = 8 is 1.0, the first normal); in binade [2^e,
@@ -156,10 +159,17 @@ __global__ void __launch_bounds__(256) quantize_row32_e2m3_kernel(const uint16_t
       if ((bit & 31) > 26) o[(bit >> 5) + 1] |= c >> (32 - (bit & 31));
     }
   }
-  uint32_t* dst = reinterpret_cast<uint32_t*>(data + t * (3 * (int64_t)C / 4) + (int64_t)j * 12);
-  dst[0] = o[0];
-  dst[1] = o[1];
-  dst[2] = o[2];
+  const int blk = j >> 1, pair = blk >> 1, odd = blk & 1;
+  uint8_t* row = data + t * (3 * (int64_t)C / 4) + 48 * pair;
+  if ((j & 1) == 0) {  // block bytes 0-11: the start of the 16-byte piece
+    uint32_t* dst = reinterpret_cast<uint32_t*>(row + 16 * odd);
+    dst[0] = o[0];
+    dst[1] = o[1];
+    dst[2] = o[2];
+  } else {  // bytes 12-15 end the 16-byte piece, bytes 16-23 are the 8-byte piece
+    *reinterpret_cast<uint32_t*>(row + 16 * odd + 12) = o[0];
+    *reinterpret_cast<uint2*>(row + 32 + 8 * odd) = make_uint2(o[1], o[2]);
+  }
   if ((j & 1) == 0) scale[t * (C >> 5) + (j >> 1)] = (uint8_t)code;
 }
 

@@ -133,6 +133,11 @@ def test_quantize_e2m1_argument_errors(kw, expect):
         assert st == expect and _last() != ""
 
 
+def test_quantize_e2m3_needs_block_pairs():
+    # the MXFP6 payload stores blocks in pairs: C must be a multiple of 64 (96 is fine for MXFP4)
+    assert _lib().mxfa_quantize_e2m3(P, 96, 256, 96, P, P, 0) == INVALID and "64" in _last()
+
+
 def test_fwd_null_outputs():
     a = _args()
     assert _lib().mxfa_fwd(ctypes.byref(a), 0, P, 0) == INVALID

@@ -2,7 +2,7 @@
 format's definition fixes (OCP MX specification; the pages name MXFP6 with MXFP4 as the next
 precisions: brifing.si "Future directions", theclarity.today paragraph 1): the magnitude grid written
 out from the format's binades, brute-force nearest rounding with ties to even, saturation, the scale
-rule, the 6-bit packing of a hand-built block, and the round-trip bound."""
+rule, the 6-bit packing and pair layout of a hand-built row, and the round-trip bound."""
 import numpy as np
 
 import synth
@@ -57,7 +57,7 @@ def bf16(vals):
 
 def test_scale_rule():
     for amax, code in ((7.5, 127), (4.0, 127), (1.0, 125), (3.0, 126), (2.0 ** -100, 25)):
-        x = np.zeros((1, 32), np.float32)
+        x = np.zeros((1, 64), np.float32)
         x[0, 9] = amax
         _, s = m.quantize_row32(bf16(x))
         assert s[0, 0] == code, (amax, s[0, 0])
@@ -65,19 +65,28 @@ def test_scale_rule():
         x = bf16(np.ones((1, 64), np.float32))
         x[0, 33] = bad
         d, s = m.quantize_row32(x)
-        assert s[0, 1] == 255 and not d[0, 24:].any() and s[0, 0] == 125
+        # block 1's bytes in the pair layout: 16-31 and 40-47
+        assert s[0, 1] == 255 and not d[0, 16:32].any() and not d[0, 40:48].any() and s[0, 0] == 125
 
 
 def test_hand_built_block_packing():
-    # amax 3.75 (exponent field 128) -> code 126, scale 2^-1: x = 1 -> 2.0 (code 16), -0.1875 -> -0.375
-    # (32 | 3), 3.75 -> 7.5 (31), 0.5 -> 1.0 (8), the rest 0. Bits: 16 | (35 << 6) | (31 << 12) | (8 << 18)
-    x = np.zeros((1, 32), np.float32)
+    # block 0: amax 3.75 (exponent field 128) -> code 126, scale 2^-1: x = 1 -> 2.0 (code 16), -0.1875 ->
+    # -0.375 (32 | 3), 3.75 -> 7.5 (31), 0.5 -> 1.0 (8), the rest 0: bits 16 | (35 << 6) | (31 << 12) |
+    # (8 << 18). Block 1: x[63] = 4 (code 127, scale 1) -> code 24 at bits 186..191 (byte 23: 24 << 2).
+    # Pair layout: bytes 0-15 block 0, 16-31 block 1, 32-39 block 0's bytes 16-23, 40-47 block 1's.
+    x = np.zeros((1, 64), np.float32)
     x[0, :4] = [1.0, -0.1875, 3.75, 0.5]
+    x[0, 63] = 4.0
     d, s = m.quantize_row32(bf16(x))
-    assert s[0, 0] == 126
-    bits = 16 | (35 << 6) | (31 << 12) | (8 << 18)
-    np.testing.assert_array_equal(d[0], np.frombuffer(bits.to_bytes(24, "little"), np.uint8))
-    np.testing.assert_array_equal(m.dequantize_row32(d, s)[0, :4], [1.0, -0.1875, 3.75, 0.5])
+    assert list(s[0]) == [126, 127]
+    b0 = np.frombuffer((16 | (35 << 6) | (31 << 12) | (8 << 18)).to_bytes(24, "little"), np.uint8)
+    b1 = np.frombuffer((24 << 186).to_bytes(24, "little"), np.uint8)
+    want = np.concatenate([b0[:16], b1[:16], b0[16:], b1[16:]])
+    np.testing.assert_array_equal(d[0], want)
+    assert d[0, 47] == 24 << 2 and not d[0, 16:32].any()
+    y = m.dequantize_row32(d, s)[0]
+    np.testing.assert_array_equal(y[:4], [1.0, -0.1875, 3.75, 0.5])
+    assert y[63] == 4.0 and not y[4:63].any()
 
 
 def test_round_trip_error_bound():
