@@ -12,6 +12,20 @@
 
 namespace {
 
+// Row t and position j in the row of the flat lane index u (u < rows * per_row, the row length in
+// lanes): a 32-bit division when the whole index space fits in 32 bits (a uniform branch on kernel
+// arguments), the 64-bit one otherwise.
+__device__ __forceinline__ void split_flat_index(int64_t u, int64_t per_row, int64_t total, int64_t& t, int& j) {
+  if (total <= (int64_t)0xffffffffu) {
+    const uint32_t q = (uint32_t)u / (uint32_t)per_row;
+    t = q;
+    j = (int)((uint32_t)u - q * (uint32_t)per_row);
+  } else {
+    t = u / per_row;
+    j = (int)(u - t * per_row);
+  }
+}
+
 // ---------------------------------------------------------------------------------------------
 // ROW32: 1 x 32 blocks along the columns. Two lanes share a block, 16 bf16 each (two 16-byte loads).
 // ---------------------------------------------------------------------------------------------
@@ -20,9 +34,11 @@ __global__ void __launch_bounds__(256) quantize_row32_kernel(const uint16_t* __r
                                                              uint8_t* __restrict__ scale) {
   const int64_t chunks_per_row = C >> 4;
   const int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (u >= T * chunks_per_row) return;  // pairs of lanes leave together (chunks_per_row is even)
-  const int64_t t = u / chunks_per_row;
-  const int j = (int)(u - t * chunks_per_row);
+  const int64_t total = T * chunks_per_row;
+  if (u >= total) return;  // pairs of lanes leave together (chunks_per_row is even)
+  int64_t t;
+  int j;
+  split_flat_index(u, chunks_per_row, total, t, j);
   const uint4* src = reinterpret_cast<const uint4*>(x + t * ld_x + (int64_t)j * 16);
   uint4 a = src[0], b = src[1];
   uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
@@ -53,30 +69,35 @@ __global__ void __launch_bounds__(256) quantize_row32_kernel(const uint16_t* __r
 }
 
 // ---------------------------------------------------------------------------------------------
-// ROW32 in MXFP4: E2M1 elements (OCP MX: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6) with the scale code
-// clamp(exponent_field(amax) - 2, 0, 254), 2 being the exponent of E2M1's largest magnitude; 255 and
-// a zero payload for blocks holding NaN or Inf. Two lanes share a block, 16 bf16 each; a lane writes
-// 8 bytes (element 2i in the low nibble of byte i).
+// ROW32 in MXFP4 and MXFP6 (OCP MX element formats E2M1 and E2M3, both with largest exponent 2): the
+// scale code is clamp(exponent_field(amax) - 2, 0, 254); 255 and a zero payload for blocks holding
+// NaN or Inf. The elements come from gfx950's scaled conversions, which take the E8M0 scale as the
+// exponent field of a float (code << 23, so code 0 is 2^-127) and give the nearest code of x / 2^(code
+// - 127): ties to the even code, saturating at the largest magnitude (6 and 7.5), the sign kept for
+// values that round to zero, bf16 subnormals exact. Measured on the device at every midpoint of both
+// grids, on saturating values, signed zeros and subnormal inputs with code 0.
 // ---------------------------------------------------------------------------------------------
-// Nearest E2M1 code of v (already scaled), ties to the even code, saturating at 6, sign kept: the
-// magnitude code counts the midpoints between consecutive magnitudes that |v| passes, a midpoint
-// whose upper neighbour has the even code (0.75, 1.75, 3.5) counting when reached, the others
-// (0.25, 1.25, 2.5, 5) when exceeded.
-__device__ __forceinline__ uint32_t e2m1_code(float v) {
-  const float a = fabsf(v);
-  const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
-  return c | ((__float_as_uint(v) >> 28) & 8u);
+__device__ __forceinline__ float e8m0_as_scale(uint32_t code) { return __uint_as_float(code << 23); }
+
+// Byte SEL of `old` <- the E2M1 codes of the two bf16 in w (low half -> low nibble).
+template <int SEL>
+__device__ __forceinline__ uint32_t e2m1_pair(uint32_t old, uint32_t w, float sc) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, __uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u),
+                                                  sc, SEL);
 }
 
+// MXFP4: two lanes share a block, 16 bf16 each; a lane writes 8 bytes (element 2i in the low nibble of
+// byte i).
 __global__ void __launch_bounds__(256) quantize_row32_e2m1_kernel(const uint16_t* __restrict__ x, int64_t ld_x,
                                                                   int64_t T, int C, uint8_t* __restrict__ data,
                                                                   uint8_t* __restrict__ scale) {
   const int64_t chunks_per_row = C >> 4;
   const int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (u >= T * chunks_per_row) return;  // pairs of lanes leave together (chunks_per_row is even)
-  const int64_t t = u / chunks_per_row;
-  const int j = (int)(u - t * chunks_per_row);
+  const int64_t total = T * chunks_per_row;
+  if (u >= total) return;  // pairs of lanes leave together (chunks_per_row is even)
+  int64_t t;
+  int j;
+  split_flat_index(u, chunks_per_row, total, t, j);
   const uint4* src = reinterpret_cast<const uint4*>(x + t * ld_x + (int64_t)j * 16);
   const uint4 a = src[0], b = src[1];
   const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
@@ -88,89 +109,75 @@ __global__ void __launch_bounds__(256) quantize_row32_e2m1_kernel(const uint16_t
   const uint32_t code = e >= 255u ? 255u : (e > 2u ? e - 2u : 0u);
   uint2 out = make_uint2(0u, 0u);
   if (code != 255u) {
-    const float inv = mx_inv_scale(code);
-    uint32_t o[2] = {0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t lo = e2m1_code(bf16_to_f32(w[i] & 0xffffu) * inv);
-      const uint32_t hi = e2m1_code(bf16_to_f32(w[i] >> 16) * inv);
-      o[i >> 2] |= (lo | (hi << 4)) << (8 * (i & 3));
-    }
-    out = make_uint2(o[0], o[1]);
+    const float sc = e8m0_as_scale(code);
+    uint32_t o0 = e2m1_pair<0>(0u, w[0], sc), o1 = e2m1_pair<0>(0u, w[4], sc);
+    o0 = e2m1_pair<1>(o0, w[1], sc);
+    o1 = e2m1_pair<1>(o1, w[5], sc);
+    o0 = e2m1_pair<2>(o0, w[2], sc);
+    o1 = e2m1_pair<2>(o1, w[6], sc);
+    o0 = e2m1_pair<3>(o0, w[3], sc);
+    o1 = e2m1_pair<3>(o1, w[7], sc);
+    out = make_uint2(o0, o1);
   }
   *reinterpret_cast<uint2*>(data + t * (C >> 1) + (int64_t)j * 8) = out;
   if ((j & 1) == 0) scale[t * (C >> 5) + (j >> 1)] = (uint8_t)code;
 }
 
-// ---------------------------------------------------------------------------------------------
-// ROW32 in MXFP6: E2M3 elements (OCP MX: f/8 below 1, then 2^e (1 + f/8) up to 7.5) with the scale
-// code clamp(exponent_field(amax) - 2, 0, 254); 255 and a zero payload for blocks holding NaN or Inf.
-// A block's 32 six-bit codes form a 24-byte little-endian bit string (code j at bits 6j .. 6j + 5).
-// Blocks go in pairs (2p, 2p + 1) of 48 bytes: bytes 0-15 of block 2p, bytes 0-15 of block 2p + 1,
+// MXFP6: a block's 32 six-bit codes form a 24-byte little-endian bit string (code j at bits 6j .. 6j +
+// 5). Blocks go in pairs (2p, 2p + 1) of 48 bytes: bytes 0-15 of block 2p, bytes 0-15 of block 2p + 1,
 // then the two blocks' bytes 16-23, so that a block is one 16-byte and one 8-byte piece (the forward
-// reads an FP6 operand as exactly these two pieces). Two lanes share a block, 16 bf16 each; lane h
-// has the block's bytes 12 h .. 12 h + 11.
-// ---------------------------------------------------------------------------------------------
-// Nearest E2M3 code of v (already scaled), ties to the even code, saturating at 7.5, sign kept: below
-// 1 the step is 1/8 (q = rne(8 a) is the code; q = 8 is 1.0, the first normal); in binade [2^e,
-// 2^(e+1)), e = 0..2, the step is 2^(e-3) and the code (e + 1) 8 + rne(a 2^(3-e)) - 8 (a rounding up
-// to the next binade gives that binade's first code); codes past 31 (a >= 7.75) saturate.
-__device__ __forceinline__ uint32_t e2m3_code(float v) {
-  const float a = fabsf(v);
-  uint32_t c;
-  if (a < 1.0f) {
-    c = (uint32_t)__builtin_rintf(a * 8.0f);
-  } else if (a >= 8.0f) {
-    c = 31u;
-  } else {
-    const int e = (int)(__float_as_uint(a) >> 23) - 127;  // 0, 1 or 2
-    const float q = __builtin_rintf(a * __uint_as_float((uint32_t)(130 - e) << 23));  // a 2^(3-e)
-    c = min((uint32_t)((e + 1) * 8) + (uint32_t)q - 8u, 31u);
-  }
-  return c | ((__float_as_uint(v) >> 26) & 32u);
-}
+// reads an FP6 operand as exactly these two pieces). One lane per block: four 16-byte loads, the block
+// maximum in the lane, one conversion of all 32 elements, one 16-byte and one 8-byte store.
+// The conversion (v_cvt_scalef32_2xpk16_fp6_f32) takes its first source as the even elements and its
+// second as the odd ones (code 2i from the first source's element i, code 2i + 1 from the second's),
+// measured on the device. It is written as inline asm with an early-clobber result: when the compiler
+// let the result registers start inside the first source (result at source register 2), the element in
+// the overwritten register came out wrong on the device, so the result must not overlap the sources.
+typedef int mx_v6i __attribute__((ext_vector_type(6)));
 
 __global__ void __launch_bounds__(256) quantize_row32_e2m3_kernel(const uint16_t* __restrict__ x, int64_t ld_x,
                                                                   int64_t T, int C, uint8_t* __restrict__ data,
                                                                   uint8_t* __restrict__ scale) {
-  const int64_t chunks_per_row = C >> 4;
+  const int64_t blocks_per_row = C >> 5;
   const int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (u >= T * chunks_per_row) return;  // pairs of lanes leave together (chunks_per_row is even)
-  const int64_t t = u / chunks_per_row;
-  const int j = (int)(u - t * chunks_per_row);
-  const uint4* src = reinterpret_cast<const uint4*>(x + t * ld_x + (int64_t)j * 16);
-  const uint4 a = src[0], b = src[1];
-  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  const int64_t total = T * blocks_per_row;
+  if (u >= total) return;
+  int64_t t;
+  int blk;
+  split_flat_index(u, blocks_per_row, total, t, blk);
+  const uint4* src = reinterpret_cast<const uint4*>(x + t * ld_x + (int64_t)blk * 32);
+  uint32_t w[16];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint4 v = src[q];
+    w[4 * q] = v.x;
+    w[4 * q + 1] = v.y;
+    w[4 * q + 2] = v.z;
+    w[4 * q + 3] = v.w;
+  }
   uint32_t amax = 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) amax = max(amax, max(w[i] & 0x7fffu, (w[i] >> 16) & 0x7fffu));
-  amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1, 64));
+  for (int i = 0; i < 16; ++i) amax = max(amax, max(w[i] & 0x7fffu, (w[i] >> 16) & 0x7fffu));
   const uint32_t e = amax >> 7;
   const uint32_t code = e >= 255u ? 255u : (e > 2u ? e - 2u : 0u);
-  uint32_t o[3] = {0u, 0u, 0u};
+  uint4 head = make_uint4(0u, 0u, 0u, 0u);
+  uint2 tail = make_uint2(0u, 0u);
   if (code != 255u) {
-    const float inv = mx_inv_scale(code);
+    mx_v16f even, odd;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const uint32_t h = (w[i >> 1] >> (16 * (i & 1))) & 0xffffu;
-      const uint32_t c = e2m3_code(bf16_to_f32(h) * inv);
-      const int bit = 6 * i;  // compile-time after unrolling
-      o[bit >> 5] |= c << (bit & 31);
-      if ((bit & 31) > 26) o[(bit >> 5) + 1] |= c >> (32 - (bit & 31));
+      even[i] = __uint_as_float(w[i] << 16);
+      odd[i] = __uint_as_float(w[i] & 0xffff0000u);
     }
+    mx_v6i r;
+    asm("v_cvt_scalef32_2xpk16_fp6_f32 %0, %1, %2, %3" : "=&v"(r) : "v"(even), "v"(odd), "v"(e8m0_as_scale(code)));
+    head = make_uint4((uint32_t)r[0], (uint32_t)r[1], (uint32_t)r[2], (uint32_t)r[3]);
+    tail = make_uint2((uint32_t)r[4], (uint32_t)r[5]);
   }
-  const int blk = j >> 1, pair = blk >> 1, odd = blk & 1;
-  uint8_t* row = data + t * (3 * (int64_t)C / 4) + 48 * pair;
-  if ((j & 1) == 0) {  // block bytes 0-11: the start of the 16-byte piece
-    uint32_t* dst = reinterpret_cast<uint32_t*>(row + 16 * odd);
-    dst[0] = o[0];
-    dst[1] = o[1];
-    dst[2] = o[2];
-  } else {  // bytes 12-15 end the 16-byte piece, bytes 16-23 are the 8-byte piece
-    *reinterpret_cast<uint32_t*>(row + 16 * odd + 12) = o[0];
-    *reinterpret_cast<uint2*>(row + 32 + 8 * odd) = make_uint2(o[1], o[2]);
-  }
-  if ((j & 1) == 0) scale[t * (C >> 5) + (j >> 1)] = (uint8_t)code;
+  uint8_t* pair = data + t * (3 * (int64_t)C / 4) + 48 * (blk >> 1);
+  *reinterpret_cast<uint4*>(pair + 16 * (blk & 1)) = head;
+  *reinterpret_cast<uint2*>(pair + 32 + 8 * (blk & 1)) = tail;
+  scale[t * blocks_per_row + blk] = (uint8_t)code;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -608,7 +615,7 @@ hipError_t launch_quantize_e2m1(const uint16_t* x, int64_t ld_x, int64_t T, int 
 
 hipError_t launch_quantize_e2m3(const uint16_t* x, int64_t ld_x, int64_t T, int C, uint8_t* data, uint8_t* scale,
                                hipStream_t stream) {
-  const int64_t units = T * (C >> 4);
+  const int64_t units = T * (C >> 5);
   if (units == 0) return hipSuccess;
   hipLaunchKernelGGL(quantize_row32_e2m3_kernel, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, stream, x, ld_x,
                      T, C, data, scale);

@@ -87,3 +87,20 @@ def test_quantize_sweep_bit_exact(mode):
         np.testing.assert_array_equal(scale_t.cpu().numpy(), st_ref)
     codes = np.unique(s_ref)
     say(f"  {codes.size} distinct codes from {codes.min()} to {codes.max()}, {np.unique(d_ref).size} distinct bytes")
+
+
+@pytest.mark.parametrize("fmt", ["e2m1", "e2m3"])
+def test_small_format_sweep_bit_exact(fmt):
+    """The same matrix through the MXFP4 and MXFP6 ROW32 quantizers: every bf16 pattern at the codes the
+    anchors fix for these formats (code = exponent field - 2), the saturation bands above 6 and 7.5 (the
+    blocks without anchor put their maxima anywhere in [4, 8) after scaling), subnormal inputs at code 0,
+    and the NaN/Inf blocks (code 255, payload 0)."""
+    from test_gpu_mxfp4 import FORMATS, gpu_quantize_small
+    x, _ = sweep_matrix()
+    say(f"{fmt} quantize sweep: {x.shape[0]} tokens x {C}")
+    d, s = gpu_quantize_small(to_dev_bf16(x), fmt)
+    d_ref, s_ref = FORMATS[fmt][2].quantize_row32(x)
+    np.testing.assert_array_equal(s, s_ref)
+    np.testing.assert_array_equal(d, d_ref)
+    codes = np.unique(s_ref)
+    say(f"  {codes.size} distinct codes from {codes.min()} to {codes.max()}, {np.unique(d_ref).size} distinct bytes")
