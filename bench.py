@@ -386,12 +386,26 @@ def bench_attention_workload(args, torch, mx, label, workload, lens_q, lens_k, H
     else:
         qop, rq = operand("q", qk_mode, Tq, nbq, Pq, cq_d, lens_q, jag_q)
         kop, rk = operand("k", qk_mode, Tk, nbk, Pk, ck_d, lens_k, jag_k)
-    vop, rv = operand("v", mx.COL32, Tk, nbk, Pk, ck_d, lens_k, jag_k)
-    runs = [rq, rk, rv]
-    if not fwd_only:
-        vdop, rvd = operand("v", mx.ROW32, Tk, nbk, Pk, ck_d, lens_k, jag_k)
+    def operand_v_both(T, nb, P, cu_d, lens, jag):
+        # V's COL32 payload (the forward's P V) and ROW32 payload (the backward's dP = dO V^T), one read
+        dcol, scol = u8(T, C), u8(*srows[mx.COL32][0](T, nb, P))
+        drow, srow = u8(T, C), u8(*srows[mx.ROW32][0](T, nb, P))
+        pcol = u8(*srows[mx.COL32][1](T, nb, P)) if jag else scol
+        prow = u8(*srows[mx.ROW32][1](T, nb, P)) if jag else srow
+
+        def run():
+            mx.mxfa_quantize_col32_row32(dev["v"], C, T, C, cu_d, len(lens), max(lens), dcol, scol, drow, srow, stream)
+            if jag:
+                mx.mxfa_varlen_scale_scatter(scol, cu_d, len(lens), max(lens), C, mx.COL32, pcol, pcol.shape[0], stream)
+                mx.mxfa_varlen_scale_scatter(srow, cu_d, len(lens), max(lens), C, mx.ROW32, prow, prow.shape[0], stream)
+        return mx.MxOperand(dcol, pcol, mx.COL32), mx.MxOperand(drow, prow, mx.ROW32), run
+    if fwd_only:
+        vop, rv = operand("v", mx.COL32, Tk, nbk, Pk, ck_d, lens_k, jag_k)
+        runs = [rq, rk, rv]
+    else:
+        vop, vdop, rv = operand_v_both(Tk, nbk, Pk, ck_d, lens_k, jag_k)
         doop, rdo = operand("do", mx.SQ32, Tq, nbq, Pq, cq_d, lens_q, jag_q)
-        runs += [rvd, rdo]
+        runs = [rq, rk, rv, rdo]
 
     def quant():
         for r in runs:
@@ -797,8 +811,7 @@ def main():
             ev["quant"][i][0].record(stream)
         mx.mxfa_quantize(dev["q"], C, T, C, cu_d, B, N, mx.SQ32, qd, qs, None, stream)
         mx.mxfa_quantize(dev["k"], C, T, C, cu_d, B, N, mx.SQ32, kd, ks, None, stream)
-        mx.mxfa_quantize(dev["v"], C, T, C, cu_d, B, N, mx.COL32, vd_, vs, None, stream)
-        mx.mxfa_quantize(dev["v"], C, T, C, cu_d, B, N, mx.ROW32, vrd, vrs, None, stream)
+        mx.mxfa_quantize_col32_row32(dev["v"], C, T, C, cu_d, B, N, vd_, vs, vrd, vrs, stream)
         mx.mxfa_quantize(dev["do"], C, T, C, cu_d, B, N, mx.SQ32, dod, dos, None, stream)
         if record:
             ev["quant"][i][1].record(stream)
@@ -884,7 +897,8 @@ def main():
     f_bwd = 2.5 * f_fwd
     step_s = wall / args.steps
     value = (f_fwd + f_bwd) / step_s / 1e15
-    quant_bytes = 5 * T * C * (2 + 1) + 3 * T * C / 1024 + T * C / 32 * 2  # bf16 in, e4m3 out, scales
+    # Q, K, V, dO read once in bf16; five E4M3 payloads (V's COL32 and ROW32 from one read); scales
+    quant_bytes = 4 * T * C * 2 + 5 * T * C + 3 * T * C / 1024 + T * C / 32 * 2
     fwd_pf, bwd_pf = f_fwd / med["fwd"] / 1e15, f_bwd / med["bwd"] / 1e15
     dominant = "bwd" if med["bwd"] >= med["fwd"] else "fwd"
     flops_dom = f_bwd if dominant == "bwd" else f_fwd

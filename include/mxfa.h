@@ -123,6 +123,20 @@ mxfa_status mxfa_quantize(const uint16_t* x, int64_t ld_x, int64_t T, int C, con
                           int max_seqlen, mxfa_block mode, uint8_t* data_out, uint8_t* scale_out,
                           uint8_t* scale_t_out, void* stream);
 
+/* COL32 and ROW32 quantization of one bf16 matrix from a single read: the payloads and scales that
+ * mxfa_quantize writes for MXFA_COL32 and for MXFA_ROW32, byte for byte, for an operand contracted
+ * over the tokens in one GEMM and over its columns in another (V: P V in the forward, dP = dO V^T in
+ * the backward) [BR item 7: both scale layouts from one producer pass; TC paragraph 3: the scale
+ * blocks run along each GEMM's contraction dimension].
+ *   x, ld_x, T, C, cu_seqlens, nseq, max_seqlen : as mxfa_quantize (cu_seqlens required; rows outside
+ *                the sequences are not written)
+ *   data_col, scale_col : the COL32 payload [T, C] and its compact scales
+ *   data_row, scale_row : the ROW32 payload [T, C] and its scales [T][C/32]
+ * All five pointers 16-byte aligned. Errors as mxfa_quantize. */
+mxfa_status mxfa_quantize_col32_row32(const uint16_t* x, int64_t ld_x, int64_t T, int C, const int32_t* cu_seqlens,
+                                      int nseq, int max_seqlen, uint8_t* data_col, uint8_t* scale_col,
+                                      uint8_t* data_row, uint8_t* scale_row, void* stream);
+
 /* MXFP4 quantization of a bf16 matrix in ROW32 blocks (1 x 32 along the columns), by the OCP MX rule
  * for E2M1 [brifing.si "Future directions"; the rule of mxfa_quantize with E2M1's largest exponent]:
  * scale code e = clamp(exponent_field(amax) - 2, 0, 254), 255 if the block holds NaN or Inf; element

@@ -257,6 +257,25 @@ mxfa_status mxfa_quantize(const uint16_t* x, int64_t ld_x, int64_t T, int C, con
                     fn);
 }
 
+mxfa_status mxfa_quantize_col32_row32(const uint16_t* x, int64_t ld_x, int64_t T, int C, const int32_t* cu_seqlens,
+                                      int nseq, int max_seqlen, uint8_t* data_col, uint8_t* scale_col,
+                                      uint8_t* data_row, uint8_t* scale_row, void* stream) {
+  const char* fn = "mxfa_quantize_col32_row32";
+  if (T < 0) return fail(MXFA_ERR_INVALID, "%s: T=%lld < 0", fn, (long long)T);
+  if (C <= 0 || C % 32) return fail(MXFA_ERR_INVALID, "%s: C=%d must be a positive multiple of 32", fn, C);
+  if (ld_x < C || ld_x % 8) return fail(MXFA_ERR_INVALID, "%s: ld_x=%lld must be >= C and a multiple of 8", fn, (long long)ld_x);
+  if (!x || !data_col || !scale_col || !data_row || !scale_row)
+    return fail(MXFA_ERR_INVALID, "%s: NULL x/data_col/scale_col/data_row/scale_row", fn);
+  if (!aligned(x, 16) || !aligned(data_col, 16) || !aligned(scale_col, 16) || !aligned(data_row, 16) ||
+      !aligned(scale_row, 16))
+    return fail(MXFA_ERR_INVALID, "%s: x and the four outputs must be 16-byte aligned", fn);
+  mxfa_status st = check_jagged(cu_seqlens, nseq, max_seqlen, T, fn);
+  if (st != MXFA_OK) return st;
+  return hip_status(mxfa::launch_quantize_col32_row32(x, ld_x, C, cu_seqlens, nseq, max_seqlen, data_col, scale_col,
+                                                      data_row, scale_row, (hipStream_t)stream),
+                    fn);
+}
+
 mxfa_status mxfa_quantize_e2m1(const uint16_t* x, int64_t ld_x, int64_t T, int C, uint8_t* data_out,
                                uint8_t* scale_out, void* stream) {
   const char* fn = "mxfa_quantize_e2m1";

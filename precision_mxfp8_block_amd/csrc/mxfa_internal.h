@@ -27,6 +27,9 @@ struct AttnProblem {
 hipError_t launch_quantize(const uint16_t* x, int64_t ld_x, int64_t T, int C, const int32_t* cu, int nseq,
                            int max_seqlen, int mode, uint8_t* data, uint8_t* scale, uint8_t* scale_t,
                            hipStream_t stream);
+hipError_t launch_quantize_col32_row32(const uint16_t* x, int64_t ld_x, int C, const int32_t* cu, int nseq,
+                                      int max_seqlen, uint8_t* data_col, uint8_t* scale_col, uint8_t* data_row,
+                                      uint8_t* scale_row, hipStream_t stream);
 // MXFP4 (E2M1) ROW32 quantization: payload [T, C/2], scales [T][C/32].
 hipError_t launch_quantize_e2m1(const uint16_t* x, int64_t ld_x, int64_t T, int C, uint8_t* data, uint8_t* scale,
                                hipStream_t stream);

@@ -246,6 +246,92 @@ __global__ void __launch_bounds__(256) quantize_col32_kernel(const uint16_t* __r
 }
 
 // ---------------------------------------------------------------------------------------------
+// COL32 and ROW32 of one matrix from one read (an operand contracted over the tokens in one GEMM and
+// over the columns in another, as V is in the attention's forward and backward). The wave layout of
+// the COL32 kernel; a row's 32-column ROW32 block is the 4 columns of 8 consecutive lanes (lane bits
+// 0-2), whose maximum takes three DPP steps. Both payloads leave as the COL32 kernel's stores; lane
+// 8 b + 0 stores the ROW32 code of its row and block. Same grid as the COL32 kernel.
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t max_over_8_lanes(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+  return max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+}
+
+__global__ void __launch_bounds__(256) quantize_col32_row32_kernel(const uint16_t* __restrict__ x, int64_t ld_x,
+                                                                   int C, const int32_t* __restrict__ cu,
+                                                                   uint8_t* __restrict__ data_c,
+                                                                   uint8_t* __restrict__ scale_c,
+                                                                   uint8_t* __restrict__ data_r,
+                                                                   uint8_t* __restrict__ scale_r) {
+  const int s = blockIdx.z, b = blockIdx.y;
+  const int64_t t0 = cu[s], L = (int64_t)cu[s + 1] - t0;
+  if ((int64_t)b * 32 >= L) return;  // uniform over the workgroup
+  const SeqOffsets off = seq_offsets(cu, s);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int cg = blockIdx.x * 4 + wave;  // 128-column group
+  if (cg * 128 >= C) return;             // whole wave leaves together
+  const int col = cg * 128 + 4 * (lane & 31);
+  // C is a multiple of 32, so the lanes past C are whole 8-lane ROW32 groups: they compute but store
+  // nothing
+  const bool col_ok = col < C;
+  const int col_ld = col_ok ? col : cg * 128;
+  const int half = lane >> 5;
+  const int rows = (int)min<int64_t>(32, L - (int64_t)b * 32);
+  const int64_t ta = t0 + (int64_t)b * 32;
+  uint2 v[16];
+  uint32_t am[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    v[i] = *reinterpret_cast<const uint2*>(x + (ta + min(16 * half + i, rows - 1)) * ld_x + col_ld);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    am[0] = max(am[0], v[i].x & 0x7fffu);
+    am[1] = max(am[1], (v[i].x >> 16) & 0x7fffu);
+    am[2] = max(am[2], v[i].y & 0x7fffu);
+    am[3] = max(am[3], (v[i].y >> 16) & 0x7fffu);
+  }
+  uint32_t code[4];
+  float inv[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    auto sw = __builtin_amdgcn_permlane32_swap(am[k], am[k], false, false);  // the other half-wave
+    const uint32_t m = max((uint32_t)sw[0], (uint32_t)sw[1]);
+    code[k] = mx_code_from_amax_bits(m << 16);
+    inv[k] = code[k] == 255u ? 0.0f : mx_inv_scale(code[k]);
+  }
+  const uint32_t cnan = (code[0] == 255u ? 0xffu : 0u) | (code[1] == 255u ? 0xff00u : 0u) |
+                        (code[2] == 255u ? 0xff0000u : 0u) | (code[3] == 255u ? 0xff000000u : 0u);
+  const int64_t cs = C >> 5;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float f0 = bf16_to_f32(v[i].x & 0xffffu), f1 = bf16_to_f32(v[i].x >> 16);
+    const float f2 = bf16_to_f32(v[i].y & 0xffffu), f3 = bf16_to_f32(v[i].y >> 16);
+    const uint32_t rm = max_over_8_lanes(max(max(v[i].x & 0x7fffu, (v[i].x >> 16) & 0x7fffu),
+                                             max(v[i].y & 0x7fffu, (v[i].y >> 16) & 0x7fffu)));
+    const uint32_t rcode = mx_code_from_amax_bits(rm << 16);
+    const int r = 16 * half + i;
+    if (col_ok && r < rows) {
+      uint32_t oc = mx_pack4(f0 * inv[0], f1 * inv[1], f2 * inv[2], f3 * inv[3]);
+      oc = (oc & ~cnan) | (0x7f7f7f7fu & cnan);
+      uint32_t orow = 0x7f7f7f7fu;
+      if (rcode != 255u) {
+        const float ri = mx_inv_scale(rcode);
+        orow = mx_pack4(f0 * ri, f1 * ri, f2 * ri, f3 * ri);
+      }
+      *reinterpret_cast<uint32_t*>(data_c + (ta + r) * C + col) = oc;
+      *reinterpret_cast<uint32_t*>(data_r + (ta + r) * C + col) = orow;
+      if ((lane & 7) == 0) scale_r[(ta + r) * cs + (col >> 5)] = (uint8_t)rcode;
+    }
+  }
+  if (half == 0 && col_ok) {
+    const int64_t br = off.blocks32 + b;
+    *reinterpret_cast<uint32_t*>(scale_c + br * C + col) =
+        code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
 // SQ32: 32 x 32 blocks. A wave covers 32 rows x 64 columns (two blocks): lane l reads the 16-byte
 // chunk l % 8 (8 bf16) of rows l / 8 + 8 i, i = 0..3, so every load and store instruction covers
 // whole 128-byte row segments. The lane's block is (l % 8) / 4; its maximum is taken over the 32
@@ -601,6 +687,16 @@ hipError_t launch_quantize(const uint16_t* x, int64_t ld_x, int64_t T, int C, co
     hipLaunchKernelGGL(quantize_sq32_kernel, grid, dim3(256), 0, stream, x, ld_x, C, cu, nseq, data, scale,
                        scale_t);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_col32_row32(const uint16_t* x, int64_t ld_x, int C, const int32_t* cu, int nseq,
+                                      int max_seqlen, uint8_t* data_col, uint8_t* scale_col, uint8_t* data_row,
+                                      uint8_t* scale_row, hipStream_t stream) {
+  if (max_seqlen == 0) return hipSuccess;
+  dim3 grid((unsigned)((C + 511) / 512), (unsigned)((max_seqlen + 31) / 32), (unsigned)nseq);
+  hipLaunchKernelGGL(quantize_col32_row32_kernel, grid, dim3(256), 0, stream, x, ld_x, C, cu, data_col, scale_col,
+                     data_row, scale_row);
   return hipGetLastError();
 }
 

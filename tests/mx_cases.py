@@ -122,6 +122,25 @@ def gpu_quantize_padded(x_dev, cu, cu_d, mode):
     return data, padded, scale
 
 
+def gpu_quantize_v_both_padded(x_dev, cu, cu_d):
+    """V's COL32 and ROW32 payloads from one read (mxfa_quantize_col32_row32, guarded outputs), each
+    with its scales scattered to the padded layout when needed: ((data, padded, compact) COL32, (...) ROW32)."""
+    T, C = x_dev.shape
+    lens = np.diff(np.asarray(cu, np.int64))
+    nb = int(np.sum((lens + 31) // 32))
+    dc, sc = Guarded((T, C), torch.uint8), Guarded((nb, C), torch.uint8)
+    dr, sr = Guarded((T, C), torch.uint8), Guarded((T, C // 32), torch.uint8)
+    mx.mxfa_quantize_col32_row32(x_dev, x_dev.stride(0), T, C, cu_d, len(lens), int(lens.max()), dc.t, sc.t, dr.t, sr.t)
+    torch.cuda.synchronize()
+    for g, n in ((dc, "COL32 payload"), (sc, "COL32 scales"), (dr, "ROW32 payload"), (sr, "ROW32 scales")):
+        g.check(n)
+    out = []
+    for d, sc_, mode in ((dc.t, sc.t, mx.COL32), (dr.t, sr.t, mx.ROW32)):
+        padded = sc_ if np.all(lens % 128 == 0) else gpu_scale_scatter(sc_, cu, cu_d, C, mode)
+        out.append((d, padded, sc_))
+    return tuple(out)
+
+
 def token_blocks(lens):
     """(start, stop) token rows of every 32-token block, counted from each sequence start."""
     out, t0 = [], 0

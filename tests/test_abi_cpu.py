@@ -26,7 +26,7 @@ def _declared_functions():
 
 def test_header_declares_the_abi():
     names = _declared_functions()
-    for n in ["mxfa_quantize", "mxfa_quantize_e2m1", "mxfa_quantize_e2m3", "mxfa_fwd", "mxfa_fwd_p_scale", "mxfa_fwd_mx_out", "mxfa_bwd", "mxfa_bwd_mx_out",
+    for n in ["mxfa_quantize", "mxfa_quantize_col32_row32", "mxfa_quantize_e2m1", "mxfa_quantize_e2m3", "mxfa_fwd", "mxfa_fwd_p_scale", "mxfa_fwd_mx_out", "mxfa_bwd", "mxfa_bwd_mx_out",
               "mxfa_varlen_scale_scatter",
               "mxfa_rmsnorm_quantize",
               "mxfa_linear_quantize", "mxfa_linear_bwd_data", "mxfa_linear_bwd_weight",
@@ -356,3 +356,25 @@ def test_rmsnorm_bwd_argument_errors(kw, expect):
                                  a["workspace_bytes"], a["dx"], a["dgamma"], 0)
     assert st == expect, _last()
     assert "mxfa_rmsnorm_bwd" in _last()
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(C=48), INVALID),
+    (dict(ld_x=100), INVALID),
+    (dict(ld_x=132), INVALID),
+    (dict(x=0), INVALID),
+    (dict(cu=0), INVALID),              # the COL32 blocks follow the sequences
+    (dict(nseq=0), INVALID),
+    (dict(max_seqlen=300), INVALID),    # > T
+    (dict(dc=P + 8), INVALID),
+    (dict(sc=0), INVALID),
+    (dict(dr=P + 4), INVALID),
+    (dict(sr=0), INVALID),
+    (dict(T=-1), INVALID),
+])
+def test_quantize_col32_row32_argument_errors(kw, expect):
+    a = dict(x=P, ld_x=128, T=256, C=128, cu=P, nseq=2, max_seqlen=128, dc=P, sc=P, dr=P, sr=P)
+    a.update(kw)
+    st = _lib().mxfa_quantize_col32_row32(a["x"], a["ld_x"], a["T"], a["C"], a["cu"], a["nseq"], a["max_seqlen"],
+                                          a["dc"], a["sc"], a["dr"], a["sr"], 0)
+    assert st == expect and "mxfa_quantize_col32_row32" in _last()

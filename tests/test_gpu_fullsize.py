@@ -25,7 +25,8 @@ import torch
 import oracle
 import precision_mxfp8_block_amd as mx
 import synth
-from mx_cases import (Guarded, LinearCase, certify_linear, check_grads, check_o, cu_dev, gpu_quantize_padded, say,
+from mx_cases import (Guarded, LinearCase, certify_linear, check_grads, check_o, cu_dev, gpu_quantize_padded,
+                      gpu_quantize_v_both_padded, say,
                       to_dev_bf16, to_host_bf16_bits)
 
 pytestmark = pytest.mark.gpu
@@ -98,7 +99,12 @@ class FullAttn:
     def gpu_fwd(self, p_scale=mx.P_STATIC):
         self.gq = gpu_quantize_padded(self.dev["q"], self.cu_q, self.cu_q_d, self.qk_mode)
         self.gk = gpu_quantize_padded(self.dev["k"], self.cu_k, self.cu_k_d, self.qk_mode)
-        self.gv = gpu_quantize_padded(self.dev["v"], self.cu_k, self.cu_k_d, mx.COL32)
+        if self.qk_mode == mx.SQ32:
+            # training: V's two payloads from one read, as the benchmark's step quantizes it
+            self.gv, self.gvd = gpu_quantize_v_both_padded(self.dev["v"], self.cu_k, self.cu_k_d)
+        else:
+            self.gv = gpu_quantize_padded(self.dev["v"], self.cu_k, self.cu_k_d, mx.COL32)
+            self.gvd = None
         self.args = mx.AttnArgs(mx.MxOperand(self.gq[0], self.gq[1], self.qk_mode),
                                 mx.MxOperand(self.gk[0], self.gk[1], self.qk_mode),
                                 mx.MxOperand(self.gv[0], self.gv[1], mx.COL32),
@@ -115,7 +121,8 @@ class FullAttn:
         self.o, self.lse = o.t, lse.t
 
     def gpu_bwd(self, dq_mode, sigma):
-        self.gvd = gpu_quantize_padded(self.dev["v"], self.cu_k, self.cu_k_d, mx.ROW32)
+        if self.gvd is None:
+            self.gvd = gpu_quantize_padded(self.dev["v"], self.cu_k, self.cu_k_d, mx.ROW32)
         self.gdo = gpu_quantize_padded(self.dev["do"], self.cu_q, self.cu_q_d, mx.SQ32)
         need = mx.mxfa_bwd_workspace_size(self.args, dq_mode)
         ws = Guarded((need,), torch.uint8)

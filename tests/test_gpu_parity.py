@@ -55,6 +55,60 @@ def test_quantize_bit_exact(mode, lens, C):
         np.testing.assert_array_equal(scale_t.cpu().numpy(), st_ref)
 
 
+def gpu_quantize_col32_row32(x_dev, cu, ld=None):
+    T, C = x_dev.shape
+    lens = np.diff(np.asarray(cu, np.int64))
+    nb = int(np.sum((lens + 31) // 32))
+    dc, sc = Guarded((T, C), torch.uint8), Guarded((nb, C), torch.uint8)
+    dr, sr = Guarded((T, C), torch.uint8), Guarded((T, C // 32), torch.uint8)
+    mx.mxfa_quantize_col32_row32(x_dev, ld or x_dev.stride(0), T, C, cu_dev(cu), len(lens), int(lens.max()), dc.t,
+                                 sc.t, dr.t, sr.t)
+    torch.cuda.synchronize()
+    for g, n in ((dc, "COL32 payload"), (sc, "COL32 scales"), (dr, "ROW32 payload"), (sr, "ROW32 scales")):
+        g.check(n)
+    return [g.t.cpu().numpy() for g in (dc, sc, dr, sr)]
+
+
+@pytest.mark.parametrize("lens", [[256], [37, 128, 1, 300, 95, 64]])
+@pytest.mark.parametrize("C", [384, 160, 224, 96, 2048])
+def test_quantize_col32_row32_bit_exact(lens, C):
+    """One read, both layouts: byte for byte the oracle's COL32 and ROW32 quantizations (NaN/Inf blocks,
+    subnormals, ties, ragged sequence tails, partial column groups)."""
+    say(f"quantize COL32+ROW32 lens={lens} C={C}")
+    cu = synth.cu_seqlens(lens)
+    T = int(cu[-1])
+    x = _special_matrix(11, T, C)
+    dc, sc, dr, sr = gpu_quantize_col32_row32(to_dev_bf16(x), cu)
+    dc_ref, sc_ref, _ = oracle.quantize(x, cu, oracle.COL32)
+    dr_ref, sr_ref, _ = oracle.quantize(x, cu, oracle.ROW32)
+    np.testing.assert_array_equal(sc, sc_ref)
+    np.testing.assert_array_equal(dc, dc_ref)
+    np.testing.assert_array_equal(sr, sr_ref)
+    np.testing.assert_array_equal(dr, dr_ref)
+
+
+def test_quantize_col32_row32_strided_and_sweep():
+    """ld_x > C, and every bf16 pattern (the exhaustive sweep matrix) through the fused quantizer."""
+    from test_gpu_quantize_sweep import sweep_matrix
+    say("quantize COL32+ROW32 strided")
+    T, C, ld = 96, 128, 200
+    full = synth.normal_bf16(5, 1, (T, ld))
+    cu = synth.cu_seqlens([40, 56])
+    x = np.ascontiguousarray(full[:, :C])
+    dc, sc, dr, sr = gpu_quantize_col32_row32(to_dev_bf16(full)[:, :C], cu, ld=ld)
+    for got, ref in zip((dc, sc), oracle.quantize(x, cu, oracle.COL32)[:2]):
+        np.testing.assert_array_equal(got, ref)
+    for got, ref in zip((dr, sr), oracle.quantize(x, cu, oracle.ROW32)[:2]):
+        np.testing.assert_array_equal(got, ref)
+    say("quantize COL32+ROW32 sweep")
+    x, cu = sweep_matrix()
+    dc, sc, dr, sr = gpu_quantize_col32_row32(to_dev_bf16(x), cu)
+    for got, ref in zip((dc, sc), oracle.quantize(x, cu, oracle.COL32)[:2]):
+        np.testing.assert_array_equal(got, ref)
+    for got, ref in zip((dr, sr), oracle.quantize(x, cu, oracle.ROW32)[:2]):
+        np.testing.assert_array_equal(got, ref)
+
+
 def test_quantize_strided_rows():
     """ld_x > C: the quantizer reads the first C columns of each row."""
     say("quantize strided")
