@@ -335,9 +335,10 @@ def attn_flops(lens_q, lens_k, H, causal):
 
 def bench_attention_workload(args, torch, mx, label, workload, lens_q, lens_k, H, causal, outlier_p, seed,
                              fwd_only=False, qk_mode=None, dq_modes=((1, 1.0), (0, 1.0)), cpu_slices=4,
-                             cpu_backward=False, extra_config=None, qk_small=None):
+                             cpu_backward=False, extra_config=None, qk_small=None, keep_fwd=None):
     """One attention workload at its full size: quantize, forward and backward (each dQ mode) timed over
-    back-to-back calls with HIP events on the launch stream. Returns the JSON dict (not printed)."""
+    back-to-back calls with HIP events on the launch stream. Returns the JSON dict (not printed); with
+    keep_fwd (a list) the forward call on the quantized operands is appended to it."""
     stream = torch.cuda.current_stream()
     qk_mode = (mx.ROW32 if fwd_only else mx.SQ32) if qk_mode is None else qk_mode
     cu_q, cu_k = synth_mod.cu_seqlens(lens_q), synth_mod.cu_seqlens(lens_k)
@@ -416,6 +417,8 @@ def bench_attention_workload(args, torch, mx, label, workload, lens_q, lens_k, H
     quant()
     t_quant = _time_back_to_back(torch, stream, quant, 2, max(3, args.steps // 4))
     t_fwd = _time_back_to_back(torch, stream, lambda: mx.mxfa_fwd(attn, o, lse, stream), 2, args.steps)
+    if keep_fwd is not None:
+        keep_fwd.append(lambda: mx.mxfa_fwd(attn, o, lse, stream))
     f_fwd = attn_flops(lens_q, lens_k, H, causal)
     res = {"fwd_us": round(t_fwd * 1e6, 2), "fwd_pflops": round(f_fwd / t_fwd / 1e15, 4),
            "quant_us": round(t_quant * 1e6, 2)}
@@ -497,22 +500,51 @@ def bench_workloads(args, torch, mx):
         print(json.dumps(line), flush=True)
 
 
+def _time_round_robin(torch, stream, calls, warmup, rounds):
+    """Median time of each call when the calls take turns (each launch between its own pair of HIP
+    events), so that a clock that drifts over the run weighs on all of them alike."""
+    for _ in range(warmup):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    ts = [[] for _ in calls]
+    for _ in range(rounds):
+        for i, c in enumerate(calls):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            c()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts[i].append(e0.elapsed_time(e1) * 1e-3)
+    return [float(np.median(t)) for t in ts]
+
+
 def bench_forward_only(args, torch, mx):
-    """The forward-only LLM shape with Q/K in MXFP8 and, on the same inputs, in MXFP4 and MXFP6."""
-    lines = []
+    """The forward-only LLM shape with Q/K in MXFP8 and, on the same inputs, in MXFP4 and MXFP6. Each line
+    times its own forward back to back; the three forwards are then also timed taking turns
+    (`fwd_us_interleaved`), which compares them at the same clock."""
+    lines, fwds = [], []
     fo = bench_attention_workload(
         args, torch, mx, "forward-only", "LLM forward B=4 H=16 N=4096, Q/K ROW32, V COL32",
-        [N] * B, [N] * B, H, False, 0.0, SEED, fwd_only=True, cpu_slices=4)
+        [N] * B, [N] * B, H, False, 0.0, SEED, fwd_only=True, cpu_slices=4, keep_fwd=fwds)
     lines.append(fo)
     f4 = bench_attention_workload(
         args, torch, mx, "forward-only MXFP4 Q/K", "LLM forward B=4 H=16 N=4096, Q/K MXFP4 (E2M1) ROW32, V E4M3 COL32",
-        [N] * B, [N] * B, H, False, 0.0, SEED, fwd_only=True, cpu_slices=2, qk_small="e2m1")
+        [N] * B, [N] * B, H, False, 0.0, SEED, fwd_only=True, cpu_slices=2, qk_small="e2m1", keep_fwd=fwds)
     f6 = bench_attention_workload(
         args, torch, mx, "forward-only MXFP6 Q/K", "LLM forward B=4 H=16 N=4096, Q/K MXFP6 (E2M3) ROW32, V E4M3 COL32",
-        [N] * B, [N] * B, H, False, 0.0, SEED, fwd_only=True, cpu_slices=2, qk_small="e2m3")
+        [N] * B, [N] * B, H, False, 0.0, SEED, fwd_only=True, cpu_slices=2, qk_small="e2m3", keep_fwd=fwds)
+    rr = _time_round_robin(torch, torch.cuda.current_stream(), fwds, 3, max(10, args.steps))
+    inter = {"mxfp8": round(rr[0] * 1e6, 2), "mxfp4": round(rr[1] * 1e6, 2), "mxfp6": round(rr[2] * 1e6, 2)}
+    print("# forward-only, the three taking turns: " + ", ".join(f"{k}={v} us" for k, v in inter.items()),
+          file=sys.stderr, flush=True)
+    fo["config"]["fwd_us_interleaved"] = inter
     for f in (f4, f6):
         f["config"]["mxfp8_qk_same_shape"] = {k: fo["config"][k] for k in ("fwd_us", "fwd_pflops", "quant_us")}
+        f["config"]["fwd_us_interleaved"] = inter
         lines.append(f)
+    fwds.clear()
+    torch.cuda.empty_cache()
     return lines
 
 
