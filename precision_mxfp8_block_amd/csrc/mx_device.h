@@ -155,16 +155,6 @@ __device__ __forceinline__ int lds_swz(int row) {
   return (k & 4) | ((k & 1) << 1) | ((k >> 1) & 1);
 }
 
-// Wave-wide (64 lanes) maximum of an unsigned value.
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    uint32_t o = (uint32_t)__shfl_xor((int)v, off, 64);
-    v = v > o ? v : o;
-  }
-  return v;
-}
-
 // Sum over the 64 lanes of a wave, returned in every lane: DPP within rows of 16 (after the quad
 // steps each group of lanes holds one value, so the mirrors add the partner group), then the
 // permlane16 and permlane32 swaps across rows. The wave must be fully active.
