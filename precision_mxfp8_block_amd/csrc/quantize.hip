@@ -3,7 +3,8 @@
 // All three are HBM-bound streaming kernels: every input byte is read once with 16-byte (or
 // 8-byte) coalesced loads, every output byte written once. The block scale comes from the
 // exponent bits of the block maximum (integer max over magnitude bit patterns, no logarithm or
-// division), the payload from the hardware E4M3 converter after a saturating clamp.
+// division), the payload from the hardware E4M3 converter after a saturating clamp (E2M1 and E2M3:
+// the scaled FP4 / FP6 converters, which saturate by themselves).
 // Pages: andresseo.expert "MXFP8 FlashAttention-4 Hits 2.85 Petaflops...", section "Inside the
 // TMEM Bargain and Zero-Gather Jagged Pipeline" (32-element blocks, bit-extraction scale, fused
 // RMSNorm producer, scale-only padding for jagged inputs); brifing.si items 5-7.
