@@ -11,8 +11,8 @@ import oracle
 import precision_mxfp8_block_amd as mx
 import synth
 from oracle import mxfp4, mxfp6
-from mx_cases import (Guarded, bf16_bits_to_f64, check_o, cu_dev, gpu_quantize_padded, gpu_scale_scatter, say,
-                      to_dev_bf16, to_host_bf16_bits)
+from mx_cases import (O_REL_FRO, Guarded, bf16_bits_to_f64, certify_mx_output, check_o, cu_dev, gpu_quantize_padded,
+                      gpu_scale_scatter, say, to_dev_bf16, to_host_bf16_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -143,6 +143,7 @@ class Fp4Case:
         args = mx.AttnArgs(mx.MxOperand(q4, qsp, mx.ROW32, elem), mx.MxOperand(k4, ksp, mx.ROW32, elem),
                            mx.MxOperand(gv[0], gv[1], mx.COL32), cq, ck, len(self.lens_q), max(self.lens_q),
                            max(self.lens_k), self.Tq, self.Tk, self.H, 128, self.c, self.causal)
+        self.args = args
         o, lse = Guarded((self.Tq, self.C), torch.bfloat16), Guarded((self.H, self.Tq), torch.float32)
         if p_scale == mx.P_STATIC:
             mx.mxfa_fwd(args, o.t, lse.t)
@@ -182,6 +183,40 @@ def test_fwd_small_qk_parity(label, seed, lq, lk, H, causal, p_scale, fmt):
     np.testing.assert_array_equal(case.q4_gpu, case.q4_ref)
     np.testing.assert_array_equal(case.k4_gpu, case.k4_ref)
     check_o(o_g, o32, lse_g, lse, label=label)
+
+
+MX_OUT_SMALL_CASES = [FWD_CASES[i] for i in (1, 2)]
+
+
+@pytest.mark.parametrize("fmt", ["e2m1", "e2m3"])
+@pytest.mark.parametrize("label,seed,lq,lk,H,causal,p_scale", MX_OUT_SMALL_CASES, ids=[c[0] for c in MX_OUT_SMALL_CASES])
+def test_fwd_small_qk_mx_out(label, seed, lq, lk, H, causal, p_scale, fmt):
+    """The MXFP4 / MXFP6 Q/K forward writing O as MXFP8 (ROW32 blocks along D) with bf16 O in the same
+    pass: the bf16 O and LSE equal mxfa_fwd's bit for bit, every code and byte of the MXFP8 O is
+    certified against that bf16 O (mx_cases.certify_mx_output), and against the oracle's FP32 O the
+    codes are within one and the dequantized O within 2^-4 + the O tolerance (relative Frobenius)."""
+    say(f"{fmt} Q/K forward with MXFP8 O, case {label}")
+    case = Fp4Case(seed, lq, lk, H, causal, fmt)
+    o_bits, lse_g = case.run_gpu()
+    T, C = case.Tq, case.C
+    o16, od, osc = Guarded((T, C), torch.bfloat16), Guarded((T, C), torch.uint8), Guarded((T, C // 32), torch.uint8)
+    lse2 = Guarded((case.H, T), torch.float32)
+    mx.mxfa_fwd_mx_out(case.args, mx.P_STATIC, o16.t, od.t, osc.t, lse2.t)
+    torch.cuda.synchronize()
+    for g in (o16, od, osc, lse2):
+        g.check("fwd_mx_out output")
+    np.testing.assert_array_equal(to_host_bf16_bits(o16.t), o_bits)
+    np.testing.assert_array_equal(lse2.t.cpu().numpy(), lse_g)
+    gd, gs = od.t.cpu().numpy(), osc.t.cpu().numpy()
+    certify_mx_output(gd, gs, o_bits, case.cu_q, oracle.ROW32, f"{fmt} {label} O")
+    _, o32, _ = case.run_oracle()
+    o32 = np.asarray(o32, np.float32)
+    _, rs, _ = oracle.quantize(o32, case.cu_q, oracle.ROW32)
+    assert np.abs(gs.astype(np.int64) - rs.astype(np.int64)).max() <= 1
+    deq = oracle.dequantize(gd, gs, case.cu_q, oracle.ROW32)
+    fro = float(np.linalg.norm(deq - o32) / np.linalg.norm(o32))
+    say(f"  rel_fro of the dequantized MXFP8 O vs the oracle's FP32 O: {fro:.3e}")
+    assert fro <= 2.0 ** -4 + O_REL_FRO
 
 
 def sqnr_db(x, ref):
