@@ -55,7 +55,9 @@ __device__ __forceinline__ uint32_t mx_pack2_hi(float a, float b, uint32_t old) 
 }
 // Four floats already known to lie in [-448, 448] (no clamp needed), e.g. P * 256 <= 256.
 __device__ __forceinline__ uint32_t mx_pack4_inrange(float a, float b, float c, float d) {
-  uint32_t r = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  // the first conversion writes bytes 0-1 and the second bytes 2-3, so the register the first one
+  // starts from is irrelevant: a's own (no zeroing move)
+  uint32_t r = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, __float_as_int(a), false);
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, (int)r, true);
 }
 __device__ __forceinline__ uint32_t mx_pack4(float a, float b, float c, float d) {
