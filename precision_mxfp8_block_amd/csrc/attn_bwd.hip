@@ -478,12 +478,11 @@ __global__ void __launch_bounds__(64 * kBwdWaves, 1) attn_bwd_kernel(BwdParams p
                 dpacc[v] = e * dpacc[v];  // 256 dS
               }
             // |256 dS| maximum of the lane as a tree of max3, then over the wave
-            float m[6];
+            float m[5];
 #pragma unroll
-            for (int g = 0; g < 5; ++g) m[g] = max3_abs(__builtin_fabsf(dpacc[3 * g]), dpacc[3 * g + 1], dpacc[3 * g + 2]);
-            m[5] = __builtin_fabsf(dpacc[15]);
+            for (int g = 0; g < 5; ++g) m[g] = max3_abs3(dpacc[3 * g], dpacc[3 * g + 1], dpacc[3 * g + 2]);
             const float am = max3_abs(max3_abs(m[0], m[1], m[2]), m[3], m[4]);
-            const float am2 = fmaxf(am, m[5]);
+            const float am2 = max3_abs(am, dpacc[15], dpacc[15]);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
               pk[i] = mx_pack4_inrange(sacc[4 * i], sacc[4 * i + 1], sacc[4 * i + 2], sacc[4 * i + 3]);

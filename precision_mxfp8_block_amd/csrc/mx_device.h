@@ -105,6 +105,14 @@ __device__ __forceinline__ float max3_abs(float acc, float a, float b) {
   return d;
 }
 
+// max(|a|, |b|, |c|) in one v_max3_f32 with absolute-value modifiers on all three sources (no separate
+// sign-clearing instruction); NaN and infinity behave as in max3_abs.
+__device__ __forceinline__ float max3_abs3(float a, float b, float c) {
+  float d;
+  asm("v_max3_f32 %0, |%1|, |%2|, |%3|" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
+}
+
 // A pointer the caller knows to be wave-uniform, moved to scalar registers (a buffer resource built
 // from a value in vector registers would need a loop over its distinct values).
 __device__ __forceinline__ void* mx_uniform_ptr(void* p) {
