@@ -589,7 +589,11 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
     };
 
     // ---- 5. ----
-    if (more) issue_s(Stage<st ^ 1>{}, KB0{}, KB2{});
+    // The next tile's scores are issued whether or not a next tile exists: after the last tile they
+    // are computed from whatever the other stage holds and never read. A conditional issue would
+    // merge two register assignments of the score accumulators after it, which the compiler
+    // resolves with 32 register moves per step.
+    issue_s(Stage<st ^ 1>{}, KB0{}, KB2{});
     pv(0);
     __builtin_amdgcn_sched_barrier(0);
 
@@ -602,7 +606,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
 
     // ---- 7. ----
     pv(1);
-    if (more) issue_s(Stage<st ^ 1>{}, KB2{}, KB4{});
+    issue_s(Stage<st ^ 1>{}, KB2{}, KB4{});
   };
 
   // two tiles per iteration so that each stage's LDS addresses are compile-time offsets
