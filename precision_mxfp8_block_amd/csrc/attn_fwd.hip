@@ -461,9 +461,10 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(FwdParams p) {
         mx0 = max3f(mx0, sacc[2][v], sacc[2][v + 1]);
         mx1 = max3f(mx1, sacc[3][v], sacc[3][v + 1]);
       }
-      const float mx = fmaxf(mx0, mx1);
+      // joins by v_max3 as well (fmaxf would first canonicalize each operand with a max of itself)
+      const float mx = max3f(mx0, mx1, mx1);
       auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      m_new = fmaxf(__uint_as_float(sw2[0]), __uint_as_float(sw2[1]));
+      m_new = max3f(__uint_as_float(sw2[0]), __uint_as_float(sw2[1]), __uint_as_float(sw2[1]));
     } else {
       // one chain per key block, each joined with the other lane half (which holds the block's
       // other 16 keys); the row maximum is the largest block maximum
