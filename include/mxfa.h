@@ -173,6 +173,21 @@ mxfa_status mxfa_varlen_scale_scatter(const uint8_t* compact, const int32_t* cu_
                                       int C, mxfa_block mode, uint8_t* padded_out, int64_t padded_rows,
                                       void* stream);
 
+/* The device's E4M3 conversion, exposed so that it can be checked against an independent encoder on
+ * every fp32 bit pattern [KC "Why MXFP8": E4M3 elements, 448 the largest finite magnitude; AE-TMEM:
+ * P converted online to E4M3]. Byte i of out is the E4M3 code of the fp32 whose bit pattern is
+ * first + i (mod 2^32), computed by the routine the kernels use for
+ *   variant 0 : unscaled values (quantizers, the MXFP8 O and gradient epilogues): round to nearest
+ *               even, saturating at +-448, the sign kept on zero results
+ *   variant 1 : x / sc with sc a power of two (dS_q and projection epilogues), same rounding and
+ *               saturation; sc in [2^-126, 2^119]
+ *   variant 2 : values already in [-448, 448] (P * 256); bytes for other patterns are unspecified
+ * NaN patterns give unspecified bytes (the kernels mark NaN blocks through scale code 255).
+ *   n   : (host) number of patterns, a multiple of 4 in [0, 2^32]
+ *   out : device bytes [n], 4-byte aligned, written entirely (caller owns it)
+ * MXFA_ERR_INVALID for a bad variant, sc, n or pointer, before any launch. */
+mxfa_status mxfa_e4m3_pack_patterns(uint32_t first, int64_t n, int variant, float sc, uint8_t* out, void* stream);
+
 /* Host helper: padded row count for given host-side sequence lengths (NULL-safe). */
 int64_t mxfa_padded_token_rows(const int32_t* cu_seqlens_host, int nseq);
 

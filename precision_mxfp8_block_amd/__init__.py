@@ -19,7 +19,7 @@ __all__ = [
     "fwd_mx_out", "bwd_mx_out",
     "mxfa_bwd_workspace_size", "mxfa_rmsnorm_quantize", "mxfa_linear_quantize", "mxfa_status_string",
     "mxfa_last_error_message", "MxOperand", "AttnArgs", "quantize", "scale_scatter", "fwd", "bwd",
-    "rmsnorm_quantize", "linear_quantize", "E4M3", "E2M1", "E2M3", "mxfa_quantize_e2m1",
+    "rmsnorm_quantize", "linear_quantize", "E4M3", "E2M1", "E2M3", "mxfa_quantize_e2m1", "mxfa_e4m3_pack_patterns",
     "quantize_e2m1", "mxfa_quantize_e2m3", "quantize_e2m3", "mxfa_quantize_col32_row32",
     "mxfa_linear_bwd_data", "mxfa_linear_bwd_weight", "mxfa_linear_bwd_weight_workspace_size", "mxfa_rmsnorm_bwd",
     "mxfa_rmsnorm_bwd_workspace_size", "linear_bwd_data", "linear_bwd_weight", "rmsnorm_bwd",
@@ -75,6 +75,7 @@ def _load():
     lib.mxfa_quantize_col32_row32.argtypes = [P, i64, i64, i32, P, i32, i32, P, P, P, P, P]
     lib.mxfa_quantize_e2m1.argtypes = [P, i64, i64, i32, P, P, P]
     lib.mxfa_quantize_e2m3.argtypes = [P, i64, i64, i32, P, P, P]
+    lib.mxfa_e4m3_pack_patterns.argtypes = [ctypes.c_uint32, i64, i32, f32, P, P]
     lib.mxfa_padded_token_rows.argtypes = [P, i32]
     lib.mxfa_padded_token_rows.restype = i64
     lib.mxfa_fwd.argtypes = [ctypes.POINTER(_AttnArgs), P, P, P]
@@ -101,7 +102,7 @@ def _load():
     lib.mxfa_status_string.restype = ctypes.c_char_p
     lib.mxfa_last_error_message.argtypes = []
     lib.mxfa_last_error_message.restype = ctypes.c_char_p
-    for n in ("mxfa_quantize", "mxfa_quantize_col32_row32", "mxfa_quantize_e2m1", "mxfa_quantize_e2m3", "mxfa_varlen_scale_scatter", "mxfa_fwd", "mxfa_fwd_p_scale", "mxfa_fwd_mx_out", "mxfa_bwd",
+    for n in ("mxfa_quantize", "mxfa_quantize_col32_row32", "mxfa_quantize_e2m1", "mxfa_quantize_e2m3", "mxfa_e4m3_pack_patterns", "mxfa_varlen_scale_scatter", "mxfa_fwd", "mxfa_fwd_p_scale", "mxfa_fwd_mx_out", "mxfa_bwd",
               "mxfa_bwd_mx_out", "mxfa_bwd_no_alloc", "mxfa_rmsnorm_quantize",
               "mxfa_linear_quantize", "mxfa_linear_bwd_data", "mxfa_linear_bwd_weight", "mxfa_rmsnorm_bwd"):
         getattr(lib, n).restype = i32
@@ -155,6 +156,10 @@ def mxfa_quantize_col32_row32(x, ld_x, T, C, cu_seqlens, nseq, max_seqlen, data_
     _check(_load().mxfa_quantize_col32_row32(_ptr(x), ld_x, T, C, _ptr(cu_seqlens), nseq, max_seqlen, _ptr(data_col),
                                              _ptr(scale_col), _ptr(data_row), _ptr(scale_row), _stream(stream)),
            "mxfa_quantize_col32_row32")
+
+
+def mxfa_e4m3_pack_patterns(first, n, variant, sc, out, stream=None):
+    _check(_load().mxfa_e4m3_pack_patterns(first, n, variant, sc, _ptr(out), _stream(stream)), "mxfa_e4m3_pack_patterns")
 
 
 def mxfa_quantize_e2m1(x, ld_x, T, C, data_out, scale_out, stream=None):

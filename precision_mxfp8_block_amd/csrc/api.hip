@@ -276,6 +276,19 @@ mxfa_status mxfa_quantize_col32_row32(const uint16_t* x, int64_t ld_x, int64_t T
                     fn);
 }
 
+mxfa_status mxfa_e4m3_pack_patterns(uint32_t first, int64_t n, int variant, float sc, uint8_t* out, void* stream) {
+  const char* fn = "mxfa_e4m3_pack_patterns";
+  if (n < 0 || n > ((int64_t)1 << 32) || n % 4)
+    return fail(MXFA_ERR_INVALID, "%s: n=%lld must be a multiple of 4 in [0, 2^32]", fn, (long long)n);
+  if (variant < 0 || variant > 2) return fail(MXFA_ERR_INVALID, "%s: variant=%d not in {0, 1, 2}", fn, variant);
+  if (variant == 1 && (!is_pow2(sc) || sc < 0x1p-126f || sc > 0x1p119f))
+    return fail(MXFA_ERR_INVALID, "%s: sc=%g must be a power of two in [2^-126, 2^119]", fn, (double)sc);
+  if (variant != 1) sc = 1.0f;
+  if (n > 0 && !out) return fail(MXFA_ERR_INVALID, "%s: out is NULL", fn);
+  if (!aligned(out, 4)) return fail(MXFA_ERR_INVALID, "%s: out not 4-byte aligned", fn);
+  return hip_status(mxfa::launch_e4m3_pack_patterns(first, n, variant, sc, out, (hipStream_t)stream), fn);
+}
+
 mxfa_status mxfa_quantize_e2m1(const uint16_t* x, int64_t ld_x, int64_t T, int C, uint8_t* data_out,
                                uint8_t* scale_out, void* stream) {
   const char* fn = "mxfa_quantize_e2m1";

@@ -36,6 +36,10 @@ hipError_t launch_quantize_e2m1(const uint16_t* x, int64_t ld_x, int64_t T, int 
 // MXFP6 (E2M3) ROW32 quantization: payload [T, 3C/4] (24 bytes per block), scales [T][C/32].
 hipError_t launch_quantize_e2m3(const uint16_t* x, int64_t ld_x, int64_t T, int C, uint8_t* data, uint8_t* scale,
                                hipStream_t stream);
+// n fp32 bit patterns first, first + 1, ... (mod 2^32) -> E4M3 bytes through pack variant 0/1/2 (n a
+// multiple of 4, out 4-byte aligned).
+hipError_t launch_e4m3_pack_patterns(uint32_t first, int64_t n, int variant, float sc, uint8_t* out,
+                                     hipStream_t stream);
 hipError_t launch_scale_scatter(const uint8_t* compact, const int32_t* cu, int nseq, int max_seqlen, int C, int mode,
                                 uint8_t* padded, int64_t padded_rows, hipStream_t stream);
 hipError_t launch_rmsnorm_quantize(const uint16_t* x, int64_t ld_x, int C, const float* gamma, float eps,

@@ -8,6 +8,8 @@
 // Pages: andresseo.expert "MXFP8 FlashAttention-4 Hits 2.85 Petaflops...", section "Inside the
 // TMEM Bargain and Zero-Gather Jagged Pipeline" (32-element blocks, bit-extraction scale, fused
 // RMSNorm producer, scale-only padding for jagged inputs); brifing.si items 5-7.
+#include <algorithm>
+
 #include "mx_device.h"
 #include "mxfa_internal.h"
 
@@ -753,6 +755,38 @@ hipError_t launch_rmsnorm_quantize(const uint16_t* x, int64_t ld_x, int C, const
       hipLaunchKernelGGL(rmsnorm_quantize_kernel, grid, dim3(256), 0, stream, x, ld_x, C, gamma, eps, cu, nseq, data,
                          scale, scale_t);
   }
+  return hipGetLastError();
+}
+
+// Consecutive fp32 bit patterns through the E4M3 packs the kernels use, four patterns per thread
+// (one 4-byte store): variant 0 the saturating pack of unscaled values (quantizers, O and projection
+// epilogues), 1 the saturating pack of x / sc (dS and projection epilogues), 2 the pack of values
+// known to lie in [-448, 448] (P * 256). Patterns wrap modulo 2^32.
+__global__ void __launch_bounds__(256) e4m3_pack_patterns_kernel(uint32_t first, int64_t nwords, int variant,
+                                                                 float sc, float lim, uint32_t* __restrict__ out) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; w < nwords; w += stride) {
+    const uint32_t b = first + 4u * (uint32_t)w;
+    const float a = __uint_as_float(b), c = __uint_as_float(b + 1u);
+    const float d = __uint_as_float(b + 2u), e = __uint_as_float(b + 3u);
+    uint32_t r;
+    if (variant == 0)
+      r = mx_pack4(a, c, d, e);
+    else if (variant == 1)
+      r = mx_pack4_scaled(a, c, d, e, sc, lim);
+    else
+      r = mx_pack4_inrange(a, c, d, e);
+    out[w] = r;
+  }
+}
+
+hipError_t launch_e4m3_pack_patterns(uint32_t first, int64_t n, int variant, float sc, uint8_t* out,
+                                     hipStream_t stream) {
+  const int64_t nwords = n >> 2;
+  if (nwords == 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((nwords + 255) / 256, 8192);
+  hipLaunchKernelGGL(e4m3_pack_patterns_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, first, nwords, variant,
+                     sc, 448.0f * sc, reinterpret_cast<uint32_t*>(out));
   return hipGetLastError();
 }
 

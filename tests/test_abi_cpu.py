@@ -378,3 +378,19 @@ def test_quantize_col32_row32_argument_errors(kw, expect):
     st = _lib().mxfa_quantize_col32_row32(a["x"], a["ld_x"], a["T"], a["C"], a["cu"], a["nseq"], a["max_seqlen"],
                                           a["dc"], a["sc"], a["dr"], a["sr"], 0)
     assert st == expect and "mxfa_quantize_col32_row32" in _last()
+
+
+@pytest.mark.parametrize("first,n,variant,sc", [(0, 6, 0, 1.0), (0, 8, 3, 1.0), (0, 8, -1, 1.0), (0, 8, 1, 3.0),
+                                                (0, 8, 1, 2.0 ** 120), (0, 8, 1, 2.0 ** -127), (0, -4, 0, 1.0),
+                                                (0, (1 << 32) + 4, 0, 1.0)])
+def test_e4m3_pack_patterns_argument_errors(first, n, variant, sc):
+    lib = _lib()
+    assert lib.mxfa_e4m3_pack_patterns(first, n, variant, sc, P, None) == INVALID
+    assert "mxfa_e4m3_pack_patterns" in _last()
+
+
+def test_e4m3_pack_patterns_pointer_errors():
+    lib = _lib()
+    assert lib.mxfa_e4m3_pack_patterns(0, 8, 0, 1.0, None, None) == INVALID
+    assert lib.mxfa_e4m3_pack_patterns(0, 8, 0, 1.0, P + 2, None) == INVALID
+    assert lib.mxfa_e4m3_pack_patterns(0, 0, 0, 1.0, None, None) == OK  # nothing to write, no launch
