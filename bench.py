@@ -335,7 +335,7 @@ def attn_flops(lens_q, lens_k, H, causal):
 
 def bench_attention_workload(args, torch, mx, label, workload, lens_q, lens_k, H, causal, outlier_p, seed,
                              fwd_only=False, qk_mode=None, dq_modes=((1, 1.0), (0, 1.0)), cpu_slices=4,
-                             cpu_backward=False, extra_config=None, qk_small=None, keep_fwd=None):
+                             cpu_backward=False, extra_config=None, qk_small=None, keep_fwd=None, cpu_repeats=1):
     """One attention workload at its full size: quantize, forward and backward (each dQ mode) timed over
     back-to-back calls with HIP events on the launch stream. Returns the JSON dict (not printed); with
     keep_fwd (a list) the forward call on the quantized operands is appended to it."""
@@ -464,23 +464,29 @@ def bench_attention_workload(args, torch, mx, label, workload, lens_q, lens_k, H
         sl = [{n: np.ascontiguousarray(host[n][int((cu_q if n in ("q", "do") else cu_k)[s]):
                                                int((cu_q if n in ("q", "do") else cu_k)[s + 1]), h * D:(h + 1) * D])
                for n in ("q", "k", "v", "do")} for s, h in picks]
-        dt, cores = oracle_slices(sl, cpu_backward, c, causal, qk_mode, qk_small)
+        runs = [oracle_slices(sl, cpu_backward, c, causal, qk_mode, qk_small) for _ in range(cpu_repeats)]
+        dt, cores = float(np.median([r[0] for r in runs])), runs[0][1]
         f = sum(attn_flops([lens_q[s]], [lens_k[s]], 1, causal) for s, _ in picks) * (3.5 if cpu_backward else 1.0)
         model, nproc, _ = host_cpu()
         out["cpu_baseline"] = {"value": round(f / dt / 1e15, 8), "unit": "PF/s", "cores": cores, "kind": "oracle",
                                "cpu_model": model, "nproc": nproc,
                                "sample": f"{len(picks)} (sequence, head) slices of the longest sequences, quantize + "
                                          f"forward{' + backward' if cpu_backward else ''}, one thread per slice, "
-                                         f"{dt:.1f} s wall"}
+                                         f"{dt:.3g} s wall" + (f" (median of {cpu_repeats} runs)" if cpu_repeats > 1
+                                                               else "")}
     del dev
     torch.cuda.empty_cache()
     return out
 
 
 def bench_workloads(args, torch, mx):
-    """The per-workload lines: causal N=8192 with outliers, jagged 32 sequences beside a uniform batch of
+    """The per-workload lines: the tiny B=1 H=1 N=256 case, causal N=8192 with outliers, jagged 32 sequences beside a uniform batch of
     the same total tokens, and the forward-only LLM shape (Q/K ROW32)."""
     lines = []
+    # the small case: the whole problem on the oracle (one (sequence, head) slice, so one thread), median of 5
+    lines.append(bench_attention_workload(
+        args, torch, mx, "tiny", "tiny B=1 H=1 N=256, fwd + bwd", [256], [256], 1, False, 0.0, 1, cpu_slices=1,
+        cpu_backward=True, cpu_repeats=5))
     lines.append(bench_attention_workload(
         args, torch, mx, "causal outliers", "causal B=4 H=16 N=8192, 0.5% of entries x64, fwd + bwd",
         [8192] * 4, [8192] * 4, 16, True, 0.005, 3, dq_modes=((1, 0.0625), (0, 1.0)), cpu_slices=4))
